@@ -1,0 +1,189 @@
+/*
+ * bi.h - batch-invariant forward-pass kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Every entry point computes each output row with a reduction order that is a
+ * function of that row's own data and of the problem's feature sizes only: it
+ * does not depend on the batch size, on the row's position in the batch, on
+ * which other requests share the launch, or on how many query tokens of a
+ * sequence are in flight.  Sources (web pages):
+ *   [TML]  "Thinking Machines Lab - Defeating Nondeterminism in LLM Inference:
+ *          The Core Role of Batch Invariance" (jasonandjarvis.org), sections
+ *          "1. Batch-Invariant RMSNorm", "2. Batch-Invariant Matrix
+ *          Multiplication", "3. Batch-Invariant Attention".
+ *   [BINR] "Batch Invariance and Numerical Reproducibility" (praveentn.live),
+ *          answers on fixed-size chunks and on sampler/trainer logprobs.
+ *   [HADA] "Como superar a não determinismo na inferência de LLMs"
+ *          (pt.news.hada.io), "Projeto de kernels invariantes a batch", Attention.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; each call enqueues its kernels on
+ *     `stream` (a hipStream_t; NULL means the default stream) and returns.
+ *   - bf16 is IEEE bfloat16 stored as 16-bit words; results are rounded to it
+ *     once, round-to-nearest-even.  Accumulation is fp32.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     negative status nothing was enqueued and no output was touched.
+ *     BI_ERR_HIP reports a failed launch (hipGetLastError after the launch).
+ *   - No global mutable state: calls are thread-safe.  No environment variable,
+ *     flag or tuning table changes the arithmetic.
+ *   - Pointers must be 16-byte aligned and leading dimensions (in elements)
+ *     multiples of 8, so rows can be moved in 16-byte vectors.
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t bi_status;
+#define BI_OK 0
+#define BI_ERR_INVALID_ARG (-1) /* null pointer, bad size, stride or alignment */
+#define BI_ERR_UNSUPPORTED (-2) /* a size the kernels are not built for      */
+#define BI_ERR_WORKSPACE (-3)   /* workspace missing or too small             */
+#define BI_ERR_HIP (-4)         /* the HIP runtime reported a launch failure  */
+
+/* Fixed split size of the split-KV reduction, in tokens ([BINR] fixed-size
+ * chunks: a 1,000-token cache is 256 + 256 + 256 + 232). */
+#define BI_KV_CHUNK 256
+
+typedef enum { BI_BF16 = 0, BI_F32 = 1 } bi_dtype;
+
+typedef void* bi_stream_t; /* a hipStream_t */
+
+/* Text for a status code (static storage; never NULL). */
+const char* bi_status_str(bi_status status);
+
+/* Library version as "major.minor.patch" (static storage). */
+const char* bi_version(void);
+
+/*
+ * RMSNorm ([TML] "1. Batch-Invariant RMSNorm", fig. "Data-Parallel RMSNorm").
+ *   y[r, j] = bf16( x[r, j] * (mean_j x[r, j]^2 + eps)^(-1/2) * gamma[j] )
+ * x: [rows, hidden] bf16, row stride ldx; gamma: [hidden] bf16;
+ * y: [rows, hidden] bf16, row stride ldy (may alias x when ldy == ldx).
+ * One workgroup owns one row and reduces it in one fixed order (per-thread
+ * sums, a fixed wavefront butterfly, a fixed sum over waves), whatever `rows`.
+ * hidden: 8 <= hidden <= 16384, hidden % 8 == 0.  rows == 0 is a no-op.
+ */
+bi_status bi_rmsnorm(const void* x, int64_t ldx, const void* gamma, float eps,
+                     void* y, int64_t ldy, int64_t rows, int64_t hidden, bi_stream_t stream);
+
+/*
+ * GEMM ([TML] "2. Batch-Invariant Matrix Multiplication", figs. "Data-Parallel
+ * Matrix Multiplication" and "Split-K Matmul").
+ *   C[m, n] = sum_k A[m, k] * W[n, k]       (C = A W^T, W stored [N, K] as in
+ *                                            a linear layer's weight)
+ * a: [m, k] bf16, row stride lda; w: [n, k] bf16, row stride ldw;
+ * c: [m, n] of c_dtype (BI_BF16 or BI_F32), row stride ldc.
+ * One tile shape, one MFMA instruction and one ascending K loop with a single
+ * fp32 accumulator per output element are used for every m: no split-K and no
+ * shape-dependent configuration, so row m of C does not depend on the other rows
+ * of A.  k % 32 == 0; m, n >= 0 (m == 0 or n == 0 is a no-op); k >= 32.
+ */
+bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw,
+                  void* c, int64_t ldc, int32_t c_dtype,
+                  int64_t m, int64_t n, int64_t k, bi_stream_t stream);
+
+/*
+ * Paged KV cache layout (one pool per layer; page = `page_size` tokens):
+ *   k_cache: [num_pages][num_kv_heads][page_size][head_dim] bf16 (token-major)
+ *   v_cache: [num_pages][num_kv_heads][head_dim][page_size] bf16 (dim-major)
+ * Token t of a sequence lives in page block_table[seq][t / page_size] at offset
+ * t % page_size.  Cached and newly appended tokens share this one layout
+ * ([HADA] Attention: keep a consistent K/V layout; [TML] fig. "FlashAttention
+ * with KV Cache").
+ */
+
+/*
+ * KV append: write new keys/values into their cache slots before attention.
+ * k_new, v_new: [num_tokens][num_kv_heads][head_dim] bf16 (contiguous);
+ * slot_mapping: [num_tokens] int32, slot = page * page_size + offset; a negative
+ * slot or one >= num_pages * page_size skips that token (padding).
+ * A pure copy: every cache element is written bit-exactly.
+ * head_dim in {64, 128}; page_size in {8, 16, 32, 64, 128, 256} (divides 256).
+ */
+bi_status bi_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                       int32_t num_tokens, void* k_cache, void* v_cache, int32_t num_pages,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                       bi_stream_t stream);
+
+/*
+ * Workspace for bi_attn_decode: per (sequence, q head, chunk) partial results
+ * (max, sum, D accumulators), fp32: num_seqs * num_q_heads * ceil(max_seq_len/256)
+ * * (head_dim + 4) * 4 bytes
+ * (accumulators, max, sum, 2 pad words per record), rounded up to 256 bytes.
+ */
+size_t bi_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                      int32_t max_seq_len);
+
+/*
+ * Decode attention over the paged cache, one query token per sequence
+ * ([TML] "3. Batch-Invariant Attention", figs. "Fixed Number Split KV Strategy"
+ * and "Fixed Size Split KV Strategy"; [BINR] fixed-size chunks).
+ *   For q head h, kv head g = h / (num_q_heads / num_kv_heads):
+ *   s_j = softmax_scale * <q[b, h], K_b[j, g]>,  j < L_b = seq_lens[b]
+ *   out[b, h] = bf16( sum_j softmax(s)_j V_b[j, g] ),  lse[b, h] = log sum_j exp(s_j)
+ * The keys are split into fixed 256-token chunks anchored at position 0 (only
+ * the last is partial); each chunk yields (max, sum, accumulators) and the
+ * chunks are merged in ascending order, starting from (-inf, 0, 0), by a
+ * log-sum-exp step.  The chunking depends on nothing but L_b.
+ * q: [num_seqs][num_q_heads][head_dim] bf16; out: same shape bf16;
+ * lse: [num_seqs][num_q_heads] fp32 or NULL (natural log).
+ * block_table: [num_seqs][max_pages_per_seq] int32; seq_lens: [num_seqs] int32.
+ * max_seq_len: host-side upper bound of seq_lens (sizes the grid; a seq_len
+ * above it is clamped to it).  Page ids outside [0, num_pages) read as zeros.
+ * A sequence with seq_len <= 0 gets out = 0 and lse = -inf.
+ * workspace: >= bi_attn_decode_workspace_bytes(...) bytes of device memory.
+ * head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 and the group size
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}; page_size divides 256.
+ */
+bi_status bi_attn_decode(const void* q, const void* k_cache, const void* v_cache, int32_t num_pages,
+                         const int32_t* block_table, int32_t max_pages_per_seq,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t page_size, float softmax_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, bi_stream_t stream);
+
+/*
+ * Chunked-prefill attention over the paged cache ([TML] "3. Batch-Invariant
+ * Attention", figs. "FlashAttention2 Strategy" and "FlashAttention with KV
+ * Cache"; [HADA] Attention).  Sequence s has ctx_lens[s] cached tokens and a
+ * chunk of n_s = q_start[s+1] - q_start[s] new tokens whose K/V were ALREADY
+ * written to the cache (bi_kv_append) at positions ctx_lens[s] .. ctx_lens[s]+n_s-1.
+ * Query i of sequence s sits at position p = ctx_lens[s] + i and attends keys
+ * 0..p (causal, inclusive).  Each query row is reduced with exactly the chunk
+ * routine and merge step of bi_attn_decode, so a prefilled row is bitwise equal
+ * to decoding the same token with seq_len = p + 1.
+ * q, out: [q_start[num_seqs]][num_q_heads][head_dim] bf16; lse: [..][num_q_heads]
+ * fp32 or NULL.  q_start: [num_seqs + 1] int32, non-decreasing from 0;
+ * ctx_lens: [num_seqs] int32.  max_q_len: host-side upper bound of n_s (sizes
+ * the grid; longer chunks are clamped to it).  Same size limits as decode.
+ */
+bi_status bi_attn_prefill(const void* q, const int32_t* q_start, const int32_t* ctx_lens,
+                          int32_t num_seqs, int32_t max_q_len,
+                          const void* k_cache, const void* v_cache, int32_t num_pages,
+                          const int32_t* block_table, int32_t max_pages_per_seq,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t page_size, float softmax_scale, void* out, float* lse,
+                          bi_stream_t stream);
+
+/*
+ * Row-wise log_softmax of fp32 logits ([BINR] answer on sampler/trainer
+ * logprob agreement).  out[r, j] = z[r, j] - (max_j z + log sum_j exp(z - max)).
+ * One workgroup per row, one fixed reduction tree whatever `rows`.
+ * logits: [rows, vocab] fp32, row stride ld_in; out: [rows, vocab] fp32, row
+ * stride ld_out (may alias logits when strides are equal). vocab >= 1,
+ * vocab % 4 == 0, strides multiples of 4.
+ */
+bi_status bi_log_softmax(const float* logits, int64_t ld_in, float* out, int64_t ld_out,
+                         int64_t rows, int64_t vocab, bi_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H */

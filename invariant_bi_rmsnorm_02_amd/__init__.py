@@ -1,0 +1,266 @@
+"""Python binding of libbi.so (include/bi.h): argument marshalling only.
+
+Every operation runs in the HIP library.  PyTorch supplies device memory and
+the current HIP stream; the wrappers check devices, dtypes and shapes (so a
+host pointer can never reach a kernel), pass ``data_ptr()`` values and sizes to
+the C entry points of the same name, and raise ``BiError`` on a negative
+status.  There is no fallback: if libbi.so is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbi.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "bi.h")
+
+BI_OK, BI_ERR_INVALID_ARG, BI_ERR_UNSUPPORTED, BI_ERR_WORKSPACE, BI_ERR_HIP = 0, -1, -2, -3, -4
+BI_BF16, BI_F32 = 0, 1
+BI_KV_CHUNK = 256
+
+_c_i32, _c_i64, _c_f32, _c_size, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGNATURES = {
+    "bi_status_str": (ctypes.c_char_p, [_c_i32]),
+    "bi_version": (ctypes.c_char_p, []),
+    "bi_rmsnorm": (_c_i32, [_c_p, _c_i64, _c_p, _c_f32, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
+    "bi_gemm": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i32, _c_i64, _c_i64, _c_i64, _c_p]),
+    "bi_kv_append": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
+    "bi_attn_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "bi_attn_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
+                                _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_size, _c_p]),
+    "bi_attn_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_i32,
+                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p]),
+    "bi_log_softmax": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class BiError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({status_str(status)})")
+        self.status = status
+
+
+def header_symbols() -> list:
+    """Names of the functions include/bi.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|bi_status|size_t)\s+(bi_\w+)\s*\(", text, re.M)))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbi.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(or python invariant_bi_rmsnorm_02_amd/_build.py)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().bi_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != BI_OK:
+        raise BiError(fn, status)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Row stride (elements) of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+# ---------------------------------------------------------------- entry points
+
+def bi_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float, out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    _dev(x, "x", torch.bfloat16)
+    _dev(gamma, "gamma", torch.bfloat16)
+    rows, hidden = x.shape
+    if gamma.shape != (hidden,) or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous [hidden] tensor")
+    if out is None:
+        out = torch.empty((rows, hidden), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", torch.bfloat16)
+    if out.shape != x.shape:
+        raise ValueError("out shape")
+    _check("bi_rmsnorm", lib().bi_rmsnorm(x.data_ptr(), _rows(x, "x"), gamma.data_ptr(), float(eps),
+                                          out.data_ptr(), _rows(out, "out"), rows, hidden, _stream(stream)))
+    return out
+
+
+def bi_gemm(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
+            out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """out[m, n] = sum_k a[m, k] * w[n, k]."""
+    _dev(a, "a", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    m, k = a.shape
+    n, k2 = w.shape
+    if k != k2:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or not out.is_cuda or out.shape != (m, n):
+        raise ValueError("out must be a GPU [m, n] bf16 or fp32 tensor")
+    cdt = BI_F32 if out.dtype == torch.float32 else BI_BF16
+    _check("bi_gemm", lib().bi_gemm(a.data_ptr(), _rows(a, "a"), w.data_ptr(), _rows(w, "w"), out.data_ptr(),
+                                    _rows(out, "out"), cdt, m, n, k, _stream(stream)))
+    return out
+
+
+def alloc_kv_cache(num_pages: int, num_kv_heads: int, head_dim: int, page_size: int = 16,
+                   device="cuda", fill: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """K cache [pages, Hkv, PS, D] and V cache [pages, Hkv, D, PS] (bf16)."""
+    k = torch.empty((num_pages, num_kv_heads, page_size, head_dim), dtype=torch.bfloat16, device=device)
+    v = torch.empty((num_pages, num_kv_heads, head_dim, page_size), dtype=torch.bfloat16, device=device)
+    if fill is not None:
+        k.fill_(fill)
+        v.fill_(fill)
+    return k, v
+
+
+def _cache_geom(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    _dev(k_cache, "k_cache", torch.bfloat16)
+    _dev(v_cache, "v_cache", torch.bfloat16)
+    if k_cache.dim() != 4 or not k_cache.is_contiguous() or not v_cache.is_contiguous():
+        raise ValueError("caches must be contiguous 4-D tensors")
+    pages, hkv, ps, d = k_cache.shape
+    if tuple(v_cache.shape) != (pages, hkv, d, ps):
+        raise ValueError("v_cache must be [pages, Hkv, D, page_size]")
+    return pages, hkv, ps, d
+
+
+def bi_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                 k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
+    pages, hkv, ps, d = _cache_geom(k_cache, v_cache)
+    _dev(k_new, "k_new", torch.bfloat16)
+    _dev(v_new, "v_new", torch.bfloat16)
+    _dev(slot_mapping, "slot_mapping", torch.int32)
+    t = k_new.shape[0]
+    if tuple(k_new.shape) != (t, hkv, d) or v_new.shape != k_new.shape or slot_mapping.shape != (t,):
+        raise ValueError("k_new/v_new must be [T, Hkv, D] and slot_mapping [T]")
+    if not (k_new.is_contiguous() and v_new.is_contiguous() and slot_mapping.is_contiguous()):
+        raise ValueError("inputs must be contiguous")
+    _check("bi_kv_append", lib().bi_kv_append(k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), t,
+                                              k_cache.data_ptr(), v_cache.data_ptr(), pages, hkv, d, ps,
+                                              _stream(stream)))
+
+
+def bi_attn_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int) -> int:
+    return int(lib().bi_attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len))
+
+
+def bi_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                   seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Decode attention; returns (out, lse) (lse is None unless a tensor is given)."""
+    pages, hkv, ps, d = _cache_geom(k_cache, v_cache)
+    _dev(q, "q", torch.bfloat16)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    b, hq, dq = q.shape
+    if dq != d or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, D] tensor")
+    if block_table.dim() != 2 or block_table.shape[0] != b or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [B, max_pages] tensor")
+    if seq_lens.shape != (b,) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out shape")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if lse.shape != (b, hq) or not lse.is_contiguous():
+            raise ValueError("lse must be [B, Hq]")
+    need = bi_attn_decode_workspace_bytes(b, hq, d, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("bi_attn_decode", lib().bi_attn_decode(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), pages, block_table.data_ptr(),
+        block_table.shape[1], seq_lens.data_ptr(), b, int(max_seq_len), hq, hkv, d, ps, float(softmax_scale),
+        out.data_ptr(), lse.data_ptr() if lse is not None else None, workspace.data_ptr(), ws_bytes,
+        _stream(stream)))
+    return out, lse
+
+
+def bi_attn_prefill(q: torch.Tensor, q_start: torch.Tensor, ctx_lens: torch.Tensor, max_q_len: int,
+                    k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                    softmax_scale: float, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, stream=None):
+    """Chunked-prefill attention; returns (out, lse)."""
+    pages, hkv, ps, d = _cache_geom(k_cache, v_cache)
+    _dev(q, "q", torch.bfloat16)
+    _dev(q_start, "q_start", torch.int32)
+    _dev(ctx_lens, "ctx_lens", torch.int32)
+    _dev(block_table, "block_table", torch.int32)
+    t, hq, dq = q.shape
+    s = ctx_lens.shape[0]
+    if dq != d or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [T, Hq, D] tensor")
+    if q_start.shape != (s + 1,) or not q_start.is_contiguous() or not ctx_lens.is_contiguous():
+        raise ValueError("q_start must be [S + 1] and ctx_lens [S]")
+    if block_table.dim() != 2 or block_table.shape[0] != s or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [S, max_pages] tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out shape")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if lse.shape != (t, hq) or not lse.is_contiguous():
+            raise ValueError("lse must be [T, Hq]")
+    _check("bi_attn_prefill", lib().bi_attn_prefill(
+        q.data_ptr(), q_start.data_ptr(), ctx_lens.data_ptr(), s, int(max_q_len), k_cache.data_ptr(),
+        v_cache.data_ptr(), pages, block_table.data_ptr(), block_table.shape[1], hq, hkv, d, ps,
+        float(softmax_scale), out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(stream)))
+    return out, lse
+
+
+def bi_log_softmax(logits: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    _dev(logits, "logits", torch.float32)
+    rows, vocab = logits.shape
+    if out is None:
+        out = torch.empty((rows, vocab), dtype=torch.float32, device=logits.device)
+    _dev(out, "out", torch.float32)
+    if out.shape != logits.shape:
+        raise ValueError("out shape")
+    _check("bi_log_softmax", lib().bi_log_softmax(logits.data_ptr(), _rows(logits, "logits"), out.data_ptr(),
+                                                  _rows(out, "out"), rows, vocab, _stream(stream)))
+    return out

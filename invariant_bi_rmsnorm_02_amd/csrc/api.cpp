@@ -1,0 +1,193 @@
+// C-ABI entry points declared in include/bi.h: host-side validation, then the
+// kernel launchers.  Nothing here allocates, frees or synchronises.  A
+// validation failure returns before anything is enqueued.
+#include "bi.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int log2_exact(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return (1 << l) == v ? l : -1;
+}
+
+bi_status from_hip(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
+
+hipStream_t as_stream(bi_stream_t s) { return static_cast<hipStream_t>(s); }
+
+// Common checks of the attention geometry.
+bi_status check_attn_geom(const void* k_cache, const void* v_cache, int32_t num_pages,
+                          const int32_t* block_table, int32_t max_pages_per_seq,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t page_size, float softmax_scale) {
+  if (!k_cache || !v_cache || !block_table) return BI_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return BI_ERR_INVALID_ARG;
+  if (num_pages <= 0 || max_pages_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0)
+    return BI_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return BI_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads) return BI_ERR_INVALID_ARG;
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return BI_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return BI_ERR_UNSUPPORTED;
+  const int l2 = log2_exact(page_size);
+  if (l2 < 3 || l2 > 8) return BI_ERR_UNSUPPORTED;  // 8 .. 256 tokens, divides the 256-token chunk
+  return BI_OK;
+}
+
+bi::AttnGeom make_geom(const void* k_cache, const void* v_cache, int32_t num_pages,
+                       const int32_t* block_table, int32_t max_pages_per_seq, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size, float softmax_scale) {
+  bi::AttnGeom g;
+  g.k_cache = k_cache;
+  g.v_cache = v_cache;
+  g.num_pages = num_pages;
+  g.block_table = block_table;
+  g.max_pages_per_seq = max_pages_per_seq;
+  g.num_q_heads = num_q_heads;
+  g.num_kv_heads = num_kv_heads;
+  g.head_dim = head_dim;
+  g.log2_page = log2_exact(page_size);
+  // One fp32 rounding of scale * log2(e), done once here for both attention
+  // kernels, so decode and prefill scale scores by the same bits.
+  g.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bi_status_str(bi_status status) {
+  switch (status) {
+    case BI_OK: return "ok";
+    case BI_ERR_INVALID_ARG: return "invalid argument";
+    case BI_ERR_UNSUPPORTED: return "unsupported size";
+    case BI_ERR_WORKSPACE: return "workspace missing or too small";
+    case BI_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* bi_version(void) { return "0.1.0"; }
+
+bi_status bi_rmsnorm(const void* x, int64_t ldx, const void* gamma, float eps, void* y, int64_t ldy,
+                     int64_t rows, int64_t hidden, bi_stream_t stream) {
+  if (rows < 0 || hidden <= 0) return BI_ERR_INVALID_ARG;
+  if (rows == 0) return BI_OK;
+  if (!x || !gamma || !y) return BI_ERR_INVALID_ARG;
+  if (hidden % 8 || hidden > 16384) return BI_ERR_UNSUPPORTED;
+  if (ldx < hidden || ldy < hidden || ldx % 8 || ldy % 8) return BI_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(y)) return BI_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return BI_ERR_INVALID_ARG;
+  if (rows > 0x7fffffff) return BI_ERR_UNSUPPORTED;
+  return from_hip(bi::launch_rmsnorm(x, ldx, gamma, eps, y, ldy, rows, static_cast<int>(hidden),
+                                     as_stream(stream)));
+}
+
+bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc,
+                  int32_t c_dtype, int64_t m, int64_t n, int64_t k, bi_stream_t stream) {
+  if (m < 0 || n < 0 || k <= 0) return BI_ERR_INVALID_ARG;
+  if (c_dtype != BI_BF16 && c_dtype != BI_F32) return BI_ERR_INVALID_ARG;
+  if (m == 0 || n == 0) return BI_OK;
+  if (!a || !w || !c) return BI_ERR_INVALID_ARG;
+  if (k % 32) return BI_ERR_UNSUPPORTED;
+  if (m > (1 << 30) || n > (1 << 30) || k > (1 << 30)) return BI_ERR_UNSUPPORTED;
+  if (lda < k || ldw < k || ldc < n || lda % 8 || ldw % 8 || ldc % 8) return BI_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(c)) return BI_ERR_INVALID_ARG;
+  const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+  if (tiles > 0x7fffffff) return BI_ERR_UNSUPPORTED;
+  return from_hip(bi::launch_gemm(a, lda, w, ldw, c, ldc, c_dtype == BI_F32, m, n, k, as_stream(stream)));
+}
+
+bi_status bi_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                       int32_t num_tokens, void* k_cache, void* v_cache, int32_t num_pages,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size, bi_stream_t stream) {
+  if (num_tokens < 0) return BI_ERR_INVALID_ARG;
+  if (num_tokens == 0) return BI_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return BI_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return BI_ERR_INVALID_ARG;
+  if (num_pages <= 0 || num_kv_heads <= 0) return BI_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return BI_ERR_UNSUPPORTED;
+  const int l2 = log2_exact(page_size);
+  if (l2 < 3 || l2 > 8) return BI_ERR_UNSUPPORTED;
+  if ((int64_t)num_pages * page_size > 0x7fffffff) return BI_ERR_UNSUPPORTED;
+  return from_hip(bi::launch_kv_append(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache,
+                                       num_pages, num_kv_heads, head_dim, page_size, as_stream(stream)));
+}
+
+size_t bi_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                      int32_t max_seq_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  const int64_t chunks = max_seq_len > 0 ? (max_seq_len + BI_KV_CHUNK - 1) / BI_KV_CHUNK : 1;
+  const size_t bytes = (size_t)num_seqs * (size_t)num_q_heads * (size_t)chunks *
+                       (size_t)(head_dim + 4) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+bi_status bi_attn_decode(const void* q, const void* k_cache, const void* v_cache, int32_t num_pages,
+                         const int32_t* block_table, int32_t max_pages_per_seq,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t page_size, float softmax_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, bi_stream_t stream) {
+  if (num_seqs < 0 || max_seq_len < 0) return BI_ERR_INVALID_ARG;
+  if (num_seqs == 0) return BI_OK;
+  bi_status st = check_attn_geom(k_cache, v_cache, num_pages, block_table, max_pages_per_seq,
+                                 num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale);
+  if (st != BI_OK) return st;
+  if (!q || !seq_lens || !out) return BI_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out)) return BI_ERR_INVALID_ARG;
+  if (num_seqs > 65535 || num_kv_heads > 65535) return BI_ERR_UNSUPPORTED;  // grid y/z limits
+  if (!workspace || !aligned16(workspace)) return BI_ERR_WORKSPACE;
+  if (workspace_bytes < bi_attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len))
+    return BI_ERR_WORKSPACE;
+  const bi::AttnGeom g = make_geom(k_cache, v_cache, num_pages, block_table, max_pages_per_seq,
+                                   num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale);
+  return from_hip(bi::launch_attn_decode(q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace,
+                                         as_stream(stream)));
+}
+
+bi_status bi_attn_prefill(const void* q, const int32_t* q_start, const int32_t* ctx_lens,
+                          int32_t num_seqs, int32_t max_q_len, const void* k_cache, const void* v_cache,
+                          int32_t num_pages, const int32_t* block_table, int32_t max_pages_per_seq,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t page_size, float softmax_scale, void* out, float* lse,
+                          bi_stream_t stream) {
+  if (num_seqs < 0 || max_q_len < 0) return BI_ERR_INVALID_ARG;
+  if (num_seqs == 0 || max_q_len == 0) return BI_OK;
+  bi_status st = check_attn_geom(k_cache, v_cache, num_pages, block_table, max_pages_per_seq,
+                                 num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale);
+  if (st != BI_OK) return st;
+  if (!q || !q_start || !ctx_lens || !out) return BI_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out)) return BI_ERR_INVALID_ARG;
+  if (num_seqs > 65535 || num_kv_heads > 65535) return BI_ERR_UNSUPPORTED;
+  if ((int64_t)max_q_len * (num_q_heads / num_kv_heads) > (1 << 30)) return BI_ERR_UNSUPPORTED;
+  const bi::AttnGeom g = make_geom(k_cache, v_cache, num_pages, block_table, max_pages_per_seq,
+                                   num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale);
+  return from_hip(bi::launch_attn_prefill(q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse,
+                                          as_stream(stream)));
+}
+
+bi_status bi_log_softmax(const float* logits, int64_t ld_in, float* out, int64_t ld_out, int64_t rows,
+                         int64_t vocab, bi_stream_t stream) {
+  if (rows < 0 || vocab <= 0) return BI_ERR_INVALID_ARG;
+  if (rows == 0) return BI_OK;
+  if (!logits || !out) return BI_ERR_INVALID_ARG;
+  if (vocab % 4 || vocab > (1 << 30)) return BI_ERR_UNSUPPORTED;
+  if (ld_in < vocab || ld_out < vocab || ld_in % 4 || ld_out % 4) return BI_ERR_INVALID_ARG;
+  if (!aligned16(logits) || !aligned16(out)) return BI_ERR_INVALID_ARG;
+  if (rows > 0x7fffffff) return BI_ERR_UNSUPPORTED;
+  return from_hip(bi::launch_log_softmax(logits, ld_in, out, ld_out, rows, vocab, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Decode attention over the paged KV cache with fixed-size split-KV
+// ("Thinking Machines Lab - Defeating Nondeterminism in LLM Inference", section
+// "3. Batch-Invariant Attention", fig. "Fixed Size Split KV Strategy";
+// "Batch Invariance and Numerical Reproducibility", answer on fixed-size chunks).
+//
+// Kernel 1 (grid: chunk x kv head x sequence, one wavefront each): the partial
+// statistics of one 256-key chunk for the q heads of one kv head, written to
+// the workspace.  A sequence of L tokens has ceil(L / 256) chunks whatever else
+// is in the batch; workgroups past a sequence's last chunk exit at once.
+// Kernel 2 (grid: q head x sequence): the ascending log-sum-exp fold of those
+// partials, normalisation and bf16 output.  No atomics, no cross-workgroup
+// ordering: every value is written by exactly one workgroup.
+#include "attn_chunk.hpp"
+#include "launch.hpp"
+
+namespace bi {
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_decode_partial_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    int num_pages, const int32_t* __restrict__ block_table, int max_pages,
+    const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq, int Hkv, int log2_ps,
+    float scale_log2, float* __restrict__ ws, int max_chunks) {
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int L = min(seq_lens[b], max_seq_len);
+  if (c * kChunk >= L) return;
+  const int G = Hq / Hkv;
+  const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
+  const bool row_ok = n < G;
+
+  u32x4_t qf[D / 32];
+  const uint16_t* qp = q + ((int64_t)b * Hq + h * G + n) * D + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    qf[ks] = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+
+  PagedChunk<D> kv;
+  kv.kc = kc;
+  kv.vc = vc;
+  kv.head = h;
+  kv.num_kv_heads = Hkv;
+  kv.log2_ps = log2_ps;
+  kv.chunk_start = c * kChunk;
+  kv.lim = L;
+  kv.page_reg = load_chunk_pages(block_table + (int64_t)b * max_pages, max_pages, c, log2_ps, L, num_pages);
+
+  Partial<D> p;
+  chunk_partial<D>(kv, qf, min(kChunk, L - c * kChunk), scale_log2, p);
+
+  if (row_ok) {
+    float* rec = ws + (((int64_t)b * Hq + h * G + n) * max_chunks + c) * (D + 4);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = p.o[dt];
+    if (g == 0) {
+      rec[D] = p.m;
+      rec[D + 1] = p.l;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_decode_merge_kernel(
+    const float* __restrict__ ws, const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq,
+    int max_chunks, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int E = D / 64;  // head dims per lane
+  const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int L = min(seq_lens[b], max_seq_len);
+  const int C = L > 0 ? (L + kChunk - 1) / kChunk : 0;
+  const float* rec = ws + ((int64_t)b * Hq + head) * max_chunks * (D + 4);
+
+  float m = -INFINITY, l = 0.0f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  for (int c = 0; c < C; ++c, rec += D + 4) {
+    const MergeCoef k = merge_coef(m, rec[D]);
+    l = merge_val(l, rec[D + 1], k);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = merge_val(acc[e], rec[lane * E + e], k);
+    m = k.m;
+  }
+  uint16_t* op = out + ((int64_t)b * Hq + head) * D + lane * E;
+  if (C > 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) op[e] = static_cast<uint16_t>(f32_to_bf16(finalize_val(acc[e], l)));
+    if (lse != nullptr && lane == 0) lse[(int64_t)b * Hq + head] = finalize_lse(m, l);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) op[e] = 0;
+    if (lse != nullptr && lane == 0) lse[(int64_t)b * Hq + head] = -INFINITY;
+  }
+}
+
+template <int D>
+hipError_t launch(const void* q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
+                  int max_seq_len, void* out, float* lse, void* workspace, hipStream_t stream) {
+  const int max_chunks = (max_seq_len + kChunk - 1) / kChunk;
+  float* ws = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(attn_decode_partial_kernel<D>,
+                     dim3(max_chunks, g.num_kv_heads, num_seqs), dim3(64), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(g.k_cache),
+                     static_cast<const uint16_t*>(g.v_cache), g.num_pages, g.block_table,
+                     g.max_pages_per_seq, seq_lens, max_seq_len, g.num_q_heads, g.num_kv_heads,
+                     g.log2_page, g.scale_log2, ws, max_chunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(64), 0, stream,
+                     ws, seq_lens, max_seq_len, g.num_q_heads, max_chunks,
+                     static_cast<uint16_t*>(out), lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_decode(const void* q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
+                              int max_seq_len, void* out, float* lse, void* workspace,
+                              hipStream_t stream) {
+  if (num_seqs == 0) return hipSuccess;
+  if (max_seq_len <= 0) max_seq_len = 1;  // grid of one empty chunk; merge writes the L <= 0 result
+  return g.head_dim == 64
+             ? launch<64>(q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace, stream)
+             : launch<128>(q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace, stream);
+}
+
+}  // namespace bi

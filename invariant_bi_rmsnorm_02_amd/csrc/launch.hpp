@@ -1,0 +1,46 @@
+// Host-side launchers, one per kernel family.  Arguments have already been
+// validated by the C-ABI layer (api.cpp); launchers only shape grids and
+// enqueue on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bi {
+
+hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* gamma, float eps, void* y,
+                          int64_t ldy, int64_t rows, int hidden, hipStream_t stream);
+
+hipError_t launch_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc,
+                       bool c_f32, int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                            int num_tokens, void* k_cache, void* v_cache, int num_pages,
+                            int num_kv_heads, int head_dim, int page_size, hipStream_t stream);
+
+struct AttnGeom {
+  const void* k_cache;
+  const void* v_cache;
+  int num_pages;
+  const int32_t* block_table;
+  int max_pages_per_seq;
+  int num_q_heads;
+  int num_kv_heads;
+  int head_dim;
+  int log2_page;
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+hipError_t launch_attn_decode(const void* q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
+                              int max_seq_len, void* out, float* lse, void* workspace,
+                              hipStream_t stream);
+
+hipError_t launch_attn_prefill(const void* q, const int32_t* q_start, const int32_t* ctx_lens,
+                               int num_seqs, int max_q_len, const AttnGeom& g, void* out, float* lse,
+                               hipStream_t stream);
+
+hipError_t launch_log_softmax(const float* logits, int64_t ld_in, float* out, int64_t ld_out,
+                              int64_t rows, int64_t vocab, hipStream_t stream);
+
+}  // namespace bi

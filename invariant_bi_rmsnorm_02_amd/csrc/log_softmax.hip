@@ -1,0 +1,82 @@
+// Row-wise log_softmax of fp32 logits ("Batch Invariance and Numerical
+// Reproducibility", answer on sampler and trainer agreeing on logprobs: the
+// logprob of a token must not depend on what else was in the batch).
+//
+// One workgroup per row, one fixed order whatever the number of rows:
+//   thread t walks float4 vectors t, t+1024, ... keeping a running (max, sum)
+//   (the sum is rescaled when the max grows); threads are combined by a
+//   butterfly over each wavefront and the 16 wave results are folded in
+//   ascending wave order.  out = z - (max + ln sum).
+#include "bi_common.hpp"
+#include "launch.hpp"
+
+namespace bi {
+namespace {
+
+constexpr int kLsmThreads = 1024;
+
+struct MaxSum {
+  float m, s;
+};
+
+// Combine two (max, sum-of-exp) pairs.  Commutative bit for bit: both orders
+// compute the same two products and add them.
+__device__ __forceinline__ MaxSum combine(MaxSum a, MaxSum b) {
+  const float m = fmaxf(a.m, b.m);
+  const float ta = a.m == -INFINITY ? 0.0f : a.s * exp2_hw((a.m - m) * kLog2e);
+  const float tb = b.m == -INFINITY ? 0.0f : b.s * exp2_hw((b.m - m) * kLog2e);
+  return MaxSum{m, ta + tb};
+}
+
+__global__ __launch_bounds__(kLsmThreads) void log_softmax_kernel(const float* z, int64_t ld_in,
+                                                                  float* out, int64_t ld_out, int vocab) {
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const f32x4_t* zr = reinterpret_cast<const f32x4_t*>(z + row * ld_in);
+  const int nvec = vocab >> 2;
+
+  MaxSum acc{-INFINITY, 0.0f};
+  for (int i = tid; i < nvec; i += kLsmThreads) {
+    const f32x4_t v = zr[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = v[e];
+      if (x > acc.m) {
+        acc.s = (acc.m == -INFINITY ? 0.0f : acc.s * exp2_hw((acc.m - x) * kLog2e)) + 1.0f;
+        acc.m = x;
+      } else {
+        acc.s = acc.s + exp2_hw((x - acc.m) * kLog2e);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    MaxSum other{shfl_xor(acc.m, o), shfl_xor(acc.s, o)};
+    acc = combine(acc, other);
+  }
+  __shared__ MaxSum part[kLsmThreads / kWave];
+  if ((tid & (kWave - 1)) == 0) part[tid / kWave] = acc;
+  __syncthreads();
+  MaxSum tot = part[0];
+#pragma unroll
+  for (int w = 1; w < kLsmThreads / kWave; ++w) tot = combine(tot, part[w]);
+  const float lse = tot.m + log2_hw(tot.s) * kLn2;
+
+  f32x4_t* orow = reinterpret_cast<f32x4_t*>(out + row * ld_out);
+  for (int i = tid; i < nvec; i += kLsmThreads) {
+    const f32x4_t v = zr[i];
+    orow[i] = f32x4_t{v[0] - lse, v[1] - lse, v[2] - lse, v[3] - lse};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_log_softmax(const float* logits, int64_t ld_in, float* out, int64_t ld_out,
+                              int64_t rows, int64_t vocab, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(log_softmax_kernel, dim3(static_cast<unsigned>(rows)), dim3(kLsmThreads), 0,
+                     stream, logits, ld_in, out, ld_out, static_cast<int>(vocab));
+  return hipGetLastError();
+}
+
+}  // namespace bi

@@ -1,0 +1,65 @@
+"""The C-ABI library on the CPU host: it loads, exports every function that
+include/bi.h declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+
+import pytest
+
+from _helpers import bi, ensure_lib
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ensure_lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = bi.header_symbols()
+    assert set(names) >= {"bi_rmsnorm", "bi_gemm", "bi_kv_append", "bi_attn_decode", "bi_attn_prefill",
+                          "bi_attn_decode_workspace_bytes", "bi_log_softmax", "bi_status_str", "bi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in bi._SIGNATURES, f"{n} has no Python binding"
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(bi.status_str(code), str) and bi.status_str(code)
+    assert bi.status_str(-3) == "workspace missing or too small"
+
+
+def test_host_validation_without_gpu(lib):
+    P = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation first
+    assert lib.bi_rmsnorm(None, 8, None, 1e-6, None, 8, 4, 8, None) == bi.BI_ERR_INVALID_ARG
+    assert lib.bi_rmsnorm(P, 16, P, 1e-6, P, 16, 4, 12, None) == bi.BI_ERR_UNSUPPORTED
+    assert lib.bi_rmsnorm(P, 16, P, 1e-6, P, 16, 0, 16, None) == bi.BI_OK          # empty: no-op
+    assert lib.bi_rmsnorm(P, 8, P, -1.0, P, 16, 4, 16, None) == bi.BI_ERR_INVALID_ARG
+    assert lib.bi_gemm(P, 64, P, 64, P, 64, 0, 4, 4, 48, None) == bi.BI_ERR_UNSUPPORTED   # k % 32
+    assert lib.bi_gemm(P, 64, P, 64, P, 64, 7, 4, 4, 64, None) == bi.BI_ERR_INVALID_ARG   # dtype
+    assert lib.bi_gemm(P, 32, P, 64, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_INVALID_ARG   # lda < k
+    assert lib.bi_gemm(P, 64, P, 64, P, 64, 0, 0, 4, 64, None) == bi.BI_OK
+    # decode: head_dim 96, group size 3, page size 12, missing workspace
+    args = dict(q=P, kc=P, vc=P, pages=8, bt=P, mp=4, lens=P, b=2, msl=64, hq=32, hkv=8, d=128, ps=16)
+
+    def dec(**kw):
+        a = dict(args, **kw)
+        return lib.bi_attn_decode(a["q"], a["kc"], a["vc"], a["pages"], a["bt"], a["mp"], a["lens"], a["b"],
+                                  a["msl"], a["hq"], a["hkv"], a["d"], a["ps"], 0.1, P, None,
+                                  a.get("ws", P), a.get("wsb", 1 << 30), None)
+
+    assert dec(d=96) == bi.BI_ERR_UNSUPPORTED
+    assert dec(hq=24) == bi.BI_ERR_UNSUPPORTED
+    assert dec(hq=30) == bi.BI_ERR_INVALID_ARG
+    assert dec(ps=12) == bi.BI_ERR_UNSUPPORTED
+    assert dec(ws=None) == bi.BI_ERR_WORKSPACE
+    assert dec(wsb=100) == bi.BI_ERR_WORKSPACE
+    assert dec(b=0) == bi.BI_OK
+    assert lib.bi_log_softmax(P, 6, P, 8, 2, 6, None) == bi.BI_ERR_UNSUPPORTED
+    assert lib.bi_kv_append(P, P, P, 3, P, P, 4, 8, 80, 16, None) == bi.BI_ERR_UNSUPPORTED
+
+
+def test_workspace_size_formula(lib):
+    # one (D + 4)-float record per (sequence, q head, 256-token chunk), rounded to 256 bytes
+    n = bi.bi_attn_decode_workspace_bytes(3, 32, 128, 1000)
+    raw = 3 * 32 * 4 * (128 + 4) * 4
+    assert n == (raw + 255) // 256 * 256
+    assert bi.bi_attn_decode_workspace_bytes(1, 1, 64, 256) == 256 * ((68 * 4 + 255) // 256)

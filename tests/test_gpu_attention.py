@@ -1,0 +1,378 @@
+"""KV append, decode and chunked-prefill attention on the GPU.
+
+Parity with the fp64 oracle (which sees each request's logical K/V, never the
+page table), the pages' worked chunk example, closed forms, and the pages'
+property checked bitwise on the GPU: a request's outputs do not depend on the
+batch size, its slot, its physical pages, the co-batched load, or whether its
+tokens are prefilled or decoded.  Unused cache slots are poisoned with NaN so
+any read of a slot past a sequence's end would show up.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from _helpers import (O, assert_bf16_close, assert_bitwise, assert_f32_close, bi, ensure_lib, f64,
+                      log_case)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+NAN = float("nan")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+
+
+class Batch:
+    """Requests over a NaN-poisoned paged cache, filled through bi_kv_append."""
+
+    def __init__(self, requests, seq_lens, hq, hkv, d, base, perm_index=0, page_size=16, extra_pages=3,
+                 kv_fn=W.request_kv, q_kind="q"):
+        self.requests, self.seq_lens = list(requests), list(seq_lens)
+        self.hq, self.hkv, self.d, self.base = hq, hkv, d, base
+        self.pb = W.allocate_pages(self.seq_lens, base, page_size, extra_pages, perm_index)
+        self.kc, self.vc = bi.alloc_kv_cache(self.pb.num_pages, hkv, d, page_size, fill=NAN)
+        self.kv = [kv_fn(r, L, hkv, d, base, device=DEV) for r, L in zip(self.requests, self.seq_lens)]
+        if sum(self.seq_lens):
+            k_all = torch.cat([k for k, _ in self.kv]).contiguous()
+            v_all = torch.cat([v for _, v in self.kv]).contiguous()
+            bi.bi_kv_append(k_all, v_all, self.pb.slot_mapping.to(DEV), self.kc, self.vc)
+        self.q = torch.stack([W.randn_bf16((hq, d), base, q_kind, r, device=DEV) for r in self.requests]) \
+            if self.requests else torch.empty((0, hq, d), dtype=torch.bfloat16, device=DEV)
+        self.bt = self.pb.block_table.to(DEV)
+        self.lens = torch.tensor(self.seq_lens, dtype=torch.int32, device=DEV)
+        self.scale = 1.0 / math.sqrt(d)
+
+    def decode(self, max_seq_len=None, q=None, lens=None, workspace=None):
+        msl = max(self.seq_lens) if max_seq_len is None else max_seq_len
+        qq = self.q if q is None else q
+        lse = torch.empty((qq.shape[0], self.hq), dtype=torch.float32, device=DEV)
+        out, lse = bi.bi_attn_decode(qq, self.kc, self.vc, self.bt, self.lens if lens is None else lens, msl,
+                                     self.scale, lse=lse, workspace=workspace)
+        return out, lse
+
+    def oracle(self, idx):
+        """fp64 decode of the listed batch slots."""
+        q = f64(self.q[idx])
+        ks = [f64(self.kv[i][0]) for i in idx]
+        vs = [f64(self.kv[i][1]) for i in idx]
+        return O.decode_attention(q, ks, vs, self.scale)
+
+
+# ---------------------------------------------------------------- KV append
+
+def test_kv_append_layout_bit_exact():
+    hkv, d, ps, pages, t = 8, 128, 16, 40, 300
+    k_new = W.randn_bf16((t, hkv, d), 1, "k", 0, device=DEV)
+    v_new = W.randn_bf16((t, hkv, d), 1, "v", 0, device=DEV)
+    slots = torch.randperm(pages * ps, generator=torch.Generator().manual_seed(3))[:t].to(torch.int32)
+    slots[7] = -1                                    # padding token: skipped
+    kc, vc = bi.alloc_kv_cache(pages, hkv, d, ps, fill=0.5)
+    bi.bi_kv_append(k_new, v_new, slots.to(DEV), kc, vc)
+    ek = torch.full((pages, hkv, ps, d), 0.5, dtype=torch.bfloat16)
+    ev = torch.full((pages, hkv, d, ps), 0.5, dtype=torch.bfloat16)
+    kh, vh = k_new.cpu(), v_new.cpu()
+    for i in range(t):
+        s = int(slots[i])
+        if s < 0:
+            continue
+        ek[s // ps, :, s % ps, :] = kh[i]
+        ev[s // ps, :, :, s % ps] = vh[i]
+    assert_bitwise(kc.cpu(), ek, "k cache")
+    assert_bitwise(vc.cpu(), ev, "v cache")
+
+
+# ---------------------------------------------------------------- decode: pins
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_decode_tiny_workload(B):
+    # Single-head decode, head_dim 64, KV lengths {1, 255, 256, 1000}; request 0 tracked.
+    lens_cycle = [1000, 1, 255, 256]
+    lens = [lens_cycle[i % 4] for i in range(B)]
+    log_case(f"decode tiny B={B} lens={lens}")
+    bt = Batch(range(B), lens, 1, 1, 64, W.SEED_TINY)
+    out, lse = bt.decode()
+    ro, rl = bt.oracle(list(range(B)))
+    for b in range(B):
+        assert_bf16_close(out[b], ro[b], f"tiny decode request {b} L={lens[b]}")
+    assert_f32_close(lse, rl, "tiny decode lse")
+    one = Batch([0], [1000], 1, 1, 64, W.SEED_TINY)
+    o1, l1 = one.decode()
+    assert_bitwise(out[0], o1[0], "tiny: request 0 vs B=1")
+    assert_bitwise(lse[0], l1[0], "tiny: request 0 lse vs B=1")
+
+
+def test_decode_single_token_exact():
+    bt = Batch(range(4), [1, 1, 1, 1], 32, 8, 128, W.SEED_DECODE)
+    out, lse = bt.decode()
+    for b in range(4):
+        v0 = bt.kv[b][1][0]                          # [Hkv, D]
+        assert_bitwise(out[b], v0.repeat_interleave(4, dim=0), f"L=1 output equals v0 (request {b})")
+    s = torch.einsum("bhd,bhd->bh", f64t(bt.q), f64t(torch.stack([kv[0][0] for kv in bt.kv]).repeat_interleave(4, 1)))
+    assert_f32_close(lse, (s * bt.scale).numpy(), "L=1 lse")
+
+
+def f64t(t):
+    return torch.from_numpy(f64(t))
+
+
+def test_decode_uniform_and_constant_value_closed_forms():
+    L, hkv, hq, d = 700, 2, 8, 128
+    bt = Batch([0], [L], hq, hkv, d, 11)
+    zero_q = torch.zeros_like(bt.q)
+    out, lse = bt.decode(q=zero_q)
+    v = f64(bt.kv[0][1])                             # [L, Hkv, D]
+    want = np.repeat(v.mean(axis=0), hq // hkv, axis=0)
+    assert_bf16_close(out[0], want, "q = 0: mean of V")
+    assert_f32_close(lse, np.full((1, hq), math.log(L)), "q = 0: lse = ln L")
+
+
+def test_decode_chunk_partials_follow_pages_example():
+    # 1,000 keys = 256 + 256 + 256 + 232: four partials are written, a fifth
+    # (allowed by max_seq_len) is not, and each matches the oracle's partial.
+    L, d = 1000, 64
+    bt = Batch([0], [L], 1, 1, d, W.SEED_TINY)
+    msl = 1280
+    need = bi.bi_attn_decode_workspace_bytes(1, 1, d, msl)
+    ws = torch.full((need // 4,), -12345.0, dtype=torch.float32, device=DEV)
+    bt.decode(max_seq_len=msl, workspace=ws)
+    rec = ws[: 5 * (d + 4)].view(5, d + 4).cpu().double().numpy()
+    q = f64(bt.q[0, 0])
+    k, v = f64(bt.kv[0][0][:, 0]), f64(bt.kv[0][1][:, 0])
+    sizes = O.kv_chunks(L)
+    assert sizes == [256, 256, 256, 232]
+    start = 0
+    for c, size in enumerate(sizes):
+        m, l, acc = O.chunk_partial(q, k[start:start + size], v[start:start + size], bt.scale)
+        start += size
+        assert abs(rec[c, d] * math.log(2.0) - m) < 1e-3, f"chunk {c} max"
+        assert abs(rec[c, d + 1] / l - 1.0) < 1e-3, f"chunk {c} sum"
+        assert np.max(np.abs(rec[c, :d] - acc)) / max(np.max(np.abs(acc)), 1e-30) < 1e-2, f"chunk {c} acc"
+    assert np.all(rec[4] == -12345.0), "no fifth partial for a 1,000-token cache"
+
+
+# ---------------------------------------------------------------- decode: parity
+
+@pytest.mark.parametrize("hq,hkv,B,check", [(32, 8, 8, 8), (32, 8, 64, 6), (64, 4, 8, 8), (16, 16, 4, 4),
+                                            (32, 16, 5, 5)])
+def test_decode_parity_workload_shapes(hq, hkv, B, check):
+    base = W.SEED_DECODE if hq == 32 else W.SEED_MOE
+    lens = W.decode_lengths(range(B), base)
+    log_case(f"decode parity hq={hq} hkv={hkv} B={B}")
+    bt = Batch(range(B), lens, hq, hkv, 128, base)
+    out, lse = bt.decode()
+    idx = sorted(set(np.linspace(0, B - 1, check).astype(int).tolist()))
+    ro, rl = bt.oracle(idx)
+    for j, b in enumerate(idx):
+        assert_bf16_close(out[b], ro[j], f"request {b} L={lens[b]}")
+    assert_f32_close(lse[idx], rl, "lse")
+
+
+def test_decode_long_context_parity():
+    L = 32768
+    log_case("decode parity L=32768")
+    bt = Batch([0], [L], 32, 8, 128, W.SEED_LONG)
+    out, lse = bt.decode()
+    ro, rl = bt.oracle([0])
+    assert_bf16_close(out[0], ro[0], "L=32768")
+    assert_f32_close(lse, rl, "L=32768 lse")
+
+
+# ---------------------------------------------------------------- decode: invariance
+
+def test_decode_batch_invariance():
+    hq, hkv, d = 32, 8, 128
+    ref = None
+    for B in (1, 8, 64, 256):
+        for pos, perm in sorted({(0, 0), (B // 2, 1), (B - 1, 2)}):
+            ids = list(range(1, B))
+            ids.insert(pos, 0)
+            lens = W.decode_lengths(ids, W.SEED_DECODE)
+            log_case(f"decode invariance B={B} slot={pos} perm={perm}")
+            bt = Batch(ids, lens, hq, hkv, d, W.SEED_DECODE, perm_index=perm)
+            out, lse = bt.decode(max_seq_len=4096 if B > 1 else None)
+            got = (out[pos].clone(), lse[pos].clone())
+            if ref is None:
+                ref = got
+            assert_bitwise(got[0], ref[0], f"request 0 output at B={B} slot={pos}")
+            assert_bitwise(got[1], ref[1], f"request 0 lse at B={B} slot={pos}")
+
+
+def test_decode_run_to_run():
+    bt = Batch(range(16), W.decode_lengths(range(16), 7), 32, 8, 128, 7)
+    o0, l0 = bt.decode()
+    for _ in range(20):
+        o, l = bt.decode()
+        assert_bitwise(o, o0, "decode repeat")
+        assert_bitwise(l, l0, "decode lse repeat")
+
+
+def test_decode_growing_cache_with_random_co_batch():
+    # One request grows token by token; at every step it is decoded alone and
+    # with a random co-batch.  Its output must match bit for bit, and the
+    # partial of a finished chunk must not change as the cache grows.
+    hq, hkv, d, Lmax = 32, 8, 128, 700
+    track = Batch([0], [Lmax], hq, hkv, d, W.SEED_LONG, kv_fn=W.request_kv_prefix_stable)
+    others_n = 40
+    others_lens = W.decode_lengths(range(1, others_n + 1), W.SEED_LONG, 1, 2000)
+    others = Batch(range(1, others_n + 1), others_lens, hq, hkv, d, W.SEED_LONG, perm_index=5)
+    rng = np.random.default_rng(4)
+    # One joint pool holding the co-batch's pages followed by the tracked request's.
+    kc = torch.cat([others.kc, track.kc]).contiguous()
+    vc = torch.cat([others.vc, track.vc]).contiguous()
+    width = max(others.bt.shape[1], track.bt.shape[1])
+
+    def pad(r):
+        return torch.cat([r, torch.full((width - r.shape[0],), -1, dtype=torch.int32, device=DEV)])
+
+    trow = pad(torch.where(track.bt[0] >= 0, track.bt[0] + others.pb.num_pages, track.bt[0]))
+    orows = [pad(others.bt[i]) for i in range(others_n)]
+    probe = W.randn_bf16((1, hq, d), W.SEED_LONG, "q", 99, device=DEV)
+    probe_ref = None
+    need = bi.bi_attn_decode_workspace_bytes(1, hq, d, Lmax)
+    for L in list(range(1, 40)) + list(range(250, 262)) + list(range(505, 520)) + [600, 699, 700]:
+        q = W.randn_bf16((1, hq, d), W.SEED_LONG, "q", 10_000 + L, device=DEV)
+        lens1 = torch.tensor([L], dtype=torch.int32, device=DEV)
+        o1, l1 = bi.bi_attn_decode(q, track.kc, track.vc, track.bt, lens1, Lmax, track.scale,
+                                   lse=torch.empty((1, hq), dtype=torch.float32, device=DEV))
+        if L >= 256:
+            # chunk-0 partial of a fixed probe query stays bitwise stable as L grows
+            ws = torch.zeros((need // 4,), dtype=torch.float32, device=DEV)
+            bi.bi_attn_decode(probe, track.kc, track.vc, track.bt, lens1, Lmax, track.scale, workspace=ws)
+            rec0 = ws[: d + 4].clone()               # (request 0, q head 0, chunk 0)
+            if probe_ref is None:
+                probe_ref = rec0
+            assert_bitwise(rec0, probe_ref, f"chunk-0 partial at L={L}")
+        k = int(rng.integers(0, others_n + 1))
+        sel = sorted(rng.choice(others_n, size=k, replace=False).tolist())
+        pos = int(rng.integers(0, k + 1))
+        qs = [others.q[i:i + 1] for i in sel]
+        qs.insert(pos, q)
+        lens = [others_lens[i] for i in sel]
+        lens.insert(pos, L)
+        rows = [orows[i] for i in sel]
+        rows.insert(pos, trow)
+        btab = torch.stack(rows).contiguous()
+        qq = torch.cat(qs).contiguous()
+        lse = torch.empty((k + 1, hq), dtype=torch.float32, device=DEV)
+        o, l = bi.bi_attn_decode(qq, kc, vc, btab, torch.tensor(lens, dtype=torch.int32, device=DEV),
+                                 max(lens + [Lmax]), track.scale, lse=lse)
+        assert_bitwise(o[pos], o1[0], f"tracked output at L={L} with {k} co-batched")
+        assert_bitwise(l[pos], l1[0], f"tracked lse at L={L} with {k} co-batched")
+
+
+# ---------------------------------------------------------------- prefill
+
+def _prefill_setup(prefixes, chunk_lens, hq=32, hkv=8, d=128, base=W.SEED_MIXED, perm_index=0):
+    """Sequences whose caches already hold prefix + chunk tokens (chunk appended)."""
+    total = [p + n for p, n in zip(prefixes, chunk_lens)]
+    bt = Batch(range(len(prefixes)), total, hq, hkv, d, base, perm_index=perm_index)
+    qs = [W.randn_bf16((n, hq, d), base, "q", 500 + s, device=DEV) for s, n in enumerate(chunk_lens)]
+    q = torch.cat(qs).contiguous()
+    q_start = torch.tensor([0] + np.cumsum(chunk_lens).tolist(), dtype=torch.int32, device=DEV)
+    ctx = torch.tensor(prefixes, dtype=torch.int32, device=DEV)
+    return bt, q, q_start, ctx
+
+
+def _prefill(bt, q, q_start, ctx, max_q_len):
+    lse = torch.empty((q.shape[0], bt.hq), dtype=torch.float32, device=DEV)
+    return bi.bi_attn_prefill(q, q_start, ctx, max_q_len, bt.kc, bt.vc, bt.bt, bt.scale, lse=lse)
+
+
+@pytest.mark.parametrize("prefixes,chunks", [([0, 200, 700], [64, 300, 512]), ([5000, 1], [512, 17])])
+def test_prefill_parity(prefixes, chunks):
+    log_case(f"prefill parity prefixes={prefixes} chunks={chunks}")
+    bt, q, q_start, ctx = _prefill_setup(prefixes, chunks)
+    out, lse = _prefill(bt, q, q_start, ctx, max(chunks))
+    qs = q_start.cpu().tolist()
+    for s, (p, n) in enumerate(zip(prefixes, chunks)):
+        rows = sorted({0, 1, n // 2, n - 1})
+        k, v = f64(bt.kv[s][0]), f64(bt.kv[s][1])
+        qq = f64(q[qs[s]:qs[s + 1]])
+        for i in rows:
+            ro, rl = O.decode_attention(qq[i][None], [k[:p + i + 1]], [v[:p + i + 1]], bt.scale)
+            assert_bf16_close(out[qs[s] + i], ro[0], f"seq {s} row {i}")
+            assert_f32_close(lse[qs[s] + i], rl[0], f"seq {s} row {i} lse")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 4, 128), (1, 1, 64)])
+def test_prefill_equals_token_by_token_decode(hq, hkv, d):
+    prefixes, chunks = [0, 250, 1100], [300, 512, 40]
+    log_case(f"prefill == decode hq={hq} hkv={hkv} d={d}")
+    bt, q, q_start, ctx = _prefill_setup(prefixes, chunks, hq, hkv, d)
+    out, lse = _prefill(bt, q, q_start, ctx, max(chunks))
+    qs = q_start.cpu().tolist()
+    for s, (p, n) in enumerate(zip(prefixes, chunks)):
+        # decode query i of the chunk with seq_len p + i + 1, all as one batch
+        lens = torch.arange(p + 1, p + n + 1, dtype=torch.int32, device=DEV)
+        btab = bt.bt[s:s + 1].repeat(n, 1).contiguous()
+        qd = q[qs[s]:qs[s + 1]].contiguous()
+        lsed = torch.empty((n, hq), dtype=torch.float32, device=DEV)
+        od, ld = bi.bi_attn_decode(qd, bt.kc, bt.vc, btab, lens, p + n, bt.scale, lse=lsed)
+        assert_bitwise(out[qs[s]:qs[s + 1]], od, f"seq {s}: prefill rows vs decode")
+        assert_bitwise(lse[qs[s]:qs[s + 1]], ld, f"seq {s}: prefill lse vs decode")
+    # and literally one token at a time for the first rows of sequence 1
+    s, p = 1, prefixes[1]
+    for i in (0, 1, 255, 256):
+        od, ld = bi.bi_attn_decode(q[qs[s] + i][None].contiguous(), bt.kc, bt.vc, bt.bt[s:s + 1].contiguous(),
+                                   torch.tensor([p + i + 1], dtype=torch.int32, device=DEV), p + i + 1,
+                                   bt.scale, lse=torch.empty((1, hq), dtype=torch.float32, device=DEV))
+        assert_bitwise(out[qs[s] + i], od[0], f"row {i}: prefill vs single decode")
+
+
+def test_prefill_co_batch_invariance():
+    prefixes, chunks = [300, 900, 0, 4000], [512, 100, 256, 333]
+    bt, q, q_start, ctx = _prefill_setup(prefixes, chunks)
+    out, lse = _prefill(bt, q, q_start, ctx, max(chunks))
+    qs = q_start.cpu().tolist()
+    # sequence 1 alone (request 1's K/V and queries) on a different page permutation
+    one_q = q[qs[1]:qs[2]].contiguous()
+    one = Batch([1], [prefixes[1] + chunks[1]], 32, 8, 128, W.SEED_MIXED, perm_index=9)
+    o1, l1 = bi.bi_attn_prefill(one_q, torch.tensor([0, chunks[1]], dtype=torch.int32, device=DEV),
+                                torch.tensor([prefixes[1]], dtype=torch.int32, device=DEV), 512,
+                                one.kc, one.vc, one.bt, one.scale,
+                                lse=torch.empty((chunks[1], 32), dtype=torch.float32, device=DEV))
+    assert_bitwise(out[qs[1]:qs[2]], o1, "sequence 1 prefill alone vs co-batched")
+    assert_bitwise(lse[qs[1]:qs[2]], l1, "sequence 1 prefill lse alone vs co-batched")
+
+
+# ---------------------------------------------------------------- edges and errors
+
+def test_decode_edges():
+    bt = Batch(range(3), [5, 300, 17], 32, 8, 128, 21)
+    lens = torch.tensor([0, 300, 17], dtype=torch.int32, device=DEV)
+    out, lse = bt.decode(lens=lens)
+    assert torch.all(out[0].view(torch.int16) == 0)
+    assert torch.all(torch.isneginf(lse[0]))
+    ref_o, ref_l = bt.decode()
+    assert_bitwise(out[1:], ref_o[1:], "other requests unaffected by an empty one")
+    # max_seq_len below a length clamps that length (no out-of-range chunk)
+    o2, _ = bt.decode(max_seq_len=256, lens=torch.tensor([5, 256, 17], dtype=torch.int32, device=DEV))
+    o3, _ = bt.decode(max_seq_len=256, lens=torch.tensor([5, 300, 17], dtype=torch.int32, device=DEV))
+    assert_bitwise(o3, o2, "seq_len clamped to max_seq_len")
+    # a block table entry outside the pool reads as zeros instead of faulting
+    btab = bt.bt.clone()
+    btab[1, 3] = 10 ** 6
+    o4, _ = bi.bi_attn_decode(bt.q, bt.kc, bt.vc, btab, bt.lens, 300, bt.scale)
+    assert torch.isfinite(o4.float()).all()
+
+
+def test_attention_errors():
+    bt = Batch([0], [10], 32, 8, 128, 22)
+    with pytest.raises(bi.BiError) as e:
+        bi.bi_attn_decode(bt.q, bt.kc, bt.vc, bt.bt, bt.lens, 10, bt.scale,
+                          workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == bi.BI_ERR_WORKSPACE
+    q3 = torch.zeros((1, 24, 128), dtype=torch.bfloat16, device=DEV)   # group size 3
+    with pytest.raises(bi.BiError) as e:
+        bi.bi_attn_decode(q3, bt.kc, bt.vc, bt.bt, bt.lens, 10, bt.scale)
+    assert e.value.status in (bi.BI_ERR_UNSUPPORTED, bi.BI_ERR_INVALID_ARG)
+    kc, vc = bi.alloc_kv_cache(4, 8, 96, 16)
+    with pytest.raises(bi.BiError) as e:
+        bi.bi_attn_decode(torch.zeros((1, 32, 96), dtype=torch.bfloat16, device=DEV), kc, vc, bt.bt, bt.lens,
+                          10, bt.scale)
+    assert e.value.status == bi.BI_ERR_UNSUPPORTED

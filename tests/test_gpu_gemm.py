@@ -1,0 +1,159 @@
+"""bi_gemm on the GPU: exact integer pins, parity with the fp64 oracle at the
+workload shapes, and the pages' property (row m's bits do not depend on the
+other rows of A, on M, or on the row's position)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from _helpers import O, assert_bf16_close, assert_bitwise, assert_f32_close, bi, ensure_lib, f64, log_case
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+
+
+def _int_bf16(shape, seed, lo=-4, hi=4):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(lo, hi + 1, shape, generator=g).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1024, 512), (8, 1024, 512), (130, 257, 4096), (300, 136, 96),
+                                   (17, 40, 32)])
+def test_gemm_integer_exact(m, n, k):
+    # Products and partial sums are integers below 2^24, so fp32 accumulation is
+    # exact in any order; the bf16 result must be the oracle rounded once (RNE).
+    log_case(f"gemm integer exact m={m} n={n} k={k}")
+    a, w = _int_bf16((m, k), 1), _int_bf16((n, k), 2)
+    ref = O.gemm(f64(a), f64(w))
+    c16 = bi.bi_gemm(a.to(DEV), w.to(DEV))
+    c32 = bi.bi_gemm(a.to(DEV), w.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = torch.from_numpy(O.f64_to_bf16_bits(ref).view(np.int16))
+    assert torch.equal(c16.view(torch.int16).cpu(), want)
+    assert np.array_equal(f64(c32), ref)
+
+
+def test_gemm_identity_and_selector():
+    k = 256
+    a = W.randn_bf16((37, k), 0, "x", 7)
+    eye = torch.eye(k, dtype=torch.bfloat16)
+    c = bi.bi_gemm(a.to(DEV), eye.to(DEV))
+    assert_bitwise(c.cpu(), a, "A @ I")
+    w = W.randn_bf16((100, k), 0, "w", 8)
+    sel = torch.zeros((2, k), dtype=torch.bfloat16)
+    sel[0, 5] = 1
+    sel[1, 200] = 1
+    cs = bi.bi_gemm(sel.to(DEV), w.to(DEV)).cpu()
+    assert_bitwise(cs[0], w[:, 5].contiguous(), "selector row 0")
+    assert_bitwise(cs[1], w[:, 200].contiguous(), "selector row 1")
+
+
+SHAPES = [
+    ("tiny 512->1024", 512, 1024, W.SEED_TINY, 1.0),
+    ("qkv 4096->6144", 4096, 6144, W.SEED_DECODE, 0.02),
+    ("up 4096->12288", 4096, 12288, W.SEED_DECODE, 0.02),
+    ("down 12288->4096", 12288, 4096, W.SEED_DECODE, 0.02),
+]
+
+
+@pytest.mark.parametrize("name,k,n,base,wstd", SHAPES)
+@pytest.mark.parametrize("m", [1, 3, 8, 64, 256])
+def test_gemm_parity_workload_shapes(name, k, n, base, wstd, m):
+    if name.startswith("tiny") and m > 8:
+        pytest.skip("tiny workload uses B in {1, 3, 8}")
+    log_case(f"gemm parity {name} m={m}")
+    w = W.randn_bf16((n, k), base, "w", W.WEIGHTS + k, std=wstd, device=DEV)
+    a = W.rows_for_requests(range(m), k, base, device=DEV)
+    c = bi.bi_gemm(a, w)
+    torch.cuda.synchronize()
+    ref = O.gemm(f64(a), f64(w))
+    assert_bf16_close(c, ref, f"{name} m={m}")
+
+
+def test_gemm_parity_large_m_sampled_rows():
+    # The mixed prefill+decode batch: M = 2048 + decode rows; check sampled rows.
+    m, k, n = 2300, 4096, 6144
+    log_case(f"gemm parity large m={m}")
+    w = W.randn_bf16((n, k), W.SEED_MIXED, "w", W.WEIGHTS, std=0.02, device=DEV)
+    a = W.rows_for_requests(range(m), k, W.SEED_MIXED, device=DEV)
+    c = bi.bi_gemm(a, w)
+    rows = [0, 1, 127, 128, 1000, 2047, 2048, 2299]
+    ref = O.gemm(f64(a[rows]), f64(w))
+    assert_bf16_close(c[rows], ref, "large m sampled rows")
+
+
+def test_gemm_ragged_tails():
+    for (m, n, k) in [(129, 131, 96), (5, 1000, 160), (255, 8, 32), (1, 136, 4128)]:
+        log_case(f"gemm ragged m={m} n={n} k={k}")
+        a = W.randn_bf16((m, k), 9, "x", m)
+        w = W.randn_bf16((n, k), 9, "w", n, std=0.05)
+        c = bi.bi_gemm(a.to(DEV), w.to(DEV))
+        c32 = bi.bi_gemm(a.to(DEV), w.to(DEV), out_dtype=torch.float32)
+        ref = O.gemm(f64(a), f64(w))
+        assert_bf16_close(c, ref, f"ragged {m}x{n}x{k}")
+        assert_f32_close(c32, ref, f"ragged fp32 {m}x{n}x{k}")
+
+
+def test_gemm_strided_operands():
+    a_full = W.randn_bf16((40, 256 + 64), 9, "x", 1).to(DEV)
+    w_full = W.randn_bf16((72, 256 + 32), 9, "w", 1).to(DEV)
+    out_full = torch.zeros((40, 72 + 24), dtype=torch.bfloat16, device=DEV)
+    a, w, out = a_full[:, :256], w_full[:, :256], out_full[:, :72]
+    bi.bi_gemm(a, w, out=out)
+    ref = O.gemm(f64(a), f64(w))
+    assert_bf16_close(out, ref, "strided")
+    assert torch.all(out_full[:, 72:] == 0)
+
+
+@pytest.mark.parametrize("k,n", [(512, 1024), (4096, 6144), (12288, 4096)])
+def test_gemm_batch_invariance(k, n):
+    w = W.randn_bf16((n, k), W.SEED_DECODE, "w", W.WEIGHTS + k, std=0.02, device=DEV)
+    ref = None
+    for m in (1, 3, 8, 64, 256, 2051):
+        for pos in sorted({0, m // 2, m - 1}):
+            ids = list(range(1, m))
+            ids.insert(pos, 0)
+            a = W.rows_for_requests(ids, k, W.SEED_DECODE, device=DEV)
+            row = bi.bi_gemm(a, w)[pos].clone()
+            if ref is None:
+                ref = row
+            assert_bitwise(row, ref, f"gemm k={k} n={n}: request 0 at M={m} slot={pos}")
+
+
+def test_gemm_fp32_lm_head_invariance():
+    # lm_head-shaped fp32 output on a vocab slice; token 0's logits at T in {1, 64, 512}.
+    k, n = 4096, 151936 // 8
+    w = W.randn_bf16((n, k), W.SEED_MOE, "w", W.WEIGHTS, std=0.02, device=DEV)
+    ref = None
+    for t in (1, 64, 512):
+        ids = list(range(1, t))
+        ids.insert(t // 3, 0)
+        a = W.rows_for_requests(ids, k, W.SEED_MOE, device=DEV)
+        row = bi.bi_gemm(a, w, out_dtype=torch.float32)[t // 3].clone()
+        if ref is None:
+            ref = row
+            assert_f32_close(row[None], O.gemm(f64(a[t // 3:t // 3 + 1]), f64(w)), "lm_head slice")
+        assert_bitwise(row, ref, f"lm_head token 0 at T={t}")
+
+
+def test_gemm_run_to_run():
+    a = W.rows_for_requests(range(64), 4096, 2, device=DEV)
+    w = W.randn_bf16((6144, 4096), 2, "w", 1, std=0.02, device=DEV)
+    c0 = bi.bi_gemm(a, w)
+    for _ in range(10):
+        assert_bitwise(bi.bi_gemm(a, w), c0, "gemm repeat")
+
+
+def test_gemm_errors():
+    a = torch.ones((4, 48), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(bi.BiError) as e:
+        bi.bi_gemm(a, a)
+    assert e.value.status == bi.BI_ERR_UNSUPPORTED
+    out = bi.bi_gemm(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV),
+                     torch.ones((8, 64), dtype=torch.bfloat16, device=DEV))
+    assert out.shape == (0, 8)

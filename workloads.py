@@ -32,14 +32,18 @@ def seed_of(base: int, kind: str, index: int) -> int:
     return (int(base) * 1_000_003 + _KINDS[kind] * 65_537 + int(index) * 7_919) % (2 ** 62)
 
 
-def gen(base: int, kind: str, index: int) -> torch.Generator:
-    g = torch.Generator()
+def gen(base: int, kind: str, index: int, device="cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
     g.manual_seed(seed_of(base, kind, index))
     return g
 
 
-def randn_bf16(shape, base: int, kind: str, index: int, std: float = 1.0, mean: float = 0.0) -> torch.Tensor:
-    x = torch.randn(*shape, generator=gen(base, kind, index), dtype=torch.float32)
+def randn_bf16(shape, base: int, kind: str, index: int, std: float = 1.0, mean: float = 0.0,
+               device="cpu") -> torch.Tensor:
+    """N(mean, std^2) drawn in fp32 then rounded to bf16.  Values depend on the
+    device that draws them (CPU and GPU generators differ); a test draws once
+    and hands the same bytes to the library and to the oracle."""
+    x = torch.randn(*shape, generator=gen(base, kind, index, device), dtype=torch.float32, device=device)
     if std != 1.0:
         x = x * std
     if mean != 0.0:
@@ -58,10 +62,10 @@ def rand_int(lo: int, hi: int, base: int, kind: str, index: int) -> int:
 
 
 def rows_for_requests(requests: Sequence[int], width: int, base: int, kind: str = "x",
-                      std: float = 1.0) -> torch.Tensor:
+                      std: float = 1.0, device="cpu") -> torch.Tensor:
     """Stack one seeded [width] bf16 row per request id."""
-    return torch.stack([randn_bf16((width,), base, kind, r, std=std) for r in requests]) \
-        if len(requests) else torch.empty((0, width), dtype=torch.bfloat16)
+    return torch.stack([randn_bf16((width,), base, kind, r, std=std, device=device) for r in requests]) \
+        if len(requests) else torch.empty((0, width), dtype=torch.bfloat16, device=device)
 
 
 # ---------------------------------------------------------------- paged KV cache
@@ -102,27 +106,26 @@ def allocate_pages(seq_lens: Sequence[int], base: int, page_size: int = PAGE,
     return PagedBatch(list(seq_lens), bt, total, sm, page_size)
 
 
-def request_kv(request: int, length: int, num_kv_heads: int, head_dim: int, base: int):
-    """Request ``request``'s logical K and V [length, Hkv, D] (bf16).  Token t of a
-    request is the same at every length (drawn once for the longest prefix is not
-    needed: each token row is seeded by (request, token))."""
-    k = randn_bf16((length, num_kv_heads, head_dim), base, "k", request)
-    v = randn_bf16((length, num_kv_heads, head_dim), base, "v", request)
+def request_kv(request: int, length: int, num_kv_heads: int, head_dim: int, base: int, device="cpu"):
+    """Request ``request``'s logical K and V [length, Hkv, D] (bf16), seeded by
+    (workload, request id)."""
+    k = randn_bf16((length, num_kv_heads, head_dim), base, "k", request, device=device)
+    v = randn_bf16((length, num_kv_heads, head_dim), base, "v", request, device=device)
     return k, v
 
 
 def request_kv_prefix_stable(request: int, length: int, num_kv_heads: int, head_dim: int,
-                             base: int, block: int = 256):
+                             base: int, block: int = 256, device="cpu"):
     """Like ``request_kv`` but token rows are drawn per 256-token block, so the
     first L tokens are identical for every total length >= L (growing caches)."""
     ks, vs = [], []
     for blk in range((length + block - 1) // block):
         n = min(block, length - blk * block)
         idx = request * 4096 + blk
-        ks.append(randn_bf16((block, num_kv_heads, head_dim), base, "k", idx)[:n])
-        vs.append(randn_bf16((block, num_kv_heads, head_dim), base, "v", idx)[:n])
+        ks.append(randn_bf16((block, num_kv_heads, head_dim), base, "k", idx, device=device)[:n])
+        vs.append(randn_bf16((block, num_kv_heads, head_dim), base, "v", idx, device=device)[:n])
     if not ks:
-        z = torch.empty((0, num_kv_heads, head_dim), dtype=torch.bfloat16)
+        z = torch.empty((0, num_kv_heads, head_dim), dtype=torch.bfloat16, device=device)
         return z, z.clone()
     return torch.cat(ks), torch.cat(vs)
 
