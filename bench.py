@@ -1,0 +1,439 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-invariant hot path on one MI355X.
+
+Timed step: one Qwen3-8B-shaped decode step over B = 256 requests (hidden 4096,
+GQA 32/8 heads, head_dim 128, paged KV with 16-token pages, per-request KV
+lengths uniform in [1, 4096]):
+    RMSNorm -> fused QKV GEMM 4096->6144 -> KV append -> decode attention
+    -> RMSNorm -> MLP GEMMs 4096->12288->4096
+every call going through the C-ABI library.  Inputs are synthetic (seeded
+N(0,1) activations/KV, N(0,0.02) weights: no checkpoints are available) and
+resident in HBM before timing starts.
+
+Printed: one JSON line.  `value` = algorithmic bytes moved by the step /
+step time (GB/s; every kernel of the step is HBM-bound at B <= 256).
+`roofline` is for the dominant kernel (decode attention: chunk kernel plus
+merge kernel, timed together with HIP events on the launch stream).
+`kernels` holds per-kernel times at every workload shape (B = 1..256,
+the M ~ 2300 GEMMs and chunked prefill of the mixed batch, the 235B-shaped
+lm_head + log_softmax and decode attention) as GB/s or TFLOP/s and fraction
+of roofline.  `cpu_baseline` times the fp64 oracle on the host on a sample of
+the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "batch-invariant GEMM/attn/RMSNorm TFLOP/s & GB/s, % roofline, B=1..256"
+EPS = 1e-6
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--kernels", choices=["all", "step", "none"], default="all",
+                    help="per-kernel table: every workload shape, only the step's B sweep, or none")
+    ap.add_argument("--cpu-sample", type=int, default=64, help="requests of the step the oracle computes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--reps", type=int, default=20)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- algorithmic work
+
+def bytes_rmsnorm(r, h):
+    return 4 * r * h + 2 * h
+
+
+def bytes_gemm(m, n, k, out_bytes=2):
+    return 2 * (m * k + n * k) + out_bytes * m * n
+
+
+def flops_gemm(m, n, k):
+    return 2 * m * n * k
+
+
+def bytes_append(t, hkv, d):
+    return 8 * t * hkv * d
+
+
+def bytes_decode(lens, hq, hkv, d):
+    return 4 * hkv * d * sum(lens) + 4 * len(lens) * hq * d
+
+
+def flops_decode(lens, hq, d):
+    return 4 * hq * d * sum(lens)
+
+
+def flops_prefill(prefixes, chunks, hq, d):
+    keys = sum(sum(p + i + 1 for i in range(n)) for p, n in zip(prefixes, chunks))
+    return 4 * hq * d * keys
+
+
+def bytes_prefill(prefixes, chunks, hq, hkv, d):
+    return sum(4 * hkv * d * (p + n) + 4 * n * hq * d for p, n in zip(prefixes, chunks))
+
+
+# ---------------------------------------------------------------- timing helpers
+
+def time_fn(torch, fn, reps, warmup=3):
+    """Median / p10 / p90 microseconds of fn() measured with HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return ts[len(ts) // 2], ts[len(ts) // 10], ts[(len(ts) * 9) // 10]
+
+
+def entry(name, us, nbytes=None, flops=None, bound="hbm", extra=None):
+    e = {"kernel": name, "us": round(us[0], 2), "us_p10": round(us[1], 2), "us_p90": round(us[2], 2)}
+    if nbytes is not None:
+        e["GBps"] = round(nbytes / (us[0] * 1e-6) / 1e9, 1)
+    if flops is not None:
+        e["TFLOPs"] = round(flops / (us[0] * 1e-6) / 1e12, 2)
+    t_roof = max((nbytes or 0) / (HBM_PEAK_GBS * 1e9), (flops or 0) / (BF16_PEAK_TFLOPS * 1e12))
+    e["bound"] = "mfma" if (flops or 0) / (BF16_PEAK_TFLOPS * 1e12) > (nbytes or 0) / (HBM_PEAK_GBS * 1e9) else "hbm"
+    e["frac_roofline"] = round(t_roof / (us[0] * 1e-6), 4)
+    if extra:
+        e.update(extra)
+    return e
+
+
+# ---------------------------------------------------------------- the decode step
+
+class DecodeStep:
+    """Qwen3-8B-shaped decode step over the first B requests of the workload."""
+
+    HQ, HKV, D, H, QKV, MLP = 32, 8, 128, 4096, 6144, 12288
+
+    def __init__(self, torch, bi, W, B, dev="cuda"):
+        self.torch, self.bi, self.B = torch, bi, B
+        base = W.SEED_DECODE
+        ids = list(range(B))
+        self.lens = W.decode_lengths(ids, base)              # cache length incl. the step's new token
+        pb = W.allocate_pages(self.lens, base)
+        self.kc, self.vc = bi.alloc_kv_cache(pb.num_pages, self.HKV, self.D, 16, dev, fill=0.0)
+        # Cache contents: every request's K/V, appended through the library.
+        for r0 in range(0, B, 32):
+            part = ids[r0:r0 + 32]
+            kv = [W.request_kv(r, self.lens[r], self.HKV, self.D, base, device=dev) for r in part]
+            lo = sum(self.lens[:r0])
+            hi = lo + sum(self.lens[r] for r in part)
+            bi.bi_kv_append(torch.cat([k for k, _ in kv]), torch.cat([v for _, v in kv]),
+                            pb.slot_mapping[lo:hi].to(dev), self.kc, self.vc)
+        self.kv_host = None
+        self.bt = pb.block_table.to(dev)
+        self.lens_t = torch.tensor(self.lens, dtype=torch.int32, device=dev)
+        starts = [0]
+        for L in self.lens[:-1]:
+            starts.append(starts[-1] + L)
+        # slot of each request's newest token (position L - 1)
+        self.new_slots = pb.slot_mapping[torch.tensor([s + L - 1 for s, L in zip(starts, self.lens)])].to(dev)
+        self.max_len = 4096
+        self.x = W.rows_for_requests(ids, self.H, base, device=dev)
+        self.g1 = W.randn_bf16((self.H,), base, "gamma", W.WEIGHTS, std=0.1, mean=1.0, device=dev)
+        self.g2 = W.randn_bf16((self.H,), base, "gamma", W.WEIGHTS + 1, std=0.1, mean=1.0, device=dev)
+        self.w_qkv = W.randn_bf16((self.QKV, self.H), base, "w", W.WEIGHTS + 1, std=0.02, device=dev)
+        self.w_up = W.randn_bf16((self.MLP, self.H), base, "w", W.WEIGHTS + 2, std=0.02, device=dev)
+        self.w_down = W.randn_bf16((self.H, self.MLP), base, "w", W.WEIGHTS + 3, std=0.02, device=dev)
+        e = dict(dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty((B, self.H), **e)
+        self.qkv = torch.empty((B, self.QKV), **e)
+        self.attn = torch.empty((B, self.HQ, self.D), **e)
+        self.h2 = torch.empty((B, self.H), **e)
+        self.up = torch.empty((B, self.MLP), **e)
+        self.down = torch.empty((B, self.H), **e)
+        self.lse = torch.empty((B, self.HQ), dtype=torch.float32, device=dev)
+        nws = bi.bi_attn_decode_workspace_bytes(B, self.HQ, self.D, self.max_len)
+        self.ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+        self.q = self.qkv[:, :4096].view(B, self.HQ, self.D)
+        self.k = self.qkv[:, 4096:5120].view(B, self.HKV, self.D)
+        self.v = self.qkv[:, 5120:].view(B, self.HKV, self.D)
+        self.scale = 1.0 / math.sqrt(self.D)
+
+    def rmsnorm1(self):
+        self.bi.bi_rmsnorm(self.x, self.g1, EPS, out=self.h)
+
+    def gemm_qkv(self):
+        self.bi.bi_gemm(self.h, self.w_qkv, out=self.qkv)
+
+    def append(self):
+        self.bi.bi_kv_append(self.k, self.v, self.new_slots, self.kc, self.vc)
+
+    def attend(self):
+        self.bi.bi_attn_decode(self.q, self.kc, self.vc, self.bt, self.lens_t, self.max_len, self.scale,
+                               out=self.attn, lse=self.lse, workspace=self.ws)
+
+    def rmsnorm2(self):
+        self.bi.bi_rmsnorm(self.attn.view(self.B, self.H), self.g2, EPS, out=self.h2)
+
+    def gemm_up(self):
+        self.bi.bi_gemm(self.h2, self.w_up, out=self.up)
+
+    def gemm_down(self):
+        self.bi.bi_gemm(self.up, self.w_down, out=self.down)
+
+    def step(self, ev=None):
+        self.rmsnorm1()
+        self.gemm_qkv()
+        self.append()
+        if ev is not None:
+            ev[0].record()
+        self.attend()
+        if ev is not None:
+            ev[1].record()
+        self.rmsnorm2()
+        self.gemm_up()
+        self.gemm_down()
+
+    def step_bytes(self):
+        B = self.B
+        return (2 * bytes_rmsnorm(B, self.H) + bytes_gemm(B, self.QKV, self.H) + bytes_append(B, self.HKV, self.D)
+                + bytes_decode(self.lens, self.HQ, self.HKV, self.D) + bytes_gemm(B, self.MLP, self.H)
+                + bytes_gemm(B, self.H, self.MLP))
+
+    def step_flops(self):
+        B = self.B
+        return (flops_gemm(B, self.QKV, self.H) + flops_gemm(B, self.MLP, self.H) + flops_gemm(B, self.H, self.MLP)
+                + flops_decode(self.lens, self.HQ, self.D))
+
+
+# ---------------------------------------------------------------- per-kernel table
+
+def kernel_table(torch, bi, W, step, reps, everything):
+    out = []
+    dev = "cuda"
+    # Rotating weight copies so the 256 MB Infinity Cache cannot serve repeated GEMM launches.
+    def copies(w, total=768 << 20):
+        n = max(1, min(16, total // (w.numel() * 2)))
+        return [w] + [w.clone() for _ in range(n - 1)]
+    wq, wu, wd = copies(step.w_qkv), copies(step.w_up), copies(step.w_down)
+    for B in (1, 8, 64, 256):
+        if B > step.B:
+            continue
+        lens = step.lens[:B]
+        x, h, qkv = step.x[:B], step.h[:B], step.qkv[:B]
+        up, h2, down = step.up[:B], step.h2[:B], step.down[:B]
+        tag = {"B": B}
+        us = time_fn(torch, lambda i=0: bi.bi_rmsnorm(x, step.g1, EPS, out=h), reps)
+        out.append(entry("rmsnorm [B,4096]", us, bytes_rmsnorm(B, 4096), extra=tag))
+        us = time_fn(torch, lambda i=0: bi.bi_gemm(h, wq[i % len(wq)], out=qkv), reps)
+        out.append(entry("gemm qkv 4096->6144", us, bytes_gemm(B, 6144, 4096), flops_gemm(B, 6144, 4096), extra=tag))
+        us = time_fn(torch, lambda i=0: bi.bi_gemm(h2, wu[i % len(wu)], out=up), reps)
+        out.append(entry("gemm up 4096->12288", us, bytes_gemm(B, 12288, 4096), flops_gemm(B, 12288, 4096), extra=tag))
+        us = time_fn(torch, lambda i=0: bi.bi_gemm(up, wd[i % len(wd)], out=down), reps)
+        out.append(entry("gemm down 12288->4096", us, bytes_gemm(B, 4096, 12288), flops_gemm(B, 4096, 12288),
+                         extra=tag))
+        q = step.q[:B]
+        attn, lse = step.attn[:B], step.lse[:B]
+        bt, lt = step.bt[:B], step.lens_t[:B]
+        us = time_fn(torch, lambda i=0: bi.bi_attn_decode(q, step.kc, step.vc, bt, lt, 4096, step.scale, out=attn,
+                                                           lse=lse, workspace=step.ws), reps)
+        out.append(entry("attn decode 32/8 D128", us, bytes_decode(lens, 32, 8, 128), flops_decode(lens, 32, 128),
+                         extra=dict(tag, sum_L=sum(lens))))
+    del wq, wu, wd
+    if not everything:
+        return out
+    torch.cuda.empty_cache()
+    # Mixed prefill + decode batch: GEMMs at M = 2048 + decode rows (MFMA-bound), chunked prefill.
+    M = 2300
+    a = W.rows_for_requests(range(M), 4096, W.SEED_MIXED, device=dev)
+    a2 = W.rows_for_requests(range(M), 12288, W.SEED_MIXED, device=dev)
+    for name, src, w in (("gemm qkv 4096->6144", a, step.w_qkv), ("gemm up 4096->12288", a, step.w_up),
+                         ("gemm down 12288->4096", a2, step.w_down)):
+        n, k = w.shape
+        c = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
+        us = time_fn(torch, lambda i=0: bi.bi_gemm(src, w, out=c), max(5, reps // 2))
+        out.append(entry(name, us, bytes_gemm(M, n, k), flops_gemm(M, n, k), extra={"M": M}))
+    del a, a2
+    xr = W.rows_for_requests(range(M), 4096, W.SEED_MIXED, device=dev)
+    yr = torch.empty_like(xr)
+    us = time_fn(torch, lambda i=0: bi.bi_rmsnorm(xr, step.g1, EPS, out=yr), reps)
+    out.append(entry("rmsnorm [2300,4096]", us, bytes_rmsnorm(M, 4096), extra={"rows": M}))
+    del xr, yr
+    prefixes = [W.rand_int(0, 8192, W.SEED_MIXED, "len", 100 + s) for s in range(4)]
+    chunks = [512] * 4
+    total = [p + n for p, n in zip(prefixes, chunks)]
+    pb = W.allocate_pages(total, W.SEED_MIXED)
+    kc, vc = bi.alloc_kv_cache(pb.num_pages, 8, 128, 16, dev, fill=0.0)
+    kv = [W.request_kv(s, L, 8, 128, W.SEED_MIXED, device=dev) for s, L in enumerate(total)]
+    bi.bi_kv_append(torch.cat([k for k, _ in kv]), torch.cat([v for _, v in kv]), pb.slot_mapping.to(dev), kc, vc)
+    del kv
+    qp = W.randn_bf16((2048, 32, 128), W.SEED_MIXED, "q", 0, device=dev)
+    op = torch.empty_like(qp)
+    qs = torch.tensor([0, 512, 1024, 1536, 2048], dtype=torch.int32, device=dev)
+    ctx = torch.tensor(prefixes, dtype=torch.int32, device=dev)
+    btp = pb.block_table.to(dev)
+    us = time_fn(torch, lambda i=0: bi.bi_attn_prefill(qp, qs, ctx, 512, kc, vc, btp, 1 / math.sqrt(128), out=op),
+                 max(5, reps // 2))
+    out.append(entry("attn prefill 4x512 32/8 D128", us, bytes_prefill(prefixes, chunks, 32, 8, 128),
+                     flops_prefill(prefixes, chunks, 32, 128), extra={"prefixes": prefixes}))
+    del kc, vc, qp, op
+    torch.cuda.empty_cache()
+    # Qwen3-235B-shaped: lm_head 4096->151936 (fp32 logits) + log_softmax; decode attention 64/4.
+    V = 151936
+    wl = W.randn_bf16((V, 4096), W.SEED_MOE, "w", W.WEIGHTS, std=0.02, device=dev)
+    for T in (1, 64, 512, 2048):
+        ht = W.rows_for_requests(range(T), 4096, W.SEED_MOE, device=dev)
+        z = torch.empty((T, V), dtype=torch.float32, device=dev)
+        us = time_fn(torch, lambda i=0: bi.bi_gemm(ht, wl, out=z), max(5, reps // 4))
+        out.append(entry("gemm lm_head 4096->151936 fp32", us, bytes_gemm(T, V, 4096, 4), flops_gemm(T, V, 4096),
+                         extra={"T": T}))
+        lp = torch.empty_like(z)
+        us = time_fn(torch, lambda i=0: bi.bi_log_softmax(z, out=lp), max(5, reps // 4))
+        out.append(entry("log_softmax [T,151936] fp32", us, 8 * T * V, extra={"T": T}))
+        del ht, z, lp
+    del wl
+    torch.cuda.empty_cache()
+    for B in (1, 64, 256):
+        lens = W.decode_lengths(range(B), W.SEED_MOE)
+        pb = W.allocate_pages(lens, W.SEED_MOE)
+        kc, vc = bi.alloc_kv_cache(pb.num_pages, 4, 128, 16, dev, fill=0.0)
+        kv = [W.request_kv(r, L, 4, 128, W.SEED_MOE, device=dev) for r, L in enumerate(lens)]
+        bi.bi_kv_append(torch.cat([k for k, _ in kv]), torch.cat([v for _, v in kv]), pb.slot_mapping.to(dev), kc, vc)
+        del kv
+        q = W.randn_bf16((B, 64, 128), W.SEED_MOE, "q", 0, device=dev)
+        o = torch.empty_like(q)
+        btd, lt = pb.block_table.to(dev), torch.tensor(lens, dtype=torch.int32, device=dev)
+        ws = torch.empty((bi.bi_attn_decode_workspace_bytes(B, 64, 128, 4096),), dtype=torch.uint8, device=dev)
+        us = time_fn(torch, lambda i=0: bi.bi_attn_decode(q, kc, vc, btd, lt, 4096, 1 / math.sqrt(128), out=o,
+                                                           workspace=ws), reps)
+        out.append(entry("attn decode 64/4 D128", us, bytes_decode(lens, 64, 4, 128), flops_decode(lens, 64, 128),
+                         extra={"B": B, "sum_L": sum(lens)}))
+        del kc, vc
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(torch, W, step, sample):
+    """The fp64 oracle, as it stands, on requests 0..sample-1 of the same step."""
+    import numpy as np
+    from oracle import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    S = min(sample, step.B)
+
+    def f64(t):
+        t = t.detach().cpu()
+        return O.bf16_to_f64(t.contiguous().view(torch.int16).numpy())
+
+    x = f64(step.x[:S])
+    g1, g2 = f64(step.g1), f64(step.g2)
+    wq, wu, wd = f64(step.w_qkv), f64(step.w_up), f64(step.w_down)
+    kv = [W.request_kv(r, step.lens[r], 8, 128, W.SEED_DECODE, device="cuda") for r in range(S)]
+    ks = [f64(k) for k, _ in kv]
+    vs = [f64(v) for _, v in kv]
+    del kv
+    t0 = time.perf_counter()
+    h = O.rmsnorm(x, g1, EPS)
+    qkv = O.gemm(h, wq)
+    q = qkv[:, :4096].reshape(S, 32, 128)
+    # the step's new token replaces position L - 1 of each request's cache
+    for r in range(S):
+        ks[r][-1] = qkv[r, 4096:5120].reshape(8, 128)
+        vs[r][-1] = qkv[r, 5120:].reshape(8, 128)
+    o, _ = O.decode_attention(q, ks, vs, 1.0 / math.sqrt(128))
+    h2 = O.rmsnorm(o.reshape(S, 4096), g2, EPS)
+    up = O.gemm(h2, wu)
+    O.gemm(up, wd)
+    dt = time.perf_counter() - t0
+    lens = step.lens[:S]
+    nbytes = (2 * bytes_rmsnorm(S, 4096) + bytes_gemm(S, 6144, 4096) + bytes_append(S, 8, 128)
+              + bytes_decode(lens, 32, 8, 128) + bytes_gemm(S, 12288, 4096) + bytes_gemm(S, 4096, 12288))
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"one decode step for requests 0-{S - 1} of {step.B} (all weights, their KV caches), "
+                      f"fp64 numpy oracle; rate = the sample's algorithmic bytes / oracle seconds"}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              "requests and kv heads with no exchange, but no multi-GPU run is part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import invariant_bi_rmsnorm_02_amd as bi
+    import workloads as W
+    if not os.path.exists(bi.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    bi.lib()
+    torch.cuda.set_device(0)
+    print(f"[bench] building the decode-step workload B={args.batch}", file=sys.stderr, flush=True)
+    step = DecodeStep(torch, bi, W, args.batch)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step.step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        step.step(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    attn_us = sum(a.elapsed_time(b) for a, b in evs) / args.steps * 1e3
+    print(f"[bench] step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms), attention {attn_us:.1f} us",
+          file=sys.stderr, flush=True)
+
+    nbytes = step.step_bytes()
+    attn_bytes = bytes_decode(step.lens, 32, 8, 128)
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    achieved = attn_bytes / (attn_us * 1e-6) / 1e9
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"Qwen3-8B-shaped decode step: RMSNorm, QKV GEMM 4096->6144, KV append, "
+                               f"decode attention 32/8 heads D128 paged (16) KV L~U[1,4096], RMSNorm, "
+                               f"MLP GEMMs 4096->12288->4096", "batch": args.batch, "sum_kv_len": sum(step.lens),
+                   "step_bytes": nbytes, "step_flops": step.step_flops(), "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "bi_attn_decode (chunk kernel + merge kernel)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_us": round(attn_us, 2), "algorithmic_bytes": attn_bytes},
+    }
+    if args.kernels != "none":
+        print("[bench] per-kernel table", file=sys.stderr, flush=True)
+        result["kernels"] = kernel_table(torch, bi, W, step, args.reps, args.kernels == "all")
+    if not args.no_cpu_baseline:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(torch, W, step, args.cpu_sample)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

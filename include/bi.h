@@ -26,8 +26,8 @@
  *     BI_ERR_HIP reports a failed launch (hipGetLastError after the launch).
  *   - No global mutable state: calls are thread-safe.  No environment variable,
  *     flag or tuning table changes the arithmetic.
- *   - Pointers must be 16-byte aligned and leading dimensions (in elements)
- *     multiples of 8, so rows can be moved in 16-byte vectors.
+ *   - Input pointers must be 16-byte aligned and input leading dimensions (in
+ *     elements) multiples of 8, so rows can be moved in 16-byte vectors.
  */
 #ifndef BI_H
 #define BI_H
@@ -78,7 +78,9 @@ bi_status bi_rmsnorm(const void* x, int64_t ldx, const void* gamma, float eps,
  *   C[m, n] = sum_k A[m, k] * W[n, k]       (C = A W^T, W stored [N, K] as in
  *                                            a linear layer's weight)
  * a: [m, k] bf16, row stride lda; w: [n, k] bf16, row stride ldw;
- * c: [m, n] of c_dtype (BI_BF16 or BI_F32), row stride ldc.
+ * c: [m, n] of c_dtype (BI_BF16 or BI_F32), row stride ldc >= n (any value;
+ *    c aligned to its element size; ldc % 4 == 0 with a 16-byte-aligned c lets
+ *    the epilogue use vector stores, which does not change any value).
  * One tile shape, one MFMA instruction and one ascending K loop with a single
  * fp32 accumulator per output element are used for every m: no split-K and no
  * shape-dependent configuration, so row m of C does not depend on the other rows
@@ -100,13 +102,15 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw,
 
 /*
  * KV append: write new keys/values into their cache slots before attention.
- * k_new, v_new: [num_tokens][num_kv_heads][head_dim] bf16 (contiguous);
+ * k_new, v_new: [num_tokens][num_kv_heads][head_dim] bf16, heads and dims
+ *   contiguous, consecutive tokens ld_new elements apart (ld_new >= Hkv * D,
+ *   ld_new % 8 == 0; e.g. the K and V columns of a fused QKV projection);
  * slot_mapping: [num_tokens] int32, slot = page * page_size + offset; a negative
  * slot or one >= num_pages * page_size skips that token (padding).
  * A pure copy: every cache element is written bit-exactly.
  * head_dim in {64, 128}; page_size in {8, 16, 32, 64, 128, 256} (divides 256).
  */
-bi_status bi_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+bi_status bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new, const int32_t* slot_mapping,
                        int32_t num_tokens, void* k_cache, void* v_cache, int32_t num_pages,
                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                        bi_stream_t stream);
@@ -131,7 +135,9 @@ size_t bi_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
  * the last is partial); each chunk yields (max, sum, accumulators) and the
  * chunks are merged in ascending order, starting from (-inf, 0, 0), by a
  * log-sum-exp step.  The chunking depends on nothing but L_b.
- * q: [num_seqs][num_q_heads][head_dim] bf16; out: same shape bf16;
+ * q: [num_seqs][num_q_heads][head_dim] bf16, consecutive sequences ld_q
+ *   elements apart (ld_q >= Hq * D, ld_q % 8 == 0); out: contiguous
+ *   [num_seqs][num_q_heads][head_dim] bf16;
  * lse: [num_seqs][num_q_heads] fp32 or NULL (natural log).
  * block_table: [num_seqs][max_pages_per_seq] int32; seq_lens: [num_seqs] int32.
  * max_seq_len: host-side upper bound of seq_lens (sizes the grid; a seq_len
@@ -141,7 +147,7 @@ size_t bi_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
  * head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 and the group size
  * num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}; page_size divides 256.
  */
-bi_status bi_attn_decode(const void* q, const void* k_cache, const void* v_cache, int32_t num_pages,
+bi_status bi_attn_decode(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache, int32_t num_pages,
                          const int32_t* block_table, int32_t max_pages_per_seq,
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -158,12 +164,13 @@ bi_status bi_attn_decode(const void* q, const void* k_cache, const void* v_cache
  * 0..p (causal, inclusive).  Each query row is reduced with exactly the chunk
  * routine and merge step of bi_attn_decode, so a prefilled row is bitwise equal
  * to decoding the same token with seq_len = p + 1.
- * q, out: [q_start[num_seqs]][num_q_heads][head_dim] bf16; lse: [..][num_q_heads]
+ * q: [q_start[num_seqs]][num_q_heads][head_dim] bf16, consecutive tokens ld_q
+ * elements apart; out: contiguous, same shape; lse: [..][num_q_heads]
  * fp32 or NULL.  q_start: [num_seqs + 1] int32, non-decreasing from 0;
  * ctx_lens: [num_seqs] int32.  max_q_len: host-side upper bound of n_s (sizes
  * the grid; longer chunks are clamped to it).  Same size limits as decode.
  */
-bi_status bi_attn_prefill(const void* q, const int32_t* q_start, const int32_t* ctx_lens,
+bi_status bi_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens,
                           int32_t num_seqs, int32_t max_q_len,
                           const void* k_cache, const void* v_cache, int32_t num_pages,
                           const int32_t* block_table, int32_t max_pages_per_seq,

@@ -30,11 +30,11 @@ _SIGNATURES = {
     "bi_version": (ctypes.c_char_p, []),
     "bi_rmsnorm": (_c_i32, [_c_p, _c_i64, _c_p, _c_f32, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_gemm": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i32, _c_i64, _c_i64, _c_i64, _c_p]),
-    "bi_kv_append": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
+    "bi_kv_append": (_c_i32, [_c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
     "bi_attn_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32]),
-    "bi_attn_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
+    "bi_attn_decode": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                 _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_size, _c_p]),
-    "bi_attn_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_i32,
+    "bi_attn_prefill": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_i32,
                                  _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p]),
     "bi_log_softmax": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
 }
@@ -91,6 +91,13 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
         raise ValueError(f"{name} must be a GPU tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _tokens(t: torch.Tensor, name: str) -> int:
+    """Token stride (elements) of a [T, H, D] tensor whose heads and dims are contiguous."""
+    if t.dim() != 3 or (t.shape[2] > 1 and t.stride(2) != 1) or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
+        raise ValueError(f"{name} must be [T, heads, dim] with heads and dims contiguous")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1] * t.shape[2], t.stride(0))
 
 
 def _rows(t: torch.Tensor, name: str) -> int:
@@ -169,9 +176,10 @@ def bi_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.T
     t = k_new.shape[0]
     if tuple(k_new.shape) != (t, hkv, d) or v_new.shape != k_new.shape or slot_mapping.shape != (t,):
         raise ValueError("k_new/v_new must be [T, Hkv, D] and slot_mapping [T]")
-    if not (k_new.is_contiguous() and v_new.is_contiguous() and slot_mapping.is_contiguous()):
-        raise ValueError("inputs must be contiguous")
-    _check("bi_kv_append", lib().bi_kv_append(k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), t,
+    ld = _tokens(k_new, "k_new")
+    if _tokens(v_new, "v_new") != ld or not slot_mapping.is_contiguous():
+        raise ValueError("k_new and v_new need the same token stride; slot_mapping contiguous")
+    _check("bi_kv_append", lib().bi_kv_append(k_new.data_ptr(), v_new.data_ptr(), ld, slot_mapping.data_ptr(), t,
                                               k_cache.data_ptr(), v_cache.data_ptr(), pages, hkv, d, ps,
                                               _stream(stream)))
 
@@ -190,14 +198,15 @@ def bi_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     _dev(block_table, "block_table", torch.int32)
     _dev(seq_lens, "seq_lens", torch.int32)
     b, hq, dq = q.shape
-    if dq != d or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [B, Hq, D] tensor")
+    if dq != d:
+        raise ValueError("q must be [B, Hq, D]")
+    ldq = _tokens(q, "q")
     if block_table.dim() != 2 or block_table.shape[0] != b or not block_table.is_contiguous():
         raise ValueError("block_table must be a contiguous [B, max_pages] tensor")
     if seq_lens.shape != (b,) or not seq_lens.is_contiguous():
         raise ValueError("seq_lens must be [B]")
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     _dev(out, "out", torch.bfloat16)
     if out.shape != q.shape or not out.is_contiguous():
         raise ValueError("out shape")
@@ -212,7 +221,7 @@ def bi_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         raise ValueError("workspace must be a contiguous GPU tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("bi_attn_decode", lib().bi_attn_decode(
-        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), pages, block_table.data_ptr(),
+        q.data_ptr(), ldq, k_cache.data_ptr(), v_cache.data_ptr(), pages, block_table.data_ptr(),
         block_table.shape[1], seq_lens.data_ptr(), b, int(max_seq_len), hq, hkv, d, ps, float(softmax_scale),
         out.data_ptr(), lse.data_ptr() if lse is not None else None, workspace.data_ptr(), ws_bytes,
         _stream(stream)))
@@ -231,14 +240,15 @@ def bi_attn_prefill(q: torch.Tensor, q_start: torch.Tensor, ctx_lens: torch.Tens
     _dev(block_table, "block_table", torch.int32)
     t, hq, dq = q.shape
     s = ctx_lens.shape[0]
-    if dq != d or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [T, Hq, D] tensor")
+    if dq != d:
+        raise ValueError("q must be [T, Hq, D]")
+    ldq = _tokens(q, "q")
     if q_start.shape != (s + 1,) or not q_start.is_contiguous() or not ctx_lens.is_contiguous():
         raise ValueError("q_start must be [S + 1] and ctx_lens [S]")
     if block_table.dim() != 2 or block_table.shape[0] != s or not block_table.is_contiguous():
         raise ValueError("block_table must be a contiguous [S, max_pages] tensor")
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     _dev(out, "out", torch.bfloat16)
     if out.shape != q.shape or not out.is_contiguous():
         raise ValueError("out shape")
@@ -247,7 +257,7 @@ def bi_attn_prefill(q: torch.Tensor, q_start: torch.Tensor, ctx_lens: torch.Tens
         if lse.shape != (t, hq) or not lse.is_contiguous():
             raise ValueError("lse must be [T, Hq]")
     _check("bi_attn_prefill", lib().bi_attn_prefill(
-        q.data_ptr(), q_start.data_ptr(), ctx_lens.data_ptr(), s, int(max_q_len), k_cache.data_ptr(),
+        q.data_ptr(), ldq, q_start.data_ptr(), ctx_lens.data_ptr(), s, int(max_q_len), k_cache.data_ptr(),
         v_cache.data_ptr(), pages, block_table.data_ptr(), block_table.shape[1], hq, hkv, d, ps,
         float(softmax_scale), out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(stream)))
     return out, lse

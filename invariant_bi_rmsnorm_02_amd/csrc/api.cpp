@@ -101,14 +101,15 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* 
   if (!a || !w || !c) return BI_ERR_INVALID_ARG;
   if (k % 32) return BI_ERR_UNSUPPORTED;
   if (m > (1 << 30) || n > (1 << 30) || k > (1 << 30)) return BI_ERR_UNSUPPORTED;
-  if (lda < k || ldw < k || ldc < n || lda % 8 || ldw % 8 || ldc % 8) return BI_ERR_INVALID_ARG;
-  if (!aligned16(a) || !aligned16(w) || !aligned16(c)) return BI_ERR_INVALID_ARG;
+  if (lda < k || ldw < k || ldc < n || lda % 8 || ldw % 8) return BI_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(w)) return BI_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(c) % (c_dtype == BI_F32 ? 4u : 2u)) return BI_ERR_INVALID_ARG;
   const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
   if (tiles > 0x7fffffff) return BI_ERR_UNSUPPORTED;
   return from_hip(bi::launch_gemm(a, lda, w, ldw, c, ldc, c_dtype == BI_F32, m, n, k, as_stream(stream)));
 }
 
-bi_status bi_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+bi_status bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new, const int32_t* slot_mapping,
                        int32_t num_tokens, void* k_cache, void* v_cache, int32_t num_pages,
                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size, bi_stream_t stream) {
   if (num_tokens < 0) return BI_ERR_INVALID_ARG;
@@ -121,7 +122,8 @@ bi_status bi_kv_append(const void* k_new, const void* v_new, const int32_t* slot
   const int l2 = log2_exact(page_size);
   if (l2 < 3 || l2 > 8) return BI_ERR_UNSUPPORTED;
   if ((int64_t)num_pages * page_size > 0x7fffffff) return BI_ERR_UNSUPPORTED;
-  return from_hip(bi::launch_kv_append(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache,
+  if (ld_new < (int64_t)num_kv_heads * head_dim || ld_new % 8) return BI_ERR_INVALID_ARG;
+  return from_hip(bi::launch_kv_append(k_new, v_new, ld_new, slot_mapping, num_tokens, k_cache, v_cache,
                                        num_pages, num_kv_heads, head_dim, page_size, as_stream(stream)));
 }
 
@@ -134,7 +136,7 @@ size_t bi_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
   return (bytes + 255) & ~(size_t)255;
 }
 
-bi_status bi_attn_decode(const void* q, const void* k_cache, const void* v_cache, int32_t num_pages,
+bi_status bi_attn_decode(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache, int32_t num_pages,
                          const int32_t* block_table, int32_t max_pages_per_seq,
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -147,17 +149,18 @@ bi_status bi_attn_decode(const void* q, const void* k_cache, const void* v_cache
   if (st != BI_OK) return st;
   if (!q || !seq_lens || !out) return BI_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(out)) return BI_ERR_INVALID_ARG;
+  if (ld_q < (int64_t)num_q_heads * head_dim || ld_q % 8) return BI_ERR_INVALID_ARG;
   if (num_seqs > 65535 || num_kv_heads > 65535) return BI_ERR_UNSUPPORTED;  // grid y/z limits
   if (!workspace || !aligned16(workspace)) return BI_ERR_WORKSPACE;
   if (workspace_bytes < bi_attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len))
     return BI_ERR_WORKSPACE;
   const bi::AttnGeom g = make_geom(k_cache, v_cache, num_pages, block_table, max_pages_per_seq,
                                    num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale);
-  return from_hip(bi::launch_attn_decode(q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace,
+  return from_hip(bi::launch_attn_decode(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace,
                                          as_stream(stream)));
 }
 
-bi_status bi_attn_prefill(const void* q, const int32_t* q_start, const int32_t* ctx_lens,
+bi_status bi_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens,
                           int32_t num_seqs, int32_t max_q_len, const void* k_cache, const void* v_cache,
                           int32_t num_pages, const int32_t* block_table, int32_t max_pages_per_seq,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -170,11 +173,12 @@ bi_status bi_attn_prefill(const void* q, const int32_t* q_start, const int32_t* 
   if (st != BI_OK) return st;
   if (!q || !q_start || !ctx_lens || !out) return BI_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(out)) return BI_ERR_INVALID_ARG;
+  if (ld_q < (int64_t)num_q_heads * head_dim || ld_q % 8) return BI_ERR_INVALID_ARG;
   if (num_seqs > 65535 || num_kv_heads > 65535) return BI_ERR_UNSUPPORTED;
   if ((int64_t)max_q_len * (num_q_heads / num_kv_heads) > (1 << 30)) return BI_ERR_UNSUPPORTED;
   const bi::AttnGeom g = make_geom(k_cache, v_cache, num_pages, block_table, max_pages_per_seq,
                                    num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale);
-  return from_hip(bi::launch_attn_prefill(q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse,
+  return from_hip(bi::launch_attn_prefill(q, ld_q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse,
                                           as_stream(stream)));
 }
 

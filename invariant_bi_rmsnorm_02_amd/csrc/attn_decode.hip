@@ -18,7 +18,7 @@ namespace {
 
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_partial_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     int num_pages, const int32_t* __restrict__ block_table, int max_pages,
     const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq, int Hkv, int log2_ps,
     float scale_log2, float* __restrict__ ws, int max_chunks) {
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(64) void attn_decode_partial_kernel(
   const bool row_ok = n < G;
 
   u32x4_t qf[D / 32];
-  const uint16_t* qp = q + ((int64_t)b * Hq + h * G + n) * D + 8 * g;
+  const uint16_t* qp = q + (int64_t)b * ldq + (h * G + n) * D + 8 * g;
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
     qf[ks] = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
@@ -92,13 +92,13 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
 }
 
 template <int D>
-hipError_t launch(const void* q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
+hipError_t launch(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
                   int max_seq_len, void* out, float* lse, void* workspace, hipStream_t stream) {
   const int max_chunks = (max_seq_len + kChunk - 1) / kChunk;
   float* ws = static_cast<float*>(workspace);
   hipLaunchKernelGGL(attn_decode_partial_kernel<D>,
                      dim3(max_chunks, g.num_kv_heads, num_seqs), dim3(64), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(g.k_cache),
+                     static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(g.k_cache),
                      static_cast<const uint16_t*>(g.v_cache), g.num_pages, g.block_table,
                      g.max_pages_per_seq, seq_lens, max_seq_len, g.num_q_heads, g.num_kv_heads,
                      g.log2_page, g.scale_log2, ws, max_chunks);
@@ -112,14 +112,14 @@ hipError_t launch(const void* q, const AttnGeom& g, const int32_t* seq_lens, int
 
 }  // namespace
 
-hipError_t launch_attn_decode(const void* q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
+hipError_t launch_attn_decode(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
                               int max_seq_len, void* out, float* lse, void* workspace,
                               hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
   if (max_seq_len <= 0) max_seq_len = 1;  // grid of one empty chunk; merge writes the L <= 0 result
   return g.head_dim == 64
-             ? launch<64>(q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace, stream)
-             : launch<128>(q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace, stream);
+             ? launch<64>(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace, stream)
+             : launch<128>(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace, stream);
 }
 
 }  // namespace bi

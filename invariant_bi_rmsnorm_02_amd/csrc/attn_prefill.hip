@@ -23,7 +23,7 @@ constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(
-    const uint16_t* __restrict__ q, const int32_t* __restrict__ q_start,
+    const uint16_t* __restrict__ q, int64_t ldq, const int32_t* __restrict__ q_start,
     const int32_t* __restrict__ ctx_lens, int max_q_len, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table,
     int max_pages, int Hq, int Hkv, int log2_ps, float scale_log2, uint16_t* __restrict__ out,
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(
   const int lim = ctx + last / G + 1;                     // keys at >= lim no row can see
 
   u32x4_t qf[D / 32];
-  const uint16_t* qp = q + ((int64_t)(qs + tok) * Hq + h * G + hh) * D + 8 * g;
+  const uint16_t* qp = q + (int64_t)(qs + tok) * ldq + (h * G + hh) * D + 8 * g;
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
     qf[ks] = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
@@ -96,12 +96,12 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(
 }
 
 template <int D>
-hipError_t launch(const void* q, const int32_t* q_start, const int32_t* ctx_lens, int num_seqs,
+hipError_t launch(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens, int num_seqs,
                   int max_q_len, const AttnGeom& g, void* out, float* lse, hipStream_t stream) {
   const int G = g.num_q_heads / g.num_kv_heads;
   const int tiles = (max_q_len * G + kRowsPerBlock - 1) / kRowsPerBlock;
   hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(tiles, g.num_kv_heads, num_seqs), dim3(kWaves * 64),
-                     0, stream, static_cast<const uint16_t*>(q), q_start, ctx_lens, max_q_len,
+                     0, stream, static_cast<const uint16_t*>(q), ld_q, q_start, ctx_lens, max_q_len,
                      static_cast<const uint16_t*>(g.k_cache), static_cast<const uint16_t*>(g.v_cache),
                      g.num_pages, g.block_table, g.max_pages_per_seq, g.num_q_heads, g.num_kv_heads,
                      g.log2_page, g.scale_log2, static_cast<uint16_t*>(out), lse);
@@ -110,12 +110,12 @@ hipError_t launch(const void* q, const int32_t* q_start, const int32_t* ctx_lens
 
 }  // namespace
 
-hipError_t launch_attn_prefill(const void* q, const int32_t* q_start, const int32_t* ctx_lens,
+hipError_t launch_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens,
                                int num_seqs, int max_q_len, const AttnGeom& g, void* out, float* lse,
                                hipStream_t stream) {
   if (num_seqs == 0 || max_q_len == 0) return hipSuccess;
-  return g.head_dim == 64 ? launch<64>(q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse, stream)
-                          : launch<128>(q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse, stream);
+  return g.head_dim == 64 ? launch<64>(q, ld_q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse, stream)
+                          : launch<128>(q, ld_q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse, stream);
 }
 
 }  // namespace bi

@@ -54,7 +54,7 @@ __device__ __forceinline__ void map_tile(int pid, int tiles_m, int tiles_n, int&
 template <bool kF32Out>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
-    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n) {
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
   __shared__ __attribute__((aligned(16))) uint16_t sW[2][TN * BK];
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][TM * BK];
 
@@ -152,14 +152,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
       const f32x4_t v = acc[i][j];
       if constexpr (kF32Out) {
         float* cp = static_cast<float*>(C) + (int64_t)m * ldc + n;
-        if (n + 3 < N) {
+        if (vec_store && n + 3 < N) {
           *reinterpret_cast<f32x4_t*>(cp) = v;
         } else {
           for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = v[e];
         }
       } else {
         uint16_t* cp = static_cast<uint16_t*>(C) + (int64_t)m * ldc + n;
-        if (n + 3 < N) {
+        if (vec_store && n + 3 < N) {
           *reinterpret_cast<u32x2_t*>(cp) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         } else {
           for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = static_cast<uint16_t>(f32_to_bf16(v[e]));
@@ -179,12 +179,14 @@ hipError_t launch_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, v
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(kThreads);
   auto* as = static_cast<const uint16_t*>(a);
   auto* ws = static_cast<const uint16_t*>(w);
+  // Vector stores need every row start 16-byte (fp32) / 8-byte (bf16) aligned.
+  const int vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(c) & 15u) == 0);
   if (c_f32)
     hipLaunchKernelGGL(gemm_kernel<true>, grid, block, 0, stream, as, lda, ws, ldw, c, ldc, (int)m,
-                       (int)n, (int)k, tiles_m, tiles_n);
+                       (int)n, (int)k, tiles_m, tiles_n, vec);
   else
     hipLaunchKernelGGL(gemm_kernel<false>, grid, block, 0, stream, as, lda, ws, ldw, c, ldc, (int)m,
-                       (int)n, (int)k, tiles_m, tiles_n);
+                       (int)n, (int)k, tiles_m, tiles_n, vec);
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* gamma, float e
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc,
                        bool c_f32, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
-hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+hipError_t launch_kv_append(const void* k_new, const void* v_new, int64_t ld_new, const int32_t* slot_mapping,
                             int num_tokens, void* k_cache, void* v_cache, int num_pages,
                             int num_kv_heads, int head_dim, int page_size, hipStream_t stream);
 
@@ -32,11 +32,11 @@ struct AttnGeom {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
-hipError_t launch_attn_decode(const void* q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
+hipError_t launch_attn_decode(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
                               int max_seq_len, void* out, float* lse, void* workspace,
                               hipStream_t stream);
 
-hipError_t launch_attn_prefill(const void* q, const int32_t* q_start, const int32_t* ctx_lens,
+hipError_t launch_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens,
                                int num_seqs, int max_q_len, const AttnGeom& g, void* out, float* lse,
                                hipStream_t stream);
 

@@ -42,7 +42,7 @@ def test_host_validation_without_gpu(lib):
 
     def dec(**kw):
         a = dict(args, **kw)
-        return lib.bi_attn_decode(a["q"], a["kc"], a["vc"], a["pages"], a["bt"], a["mp"], a["lens"], a["b"],
+        return lib.bi_attn_decode(a["q"], a.get("ldq", 4096), a["kc"], a["vc"], a["pages"], a["bt"], a["mp"], a["lens"], a["b"],
                                   a["msl"], a["hq"], a["hkv"], a["d"], a["ps"], 0.1, P, None,
                                   a.get("ws", P), a.get("wsb", 1 << 30), None)
 
@@ -53,8 +53,10 @@ def test_host_validation_without_gpu(lib):
     assert dec(ws=None) == bi.BI_ERR_WORKSPACE
     assert dec(wsb=100) == bi.BI_ERR_WORKSPACE
     assert dec(b=0) == bi.BI_OK
+    assert dec(ldq=4000) == bi.BI_ERR_INVALID_ARG
     assert lib.bi_log_softmax(P, 6, P, 8, 2, 6, None) == bi.BI_ERR_UNSUPPORTED
-    assert lib.bi_kv_append(P, P, P, 3, P, P, 4, 8, 80, 16, None) == bi.BI_ERR_UNSUPPORTED
+    assert lib.bi_kv_append(P, P, 640, P, 3, P, P, 4, 8, 80, 16, None) == bi.BI_ERR_UNSUPPORTED
+    assert lib.bi_kv_append(P, P, 1000, P, 3, P, P, 4, 8, 128, 16, None) == bi.BI_ERR_INVALID_ARG
 
 
 def test_workspace_size_formula(lib):

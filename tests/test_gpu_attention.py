@@ -376,3 +376,21 @@ def test_attention_errors():
         bi.bi_attn_decode(torch.zeros((1, 32, 96), dtype=torch.bfloat16, device=DEV), kc, vc, bt.bt, bt.lens,
                           10, bt.scale)
     assert e.value.status == bi.BI_ERR_UNSUPPORTED
+
+
+def test_strided_fused_qkv_inputs():
+    # q / k / v read straight out of a fused QKV projection output [B, 6144].
+    B, hq, hkv, d = 12, 32, 8, 128
+    lens = W.decode_lengths(range(B), 31)
+    bt = Batch(range(B), lens, hq, hkv, d, 31)
+    qkv = W.randn_bf16((B, 6144), 31, "x", 5, device=DEV)
+    q, k, v = (qkv[:, :4096].view(B, hq, d), qkv[:, 4096:5120].view(B, hkv, d), qkv[:, 5120:].view(B, hkv, d))
+    o1, _ = bi.bi_attn_decode(q, bt.kc, bt.vc, bt.bt, bt.lens, 4096, bt.scale)
+    o2, _ = bi.bi_attn_decode(q.contiguous(), bt.kc, bt.vc, bt.bt, bt.lens, 4096, bt.scale)
+    assert_bitwise(o1, o2, "strided q")
+    kc2, vc2 = bt.kc.clone(), bt.vc.clone()
+    slots = torch.tensor([5, 77, 200, 3, 9, 11, 13, 15, 17, 19, 21, 23], dtype=torch.int32, device=DEV)
+    bi.bi_kv_append(k, v, slots, bt.kc, bt.vc)
+    bi.bi_kv_append(k.contiguous(), v.contiguous(), slots, kc2, vc2)
+    assert_bitwise(bt.kc, kc2, "strided k append")
+    assert_bitwise(bt.vc, vc2, "strided v append")
