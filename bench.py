@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--kernels", choices=["all", "step", "none"], default="all",
                     help="per-kernel table: every workload shape, only the step's B sweep, or none")
-    ap.add_argument("--cpu-sample", type=int, default=64, help="requests of the step the oracle computes")
+    ap.add_argument("--cpu-sample", type=int, default=256, help="requests of the step the oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reps", type=int, default=20)
     return ap.parse_args()
@@ -325,8 +325,9 @@ def kernel_table(torch, bi, W, step, reps, everything):
 
 # ---------------------------------------------------------------- CPU oracle baseline
 
-def cpu_baseline(torch, W, step, sample):
-    """The fp64 oracle, as it stands, on requests 0..sample-1 of the same step."""
+def cpu_baseline(torch, W, step, sample, min_seconds=10.0, max_reps=50):
+    """The fp64 oracle, as it stands, on requests 0..sample-1 of the same decode
+    step, repeated until about `min_seconds` of host time have been spent."""
     import numpy as np
     from oracle import oracle as O
     try:
@@ -347,26 +348,33 @@ def cpu_baseline(torch, W, step, sample):
     ks = [f64(k) for k, _ in kv]
     vs = [f64(v) for _, v in kv]
     del kv
-    t0 = time.perf_counter()
-    h = O.rmsnorm(x, g1, EPS)
-    qkv = O.gemm(h, wq)
-    q = qkv[:, :4096].reshape(S, 32, 128)
-    # the step's new token replaces position L - 1 of each request's cache
-    for r in range(S):
-        ks[r][-1] = qkv[r, 4096:5120].reshape(8, 128)
-        vs[r][-1] = qkv[r, 5120:].reshape(8, 128)
-    o, _ = O.decode_attention(q, ks, vs, 1.0 / math.sqrt(128))
-    h2 = O.rmsnorm(o.reshape(S, 4096), g2, EPS)
-    up = O.gemm(h2, wu)
-    O.gemm(up, wd)
-    dt = time.perf_counter() - t0
+
+    def one_step():
+        h = O.rmsnorm(x, g1, EPS)
+        qkv = O.gemm(h, wq)
+        q = qkv[:, :4096].reshape(S, 32, 128)
+        # the step's new token is position L - 1 of each request's cache
+        for r in range(S):
+            ks[r][-1] = qkv[r, 4096:5120].reshape(8, 128)
+            vs[r][-1] = qkv[r, 5120:].reshape(8, 128)
+        o, _ = O.decode_attention(q, ks, vs, 1.0 / math.sqrt(128))
+        h2 = O.rmsnorm(o.reshape(S, 4096), g2, EPS)
+        O.gemm(O.gemm(h2, wu), wd)
+
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        one_step()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            break
     lens = step.lens[:S]
     nbytes = (2 * bytes_rmsnorm(S, 4096) + bytes_gemm(S, 6144, 4096) + bytes_append(S, 8, 128)
               + bytes_decode(lens, 32, 8, 128) + bytes_gemm(S, 12288, 4096) + bytes_gemm(S, 4096, 12288))
-    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"one decode step for requests 0-{S - 1} of {step.B} (all weights, their KV caches), "
-                      f"fp64 numpy oracle; rate = the sample's algorithmic bytes / oracle seconds"}
+    return {"value": round(nbytes * reps / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2), "reps": reps, "ms_per_step": round(dt / reps * 1e3, 1),
+            "sample": f"the decode step for requests 0-{S - 1} of {step.B} (all weights, their KV caches), "
+                      f"fp64 numpy oracle, repeated {reps} times; rate = algorithmic bytes / oracle seconds"}
 
 
 # ---------------------------------------------------------------- main

@@ -5,188 +5,122 @@
 // "Fixed Size Split KV Strategy"), and "Batch Invariance and Numerical
 // Reproducibility" (answer on fixed-size chunks): the keys of a sequence are
 // cut into fixed 256-token chunks anchored at position 0; every chunk yields
-// un-normalised softmax statistics and the chunks are folded in ascending
-// order.  Both kernels call exactly the routines below, so a query row's result
-// depends only on its own query vector, its position and the cache contents -
-// not on which kernel, batch, or other query rows it was computed with.
+// un-normalised softmax statistics (max, sum, accumulators) and the chunks are
+// folded in ascending order.  Both kernels run exactly the arithmetic below,
+// so a query row's result depends only on its own query vector, its position
+// and the cache contents - never on which kernel, batch or other query rows it
+// was computed with.  The kernels differ only in how K/V fragments reach the
+// registers (decode: straight from the paged cache; prefill: staged in LDS and
+// shared by the workgroup's wavefronts), which moves bits, not arithmetic.
 //
-// Data layout seen by one wavefront (16 query rows = "columns" n of the MFMA
-// output, one kv head, one 256-key chunk):
-//   S^T = K Q^T   with MFMA A = K rows (keys), B = Q^T (queries), k = head dim.
-//     d of MFMA k index (step ks, lane group g, element j) = 32 ks + 8 g + j.
-//     Key of MFMA row m' in block b of 32-key group s:
-//       key = 32 s + 8 (m' / 4) + 4 b + (m' % 4),
-//     chosen so that lane group g ends up holding the 8 consecutive keys
-//     32 s + 8 g + (4 b + i) of its column after the two blocks.
-//   O^T = V^T P^T with MFMA A = V^T (head dim rows), B = P^T, k = keys; the k
-//     index j of lane group g is key 32 s + 8 g + j, i.e. exactly the keys the
-//     lane already holds, so P never leaves its registers.  V is stored
-//     dim-major inside a page, so a lane's 8 keys of one dim are 16 contiguous
-//     bytes.
-// Reduction order inside a chunk, per query column:
-//   max: exact (order-free);  sum of p: lane-local over (s, b, i) ascending,
-//   then + lane^16, then + lane^32;  O: MFMA chain over s = 0..7 ascending.
-// p is rounded once to bf16 for the PV product; the sum uses the fp32 p.
+// Inside a chunk, keys are consumed in eight 32-key sub-blocks in ascending
+// order with an online max: for sub-block s and one query column,
+//   t_j   = (q . k_j) * scale * log2(e)             (masked keys: -inf)
+//   mx    = max_j t_j;  mn = max(m, mx);  ms = (mn == -inf ? 0 : mn)
+//   alpha = 2^(m - ms);  p_j = 2^(t_j - ms)
+//   l     = l * alpha + sum_j p_j
+//   o     = o * alpha + sum_j bf16(p_j) v_j          (one MFMA per 16 head dims)
+//   m     = mn
+// starting from (m, l, o) = (-inf, 0, 0).  A sub-block with no key visible to
+// a column leaves that column's (m, l, o) bit-identical (alpha = 2^0 = 1,
+// p = 0), so a kernel may skip sub-blocks that no column of its wave can see.
+// Sums over the 8 keys a lane holds run in key order, then lane^16, lane^32.
+//
+// Register layout of one wavefront (16 query rows = MFMA columns n):
+//   S^T = K Q^T  (MFMA A = keys, B = Q^T, k = head dim; d of k index
+//     (step ks, lane group g, element j) = 32 ks + 8 g + j).  Row m' of
+//     block b of a sub-block is key 8 (m' / 4) + 4 b + (m' % 4), so lane group
+//     g ends up holding keys 8 g .. 8 g + 7 of its column.
+//   O^T = V^T P^T (MFMA A = V^T rows = head dims, k = keys 8 g + j of lane
+//     group g): P never leaves the registers; V is stored dim-major in a page
+//     so a lane's 8 keys of one dim are 16 contiguous bytes.
 #pragma once
 
 #include "bi_common.hpp"
 
 namespace bi {
 
-constexpr int kChunk = 256;  // fixed split size in tokens
+constexpr int kChunk = 256;   // fixed split size in tokens
+constexpr int kSub = 32;      // keys per sub-block
+constexpr int kSubs = kChunk / kSub;
 
-// Paged K/V fragment source for one kv head and one chunk.
-//   k_cache: [pages][Hkv][PS][D]   v_cache: [pages][Hkv][D][PS]
-// Keys at positions >= lim (no query row of the wave can see them) and pages
-// outside [0, num_pages) read as zeros, so unwritten slots never enter.
-template <int D>
-struct PagedChunk {
-  const uint16_t* kc;  // k_cache + head offset handled in address math
-  const uint16_t* vc;
-  int head;            // kv head
-  int num_kv_heads;
-  int log2_ps;
-  int chunk_start;     // absolute position of key 0 of the chunk
-  int lim;             // keys at absolute positions >= lim read as zero
-  int page_reg;        // lane l: page id of logical page (chunk page l % pages-per-chunk), or -1
+// Key (relative to the sub-block) of MFMA row m' of S^T block b.
+__device__ __forceinline__ int sub_key_of_row(int mr, int b) { return 8 * (mr >> 2) + 4 * b + (mr & 3); }
 
-  __device__ __forceinline__ int page_of(int key_in_chunk) const {
-    return __shfl(page_reg, key_in_chunk >> log2_ps, kWave);
-  }
-
-  // MFMA A operand of S^T for 32-key group s, half b, head-dim step ks.
-  __device__ __forceinline__ void k_frags(int s, int b, u32x4_t (&f)[D / 32]) const {
-    const int lane = threadIdx.x & 63;
-    const int mr = lane & 15, g = lane >> 4;
-    const int key = 32 * s + 8 * (mr >> 2) + 4 * b + (mr & 3);
-    const int page = page_of(key);
-    const int pos = chunk_start + key;
-    const int ps = 1 << log2_ps;
-    if (pos < lim && page >= 0) {
-      const uint16_t* p = kc + (((int64_t)page * num_kv_heads + head) * ps + (pos & (ps - 1))) * D + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) f[ks] = *reinterpret_cast<const u32x4_t*>(p + 32 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) f[ks] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-
-  // MFMA A operand of O^T for head-dim tile dt and 32-key group s.
-  __device__ __forceinline__ u32x4_t v_frag(int dt, int s) const {
-    const int lane = threadIdx.x & 63;
-    const int d = 16 * dt + (lane & 15), g = lane >> 4;
-    const int key0 = 32 * s + 8 * g;
-    const int page = page_of(key0);
-    const int pos0 = chunk_start + key0;
-    const int ps = 1 << log2_ps;
-    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-    if (pos0 < lim && page >= 0) {
-      v = *reinterpret_cast<const u32x4_t*>(
-          vc + (((int64_t)page * num_kv_heads + head) * D + d) * ps + (pos0 & (ps - 1)));
-      const int nv = lim - pos0;  // keys of this fragment that exist
-      if (nv < 8) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t keep_lo = (2 * e < nv) ? 0x0000ffffu : 0u;
-          const uint32_t keep_hi = (2 * e + 1 < nv) ? 0xffff0000u : 0u;
-          v[e] &= (keep_lo | keep_hi);
-        }
-      }
-    }
-    return v;
-  }
+template <int D, int NB>
+struct ChunkAcc {
+  float m[NB];             // running max (log2 units), -inf before the first visible key
+  float l[NB];             // running sum of 2^(t - m)
+  f32x4_t o[NB][D / 16];   // lane: column n = lane % 16, head dims 16 dt + 4 g + i
 };
 
-// Page ids of the chunk, one per lane (lane l holds logical page
-// chunk_first_page + l % pages_per_chunk).  Pages past the last one any row of
-// the wave can see, or outside the pool, become -1.
-__device__ __forceinline__ int load_chunk_pages(const int32_t* bt_row, int max_pages, int chunk,
-                                                int log2_ps, int lim, int num_pages) {
-  const int lane = threadIdx.x & 63;
-  const int ppc = kChunk >> log2_ps;
-  const int lp = chunk * ppc + (lane % ppc);
-  int pg = -1;
-  if (lp < max_pages && (lp << log2_ps) < lim) {
-    pg = bt_row[lp];
-    if (pg < 0 || pg >= num_pages) pg = -1;
+template <int D, int NB>
+__device__ __forceinline__ void chunk_init(ChunkAcc<D, NB>& a) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    a.m[nb] = -INFINITY;
+    a.l[nb] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) a.o[nb][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  return pg;
 }
 
-template <int D>
-struct Partial {
-  float m;              // chunk max of scaled scores (log2 units); -inf if no valid key
-  float l;              // sum over the chunk of exp2(t - m)
-  f32x4_t o[D / 16];    // lane: column n = lane % 16, head dims 16 dt + 4 g + i
-};
-
-// Chunk partial for the wave's 16 query columns.  qf: Q^T fragments (lane
-// column n = lane % 16, dims 32 ks + 8 g .. +7).  n_valid: number of keys of the
-// chunk this lane's query column may see (0..256), keys 0..n_valid-1.
-template <int D>
-__device__ __forceinline__ void chunk_partial(const PagedChunk<D>& kv, const u32x4_t (&qf)[D / 32],
-                                              int n_valid, float scale_log2, Partial<D>& out) {
-  const int lane = threadIdx.x & 63, g = lane >> 4;
-  f32x4_t S[8][2];
+// One 32-key sub-block s of the chunk.  kf: S^T A operands [block b][step ks];
+// vf: O^T A operands [dim tile dt]; qf: Q^T B operands [n-block][step ks];
+// n_valid[nb]: keys of the chunk column (lane % 16) of n-block nb may see
+// (keys 0 .. n_valid - 1 relative to the chunk start).
+template <int D, int NB>
+__device__ __forceinline__ void chunk_step(ChunkAcc<D, NB>& a, const u32x4_t (&kf)[2][D / 32],
+                                           const u32x4_t (&vf)[D / 16], const u32x4_t (&qf)[NB][D / 32],
+                                           const int (&n_valid)[NB], int s, float scale_log2) {
+  const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int nb = 0; nb < NB; ++nb) {
+    f32x4_t S[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      u32x4_t kf[D / 32];
-      kv.k_frags(s, b, kf);
-      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      S[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) acc = mfma_16x16x32(kf[ks], qf[ks], acc);
-      S[s][b] = acc;
+      for (int ks = 0; ks < D / 32; ++ks) S[b] = mfma_16x16x32(kf[b][ks], qf[nb][ks], S[b]);
     }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
+    float t[8];
+    float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = 32 * s + 8 * g + 4 * b + i;
-        const float t = key < n_valid ? S[s][b][i] * scale_log2 : -INFINITY;
-        S[s][b][i] = t;
-        mx = fmaxf(mx, t);
+        const int key = kSub * s + 8 * g + 4 * b + i;
+        t[4 * b + i] = key < n_valid[nb] ? S[b][i] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, t[4 * b + i]);
       }
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
-  const float ms = (mx == -INFINITY) ? 0.0f : mx;
-
-  float ls = 0.0f;
-  u32x4_t pb[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float mn = fmaxf(a.m[nb], mx);
+    const float ms = (mn == -INFINITY) ? 0.0f : mn;
+    const float alpha = exp2_hw(a.m[nb] - ms);
     float p[8];
+    float ls = 0.0f;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int j = 0; j < 8; ++j) {
+      p[j] = exp2_hw(t[j] - ms);
+      ls = ls + p[j];
+    }
+    ls = ls + shfl_xor(ls, 16);
+    ls = ls + shfl_xor(ls, 32);
+    a.l[nb] = a.l[nb] * alpha + ls;
+    const u32x4_t pb = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                               pack_bf16x2(p[6], p[7])};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[4 * b + i] = exp2_hw(S[s][b][i] - ms);
-        ls = ls + p[4 * b + i];
-      }
-    pb[s] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                    pack_bf16x2(p[6], p[7])};
+    for (int dt = 0; dt < D / 16; ++dt) {
+      f32x4_t o = a.o[nb][dt];
+      o = f32x4_t{o[0] * alpha, o[1] * alpha, o[2] * alpha, o[3] * alpha};
+      a.o[nb][dt] = mfma_16x16x32(vf[dt], pb, o);
+    }
+    a.m[nb] = mn;
   }
-  ls = ls + shfl_xor(ls, 16);
-  ls = ls + shfl_xor(ls, 32);
-
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc = mfma_16x16x32(kv.v_frag(dt, s), pb[s], acc);
-    out.o[dt] = acc;
-  }
-  out.m = mx;
-  out.l = ls;
 }
 
-// One step of the ascending log-sum-exp fold: state (m, l, acc) absorbs the
+// One step of the ascending fold over chunks: state (m, l, acc) absorbs the
 // chunk partial (mc, lc, accc).  The state starts at (-inf, 0, 0); mc is
 // finite for every chunk that is folded.  Both kernels call this, element by
 // element, with the same operands.
@@ -201,9 +135,38 @@ __device__ __forceinline__ float merge_val(float acc, float accc, const MergeCoe
   return acc * k.alpha + accc * k.beta;
 }
 
-// Final normalisation and output rounding; +0.0f turns a -0 into +0 so that a
-// zero result has one bit pattern whichever keys contributed exact zeros.
+// Final normalisation; +0.0f turns a -0 into +0 so that a zero result has one
+// bit pattern whichever keys contributed exact zeros.
 __device__ __forceinline__ float finalize_val(float acc, float l) { return acc / l + 0.0f; }
 __device__ __forceinline__ float finalize_lse(float m, float l) { return (m + log2_hw(l)) * kLn2; }
+
+// Page ids of one chunk, one per lane: lane l holds logical page
+// chunk * pages_per_chunk + l % pages_per_chunk, or -1 when that page is past
+// `lim` (no row can see it), past the table, or outside the pool.
+__device__ __forceinline__ int load_chunk_pages(const int32_t* bt_row, int max_pages, int chunk,
+                                                int log2_ps, int lim, int num_pages) {
+  const int lane = threadIdx.x & 63;
+  const int ppc = kChunk >> log2_ps;
+  const int lp = chunk * ppc + (lane % ppc);
+  int pg = -1;
+  if (lp < max_pages && (lp << log2_ps) < lim) {
+    pg = bt_row[lp];
+    if (pg < 0 || pg >= num_pages) pg = -1;
+  }
+  return pg;
+}
+
+__device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
+
+// Keep bf16 elements 0 .. nv-1 of an 8-element fragment, zero the rest.
+__device__ __forceinline__ u32x4_t keep_first(u32x4_t v, int nv) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t lo = (2 * e < nv) ? 0x0000ffffu : 0u;
+    const uint32_t hi = (2 * e + 1 < nv) ? 0xffff0000u : 0u;
+    v[e] &= (lo | hi);
+  }
+  return v;
+}
 
 }  // namespace bi

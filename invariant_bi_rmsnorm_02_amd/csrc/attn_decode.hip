@@ -6,21 +6,90 @@
 // Kernel 1 (grid: chunk x kv head x sequence, one wavefront each): the partial
 // statistics of one 256-key chunk for the q heads of one kv head, written to
 // the workspace.  A sequence of L tokens has ceil(L / 256) chunks whatever else
-// is in the batch; workgroups past a sequence's last chunk exit at once.
-// Kernel 2 (grid: q head x sequence): the ascending log-sum-exp fold of those
-// partials, normalisation and bf16 output.  No atomics, no cross-workgroup
-// ordering: every value is written by exactly one workgroup.
+// is in the batch; workgroups past a sequence's last chunk exit at once.  K and
+// V fragments go from HBM straight into registers in MFMA layout; the next
+// 32-key sub-block is in flight while the current one is computed.
+// Kernel 2 (grid: q head x sequence): the ascending fold of those partials,
+// normalisation and bf16 output.  No atomics, no cross-workgroup ordering:
+// every value is written by exactly one workgroup.
 #include "attn_chunk.hpp"
 #include "launch.hpp"
 
 namespace bi {
 namespace {
 
+// Fragments of one chunk of one (sequence, kv head), read from the paged cache.
+// Loads are unconditional: a lane whose key is past `lim` or whose page is
+// outside the pool loads from the pool's first bytes instead.  The fetched
+// words are masked only where they are used (mask()), so no load waits on a
+// branch.  K rows past `lim` need no mask (their scores are masked in the
+// chunk step); V keys past `lim` and keys of invalid pages are zeroed.
+template <int D>
+struct GlobalChunk {
+  const uint16_t* kc;
+  const uint16_t* vc;
+  int64_t head_k;       // elements from a page start to this kv head (K)
+  int64_t head_v;       // same for V
+  int64_t page_elems;   // elements per page (all heads)
+  int log2_ps;
+  int chunk_start;
+  int lim;
+  int page_reg;
+
+  struct Frags {
+    u32x4_t k[2][D / 32];
+    u32x4_t v[D / 16];
+    bool kok;   // this lane's K page is in the pool
+    int vnv;    // keys of this lane's V group that exist (<= 0: none)
+  };
+
+  __device__ __forceinline__ void fetch(int s, Frags& f) const {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    const int ps = 1 << log2_ps;
+    // K rows: key 32 s + 8 (l16 / 4) + 4 b + (l16 % 4); both b share one page.
+    const int kkey0 = kSub * s + 8 * (l16 >> 2);
+    const int kpage = __shfl(page_reg, kkey0 >> log2_ps, kWave);
+    f.kok = kpage >= 0;
+    const int64_t kpg = f.kok ? (int64_t)kpage * page_elems + head_k : 0;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int off = (kkey0 + 4 * b + (l16 & 3)) & (ps - 1);
+      const uint16_t* p = kc + (f.kok ? kpg + (int64_t)off * D + 8 * g : 0);
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) f.k[b][ks] = *reinterpret_cast<const u32x4_t*>(p + 32 * ks);
+    }
+    // V^T rows: head dim 16 dt + l16, keys 32 s + 8 g .. +7 (one page).
+    const int vkey0 = kSub * s + 8 * g;
+    const int vpage = __shfl(page_reg, vkey0 >> log2_ps, kWave);
+    const int pos0 = chunk_start + vkey0;
+    f.vnv = vpage >= 0 ? lim - pos0 : 0;
+    const uint16_t* vp = vc + (vpage >= 0 ? (int64_t)vpage * page_elems + head_v + (int64_t)l16 * ps +
+                                                (pos0 & (ps - 1))
+                                          : 0);
+    const int64_t vstep = vpage >= 0 ? (int64_t)16 * ps : 0;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = *reinterpret_cast<const u32x4_t*>(vp + dt * vstep);
+  }
+
+  __device__ __forceinline__ static void mask(Frags& f) {
+    if (!f.kok) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) f.k[b][ks] = zero4();
+    }
+    if (f.vnv < 8) {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = keep_first(f.v[dt], f.vnv);
+    }
+  }
+};
+
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_partial_kernel(
-    const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    int num_pages, const int32_t* __restrict__ block_table, int max_pages,
-    const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq, int Hkv, int log2_ps,
+    const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table,
+    int max_pages, const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq, int Hkv, int log2_ps,
     float scale_log2, float* __restrict__ ws, int max_chunks) {
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int L = min(seq_lens[b], max_seq_len);
@@ -29,32 +98,49 @@ __global__ __launch_bounds__(64) void attn_decode_partial_kernel(
   const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
   const bool row_ok = n < G;
 
-  u32x4_t qf[D / 32];
+  u32x4_t qf[1][D / 32];
   const uint16_t* qp = q + (int64_t)b * ldq + (h * G + n) * D + 8 * g;
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
-    qf[ks] = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+    qf[0][ks] = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : zero4();
 
-  PagedChunk<D> kv;
-  kv.kc = kc;
-  kv.vc = vc;
-  kv.head = h;
-  kv.num_kv_heads = Hkv;
-  kv.log2_ps = log2_ps;
-  kv.chunk_start = c * kChunk;
-  kv.lim = L;
-  kv.page_reg = load_chunk_pages(block_table + (int64_t)b * max_pages, max_pages, c, log2_ps, L, num_pages);
+  const int ps = 1 << log2_ps;
+  GlobalChunk<D> src;
+  src.kc = kc;
+  src.vc = vc;
+  src.page_elems = (int64_t)Hkv * ps * D;
+  src.head_k = (int64_t)h * ps * D;
+  src.head_v = (int64_t)h * D * ps;
+  src.log2_ps = log2_ps;
+  src.chunk_start = c * kChunk;
+  src.lim = L;
+  src.page_reg = load_chunk_pages(block_table + (int64_t)b * max_pages, max_pages, c, log2_ps, L, num_pages);
 
-  Partial<D> p;
-  chunk_partial<D>(kv, qf, min(kChunk, L - c * kChunk), scale_log2, p);
+  const int nvalid[1] = {min(kChunk, L - c * kChunk)};
+  const int n_sub = (nvalid[0] + kSub - 1) / kSub;
+  ChunkAcc<D, 1> acc;
+  chunk_init(acc);
+  typename GlobalChunk<D>::Frags fa, fb;
+  src.fetch(0, fa);
+#pragma unroll
+  for (int s = 0; s < kSubs; s += 2) {
+    if (s >= n_sub) break;
+    if (s + 1 < n_sub) src.fetch(s + 1, fb);
+    GlobalChunk<D>::mask(fa);
+    chunk_step<D, 1>(acc, fa.k, fa.v, qf, nvalid, s, scale_log2);
+    if (s + 1 >= n_sub) break;
+    if (s + 2 < n_sub) src.fetch(s + 2, fa);
+    GlobalChunk<D>::mask(fb);
+    chunk_step<D, 1>(acc, fb.k, fb.v, qf, nvalid, s + 1, scale_log2);
+  }
 
   if (row_ok) {
     float* rec = ws + (((int64_t)b * Hq + h * G + n) * max_chunks + c) * (D + 4);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = p.o[dt];
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = acc.o[0][dt];
     if (g == 0) {
-      rec[D] = p.m;
-      rec[D + 1] = p.l;
+      rec[D] = acc.m[0];
+      rec[D + 1] = acc.l[0];
     }
   }
 }
@@ -96,30 +182,27 @@ hipError_t launch(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t*
                   int max_seq_len, void* out, float* lse, void* workspace, hipStream_t stream) {
   const int max_chunks = (max_seq_len + kChunk - 1) / kChunk;
   float* ws = static_cast<float*>(workspace);
-  hipLaunchKernelGGL(attn_decode_partial_kernel<D>,
-                     dim3(max_chunks, g.num_kv_heads, num_seqs), dim3(64), 0, stream,
-                     static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(g.k_cache),
-                     static_cast<const uint16_t*>(g.v_cache), g.num_pages, g.block_table,
-                     g.max_pages_per_seq, seq_lens, max_seq_len, g.num_q_heads, g.num_kv_heads,
-                     g.log2_page, g.scale_log2, ws, max_chunks);
+  hipLaunchKernelGGL(attn_decode_partial_kernel<D>, dim3(max_chunks, g.num_kv_heads, num_seqs), dim3(64), 0,
+                     stream, static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(g.k_cache),
+                     static_cast<const uint16_t*>(g.v_cache), g.num_pages, g.block_table, g.max_pages_per_seq,
+                     seq_lens, max_seq_len, g.num_q_heads, g.num_kv_heads, g.log2_page, g.scale_log2, ws,
+                     max_chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(64), 0, stream,
-                     ws, seq_lens, max_seq_len, g.num_q_heads, max_chunks,
-                     static_cast<uint16_t*>(out), lse);
+  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(64), 0, stream, ws,
+                     seq_lens, max_seq_len, g.num_q_heads, max_chunks, static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_decode(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
-                              int max_seq_len, void* out, float* lse, void* workspace,
+hipError_t launch_attn_decode(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t* seq_lens,
+                              int num_seqs, int max_seq_len, void* out, float* lse, void* workspace,
                               hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
   if (max_seq_len <= 0) max_seq_len = 1;  // grid of one empty chunk; merge writes the L <= 0 result
-  return g.head_dim == 64
-             ? launch<64>(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace, stream)
-             : launch<128>(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace, stream);
+  return g.head_dim == 64 ? launch<64>(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace, stream)
+                          : launch<128>(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace, stream);
 }
 
 }  // namespace bi

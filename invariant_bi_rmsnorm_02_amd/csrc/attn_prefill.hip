@@ -4,94 +4,207 @@
 // Cache"; "Como superar a não determinismo na inferência de LLMs", Attention:
 // one K/V layout for cached and new tokens).
 //
-// Parallel over query rows (FlashAttention-2 style): a workgroup owns 64
-// (token, q head) rows of one sequence and one kv head, 16 rows per wavefront.
-// The chunk's own keys/values are already in the paged cache, so cached and new
-// tokens are read through one path.  Each wavefront walks the 256-key chunks in
-// ascending order, calls the same chunk routine as decode (causal mask: a query
-// at position p sees keys 0..p) and folds every chunk its row can see with the
-// same merge step, so row p is bitwise what decode returns at seq_len p + 1.
+// Parallel over query rows (FlashAttention-2 style): a workgroup owns 128
+// (token, q head) rows of one sequence and one kv head - four wavefronts of two
+// 16-row column blocks.  The chunk's own keys/values are already in the paged
+// cache, so cached and new tokens are read through one path.  The workgroup
+// walks the 256-key chunks in ascending order, 32 keys at a time: each K/V
+// sub-block is staged once into LDS (double-buffered, the next one loading from
+// HBM while the current one is used) and every wavefront runs the same chunk
+// step as decode on it (causal mask: a query at position p sees keys 0..p).
+// After a chunk each column folds it with the same merge step as decode, so row
+// p is bitwise what decode returns at seq_len p + 1.
 #include "attn_chunk.hpp"
 #include "launch.hpp"
 
 namespace bi {
 namespace {
 
-constexpr int kRowsPerWave = 16;
 constexpr int kWaves = 4;
+constexpr int kNB = 2;                              // 16-row column blocks per wavefront
+constexpr int kRowsPerWave = 16 * kNB;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
+constexpr int kThreads = kWaves * 64;
+
+// LDS layouts of one staged sub-block (bf16 elements):
+//   K: [32 keys][D], 16-byte chunk ch of key row r at (ch ^ k_swz(r)) so the 8
+//      rows one MFMA-fragment read touches per LDS cycle hit distinct banks;
+//   V^T: [D][32 keys], 8-key group grp of dim row d at (grp ^ v_swz(d)).
+__device__ __forceinline__ int k_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+__device__ __forceinline__ int v_swz(int d) { return (d >> 2) & 3; }
+template <int D>
+__device__ __forceinline__ int k_lds(int r, int ch) { return r * D + ((ch ^ k_swz(r)) << 3); }
+__device__ __forceinline__ int v_lds(int d, int grp) { return d * kSub + ((grp ^ v_swz(d)) << 3); }
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(
+__global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const int32_t* __restrict__ q_start,
     const int32_t* __restrict__ ctx_lens, int max_q_len, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table,
-    int max_pages, int Hq, int Hkv, int log2_ps, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table, int max_pages,
+    int Hq, int Hkv, int log2_ps, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int KP = kSub * D / 8 / kThreads;   // 16-byte K pieces per thread per sub-block
+  constexpr int VP = D * (kSub / 8) / kThreads; // 16-byte V pieces per thread per sub-block
+  static_assert(KP >= 1 && VP >= 1, "staging split");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kSub * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * kSub];
+
   const int tile = blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int G = Hq / Hkv;
   const int qs = q_start[sq];
   const int nq = min(q_start[sq + 1] - qs, max_q_len);
   const int ctx = ctx_lens[sq];
   const int rows = nq * G;
-  const int row0 = tile * kRowsPerBlock + wave * kRowsPerWave;
-  if (nq <= 0 || ctx < 0 || row0 >= rows) return;  // no barrier in this kernel: early exit is safe
-  const int rho = row0 + n;
-  const bool row_ok = rho < rows;
-  const int tok = rho / G, hh = rho - (rho / G) * G;
-  const int pos = ctx + tok;
-  const int last = min(row0 + kRowsPerWave, rows) - 1;  // last real row of the wave
-  const int lim = ctx + last / G + 1;                     // keys at >= lim no row can see
+  const int row0 = tile * kRowsPerBlock;
+  // Uniform over the workgroup, before any barrier.
+  if (nq <= 0 || ctx < 0 || row0 >= rows) return;
+  const int lim = ctx + (min(row0 + kRowsPerBlock, rows) - 1) / G + 1;   // keys >= lim: no row sees them
+  const int wrow0 = row0 + wave * kRowsPerWave;
+  const int wave_lim = wrow0 < rows ? ctx + (min(wrow0 + kRowsPerWave, rows) - 1) / G + 1 : 0;
 
-  u32x4_t qf[D / 32];
-  const uint16_t* qp = q + (int64_t)(qs + tok) * ldq + (h * G + hh) * D + 8 * g;
+  int pos[kNB];
+  bool row_ok[kNB];
+  u32x4_t qf[kNB][D / 32];
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    qf[ks] = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
-
-  PagedChunk<D> kv;
-  kv.kc = kc;
-  kv.vc = vc;
-  kv.head = h;
-  kv.num_kv_heads = Hkv;
-  kv.log2_ps = log2_ps;
-  kv.lim = lim;
-  const int32_t* bt = block_table + (int64_t)sq * max_pages;
-
-  float m = -INFINITY, l = 0.0f;
-  f32x4_t acc[D / 16];
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int rho = wrow0 + 16 * nb + n;
+    row_ok[nb] = rho < rows;
+    const int tok = rho / G, hh = rho - tok * G;
+    pos[nb] = ctx + tok;
+    const uint16_t* qp = q + (int64_t)(qs + tok) * ldq + (h * G + hh) * D + 8 * g;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nch = (lim + kChunk - 1) / kChunk;
-  for (int c = 0; c < nch; ++c) {
-    kv.chunk_start = c * kChunk;
-    kv.page_reg = load_chunk_pages(bt, max_pages, c, log2_ps, lim, num_pages);
-    const int nv = row_ok ? max(0, min(kChunk, pos + 1 - c * kChunk)) : 0;
-    Partial<D> p;
-    chunk_partial<D>(kv, qf, nv, scale_log2, p);
-    if (nv > 0) {
-      const MergeCoef k = merge_coef(m, p.m);
-      l = merge_val(l, p.l, k);
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[dt][i] = merge_val(acc[dt][i], p.o[dt][i], k);
-      m = k.m;
-    }
+    for (int ks = 0; ks < D / 32; ++ks)
+      qf[nb][ks] = row_ok[nb] ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : zero4();
   }
 
-  if (row_ok) {
+  const int ps = 1 << log2_ps;
+  const int64_t page_elems = (int64_t)Hkv * ps * D;
+  const int32_t* bt = block_table + (int64_t)sq * max_pages;
+  auto page_at = [&](int p) -> int {   // physical page holding position p, or -1
+    const int lp = p >> log2_ps;
+    if (p >= lim || lp >= max_pages) return -1;
+    const int pg = bt[lp];
+    return (pg >= 0 && pg < num_pages) ? pg : -1;
+  };
+
+  // Global -> register staging of sub-block u (chunk u / 8, sub-block u % 8).
+  u32x4_t rk[KP], rv[VP];
+  auto load_sub = [&](int u) {
+    const int base = (u >> 3) * kChunk + (u & 7) * kSub;
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int pc = tid + i * kThreads, r = pc / (D / 8), ch = pc % (D / 8);
+      const int p = base + r;
+      const int pg = page_at(p);
+      const uint16_t* src = pg >= 0 ? kc + (int64_t)pg * page_elems + (int64_t)h * ps * D +
+                                          (int64_t)(p & (ps - 1)) * D + ch * 8
+                                    : kc;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src);
+      rk[i] = pg >= 0 ? v : zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const int pc = tid + i * kThreads, d = pc / (kSub / 8), grp = pc % (kSub / 8);
+      const int p0 = base + 8 * grp;
+      const int pg = page_at(p0);
+      const uint16_t* src = pg >= 0 ? vc + (int64_t)pg * page_elems + (int64_t)h * D * ps + (int64_t)d * ps +
+                                          (p0 & (ps - 1))
+                                    : vc;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src);
+      rv[i] = pg >= 0 ? keep_first(v, lim - p0) : zero4();
+    }
+  };
+  auto store_sub = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int pc = tid + i * kThreads, r = pc / (D / 8), ch = pc % (D / 8);
+      *reinterpret_cast<u32x4_t*>(&sK[buf][k_lds<D>(r, ch)]) = rk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const int pc = tid + i * kThreads, d = pc / (kSub / 8), grp = pc % (kSub / 8);
+      *reinterpret_cast<u32x4_t*>(&sV[buf][v_lds(d, grp)]) = rv[i];
+    }
+  };
+
+  // Running state of the fold over chunks (per column block).
+  float m_run[kNB], l_run[kNB];
+  f32x4_t o_run[kNB][D / 16];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    m_run[nb] = -INFINITY;
+    l_run[nb] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o_run[nb][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nch = (lim + kChunk - 1) / kChunk;
+  const int last_subs = (lim - (nch - 1) * kChunk + kSub - 1) / kSub;
+  const int U = (nch - 1) * kSubs + last_subs;
+
+  ChunkAcc<D, kNB> ca;
+  int nvalid[kNB];
+  load_sub(0);
+  store_sub(0);
+  __syncthreads();
+  for (int u = 0; u < U; ++u) {
+    const int c = u >> 3, s = u & 7;
+    if (s == 0) {
+      chunk_init(ca);
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+        nvalid[nb] = row_ok[nb] ? max(0, min(kChunk, pos[nb] + 1 - c * kChunk)) : 0;
+    }
+    if (u + 1 < U) load_sub(u + 1);
+    if (c * kChunk + s * kSub < wave_lim) {   // some column of this wave sees a key here
+      const int buf = u & 1;
+      const int l16 = n;
+      u32x4_t kf[2][D / 32], vf[D / 16];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int r = sub_key_of_row(l16, b);
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+          kf[b][ks] = *reinterpret_cast<const u32x4_t*>(&sK[buf][k_lds<D>(r, 4 * ks + g)]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        vf[dt] = *reinterpret_cast<const u32x4_t*>(&sV[buf][v_lds(16 * dt + l16, g)]);
+      chunk_step<D, kNB>(ca, kf, vf, qf, nvalid, s, scale_log2);
+    }
+    const bool chunk_end = (s == kSubs - 1) || (u == U - 1);
+    if (chunk_end) {
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        if (nvalid[nb] > 0) {
+          const MergeCoef k = merge_coef(m_run[nb], ca.m[nb]);
+          l_run[nb] = merge_val(l_run[nb], ca.l[nb], k);
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o_run[nb][dt][i] = merge_val(o_run[nb][dt][i], ca.o[nb][dt][i], k);
+          m_run[nb] = k.m;
+        }
+      }
+    }
+    if (u + 1 < U) store_sub((u + 1) & 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    if (!row_ok[nb]) continue;
+    const int rho = wrow0 + 16 * nb + n;
+    const int tok = rho / G, hh = rho - tok * G;
     uint16_t* op = out + ((int64_t)(qs + tok) * Hq + h * G + hh) * D + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const f32x4_t a = acc[dt];
+      const f32x4_t a = o_run[nb][dt];
       *reinterpret_cast<u32x2_t*>(op + 16 * dt) =
-          u32x2_t{pack_bf16x2(finalize_val(a[0], l), finalize_val(a[1], l)),
-                  pack_bf16x2(finalize_val(a[2], l), finalize_val(a[3], l))};
+          u32x2_t{pack_bf16x2(finalize_val(a[0], l_run[nb]), finalize_val(a[1], l_run[nb])),
+                  pack_bf16x2(finalize_val(a[2], l_run[nb]), finalize_val(a[3], l_run[nb]))};
     }
-    if (lse != nullptr && g == 0) lse[(int64_t)(qs + tok) * Hq + h * G + hh] = finalize_lse(m, l);
+    if (lse != nullptr && g == 0) lse[(int64_t)(qs + tok) * Hq + h * G + hh] = finalize_lse(m_run[nb], l_run[nb]);
   }
 }
 
@@ -100,8 +213,8 @@ hipError_t launch(const void* q, int64_t ld_q, const int32_t* q_start, const int
                   int max_q_len, const AttnGeom& g, void* out, float* lse, hipStream_t stream) {
   const int G = g.num_q_heads / g.num_kv_heads;
   const int tiles = (max_q_len * G + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(tiles, g.num_kv_heads, num_seqs), dim3(kWaves * 64),
-                     0, stream, static_cast<const uint16_t*>(q), ld_q, q_start, ctx_lens, max_q_len,
+  hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(tiles, g.num_kv_heads, num_seqs), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), ld_q, q_start, ctx_lens, max_q_len,
                      static_cast<const uint16_t*>(g.k_cache), static_cast<const uint16_t*>(g.v_cache),
                      g.num_pages, g.block_table, g.max_pages_per_seq, g.num_q_heads, g.num_kv_heads,
                      g.log2_page, g.scale_log2, static_cast<uint16_t*>(out), lse);
