@@ -91,13 +91,22 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw,
                   int64_t m, int64_t n, int64_t k, bi_stream_t stream);
 
 /*
- * Paged KV cache layout (one pool per layer; page = `page_size` tokens):
- *   k_cache: [num_pages][num_kv_heads][page_size][head_dim] bf16 (token-major)
- *   v_cache: [num_pages][num_kv_heads][head_dim][page_size] bf16 (dim-major)
- * Token t of a sequence lives in page block_table[seq][t / page_size] at offset
- * t % page_size.  Cached and newly appended tokens share this one layout
- * ([HADA] Attention: keep a consistent K/V layout; [TML] fig. "FlashAttention
- * with KV Cache").
+ * Paged KV cache layout (one pool per layer; page = `page_size` tokens, a
+ * multiple of 16).  Both caches are [num_pages][num_kv_heads][page block] bf16;
+ * a page block holds page_size / 16 tiles of 16 tokens, one after the other,
+ * and a tile holds 16 * head_dim elements laid out so that the attention
+ * kernels read every matrix-core operand as whole, contiguous 128-byte lines:
+ *   K tile: element (token j, dim d) at (d / 8) * 128 + slot(j) * 8 + d % 8,
+ *           slot(j) = 8 * ((j / 4) % 2) + 4 * (j / 8) + j % 4
+ *           (tokens 0-3, 8-11 fill the first 128 bytes of each 8-dim group,
+ *           tokens 4-7, 12-15 the second);
+ *   V tile: element (token j, dim d) at (d / 16) * 256 + (j / 8) * 128
+ *           + (d % 16) * 8 + j % 8.
+ * Token t of a sequence lives in page block_table[seq][t / page_size], tile
+ * (t % page_size) / 16, token t % 16 of that tile.  Cached and newly appended
+ * tokens share this one layout ([HADA] Attention: keep a consistent K/V
+ * layout; [TML] fig. "FlashAttention with KV Cache").  Only the library's own
+ * kernels write it (bi_kv_append).
  */
 
 /*
@@ -108,7 +117,7 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw,
  * slot_mapping: [num_tokens] int32, slot = page * page_size + offset; a negative
  * slot or one >= num_pages * page_size skips that token (padding).
  * A pure copy: every cache element is written bit-exactly.
- * head_dim in {64, 128}; page_size in {8, 16, 32, 64, 128, 256} (divides 256).
+ * head_dim in {64, 128}; page_size in {16, 32, 64, 128, 256}.
  */
 bi_status bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new, const int32_t* slot_mapping,
                        int32_t num_tokens, void* k_cache, void* v_cache, int32_t num_pages,
@@ -145,7 +154,7 @@ size_t bi_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
  * A sequence with seq_len <= 0 gets out = 0 and lse = -inf.
  * workspace: >= bi_attn_decode_workspace_bytes(...) bytes of device memory.
  * head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 and the group size
- * num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}; page_size divides 256.
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}; page_size in {16, 32, 64, 128, 256}.
  */
 bi_status bi_attn_decode(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache, int32_t num_pages,
                          const int32_t* block_table, int32_t max_pages_per_seq,

@@ -147,9 +147,11 @@ def bi_gemm(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None
 
 def alloc_kv_cache(num_pages: int, num_kv_heads: int, head_dim: int, page_size: int = 16,
                    device="cuda", fill: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """K cache [pages, Hkv, PS, D] and V cache [pages, Hkv, D, PS] (bf16)."""
+    """K and V caches, each [pages, Hkv, page_size, D] bf16.  The shape only
+    sizes the storage: inside a (page, head) block the elements follow the
+    tiled order documented in include/bi.h, written by bi_kv_append."""
     k = torch.empty((num_pages, num_kv_heads, page_size, head_dim), dtype=torch.bfloat16, device=device)
-    v = torch.empty((num_pages, num_kv_heads, head_dim, page_size), dtype=torch.bfloat16, device=device)
+    v = torch.empty((num_pages, num_kv_heads, page_size, head_dim), dtype=torch.bfloat16, device=device)
     if fill is not None:
         k.fill_(fill)
         v.fill_(fill)
@@ -162,8 +164,8 @@ def _cache_geom(k_cache: torch.Tensor, v_cache: torch.Tensor):
     if k_cache.dim() != 4 or not k_cache.is_contiguous() or not v_cache.is_contiguous():
         raise ValueError("caches must be contiguous 4-D tensors")
     pages, hkv, ps, d = k_cache.shape
-    if tuple(v_cache.shape) != (pages, hkv, d, ps):
-        raise ValueError("v_cache must be [pages, Hkv, D, page_size]")
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [pages, Hkv, page_size, D]")
     return pages, hkv, ps, d
 
 

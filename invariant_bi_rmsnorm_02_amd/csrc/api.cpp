@@ -39,7 +39,7 @@ bi_status check_attn_geom(const void* k_cache, const void* v_cache, int32_t num_
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return BI_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return BI_ERR_UNSUPPORTED;
   const int l2 = log2_exact(page_size);
-  if (l2 < 3 || l2 > 8) return BI_ERR_UNSUPPORTED;  // 8 .. 256 tokens, divides the 256-token chunk
+  if (l2 < 4 || l2 > 8) return BI_ERR_UNSUPPORTED;  // 16 .. 256 tokens: whole 16-token tiles, divides the chunk
   return BI_OK;
 }
 
@@ -120,7 +120,7 @@ bi_status bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new, con
   if (num_pages <= 0 || num_kv_heads <= 0) return BI_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return BI_ERR_UNSUPPORTED;
   const int l2 = log2_exact(page_size);
-  if (l2 < 3 || l2 > 8) return BI_ERR_UNSUPPORTED;
+  if (l2 < 4 || l2 > 8) return BI_ERR_UNSUPPORTED;
   if ((int64_t)num_pages * page_size > 0x7fffffff) return BI_ERR_UNSUPPORTED;
   if (ld_new < (int64_t)num_kv_heads * head_dim || ld_new % 8) return BI_ERR_INVALID_ARG;
   return from_hip(bi::launch_kv_append(k_new, v_new, ld_new, slot_mapping, num_tokens, k_cache, v_cache,

@@ -65,14 +65,22 @@ __device__ __forceinline__ void chunk_init(ChunkAcc<D, NB>& a) {
   }
 }
 
-// One 32-key sub-block s of the chunk.  kf: S^T A operands [block b][step ks];
-// vf: O^T A operands [dim tile dt]; qf: Q^T B operands [n-block][step ks];
-// n_valid[nb]: keys of the chunk column (lane % 16) of n-block nb may see
-// (keys 0 .. n_valid - 1 relative to the chunk start).
+// One 32-key sub-block s of the chunk, in two halves so that a kernel can
+// bring in V between them: chunk_scores (S = K Q^T, online max and sum, the
+// bf16 probabilities) and chunk_values (O = O * alpha + V^T P^T).
+// kf: S^T A operands [block b][step ks]; vf: O^T A operands [dim tile dt];
+// qf: Q^T B operands [n-block][step ks]; n_valid[nb]: keys of the chunk that
+// column (lane % 16) of n-block nb may see (keys 0 .. n_valid - 1).
+template <int NB>
+struct SubProbs {
+  u32x4_t pb[NB];   // bf16 p of the lane's 8 keys (MFMA B operand of O^T)
+  float alpha[NB];  // rescale of the previous (l, o)
+};
+
 template <int D, int NB>
-__device__ __forceinline__ void chunk_step(ChunkAcc<D, NB>& a, const u32x4_t (&kf)[2][D / 32],
-                                           const u32x4_t (&vf)[D / 16], const u32x4_t (&qf)[NB][D / 32],
-                                           const int (&n_valid)[NB], int s, float scale_log2) {
+__device__ __forceinline__ void chunk_scores(ChunkAcc<D, NB>& a, const u32x4_t (&kf)[2][D / 32],
+                                             const u32x4_t (&qf)[NB][D / 32], const int (&n_valid)[NB], int s,
+                                             float scale_log2, SubProbs<NB>& sp) {
   const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -108,15 +116,25 @@ __device__ __forceinline__ void chunk_step(ChunkAcc<D, NB>& a, const u32x4_t (&k
     ls = ls + shfl_xor(ls, 16);
     ls = ls + shfl_xor(ls, 32);
     a.l[nb] = a.l[nb] * alpha + ls;
-    const u32x4_t pb = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                               pack_bf16x2(p[6], p[7])};
+    a.m[nb] = mn;
+    sp.alpha[nb] = alpha;
+    sp.pb[nb] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                        pack_bf16x2(p[6], p[7])};
+  }
+}
+
+template <int D, int NB>
+__device__ __forceinline__ void chunk_values(ChunkAcc<D, NB>& a, const u32x4_t (&vf)[D / 16],
+                                             const SubProbs<NB>& sp) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float alpha = sp.alpha[nb];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       f32x4_t o = a.o[nb][dt];
       o = f32x4_t{o[0] * alpha, o[1] * alpha, o[2] * alpha, o[3] * alpha};
-      a.o[nb][dt] = mfma_16x16x32(vf[dt], pb, o);
+      a.o[nb][dt] = mfma_16x16x32(vf[dt], sp.pb[nb], o);
     }
-    a.m[nb] = mn;
   }
 }
 
@@ -158,15 +176,20 @@ __device__ __forceinline__ int load_chunk_pages(const int32_t* bt_row, int max_p
 
 __device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 
-// Keep bf16 elements 0 .. nv-1 of an 8-element fragment, zero the rest.
-__device__ __forceinline__ u32x4_t keep_first(u32x4_t v, int nv) {
+// Word masks keeping bf16 elements 0 .. nv-1 of an 8-element fragment.
+struct KeepMask {
+  uint32_t w[4];
+};
+__device__ __forceinline__ KeepMask keep_mask(int nv) {
+  KeepMask k;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t lo = (2 * e < nv) ? 0x0000ffffu : 0u;
-    const uint32_t hi = (2 * e + 1 < nv) ? 0xffff0000u : 0u;
-    v[e] &= (lo | hi);
-  }
-  return v;
+  for (int e = 0; e < 4; ++e)
+    k.w[e] = ((2 * e < nv) ? 0x0000ffffu : 0u) | ((2 * e + 1 < nv) ? 0xffff0000u : 0u);
+  return k;
 }
+__device__ __forceinline__ u32x4_t apply_keep(u32x4_t v, const KeepMask& k) {
+  return u32x4_t{v[0] & k.w[0], v[1] & k.w[1], v[2] & k.w[2], v[3] & k.w[3]};
+}
+__device__ __forceinline__ u32x4_t keep_first(u32x4_t v, int nv) { return apply_keep(v, keep_mask(nv)); }
 
 }  // namespace bi

@@ -13,14 +13,18 @@
 // normalisation and bf16 output.  No atomics, no cross-workgroup ordering:
 // every value is written by exactly one workgroup.
 #include "attn_chunk.hpp"
+#include "kv_layout.hpp"
 #include "launch.hpp"
 
 namespace bi {
 namespace {
 
-// Fragments of one chunk of one (sequence, kv head), read from the paged cache.
-// Loads are unconditional: a lane whose key is past `lim` or whose page is
-// outside the pool loads from the pool's first bytes instead.  The fetched
+// Fragments of one chunk of one (sequence, kv head), read from the paged cache
+// (tiled layout of kv_layout.hpp: each 16-byte operand load of a wavefront
+// covers whole 128-byte lines).  Every K/V byte is read once, so loads carry
+// the non-temporal hint.  Loads
+// are unconditional: a lane whose key is past `lim` or whose page is outside
+// the pool loads from the pool's first bytes instead.  The fetched
 // words are masked only where they are used (mask()), so no load waits on a
 // branch.  K rows past `lim` need no mask (their scores are masked in the
 // chunk step); V keys past `lim` and keys of invalid pages are zeroed.
@@ -28,9 +32,9 @@ template <int D>
 struct GlobalChunk {
   const uint16_t* kc;
   const uint16_t* vc;
-  int64_t head_k;       // elements from a page start to this kv head (K)
+  int64_t head_k;       // elements from a page start to this kv head's block
   int64_t head_v;       // same for V
-  int64_t page_elems;   // elements per page (all heads)
+  int num_kv_heads;
   int log2_ps;
   int chunk_start;
   int lim;
@@ -43,45 +47,52 @@ struct GlobalChunk {
     int vnv;    // keys of this lane's V group that exist (<= 0: none)
   };
 
-  __device__ __forceinline__ void fetch(int s, Frags& f) const {
+  // active == false points every load at the pool's first bytes (the result
+  // is never used): the loads are still issued so that every path through the
+  // caller's loop has the same loads in flight.
+  __device__ __forceinline__ void fetch(int s, Frags& f, bool active) const {
     const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
     const int ps = 1 << log2_ps;
-    // K rows: key 32 s + 8 (l16 / 4) + 4 b + (l16 % 4); both b share one page.
-    const int kkey0 = kSub * s + 8 * (l16 >> 2);
-    const int kpage = __shfl(page_reg, kkey0 >> log2_ps, kWave);
-    f.kok = kpage >= 0;
-    const int64_t kpg = f.kok ? (int64_t)kpage * page_elems + head_k : 0;
+    // K: lanes l16 < 8 read tile 0 of the sub-block, l16 >= 8 tile 1; in both,
+    // the 8 lanes of a group cover 128 contiguous bytes (slots 8 b .. 8 b + 7).
+    const int ktile_key = kSub * s + kTile * (l16 >> 3);       // key of the tile's token 0
+    const int kpage = __shfl(page_reg, ktile_key >> log2_ps, kWave);
+    f.kok = active && kpage >= 0;
+    const int64_t kb = f.kok ? tile_base(kpage, 0, ktile_key & (ps - 1), num_kv_heads, log2_ps, D) + head_k +
+                                   (int64_t)g * 128 + (l16 & 7) * 8
+                             : 0;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int off = (kkey0 + 4 * b + (l16 & 3)) & (ps - 1);
-      const uint16_t* p = kc + (f.kok ? kpg + (int64_t)off * D + 8 * g : 0);
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) f.k[b][ks] = *reinterpret_cast<const u32x4_t*>(p + 32 * ks);
-    }
-    // V^T rows: head dim 16 dt + l16, keys 32 s + 8 g .. +7 (one page).
-    const int vkey0 = kSub * s + 8 * g;
-    const int vpage = __shfl(page_reg, vkey0 >> log2_ps, kWave);
-    const int pos0 = chunk_start + vkey0;
-    f.vnv = vpage >= 0 ? lim - pos0 : 0;
-    const uint16_t* vp = vc + (vpage >= 0 ? (int64_t)vpage * page_elems + head_v + (int64_t)l16 * ps +
-                                                (pos0 & (ps - 1))
-                                          : 0);
-    const int64_t vstep = vpage >= 0 ? (int64_t)16 * ps : 0;
+      for (int ks = 0; ks < D / 32; ++ks)
+        f.k[b][ks] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(kc + kb + (f.kok ? 4 * ks * 128 + 8 * b * 8 : 0)));
+    // V: lane group g holds keys 8 g .. 8 g + 7 of the sub-block = tile g / 2,
+    // half g % 2; the 16 lanes of a group cover 256 contiguous bytes.
+    const int vtile_key = kSub * s + kTile * (g >> 1);
+    const int vpage = __shfl(page_reg, vtile_key >> log2_ps, kWave);
+    const bool vok = active && vpage >= 0;
+    f.vnv = vok ? lim - (chunk_start + kSub * s + 8 * g) : 0;
+    const int64_t vb = vok ? tile_base(vpage, 0, vtile_key & (ps - 1), num_kv_heads, log2_ps, D) + head_v +
+                                 (g & 1) * 128 + l16 * 8
+                           : 0;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = *reinterpret_cast<const u32x4_t*>(vp + dt * vstep);
+    for (int dt = 0; dt < D / 16; ++dt)
+      f.v[dt] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vc + vb + (vok ? dt * 256 : 0)));
   }
 
-  __device__ __forceinline__ static void mask(Frags& f) {
-    if (!f.kok) {
+  // Branch-free masking, applied right where each half is consumed so the
+  // wait for a fragment never covers the loads of the next sub-block.
+  __device__ __forceinline__ static void mask_k(Frags& f) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) f.k[b][ks] = zero4();
-    }
-    if (f.vnv < 8) {
+      for (int ks = 0; ks < D / 32; ++ks) f.k[b][ks] = f.kok ? f.k[b][ks] : zero4();
+  }
+  __device__ __forceinline__ static void mask_v(Frags& f) {
+    const KeepMask km = keep_mask(f.vnv);
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = keep_first(f.v[dt], f.vnv);
-    }
+    for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = apply_keep(f.v[dt], km);
   }
 };
 
@@ -108,9 +119,9 @@ __global__ __launch_bounds__(64) void attn_decode_partial_kernel(
   GlobalChunk<D> src;
   src.kc = kc;
   src.vc = vc;
-  src.page_elems = (int64_t)Hkv * ps * D;
   src.head_k = (int64_t)h * ps * D;
-  src.head_v = (int64_t)h * D * ps;
+  src.head_v = (int64_t)h * ps * D;
+  src.num_kv_heads = Hkv;
   src.log2_ps = log2_ps;
   src.chunk_start = c * kChunk;
   src.lim = L;
@@ -120,18 +131,26 @@ __global__ __launch_bounds__(64) void attn_decode_partial_kernel(
   const int n_sub = (nvalid[0] + kSub - 1) / kSub;
   ChunkAcc<D, 1> acc;
   chunk_init(acc);
-  typename GlobalChunk<D>::Frags fa, fb;
-  src.fetch(0, fa);
+  // Ping-pong over sub-blocks: the loads of sub-block s + 1 are always in
+  // flight while sub-block s is computed.
+  using Src = GlobalChunk<D>;
+  typename Src::Frags fa, fb;
+  SubProbs<1> sp;
+  src.fetch(0, fa, true);
 #pragma unroll
   for (int s = 0; s < kSubs; s += 2) {
-    if (s >= n_sub) break;
-    if (s + 1 < n_sub) src.fetch(s + 1, fb);
-    GlobalChunk<D>::mask(fa);
-    chunk_step<D, 1>(acc, fa.k, fa.v, qf, nvalid, s, scale_log2);
+    src.fetch(s + 1, fb, s + 1 < n_sub);
+    Src::mask_k(fa);
+    chunk_scores<D, 1>(acc, fa.k, qf, nvalid, s, scale_log2, sp);
+    Src::mask_v(fa);
+    chunk_values<D, 1>(acc, fa.v, sp);
     if (s + 1 >= n_sub) break;
-    if (s + 2 < n_sub) src.fetch(s + 2, fa);
-    GlobalChunk<D>::mask(fb);
-    chunk_step<D, 1>(acc, fb.k, fb.v, qf, nvalid, s + 1, scale_log2);
+    src.fetch(s + 2, fa, s + 2 < n_sub);
+    Src::mask_k(fb);
+    chunk_scores<D, 1>(acc, fb.k, qf, nvalid, s + 1, scale_log2, sp);
+    Src::mask_v(fb);
+    chunk_values<D, 1>(acc, fb.v, sp);
+    if (s + 2 >= n_sub) break;
   }
 
   if (row_ok) {

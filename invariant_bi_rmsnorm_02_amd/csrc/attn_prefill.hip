@@ -15,6 +15,7 @@
 // After a chunk each column folds it with the same merge step as decode, so row
 // p is bitwise what decode returns at seq_len p + 1.
 #include "attn_chunk.hpp"
+#include "kv_layout.hpp"
 #include "launch.hpp"
 
 namespace bi {
@@ -26,15 +27,10 @@ constexpr int kRowsPerWave = 16 * kNB;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 constexpr int kThreads = kWaves * 64;
 
-// LDS layouts of one staged sub-block (bf16 elements):
-//   K: [32 keys][D], 16-byte chunk ch of key row r at (ch ^ k_swz(r)) so the 8
-//      rows one MFMA-fragment read touches per LDS cycle hit distinct banks;
-//   V^T: [D][32 keys], 8-key group grp of dim row d at (grp ^ v_swz(d)).
-__device__ __forceinline__ int k_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
-__device__ __forceinline__ int v_swz(int d) { return (d >> 2) & 3; }
-template <int D>
-__device__ __forceinline__ int k_lds(int r, int ch) { return r * D + ((ch ^ k_swz(r)) << 3); }
-__device__ __forceinline__ int v_lds(int d, int grp) { return d * kSub + ((grp ^ v_swz(d)) << 3); }
+// LDS holds one staged 32-key sub-block as its two 16-token tiles, in the same
+// tiled order as the cache (kv_layout.hpp), so staging is a straight copy of
+// contiguous 16-byte pieces and every fragment read is a run of contiguous
+// 16-byte LDS words (128 bytes per 8 lanes for K, 256 bytes per 16 lanes for V).
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
@@ -42,11 +38,11 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
     const int32_t* __restrict__ ctx_lens, int max_q_len, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table, int max_pages,
     int Hq, int Hkv, int log2_ps, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int KP = kSub * D / 8 / kThreads;   // 16-byte K pieces per thread per sub-block
-  constexpr int VP = D * (kSub / 8) / kThreads; // 16-byte V pieces per thread per sub-block
-  static_assert(KP >= 1 && VP >= 1, "staging split");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kSub * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * kSub];
+  constexpr int TE = kTile * D;                 // elements per tile
+  constexpr int NP = 2 * TE / 8 / kThreads;     // 16-byte pieces per thread per sub-block (K and V each)
+  static_assert(NP >= 1 && (2 * TE / 8) % kThreads == 0, "staging split");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][2 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][2 * TE];
 
   const int tile = blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
@@ -78,7 +74,6 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
   }
 
   const int ps = 1 << log2_ps;
-  const int64_t page_elems = (int64_t)Hkv * ps * D;
   const int32_t* bt = block_table + (int64_t)sq * max_pages;
   auto page_at = [&](int p) -> int {   // physical page holding position p, or -1
     const int lp = p >> log2_ps;
@@ -87,43 +82,32 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
     return (pg >= 0 && pg < num_pages) ? pg : -1;
   };
 
-  // Global -> register staging of sub-block u (chunk u / 8, sub-block u % 8).
-  u32x4_t rk[KP], rv[VP];
+  // Global -> register staging of sub-block u (chunk u / 8, sub-block u % 8):
+  // piece pc covers elements 8 pc .. 8 pc + 7 of the sub-block's two tiles.
+  u32x4_t rk[NP], rv[NP];
   auto load_sub = [&](int u) {
     const int base = (u >> 3) * kChunk + (u & 7) * kSub;
 #pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      const int pc = tid + i * kThreads, r = pc / (D / 8), ch = pc % (D / 8);
-      const int p = base + r;
-      const int pg = page_at(p);
-      const uint16_t* src = pg >= 0 ? kc + (int64_t)pg * page_elems + (int64_t)h * ps * D +
-                                          (int64_t)(p & (ps - 1)) * D + ch * 8
-                                    : kc;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src);
-      rk[i] = pg >= 0 ? v : zero4();
-    }
-#pragma unroll
-    for (int i = 0; i < VP; ++i) {
-      const int pc = tid + i * kThreads, d = pc / (kSub / 8), grp = pc % (kSub / 8);
-      const int p0 = base + 8 * grp;
-      const int pg = page_at(p0);
-      const uint16_t* src = pg >= 0 ? vc + (int64_t)pg * page_elems + (int64_t)h * D * ps + (int64_t)d * ps +
-                                          (p0 & (ps - 1))
-                                    : vc;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src);
-      rv[i] = pg >= 0 ? keep_first(v, lim - p0) : zero4();
+    for (int i = 0; i < NP; ++i) {
+      const int pc = tid + i * kThreads;
+      const int tile = (pc * 8) / TE, w = (pc * 8) % TE;
+      const int t0 = base + kTile * tile;                      // position of the tile's token 0
+      const int pg = page_at(t0);
+      const int64_t tb = pg >= 0 ? tile_base(pg, h, t0 & (ps - 1), Hkv, log2_ps, D) + w : 0;
+      const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(kc + tb);
+      const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(vc + tb);
+      // K rows past lim are masked in the scores; only a missing page is zeroed.
+      rk[i] = pg >= 0 ? kv : zero4();
+      // V piece: one dim of 8 tokens, 8 * ((w / 128) % 2) .. +7 of the tile.
+      rv[i] = pg >= 0 ? keep_first(vv, lim - (t0 + 8 * ((w >> 7) & 1))) : zero4();
     }
   };
   auto store_sub = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      const int pc = tid + i * kThreads, r = pc / (D / 8), ch = pc % (D / 8);
-      *reinterpret_cast<u32x4_t*>(&sK[buf][k_lds<D>(r, ch)]) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VP; ++i) {
-      const int pc = tid + i * kThreads, d = pc / (kSub / 8), grp = pc % (kSub / 8);
-      *reinterpret_cast<u32x4_t*>(&sV[buf][v_lds(d, grp)]) = rv[i];
+    for (int i = 0; i < NP; ++i) {
+      const int pc = tid + i * kThreads;
+      *reinterpret_cast<u32x4_t*>(&sK[buf][pc * 8]) = rk[i];
+      *reinterpret_cast<u32x4_t*>(&sV[buf][pc * 8]) = rv[i];
     }
   };
 
@@ -160,17 +144,20 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
       const int buf = u & 1;
       const int l16 = n;
       u32x4_t kf[2][D / 32], vf[D / 16];
+      // Same operand addressing as decode, inside the LDS copy of the two tiles.
+      const int kofs = (l16 >> 3) * TE + g * 128 + (l16 & 7) * 8;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int r = sub_key_of_row(l16, b);
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks)
-          kf[b][ks] = *reinterpret_cast<const u32x4_t*>(&sK[buf][k_lds<D>(r, 4 * ks + g)]);
-      }
+          kf[b][ks] = *reinterpret_cast<const u32x4_t*>(&sK[buf][kofs + 4 * ks * 128 + 8 * b * 8]);
+      const int vofs = (g >> 1) * TE + (g & 1) * 128 + l16 * 8;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt)
-        vf[dt] = *reinterpret_cast<const u32x4_t*>(&sV[buf][v_lds(16 * dt + l16, g)]);
-      chunk_step<D, kNB>(ca, kf, vf, qf, nvalid, s, scale_log2);
+        vf[dt] = *reinterpret_cast<const u32x4_t*>(&sV[buf][vofs + dt * 256]);
+      SubProbs<kNB> sp;
+      chunk_scores<D, kNB>(ca, kf, qf, nvalid, s, scale_log2, sp);
+      chunk_values<D, kNB>(ca, vf, sp);
     }
     const bool chunk_end = (s == kSubs - 1) || (u == U - 1);
     if (chunk_end) {

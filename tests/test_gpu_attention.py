@@ -65,25 +65,42 @@ class Batch:
 
 # ---------------------------------------------------------------- KV append
 
-def test_kv_append_layout_bit_exact():
-    hkv, d, ps, pages, t = 8, 128, 16, 40, 300
+def _tile_positions(off, d):
+    """Element offset inside a (page, head) block of in-page token `off`, dim d,
+    per the tiled layout documented in include/bi.h (restated here)."""
+    t, j = off // 16, off % 16
+    slot = 8 * ((j // 4) % 2) + 4 * (j // 8) + j % 4
+    k = t * 16 * D_ALL[0] + (d // 8) * 128 + slot * 8 + d % 8
+    v = t * 16 * D_ALL[0] + (d // 16) * 256 + (j // 8) * 128 + (d % 16) * 8 + j % 8
+    return k, v
+
+
+D_ALL = [0]
+
+
+@pytest.mark.parametrize("ps", [16, 64])
+def test_kv_append_layout_bit_exact(ps):
+    hkv, d, pages, t = 8, 128, 40, 300
+    D_ALL[0] = d
     k_new = W.randn_bf16((t, hkv, d), 1, "k", 0, device=DEV)
     v_new = W.randn_bf16((t, hkv, d), 1, "v", 0, device=DEV)
     slots = torch.randperm(pages * ps, generator=torch.Generator().manual_seed(3))[:t].to(torch.int32)
     slots[7] = -1                                    # padding token: skipped
     kc, vc = bi.alloc_kv_cache(pages, hkv, d, ps, fill=0.5)
     bi.bi_kv_append(k_new, v_new, slots.to(DEV), kc, vc)
-    ek = torch.full((pages, hkv, ps, d), 0.5, dtype=torch.bfloat16)
-    ev = torch.full((pages, hkv, d, ps), 0.5, dtype=torch.bfloat16)
+    ek = torch.full((pages, hkv, ps * d), 0.5, dtype=torch.bfloat16)
+    ev = torch.full((pages, hkv, ps * d), 0.5, dtype=torch.bfloat16)
     kh, vh = k_new.cpu(), v_new.cpu()
+    dims = np.arange(d)
     for i in range(t):
         s = int(slots[i])
         if s < 0:
             continue
-        ek[s // ps, :, s % ps, :] = kh[i]
-        ev[s // ps, :, :, s % ps] = vh[i]
-    assert_bitwise(kc.cpu(), ek, "k cache")
-    assert_bitwise(vc.cpu(), ev, "v cache")
+        kpos, vpos = _tile_positions(s % ps, dims)
+        ek[s // ps, :, torch.from_numpy(kpos)] = kh[i]
+        ev[s // ps, :, torch.from_numpy(vpos)] = vh[i]
+    assert_bitwise(kc.cpu().view(pages, hkv, -1), ek, "k cache")
+    assert_bitwise(vc.cpu().view(pages, hkv, -1), ev, "v cache")
 
 
 # ---------------------------------------------------------------- decode: pins
