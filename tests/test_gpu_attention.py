@@ -411,3 +411,27 @@ def test_strided_fused_qkv_inputs():
     bi.bi_kv_append(k.contiguous(), v.contiguous(), slots, kc2, vc2)
     assert_bitwise(bt.kc, kc2, "strided k append")
     assert_bitwise(bt.vc, vc2, "strided v append")
+
+
+@pytest.mark.parametrize("ps", [32, 256])
+def test_page_sizes_decode_parity_and_prefill_equality(ps):
+    lens = [1000, 37, 600]
+    log_case(f"page size {ps}")
+    bt = Batch(range(3), lens, 32, 8, 128, 41, page_size=ps)
+    out, lse = bt.decode()
+    ro, rl = bt.oracle([0, 1, 2])
+    for b in range(3):
+        assert_bf16_close(out[b], ro[b], f"ps={ps} request {b}")
+    assert_f32_close(lse, rl, f"ps={ps} lse")
+    # prefill of the last 64 tokens of request 0 == decode of the same rows
+    p, n = 1000 - 64, 64
+    q = W.randn_bf16((n, 32, 128), 41, "q", 77, device=DEV)
+    po, pl = bi.bi_attn_prefill(q, torch.tensor([0, n], dtype=torch.int32, device=DEV),
+                                torch.tensor([p], dtype=torch.int32, device=DEV), n, bt.kc, bt.vc,
+                                bt.bt[:1].contiguous(), bt.scale,
+                                lse=torch.empty((n, 32), dtype=torch.float32, device=DEV))
+    od, ld = bi.bi_attn_decode(q, bt.kc, bt.vc, bt.bt[:1].repeat(n, 1).contiguous(),
+                               torch.arange(p + 1, p + n + 1, dtype=torch.int32, device=DEV), 1000, bt.scale,
+                               lse=torch.empty((n, 32), dtype=torch.float32, device=DEV))
+    assert_bitwise(po, od, f"ps={ps} prefill vs decode")
+    assert_bitwise(pl, ld, f"ps={ps} prefill lse vs decode")
