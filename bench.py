@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=256, help="requests of the step the oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes 20 times (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -89,17 +91,41 @@ def bytes_prefill(prefixes, chunks, hq, hkv, d):
 
 # ---------------------------------------------------------------- timing helpers
 
-def time_fn(torch, fn, reps, warmup=3):
-    """Median / p10 / p90 microseconds of fn() measured with HIP events on the current stream."""
-    for _ in range(warmup):
-        fn()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for i in range(reps):
-        evs[i][0].record()
+def time_fn(torch, fn, reps, warmup=3, per_graph=10):
+    """Median / p10 / p90 microseconds per call of fn(i).
+
+    The calls are captured into HIP graphs of `per_graph` back-to-back launches
+    (the library only enqueues kernels on the current stream, so it captures),
+    and each graph replay is timed with HIP events on that stream, so launch
+    gaps of the host do not inflate short kernels."""
+    for i in range(warmup):
         fn(i)
-        evs[i][1].record()
     torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(side):
+        for r in range(max(1, reps // per_graph) if reps >= per_graph else 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for i in range(per_graph):
+                    fn(r * per_graph + i)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for g in graphs[:1]:
+        g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(3):
+        for g in graphs:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / per_graph)
+    ts.sort()
     return ts[len(ts) // 2], ts[len(ts) // 10], ts[(len(ts) * 9) // 10]
 
 
@@ -387,6 +413,14 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_bytes:
+        x = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(20):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": 20}), flush=True)
+        return
     import invariant_bi_rmsnorm_02_amd as bi
     import workloads as W
     if not os.path.exists(bi.LIB_PATH):
