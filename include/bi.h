@@ -85,6 +85,8 @@ bi_status bi_rmsnorm(const void* x, int64_t ldx, const void* gamma, float eps,
  * fp32 accumulator per output element are used for every m: no split-K and no
  * shape-dependent configuration, so row m of C does not depend on the other rows
  * of A.  k % 32 == 0; m, n >= 0 (m == 0 or n == 0 is a no-op); k >= 32.
+ * BI_ERR_UNSUPPORTED when a 64-row slice of A or W spans 2^31 bytes or more
+ * (63 * ld + k >= 2^30 elements) or the tile count overflows 32 bits.
  */
 bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw,
                   void* c, int64_t ldc, int32_t c_dtype,

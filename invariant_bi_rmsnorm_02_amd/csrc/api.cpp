@@ -104,8 +104,7 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* 
   if (lda < k || ldw < k || ldc < n || lda % 8 || ldw % 8) return BI_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(w)) return BI_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(c) % (c_dtype == BI_F32 ? 4u : 2u)) return BI_ERR_INVALID_ARG;
-  const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
-  if (tiles > 0x7fffffff) return BI_ERR_UNSUPPORTED;
+  if (!bi::gemm_supported(lda, ldw, m, n, k)) return BI_ERR_UNSUPPORTED;
   return from_hip(bi::launch_gemm(a, lda, w, ldw, c, ldc, c_dtype == BI_F32, m, n, k, as_stream(stream)));
 }
 

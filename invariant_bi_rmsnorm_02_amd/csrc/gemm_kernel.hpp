@@ -1,0 +1,272 @@
+// Batch-invariant bf16 GEMM kernel template, C = A W^T ("Thinking Machines Lab -
+// Defeating Nondeterminism in LLM Inference", section "2. Batch-Invariant
+// Matrix Multiplication", figs. "Data-Parallel Matrix Multiplication" and
+// "Split-K Matmul").
+//
+// The library instantiates exactly one configuration (gemm.hip) and uses it for
+// every shape.  Whatever the configuration, the arithmetic of an output element
+// is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
+// k = 0, 32, 64, ... in ascending order, no split of K.  Nothing here depends on
+// M except which rows are loaded and which 16-row MFMA blocks are skipped
+// because all their rows are past M.
+//
+// Data movement.  K advances in BK-wide stages.  Every global read is a raw
+// buffer load whose resource covers only this workgroup's rows: a row past N
+// or M, or a k past K, gets an out-of-range offset and the hardware returns
+// zeros without touching memory.  So the load stream has no branches, and the
+// compiler can wait for exactly the stage it needs (vmcnt(n) rather than
+// vmcnt(0)) while later stages stay in flight.  W stages are fetched PW stages
+// ahead into a register ring and A stages PA ahead; each stage is then copied
+// into a double-buffered, XOR-swizzled LDS tile that the wavefronts read their
+// MFMA operands from.  The tile is computed as C^T = W A^T so each lane stores
+// 4 consecutive n.
+#pragma once
+
+#include "bi_common.hpp"
+
+namespace bi {
+
+template <int TN_, int TM_, int WGN_, int WGM_, int PW_, int PA_, int BK_ = 64>
+struct GemmCfg {
+  static constexpr int TN = TN_, TM = TM_;          // workgroup tile: W rows x A rows
+  static constexpr int WGN = WGN_, WGM = WGM_;      // wavefront grid
+  static constexpr int PW = PW_, PA = PA_;          // register prefetch depth (stages) of W and A
+  static constexpr int BK = BK_;                    // K per stage (64 or 128)
+  static constexpr int kThreads = 64 * WGN * WGM;
+  static constexpr int WTN = TN / WGN, WTM = TM / WGM;
+  static constexpr int NB = WTN / 16, MB = WTM / 16;
+  static constexpr int kChunks = BK / 8;                    // 16-byte chunks per tile row
+  static constexpr int LW = TN * kChunks / kThreads;        // W loads per thread per stage
+  static constexpr int LA = TM * kChunks / kThreads;        // A loads per thread per stage
+  static constexpr int U = (PW > PA ? PW : PA) % 2 ? 2 * (PW > PA ? PW : PA) : (PW > PA ? PW : PA);
+  static_assert(LW >= 1 && LA >= 1 && TN * kChunks % kThreads == 0 && TM * kChunks % kThreads == 0, "split");
+  static_assert(NB >= 1 && MB >= 1, "wave tile");
+  static_assert(U % PW == 0 && U % PA == 0 && U % 2 == 0, "ring unroll");
+  static_assert(PW * LW + PA * LA <= 60, "outstanding loads per wave");
+  static_assert(BK == 64 || BK == 128, "stage depth");
+};
+
+// Host-side limit: every offset of a workgroup's buffer resource must fit in
+// 31 bits (rows - 1 full row strides plus one row of K elements, in bytes).
+template <class Cfg>
+inline bool gemm_offsets_fit(int64_t lda, int64_t ldw, int64_t k) {
+  const int64_t lim = (int64_t)1 << 31;
+  return ((int64_t)(Cfg::TN - 1) * ldw + k) * 2 < lim && ((int64_t)(Cfg::TM - 1) * lda + k) * 2 < lim;
+}
+
+// LDS element offset of 16-byte chunk c of tile row r (KC chunks per row).  The
+// XOR swizzle puts the 16 rows that one MFMA operand read touches at one chunk
+// index into distinct 16-byte bank groups.
+template <int KC>
+__device__ __forceinline__ int gemm_lds_off(int r, int c) { return r * KC * 8 + ((c ^ (r & (KC - 1))) << 3); }
+
+__device__ __forceinline__ void gemm_map_tile(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  // Workgroup i runs on XCD i % 8.  Give each XCD a contiguous range of tiles
+  // (so tiles sharing A or W rows share an L2), then walk that range in groups
+  // of 8 m-tiles.  Only placement changes; the arithmetic does not.
+  const int total = tiles_m * tiles_n;
+  const int q = total >> 3, r = total & 7;
+  const int x = pid & 7, j = pid >> 3;
+  const int lin = (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+  constexpr int G = 8;
+  const int group = lin / (G * tiles_n);
+  const int first_m = group * G;
+  const int gsize = min(tiles_m - first_m, G);
+  const int in_group = lin - group * G * tiles_n;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+constexpr uint32_t kBufOOB = 0x80000000u;  // beyond every resource's range: the load returns zeros
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, uint32_t bytes) {
+  // Raw (stride 0) resource; the last word is the gfx9 data-format default.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t gemm_buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <class Cfg, bool kF32Out>
+__global__ __launch_bounds__(Cfg::kThreads, 2) void gemm_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
+  constexpr int TN = Cfg::TN, TM = Cfg::TM, BK = Cfg::BK, NT = Cfg::kThreads;
+  constexpr int NB = Cfg::NB, MB = Cfg::MB, LW = Cfg::LW, LA = Cfg::LA, PW = Cfg::PW, PA = Cfg::PA;
+  constexpr int KC = Cfg::kChunks, U = Cfg::U;
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][TN * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][TM * BK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % Cfg::WGN, wm = wave / Cfg::WGN;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  int tile_m, tile_n;
+  gemm_map_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+  const int m0 = tile_m * TM, n0 = tile_n * TN;
+  const int KT = (K + BK - 1) / BK;
+  const int rows_w = min(TN, N - n0), rows_a = min(TM, M - m0);
+
+  // Resources cover exactly this tile's rows (the host checked the offsets fit).
+  const __amdgpu_buffer_rsrc_t rsw =
+      gemm_rsrc(W + (int64_t)n0 * ldw, (uint32_t)(((int64_t)(rows_w - 1) * ldw + K) * 2));
+  const __amdgpu_buffer_rsrc_t rsa =
+      gemm_rsrc(A + (int64_t)m0 * lda, (uint32_t)(((int64_t)(rows_a - 1) * lda + K) * 2));
+
+  // Per load slot: byte offset of its chunk in stage 0, its k in stage 0, and
+  // whether its row exists.
+  uint32_t wofs[LW], aofs[LA];
+  int wk[LW], ak[LA];
+#pragma unroll
+  for (int i = 0; i < LW; ++i) {
+    const int id = tid + i * NT, r = id / KC, c = id % KC;
+    wofs[i] = r < rows_w ? (uint32_t)(((int64_t)r * ldw + c * 8) * 2) : kBufOOB;
+    wk[i] = c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int id = tid + i * NT, r = id / KC, c = id % KC;
+    aofs[i] = r < rows_a ? (uint32_t)(((int64_t)r * lda + c * 8) * 2) : kBufOOB;
+    ak[i] = c * 8;
+  }
+
+  u32x4_t rw[PW][LW], ra[PA][LA];
+  auto load_w = [&](int kt, u32x4_t (&dst)[LW]) {
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+      const bool ok = wofs[i] != kBufOOB && kt * BK + wk[i] < K;
+      dst[i] = gemm_buf_load(rsw, ok ? wofs[i] + (uint32_t)(kt * BK * 2) : kBufOOB);
+    }
+  };
+  auto load_a = [&](int kt, u32x4_t (&dst)[LA]) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const bool ok = aofs[i] != kBufOOB && kt * BK + ak[i] < K;
+      dst[i] = gemm_buf_load(rsa, ok ? aofs[i] + (uint32_t)(kt * BK * 2) : kBufOOB);
+    }
+  };
+  auto store = [&](int buf, const u32x4_t (&w)[LW], const u32x4_t (&a)[LA]) {
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+      const int id = tid + i * NT;
+      *reinterpret_cast<u32x4_t*>(&sW[buf][gemm_lds_off<KC>(id / KC, id % KC)]) = w[i];
+    }
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      const int id = tid + i * NT;
+      *reinterpret_cast<u32x4_t*>(&sA[buf][gemm_lds_off<KC>(id / KC, id % KC)]) = a[i];
+    }
+  };
+
+  f32x4_t acc[NB][MB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // 16-row blocks of this wave that hold at least one real row of A.
+  const int wave_m0 = m0 + wm * Cfg::WTM;
+  const int live_mb = min(MB, max(0, (M - wave_m0 + 15) >> 4));
+
+  auto compute = [&](int buf) {
+    if (live_mb <= 0) return;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int c = ks * 4 + g;
+      u32x4_t af[NB], bf[MB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        af[i] = *reinterpret_cast<const u32x4_t*>(&sW[buf][gemm_lds_off<KC>(wn * Cfg::WTN + i * 16 + l16, c)]);
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+        bf[j] = *reinterpret_cast<const u32x4_t*>(&sA[buf][gemm_lds_off<KC>(wm * Cfg::WTM + j * 16 + l16, c)]);
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        if (j < live_mb) {
+#pragma unroll
+          for (int i = 0; i < NB; ++i) acc[i][j] = mfma_16x16x32(af[i], bf[j], acc[i][j]);
+        }
+      }
+    }
+  };
+
+  // Prologue: stages 0 .. PW-1 (W) and 0 .. PA-1 (A) in flight, stage 0 in LDS.
+  // Stages past the end of K load zeros and cost no memory traffic.
+#pragma unroll
+  for (int p = 0; p < PW; ++p) load_w(p, rw[p]);
+#pragma unroll
+  for (int p = 0; p < PA; ++p) load_a(p, ra[p]);
+  store(0, rw[0], ra[0]);
+  __syncthreads();
+
+  // Stage kt lives in W slot kt % PW and A slot kt % PA until it is copied into
+  // LDS buffer kt % 2 (at the end of iteration kt - 1); at the start of
+  // iteration kt the slot is refilled with stage kt + PW (kt + PA).  The loop
+  // runs whole groups of U stages and only the MFMA step is skipped past K, so
+  // every path through the loop issues the same loads (no conservative waits).
+  const int KTU = (KT + U - 1) / U * U;
+  for (int kb = 0; kb < KTU; kb += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kt = kb + u;
+      load_w(kt + PW, rw[u % PW]);
+      load_a(kt + PA, ra[u % PA]);
+      if (kt < KT) compute(u & 1);
+      store((u + 1) & 1, rw[(u + 1) % PW], ra[(u + 1) % PA]);
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: lane holds C[m][n .. n+3].
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int m = wave_m0 + j * 16 + l16;
+    if (j >= live_mb || m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int n = n0 + wn * Cfg::WTN + i * 16 + 4 * g;
+      if (n >= N) continue;
+      const f32x4_t v = acc[i][j];
+      if constexpr (kF32Out) {
+        float* cp = static_cast<float*>(C) + (int64_t)m * ldc + n;
+        if (vec_store && n + 3 < N) {
+          *reinterpret_cast<f32x4_t*>(cp) = v;
+        } else {
+          for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = v[e];
+        }
+      } else {
+        uint16_t* cp = static_cast<uint16_t*>(C) + (int64_t)m * ldc + n;
+        if (vec_store && n + 3 < N) {
+          *reinterpret_cast<u32x2_t*>(cp) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        } else {
+          for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = static_cast<uint16_t>(f32_to_bf16(v[e]));
+        }
+      }
+    }
+  }
+}
+
+template <class Cfg>
+hipError_t launch_gemm_cfg(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc,
+                           bool c_f32, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  if (m == 0 || n == 0) return hipSuccess;
+  if (!gemm_offsets_fit<Cfg>(lda, ldw, k)) return hipErrorInvalidValue;
+  const int tiles_m = static_cast<int>((m + Cfg::TM - 1) / Cfg::TM);
+  const int tiles_n = static_cast<int>((n + Cfg::TN - 1) / Cfg::TN);
+  const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n)), block(Cfg::kThreads);
+  auto* as = static_cast<const uint16_t*>(a);
+  auto* ws = static_cast<const uint16_t*>(w);
+  // Vector stores need every row start 16-byte (fp32) / 8-byte (bf16) aligned.
+  const int vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(c) & 15u) == 0);
+  if (c_f32)
+    hipLaunchKernelGGL((gemm_kernel<Cfg, true>), grid, block, 0, stream, as, lda, ws, ldw, c, ldc, (int)m, (int)n,
+                       (int)k, tiles_m, tiles_n, vec);
+  else
+    hipLaunchKernelGGL((gemm_kernel<Cfg, false>), grid, block, 0, stream, as, lda, ws, ldw, c, ldc, (int)m, (int)n,
+                       (int)k, tiles_m, tiles_n, vec);
+  return hipGetLastError();
+}
+
+}  // namespace bi

@@ -12,6 +12,9 @@ namespace bi {
 hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* gamma, float eps, void* y,
                           int64_t ldy, int64_t rows, int hidden, hipStream_t stream);
 
+// False when the tile count or a workgroup's buffer offsets would overflow.
+bool gemm_supported(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k);
+
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc,
                        bool c_f32, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 

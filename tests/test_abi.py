@@ -37,6 +37,9 @@ def test_host_validation_without_gpu(lib):
     assert lib.bi_gemm(P, 64, P, 64, P, 64, 7, 4, 4, 64, None) == bi.BI_ERR_INVALID_ARG   # dtype
     assert lib.bi_gemm(P, 32, P, 64, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_INVALID_ARG   # lda < k
     assert lib.bi_gemm(P, 64, P, 64, P, 64, 0, 0, 4, 64, None) == bi.BI_OK
+    # a 64-row slice of W spanning 2^31 bytes cannot be addressed by one buffer resource
+    assert lib.bi_gemm(P, 64, P, 1 << 25, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_UNSUPPORTED
+    assert lib.bi_gemm(P, 1 << 25, P, 64, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_UNSUPPORTED
     # decode: head_dim 96, group size 3, page size 12, missing workspace
     args = dict(q=P, kc=P, vc=P, pages=8, bt=P, mp=4, lens=P, b=2, msl=64, hq=32, hkv=8, d=128, ps=16)
 
