@@ -85,6 +85,19 @@ def flops_prefill(prefixes, chunks, hq, d):
     return 4 * hq * d * keys
 
 
+def bytes_moe(expert_ids, num_experts, h, f):
+    """Weights of every expert the batch routes to, plus x and y (bf16) and the routing."""
+    import numpy as np
+    ids = np.asarray(expert_ids).reshape(-1)
+    touched = len(set(int(e) for e in ids if 0 <= e < num_experts))
+    t = np.asarray(expert_ids).shape[0]
+    return touched * 2 * (2 * h * f) + 2 * t * h * 2 + ids.size * 8
+
+
+def flops_moe(t, k, h, f):
+    return 4 * t * k * h * f
+
+
 def bytes_prefill(prefixes, chunks, hq, hkv, d):
     return sum(4 * hkv * d * (p + n) + 4 * n * hq * d for p, n in zip(prefixes, chunks))
 
@@ -328,6 +341,28 @@ def kernel_table(torch, bi, W, step, reps, everything):
         out.append(entry("log_softmax [T,151936] fp32", us, 8 * T * V, extra={"T": T}))
         del ht, z, lp
     del wl
+    torch.cuda.empty_cache()
+    # Routed experts: 128 experts, top-8, 4096->1536->4096.  Each timed launch
+    # uses another routing set, so repeats cannot be served from the Infinity Cache.
+    E, K8, F = 128, 8, 1536
+    w_up, w_down = W.moe_weights(E, 4096, F, W.SEED_MOE, device=dev)
+    for T in (1, 64, 512, 2048):
+        sets = 16 if T == 1 else 2
+        xs, rts = [], []
+        for r in range(sets):
+            ids = range(r * T, (r + 1) * T)
+            xs.append(W.rows_for_requests(ids, 4096, W.SEED_MOE, device=dev))
+            ex, wt = W.moe_routing(ids, E, K8, W.SEED_MOE)
+            rts.append((ex.to(dev), wt.to(dev), ex))
+        y = torch.empty((T, 4096), dtype=torch.bfloat16, device=dev)
+        mws = torch.empty((bi.moe_workspace_bytes(T, K8, E, 4096, F),), dtype=torch.uint8, device=dev)
+        us = time_fn(torch, lambda i=0: bi.bi_moe_ffn(xs[i % sets], rts[i % sets][0], rts[i % sets][1], w_up, w_down,
+                                                      out=y, workspace=mws), max(5, reps // 4))
+        nbytes = sum(bytes_moe(r[2].numpy(), E, 4096, F) for r in rts) / sets
+        out.append(entry("moe experts 128x(4096->1536->4096) top-8", us, nbytes, flops_moe(T, K8, 4096, F),
+                         extra={"T": T}))
+        del xs, rts, y, mws
+    del w_up, w_down
     torch.cuda.empty_cache()
     for B in (1, 64, 256):
         lens = W.decode_lengths(range(B), W.SEED_MOE)

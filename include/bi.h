@@ -190,6 +190,40 @@ bi_status bi_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, c
                           bi_stream_t stream);
 
 /*
+ * Mixture-of-experts FFN over a batch of tokens (the routed expert layer of the
+ * Qwen3-235B-A22B-shaped workload; the expert FFN is not on the pages).  The
+ * invariance rule is [BINR]'s answer on a fixed per-element reduction order
+ * regardless of batch size or position in the batch: a token's output depends
+ * only on its own x row, routing and the weights, never on which other tokens
+ * share its experts.
+ *   y[t] = bf16( sum over s = 0 .. top_k-1 ascending, in fp32, of
+ *                w[t, s] * W_down[e] h ),  h = bf16(SiLU(W_up[e] x[t])),
+ *          e = expert_ids[t, s],  SiLU(v) = v / (1 + exp(-v)).
+ * Both expert products are bi_gemm's configuration and K loop (one fp32
+ * accumulator per element, k ascending); the W_down product stays fp32 until
+ * the weighted sum.
+ * x: [num_tokens, hidden] bf16, row stride ldx (ldx % 8 == 0);
+ * expert_ids: [num_tokens, top_k] int32, contiguous; an id outside
+ *   [0, num_experts) drops that slot;
+ * expert_weights: [num_tokens, top_k] fp32, contiguous;
+ * w_up: [num_experts][ffn][hidden] bf16; w_down: [num_experts][hidden][ffn] bf16;
+ * y: [num_tokens, hidden] bf16, row stride ldy (ldy % 8 == 0), must not alias x.
+ * hidden, ffn: multiples of 32, at most 65536; 1 <= top_k <= 64;
+ * 1 <= num_experts <= 65535; num_tokens == 0 is a no-op.  BI_ERR_UNSUPPORTED
+ * when num_tokens * top_k > 2^24 or x spans 2^31 bytes or more.
+ * workspace: at least bi_moe_workspace_bytes(...) bytes, 256-byte aligned, owned
+ * by the caller (routing tables, the bf16 intermediate and the fp32 per-slot
+ * outputs; about num_tokens * top_k * (2 * ffn + 4 * hidden) bytes); else
+ * BI_ERR_WORKSPACE.
+ */
+size_t bi_moe_workspace_bytes(int32_t num_tokens, int32_t top_k, int32_t num_experts,
+                              int32_t hidden, int32_t ffn);
+bi_status bi_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids, const float* expert_weights,
+                     int32_t num_tokens, int32_t top_k, int32_t num_experts,
+                     const void* w_up, const void* w_down, int32_t hidden, int32_t ffn,
+                     void* y, int64_t ldy, void* workspace, size_t workspace_bytes, bi_stream_t stream);
+
+/*
  * Row-wise log_softmax of fp32 logits ([BINR] answer on sampler/trainer
  * logprob agreement).  out[r, j] = z[r, j] - (max_j z + log sum_j exp(z - max)).
  * One workgroup per row, one fixed reduction tree whatever `rows`.

@@ -37,6 +37,9 @@ _SIGNATURES = {
     "bi_attn_prefill": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_i32,
                                  _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p]),
     "bi_log_softmax": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
+    "bi_moe_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "bi_moe_ffn": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_i32,
+                            _c_p, _c_i64, _c_p, _c_size, _c_p]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -275,4 +278,45 @@ def bi_log_softmax(logits: torch.Tensor, out: Optional[torch.Tensor] = None, str
         raise ValueError("out shape")
     _check("bi_log_softmax", lib().bi_log_softmax(logits.data_ptr(), _rows(logits, "logits"), out.data_ptr(),
                                                   _rows(out, "out"), rows, vocab, _stream(stream)))
+    return out
+
+
+def moe_workspace_bytes(num_tokens: int, top_k: int, num_experts: int, hidden: int, ffn: int) -> int:
+    return int(lib().bi_moe_workspace_bytes(num_tokens, top_k, num_experts, hidden, ffn))
+
+
+def bi_moe_ffn(x: torch.Tensor, expert_ids: torch.Tensor, expert_weights: torch.Tensor, w_up: torch.Tensor,
+               w_down: torch.Tensor, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """x [T, H] bf16; expert_ids [T, k] int32; expert_weights [T, k] fp32;
+    w_up [E, F, H] bf16; w_down [E, H, F] bf16 -> y [T, H] bf16."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(expert_ids, "expert_ids", torch.int32)
+    _dev(expert_weights, "expert_weights", torch.float32)
+    _dev(w_up, "w_up", torch.bfloat16)
+    _dev(w_down, "w_down", torch.bfloat16)
+    T, H = x.shape
+    E, F, H2 = w_up.shape
+    if H2 != H or tuple(w_down.shape) != (E, H, F):
+        raise ValueError("w_up must be [E, F, H] and w_down [E, H, F]")
+    if expert_ids.dim() != 2 or expert_ids.shape[0] != T or expert_weights.shape != expert_ids.shape:
+        raise ValueError("expert_ids / expert_weights must be [T, top_k]")
+    for t, name in ((expert_ids, "expert_ids"), (expert_weights, "expert_weights"), (w_up, "w_up"),
+                    (w_down, "w_down")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    k = expert_ids.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", torch.bfloat16)
+    if out.shape != (T, H):
+        raise ValueError("out shape")
+    need = moe_workspace_bytes(T, k, E, H, F)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    _check("bi_moe_ffn", lib().bi_moe_ffn(x.data_ptr(), _rows(x, "x"), expert_ids.data_ptr(),
+                                          expert_weights.data_ptr(), T, k, E, w_up.data_ptr(), w_down.data_ptr(),
+                                          H, F, out.data_ptr(), _rows(out, "out"), workspace.data_ptr(),
+                                          workspace.numel(), _stream(stream)))
     return out

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libbi.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "rmsnorm.hip", "gemm.hip", "kv_append.hip", "attn_decode.hip",
-           "attn_prefill.hip", "log_softmax.hip"]
+           "attn_prefill.hip", "log_softmax.hip", "moe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -193,4 +193,30 @@ bi_status bi_log_softmax(const float* logits, int64_t ld_in, float* out, int64_t
   return from_hip(bi::launch_log_softmax(logits, ld_in, out, ld_out, rows, vocab, as_stream(stream)));
 }
 
+size_t bi_moe_workspace_bytes(int32_t num_tokens, int32_t top_k, int32_t num_experts, int32_t hidden,
+                              int32_t ffn) {
+  if (num_tokens <= 0 || top_k <= 0 || num_experts <= 0 || hidden <= 0 || ffn <= 0) return 0;
+  return bi::moe_workspace_bytes(num_tokens, top_k, num_experts, hidden, ffn);
+}
+
+bi_status bi_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids, const float* expert_weights,
+                     int32_t num_tokens, int32_t top_k, int32_t num_experts, const void* w_up, const void* w_down,
+                     int32_t hidden, int32_t ffn, void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                     bi_stream_t stream) {
+  if (num_tokens < 0 || top_k <= 0 || num_experts <= 0 || hidden <= 0 || ffn <= 0) return BI_ERR_INVALID_ARG;
+  if (num_tokens == 0) return BI_OK;
+  if (!x || !expert_ids || !expert_weights || !w_up || !w_down || !y) return BI_ERR_INVALID_ARG;
+  if (top_k > 64 || num_experts > 65535) return BI_ERR_UNSUPPORTED;
+  if (hidden % 32 || ffn % 32 || hidden > 65536 || ffn > 65536) return BI_ERR_UNSUPPORTED;
+  if (ldx < hidden || ldx % 8 || ldy < hidden || ldy % 8) return BI_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(y)) return BI_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(expert_ids) & 3u) || (reinterpret_cast<uintptr_t>(expert_weights) & 3u))
+    return BI_ERR_INVALID_ARG;
+  if (!bi::moe_supported(num_tokens, ldx, top_k, num_experts, hidden, ffn)) return BI_ERR_UNSUPPORTED;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return BI_ERR_WORKSPACE;
+  if (workspace_bytes < bi::moe_workspace_bytes(num_tokens, top_k, num_experts, hidden, ffn)) return BI_ERR_WORKSPACE;
+  return from_hip(bi::launch_moe_ffn(x, ldx, expert_ids, expert_weights, num_tokens, top_k, num_experts, w_up,
+                                     w_down, hidden, ffn, y, ldy, workspace, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -1,25 +1,19 @@
-// The library's one GEMM configuration (gemm_kernel.hpp holds the kernel and
-// its invariance argument).  It was chosen once, by timing candidate tiles at
-// every workload shape on MI355X, and is used for every M:
-//   64 (n) x 64 (m) output tile, 2 x 2 wavefronts of 32 x 32, K in 128-wide
-//   stages, W and A both prefetched 4 stages ahead into registers.
-// A small n-extent keeps enough workgroups streaming weights at decode batch
-// sizes (N / 64 of them), which is what bounds those HBM-bound shapes.
+// bi_gemm's launcher: the library's one GEMM configuration (GemmLibraryCfg in
+// gemm_kernel.hpp, which also holds the kernel and its invariance argument).
 #include "gemm_kernel.hpp"
 #include "launch.hpp"
 
 namespace bi {
 
-using GemmChosen = GemmCfg<64, 64, 2, 2, 4, 4, 128>;
-
 bool gemm_supported(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k) {
-  const int64_t tiles = ((m + GemmChosen::TM - 1) / GemmChosen::TM) * ((n + GemmChosen::TN - 1) / GemmChosen::TN);
-  return tiles <= 0x7fffffff && gemm_offsets_fit<GemmChosen>(lda, ldw, k);
+  using C = GemmLibraryCfg;
+  const int64_t tiles = ((m + C::TM - 1) / C::TM) * ((n + C::TN - 1) / C::TN);
+  return tiles <= 0x7fffffff && gemm_offsets_fit<C>(lda, ldw, k);
 }
 
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc, bool c_f32,
                        int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  return launch_gemm_cfg<GemmChosen>(a, lda, w, ldw, c, ldc, c_f32, m, n, k, stream);
+  return launch_gemm_cfg<GemmLibraryCfg>(a, lda, w, ldw, c, ldc, c_f32, m, n, k, stream);
 }
 
 }  // namespace bi

@@ -88,63 +88,59 @@ __device__ __forceinline__ u32x4_t gemm_buf_load(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-template <class Cfg, bool kF32Out>
-__global__ __launch_bounds__(Cfg::kThreads, 2) void gemm_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
-    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
-  constexpr int TN = Cfg::TN, TM = Cfg::TM, BK = Cfg::BK, NT = Cfg::kThreads;
+// The operands of one workgroup tile: a buffer resource over the W rows and
+// one over the A rows it reads, and for every load slot of this thread the
+// byte offset (within its resource) of the slot's 16-byte chunk in stage 0, or
+// kBufOOB when the slot's row does not exist.  Slot i of a thread covers tile
+// row (tid + i * threads) / chunks, chunk (tid + i * threads) % chunks.
+template <class Cfg>
+struct GemmOperands {
+  __amdgpu_buffer_rsrc_t rsw, rsa;
+  uint32_t wofs[Cfg::LW], aofs[Cfg::LA];
+};
+
+// Byte offset of load slot i's chunk in a row that starts at row_byte.
+template <class Cfg>
+__device__ __forceinline__ uint32_t gemm_slot_chunk_bytes(int i) {
+  return (uint32_t)(((threadIdx.x + i * Cfg::kThreads) % Cfg::kChunks) * 16);
+}
+template <class Cfg>
+__device__ __forceinline__ int gemm_slot_row(int i) {
+  return (threadIdx.x + i * Cfg::kThreads) / Cfg::kChunks;
+}
+
+// Accumulates the workgroup's tile over the whole of K into acc (which the
+// caller zeroes): for every output element one fp32 chain of MFMA steps over
+// k = 0, 32, 64, ... in ascending order.  live_mb = 16-row blocks of this
+// wave's m-range that hold at least one real row (their MFMAs are the only
+// ones issued; the others would only compute padding).
+template <class Cfg>
+__device__ __forceinline__ void gemm_mainloop(const GemmOperands<Cfg>& op, int K, int live_mb,
+                                              uint16_t (*sW)[Cfg::TN * Cfg::BK],
+                                              uint16_t (*sA)[Cfg::TM * Cfg::BK],
+                                              f32x4_t (&acc)[Cfg::NB][Cfg::MB]) {
+  constexpr int BK = Cfg::BK, NT = Cfg::kThreads;
   constexpr int NB = Cfg::NB, MB = Cfg::MB, LW = Cfg::LW, LA = Cfg::LA, PW = Cfg::PW, PA = Cfg::PA;
   constexpr int KC = Cfg::kChunks, U = Cfg::U;
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][TN * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][TM * BK];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave % Cfg::WGN, wm = wave / Cfg::WGN;
   const int l16 = lane & 15, g = lane >> 4;
-
-  int tile_m, tile_n;
-  gemm_map_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
-  const int m0 = tile_m * TM, n0 = tile_n * TN;
   const int KT = (K + BK - 1) / BK;
-  const int rows_w = min(TN, N - n0), rows_a = min(TM, M - m0);
-
-  // Resources cover exactly this tile's rows (the host checked the offsets fit).
-  const __amdgpu_buffer_rsrc_t rsw =
-      gemm_rsrc(W + (int64_t)n0 * ldw, (uint32_t)(((int64_t)(rows_w - 1) * ldw + K) * 2));
-  const __amdgpu_buffer_rsrc_t rsa =
-      gemm_rsrc(A + (int64_t)m0 * lda, (uint32_t)(((int64_t)(rows_a - 1) * lda + K) * 2));
-
-  // Per load slot: byte offset of its chunk in stage 0, its k in stage 0, and
-  // whether its row exists.
-  uint32_t wofs[LW], aofs[LA];
-  int wk[LW], ak[LA];
-#pragma unroll
-  for (int i = 0; i < LW; ++i) {
-    const int id = tid + i * NT, r = id / KC, c = id % KC;
-    wofs[i] = r < rows_w ? (uint32_t)(((int64_t)r * ldw + c * 8) * 2) : kBufOOB;
-    wk[i] = c * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int id = tid + i * NT, r = id / KC, c = id % KC;
-    aofs[i] = r < rows_a ? (uint32_t)(((int64_t)r * lda + c * 8) * 2) : kBufOOB;
-    ak[i] = c * 8;
-  }
 
   u32x4_t rw[PW][LW], ra[PA][LA];
   auto load_w = [&](int kt, u32x4_t (&dst)[LW]) {
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
-      const bool ok = wofs[i] != kBufOOB && kt * BK + wk[i] < K;
-      dst[i] = gemm_buf_load(rsw, ok ? wofs[i] + (uint32_t)(kt * BK * 2) : kBufOOB);
+      const bool ok = op.wofs[i] != kBufOOB && kt * BK + ((tid + i * NT) % KC) * 8 < K;
+      dst[i] = gemm_buf_load(op.rsw, ok ? op.wofs[i] + (uint32_t)(kt * BK * 2) : kBufOOB);
     }
   };
   auto load_a = [&](int kt, u32x4_t (&dst)[LA]) {
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const bool ok = aofs[i] != kBufOOB && kt * BK + ak[i] < K;
-      dst[i] = gemm_buf_load(rsa, ok ? aofs[i] + (uint32_t)(kt * BK * 2) : kBufOOB);
+      const bool ok = op.aofs[i] != kBufOOB && kt * BK + ((tid + i * NT) % KC) * 8 < K;
+      dst[i] = gemm_buf_load(op.rsa, ok ? op.aofs[i] + (uint32_t)(kt * BK * 2) : kBufOOB);
     }
   };
   auto store = [&](int buf, const u32x4_t (&w)[LW], const u32x4_t (&a)[LA]) {
@@ -159,17 +155,6 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void gemm_kernel(
       *reinterpret_cast<u32x4_t*>(&sA[buf][gemm_lds_off<KC>(id / KC, id % KC)]) = a[i];
     }
   };
-
-  f32x4_t acc[NB][MB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-#pragma unroll
-    for (int j = 0; j < MB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // 16-row blocks of this wave that hold at least one real row of A.
-  const int wave_m0 = m0 + wm * Cfg::WTM;
-  const int live_mb = min(MB, max(0, (M - wave_m0 + 15) >> 4));
-
   auto compute = [&](int buf) {
     if (live_mb <= 0) return;
 #pragma unroll
@@ -218,35 +203,109 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void gemm_kernel(
       __syncthreads();
     }
   }
+}
 
-  // Epilogue: lane holds C[m][n .. n+3].
+// 16-row blocks of this wave's m-range (tile rows wm*WTM ..) that hold at least
+// one of the tile's `rows` real rows.
+template <class Cfg>
+__device__ __forceinline__ int gemm_live_blocks(int rows) {
+  const int wm = (threadIdx.x >> 6) / Cfg::WGN;
+  return min(Cfg::MB, max(0, (rows - wm * Cfg::WTM + 15) >> 4));
+}
+
+// Hands every finished output group to st(m, n, v, cnt): tile-local row m
+// (< rows), global column n, v = C[m][n .. n+3], cnt = columns of v below N.
+template <class Cfg, class Store>
+__device__ __forceinline__ void gemm_epilogue(const f32x4_t (&acc)[Cfg::NB][Cfg::MB], int rows, int n0, int N,
+                                              Store&& st) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave % Cfg::WGN, wm = wave / Cfg::WGN;
+  const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < MB; ++j) {
-    const int m = wave_m0 + j * 16 + l16;
-    if (j >= live_mb || m >= M) continue;
+  for (int j = 0; j < Cfg::MB; ++j) {
+    const int m = wm * Cfg::WTM + j * 16 + l16;
+    if (m >= rows) continue;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
+    for (int i = 0; i < Cfg::NB; ++i) {
       const int n = n0 + wn * Cfg::WTN + i * 16 + 4 * g;
       if (n >= N) continue;
-      const f32x4_t v = acc[i][j];
-      if constexpr (kF32Out) {
-        float* cp = static_cast<float*>(C) + (int64_t)m * ldc + n;
-        if (vec_store && n + 3 < N) {
-          *reinterpret_cast<f32x4_t*>(cp) = v;
-        } else {
-          for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = v[e];
-        }
-      } else {
-        uint16_t* cp = static_cast<uint16_t*>(C) + (int64_t)m * ldc + n;
-        if (vec_store && n + 3 < N) {
-          *reinterpret_cast<u32x2_t*>(cp) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        } else {
-          for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = static_cast<uint16_t>(f32_to_bf16(v[e]));
-        }
-      }
+      st(m, n, acc[i][j], min(4, N - n));
     }
   }
 }
+
+template <class Cfg>
+__device__ __forceinline__ void gemm_zero(f32x4_t (&acc)[Cfg::NB][Cfg::MB]) {
+#pragma unroll
+  for (int i = 0; i < Cfg::NB; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::MB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// Stores v (4 consecutive columns, cnt of them real) at cp as bf16 or fp32.
+__device__ __forceinline__ void gemm_store4_bf16(uint16_t* cp, f32x4_t v, int cnt, bool vec) {
+  if (vec && cnt == 4) {
+    *reinterpret_cast<u32x2_t*>(cp) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  } else {
+    for (int e = 0; e < cnt; ++e) cp[e] = static_cast<uint16_t>(f32_to_bf16(v[e]));
+  }
+}
+__device__ __forceinline__ void gemm_store4_f32(float* cp, f32x4_t v, int cnt, bool vec) {
+  if (vec && cnt == 4) {
+    *reinterpret_cast<f32x4_t*>(cp) = v;
+  } else {
+    for (int e = 0; e < cnt; ++e) cp[e] = v[e];
+  }
+}
+
+template <class Cfg, bool kF32Out>
+__global__ __launch_bounds__(Cfg::kThreads, 2) void gemm_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][Cfg::TN * Cfg::BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][Cfg::TM * Cfg::BK];
+
+  int tile_m, tile_n;
+  gemm_map_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
+  const int m0 = tile_m * Cfg::TM, n0 = tile_n * Cfg::TN;
+  const int rows_w = min(Cfg::TN, N - n0), rows_a = min(Cfg::TM, M - m0);
+
+  // Resources cover exactly this tile's rows (the host checked the offsets fit).
+  GemmOperands<Cfg> op;
+  op.rsw = gemm_rsrc(W + (int64_t)n0 * ldw, (uint32_t)(((int64_t)(rows_w - 1) * ldw + K) * 2));
+  op.rsa = gemm_rsrc(A + (int64_t)m0 * lda, (uint32_t)(((int64_t)(rows_a - 1) * lda + K) * 2));
+#pragma unroll
+  for (int i = 0; i < Cfg::LW; ++i) {
+    const int r = gemm_slot_row<Cfg>(i);
+    op.wofs[i] = r < rows_w ? (uint32_t)((int64_t)r * ldw * 2) + gemm_slot_chunk_bytes<Cfg>(i) : kBufOOB;
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg::LA; ++i) {
+    const int r = gemm_slot_row<Cfg>(i);
+    op.aofs[i] = r < rows_a ? (uint32_t)((int64_t)r * lda * 2) + gemm_slot_chunk_bytes<Cfg>(i) : kBufOOB;
+  }
+
+  f32x4_t acc[Cfg::NB][Cfg::MB];
+  gemm_zero<Cfg>(acc);
+  gemm_mainloop<Cfg>(op, K, gemm_live_blocks<Cfg>(rows_a), sW, sA, acc);
+
+  // Epilogue: lane holds C[m][n .. n+3].
+  gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) {
+    if constexpr (kF32Out)
+      gemm_store4_f32(static_cast<float*>(C) + (int64_t)(m0 + m) * ldc + n, v, cnt, vec_store);
+    else
+      gemm_store4_bf16(static_cast<uint16_t*>(C) + (int64_t)(m0 + m) * ldc + n, v, cnt, vec_store);
+  });
+}
+
+// The library's one GEMM configuration, used by bi_gemm and by the expert
+// GEMMs of bi_moe_ffn.  Chosen once, by timing candidate tiles at every
+// workload shape on MI355X, and used for every M: 64 (n) x 64 (m) output tile,
+// 2 x 2 wavefronts of 32 x 32, K in 128-wide stages, W and A both prefetched 4
+// stages ahead into registers.  A small n-extent keeps enough workgroups
+// streaming weights at decode batch sizes (N / 64 of them), which is what
+// bounds those HBM-bound shapes.
+using GemmLibraryCfg = GemmCfg<64, 64, 2, 2, 4, 4, 128>;
 
 template <class Cfg>
 hipError_t launch_gemm_cfg(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc,

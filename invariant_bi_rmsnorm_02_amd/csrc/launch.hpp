@@ -43,6 +43,13 @@ hipError_t launch_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_sta
                                int num_seqs, int max_q_len, const AttnGeom& g, void* out, float* lse,
                                hipStream_t stream);
 
+// Mixture-of-experts FFN (moe.hip).
+size_t moe_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t H, int64_t F);
+bool moe_supported(int64_t T, int64_t ldx, int64_t top_k, int64_t E, int64_t H, int64_t F);
+hipError_t launch_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids, const float* expert_weights,
+                          int T, int top_k, int E, const void* w_up, const void* w_down, int H, int F, void* y,
+                          int64_t ldy, void* workspace, hipStream_t stream);
+
 hipError_t launch_log_softmax(const float* logits, int64_t ld_in, float* out, int64_t ld_out,
                               int64_t rows, int64_t vocab, hipStream_t stream);
 

@@ -37,6 +37,13 @@ def test_host_validation_without_gpu(lib):
     assert lib.bi_gemm(P, 64, P, 64, P, 64, 7, 4, 4, 64, None) == bi.BI_ERR_INVALID_ARG   # dtype
     assert lib.bi_gemm(P, 32, P, 64, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_INVALID_ARG   # lda < k
     assert lib.bi_gemm(P, 64, P, 64, P, 64, 0, 0, 4, 64, None) == bi.BI_OK
+    # MoE: hidden not a multiple of 32, missing workspace, empty batch
+    moe = lambda T, H, ws, nbytes: lib.bi_moe_ffn(P, H, P, P, T, 8, 128, P, P, H, 1536, P, H, ws, nbytes, None)
+    assert moe(4, 4016, P, 1 << 30) == bi.BI_ERR_UNSUPPORTED
+    assert moe(4, 4096, None, 1 << 30) == bi.BI_ERR_WORKSPACE
+    assert moe(4, 4096, ctypes.c_void_p(256), 16) == bi.BI_ERR_WORKSPACE
+    assert moe(0, 4096, None, 0) == bi.BI_OK
+    assert lib.bi_moe_workspace_bytes(2048, 8, 128, 4096, 1536) >= 2048 * 8 * (2 * 1536 + 4 * 4096)
     # a 64-row slice of W spanning 2^31 bytes cannot be addressed by one buffer resource
     assert lib.bi_gemm(P, 64, P, 1 << 25, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_UNSUPPORTED
     assert lib.bi_gemm(P, 1 << 25, P, 64, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_UNSUPPORTED

@@ -68,6 +68,18 @@ def rows_for_requests(requests: Sequence[int], width: int, base: int, kind: str 
         if len(requests) else torch.empty((0, width), dtype=torch.bfloat16, device=device)
 
 
+def moe_weights(num_experts: int, hidden: int, ffn: int, base: int, std_up: float = 0.02,
+                std_down: float = 0.02, device="cpu"):
+    """Expert weights w_up [E, ffn, hidden] and w_down [E, hidden, ffn] (bf16),
+    one seeded draw per expert and matrix."""
+    w_up = torch.empty((num_experts, ffn, hidden), dtype=torch.bfloat16, device=device)
+    w_down = torch.empty((num_experts, hidden, ffn), dtype=torch.bfloat16, device=device)
+    for e in range(num_experts):
+        w_up[e] = randn_bf16((ffn, hidden), base, "w", WEIGHTS + 2 * e + 1, std=std_up, device=device)
+        w_down[e] = randn_bf16((hidden, ffn), base, "w", WEIGHTS + 2 * e + 2, std=std_down, device=device)
+    return w_up, w_down
+
+
 # ---------------------------------------------------------------- paged KV cache
 
 @dataclass
