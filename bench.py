@@ -384,6 +384,33 @@ def kernel_table(torch, bi, W, step, reps, everything):
     return out
 
 
+# ---------------------------------------------------------------- HBM traffic (rocprofv3 counters)
+
+COUNTERS_MD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_step_b256_hbm_counters.md")
+DECODE_SOURCES = ["attn_decode.hip", "attn_chunk.hpp", "kv_layout.hpp", "bi_common.hpp"]
+
+
+def decode_traffic():
+    """HBM bytes per bi_attn_decode launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary (calibrated against a plain copy), or None when the decode sources have
+    changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(COUNTERS_MD).read()
+    except OSError:
+        return None
+    m = re.search(r"traffic bi_attn_decode bytes_per_launch=(\d+) sources_sha256_16=([0-9a-f]+)", text)
+    if not m:
+        return None
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "invariant_bi_rmsnorm_02_amd", "csrc")
+    for name in DECODE_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return int(m.group(1)) if h.hexdigest()[:16] == m.group(2) else None
+
+
 # ---------------------------------------------------------------- CPU oracle baseline
 
 def cpu_baseline(torch, W, step, sample, min_seconds=10.0, max_reps=50):
@@ -500,7 +527,9 @@ def main():
                    "step_bytes": nbytes, "step_flops": step.step_flops(), "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "bi_attn_decode (chunk kernel + merge kernel)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated; "
+                                     "profiles/decode_step_b256_hbm_counters.md)",
                      "avg_us": round(attn_us, 2), "algorithmic_bytes": attn_bytes},
     }
     if args.kernels != "none":
