@@ -257,13 +257,15 @@ class DecodeStep:
 
 # ---------------------------------------------------------------- per-kernel table
 
+def copies(w, total=768 << 20):
+    """Rotating weight copies so the 256 MB Infinity Cache cannot serve repeated GEMM launches."""
+    n = max(1, min(16, total // (w.numel() * 2)))
+    return [w] + [w.clone() for _ in range(n - 1)]
+
+
 def kernel_table(torch, bi, W, step, reps, everything):
     out = []
     dev = "cuda"
-    # Rotating weight copies so the 256 MB Infinity Cache cannot serve repeated GEMM launches.
-    def copies(w, total=768 << 20):
-        n = max(1, min(16, total // (w.numel() * 2)))
-        return [w] + [w.clone() for _ in range(n - 1)]
     wq, wu, wd = copies(step.w_qkv), copies(step.w_up), copies(step.w_down)
     for B in (1, 8, 64, 256):
         if B > step.B:
@@ -380,6 +382,63 @@ def kernel_table(torch, bi, W, step, reps, everything):
         out.append(entry("attn decode 64/4 D128", us, bytes_decode(lens, 64, 4, 128), flops_decode(lens, 64, 128),
                          extra={"B": B, "sum_L": sum(lens)}))
         del kc, vc
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------- cost of invariance
+
+def cost_of_invariance(torch, bi, step, reps):
+    """Each op of the decode step at B = 1, 8, 64, 256: libbi.so against the
+    shape-adaptive comparator of libbi_adaptive.so (split-K GEMM, fixed
+    split-count decode, split-reduction RMSNorm) on the same inputs.  cost =
+    t_invariant / t_adaptive - 1; mismatched = output elements whose bits
+    differ from libbi.so's (which are the same at every batch size)."""
+    from invariant_bi_rmsnorm_02_amd import adaptive as A
+    dev = "cuda"
+    out = []
+
+    def mism(a, b):
+        torch.cuda.synchronize()
+        return int((a.view(torch.int16) != b.view(torch.int16)).sum().item())
+
+    wq, wu, wd = copies(step.w_qkv), copies(step.w_up), copies(step.w_down)
+    for B in (1, 8, 64, 256):
+        if B > step.B:
+            continue
+        x, h = step.x[:B], step.h[:B]
+        ha = torch.empty_like(h)
+        wsn = torch.empty((max(256, A.lib().bia_rmsnorm_workspace_bytes(B, 4096)),), dtype=torch.uint8, device=dev)
+        ti = time_fn(torch, lambda i=0: bi.bi_rmsnorm(x, step.g1, EPS, out=h), reps)
+        ta = time_fn(torch, lambda i=0: A.bia_rmsnorm(x, step.g1, EPS, out=ha, workspace=wsn), reps)
+        out.append({"op": "rmsnorm [B,4096]", "B": B, "us_invariant": round(ti[0], 2), "us_adaptive": round(ta[0], 2),
+                    "cost": round(ti[0] / ta[0] - 1, 3), "splits": A.rmsnorm_slices(B, 4096),
+                    "mismatched": mism(ha, h), "elements": ha.numel()})
+        for name, src, ws_, dst in (("gemm qkv 4096->6144", h, wq, step.qkv[:B]),
+                                    ("gemm up 4096->12288", step.h2[:B], wu, step.up[:B]),
+                                    ("gemm down 12288->4096", step.up[:B], wd, step.down[:B])):
+            n, k = ws_[0].shape
+            da = torch.empty_like(dst)
+            wsg = torch.empty((max(256, A.lib().bia_gemm_workspace_bytes(B, n, k)),), dtype=torch.uint8, device=dev)
+            ti = time_fn(torch, lambda i=0: bi.bi_gemm(src, ws_[i % len(ws_)], out=dst), reps)
+            ta = time_fn(torch, lambda i=0: A.bia_gemm(src, ws_[i % len(ws_)], out=da, workspace=wsg), reps)
+            bi.bi_gemm(src, ws_[0], out=dst)
+            A.bia_gemm(src, ws_[0], out=da, workspace=wsg)
+            out.append({"op": name, "B": B, "us_invariant": round(ti[0], 2), "us_adaptive": round(ta[0], 2),
+                        "cost": round(ti[0] / ta[0] - 1, 3), "splits": A.gemm_splits(B, n, k),
+                        "mismatched": mism(da, dst), "elements": da.numel()})
+        q, attn = step.q[:B], step.attn[:B]
+        aa = torch.empty_like(attn)
+        bt, lt = step.bt[:B], step.lens_t[:B]
+        wsa = torch.empty((A.lib().bia_attn_decode_workspace_bytes(B, 32, 8, 128),), dtype=torch.uint8, device=dev)
+        ti = time_fn(torch, lambda i=0: bi.bi_attn_decode(q, step.kc, step.vc, bt, lt, 4096, step.scale, out=attn,
+                                                          workspace=step.ws), reps)
+        ta = time_fn(torch, lambda i=0: A.bia_attn_decode(q, step.kc, step.vc, bt, lt, 4096, step.scale, out=aa,
+                                                          workspace=wsa), reps)
+        out.append({"op": "attn decode 32/8 D128", "B": B, "us_invariant": round(ti[0], 2),
+                    "us_adaptive": round(ta[0], 2), "cost": round(ti[0] / ta[0] - 1, 3),
+                    "splits": A.decode_splits(B, 8), "mismatched": mism(aa, attn), "elements": aa.numel()})
+    del wq, wu, wd
     torch.cuda.empty_cache()
     return out
 
@@ -535,6 +594,8 @@ def main():
     if args.kernels != "none":
         print("[bench] per-kernel table", file=sys.stderr, flush=True)
         result["kernels"] = kernel_table(torch, bi, W, step, args.reps, args.kernels == "all")
+        print("[bench] cost of invariance", file=sys.stderr, flush=True)
+        result["cost_of_invariance"] = cost_of_invariance(torch, bi, step, args.reps)
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(torch, W, step, args.cpu_sample)

@@ -1,4 +1,8 @@
-"""Build libbi.so (HIP for gfx950) in-tree with hipcc.
+"""Build libbi.so and libbi_adaptive.so (HIP for gfx950) in-tree with hipcc.
+
+libbi_adaptive.so holds the shape-adaptive comparators (include/bi_adaptive.h)
+and the two libbi kernels they fall back to (GEMM, RMSNorm); nothing in
+libbi.so depends on it.
 
 Every translation unit is compiled with -ffp-contract=off and without fast
 math, so each floating-point expression runs exactly as written (the
@@ -17,6 +21,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbi.so")
+ADAPTIVE_LIB = os.path.join(PKG, "libbi_adaptive.so")
+ADAPTIVE_SOURCES = ["adaptive.hip"]
+ADAPTIVE_SHARED = ["gemm.hip", "rmsnorm.hip"]   # libbi objects linked into the comparator library
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "rmsnorm.hip", "gemm.hip", "kv_append.hip", "attn_decode.hip",
@@ -38,18 +45,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + ADAPTIVE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in ADAPTIVE_SOURCES + ADAPTIVE_SHARED], ADAPTIVE_LIB)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {ADAPTIVE_LIB}", file=sys.stderr)
     return LIB
 
 

@@ -1,6 +1,7 @@
 """The C-ABI library on the CPU host: it loads, exports every function that
 include/bi.h declares, and rejects bad arguments before touching the GPU."""
 import ctypes
+import os
 
 import pytest
 
@@ -75,3 +76,19 @@ def test_workspace_size_formula(lib):
     raw = 3 * 32 * 4 * (128 + 4) * 4
     assert n == (raw + 255) // 256 * 256
     assert bi.bi_attn_decode_workspace_bytes(1, 1, 64, 256) == 256 * ((68 * 4 + 255) // 256)
+
+
+def test_adaptive_library_exports_its_header():
+    """libbi_adaptive.so (the shape-adaptive comparators) loads and exports
+    every function include/bi_adaptive.h declares."""
+    import re
+    from invariant_bi_rmsnorm_02_amd import adaptive as A
+    text = open(os.path.join(os.path.dirname(bi.HEADER), "bi_adaptive.h")).read()
+    names = sorted(set(re.findall(r"^\s*(?:int32_t|size_t|bi_status)\s+(bia_\w+)\s*\(", text, re.M)))
+    assert len(names) == 9
+    lib = A.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert A.gemm_splits(1, 6144, 4096) > 1 and A.gemm_splits(2300, 6144, 4096) == 1
+    assert A.decode_splits(1, 8) == 64 and A.decode_splits(256, 8) == 1
+    assert lib.bia_gemm(None, 64, None, 64, None, 64, 4, 4, 64, None, 0, None) == bi.BI_ERR_INVALID_ARG

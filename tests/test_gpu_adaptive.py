@@ -1,0 +1,98 @@
+"""The shape-adaptive comparators (libbi_adaptive.so) on the GPU.
+
+They must be correct (parity with the fp64 oracle), reduce to libbi.so's
+bits where their heuristic picks one split, and - the negative control of the
+pages' property - give a request different bits at different batch sizes,
+which is what the batch-invariant library exists to prevent."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from _helpers import O, assert_bf16_close, assert_bitwise, bi, ensure_lib, f64, log_case
+from test_gpu_attention import Batch
+
+from invariant_bi_rmsnorm_02_amd import adaptive as A
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+    A.lib()
+
+
+def _mismatch(a, b):
+    return int((a.contiguous().view(torch.int16) != b.contiguous().view(torch.int16)).sum().item())
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 6144, 4096), (37, 1024, 512), (256, 4096, 12288), (5, 136, 96)])
+def test_splitk_gemm_parity(m, n, k):
+    log_case(f"split-K gemm m={m} n={n} k={k} splits={A.gemm_splits(m, n, k)}")
+    a = W.rows_for_requests(range(m), k, W.SEED_DECODE)
+    w = W.randn_bf16((n, k), W.SEED_DECODE, "w", W.WEIGHTS + 77, std=0.02)
+    c = A.bia_gemm(a.to(DEV), w.to(DEV)).cpu()
+    rows = list(range(min(m, 8)))
+    assert_bf16_close(c[rows], O.gemm(f64(a[rows]), f64(w)), "split-K gemm")
+
+
+def test_splitk_gemm_one_split_is_libbi():
+    m, n, k = 2300, 1024, 512
+    assert A.gemm_splits(m, n, k) == 1
+    a = W.rows_for_requests(range(m), k, W.SEED_DECODE).to(DEV)
+    w = W.randn_bf16((n, k), W.SEED_DECODE, "w", W.WEIGHTS + 78, std=0.02).to(DEV)
+    assert_bitwise(A.bia_gemm(a, w), bi.bi_gemm(a, w), "one split == bi_gemm")
+
+
+def test_splitk_gemm_is_not_batch_invariant():
+    """Row 0 alone (6 K slices) against row 0 in a 2300-row batch (one slice)."""
+    n, k = 6144, 4096
+    assert A.gemm_splits(1, n, k) > 1 and A.gemm_splits(2300, n, k) == 1
+    a = W.rows_for_requests(range(2300), k, W.SEED_DECODE).to(DEV)
+    w = W.randn_bf16((n, k), W.SEED_DECODE, "w", W.WEIGHTS + 79, std=0.02).to(DEV)
+    alone = A.bia_gemm(a[:1].contiguous(), w)
+    batched = A.bia_gemm(a, w)[:1]
+    assert _mismatch(alone, batched) > 0
+    # the invariant library gives row 0 the same bits either way
+    assert_bitwise(bi.bi_gemm(a[:1].contiguous(), w), bi.bi_gemm(a, w)[:1], "bi_gemm row 0")
+
+
+def test_split_decode_parity_and_negative_control():
+    hq, hkv, d = 32, 8, 128
+    lens = W.decode_lengths(range(64), W.SEED_DECODE)
+    big = Batch(range(64), lens, hq, hkv, d, W.SEED_DECODE)
+    out64, _ = A.bia_attn_decode(big.q, big.kc, big.vc, big.bt, big.lens, max(lens), big.scale)
+    one = Batch([0], lens[:1], hq, hkv, d, W.SEED_DECODE)
+    log_case(f"split decode L0={lens[0]} splits B=1: {A.decode_splits(1, hkv)}, B=64: {A.decode_splits(64, hkv)}")
+    out1, _ = A.bia_attn_decode(one.q, one.kc, one.vc, one.bt, one.lens, lens[0], one.scale)
+    ref, _ = big.oracle([0, 5, 63])
+    got = out64[[0, 5, 63]].cpu()
+    for i in range(3):
+        assert_bf16_close(got[i], ref[i], f"split decode batch row {i}")
+    assert_bf16_close(out1.cpu()[0], ref[0], "split decode alone")
+    assert _mismatch(out1[0], out64[0]) > 0
+    # libbi: request 0 has the same bits alone and in the batch
+    a1, _ = one.decode()
+    a64, _ = big.decode()
+    assert_bitwise(a1[0], a64[0], "bi_attn_decode request 0")
+
+
+def test_split_rmsnorm_parity_and_negative_control():
+    """255 rows (two slices per row) against the same rows in a 256-row batch
+    (one slice).  The slices change the fp32 sum of squares only in its last
+    bits, which moves a bf16 output about once in 2^15 elements, so the
+    control needs many rows to show the difference."""
+    h = 4096
+    x = W.rows_for_requests(range(256), h, W.SEED_DECODE).to(DEV)
+    g = W.randn_bf16((h,), W.SEED_TINY, "gamma", W.WEIGHTS, std=0.1, mean=1.0).to(DEV)
+    assert A.rmsnorm_slices(255, h) > 1 and A.rmsnorm_slices(256, h) == 1
+    small = A.bia_rmsnorm(x[:255].contiguous(), g, 1e-6)
+    full = A.bia_rmsnorm(x, g, 1e-6)
+    rows = [0, 100, 254]
+    assert_bf16_close(small[rows].cpu(), O.rmsnorm(f64(x[rows]), f64(g), 1e-6), "split rmsnorm")
+    assert_bitwise(full, bi.bi_rmsnorm(x, g, 1e-6), "one slice == bi_rmsnorm")
+    n = _mismatch(small, full[:255])
+    log_case(f"split rmsnorm mismatches rows 0-254: {n}")
+    assert n > 0
