@@ -12,6 +12,8 @@
 // Kernel 2 (grid: q head x sequence): the ascending fold of those partials,
 // normalisation and bf16 output.  No atomics, no cross-workgroup ordering:
 // every value is written by exactly one workgroup.
+#include <algorithm>
+
 #include "attn_chunk.hpp"
 #include "kv_layout.hpp"
 #include "launch.hpp"
@@ -38,7 +40,11 @@ struct GlobalChunk {
   int log2_ps;
   int chunk_start;
   int lim;
-  int page_reg;
+  int max_pages;
+  int num_pages;
+  int page_reg;   // raw block-table entry of this lane's logical page (validated where used)
+  int lane;       // lane index, re-materialised per chunk so that per-lane address
+                  // terms are recomputed rather than held across the chunk loop
 
   struct Frags {
     u32x4_t k[2][D / 32];
@@ -47,38 +53,56 @@ struct GlobalChunk {
     int vnv;    // keys of this lane's V group that exist (<= 0: none)
   };
 
-  // active == false points every load at the pool's first bytes (the result
-  // is never used): the loads are still issued so that every path through the
-  // caller's loop has the same loads in flight.
+  // Whether the page holding chunk-relative key `key` may be read: its logical
+  // index is inside the block table, the page starts before `lim`, and the
+  // table entry names a page of the pool.
+  __device__ __forceinline__ bool page_ok(int key, int page) const {
+    const int lp = (chunk_start + key) >> log2_ps;
+    return lp < max_pages && (lp << log2_ps) < lim && page >= 0 && page < num_pages;
+  }
+
+  // Raw block-table entries of `nch` chunks from `chunk`, one per lane as in
+  // load_chunk_pages, read from a clamped (always valid) index; nothing here
+  // waits for the load, so a later chunk's entries can be fetched early.
+  __device__ __forceinline__ static int raw_pages(const int32_t* bt_row, int max_pages, int chunk, int log2_ps) {
+    const int ppc = kChunk >> log2_ps;
+    const int lp = chunk * ppc + ((threadIdx.x & 63) % ppc);
+    return bt_row[min(lp, max_pages - 1)];
+  }
+
+  // active == false, or a page that may not be read, points a lane's loads at
+  // the pool's first tile block (the result is never used; the constant
+  // per-load offsets stay below the 4 KiB that one page of any supported
+  // geometry spans): the loads are still issued so that every path through
+  // the caller's loop has the same loads in flight, and the constant offsets
+  // fold into the instructions.
   __device__ __forceinline__ void fetch(int s, Frags& f, bool active) const {
-    const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+    const int l16 = lane & 15, g = lane >> 4;
     const int ps = 1 << log2_ps;
+    const int64_t page_elems = (int64_t)(num_kv_heads << log2_ps) * D;   // one page, all kv heads
     // K: lanes l16 < 8 read tile 0 of the sub-block, l16 >= 8 tile 1; in both,
     // the 8 lanes of a group cover 128 contiguous bytes (slots 8 b .. 8 b + 7).
     const int ktile_key = kSub * s + kTile * (l16 >> 3);       // key of the tile's token 0
     const int kpage = __shfl(page_reg, ktile_key >> log2_ps, kWave);
-    f.kok = active && kpage >= 0;
-    const int64_t kb = f.kok ? tile_base(kpage, 0, ktile_key & (ps - 1), num_kv_heads, log2_ps, D) + head_k +
-                                   (int64_t)g * 128 + (l16 & 7) * 8
-                             : 0;
+    f.kok = active && page_ok(ktile_key, kpage);
+    const uint16_t* kp = kc + (f.kok ? kpage * page_elems + head_k : 0) +
+                         (f.kok ? ((ktile_key & (ps - 1)) >> 4) * (kTile * D) + g * 128 + (l16 & 7) * 8 : 0);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks)
-        f.k[b][ks] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(kc + kb + (f.kok ? 4 * ks * 128 + 8 * b * 8 : 0)));
+        f.k[b][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + 4 * ks * 128 + 8 * b * 8));
     // V: lane group g holds keys 8 g .. 8 g + 7 of the sub-block = tile g / 2,
     // half g % 2; the 16 lanes of a group cover 256 contiguous bytes.
     const int vtile_key = kSub * s + kTile * (g >> 1);
     const int vpage = __shfl(page_reg, vtile_key >> log2_ps, kWave);
-    const bool vok = active && vpage >= 0;
+    const bool vok = active && page_ok(vtile_key, vpage);
     f.vnv = vok ? lim - (chunk_start + kSub * s + 8 * g) : 0;
-    const int64_t vb = vok ? tile_base(vpage, 0, vtile_key & (ps - 1), num_kv_heads, log2_ps, D) + head_v +
-                                 (g & 1) * 128 + l16 * 8
-                           : 0;
+    const uint16_t* vp = vc + (vok ? vpage * page_elems + head_v : 0) +
+                         (vok ? ((vtile_key & (ps - 1)) >> 4) * (kTile * D) + (g & 1) * 128 + l16 * 8 : 0);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-      f.v[dt] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vc + vb + (vok ? dt * 256 : 0)));
+      f.v[dt] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vp + dt * 256));
   }
 
   // Branch-free masking, applied right where each half is consumed so the
@@ -97,14 +121,15 @@ struct GlobalChunk {
 };
 
 template <int D>
-__global__ __launch_bounds__(64) void attn_decode_partial_kernel(
+__global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table,
     int max_pages, const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq, int Hkv, int log2_ps,
-    float scale_log2, float* __restrict__ ws, int max_chunks) {
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    float scale_log2, float* __restrict__ ws, int max_chunks, int chunks_per_wave) {
+  const int c_first = blockIdx.x * chunks_per_wave, h = blockIdx.y, b = blockIdx.z;
   const int L = min(seq_lens[b], max_seq_len);
-  if (c * kChunk >= L) return;
+  if (c_first * kChunk >= L) return;
+  const int c_end = min((L + kChunk - 1) / kChunk, c_first + chunks_per_wave);
   const int G = Hq / Hkv;
   const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
   const bool row_ok = n < G;
@@ -116,6 +141,7 @@ __global__ __launch_bounds__(64) void attn_decode_partial_kernel(
     qf[0][ks] = row_ok ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : zero4();
 
   const int ps = 1 << log2_ps;
+  const int32_t* bt_row = block_table + (int64_t)b * max_pages;
   GlobalChunk<D> src;
   src.kc = kc;
   src.vc = vc;
@@ -123,44 +149,67 @@ __global__ __launch_bounds__(64) void attn_decode_partial_kernel(
   src.head_v = (int64_t)h * ps * D;
   src.num_kv_heads = Hkv;
   src.log2_ps = log2_ps;
-  src.chunk_start = c * kChunk;
+  src.chunk_start = c_first * kChunk;
   src.lim = L;
-  src.page_reg = load_chunk_pages(block_table + (int64_t)b * max_pages, max_pages, c, log2_ps, L, num_pages);
+  src.max_pages = max_pages;
+  src.num_pages = num_pages;
+  src.page_reg = GlobalChunk<D>::raw_pages(bt_row, max_pages, c_first, log2_ps);
+  src.lane = lane;
+  float* rec = ws + (((int64_t)b * Hq + h * G + n) * max_chunks + c_first) * (D + 4);
 
-  const int nvalid[1] = {min(kChunk, L - c * kChunk)};
-  const int n_sub = (nvalid[0] + kSub - 1) / kSub;
-  ChunkAcc<D, 1> acc;
-  chunk_init(acc);
-  // Ping-pong over sub-blocks: the loads of sub-block s + 1 are always in
-  // flight while sub-block s is computed.
+  // Chunks c_first .. c_end - 1, one after the other.  Each chunk is reduced
+  // from a fresh state and written to its own record, exactly as a wavefront
+  // of its own would; the sub-block prefetch runs on across the boundary into
+  // the next chunk (whose page ids are loaded one chunk ahead).
   using Src = GlobalChunk<D>;
   typename Src::Frags fa, fb;
   SubProbs<1> sp;
+  ChunkAcc<D, 1> acc;
   src.fetch(0, fa, true);
+  for (int c = c_first; c < c_end; ++c) {
+    int ln = threadIdx.x & 63;
+    asm volatile("" : "+v"(ln));
+    src.lane = ln;
+    const bool more = c + 1 < c_end;
+    const int next_pages = GlobalChunk<D>::raw_pages(bt_row, max_pages, c + 1, log2_ps);
+    const int nvalid[1] = {min(kChunk, L - c * kChunk)};
+    const int n_sub = (nvalid[0] + kSub - 1) / kSub;
+    chunk_init(acc);
+    // Ping-pong over sub-blocks: the loads of sub-block s + 1 are always in
+    // flight while sub-block s is computed.  After the last fetch of a full
+    // chunk, `src` moves on to the next chunk and fetches its sub-block 0
+    // (masks are taken at fetch time, so the sub-block still being computed
+    // does not need `src`).
 #pragma unroll
-  for (int s = 0; s < kSubs; s += 2) {
-    src.fetch(s + 1, fb, s + 1 < n_sub);
-    Src::mask_k(fa);
-    chunk_scores<D, 1>(acc, fa.k, qf, nvalid, s, scale_log2, sp);
-    Src::mask_v(fa);
-    chunk_values<D, 1>(acc, fa.v, sp);
-    if (s + 1 >= n_sub) break;
-    src.fetch(s + 2, fa, s + 2 < n_sub);
-    Src::mask_k(fb);
-    chunk_scores<D, 1>(acc, fb.k, qf, nvalid, s + 1, scale_log2, sp);
-    Src::mask_v(fb);
-    chunk_values<D, 1>(acc, fb.v, sp);
-    if (s + 2 >= n_sub) break;
-  }
-
-  if (row_ok) {
-    float* rec = ws + (((int64_t)b * Hq + h * G + n) * max_chunks + c) * (D + 4);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = acc.o[0][dt];
-    if (g == 0) {
-      rec[D] = acc.m[0];
-      rec[D + 1] = acc.l[0];
+    for (int s = 0; s < kSubs; s += 2) {
+      src.fetch(s + 1, fb, s + 1 < n_sub);
+      Src::mask_k(fa);
+      chunk_scores<D, 1>(acc, fa.k, qf, nvalid, s, scale_log2, sp);
+      Src::mask_v(fa);
+      chunk_values<D, 1>(acc, fa.v, sp);
+      if (s + 1 >= n_sub) break;
+      if (s + 2 < kSubs) {
+        src.fetch(s + 2, fa, s + 2 < n_sub);
+      } else {
+        src.chunk_start += kChunk;
+        src.page_reg = next_pages;
+        src.fetch(0, fa, more);
+      }
+      Src::mask_k(fb);
+      chunk_scores<D, 1>(acc, fb.k, qf, nvalid, s + 1, scale_log2, sp);
+      Src::mask_v(fb);
+      chunk_values<D, 1>(acc, fb.v, sp);
+      if (s + 2 >= n_sub) break;
     }
+    if (row_ok) {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = acc.o[0][dt];
+      if (g == 0) {
+        rec[D] = acc.m[0];
+        rec[D + 1] = acc.l[0];
+      }
+    }
+    rec += D + 4;
   }
 }
 
@@ -196,16 +245,30 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
   }
 }
 
+// Consecutive chunks per wavefront.  This is scheduling only: every chunk is
+// reduced and recorded the same way whichever wavefront runs it, so the bits of
+// a result do not depend on it (the batch-invariance tests compare batches that
+// take both branches).  Measured on MI355X: once one wavefront per (sequence,
+// kv head) already fills the GPU (kDecodeWaves = 8 per CU), wavefronts that
+// stream a whole sequence use HBM better than one wavefront per chunk; below
+// that, one chunk per wavefront keeps the most loads in flight.
+constexpr int kDecodeWaves = 2048;
+int decode_chunks_per_wave(int num_seqs, int num_kv_heads, int max_chunks) {
+  return (int64_t)num_seqs * num_kv_heads >= kDecodeWaves ? max_chunks : 1;
+}
+
 template <int D>
 hipError_t launch(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
                   int max_seq_len, void* out, float* lse, void* workspace, hipStream_t stream) {
   const int max_chunks = (max_seq_len + kChunk - 1) / kChunk;
   float* ws = static_cast<float*>(workspace);
-  hipLaunchKernelGGL(attn_decode_partial_kernel<D>, dim3(max_chunks, g.num_kv_heads, num_seqs), dim3(64), 0,
+  const int cpw = decode_chunks_per_wave(num_seqs, g.num_kv_heads, max_chunks);
+  hipLaunchKernelGGL(attn_decode_partial_kernel<D>, dim3((max_chunks + cpw - 1) / cpw, g.num_kv_heads, num_seqs),
+                     dim3(64), 0,
                      stream, static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(g.k_cache),
                      static_cast<const uint16_t*>(g.v_cache), g.num_pages, g.block_table, g.max_pages_per_seq,
                      seq_lens, max_seq_len, g.num_q_heads, g.num_kv_heads, g.log2_page, g.scale_log2, ws,
-                     max_chunks);
+                     max_chunks, cpw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(64), 0, stream, ws,
