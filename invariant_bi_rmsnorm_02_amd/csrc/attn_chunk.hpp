@@ -93,14 +93,26 @@ __device__ __forceinline__ void chunk_scores(ChunkAcc<D, NB>& a, const u32x4_t (
     }
     float t[8];
     float mx = -INFINITY;
+    // When every column of the wavefront sees the whole sub-block the mask
+    // selects nothing; skipping it leaves every value as it is.
+    if (__all(kSub * (s + 1) <= n_valid[nb])) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kSub * s + 8 * g + 4 * b + i;
-        t[4 * b + i] = key < n_valid[nb] ? S[b][i] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, t[4 * b + i]);
-      }
+        for (int i = 0; i < 4; ++i) {
+          t[4 * b + i] = S[b][i] * scale_log2;
+          mx = fmaxf(mx, t[4 * b + i]);
+        }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kSub * s + 8 * g + 4 * b + i;
+          t[4 * b + i] = key < n_valid[nb] ? S[b][i] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, t[4 * b + i]);
+        }
+    }
     mx = fmaxf(mx, shfl_xor(mx, 16));
     mx = fmaxf(mx, shfl_xor(mx, 32));
     const float mn = fmaxf(a.m[nb], mx);
@@ -129,12 +141,17 @@ __device__ __forceinline__ void chunk_values(ChunkAcc<D, NB>& a, const u32x4_t (
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float alpha = sp.alpha[nb];
+    // alpha == 1 (the running max did not move) in every lane: o * 1 is o, so
+    // the rescale is skipped without changing a bit.
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      f32x4_t o = a.o[nb][dt];
-      o = f32x4_t{o[0] * alpha, o[1] * alpha, o[2] * alpha, o[3] * alpha};
-      a.o[nb][dt] = mfma_16x16x32(vf[dt], sp.pb[nb], o);
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const f32x4_t o = a.o[nb][dt];
+        a.o[nb][dt] = f32x4_t{o[0] * alpha, o[1] * alpha, o[2] * alpha, o[3] * alpha};
+      }
     }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) a.o[nb][dt] = mfma_16x16x32(vf[dt], sp.pb[nb], a.o[nb][dt]);
   }
 }
 

@@ -9,9 +9,10 @@
 // 16-row column blocks.  The chunk's own keys/values are already in the paged
 // cache, so cached and new tokens are read through one path.  The workgroup
 // walks the 256-key chunks in ascending order, 32 keys at a time: each K/V
-// sub-block is staged once into LDS (double-buffered, the next one loading from
-// HBM while the current one is used) and every wavefront runs the same chunk
-// step as decode on it (causal mask: a query at position p sees keys 0..p).
+// sub-block is fetched from HBM four sub-blocks ahead into a register ring,
+// staged once into LDS (double-buffered) and every wavefront runs the same
+// chunk step as decode on it (causal mask: a query at position p sees keys
+// 0..p).  Block-table entries are read one chunk ahead.
 // After a chunk each column folds it with the same merge step as decode, so row
 // p is bitwise what decode returns at seq_len p + 1.
 #include "attn_chunk.hpp"
@@ -74,40 +75,56 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
   }
 
   const int ps = 1 << log2_ps;
+  const int ppc = kChunk >> log2_ps;   // pages per chunk
   const int32_t* bt = block_table + (int64_t)sq * max_pages;
-  auto page_at = [&](int p) -> int {   // physical page holding position p, or -1
-    const int lp = p >> log2_ps;
-    if (p >= lim || lp >= max_pages) return -1;
-    const int pg = bt[lp];
-    return (pg >= 0 && pg < num_pages) ? pg : -1;
-  };
+  const int64_t page_elems = (int64_t)(Hkv << log2_ps) * D;
+  const int64_t head_off = (int64_t)h * ps * D;
+  // Raw block-table entries of chunk c, one logical page per lane (lane l:
+  // page c * ppc + l % ppc), read from a clamped index; validated where used,
+  // so loading the next chunk's entries early never waits.
+  auto raw_pages = [&](int c) { return bt[min(c * ppc + (lane % ppc), max_pages - 1)]; };
 
-  // Global -> register staging of sub-block u (chunk u / 8, sub-block u % 8):
-  // piece pc covers elements 8 pc .. 8 pc + 7 of the sub-block's two tiles.
-  u32x4_t rk[NP], rv[NP];
-  auto load_sub = [&](int u) {
-    const int base = (u >> 3) * kChunk + (u & 7) * kSub;
+  // Global -> register staging of sub-block u (chunk u / 8, sub-block u % 8),
+  // P sub-blocks ahead of the LDS copy: piece pc covers elements 8 pc .. 8 pc
+  // + 7 of the sub-block's two tiles.  `pages` holds the raw entries of the
+  // sub-block's chunk.  Loads are unconditional (a page that may not be read
+  // points at the pool start); the masks are applied when the ring slot is
+  // copied into LDS.
+  constexpr int P = 4;                 // divides the 8 sub-blocks of a chunk: ring slot of u is u % P
+  struct Stage {
+    u32x4_t k[NP], v[NP];
+    int ok;                            // bit i: piece i's page may be read
+  };
+  Stage ring[P];
+  auto piece_t0 = [&](int u, int i) {  // position of piece i's tile token 0 in sub-block u
+    return (u >> 3) * kChunk + (u & 7) * kSub + kTile * (((tid + i * kThreads) * 8) / TE);
+  };
+  auto load_sub = [&](int u, int pages, Stage& st) {
+    st.ok = 0;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int pc = tid + i * kThreads;
-      const int tile = (pc * 8) / TE, w = (pc * 8) % TE;
-      const int t0 = base + kTile * tile;                      // position of the tile's token 0
-      const int pg = page_at(t0);
-      const int64_t tb = pg >= 0 ? tile_base(pg, h, t0 & (ps - 1), Hkv, log2_ps, D) + w : 0;
-      const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(kc + tb);
-      const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(vc + tb);
-      // K rows past lim are masked in the scores; only a missing page is zeroed.
-      rk[i] = pg >= 0 ? kv : zero4();
-      // V piece: one dim of 8 tokens, 8 * ((w / 128) % 2) .. +7 of the tile.
-      rv[i] = pg >= 0 ? keep_first(vv, lim - (t0 + 8 * ((w >> 7) & 1))) : zero4();
+      const int w = ((tid + i * kThreads) * 8) % TE;
+      const int t0 = piece_t0(u, i);
+      const int lp = t0 >> log2_ps;
+      const int raw = __shfl(pages, (t0 & (kChunk - 1)) >> log2_ps, kWave);
+      const bool ok = t0 < lim && lp < max_pages && raw >= 0 && raw < num_pages;
+      const int64_t tb = ok ? raw * page_elems + head_off + (int64_t)((t0 & (ps - 1)) >> 4) * TE + w : 0;
+      st.k[i] = *reinterpret_cast<const u32x4_t*>(kc + tb);
+      st.v[i] = *reinterpret_cast<const u32x4_t*>(vc + tb);
+      st.ok |= ok ? (1 << i) : 0;
     }
   };
-  auto store_sub = [&](int buf) {
+  auto store_sub = [&](int buf, int u, const Stage& st) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int pc = tid + i * kThreads;
-      *reinterpret_cast<u32x4_t*>(&sK[buf][pc * 8]) = rk[i];
-      *reinterpret_cast<u32x4_t*>(&sV[buf][pc * 8]) = rv[i];
+      const bool ok = (st.ok >> i) & 1;
+      // K rows past lim are masked in the scores; only a missing page is zeroed.
+      *reinterpret_cast<u32x4_t*>(&sK[buf][pc * 8]) = ok ? st.k[i] : zero4();
+      // V piece: one dim of 8 tokens (half (w / 128) % 2 of the tile); tokens
+      // past lim are zeroed.
+      const int vt0 = piece_t0(u, i) + 8 * (((pc * 8) % TE >> 7) & 1);
+      *reinterpret_cast<u32x4_t*>(&sV[buf][pc * 8]) = ok ? keep_first(st.v[i], lim - vt0) : zero4();
     }
   };
 
@@ -128,54 +145,71 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
 
   ChunkAcc<D, kNB> ca;
   int nvalid[kNB];
-  load_sub(0);
-  store_sub(0);
+  int cur_pages = raw_pages(0), next_pages = raw_pages(1);
+#pragma unroll
+  for (int p = 0; p < P; ++p) load_sub(p, cur_pages, ring[p]);
+  store_sub(0, 0, ring[0]);
   __syncthreads();
-  for (int u = 0; u < U; ++u) {
-    const int c = u >> 3, s = u & 7;
-    if (s == 0) {
-      chunk_init(ca);
+  // Outer loop over chunks, the 8 sub-blocks of a chunk unrolled so that ring
+  // slots and LDS buffers are static: sub-block u = 8 c + s sits in ring slot
+  // s % P and LDS buffer s & 1.
+  for (int c = 0; c < nch; ++c) {
+    const int after_pages = raw_pages(c + 2);
+    chunk_init(ca);
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb)
-        nvalid[nb] = row_ok[nb] ? max(0, min(kChunk, pos[nb] + 1 - c * kChunk)) : 0;
+    for (int nb = 0; nb < kNB; ++nb)
+      nvalid[nb] = row_ok[nb] ? max(0, min(kChunk, pos[nb] + 1 - c * kChunk)) : 0;
+    const int subs = c == nch - 1 ? last_subs : kSubs;
+    // One 32-key sub-block: refill its ring slot with sub-block u + P (chunk c
+    // or c + 1; the slot was copied into LDS at the end of step u - 1), run the
+    // chunk step on LDS buffer s & 1, copy sub-block u + 1 from its slot into
+    // the other buffer.  Ring slots are named statically: slot of u is s % P.
+    auto step = [&](int s, Stage& refill, const Stage& next) {
+      const int u = c * kSubs + s;
+      load_sub(u + P, s + P < kSubs ? cur_pages : next_pages, refill);
+      if (c * kChunk + s * kSub < wave_lim) {   // some column of this wave sees a key here
+        const int buf = s & 1;
+        const int l16 = n;
+        u32x4_t kf[2][D / 32], vf[D / 16];
+        // Same operand addressing as decode, inside the LDS copy of the two tiles.
+        const int kofs = (l16 >> 3) * TE + g * 128 + (l16 & 7) * 8;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks)
+            kf[b][ks] = *reinterpret_cast<const u32x4_t*>(&sK[buf][kofs + 4 * ks * 128 + 8 * b * 8]);
+        const int vofs = (g >> 1) * TE + (g & 1) * 128 + l16 * 8;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+          vf[dt] = *reinterpret_cast<const u32x4_t*>(&sV[buf][vofs + dt * 256]);
+        SubProbs<kNB> sp;
+        chunk_scores<D, kNB>(ca, kf, qf, nvalid, s, scale_log2, sp);
+        chunk_values<D, kNB>(ca, vf, sp);
+      }
+      if (u + 1 < U) store_sub((s + 1) & 1, u + 1, next);
+      __syncthreads();
+    };
+    static_assert(P == 4 && kSubs == 8, "ring slots below are written out for P = 4");
+    for (int s4 = 0; s4 < kSubs; s4 += 4) {
+      if (s4 + 0 < subs) step(s4 + 0, ring[0], ring[1]);
+      if (s4 + 1 < subs) step(s4 + 1, ring[1], ring[2]);
+      if (s4 + 2 < subs) step(s4 + 2, ring[2], ring[3]);
+      if (s4 + 3 < subs) step(s4 + 3, ring[3], ring[0]);
     }
-    if (u + 1 < U) load_sub(u + 1);
-    if (c * kChunk + s * kSub < wave_lim) {   // some column of this wave sees a key here
-      const int buf = u & 1;
-      const int l16 = n;
-      u32x4_t kf[2][D / 32], vf[D / 16];
-      // Same operand addressing as decode, inside the LDS copy of the two tiles.
-      const int kofs = (l16 >> 3) * TE + g * 128 + (l16 & 7) * 8;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+    for (int nb = 0; nb < kNB; ++nb) {
+      if (nvalid[nb] > 0) {
+        const MergeCoef k = merge_coef(m_run[nb], ca.m[nb]);
+        l_run[nb] = merge_val(l_run[nb], ca.l[nb], k);
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-          kf[b][ks] = *reinterpret_cast<const u32x4_t*>(&sK[buf][kofs + 4 * ks * 128 + 8 * b * 8]);
-      const int vofs = (g >> 1) * TE + (g & 1) * 128 + l16 * 8;
+        for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        vf[dt] = *reinterpret_cast<const u32x4_t*>(&sV[buf][vofs + dt * 256]);
-      SubProbs<kNB> sp;
-      chunk_scores<D, kNB>(ca, kf, qf, nvalid, s, scale_log2, sp);
-      chunk_values<D, kNB>(ca, vf, sp);
-    }
-    const bool chunk_end = (s == kSubs - 1) || (u == U - 1);
-    if (chunk_end) {
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        if (nvalid[nb] > 0) {
-          const MergeCoef k = merge_coef(m_run[nb], ca.m[nb]);
-          l_run[nb] = merge_val(l_run[nb], ca.l[nb], k);
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o_run[nb][dt][i] = merge_val(o_run[nb][dt][i], ca.o[nb][dt][i], k);
-          m_run[nb] = k.m;
-        }
+          for (int i = 0; i < 4; ++i) o_run[nb][dt][i] = merge_val(o_run[nb][dt][i], ca.o[nb][dt][i], k);
+        m_run[nb] = k.m;
       }
     }
-    if (u + 1 < U) store_sub((u + 1) & 1);
-    __syncthreads();
+    cur_pages = next_pages;
+    next_pages = after_pages;
   }
 
 #pragma unroll

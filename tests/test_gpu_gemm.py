@@ -38,6 +38,23 @@ def test_gemm_integer_exact(m, n, k):
     assert np.array_equal(f64(c32), ref)
 
 
+def test_gemm_bf16_output_is_rne_of_fp32_output():
+    """The bf16 epilogue (gfx950's v_cvt_pk_bf16_f32) rounds the same fp32
+    accumulator the fp32 epilogue stores, once, to nearest with ties to even:
+    bitwise equal to the oracle's RNE encoder applied to the fp32 output, over
+    1.5 M values spanning many binades (inputs scaled by 2^-20 .. 2^20 per row)."""
+    m, n, k = 256, 6144, 256
+    a = W.randn_bf16((m, k), W.SEED_DECODE, "x", 4242)
+    scale = torch.pow(2.0, torch.linspace(-20, 20, m)).to(torch.bfloat16).unsqueeze(1)
+    a = (a * scale).to(torch.bfloat16)
+    w = W.randn_bf16((n, k), W.SEED_DECODE, "w", 4243)
+    c32 = bi.bi_gemm(a.to(DEV), w.to(DEV), out_dtype=torch.float32)
+    c16 = bi.bi_gemm(a.to(DEV), w.to(DEV))
+    torch.cuda.synchronize()
+    want = torch.from_numpy(O.f64_to_bf16_bits(c32.cpu().double().numpy()).view(np.int16))
+    assert torch.equal(c16.cpu().view(torch.int16), want)
+
+
 def test_gemm_identity_and_selector():
     k = 256
     a = W.randn_bf16((37, k), 0, "x", 7)
