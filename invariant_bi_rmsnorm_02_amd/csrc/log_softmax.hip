@@ -3,10 +3,14 @@
 // logprob of a token must not depend on what else was in the batch).
 //
 // One workgroup per row, one fixed order whatever the number of rows:
-//   thread t walks float4 vectors t, t+1024, ... keeping a running (max, sum)
-//   (the sum is rescaled when the max grows); threads are combined by a
-//   butterfly over each wavefront and the 16 wave results are folded in
-//   ascending wave order.  out = z - (max + ln sum).
+//   thread t takes its float4 vectors t, t+1024, t+2048, ... four at a time
+//   (16 values, in order); per group it takes the group max, rescales its
+//   running sum once to the new max and adds the 16 terms exp(x - max) in
+//   order; threads are combined by a butterfly over each wavefront and the 16
+//   wave results are folded in ascending wave order.  out = z - (max + ln sum).
+// The next group's loads are issued before the current group is reduced, so
+// eight 16-byte loads per thread are in flight; there are no data-dependent
+// branches.
 #include "bi_common.hpp"
 #include "launch.hpp"
 
@@ -35,19 +39,39 @@ __global__ __launch_bounds__(kLsmThreads) void log_softmax_kernel(const float* z
   const f32x4_t* zr = reinterpret_cast<const f32x4_t*>(z + row * ld_in);
   const int nvec = vocab >> 2;
 
-  MaxSum acc{-INFINITY, 0.0f};
-  for (int i = tid; i < nvec; i += kLsmThreads) {
-    const f32x4_t v = zr[i];
+  constexpr int kGroup = 4;   // float4 vectors per thread per step
+  // Loads are unconditional (a vector past the row reads the row's last
+  // vector); padding is replaced by -inf where the group is reduced, so no
+  // load waits on a branch.
+  auto load_group = [&](int j0, f32x4_t (&v)[kGroup]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = v[e];
-      if (x > acc.m) {
-        acc.s = (acc.m == -INFINITY ? 0.0f : acc.s * exp2_hw((acc.m - x) * kLog2e)) + 1.0f;
-        acc.m = x;
-      } else {
-        acc.s = acc.s + exp2_hw((x - acc.m) * kLog2e);
-      }
-    }
+    for (int q = 0; q < kGroup; ++q) v[q] = zr[min(tid + (j0 + q) * kLsmThreads, nvec - 1)];
+  };
+  MaxSum acc{-INFINITY, 0.0f};
+  const int steps = (nvec + kLsmThreads - 1) / kLsmThreads;   // vectors per thread, rounded up
+  f32x4_t cur[kGroup], nxt[kGroup];
+  load_group(0, cur);
+  for (int j0 = 0; j0 < steps; j0 += kGroup) {
+    load_group(j0 + kGroup, nxt);
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q)
+      if (tid + (j0 + q) * kLsmThreads >= nvec) cur[q] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float gm = cur[0][0];
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gm = fmaxf(gm, cur[q][e]);
+    const float m = fmaxf(acc.m, gm);
+    // ms keeps exp finite while every value so far is -inf (padding).
+    const float ms = m == -INFINITY ? 0.0f : m;
+    float s = acc.m == -INFINITY ? 0.0f : acc.s * exp2_hw((acc.m - ms) * kLog2e);
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = s + exp2_hw((cur[q][e] - ms) * kLog2e);
+    acc = MaxSum{m, s};
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) cur[q] = nxt[q];
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -63,6 +87,7 @@ __global__ __launch_bounds__(kLsmThreads) void log_softmax_kernel(const float* z
   const float lse = tot.m + log2_hw(tot.s) * kLn2;
 
   f32x4_t* orow = reinterpret_cast<f32x4_t*>(out + row * ld_out);
+#pragma unroll 4
   for (int i = tid; i < nvec; i += kLsmThreads) {
     const f32x4_t v = zr[i];
     orow[i] = f32x4_t{v[0] - lse, v[1] - lse, v[2] - lse, v[3] - lse};
