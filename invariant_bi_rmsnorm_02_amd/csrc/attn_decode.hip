@@ -120,14 +120,32 @@ struct GlobalChunk {
   }
 };
 
-template <int D>
+// kFold == false: each chunk's partial goes to its workspace record and the
+// merge kernel folds them.  kFold == true (the wavefront owns every chunk of
+// its sequence): the wavefront folds each chunk's partial into a running state
+// right after computing it - per element the same merge step, in the same
+// ascending order, as the merge kernel - and writes out / lse itself.
+template <int D, bool kFold>
 __global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table,
     int max_pages, const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq, int Hkv, int log2_ps,
-    float scale_log2, float* __restrict__ ws, int max_chunks, int chunks_per_wave) {
+    float scale_log2, float* __restrict__ ws, int max_chunks, int chunks_per_wave, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
   const int c_first = blockIdx.x * chunks_per_wave, h = blockIdx.y, b = blockIdx.z;
   const int L = min(seq_lens[b], max_seq_len);
+  if constexpr (kFold) {
+    if (L <= 0) {   // the merge kernel's result for an empty sequence
+      const int lane = threadIdx.x, n = lane & 15, g = lane >> 4, G = Hq / Hkv;
+      if (n < G) {
+        uint16_t* op = out + ((int64_t)b * Hq + h * G + n) * D + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<u32x2_t*>(op + 16 * dt) = u32x2_t{0u, 0u};
+        if (lse != nullptr && g == 0) lse[(int64_t)b * Hq + h * G + n] = -INFINITY;
+      }
+      return;
+    }
+  }
   if (c_first * kChunk >= L) return;
   const int c_end = min((L + kChunk - 1) / kChunk, c_first + chunks_per_wave);
   const int G = Hq / Hkv;
@@ -165,6 +183,15 @@ __global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(
   typename Src::Frags fa, fb;
   SubProbs<1> sp;
   ChunkAcc<D, 1> acc;
+  // Fold state (kFold): m and l in registers, the running o in LDS (the
+  // wavefront is its own workgroup; lane l owns o_run[.][l]), which keeps it
+  // out of the registers the load pipeline needs.
+  float m_run = -INFINITY, l_run = 0.0f;
+  __shared__ f32x4_t o_run[kFold ? D / 16 : 1][64];
+  if constexpr (kFold) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o_run[dt][lane] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   src.fetch(0, fa, true);
   for (int c = c_first; c < c_end; ++c) {
     int ln = threadIdx.x & 63;
@@ -201,15 +228,41 @@ __global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(
       chunk_values<D, 1>(acc, fb.v, sp);
       if (s + 2 >= n_sub) break;
     }
-    if (row_ok) {
+    if constexpr (kFold) {
+      const MergeCoef k = merge_coef(m_run, acc.m[0]);
+      l_run = merge_val(l_run, acc.l[0], k);
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = acc.o[0][dt];
-      if (g == 0) {
-        rec[D] = acc.m[0];
-        rec[D + 1] = acc.l[0];
+      for (int dt = 0; dt < D / 16; ++dt) {
+        f32x4_t r = o_run[dt][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = merge_val(r[i], acc.o[0][dt][i], k);
+        o_run[dt][lane] = r;
       }
+      m_run = k.m;
+    } else {
+      if (row_ok) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = acc.o[0][dt];
+        if (g == 0) {
+          rec[D] = acc.m[0];
+          rec[D + 1] = acc.l[0];
+        }
+      }
+      rec += D + 4;
     }
-    rec += D + 4;
+  }
+  if constexpr (kFold) {
+    if (row_ok) {
+      uint16_t* op = out + ((int64_t)b * Hq + h * G + n) * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const f32x4_t a = o_run[dt][lane];
+        *reinterpret_cast<u32x2_t*>(op + 16 * dt) =
+            u32x2_t{pack_bf16x2(finalize_val(a[0], l_run), finalize_val(a[1], l_run)),
+                    pack_bf16x2(finalize_val(a[2], l_run), finalize_val(a[3], l_run))};
+      }
+      if (lse != nullptr && g == 0) lse[(int64_t)b * Hq + h * G + n] = finalize_lse(m_run, l_run);
+    }
   }
 }
 
@@ -263,16 +316,25 @@ hipError_t launch(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t*
   const int max_chunks = (max_seq_len + kChunk - 1) / kChunk;
   float* ws = static_cast<float*>(workspace);
   const int cpw = decode_chunks_per_wave(num_seqs, g.num_kv_heads, max_chunks);
-  hipLaunchKernelGGL(attn_decode_partial_kernel<D>, dim3((max_chunks + cpw - 1) / cpw, g.num_kv_heads, num_seqs),
-                     dim3(64), 0,
-                     stream, static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(g.k_cache),
-                     static_cast<const uint16_t*>(g.v_cache), g.num_pages, g.block_table, g.max_pages_per_seq,
+  const auto* qs = static_cast<const uint16_t*>(q);
+  const auto* kcs = static_cast<const uint16_t*>(g.k_cache);
+  const auto* vcs = static_cast<const uint16_t*>(g.v_cache);
+  auto* os = static_cast<uint16_t*>(out);
+  if (cpw == max_chunks) {
+    // Every wavefront owns a whole sequence: it folds the chunks itself.
+    hipLaunchKernelGGL((attn_decode_partial_kernel<D, true>), dim3(1, g.num_kv_heads, num_seqs), dim3(64), 0, stream,
+                       qs, ld_q, kcs, vcs, g.num_pages, g.block_table, g.max_pages_per_seq, seq_lens, max_seq_len,
+                       g.num_q_heads, g.num_kv_heads, g.log2_page, g.scale_log2, ws, max_chunks, cpw, os, lse);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((attn_decode_partial_kernel<D, false>), dim3((max_chunks + cpw - 1) / cpw, g.num_kv_heads, num_seqs),
+                     dim3(64), 0, stream, qs, ld_q, kcs, vcs, g.num_pages, g.block_table, g.max_pages_per_seq,
                      seq_lens, max_seq_len, g.num_q_heads, g.num_kv_heads, g.log2_page, g.scale_log2, ws,
-                     max_chunks, cpw);
+                     max_chunks, cpw, os, lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(64), 0, stream, ws,
-                     seq_lens, max_seq_len, g.num_q_heads, max_chunks, static_cast<uint16_t*>(out), lse);
+                     seq_lens, max_seq_len, g.num_q_heads, max_chunks, os, lse);
   return hipGetLastError();
 }
 
