@@ -75,7 +75,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void splitk_partial_kernel(
   }
   f32x4_t acc[Cfg::NB][Cfg::MB];
   gemm_zero<Cfg>(acc);
-  gemm_mainloop<Cfg>(op, klen, gemm_live_blocks<Cfg>(rows_a), sW, sA, acc);
+  gemm_mainloop<Cfg>(op, klen, rows_a, sW, sA, acc);
   float* part = ws + (int64_t)split * M * N;
   gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) {
     gemm_store4_f32(part + (int64_t)(m0 + m) * N + n, v, cnt, (N & 3) == 0);

@@ -109,16 +109,41 @@ __device__ __forceinline__ int gemm_slot_row(int i) {
   return (threadIdx.x + i * Cfg::kThreads) / Cfg::kChunks;
 }
 
-// Accumulates the workgroup's tile over the whole of K into acc (which the
-// caller zeroes): for every output element one fp32 chain of MFMA steps over
-// k = 0, 32, 64, ... in ascending order.  live_mb = 16-row blocks of this
-// wave's m-range that hold at least one real row (their MFMAs are the only
-// ones issued; the others would only compute padding).
+template <int V>
+struct GemmInt {
+  static constexpr int value = V;
+};
+
+// Calls f(GemmInt<live>{}) for 1 <= live <= L; nothing for live <= 0.
+template <int L, class F>
+__device__ __forceinline__ void gemm_dispatch_live(int live, F&& f) {
+  if constexpr (L >= 1) {
+    if (live >= L)
+      f(GemmInt<L>{});
+    else
+      gemm_dispatch_live<L - 1>(live, f);
+  }
+}
+
+// 16-row blocks of this wave's m-range (tile rows wm*WTM ..) that hold at least
+// one of the tile's `rows` real rows.
 template <class Cfg>
-__device__ __forceinline__ void gemm_mainloop(const GemmOperands<Cfg>& op, int K, int live_mb,
-                                              uint16_t (*sW)[Cfg::TN * Cfg::BK],
-                                              uint16_t (*sA)[Cfg::TM * Cfg::BK],
-                                              f32x4_t (&acc)[Cfg::NB][Cfg::MB]) {
+__device__ __forceinline__ int gemm_live_blocks(int rows) {
+  const int wm = (threadIdx.x >> 6) / Cfg::WGN;
+  return min(Cfg::MB, max(0, (rows - wm * Cfg::WTM + 15) >> 4));
+}
+
+// The main loop for a tile whose first LAL A load slots hold real rows (slot i
+// of every thread covers tile rows i * R .. i * R + R - 1, R = threads / chunks
+// per row).  The other A slots are neither loaded nor copied: their rows are
+// past M, so the MFMA blocks that would read them are skipped, and their loads
+// would only occupy the texture units.  Which slots are live is uniform over
+// the workgroup and fixed for the whole loop, so the loop stays branch-free.
+template <class Cfg, int LAL>
+__device__ __forceinline__ void gemm_mainloop_live(const GemmOperands<Cfg>& op, int K, int live_mb,
+                                                   uint16_t (*sW)[Cfg::TN * Cfg::BK],
+                                                   uint16_t (*sA)[Cfg::TM * Cfg::BK],
+                                                   f32x4_t (&acc)[Cfg::NB][Cfg::MB]) {
   constexpr int BK = Cfg::BK, NT = Cfg::kThreads;
   constexpr int NB = Cfg::NB, MB = Cfg::MB, LW = Cfg::LW, LA = Cfg::LA, PW = Cfg::PW, PA = Cfg::PA;
   constexpr int KC = Cfg::kChunks, U = Cfg::U;
@@ -138,7 +163,7 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands<Cfg>& op, int K
   };
   auto load_a = [&](int kt, u32x4_t (&dst)[LA]) {
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
+    for (int i = 0; i < LAL; ++i) {
       const bool ok = op.aofs[i] != kBufOOB && kt * BK + ((tid + i * NT) % KC) * 8 < K;
       dst[i] = gemm_buf_load(op.rsa, ok ? op.aofs[i] + (uint32_t)(kt * BK * 2) : kBufOOB);
     }
@@ -150,32 +175,36 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands<Cfg>& op, int K
       *reinterpret_cast<u32x4_t*>(&sW[buf][gemm_lds_off<KC>(id / KC, id % KC)]) = w[i];
     }
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
+    for (int i = 0; i < LAL; ++i) {
       const int id = tid + i * NT;
       *reinterpret_cast<u32x4_t*>(&sA[buf][gemm_lds_off<KC>(id / KC, id % KC)]) = a[i];
     }
   };
-  auto compute = [&](int buf) {
-    if (live_mb <= 0) return;
+  // One stage of MFMAs on LDS buffer buf for the first L m-blocks (L known at
+  // compile time, so the stage has no branch: every fragment read is issued
+  // before the MFMAs that use it and the LDS latency overlaps the MFMAs).
+  // Each accumulator still takes its MFMA steps in ascending k.
+  auto compute_live = [&](int buf, auto live_c) {
+    constexpr int L = decltype(live_c)::value;
+    u32x4_t af[BK / 32][NB], bf[BK / 32][L];
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       const int c = ks * 4 + g;
-      u32x4_t af[NB], bf[MB];
 #pragma unroll
       for (int i = 0; i < NB; ++i)
-        af[i] = *reinterpret_cast<const u32x4_t*>(&sW[buf][gemm_lds_off<KC>(wn * Cfg::WTN + i * 16 + l16, c)]);
+        af[ks][i] = *reinterpret_cast<const u32x4_t*>(&sW[buf][gemm_lds_off<KC>(wn * Cfg::WTN + i * 16 + l16, c)]);
 #pragma unroll
-      for (int j = 0; j < MB; ++j)
-        bf[j] = *reinterpret_cast<const u32x4_t*>(&sA[buf][gemm_lds_off<KC>(wm * Cfg::WTM + j * 16 + l16, c)]);
-#pragma unroll
-      for (int j = 0; j < MB; ++j) {
-        if (j < live_mb) {
-#pragma unroll
-          for (int i = 0; i < NB; ++i) acc[i][j] = mfma_16x16x32(af[i], bf[j], acc[i][j]);
-        }
-      }
+      for (int j = 0; j < L; ++j)
+        bf[ks][j] = *reinterpret_cast<const u32x4_t*>(&sA[buf][gemm_lds_off<KC>(wm * Cfg::WTM + j * 16 + l16, c)]);
     }
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks)
+#pragma unroll
+      for (int j = 0; j < L; ++j)
+#pragma unroll
+        for (int i = 0; i < NB; ++i) acc[i][j] = mfma_16x16x32(af[ks][i], bf[ks][j], acc[i][j]);
   };
+  auto compute = [&](int buf) { gemm_dispatch_live<MB>(live_mb, [&](auto live_c) { compute_live(buf, live_c); }); };
 
   // Prologue: stages 0 .. PW-1 (W) and 0 .. PA-1 (A) in flight, stage 0 in LDS.
   // Stages past the end of K load zeros and cost no memory traffic.
@@ -205,12 +234,23 @@ __device__ __forceinline__ void gemm_mainloop(const GemmOperands<Cfg>& op, int K
   }
 }
 
-// 16-row blocks of this wave's m-range (tile rows wm*WTM ..) that hold at least
-// one of the tile's `rows` real rows.
+// Accumulates the workgroup's tile over the whole of K into acc (which the
+// caller zeroes): for every output element one fp32 chain of MFMA steps over
+// k = 0, 32, 64, ... in ascending order.  rows_a = real A rows of the tile;
+// only the MFMA blocks and A load slots that hold one of them are issued (the
+// others would only compute or load padding), which changes no real output.
 template <class Cfg>
-__device__ __forceinline__ int gemm_live_blocks(int rows) {
-  const int wm = (threadIdx.x >> 6) / Cfg::WGN;
-  return min(Cfg::MB, max(0, (rows - wm * Cfg::WTM + 15) >> 4));
+__device__ __forceinline__ void gemm_mainloop(const GemmOperands<Cfg>& op, int K, int rows_a,
+                                              uint16_t (*sW)[Cfg::TN * Cfg::BK],
+                                              uint16_t (*sA)[Cfg::TM * Cfg::BK],
+                                              f32x4_t (&acc)[Cfg::NB][Cfg::MB]) {
+  constexpr int R = Cfg::kThreads / Cfg::kChunks;   // tile rows per load slot
+  static_assert(Cfg::kThreads % Cfg::kChunks == 0, "slot rows");
+  const int live_mb = gemm_live_blocks<Cfg>(rows_a);
+  const int la_live = min(Cfg::LA, (rows_a + R - 1) / R);
+  gemm_dispatch_live<Cfg::LA>(la_live, [&](auto lal) {
+    gemm_mainloop_live<Cfg, decltype(lal)::value>(op, K, live_mb, sW, sA, acc);
+  });
 }
 
 // Hands every finished output group to st(m, n, v, cnt): tile-local row m
@@ -287,7 +327,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void gemm_kernel(
 
   f32x4_t acc[Cfg::NB][Cfg::MB];
   gemm_zero<Cfg>(acc);
-  gemm_mainloop<Cfg>(op, K, gemm_live_blocks<Cfg>(rows_a), sW, sA, acc);
+  gemm_mainloop<Cfg>(op, K, rows_a, sW, sA, acc);
 
   // Epilogue: lane holds C[m][n .. n+3].
   gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) {

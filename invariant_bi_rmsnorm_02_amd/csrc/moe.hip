@@ -192,7 +192,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void moe_gemm_kernel(
 
   f32x4_t acc[Cfg::NB][Cfg::MB];
   gemm_zero<Cfg>(acc);
-  gemm_mainloop<Cfg>(op, K, gemm_live_blocks<Cfg>(rows_a), sW, sA, acc);
+  gemm_mainloop<Cfg>(op, K, rows_a, sW, sA, acc);
 
   gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) {
     if constexpr (kUp) {
