@@ -31,9 +31,13 @@ SOURCES = ["api.cpp", "rmsnorm.hip", "gemm.hip", "kv_append.hip", "attn_decode.h
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in VGPRs rather than AGPRs, so the
+# VALU can rescale them in place (the attention accumulators are rescaled on
+# every 32-key step; in AGPRs each rescale costs two moves per element).  It
+# selects register classes only, never instructions or their order.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
          "-fno-fast-math", "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-I", INCLUDE, "-I", CSRC]
+         "-mllvm", "-amdgpu-mfma-vgpr-form", "-I", INCLUDE, "-I", CSRC]
 
 
 def _compile(src: str) -> str:

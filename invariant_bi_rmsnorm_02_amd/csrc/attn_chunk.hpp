@@ -104,17 +104,17 @@ __device__ __forceinline__ void chunk_scores(ChunkAcc<D, NB>& a, const u32x4_t (
           mx = fmaxf(mx, t[4 * b + i]);
         }
     } else {
+      // Key 32 s + 8 g + j of the lane is visible iff j < r.
+      const int r = n_valid[nb] - kSub * s - 8 * g;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = kSub * s + 8 * g + 4 * b + i;
-          t[4 * b + i] = key < n_valid[nb] ? S[b][i] * scale_log2 : -INFINITY;
+          t[4 * b + i] = 4 * b + i < r ? S[b][i] * scale_log2 : -INFINITY;
           mx = fmaxf(mx, t[4 * b + i]);
         }
     }
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float mn = fmaxf(a.m[nb], mx);
     const float ms = (mn == -INFINITY) ? 0.0f : mn;
     const float alpha = exp2_hw(a.m[nb] - ms);
@@ -125,8 +125,7 @@ __device__ __forceinline__ void chunk_scores(ChunkAcc<D, NB>& a, const u32x4_t (
       p[j] = exp2_hw(t[j] - ms);
       ls = ls + p[j];
     }
-    ls = ls + shfl_xor(ls, 16);
-    ls = ls + shfl_xor(ls, 32);
+    ls = add_xor32(add_xor16(ls));
     a.l[nb] = a.l[nb] * alpha + ls;
     a.m[nb] = mn;
     sp.alpha[nb] = alpha;

@@ -8,13 +8,21 @@
 // (token, q head) rows of one sequence and one kv head - four wavefronts of two
 // 16-row column blocks.  The chunk's own keys/values are already in the paged
 // cache, so cached and new tokens are read through one path.  The workgroup
-// walks the 256-key chunks in ascending order, 32 keys at a time: each K/V
-// sub-block is fetched from HBM four sub-blocks ahead into a register ring,
-// staged once into LDS (double-buffered) and every wavefront runs the same
-// chunk step as decode on it (causal mask: a query at position p sees keys
-// 0..p).  Block-table entries are read one chunk ahead.
-// After a chunk each column folds it with the same merge step as decode, so row
-// p is bitwise what decode returns at seq_len p + 1.
+// walks the 256-key chunks in ascending order, 32 keys at a time, and every
+// wavefront runs the same chunk step as decode on each 32-key sub-block (causal
+// mask: a query at position p sees keys 0..p).  After a chunk each column folds
+// it with the same merge step as decode, so row p is bitwise what decode
+// returns at seq_len p + 1.
+//
+// K/V sub-blocks travel from HBM straight into a four-stage LDS ring (buffer
+// loads that write LDS, no register staging), three sub-blocks ahead of the
+// one being computed.  Each 1 KB load lies inside one 16-token tile, so one
+// scalar buffer resource per load covers it; a tile whose page is missing,
+// past the block table or wholly past the last visible key gets an empty
+// resource and lands as zeros.  Keys of a valid page past the last visible key
+// are masked where they are used (scores of such keys are never visible; their
+// V entries are zeroed on the one sub-block that straddles the limit).  Block-
+// table entries are read one chunk ahead.
 #include "attn_chunk.hpp"
 #include "kv_layout.hpp"
 #include "launch.hpp"
@@ -27,11 +35,32 @@ constexpr int kNB = 2;                              // 16-row column blocks per 
 constexpr int kRowsPerWave = 16 * kNB;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 constexpr int kThreads = kWaves * 64;
+constexpr int kStages = 4;                          // LDS ring depth (sub-blocks); divides the 8 of a chunk
 
-// LDS holds one staged 32-key sub-block as its two 16-token tiles, in the same
-// tiled order as the cache (kv_layout.hpp), so staging is a straight copy of
-// contiguous 16-byte pieces and every fragment read is a run of contiguous
-// 16-byte LDS words (128 bytes per 8 lanes for K, 256 bytes per 16 lanes for V).
+template <int V>
+struct StageIdx {
+  static constexpr int value = V;
+};
+
+// One 16-byte-per-lane load of [base, base + bytes) at byte offset voff into LDS
+// at lds + 16 * lane (lds is the same for the whole wavefront).  Offsets at or
+// past `bytes` (all of them when bytes = 0) write zeros and read nothing.
+__device__ __forceinline__ void lds_dma16(const uint16_t* base, uint32_t bytes, uint32_t voff, uint16_t* lds) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Waits until at most N of this wavefront's vector-memory operations are
+// outstanding, then joins the workgroup barrier.  Written out because the
+// barrier of __syncthreads also waits for every LDS-writing load in flight,
+// which would drain the ring.  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vmem_then_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
@@ -39,14 +68,28 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
     const int32_t* __restrict__ ctx_lens, int max_q_len, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table, int max_pages,
     int Hq, int Hkv, int log2_ps, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int TE = kTile * D;                 // elements per tile
-  constexpr int NP = 2 * TE / 8 / kThreads;     // 16-byte pieces per thread per sub-block (K and V each)
-  static_assert(NP >= 1 && (2 * TE / 8) % kThreads == 0, "staging split");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][2 * TE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][2 * TE];
+  constexpr int TE = kTile * D;                          // elements per tile
+  constexpr int kPieces = 2 * TE * 2 / 1024;             // 1 KB loads per sub-block (K or V: two tiles)
+  constexpr int IPW = kPieces / kWaves;                  // ... per wavefront
+  static_assert(IPW >= 1 && kPieces % kWaves == 0, "staging split");
+  // One array per stage (K at 0, V at 2 TE), so the compiler can tell the
+  // stages' loads apart and wait only for the stage an LDS read needs.
+  __shared__ __attribute__((aligned(16))) uint16_t st0[4 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t st1[4 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[4 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t st3[4 * TE];
+  static_assert(kStages == 4, "one array per stage below");
+  auto stage = [&](auto idx) -> uint16_t* {
+    constexpr int i = decltype(idx)::value;
+    if constexpr (i == 0) return st0;
+    else if constexpr (i == 1) return st1;
+    else if constexpr (i == 2) return st2;
+    else return st3;
+  };
 
   const int tile = blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = Hq / Hkv;
   const int qs = q_start[sq];
   const int nq = min(q_start[sq + 1] - qs, max_q_len);
@@ -84,75 +127,56 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
   // so loading the next chunk's entries early never waits.
   auto raw_pages = [&](int c) { return bt[min(c * ppc + (lane % ppc), max_pages - 1)]; };
 
-  // Global -> register staging of sub-block u (chunk u / 8, sub-block u % 8),
-  // P sub-blocks ahead of the LDS copy: piece pc covers elements 8 pc .. 8 pc
-  // + 7 of the sub-block's two tiles.  `pages` holds the raw entries of the
-  // sub-block's chunk.  Loads are unconditional (a page that may not be read
-  // points at the pool start); the masks are applied when the ring slot is
-  // copied into LDS.
-  constexpr int P = 4;                 // divides the 8 sub-blocks of a chunk: ring slot of u is u % P
-  struct Stage {
-    u32x4_t k[NP], v[NP];
-    int ok;                            // bit i: piece i's page may be read
-  };
-  Stage ring[P];
-  auto piece_t0 = [&](int u, int i) {  // position of piece i's tile token 0 in sub-block u
-    return (u >> 3) * kChunk + (u & 7) * kSub + kTile * (((tid + i * kThreads) * 8) / TE);
-  };
-  auto load_sub = [&](int u, int pages, Stage& st) {
-    st.ok = 0;
+  // Loads of sub-block u (keys 32 u .. 32 u + 31) into a stage: this
+  // wavefront's IPW 1 KB pieces of the K tiles and of the V tiles.  `pages`
+  // holds the raw entries of the sub-block's chunk.  Issued for every u, also
+  // past the end (as zeros), so every wavefront always has the same number of
+  // loads in flight.
+  auto issue = [&](int u, int pages, uint16_t* dst) {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int w = ((tid + i * kThreads) * 8) % TE;
-      const int t0 = piece_t0(u, i);
+    for (int j = 0; j < IPW; ++j) {
+      const int pc = wave * IPW + j;                     // piece of the sub-block
+      const int tt = pc * 1024 / (TE * 2);               // its tile (0 or 1)
+      const int inb = pc * 1024 - tt * (TE * 2);         // byte offset inside the tile
+      const int t0 = u * kSub + kTile * tt;              // the tile's first key
       const int lp = t0 >> log2_ps;
-      const int raw = __shfl(pages, (t0 & (kChunk - 1)) >> log2_ps, kWave);
+      const int raw = __builtin_amdgcn_readlane(pages, (t0 & (kChunk - 1)) >> log2_ps);
       const bool ok = t0 < lim && lp < max_pages && raw >= 0 && raw < num_pages;
-      const int64_t tb = ok ? raw * page_elems + head_off + (int64_t)((t0 & (ps - 1)) >> 4) * TE + w : 0;
-      st.k[i] = *reinterpret_cast<const u32x4_t*>(kc + tb);
-      st.v[i] = *reinterpret_cast<const u32x4_t*>(vc + tb);
-      st.ok |= ok ? (1 << i) : 0;
+      const int64_t tb = ok ? raw * page_elems + head_off + (int64_t)((t0 & (ps - 1)) >> 4) * TE : 0;
+      const uint32_t bytes = ok ? TE * 2 : 0;
+      lds_dma16(kc + tb, bytes, inb + lane * 16, dst + pc * 512);
+      lds_dma16(vc + tb, bytes, inb + lane * 16, dst + 2 * TE + pc * 512);
     }
   };
-  auto store_sub = [&](int buf, int u, const Stage& st) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int pc = tid + i * kThreads;
-      const bool ok = (st.ok >> i) & 1;
-      // K rows past lim are masked in the scores; only a missing page is zeroed.
-      *reinterpret_cast<u32x4_t*>(&sK[buf][pc * 8]) = ok ? st.k[i] : zero4();
-      // V piece: one dim of 8 tokens (half (w / 128) % 2 of the tile); tokens
-      // past lim are zeroed.
-      const int vt0 = piece_t0(u, i) + 8 * (((pc * 8) % TE >> 7) & 1);
-      *reinterpret_cast<u32x4_t*>(&sV[buf][pc * 8]) = ok ? keep_first(st.v[i], lim - vt0) : zero4();
-    }
-  };
+  // Loads issued after sub-block u's when the wavefront waits for u.
+  constexpr int kAfter = (kStages - 2) * 2 * IPW;
 
-  // Running state of the fold over chunks (per column block).
+  // Running state of the fold over chunks (per column block).  The
+  // accumulators are touched once per chunk, so they wait in LDS (each lane
+  // owns its slots; no other lane reads them) and leave the registers to the
+  // chunk step.
+  __shared__ __attribute__((aligned(16))) f32x4_t s_orun[kWaves][kNB][D / 16][64];
   float m_run[kNB], l_run[kNB];
-  f32x4_t o_run[kNB][D / 16];
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     m_run[nb] = -INFINITY;
     l_run[nb] = 0.0f;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o_run[nb][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < D / 16; ++dt) s_orun[wave][nb][dt][lane] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   const int nch = (lim + kChunk - 1) / kChunk;
   const int last_subs = (lim - (nch - 1) * kChunk + kSub - 1) / kSub;
-  const int U = (nch - 1) * kSubs + last_subs;
 
   ChunkAcc<D, kNB> ca;
   int nvalid[kNB];
   int cur_pages = raw_pages(0), next_pages = raw_pages(1);
-#pragma unroll
-  for (int p = 0; p < P; ++p) load_sub(p, cur_pages, ring[p]);
-  store_sub(0, 0, ring[0]);
-  __syncthreads();
-  // Outer loop over chunks, the 8 sub-blocks of a chunk unrolled so that ring
-  // slots and LDS buffers are static: sub-block u = 8 c + s sits in ring slot
-  // s % P and LDS buffer s & 1.
+  static_assert(kStages - 1 <= kSubs, "prologue stays in chunk 0");
+  issue(0, cur_pages, stage(StageIdx<0>{}));
+  issue(1, cur_pages, stage(StageIdx<1>{}));
+  issue(2, cur_pages, stage(StageIdx<2>{}));
+  // Outer loop over chunks, the 8 sub-blocks of a chunk written out so that
+  // stages are static: sub-block u = 8 c + s sits in stage s % 4.
   for (int c = 0; c < nch; ++c) {
     const int after_pages = raw_pages(c + 2);
     chunk_init(ca);
@@ -160,15 +184,17 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
     for (int nb = 0; nb < kNB; ++nb)
       nvalid[nb] = row_ok[nb] ? max(0, min(kChunk, pos[nb] + 1 - c * kChunk)) : 0;
     const int subs = c == nch - 1 ? last_subs : kSubs;
-    // One 32-key sub-block: refill its ring slot with sub-block u + P (chunk c
-    // or c + 1; the slot was copied into LDS at the end of step u - 1), run the
-    // chunk step on LDS buffer s & 1, copy sub-block u + 1 from its slot into
-    // the other buffer.  Ring slots are named statically: slot of u is s % P.
-    auto step = [&](int s, Stage& refill, const Stage& next) {
+    // One 32-key sub-block: wait for its stage, refill the stage that the
+    // previous step read with sub-block u + 3, run the chunk step.
+    auto step = [&](auto sidx, auto cur_stage, auto refill_stage) {
+      constexpr int s = decltype(sidx)::value;
       const int u = c * kSubs + s;
-      load_sub(u + P, s + P < kSubs ? cur_pages : next_pages, refill);
-      if (c * kChunk + s * kSub < wave_lim) {   // some column of this wave sees a key here
-        const int buf = s & 1;
+      wait_vmem_then_barrier<kAfter>();
+      issue(u + kStages - 1, s + kStages - 1 < kSubs ? cur_pages : next_pages, stage(refill_stage));
+      const int sub0 = u * kSub;
+      if (sub0 < wave_lim) {   // some column of this wave sees a key here
+        const uint16_t* sK = stage(cur_stage);
+        const uint16_t* sV = sK + 2 * TE;
         const int l16 = n;
         u32x4_t kf[2][D / 32], vf[D / 16];
         // Same operand addressing as decode, inside the LDS copy of the two tiles.
@@ -177,40 +203,53 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int ks = 0; ks < D / 32; ++ks)
-            kf[b][ks] = *reinterpret_cast<const u32x4_t*>(&sK[buf][kofs + 4 * ks * 128 + 8 * b * 8]);
-        const int vofs = (g >> 1) * TE + (g & 1) * 128 + l16 * 8;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-          vf[dt] = *reinterpret_cast<const u32x4_t*>(&sV[buf][vofs + dt * 256]);
+            kf[b][ks] = *reinterpret_cast<const u32x4_t*>(&sK[kofs + 4 * ks * 128 + 8 * b * 8]);
         SubProbs<kNB> sp;
         chunk_scores<D, kNB>(ca, kf, qf, nvalid, s, scale_log2, sp);
+        // V is read once the K fragments are dead, which keeps the two apart
+        // in the register file.
+        const int vofs = (g >> 1) * TE + (g & 1) * 128 + l16 * 8;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *reinterpret_cast<const u32x4_t*>(&sV[vofs + dt * 256]);
+        // The sub-block holding the limit: V of keys >= lim may be stale.
+        if (sub0 + kSub > lim) {
+          const KeepMask km = keep_mask(lim - (sub0 + 8 * g));
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) vf[dt] = apply_keep(vf[dt], km);
+        }
         chunk_values<D, kNB>(ca, vf, sp);
       }
-      if (u + 1 < U) store_sub((s + 1) & 1, u + 1, next);
-      __syncthreads();
     };
-    static_assert(P == 4 && kSubs == 8, "ring slots below are written out for P = 4");
-    for (int s4 = 0; s4 < kSubs; s4 += 4) {
-      if (s4 + 0 < subs) step(s4 + 0, ring[0], ring[1]);
-      if (s4 + 1 < subs) step(s4 + 1, ring[1], ring[2]);
-      if (s4 + 2 < subs) step(s4 + 2, ring[2], ring[3]);
-      if (s4 + 3 < subs) step(s4 + 3, ring[3], ring[0]);
-    }
+    static_assert(kStages == 4 && kSubs == 8, "stage indices below are written out for 4 stages");
+    if (0 < subs) step(StageIdx<0>{}, StageIdx<0>{}, StageIdx<3>{});
+    if (1 < subs) step(StageIdx<1>{}, StageIdx<1>{}, StageIdx<0>{});
+    if (2 < subs) step(StageIdx<2>{}, StageIdx<2>{}, StageIdx<1>{});
+    if (3 < subs) step(StageIdx<3>{}, StageIdx<3>{}, StageIdx<2>{});
+    if (4 < subs) step(StageIdx<4>{}, StageIdx<0>{}, StageIdx<3>{});
+    if (5 < subs) step(StageIdx<5>{}, StageIdx<1>{}, StageIdx<0>{});
+    if (6 < subs) step(StageIdx<6>{}, StageIdx<2>{}, StageIdx<1>{});
+    if (7 < subs) step(StageIdx<7>{}, StageIdx<3>{}, StageIdx<2>{});
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       if (nvalid[nb] > 0) {
         const MergeCoef k = merge_coef(m_run[nb], ca.m[nb]);
         l_run[nb] = merge_val(l_run[nb], ca.l[nb], k);
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
+        for (int dt = 0; dt < D / 16; ++dt) {
+          f32x4_t o = s_orun[wave][nb][dt][lane];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o_run[nb][dt][i] = merge_val(o_run[nb][dt][i], ca.o[nb][dt][i], k);
+          for (int i = 0; i < 4; ++i) o[i] = merge_val(o[i], ca.o[nb][dt][i], k);
+          s_orun[wave][nb][dt][lane] = o;
+        }
         m_run[nb] = k.m;
       }
     }
     cur_pages = next_pages;
     next_pages = after_pages;
   }
+  // The ring's last loads (zeros past the end) must land before the
+  // workgroup's LDS is released.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
@@ -220,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
     uint16_t* op = out + ((int64_t)(qs + tok) * Hq + h * G + hh) * D + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const f32x4_t a = o_run[nb][dt];
+      const f32x4_t a = s_orun[wave][nb][dt][lane];
       *reinterpret_cast<u32x2_t*>(op + 16 * dt) =
           u32x2_t{pack_bf16x2(finalize_val(a[0], l_run[nb]), finalize_val(a[1], l_run[nb])),
                   pack_bf16x2(finalize_val(a[2], l_run[nb]), finalize_val(a[3], l_run[nb]))};

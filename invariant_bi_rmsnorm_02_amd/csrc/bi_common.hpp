@@ -62,6 +62,29 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Exchange across 16-lane rows (lanes l and l ^ 16) and across wavefront
+// halves (l and l ^ 32) with v_permlane16_swap / v_permlane32_swap: every lane
+// gets the pair {x[l], x[l ^ 16]} (resp. l ^ 32) in one VALU instruction
+// instead of a round trip through LDS.  The pair's order depends on the row,
+// which neither max nor + (commutative, bit for bit) can see, so these give
+// the same bits as v op shfl_xor(v, 16 or 32).
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, shfl_xor(v, o));

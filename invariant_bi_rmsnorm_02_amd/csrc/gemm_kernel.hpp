@@ -26,12 +26,13 @@
 
 namespace bi {
 
-template <int TN_, int TM_, int WGN_, int WGM_, int PW_, int PA_, int BK_ = 64>
+template <int TN_, int TM_, int WGN_, int WGM_, int PW_, int PA_, int BK_ = 64, int OCC_ = 2>
 struct GemmCfg {
   static constexpr int TN = TN_, TM = TM_;          // workgroup tile: W rows x A rows
   static constexpr int WGN = WGN_, WGM = WGM_;      // wavefront grid
   static constexpr int PW = PW_, PA = PA_;          // register prefetch depth (stages) of W and A
   static constexpr int BK = BK_;                    // K per stage (64 or 128)
+  static constexpr int OCC = OCC_;                  // workgroups per CU the register budget aims at
   static constexpr int kThreads = 64 * WGN * WGM;
   static constexpr int WTN = TN / WGN, WTM = TM / WGM;
   static constexpr int NB = WTN / 16, MB = WTM / 16;
@@ -299,7 +300,7 @@ __device__ __forceinline__ void gemm_store4_f32(float* cp, f32x4_t v, int cnt, b
 }
 
 template <class Cfg, bool kF32Out>
-__global__ __launch_bounds__(Cfg::kThreads, 2) void gemm_kernel(
+__global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
   __shared__ __attribute__((aligned(16))) uint16_t sW[2][Cfg::TN * Cfg::BK];
