@@ -65,7 +65,7 @@ __device__ __forceinline__ void wait_vmem_then_barrier() {
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const int32_t* __restrict__ q_start,
-    const int32_t* __restrict__ ctx_lens, int max_q_len, const uint16_t* __restrict__ kc,
+    const int32_t* __restrict__ ctx_lens, int num_seqs, int tiles, int max_q_len, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table, int max_pages,
     int Hq, int Hkv, int log2_ps, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int TE = kTile * D;                          // elements per tile
@@ -87,8 +87,31 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
     else return st3;
   };
 
-  const int tile = blockIdx.x, h = blockIdx.y, sq = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  // Work placement (arithmetic does not depend on it).  Workgroups start in
+  // index order, so the longest ones go first: sequences by descending last
+  // key (ties by index), then a sequence's tiles from the last, whose rows see
+  // the most keys.  The kv head is the fastest index: workgroups go to the 8
+  // XCDs round-robin, so every workgroup of one kv head shares one L2.
+  const int per_seq = tiles * Hkv;
+  const int rank = blockIdx.x / per_seq, rem = blockIdx.x - rank * per_seq;
+  const int tile = tiles - 1 - rem / Hkv, h = rem % Hkv;
+  auto seq_key = [&](int j) { return ctx_lens[j] + min(q_start[j + 1] - q_start[j], max_q_len); };
+  int sq = 0;
+  for (int base = 0; base < num_seqs; base += kWave) {
+    const int i = base + lane;
+    const int ki = i < num_seqs ? seq_key(i) : 0;
+    int r = 0;   // sequences ordered before sequence i
+    for (int j = 0; j < num_seqs; ++j) {
+      const int kj = seq_key(j);
+      r += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
+    }
+    const uint64_t hit = __ballot(i < num_seqs && r == rank);
+    if (hit != 0) {
+      sq = base + (int)__builtin_ctzll(hit);
+      break;
+    }
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = Hq / Hkv;
   const int qs = q_start[sq];
@@ -273,8 +296,10 @@ hipError_t launch(const void* q, int64_t ld_q, const int32_t* q_start, const int
                   int max_q_len, const AttnGeom& g, void* out, float* lse, hipStream_t stream) {
   const int G = g.num_q_heads / g.num_kv_heads;
   const int tiles = (max_q_len * G + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(tiles, g.num_kv_heads, num_seqs), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(q), ld_q, q_start, ctx_lens, max_q_len,
+  const int64_t blocks = (int64_t)tiles * g.num_kv_heads * num_seqs;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), ld_q, q_start, ctx_lens, num_seqs, tiles, max_q_len,
                      static_cast<const uint16_t*>(g.k_cache), static_cast<const uint16_t*>(g.v_cache),
                      g.num_pages, g.block_table, g.max_pages_per_seq, g.num_q_heads, g.num_kv_heads,
                      g.log2_page, g.scale_log2, static_cast<uint16_t*>(out), lse);
