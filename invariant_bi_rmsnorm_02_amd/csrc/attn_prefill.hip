@@ -35,7 +35,6 @@ constexpr int kNB = 2;                              // 16-row column blocks per 
 constexpr int kRowsPerWave = 16 * kNB;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 constexpr int kThreads = kWaves * 64;
-constexpr int kStages = 4;                          // LDS ring depth (sub-blocks); divides the 8 of a chunk
 
 template <int V>
 struct StageIdx {
@@ -62,8 +61,12 @@ __device__ __forceinline__ void wait_vmem_then_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
+// D: head dim.  STAGES: LDS ring depth in sub-blocks (divides the 8 of a
+// chunk, so a sub-block's stage is static).  REGFOLD: column blocks whose fold
+// state stays in registers (the rest wait in LDS).  OCC: workgroups per CU the
+// register budget aims at.
+template <int D, int STAGES, int REGFOLD, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const int32_t* __restrict__ q_start,
     const int32_t* __restrict__ ctx_lens, int num_seqs, int tiles, int max_q_len, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table, int max_pages,
@@ -78,7 +81,8 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t st1[4 * TE];
   __shared__ __attribute__((aligned(16))) uint16_t st2[4 * TE];
   __shared__ __attribute__((aligned(16))) uint16_t st3[4 * TE];
-  static_assert(kStages == 4, "one array per stage below");
+  static_assert(STAGES == 2 || STAGES == 4, "one array per stage above");
+  static_assert(REGFOLD >= 0 && REGFOLD <= kNB, "fold split");
   auto stage = [&](auto idx) -> uint16_t* {
     constexpr int i = decltype(idx)::value;
     if constexpr (i == 0) return st0;
@@ -172,20 +176,31 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
     }
   };
   // Loads issued after sub-block u's when the wavefront waits for u.
-  constexpr int kAfter = (kStages - 2) * 2 * IPW;
+  constexpr int kAfter = (STAGES - 2) * 2 * IPW;
 
   // Running state of the fold over chunks (per column block).  The
-  // accumulators are touched once per chunk, so they wait in LDS (each lane
-  // owns its slots; no other lane reads them) and leave the registers to the
-  // chunk step.
-  __shared__ __attribute__((aligned(16))) f32x4_t s_orun[kWaves][kNB][D / 16][64];
+  // accumulators are touched once per chunk; those of column blocks >= REGFOLD
+  // wait in LDS (each lane owns its slots; no other lane reads them) and leave
+  // the registers to the chunk step.
+  constexpr int kLdsFold = kNB - REGFOLD;
+  __shared__ __attribute__((aligned(16))) f32x4_t s_orun[kWaves][kLdsFold > 0 ? kLdsFold : 1][D / 16][64];
+  f32x4_t o_reg[REGFOLD > 0 ? REGFOLD : 1][D / 16];
+  auto fold_get = [&](int nb, int dt) -> f32x4_t {
+    return nb < REGFOLD ? o_reg[nb < REGFOLD ? nb : 0][dt] : s_orun[wave][nb >= REGFOLD ? nb - REGFOLD : 0][dt][lane];
+  };
+  auto fold_put = [&](int nb, int dt, f32x4_t v) {
+    if (nb < REGFOLD)
+      o_reg[nb < REGFOLD ? nb : 0][dt] = v;
+    else
+      s_orun[wave][nb >= REGFOLD ? nb - REGFOLD : 0][dt][lane] = v;
+  };
   float m_run[kNB], l_run[kNB];
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     m_run[nb] = -INFINITY;
     l_run[nb] = 0.0f;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) s_orun[wave][nb][dt][lane] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < D / 16; ++dt) fold_put(nb, dt, f32x4_t{0.f, 0.f, 0.f, 0.f});
   }
 
   const int nch = (lim + kChunk - 1) / kChunk;
@@ -194,10 +209,12 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
   ChunkAcc<D, kNB> ca;
   int nvalid[kNB];
   int cur_pages = raw_pages(0), next_pages = raw_pages(1);
-  static_assert(kStages - 1 <= kSubs, "prologue stays in chunk 0");
+  static_assert(STAGES - 1 <= kSubs, "prologue stays in chunk 0");
   issue(0, cur_pages, stage(StageIdx<0>{}));
-  issue(1, cur_pages, stage(StageIdx<1>{}));
-  issue(2, cur_pages, stage(StageIdx<2>{}));
+  if constexpr (STAGES == 4) {
+    issue(1, cur_pages, stage(StageIdx<1>{}));
+    issue(2, cur_pages, stage(StageIdx<2>{}));
+  }
   // Outer loop over chunks, the 8 sub-blocks of a chunk written out so that
   // stages are static: sub-block u = 8 c + s sits in stage s % 4.
   for (int c = 0; c < nch; ++c) {
@@ -213,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
       constexpr int s = decltype(sidx)::value;
       const int u = c * kSubs + s;
       wait_vmem_then_barrier<kAfter>();
-      issue(u + kStages - 1, s + kStages - 1 < kSubs ? cur_pages : next_pages, stage(refill_stage));
+      issue(u + STAGES - 1, s + STAGES - 1 < kSubs ? cur_pages : next_pages, stage(refill_stage));
       const int sub0 = u * kSub;
       if (sub0 < wave_lim) {   // some column of this wave sees a key here
         const uint16_t* sK = stage(cur_stage);
@@ -243,15 +260,20 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
         chunk_values<D, kNB>(ca, vf, sp);
       }
     };
-    static_assert(kStages == 4 && kSubs == 8, "stage indices below are written out for 4 stages");
-    if (0 < subs) step(StageIdx<0>{}, StageIdx<0>{}, StageIdx<3>{});
-    if (1 < subs) step(StageIdx<1>{}, StageIdx<1>{}, StageIdx<0>{});
-    if (2 < subs) step(StageIdx<2>{}, StageIdx<2>{}, StageIdx<1>{});
-    if (3 < subs) step(StageIdx<3>{}, StageIdx<3>{}, StageIdx<2>{});
-    if (4 < subs) step(StageIdx<4>{}, StageIdx<0>{}, StageIdx<3>{});
-    if (5 < subs) step(StageIdx<5>{}, StageIdx<1>{}, StageIdx<0>{});
-    if (6 < subs) step(StageIdx<6>{}, StageIdx<2>{}, StageIdx<1>{});
-    if (7 < subs) step(StageIdx<7>{}, StageIdx<3>{}, StageIdx<2>{});
+    // Sub-block s reads stage s % STAGES and refills the stage read by s - 1.
+    auto run = [&](auto sidx) {
+      constexpr int s = decltype(sidx)::value;
+      if (s < subs) step(sidx, StageIdx<s % STAGES>{}, StageIdx<(s + STAGES - 1) % STAGES>{});
+    };
+    static_assert(kSubs == 8, "sub-blocks below are written out");
+    run(StageIdx<0>{});
+    run(StageIdx<1>{});
+    run(StageIdx<2>{});
+    run(StageIdx<3>{});
+    run(StageIdx<4>{});
+    run(StageIdx<5>{});
+    run(StageIdx<6>{});
+    run(StageIdx<7>{});
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       if (nvalid[nb] > 0) {
@@ -259,10 +281,10 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
         l_run[nb] = merge_val(l_run[nb], ca.l[nb], k);
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-          f32x4_t o = s_orun[wave][nb][dt][lane];
+          f32x4_t o = fold_get(nb, dt);
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[i] = merge_val(o[i], ca.o[nb][dt][i], k);
-          s_orun[wave][nb][dt][lane] = o;
+          fold_put(nb, dt, o);
         }
         m_run[nb] = k.m;
       }
@@ -282,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
     uint16_t* op = out + ((int64_t)(qs + tok) * Hq + h * G + hh) * D + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const f32x4_t a = s_orun[wave][nb][dt][lane];
+      const f32x4_t a = fold_get(nb, dt);
       *reinterpret_cast<u32x2_t*>(op + 16 * dt) =
           u32x2_t{pack_bf16x2(finalize_val(a[0], l_run[nb]), finalize_val(a[1], l_run[nb])),
                   pack_bf16x2(finalize_val(a[2], l_run[nb]), finalize_val(a[3], l_run[nb]))};
@@ -291,6 +313,11 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_kernel(
   }
 }
 
+// The library's configuration: two workgroups per CU (registers <= 256 and
+// LDS <= 80 KB each), a two-stage ring and column block 0's fold state in
+// registers.
+constexpr int kLibStages = 2, kLibRegFold = 1, kLibOcc = 2;
+
 template <int D>
 hipError_t launch(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens, int num_seqs,
                   int max_q_len, const AttnGeom& g, void* out, float* lse, hipStream_t stream) {
@@ -298,7 +325,7 @@ hipError_t launch(const void* q, int64_t ld_q, const int32_t* q_start, const int
   const int tiles = (max_q_len * G + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t blocks = (int64_t)tiles * g.num_kv_heads * num_seqs;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_prefill_kernel<D, kLibStages, kLibRegFold, kLibOcc>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), ld_q, q_start, ctx_lens, num_seqs, tiles, max_q_len,
                      static_cast<const uint16_t*>(g.k_cache), static_cast<const uint16_t*>(g.v_cache),
                      g.num_pages, g.block_table, g.max_pages_per_seq, g.num_q_heads, g.num_kv_heads,
