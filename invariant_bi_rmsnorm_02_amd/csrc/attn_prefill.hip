@@ -92,14 +92,18 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
   };
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  // Work placement (arithmetic does not depend on it).  Workgroups start in
-  // index order, so the longest ones go first: sequences by descending last
-  // key (ties by index), then a sequence's tiles from the last, whose rows see
-  // the most keys.  The kv head is the fastest index: workgroups go to the 8
-  // XCDs round-robin, so every workgroup of one kv head shares one L2.
-  const int per_seq = tiles * Hkv;
-  const int rank = blockIdx.x / per_seq, rem = blockIdx.x - rank * per_seq;
-  const int tile = tiles - 1 - rem / Hkv, h = rem % Hkv;
+  // Work placement (arithmetic does not depend on it).  Items (sequence,
+  // tile) are ranked longest first: sequences by descending last key (ties by
+  // index), then a sequence's tiles from the last, whose rows see the most
+  // keys.  The first half of the workgroups takes the items in that order and
+  // the second half in reverse, so the two workgroups that share a CU tend to
+  // pair a long item with a short one (measured on MI355X: 3-7% faster than
+  // longest-first throughout).  The kv head is the fastest index: workgroups go
+  // to the 8 XCDs round-robin, so every workgroup of one kv head shares one L2.
+  const int items = tiles * num_seqs, half = (items + 1) / 2;
+  const int qi = blockIdx.x / Hkv, h = blockIdx.x % Hkv;
+  const int item = qi < half ? qi : items - 1 - (qi - half);
+  const int rank = item / tiles, tile = tiles - 1 - item % tiles;
   auto seq_key = [&](int j) { return ctx_lens[j] + min(q_start[j + 1] - q_start[j], max_q_len); };
   int sq = 0;
   for (int base = 0; base < num_seqs; base += kWave) {
