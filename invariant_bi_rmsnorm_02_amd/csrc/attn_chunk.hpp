@@ -92,39 +92,32 @@ __device__ __forceinline__ void chunk_scores(ChunkAcc<D, NB>& a, const u32x4_t (
       for (int ks = 0; ks < D / 32; ++ks) S[b] = mfma_16x16x32(kf[b][ks], qf[nb][ks], S[b]);
     }
     float t[8];
-    float mx = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[4 * b + i] = S[b][i] * scale_log2;
     // When every column of the wavefront sees the whole sub-block the mask
-    // selects nothing; skipping it leaves every value as it is.
-    if (__all(kSub * (s + 1) <= n_valid[nb])) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          t[4 * b + i] = S[b][i] * scale_log2;
-          mx = fmaxf(mx, t[4 * b + i]);
-        }
-    } else {
-      // Key 32 s + 8 g + j of the lane is visible iff j < r.
+    // selects nothing; skipping it leaves every value as it is.  Otherwise key
+    // 32 s + 8 g + j of the lane is visible iff j < r.
+    if (!__all(kSub * (s + 1) <= n_valid[nb])) {
       const int r = n_valid[nb] - kSub * s - 8 * g;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          t[4 * b + i] = 4 * b + i < r ? S[b][i] * scale_log2 : -INFINITY;
-          mx = fmaxf(mx, t[4 * b + i]);
-        }
+      for (int j = 0; j < 8; ++j) t[j] = j < r ? t[j] : -INFINITY;
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, t[j]);
     mx = max_xor32(max_xor16(mx));
     const float mn = fmaxf(a.m[nb], mx);
     const float ms = (mn == -INFINITY) ? 0.0f : mn;
     const float alpha = exp2_hw(a.m[nb] - ms);
     float p[8];
-    float ls = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = exp2_hw(t[j] - ms);
-      ls = ls + p[j];
-    }
+    for (int j = 0; j < 8; ++j) p[j] = exp2_hw(t[j] - ms);
+    // Key order.  p >= 0 is never -0, so starting from p[0] is 0 + p[0] to the bit.
+    float ls = p[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) ls = ls + p[j];
     ls = add_xor32(add_xor16(ls));
     a.l[nb] = a.l[nb] * alpha + ls;
     a.m[nb] = mn;
