@@ -12,12 +12,13 @@ resident in HBM before timing starts.
 
 Printed: one JSON line.  `value` = algorithmic bytes moved by the step /
 step time (GB/s; every kernel of the step is HBM-bound at B <= 256).
-`roofline` is for the dominant kernel (decode attention: chunk kernel plus
-merge kernel, timed together with HIP events on the launch stream).
+`roofline` is for the dominant kernel (decode attention, timed with HIP
+events on the launch stream; at B=256 it is a single kernel, below the
+1024 (sequence, kv head) threshold a chunk kernel plus a merge kernel).
 `kernels` holds per-kernel times at every workload shape (B = 1..256,
 the M ~ 2300 GEMMs and chunked prefill of the mixed batch, the 235B-shaped
-lm_head + log_softmax and decode attention) as GB/s or TFLOP/s and fraction
-of roofline.  `cpu_baseline` times the fp64 oracle on the host on a sample of
+lm_head + log_softmax (two calls and fused) and decode attention) as GB/s or
+TFLOP/s and fraction of roofline.  `cpu_baseline` times the fp64 oracle on the host on a sample of
 the same step.
 """
 from __future__ import annotations
@@ -329,7 +330,8 @@ def kernel_table(torch, bi, W, step, reps, everything):
                      flops_prefill(prefixes, chunks, 32, 128), extra={"prefixes": prefixes}))
     del kc, vc, qp, op
     torch.cuda.empty_cache()
-    # Qwen3-235B-shaped: lm_head 4096->151936 (fp32 logits) + log_softmax; decode attention 64/4.
+    # Qwen3-235B-shaped: lm_head 4096->151936 (fp32 logits) + log_softmax, separately and fused;
+    # decode attention 64/4.
     V = 151936
     wl = W.randn_bf16((V, 4096), W.SEED_MOE, "w", W.WEIGHTS, std=0.02, device=dev)
     for T in (1, 64, 512, 2048):
@@ -341,7 +343,13 @@ def kernel_table(torch, bi, W, step, reps, everything):
         lp = torch.empty_like(z)
         us = time_fn(torch, lambda i=0: bi.bi_log_softmax(z, out=lp), max(5, reps // 4))
         out.append(entry("log_softmax [T,151936] fp32", us, 8 * T * V, extra={"T": T}))
-        del ht, z, lp
+        # The same two steps fused (bi_lm_head_logprobs): algorithmic work is the
+        # GEMM's with the logprobs as its fp32 output.
+        lws = torch.empty((bi.lm_head_logprobs_workspace_bytes(T, V),), dtype=torch.uint8, device=dev)
+        us = time_fn(torch, lambda i=0: bi.bi_lm_head_logprobs(ht, wl, out=lp, workspace=lws), max(5, reps // 4))
+        out.append(entry("lm_head+log_softmax fused 4096->151936 fp32", us, bytes_gemm(T, V, 4096, 4),
+                         flops_gemm(T, V, 4096), extra={"T": T}))
+        del ht, z, lp, lws
     del wl
     torch.cuda.empty_cache()
     # Routed experts: 128 experts, top-8, 4096->1536->4096.  Each timed launch

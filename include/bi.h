@@ -234,6 +234,33 @@ bi_status bi_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids, cons
 bi_status bi_log_softmax(const float* logits, int64_t ld_in, float* out, int64_t ld_out,
                          int64_t rows, int64_t vocab, bi_stream_t stream);
 
+/*
+ * lm_head followed by log_softmax, the reduction fused into the GEMM's
+ * epilogue ([BINR] answer on sampler/trainer logprob agreement; the product is
+ * bi_gemm's, [TML] section "2. Batch-Invariant Matrix Multiplication").
+ *   z[i, j]   = sum_k a[i, k] w[j, k]        (bi_gemm's tile and fp32 K chain)
+ *   out[i, j] = z[i, j] - lse[i],  lse[i] = log sum_j exp(z[i, j])
+ * lse is reduced in one fixed tree that depends on n only: (max, sum of exp)
+ * pairs over 64-column tiles, folded in ascending tile order.  It is not
+ * bi_log_softmax's tree, so the two agree to rounding, not bit for bit; each
+ * is batch-invariant on its own.
+ * a: [m, k] bf16, row stride lda; w: [n, k] bf16, row stride ldw (k % 32 == 0,
+ *   strides multiples of 8, both 16-byte aligned);
+ * out: [m, n] fp32 logprobs, row stride ldo >= n, ldo % 4 == 0, 16-byte
+ *   aligned; n % 4 == 0; z is staged in out, so out must not overlap a or w;
+ * lse: [m] fp32 or NULL;
+ * workspace: device memory of at least
+ *   bi_lm_head_logprobs_workspace_bytes(m, n) bytes (the tile pairs), 256-byte
+ *   aligned, owned by the caller; its contents on entry do not matter.
+ * Errors: BI_ERR_INVALID_ARG (sizes, strides, alignment), BI_ERR_UNSUPPORTED
+ * (k % 32, n % 4, sizes beyond the GEMM's offset limits), BI_ERR_WORKSPACE
+ * (missing, misaligned or short workspace).  Nothing is written on error.
+ */
+size_t bi_lm_head_logprobs_workspace_bytes(int64_t m, int64_t n);
+bi_status bi_lm_head_logprobs(const void* a, int64_t lda, const void* w, int64_t ldw, float* out, int64_t ldo,
+                              float* lse, int64_t m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
+                              bi_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

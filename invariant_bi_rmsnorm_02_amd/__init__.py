@@ -40,6 +40,9 @@ _SIGNATURES = {
     "bi_moe_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "bi_moe_ffn": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_i32,
                             _c_p, _c_i64, _c_p, _c_size, _c_p]),
+    "bi_lm_head_logprobs_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
+    "bi_lm_head_logprobs": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64,
+                                     _c_p, _c_size, _c_p]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -319,4 +322,38 @@ def bi_moe_ffn(x: torch.Tensor, expert_ids: torch.Tensor, expert_weights: torch.
                                           expert_weights.data_ptr(), T, k, E, w_up.data_ptr(), w_down.data_ptr(),
                                           H, F, out.data_ptr(), _rows(out, "out"), workspace.data_ptr(),
                                           workspace.numel(), _stream(stream)))
+    return out
+
+
+def lm_head_logprobs_workspace_bytes(m: int, n: int) -> int:
+    return int(lib().bi_lm_head_logprobs_workspace_bytes(m, n))
+
+
+def bi_lm_head_logprobs(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """out[m, n] = log_softmax_n(sum_k a[m, k] * w[n, k]) in fp32 (GEMM and reduction fused)."""
+    _dev(a, "a", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    m, k = a.shape
+    n, k2 = w.shape
+    if k != k2:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=a.device)
+    _dev(out, "out", torch.float32)
+    if out.shape != (m, n):
+        raise ValueError("out shape")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if lse.shape != (m,) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous [m] tensor")
+    need = lm_head_logprobs_workspace_bytes(m, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=a.device)
+    _dev(workspace, "workspace", torch.uint8)
+    _check("bi_lm_head_logprobs", lib().bi_lm_head_logprobs(
+        a.data_ptr(), _rows(a, "a"), w.data_ptr(), _rows(w, "w"), out.data_ptr(), _rows(out, "out"),
+        lse.data_ptr() if lse is not None else None, m, n, k, workspace.data_ptr(), workspace.numel(),
+        _stream(stream)))
     return out

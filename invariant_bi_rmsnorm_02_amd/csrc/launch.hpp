@@ -50,6 +50,13 @@ hipError_t launch_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids,
                           int T, int top_k, int E, const void* w_up, const void* w_down, int H, int F, void* y,
                           int64_t ldy, void* workspace, hipStream_t stream);
 
+// lm_head + log_softmax fused into the GEMM epilogue (lm_head.hip).
+size_t lm_head_workspace_bytes(int64_t m, int64_t n);
+bool lm_head_supported(int64_t lda, int64_t ldw, int64_t k);
+hipError_t launch_lm_head_logprobs(const void* a, int64_t lda, const void* w, int64_t ldw, float* out, int64_t ldo,
+                                   float* lse, int64_t m, int64_t n, int64_t k, void* workspace,
+                                   hipStream_t stream);
+
 hipError_t launch_log_softmax(const float* logits, int64_t ld_in, float* out, int64_t ld_out,
                               int64_t rows, int64_t vocab, hipStream_t stream);
 

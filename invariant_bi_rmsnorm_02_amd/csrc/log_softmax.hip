@@ -11,26 +11,13 @@
 // The next group's loads are issued before the current group is reduced, so
 // eight 16-byte loads per thread are in flight; there are no data-dependent
 // branches.
-#include "bi_common.hpp"
 #include "launch.hpp"
+#include "lse.hpp"
 
 namespace bi {
 namespace {
 
 constexpr int kLsmThreads = 1024;
-
-struct MaxSum {
-  float m, s;
-};
-
-// Combine two (max, sum-of-exp) pairs.  Commutative bit for bit: both orders
-// compute the same two products and add them.
-__device__ __forceinline__ MaxSum combine(MaxSum a, MaxSum b) {
-  const float m = fmaxf(a.m, b.m);
-  const float ta = a.m == -INFINITY ? 0.0f : a.s * exp2_hw((a.m - m) * kLog2e);
-  const float tb = b.m == -INFINITY ? 0.0f : b.s * exp2_hw((b.m - m) * kLog2e);
-  return MaxSum{m, ta + tb};
-}
 
 __global__ __launch_bounds__(kLsmThreads) void log_softmax_kernel(const float* z, int64_t ld_in,
                                                                   float* out, int64_t ld_out, int vocab) {
@@ -84,7 +71,7 @@ __global__ __launch_bounds__(kLsmThreads) void log_softmax_kernel(const float* z
   MaxSum tot = part[0];
 #pragma unroll
   for (int w = 1; w < kLsmThreads / kWave; ++w) tot = combine(tot, part[w]);
-  const float lse = tot.m + log2_hw(tot.s) * kLn2;
+  const float lse = lse_of(tot);
 
   f32x4_t* orow = reinterpret_cast<f32x4_t*>(out + row * ld_out);
 #pragma unroll 4

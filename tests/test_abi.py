@@ -66,6 +66,16 @@ def test_host_validation_without_gpu(lib):
     assert dec(b=0) == bi.BI_OK
     assert dec(ldq=4000) == bi.BI_ERR_INVALID_ARG
     assert lib.bi_log_softmax(P, 6, P, 8, 2, 6, None) == bi.BI_ERR_UNSUPPORTED
+    # fused lm_head + log_softmax: n % 4, k % 32, short or missing or misaligned workspace, ldo, empty batch
+    W256 = ctypes.c_void_p(256)
+    lmh = lambda m, n, k, ldo, ws, nbytes: lib.bi_lm_head_logprobs(P, k, P, k, P, ldo, None, m, n, k, ws, nbytes, None)
+    assert lmh(2, 1026, 64, 1028, W256, 1 << 30) == bi.BI_ERR_UNSUPPORTED
+    assert lmh(2, 1024, 48, 1024, W256, 1 << 30) == bi.BI_ERR_UNSUPPORTED
+    assert lmh(2, 1024, 64, 1024, None, 1 << 30) == bi.BI_ERR_WORKSPACE
+    assert lmh(2, 1024, 64, 1024, ctypes.c_void_p(272), 1 << 30) == bi.BI_ERR_WORKSPACE
+    assert lmh(2, 1024, 64, 1024, W256, 16) == bi.BI_ERR_WORKSPACE
+    assert lmh(2, 1024, 64, 1022, W256, 1 << 30) == bi.BI_ERR_INVALID_ARG
+    assert lmh(0, 1024, 64, 1024, None, 0) == bi.BI_OK
     assert lib.bi_kv_append(P, P, 640, P, 3, P, P, 4, 8, 80, 16, None) == bi.BI_ERR_UNSUPPORTED
     assert lib.bi_kv_append(P, P, 1000, P, 3, P, P, 4, 8, 128, 16, None) == bi.BI_ERR_INVALID_ARG
 
@@ -76,6 +86,9 @@ def test_workspace_size_formula(lib):
     raw = 3 * 32 * 4 * (128 + 4) * 4
     assert n == (raw + 255) // 256 * 256
     assert bi.bi_attn_decode_workspace_bytes(1, 1, 64, 256) == 256 * ((68 * 4 + 255) // 256)
+    # one (max, sum) pair of fp32 per (row, 64-column tile), rounded to 256 bytes
+    assert bi.lm_head_logprobs_workspace_bytes(2048, 151936) == 2048 * 2374 * 8
+    assert bi.lm_head_logprobs_workspace_bytes(3, 100) == 256
 
 
 def test_adaptive_library_exports_its_header():

@@ -1,0 +1,114 @@
+"""bi_lm_head_logprobs on the GPU (lm_head GEMM with log_softmax fused into its
+epilogue): parity with the oracle's log_softmax of the oracle's GEMM (fp32
+max abs err <= 1e-3), closed forms, a token's logprobs bitwise across batch
+compositions, and agreement with the two-call path to rounding."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from _helpers import O, assert_bitwise, assert_f32_close, bi, ensure_lib, f64, log_case
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+V = 151936
+K = 4096
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+
+
+def _weights(n, k=K):
+    return W.randn_bf16((n, k), W.SEED_MOE, "w", W.WEIGHTS, std=0.02, device=DEV)
+
+
+def _ref(a, w):
+    """Oracle logprobs and lse (= z - logprob, read off column 0)."""
+    z = O.gemm(f64(a), f64(w))
+    lp = O.log_softmax(z)
+    return lp, z[:, 0] - lp[:, 0]
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1024, 256), (3, 2052, 256), (70, 2052, 512), (5, V // 8, K)])
+def test_lm_head_logprobs_parity(m, n, k):
+    log_case(f"lm_head logprobs parity m={m} n={n} k={k}")
+    a = W.rows_for_requests(range(m), k, W.SEED_MOE, device=DEV)
+    w = _weights(n, k)
+    lse = torch.empty(m, dtype=torch.float32, device=DEV)
+    lp = bi.bi_lm_head_logprobs(a, w, lse=lse)
+    ref_lp, ref_lse = _ref(a, w)
+    assert_f32_close(lp, ref_lp, f"logprobs {m}x{n}x{k}")
+    assert_f32_close(lse, ref_lse, f"lse {m}x{n}x{k}")
+
+
+def test_lm_head_logprobs_full_vocab():
+    log_case("lm_head logprobs full vocab T=1")
+    a = W.rows_for_requests([0], K, W.SEED_MOE, device=DEV)
+    w = _weights(V)
+    lp = bi.bi_lm_head_logprobs(a, w)
+    assert_f32_close(lp, _ref(a, w)[0], "logprobs 1x151936x4096")
+    # probabilities sum to one
+    assert abs(float(torch.exp(lp.double()).sum()) - 1.0) < 1e-4
+
+
+def test_lm_head_logprobs_closed_forms():
+    a = W.rows_for_requests(range(2), 256, W.SEED_MOE, device=DEV)
+    w = torch.zeros((4096, 256), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(2, dtype=torch.float32, device=DEV)
+    lp = bi.bi_lm_head_logprobs(a, w, lse=lse)
+    assert_f32_close(lp, np.full((2, 4096), -math.log(4096)), "zero weights: uniform")
+    assert_f32_close(lse, np.full(2, math.log(4096)), "zero weights: lse = log n")
+    # one-hot rows of A select one column of W: z = w[:, j]
+    a1 = torch.zeros((1, 256), dtype=torch.bfloat16, device=DEV)
+    a1[0, 7] = 1.0
+    w1 = _weights(1024, 256)
+    z = f64(w1)[:, 7][None, :]
+    assert_f32_close(bi.bi_lm_head_logprobs(a1, w1), O.log_softmax(z), "one-hot row")
+
+
+def test_lm_head_logprobs_batch_invariance():
+    n = V // 8
+    w = _weights(n)
+    ref = None
+    ws = None
+    for T in (1, 64, 512):
+        for pos in sorted({0, T // 3, T - 1}):
+            ids = list(range(1, T))
+            ids.insert(pos, 0)
+            a = W.rows_for_requests(ids, K, W.SEED_MOE, device=DEV)
+            need = bi.lm_head_logprobs_workspace_bytes(T, n)
+            if ws is None or ws.numel() < need:
+                ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+            row = bi.bi_lm_head_logprobs(a, w, workspace=ws)[pos].clone()
+            if ref is None:
+                ref = row
+            assert_bitwise(row, ref, f"token 0 logprobs at T={T} slot={pos}")
+
+
+def test_lm_head_logprobs_matches_two_calls():
+    """Same mathematics as bi_gemm (fp32) + bi_log_softmax; a different fixed
+    reduction tree for lse, so equal to rounding, not to the bit."""
+    a = W.rows_for_requests(range(6), K, W.SEED_MOE, device=DEV)
+    w = _weights(V // 8)
+    fused = bi.bi_lm_head_logprobs(a, w)
+    two = bi.bi_log_softmax(bi.bi_gemm(a, w, out_dtype=torch.float32))
+    assert float((fused - two).abs().max()) < 1e-4
+
+
+def test_lm_head_logprobs_workspace_reuse_and_errors():
+    w = _weights(2052, 256)
+    a_big = W.rows_for_requests(range(33), 256, W.SEED_MOE, device=DEV)
+    a_small = W.rows_for_requests(range(5), 256, W.SEED_MOE, device=DEV)
+    ws = torch.full((bi.lm_head_logprobs_workspace_bytes(33, 2052),), 0x7f, dtype=torch.uint8, device=DEV)
+    bi.bi_lm_head_logprobs(a_big, w, workspace=ws)
+    small = bi.bi_lm_head_logprobs(a_small, w, workspace=ws)   # stale pairs of the bigger call in the workspace
+    assert_bitwise(small, bi.bi_lm_head_logprobs(a_small, w), "workspace contents on entry do not matter")
+    out = torch.full((5, 2052), 7.0, device=DEV)
+    with pytest.raises(bi.BiError) as e:
+        bi.bi_lm_head_logprobs(a_small, w, out=out, workspace=ws[:64])
+    assert e.value.status == bi.BI_ERR_WORKSPACE
+    assert bool((out == 7.0).all()), "nothing written on error"
