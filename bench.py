@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes 20 times (counter calibration) and exit")
+    ap.add_argument("--only", choices=sorted(ONLY), default=None,
+                    help="only run one workload --reps times (for rocprofv3 counter runs) and exit")
     return ap.parse_args()
 
 
@@ -532,14 +534,67 @@ def cpu_baseline(torch, W, step, sample, min_seconds=10.0, max_reps=50):
                       f"fp64 numpy oracle, repeated {reps} times; rate = algorithmic bytes / oracle seconds"}
 
 
+# ---------------------------------------------------------------- single workloads for counter runs
+
+ONLY = {
+    "gemm-up-m2300": "up GEMM 4096->12288 at M=2300 (mixed batch), bf16 out",
+    "gemm-up-m256": "up GEMM 4096->12288 at M=256 (decode step), bf16 out",
+    "prefill-4x512": "chunked prefill, 4 x 512 tokens over the seeded prefixes, 32/8 heads, D=128",
+    "rmsnorm-2300": "RMSNorm [2300, 4096]",
+    "lm-head-t2048": "fused lm_head + log_softmax, T=2048, vocab 151936",
+}
+
+
+def run_only(torch, bi, W, what, reps):
+    """Build one workload of the per-kernel table and launch it `reps` times."""
+    dev = "cuda"
+    print(f"[bench] only {what}: {ONLY[what]}, {reps} launches", file=sys.stderr, flush=True)
+    if what.startswith("gemm-up"):
+        M = 2300 if what.endswith("m2300") else 256
+        w = W.randn_bf16((12288, 4096), W.SEED_DECODE, "w", W.WEIGHTS + 2, std=0.02, device=dev)
+        a = W.rows_for_requests(range(M), 4096, W.SEED_MIXED, device=dev)
+        c = torch.empty((M, 12288), dtype=torch.bfloat16, device=dev)
+        fn = lambda: bi.bi_gemm(a, w, out=c)
+    elif what == "prefill-4x512":
+        prefixes = [W.rand_int(0, 8192, W.SEED_MIXED, "len", 100 + s) for s in range(4)]
+        total = [p + 512 for p in prefixes]
+        pb = W.allocate_pages(total, W.SEED_MIXED)
+        kc, vc = bi.alloc_kv_cache(pb.num_pages, 8, 128, 16, dev, fill=0.0)
+        kv = [W.request_kv(s, L, 8, 128, W.SEED_MIXED, device=dev) for s, L in enumerate(total)]
+        bi.bi_kv_append(torch.cat([k for k, _ in kv]), torch.cat([v for _, v in kv]), pb.slot_mapping.to(dev),
+                        kc, vc)
+        qp = W.randn_bf16((2048, 32, 128), W.SEED_MIXED, "q", 0, device=dev)
+        op = torch.empty_like(qp)
+        qs = torch.tensor([0, 512, 1024, 1536, 2048], dtype=torch.int32, device=dev)
+        ctx = torch.tensor(prefixes, dtype=torch.int32, device=dev)
+        btp = pb.block_table.to(dev)
+        fn = lambda: bi.bi_attn_prefill(qp, qs, ctx, 512, kc, vc, btp, 1 / math.sqrt(128), out=op)
+    elif what == "rmsnorm-2300":
+        x = W.rows_for_requests(range(2300), 4096, W.SEED_MIXED, device=dev)
+        g = W.randn_bf16((4096,), W.SEED_MIXED, "gamma", W.WEIGHTS, std=0.1, mean=1.0, device=dev)
+        y = torch.empty_like(x)
+        fn = lambda: bi.bi_rmsnorm(x, g, EPS, out=y)
+    else:
+        V, T = 151936, 2048
+        wl = W.randn_bf16((V, 4096), W.SEED_MOE, "w", W.WEIGHTS, std=0.02, device=dev)
+        ht = W.rows_for_requests(range(T), 4096, W.SEED_MOE, device=dev)
+        lp = torch.empty((T, V), dtype=torch.float32, device=dev)
+        lws = torch.empty((bi.lm_head_logprobs_workspace_bytes(T, V),), dtype=torch.uint8, device=dev)
+        fn = lambda: bi.bi_lm_head_logprobs(ht, wl, out=lp, workspace=lws)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"only": what, "launches": reps}), flush=True)
+
+
 # ---------------------------------------------------------------- main
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
-              "requests and kv heads with no exchange, but no multi-GPU run is part of this build.",
-              file=sys.stderr)
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported (the path shards by "
+              "requests and kv heads with no exchange across GPUs).", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.copy_bytes:
@@ -557,6 +612,9 @@ def main():
         __graft_entry__.build()
     bi.lib()
     torch.cuda.set_device(0)
+    if args.only:
+        run_only(torch, bi, W, args.only, args.reps)
+        return
     print(f"[bench] building the decode-step workload B={args.batch}", file=sys.stderr, flush=True)
     step = DecodeStep(torch, bi, W, args.batch)
     torch.cuda.synchronize()
