@@ -75,12 +75,16 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
   constexpr int kPieces = 2 * TE * 2 / 1024;             // 1 KB loads per sub-block (K or V: two tiles)
   constexpr int IPW = kPieces / kWaves;                  // ... per wavefront
   static_assert(IPW >= 1 && kPieces % kWaves == 0, "staging split");
-  // One array per stage (K at 0, V at 2 TE), so the compiler can tell the
+  // Tiles sit TS elements apart in a stage: the 128-byte pad puts tile 1 on
+  // the other half of the LDS banks, so a K fragment read (lanes 0-7 in tile
+  // 0, lanes 8-15 in tile 1) is free of bank conflicts.
+  constexpr int TS = TE + 64;
+  // One array per stage (K tiles at 0 and TS, V tiles at 2 TS and 3 TS), so the compiler can tell the
   // stages' loads apart and wait only for the stage an LDS read needs.
-  __shared__ __attribute__((aligned(16))) uint16_t st0[4 * TE];
-  __shared__ __attribute__((aligned(16))) uint16_t st1[4 * TE];
-  __shared__ __attribute__((aligned(16))) uint16_t st2[4 * TE];
-  __shared__ __attribute__((aligned(16))) uint16_t st3[4 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t st0[4 * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t st1[4 * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[4 * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t st3[4 * TS];
   static_assert(STAGES == 2 || STAGES == 4, "one array per stage above");
   static_assert(REGFOLD >= 0 && REGFOLD <= kNB, "fold split");
   auto stage = [&](auto idx) -> uint16_t* {
@@ -175,8 +179,8 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
       const bool ok = t0 < lim && lp < max_pages && raw >= 0 && raw < num_pages;
       const int64_t tb = ok ? raw * page_elems + head_off + (int64_t)((t0 & (ps - 1)) >> 4) * TE : 0;
       const uint32_t bytes = ok ? TE * 2 : 0;
-      lds_dma16(kc + tb, bytes, inb + lane * 16, dst + pc * 512);
-      lds_dma16(vc + tb, bytes, inb + lane * 16, dst + 2 * TE + pc * 512);
+      lds_dma16(kc + tb, bytes, inb + lane * 16, dst + tt * TS + inb / 2);
+      lds_dma16(vc + tb, bytes, inb + lane * 16, dst + (2 + tt) * TS + inb / 2);
     }
   };
   // Loads issued after sub-block u's when the wavefront waits for u.
@@ -238,11 +242,11 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
       const int sub0 = u * kSub;
       if (sub0 < wave_lim) {   // some column of this wave sees a key here
         const uint16_t* sK = stage(cur_stage);
-        const uint16_t* sV = sK + 2 * TE;
+        const uint16_t* sV = sK + 2 * TS;
         const int l16 = n;
         u32x4_t kf[2][D / 32], vf[D / 16];
         // Same operand addressing as decode, inside the LDS copy of the two tiles.
-        const int kofs = (l16 >> 3) * TE + g * 128 + (l16 & 7) * 8;
+        const int kofs = (l16 >> 3) * TS + g * 128 + (l16 & 7) * 8;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
         chunk_scores<D, kNB>(ca, kf, qf, nvalid, s, scale_log2, sp);
         // V is read once the K fragments are dead, which keeps the two apart
         // in the register file.
-        const int vofs = (g >> 1) * TE + (g & 1) * 128 + l16 * 8;
+        const int vofs = (g >> 1) * TS + (g & 1) * 128 + l16 * 8;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *reinterpret_cast<const u32x4_t*>(&sV[vofs + dt * 256]);
         // The sub-block holding the limit: V of keys >= lim may be stale.
