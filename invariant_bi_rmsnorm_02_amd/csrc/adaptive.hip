@@ -51,8 +51,6 @@ SplitK choose_splitk(int64_t m, int64_t n, int64_t k) {
 __global__ __launch_bounds__(Cfg::kThreads, 2) void splitk_partial_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
     float* __restrict__ ws, int M, int N, int K, int kc, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][Cfg::TN * Cfg::BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][Cfg::TM * Cfg::BK];
   const int split = blockIdx.y;
   int tile_m, tile_n;
   gemm_map_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
@@ -75,7 +73,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void splitk_partial_kernel(
   }
   f32x4_t acc[Cfg::NB][Cfg::MB];
   gemm_zero<Cfg>(acc);
-  gemm_mainloop<Cfg>(op, klen, rows_a, sW, sA, acc);
+  gemm_mainloop<Cfg>(op, klen, rows_a, acc);
   float* part = ws + (int64_t)split * M * N;
   gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) {
     gemm_store4_f32(part + (int64_t)(m0 + m) * N + n, v, cnt, (N & 3) == 0);

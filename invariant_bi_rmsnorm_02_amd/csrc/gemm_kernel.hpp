@@ -10,40 +10,43 @@
 // M except which rows are loaded and which 16-row MFMA blocks are skipped
 // because all their rows are past M.
 //
-// Data movement.  K advances in BK-wide stages.  Every global read is a raw
-// buffer load whose resource covers only this workgroup's rows: a row past N
-// or M, or a k past K, gets an out-of-range offset and the hardware returns
-// zeros without touching memory.  So the load stream has no branches, and the
-// compiler can wait for exactly the stage it needs (vmcnt(n) rather than
-// vmcnt(0)) while later stages stay in flight.  W stages are fetched PW stages
-// ahead into a register ring and A stages PA ahead; each stage is then copied
-// into a double-buffered, XOR-swizzled LDS tile that the wavefronts read their
-// MFMA operands from.  The tile is computed as C^T = W A^T so each lane stores
-// 4 consecutive n.
+// Data movement.  K advances in BK-wide stages held in an S-stage LDS ring.
+// Stages travel from memory straight into LDS (buffer loads that write LDS,
+// 16 bytes per lane), S - 1 stages ahead of the one being multiplied; no
+// register holds them in flight and no instruction copies them.  Every load
+// is a raw buffer load whose resource covers only this workgroup's rows: a row
+// past N or M, or a k past K, gets an out-of-range offset and the hardware
+// writes zeros without touching memory.  Each wavefront's loads for a stage
+// fill 1 KB runs of the XOR-swizzled tile: lane l writes 16 bytes at l * 16 of
+// its run, so the lane fetches whichever 16-byte chunk of its row the swizzle
+// puts there.  The wavefronts read their MFMA operands from the tile.  The tile
+// is computed as C^T = W A^T so each lane stores 4 consecutive n.
 #pragma once
+
+#include <utility>
 
 #include "bi_common.hpp"
 
 namespace bi {
 
-template <int TN_, int TM_, int WGN_, int WGM_, int PW_, int PA_, int BK_ = 64, int OCC_ = 2>
+template <int TN_, int TM_, int WGN_, int WGM_, int S_, int BK_ = 64, int OCC_ = 2>
 struct GemmCfg {
   static constexpr int TN = TN_, TM = TM_;          // workgroup tile: W rows x A rows
   static constexpr int WGN = WGN_, WGM = WGM_;      // wavefront grid
-  static constexpr int PW = PW_, PA = PA_;          // register prefetch depth (stages) of W and A
+  static constexpr int S = S_;                      // LDS ring depth (stages)
   static constexpr int BK = BK_;                    // K per stage (64 or 128)
-  static constexpr int OCC = OCC_;                  // workgroups per CU the register budget aims at
+  static constexpr int OCC = OCC_;                  // workgroups per CU the registers and LDS aim at
   static constexpr int kThreads = 64 * WGN * WGM;
   static constexpr int WTN = TN / WGN, WTM = TM / WGM;
   static constexpr int NB = WTN / 16, MB = WTM / 16;
   static constexpr int kChunks = BK / 8;                    // 16-byte chunks per tile row
   static constexpr int LW = TN * kChunks / kThreads;        // W loads per thread per stage
   static constexpr int LA = TM * kChunks / kThreads;        // A loads per thread per stage
-  static constexpr int U = (PW > PA ? PW : PA) % 2 ? 2 * (PW > PA ? PW : PA) : (PW > PA ? PW : PA);
   static_assert(LW >= 1 && LA >= 1 && TN * kChunks % kThreads == 0 && TM * kChunks % kThreads == 0, "split");
   static_assert(NB >= 1 && MB >= 1, "wave tile");
-  static_assert(U % PW == 0 && U % PA == 0 && U % 2 == 0, "ring unroll");
-  static_assert(PW * LW + PA * LA <= 60, "outstanding loads per wave");
+  static_assert(S >= 2 && S <= 8, "ring depth");
+  static_assert((S - 2) * (LW + LA) < 64, "loads in flight per wave fit the wait counter");
+  static_assert(S * (TN + TM) * BK * 2 * OCC <= 160 * 1024, "LDS per CU");
   static_assert(BK == 64 || BK == 128, "stage depth");
 };
 
@@ -85,35 +88,45 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4_t gemm_buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 // The operands of one workgroup tile: a buffer resource over the W rows and
 // one over the A rows it reads, and for every load slot of this thread the
 // byte offset (within its resource) of the slot's 16-byte chunk in stage 0, or
-// kBufOOB when the slot's row does not exist.  Slot i of a thread covers tile
-// row (tid + i * threads) / chunks, chunk (tid + i * threads) % chunks.
+// kBufOOB when the slot's row does not exist (slots: gemm_slot_row and
+// gemm_slot_chunk).
 template <class Cfg>
 struct GemmOperands {
   __amdgpu_buffer_rsrc_t rsw, rsa;
   uint32_t wofs[Cfg::LW], aofs[Cfg::LA];
 };
 
-// Byte offset of load slot i's chunk in a row that starts at row_byte.
-template <class Cfg>
-__device__ __forceinline__ uint32_t gemm_slot_chunk_bytes(int i) {
-  return (uint32_t)(((threadIdx.x + i * Cfg::kThreads) % Cfg::kChunks) * 16);
-}
+// Load slot i of a thread writes tile row (tid + i * threads) / chunks at
+// swizzled position (tid + i * threads) % chunks; it fetches the row's chunk
+// that gemm_lds_off puts there.
 template <class Cfg>
 __device__ __forceinline__ int gemm_slot_row(int i) {
   return (threadIdx.x + i * Cfg::kThreads) / Cfg::kChunks;
+}
+template <class Cfg>
+__device__ __forceinline__ int gemm_slot_chunk(int i) {
+  constexpr int KC = Cfg::kChunks;
+  return ((threadIdx.x + i * Cfg::kThreads) % KC) ^ (gemm_slot_row<Cfg>(i) & (KC - 1));
+}
+// Byte offset of load slot i's chunk within its row.
+template <class Cfg>
+__device__ __forceinline__ uint32_t gemm_slot_chunk_bytes(int i) {
+  return (uint32_t)(gemm_slot_chunk<Cfg>(i) * 16);
 }
 
 template <int V>
 struct GemmInt {
   static constexpr int value = V;
 };
+
+// Calls f(GemmInt<I>{}) for each I of the sequence, in order.
+template <int... I, class F>
+__device__ __forceinline__ void gemm_for_each(std::integer_sequence<int, I...>, F&& f) {
+  (f(GemmInt<I>{}), ...);
+}
 
 // Calls f(GemmInt<live>{}) for 1 <= live <= L; nothing for live <= 0.
 template <int L, class F>
@@ -134,58 +147,86 @@ __device__ __forceinline__ int gemm_live_blocks(int rows) {
   return min(Cfg::MB, max(0, (rows - wm * Cfg::WTM + 15) >> 4));
 }
 
+// One 16-byte-per-lane load of the resource at byte offset voff into LDS at
+// lds + 16 * lane (lds is the same for the whole wavefront).
+__device__ __forceinline__ void gemm_lds_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint16_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Waits until at most N of this wavefront's vector-memory operations are
+// outstanding, then joins the workgroup barrier.  Written out because the
+// barrier of __syncthreads also waits for every LDS-writing load in flight,
+// which would drain the ring; the memory clobber keeps the compiler from
+// moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void gemm_wait_then_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// The ring: one W and one A array per stage, each its own __shared__ object,
+// so the compiler can tell the stages' loads apart and waits for exactly the
+// stage an LDS read needs.  Stages past S are one element (never used).
+template <class Cfg>
+struct GemmRing {
+  template <int I>
+  __device__ __forceinline__ static uint16_t* w() {
+    __shared__ __attribute__((aligned(16))) uint16_t buf[I < Cfg::S ? Cfg::TN * Cfg::BK : 8];
+    return buf;
+  }
+  template <int I>
+  __device__ __forceinline__ static uint16_t* a() {
+    __shared__ __attribute__((aligned(16))) uint16_t buf[I < Cfg::S ? Cfg::TM * Cfg::BK : 8];
+    return buf;
+  }
+};
+
 // The main loop for a tile whose first LAL A load slots hold real rows (slot i
 // of every thread covers tile rows i * R .. i * R + R - 1, R = threads / chunks
-// per row).  The other A slots are neither loaded nor copied: their rows are
-// past M, so the MFMA blocks that would read them are skipped, and their loads
-// would only occupy the texture units.  Which slots are live is uniform over
-// the workgroup and fixed for the whole loop, so the loop stays branch-free.
+// per row).  The other A slots are not loaded: their rows are past M, so the
+// MFMA blocks that would read them are skipped, and their loads would only
+// occupy the texture units.  Which slots are live is uniform over the
+// workgroup and fixed for the whole loop, so the loop stays branch-free.
+//
+// Stage kt is loaded into ring slot kt % S by the iteration kt - S + 1 (the
+// prologue for the first S - 1 stages).  Iteration kt waits for its own
+// loads of stage kt (the S - 2 later stages stay in flight), joins the
+// barrier, which also guarantees that every wavefront has finished reading
+// the slot read by iteration kt - 1, refills that slot with stage kt + S - 1,
+// and multiplies stage kt.  Stages past the end of K load zeros at no memory
+// cost, so every wavefront always has the same loads in flight.
 template <class Cfg, int LAL>
 __device__ __forceinline__ void gemm_mainloop_live(const GemmOperands<Cfg>& op, int K, int live_mb,
-                                                   uint16_t (*sW)[Cfg::TN * Cfg::BK],
-                                                   uint16_t (*sA)[Cfg::TM * Cfg::BK],
                                                    f32x4_t (&acc)[Cfg::NB][Cfg::MB]) {
-  constexpr int BK = Cfg::BK, NT = Cfg::kThreads;
-  constexpr int NB = Cfg::NB, MB = Cfg::MB, LW = Cfg::LW, LA = Cfg::LA, PW = Cfg::PW, PA = Cfg::PA;
-  constexpr int KC = Cfg::kChunks, U = Cfg::U;
+  constexpr int BK = Cfg::BK, NT = Cfg::kThreads, S = Cfg::S;
+  constexpr int NB = Cfg::NB, MB = Cfg::MB, LW = Cfg::LW, TN = Cfg::TN, TM = Cfg::TM;
+  constexpr int KC = Cfg::kChunks;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % Cfg::WGN, wm = wave / Cfg::WGN;
   const int l16 = lane & 15, g = lane >> 4;
   const int KT = (K + BK - 1) / BK;
+  using Ring = GemmRing<Cfg>;
 
-  u32x4_t rw[PW][LW], ra[PA][LA];
-  auto load_w = [&](int kt, u32x4_t (&dst)[LW]) {
+  // Loads of stage kt: slot i of this wavefront fills the 1 KB run that starts
+  // at thread (wave * 64 + i * NT)'s position of the tile.
+  auto issue = [&](int kt, uint16_t* dw, uint16_t* da) {
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
-      const bool ok = op.wofs[i] != kBufOOB && kt * BK + ((tid + i * NT) % KC) * 8 < K;
-      dst[i] = gemm_buf_load(op.rsw, ok ? op.wofs[i] + (uint32_t)(kt * BK * 2) : kBufOOB);
-    }
-  };
-  auto load_a = [&](int kt, u32x4_t (&dst)[LA]) {
-#pragma unroll
-    for (int i = 0; i < LAL; ++i) {
-      const bool ok = op.aofs[i] != kBufOOB && kt * BK + ((tid + i * NT) % KC) * 8 < K;
-      dst[i] = gemm_buf_load(op.rsa, ok ? op.aofs[i] + (uint32_t)(kt * BK * 2) : kBufOOB);
-    }
-  };
-  auto store = [&](int buf, const u32x4_t (&w)[LW], const u32x4_t (&a)[LA]) {
-#pragma unroll
-    for (int i = 0; i < LW; ++i) {
-      const int id = tid + i * NT;
-      *reinterpret_cast<u32x4_t*>(&sW[buf][gemm_lds_off<KC>(id / KC, id % KC)]) = w[i];
+      const bool ok = op.wofs[i] != kBufOOB && kt * BK + gemm_slot_chunk<Cfg>(i) * 8 < K;
+      gemm_lds_load(op.rsw, ok ? op.wofs[i] + (uint32_t)(kt * BK * 2) : kBufOOB, dw + (wave * 64 + i * NT) * 8);
     }
 #pragma unroll
     for (int i = 0; i < LAL; ++i) {
-      const int id = tid + i * NT;
-      *reinterpret_cast<u32x4_t*>(&sA[buf][gemm_lds_off<KC>(id / KC, id % KC)]) = a[i];
+      const bool ok = op.aofs[i] != kBufOOB && kt * BK + gemm_slot_chunk<Cfg>(i) * 8 < K;
+      gemm_lds_load(op.rsa, ok ? op.aofs[i] + (uint32_t)(kt * BK * 2) : kBufOOB, da + (wave * 64 + i * NT) * 8);
     }
   };
-  // One stage of MFMAs on LDS buffer buf for the first L m-blocks (L known at
-  // compile time, so the stage has no branch: every fragment read is issued
-  // before the MFMAs that use it and the LDS latency overlaps the MFMAs).
-  // Each accumulator still takes its MFMA steps in ascending k.
-  auto compute_live = [&](int buf, auto live_c) {
+  // One stage of MFMAs for the first L m-blocks (L known at compile time, so
+  // the stage has no branch: every fragment read is issued before the MFMAs
+  // that use it).  Each accumulator takes its MFMA steps in ascending k.
+  auto compute_live = [&](const uint16_t* sW, const uint16_t* sA, auto live_c) {
     constexpr int L = decltype(live_c)::value;
     u32x4_t af[BK / 32][NB], bf[BK / 32][L];
 #pragma unroll
@@ -193,10 +234,10 @@ __device__ __forceinline__ void gemm_mainloop_live(const GemmOperands<Cfg>& op, 
       const int c = ks * 4 + g;
 #pragma unroll
       for (int i = 0; i < NB; ++i)
-        af[ks][i] = *reinterpret_cast<const u32x4_t*>(&sW[buf][gemm_lds_off<KC>(wn * Cfg::WTN + i * 16 + l16, c)]);
+        af[ks][i] = *reinterpret_cast<const u32x4_t*>(&sW[gemm_lds_off<KC>(wn * Cfg::WTN + i * 16 + l16, c)]);
 #pragma unroll
       for (int j = 0; j < L; ++j)
-        bf[ks][j] = *reinterpret_cast<const u32x4_t*>(&sA[buf][gemm_lds_off<KC>(wm * Cfg::WTM + j * 16 + l16, c)]);
+        bf[ks][j] = *reinterpret_cast<const u32x4_t*>(&sA[gemm_lds_off<KC>(wm * Cfg::WTM + j * 16 + l16, c)]);
     }
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks)
@@ -205,34 +246,31 @@ __device__ __forceinline__ void gemm_mainloop_live(const GemmOperands<Cfg>& op, 
 #pragma unroll
         for (int i = 0; i < NB; ++i) acc[i][j] = mfma_16x16x32(af[ks][i], bf[ks][j], acc[i][j]);
   };
-  auto compute = [&](int buf) { gemm_dispatch_live<MB>(live_mb, [&](auto live_c) { compute_live(buf, live_c); }); };
+  auto compute = [&](const uint16_t* sW, const uint16_t* sA) {
+    gemm_dispatch_live<MB>(live_mb, [&](auto live_c) { compute_live(sW, sA, live_c); });
+  };
+  constexpr int kAfter = (S - 2) * (LW + LAL);   // loads issued after stage kt's when it is awaited
+  static_assert(TN * BK > 0 && TM * BK > 0, "tile");
 
-  // Prologue: stages 0 .. PW-1 (W) and 0 .. PA-1 (A) in flight, stage 0 in LDS.
-  // Stages past the end of K load zeros and cost no memory traffic.
-#pragma unroll
-  for (int p = 0; p < PW; ++p) load_w(p, rw[p]);
-#pragma unroll
-  for (int p = 0; p < PA; ++p) load_a(p, ra[p]);
-  store(0, rw[0], ra[0]);
-  __syncthreads();
-
-  // Stage kt lives in W slot kt % PW and A slot kt % PA until it is copied into
-  // LDS buffer kt % 2 (at the end of iteration kt - 1); at the start of
-  // iteration kt the slot is refilled with stage kt + PW (kt + PA).  The loop
-  // runs whole groups of U stages and only the MFMA step is skipped past K, so
-  // every path through the loop issues the same loads (no conservative waits).
-  const int KTU = (KT + U - 1) / U * U;
-  for (int kb = 0; kb < KTU; kb += U) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
+  gemm_for_each(std::make_integer_sequence<int, S - 1>{}, [&](auto pidx) {
+    constexpr int p = decltype(pidx)::value;
+    issue(p, Ring::template w<p>(), Ring::template a<p>());
+  });
+  const int KTS = (KT + S - 1) / S * S;
+  for (int kb = 0; kb < KTS; kb += S) {
+    auto step = [&](auto uidx) {
+      constexpr int u = decltype(uidx)::value;
+      constexpr int r = (u + S - 1) % S;
       const int kt = kb + u;
-      load_w(kt + PW, rw[u % PW]);
-      load_a(kt + PA, ra[u % PA]);
-      if (kt < KT) compute(u & 1);
-      store((u + 1) & 1, rw[(u + 1) % PW], ra[(u + 1) % PA]);
-      __syncthreads();
-    }
+      gemm_wait_then_barrier<kAfter>();
+      issue(kt + S - 1, Ring::template w<r>(), Ring::template a<r>());
+      if (kt < KT) compute(Ring::template w<u>(), Ring::template a<u>());
+    };
+    gemm_for_each(std::make_integer_sequence<int, S>{}, step);
   }
+  // The ring's last loads (zeros past the end) must land before the
+  // workgroup's LDS is released or reused by the caller.
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Accumulates the workgroup's tile over the whole of K into acc (which the
@@ -242,15 +280,13 @@ __device__ __forceinline__ void gemm_mainloop_live(const GemmOperands<Cfg>& op, 
 // others would only compute or load padding), which changes no real output.
 template <class Cfg>
 __device__ __forceinline__ void gemm_mainloop(const GemmOperands<Cfg>& op, int K, int rows_a,
-                                              uint16_t (*sW)[Cfg::TN * Cfg::BK],
-                                              uint16_t (*sA)[Cfg::TM * Cfg::BK],
                                               f32x4_t (&acc)[Cfg::NB][Cfg::MB]) {
   constexpr int R = Cfg::kThreads / Cfg::kChunks;   // tile rows per load slot
   static_assert(Cfg::kThreads % Cfg::kChunks == 0, "slot rows");
   const int live_mb = gemm_live_blocks<Cfg>(rows_a);
   const int la_live = min(Cfg::LA, (rows_a + R - 1) / R);
   gemm_dispatch_live<Cfg::LA>(la_live, [&](auto lal) {
-    gemm_mainloop_live<Cfg, decltype(lal)::value>(op, K, live_mb, sW, sA, acc);
+    gemm_mainloop_live<Cfg, decltype(lal)::value>(op, K, live_mb, acc);
   });
 }
 
@@ -303,9 +339,6 @@ template <class Cfg, bool kF32Out>
 __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][Cfg::TN * Cfg::BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][Cfg::TM * Cfg::BK];
-
   int tile_m, tile_n;
   gemm_map_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * Cfg::TM, n0 = tile_n * Cfg::TN;
@@ -328,7 +361,7 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
 
   f32x4_t acc[Cfg::NB][Cfg::MB];
   gemm_zero<Cfg>(acc);
-  gemm_mainloop<Cfg>(op, K, rows_a, sW, sA, acc);
+  gemm_mainloop<Cfg>(op, K, rows_a, acc);
 
   // Epilogue: lane holds C[m][n .. n+3].
   gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) {
@@ -339,14 +372,14 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
   });
 }
 
-// The library's one GEMM configuration, used by bi_gemm and by the expert
-// GEMMs of bi_moe_ffn.  Chosen once, by timing candidate tiles at every
+// The library's one GEMM configuration, used by bi_gemm, the expert GEMMs of
+// bi_moe_ffn and the fused lm_head.  Chosen by timing candidates at every
 // workload shape on MI355X, and used for every M: 64 (n) x 64 (m) output tile,
-// 2 x 2 wavefronts of 32 x 32, K in 128-wide stages, W and A both prefetched 4
-// stages ahead into registers.  A small n-extent keeps enough workgroups
-// streaming weights at decode batch sizes (N / 64 of them), which is what
-// bounds those HBM-bound shapes.
-using GemmLibraryCfg = GemmCfg<64, 64, 2, 2, 4, 4, 128>;
+// 2 x 2 wavefronts of 32 x 32, K in 64-wide stages, a 5-stage LDS ring (80 KB,
+// two workgroups per CU).  A small n-extent keeps enough workgroups streaming
+// weights at decode batch sizes (N / 64 of them), which is what bounds those
+// HBM-bound shapes.
+using GemmLibraryCfg = GemmCfg<64, 64, 2, 2, 5, 64, 2>;
 
 template <class Cfg>
 hipError_t launch_gemm_cfg(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc,

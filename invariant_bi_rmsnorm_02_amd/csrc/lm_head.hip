@@ -40,9 +40,6 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void lm_head_lse_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
     float* __restrict__ Z, int64_t ldz, MaxSum* __restrict__ part, int M, int N, int K, int tiles_m, int tiles_n,
     int vec_store) {
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][Cfg::TN * Cfg::BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][Cfg::TM * Cfg::BK];
-  __shared__ MaxSum xw[Cfg::WGN][Cfg::WGM][Cfg::MB][16];
 
   int tile_m, tile_n;
   gemm_map_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
@@ -65,14 +62,19 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void lm_head_lse_kernel(
 
   f32x4_t acc[Cfg::NB][Cfg::MB];
   gemm_zero<Cfg>(acc);
-  gemm_mainloop<Cfg>(op, K, rows_a, sW, sA, acc);
+  gemm_mainloop<Cfg>(op, K, rows_a, acc);
 
   gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) {
     gemm_store4_f32(Z + (int64_t)(m0 + m) * ldz + n, v, cnt, vec_store);
   });
 
   // Tile pairs.  Lane (l16, g) of wavefront (wn, wm) holds, for m-block j,
-  // row wm * WTM + 16 j + l16 at columns wn * WTN + 16 i + 4 g + e.
+  // row wm * WTM + 16 j + l16 at columns wn * WTN + 16 i + 4 g + e.  The
+  // wavefronts exchange them through the ring's first W stage, which the main
+  // loop has finished with (it ends with every load landed and a barrier).
+  using Xw = MaxSum[Cfg::WGN][Cfg::WGM][Cfg::MB][16];
+  static_assert(sizeof(Xw) <= Cfg::TN * Cfg::BK * sizeof(uint16_t), "exchange fits the ring stage");
+  Xw& xw = *reinterpret_cast<Xw*>(GemmRing<Cfg>::template w<0>());
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wn = wave % Cfg::WGN, wm = wave / Cfg::WGN;
   const int l16 = lane & 15, g = lane >> 4;

@@ -142,8 +142,6 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void moe_gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int a_rows, const uint16_t* __restrict__ Wb,
     int64_t w_expert_stride, const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ src, int E, int N, int K, int tiles_n, void* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][Cfg::TN * Cfg::BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][Cfg::TM * Cfg::BK];
 
   // The grid is sized for the worst case; only the first tiles[E] * tiles_n
   // workgroups have a tile.  Placing the real tiles (not the padded grid)
@@ -192,7 +190,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void moe_gemm_kernel(
 
   f32x4_t acc[Cfg::NB][Cfg::MB];
   gemm_zero<Cfg>(acc);
-  gemm_mainloop<Cfg>(op, K, rows_a, sW, sA, acc);
+  gemm_mainloop<Cfg>(op, K, rows_a, acc);
 
   gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) {
     if constexpr (kUp) {
