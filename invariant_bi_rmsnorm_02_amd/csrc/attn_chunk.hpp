@@ -14,16 +14,21 @@
 // shared by the workgroup's wavefronts), which moves bits, not arithmetic.
 //
 // Inside a chunk, keys are consumed in eight 32-key sub-blocks in ascending
-// order with an online max: for sub-block s and one query column,
-//   t_j   = (q . k_j) * scale * log2(e)             (masked keys: -inf)
-//   mx    = max_j t_j;  mn = max(m, mx);  ms = (mn == -inf ? 0 : mn)
-//   alpha = 2^(m - ms);  p_j = 2^(t_j - ms)
+// order with a lazily raised reference max m (log2 units): for sub-block s and
+// one query column, with c = scale * log2(e) and S_j = q . k_j (masked: -inf),
+//   mx    = c * max_j S_j                            (= max_j of c S_j: rounding is monotone)
+//   if mx > m + 8:  alpha = (m == -inf ? 1 : 2^(m - mx)),  m = mx   (else alpha = 1)
+//   p_j   = 2^(fma(S_j, c, -m'))                     (m' = m, or 0 while m = -inf)
 //   l     = l * alpha + sum_j p_j
 //   o     = o * alpha + sum_j bf16(p_j) v_j          (one MFMA per 16 head dims)
-//   m     = mn
-// starting from (m, l, o) = (-inf, 0, 0).  A sub-block with no key visible to
-// a column leaves that column's (m, l, o) bit-identical (alpha = 2^0 = 1,
-// p = 0), so a kernel may skip sub-blocks that no column of its wave can see.
+// starting from (m, l, o) = (-inf, 0, 0).  Any reference gives the same
+// softmax in exact arithmetic; raising it only when a score passes it by more
+// than 2^8 keeps every p_j <= 256 (far inside fp32 and bf16 range) while the
+// rescale of o, the costly part of an online softmax, almost never runs.
+// While m = -inf every p so far was 0, so l and o are zeros and alpha = 1
+// leaves them as they are.  A sub-block with no key visible to a column leaves
+// that column's (m, l, o) bit-identical (alpha = 1, p = 0), so a kernel may
+// skip sub-blocks that no column of its wave can see.
 // Sums over the 8 keys a lane holds run in key order, then lane^16, lane^32.
 //
 // Register layout of one wavefront (16 query rows = MFMA columns n):
@@ -43,14 +48,16 @@ namespace bi {
 constexpr int kChunk = 256;   // fixed split size in tokens
 constexpr int kSub = 32;      // keys per sub-block
 constexpr int kSubs = kChunk / kSub;
+constexpr float kRefSlack = 8.0f;   // log2 units a score may pass the reference max by
 
 // Key (relative to the sub-block) of MFMA row m' of S^T block b.
 __device__ __forceinline__ int sub_key_of_row(int mr, int b) { return 8 * (mr >> 2) + 4 * b + (mr & 3); }
 
 template <int D, int NB>
 struct ChunkAcc {
-  float m[NB];             // running max (log2 units), -inf before the first visible key
-  float l[NB];             // running sum of 2^(t - m)
+  float m[NB];             // reference max (log2 units), -inf before the first visible key
+  float nm[NB];            // -m, or 0 while m = -inf (the exponent offset)
+  float l[NB];             // running sum of 2^(c S - m)
   f32x4_t o[NB][D / 16];   // lane: column n = lane % 16, head dims 16 dt + 4 g + i
 };
 
@@ -59,6 +66,7 @@ __device__ __forceinline__ void chunk_init(ChunkAcc<D, NB>& a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     a.m[nb] = -INFINITY;
+    a.nm[nb] = 0.0f;
     a.l[nb] = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) a.o[nb][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -95,7 +103,7 @@ __device__ __forceinline__ void chunk_scores(ChunkAcc<D, NB>& a, const u32x4_t (
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) t[4 * b + i] = S[b][i] * scale_log2;
+      for (int i = 0; i < 4; ++i) t[4 * b + i] = S[b][i];
     // When every column of the wavefront sees the whole sub-block the mask
     // selects nothing; skipping it leaves every value as it is.  Otherwise key
     // 32 s + 8 g + j of the lane is visible iff j < r.
@@ -104,23 +112,30 @@ __device__ __forceinline__ void chunk_scores(ChunkAcc<D, NB>& a, const u32x4_t (
 #pragma unroll
       for (int j = 0; j < 8; ++j) t[j] = j < r ? t[j] : -INFINITY;
     }
-    float mx = -INFINITY;
+    float mx = t[0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, t[j]);
-    mx = max_xor32(max_xor16(mx));
-    const float mn = fmaxf(a.m[nb], mx);
-    const float ms = (mn == -INFINITY) ? 0.0f : mn;
-    const float alpha = exp2_hw(a.m[nb] - ms);
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, t[j]);
+    // The column max needs the other lane groups only when some lane's own
+    // keys pass the reference by more than the slack; otherwise no column of
+    // the wavefront moves and the exchange is skipped.
+    float alpha = 1.0f;
+    if (__any(mx * scale_log2 > a.m[nb] + kRefSlack)) {
+      const float cm = max_xor32(max_xor16(mx)) * scale_log2;
+      if (cm > a.m[nb] + kRefSlack) {
+        alpha = a.m[nb] == -INFINITY ? 1.0f : exp2_hw(a.m[nb] - cm);
+        a.m[nb] = cm;
+        a.nm[nb] = -cm;
+      }
+    }
     float p[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = exp2_hw(t[j] - ms);
+    for (int j = 0; j < 8; ++j) p[j] = exp2_hw(fmaf(t[j], scale_log2, a.nm[nb]));
     // Key order.  p >= 0 is never -0, so starting from p[0] is 0 + p[0] to the bit.
     float ls = p[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) ls = ls + p[j];
     ls = add_xor32(add_xor16(ls));
     a.l[nb] = a.l[nb] * alpha + ls;
-    a.m[nb] = mn;
     sp.alpha[nb] = alpha;
     sp.pb[nb] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                         pack_bf16x2(p[6], p[7])};
