@@ -171,7 +171,7 @@ __global__ __launch_bounds__(64, 2) void split_decode_partial_kernel(
   const int n_sub = (len + kSub - 1) / kSub;
   ChunkAcc<D, 1> acc;
   chunk_init(acc);
-  SubProbs<1> spb;
+  u32x4_t spb[1];
   // Ping-pong over sub-blocks; the fetch of a sub-block past the split is still
   // issued (from valid memory, its result unused) so every path keeps the same
   // loads in flight.
@@ -182,21 +182,22 @@ __global__ __launch_bounds__(64, 2) void split_decode_partial_kernel(
     mask_k(fa);
     chunk_scores<D, 1>(acc, fa.k, qf, nvalid, j, scale_log2, spb);
     mask_v(fa);
-    chunk_values<D, 1>(acc, fa.v, spb);
+    sub_values<D, 1>(acc, fa.v, spb);
     if (j + 1 >= n_sub) break;
     fetch(j + 2, fa);
     mask_k(fb);
     chunk_scores<D, 1>(acc, fb.k, qf, nvalid, j + 1, scale_log2, spb);
     mask_v(fb);
-    chunk_values<D, 1>(acc, fb.v, spb);
+    sub_values<D, 1>(acc, fb.v, spb);
   }
+  const float lc = chunk_l(acc, 0);   // cross-lane: every lane takes part
   if (n < G) {
     float* rec = ws + (((int64_t)b * Hq + h * G + n) * splits + sp) * (D + 4);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = acc.o[0][dt];
     if (g == 0) {
       rec[D] = acc.m[0];
-      rec[D + 1] = acc.l[0];
+      rec[D + 1] = lc;
     }
   }
 }

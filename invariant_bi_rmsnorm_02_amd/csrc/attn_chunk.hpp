@@ -18,9 +18,10 @@
 // one query column, with c = scale * log2(e) and S_j = q . k_j (masked: -inf),
 //   mx    = c * max_j S_j                            (= max_j of c S_j: rounding is monotone)
 //   if mx > m + 8:  alpha = (m == -inf ? 1 : 2^(m - mx)),  m = mx   (else alpha = 1)
+//   l     = l * alpha,  o = o * alpha
 //   p_j   = 2^(fma(S_j, c, -m'))                     (m' = m, or 0 while m = -inf)
-//   l     = l * alpha + sum_j p_j
-//   o     = o * alpha + sum_j bf16(p_j) v_j          (one MFMA per 16 head dims)
+//   l     = l + sum_j p_j                            (per lane, see below)
+//   o     = o + sum_j bf16(p_j) v_j                  (one MFMA per 16 head dims)
 // starting from (m, l, o) = (-inf, 0, 0).  Any reference gives the same
 // softmax in exact arithmetic; raising it only when a score passes it by more
 // than 2^8 keeps every p_j <= 256 (far inside fp32 and bf16 range) while the
@@ -28,8 +29,10 @@
 // While m = -inf every p so far was 0, so l and o are zeros and alpha = 1
 // leaves them as they are.  A sub-block with no key visible to a column leaves
 // that column's (m, l, o) bit-identical (alpha = 1, p = 0), so a kernel may
-// skip sub-blocks that no column of its wave can see.
-// Sums over the 8 keys a lane holds run in key order, then lane^16, lane^32.
+// skip sub-blocks that no column of its wave can see.  Each lane keeps its
+// own part of l: the sum over the keys it holds (8 g .. 8 g + 7 of every
+// sub-block), added in key order and rescaled with the column; the four parts
+// of a column are combined once per chunk, lane^16 then lane^32.
 //
 // Register layout of one wavefront (16 query rows = MFMA columns n):
 //   S^T = K Q^T  (MFMA A = keys, B = Q^T, k = head dim; d of k index
@@ -57,7 +60,7 @@ template <int D, int NB>
 struct ChunkAcc {
   float m[NB];             // reference max (log2 units), -inf before the first visible key
   float nm[NB];            // -m, or 0 while m = -inf (the exponent offset)
-  float l[NB];             // running sum of 2^(c S - m)
+  float l[NB];             // this lane's part of the running sum of 2^(c S - m)
   f32x4_t o[NB][D / 16];   // lane: column n = lane % 16, head dims 16 dt + 4 g + i
 };
 
@@ -73,108 +76,143 @@ __device__ __forceinline__ void chunk_init(ChunkAcc<D, NB>& a) {
   }
 }
 
-// One 32-key sub-block s of the chunk, in two halves so that a kernel can
-// bring in V between them: chunk_scores (S = K Q^T, online max and sum, the
-// bf16 probabilities) and chunk_values (O = O * alpha + V^T P^T).
+// One 32-key sub-block s of the chunk, as five steps that every kernel runs in
+// this order for each column (a kernel may interleave the steps of different
+// sub-blocks, e.g. start the scores of s + 1 before the values of s):
+//   sub_scores    S = K Q^T (raw q . k, one fp32 MFMA chain per element)
+//   sub_mask      keys the column cannot see -> -inf
+//   sub_reference maybe raise m; a column that moves rescales its l and o
+//   sub_probs     p = 2^fma(S, c, -m), l += sum p, P^T in bf16
+//   sub_values    O^T += V^T P^T
 // kf: S^T A operands [block b][step ks]; vf: O^T A operands [dim tile dt];
 // qf: Q^T B operands [n-block][step ks]; n_valid[nb]: keys of the chunk that
 // column (lane % 16) of n-block nb may see (keys 0 .. n_valid - 1).
-template <int NB>
-struct SubProbs {
-  u32x4_t pb[NB];   // bf16 p of the lane's 8 keys (MFMA B operand of O^T)
-  float alpha[NB];  // rescale of the previous (l, o)
-};
-
 template <int D, int NB>
-__device__ __forceinline__ void chunk_scores(ChunkAcc<D, NB>& a, const u32x4_t (&kf)[2][D / 32],
-                                             const u32x4_t (&qf)[NB][D / 32], const int (&n_valid)[NB], int s,
-                                             float scale_log2, SubProbs<NB>& sp) {
+__device__ __forceinline__ void sub_scores(const u32x4_t (&kf)[2][D / 32], const u32x4_t (&qf)[NB][D / 32],
+                                           f32x4_t (&S)[NB][2]) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      S[nb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) S[nb][b] = mfma_16x16x32(kf[b][ks], qf[nb][ks], S[nb][b]);
+    }
+}
+
+// Lane group g holds keys 8 g + j of the sub-block, j = 4 b + i for S[nb][b][i].
+// When every column of the wavefront sees the whole sub-block the mask selects
+// nothing; skipping it leaves every value as it is.  Otherwise key 32 s + 8 g
+// + j is visible iff j < r.
+template <int NB>
+__device__ __forceinline__ void sub_mask(f32x4_t (&S)[NB][2], const int (&n_valid)[NB], int s) {
   const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    f32x4_t S[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      S[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) S[b] = mfma_16x16x32(kf[b][ks], qf[nb][ks], S[b]);
-    }
-    float t[8];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t[4 * b + i] = S[b][i];
-    // When every column of the wavefront sees the whole sub-block the mask
-    // selects nothing; skipping it leaves every value as it is.  Otherwise key
-    // 32 s + 8 g + j of the lane is visible iff j < r.
     if (!__all(kSub * (s + 1) <= n_valid[nb])) {
       const int r = n_valid[nb] - kSub * s - 8 * g;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t[j] = j < r ? t[j] : -INFINITY;
-    }
-    float mx = t[0];
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, t[j]);
-    // The column max needs the other lane groups only when some lane's own
-    // keys pass the reference by more than the slack; otherwise no column of
-    // the wavefront moves and the exchange is skipped.
-    float alpha = 1.0f;
+        for (int i = 0; i < 4; ++i) S[nb][b][i] = 4 * b + i < r ? S[nb][b][i] : -INFINITY;
+    }
+  }
+}
+
+// The column max needs the other lane groups only when some lane's own keys
+// pass the reference by more than the slack; otherwise no column of the
+// wavefront moves and the exchange is skipped.  A column that moves has its l
+// and o multiplied by alpha = 2^(m_old - m_new) (alpha = 1 while m_old = -inf:
+// l and o are zeros then); the others keep theirs, as alpha = 1 would.
+template <int D, int NB>
+__device__ __forceinline__ void sub_reference(ChunkAcc<D, NB>& a, const f32x4_t (&S)[NB][2], float scale_log2) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float mx = S[nb][0][0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, S[nb][j >> 2][j & 3]);
     if (__any(mx * scale_log2 > a.m[nb] + kRefSlack)) {
       const float cm = max_xor32(max_xor16(mx)) * scale_log2;
       if (cm > a.m[nb] + kRefSlack) {
-        alpha = a.m[nb] == -INFINITY ? 1.0f : exp2_hw(a.m[nb] - cm);
+        const float alpha = a.m[nb] == -INFINITY ? 1.0f : exp2_hw(a.m[nb] - cm);
         a.m[nb] = cm;
         a.nm[nb] = -cm;
+        a.l[nb] = a.l[nb] * alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const f32x4_t o = a.o[nb][dt];
+          a.o[nb][dt] = f32x4_t{o[0] * alpha, o[1] * alpha, o[2] * alpha, o[3] * alpha};
+        }
       }
     }
-    float p[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = exp2_hw(fmaf(t[j], scale_log2, a.nm[nb]));
-    // Key order.  p >= 0 is never -0, so starting from p[0] is 0 + p[0] to the bit.
-    float ls = p[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) ls = ls + p[j];
-    ls = add_xor32(add_xor16(ls));
-    a.l[nb] = a.l[nb] * alpha + ls;
-    sp.alpha[nb] = alpha;
-    sp.pb[nb] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                        pack_bf16x2(p[6], p[7])};
   }
 }
 
 template <int D, int NB>
-__device__ __forceinline__ void chunk_values(ChunkAcc<D, NB>& a, const u32x4_t (&vf)[D / 16],
-                                             const SubProbs<NB>& sp) {
+__device__ __forceinline__ void sub_probs(ChunkAcc<D, NB>& a, const f32x4_t (&S)[NB][2], float scale_log2,
+                                          u32x4_t (&pb)[NB]) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const float alpha = sp.alpha[nb];
-    // alpha == 1 (the running max did not move) in every lane: o * 1 is o, so
-    // the rescale is skipped without changing a bit.
-    if (__any(alpha != 1.0f)) {
+    float p[8];
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const f32x4_t o = a.o[nb][dt];
-        a.o[nb][dt] = f32x4_t{o[0] * alpha, o[1] * alpha, o[2] * alpha, o[3] * alpha};
-      }
-    }
+    for (int j = 0; j < 8; ++j) p[j] = exp2_hw(fmaf(S[nb][j >> 2][j & 3], scale_log2, a.nm[nb]));
+    float l = a.l[nb];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) a.o[nb][dt] = mfma_16x16x32(vf[dt], sp.pb[nb], a.o[nb][dt]);
+    for (int j = 0; j < 8; ++j) l = l + p[j];
+    a.l[nb] = l;
+    pb[nb] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                     pack_bf16x2(p[6], p[7])};
   }
+}
+
+template <int D, int NB>
+__device__ __forceinline__ void sub_values(ChunkAcc<D, NB>& a, const u32x4_t (&vf)[D / 16], const u32x4_t (&pb)[NB]) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) a.o[nb][dt] = mfma_16x16x32(vf[dt], pb[nb], a.o[nb][dt]);
+}
+
+// The column's l: its four lane parts combined, lane^16 then lane^32 (every
+// lane of the column gets the same value).
+template <int D, int NB>
+__device__ __forceinline__ float chunk_l(const ChunkAcc<D, NB>& a, int nb) {
+  return add_xor32(add_xor16(a.l[nb]));
+}
+
+// The first four steps of a sub-block in one call (the fifth, sub_values,
+// follows once V is in the registers).
+template <int D, int NB>
+__device__ __forceinline__ void chunk_scores(ChunkAcc<D, NB>& a, const u32x4_t (&kf)[2][D / 32],
+                                             const u32x4_t (&qf)[NB][D / 32], const int (&n_valid)[NB], int s,
+                                             float scale_log2, u32x4_t (&pb)[NB]) {
+  f32x4_t S[NB][2];
+  sub_scores<D, NB>(kf, qf, S);
+  sub_mask<NB>(S, n_valid, s);
+  sub_reference<D, NB>(a, S, scale_log2);
+  sub_probs<D, NB>(a, S, scale_log2, pb);
 }
 
 // One step of the ascending fold over chunks: state (m, l, acc) absorbs the
 // chunk partial (mc, lc, accc).  The state starts at (-inf, 0, 0); mc is
-// finite for every chunk that is folded.  Both kernels call this, element by
-// element, with the same operands.
+// finite for every chunk that is folded.  Like the chunk step, the state's
+// reference moves only when the chunk's passes it by more than the slack, so
+// in the common case alpha = 1 and a merge is one fma per element.  Every
+// kernel calls these, element by element, with the same operands.
 struct MergeCoef {
   float m, alpha, beta;
 };
 __device__ __forceinline__ MergeCoef merge_coef(float m, float mc) {
-  const float mn = fmaxf(m, mc);
-  return MergeCoef{mn, exp2_hw(m - mn), exp2_hw(mc - mn)};
+  const bool mv = mc > m + kRefSlack;   // always while m = -inf (acc and l are zeros then)
+  const float d = exp2_hw(mv ? m - mc : mc - m);
+  return MergeCoef{mv ? mc : m, mv && m != -INFINITY ? d : 1.0f, mv ? 1.0f : d};
 }
 __device__ __forceinline__ float merge_val(float acc, float accc, const MergeCoef& k) {
-  return acc * k.alpha + accc * k.beta;
+  return fmaf(accc, k.beta, acc * k.alpha);
+}
+// merge_val when alpha = 1 (acc * 1 is acc, so the bits are the same).
+__device__ __forceinline__ float merge_val_unit(float acc, float accc, const MergeCoef& k) {
+  return fmaf(accc, k.beta, acc);
 }
 
 // Final normalisation; +0.0f turns a -0 into +0 so that a zero result has one

@@ -181,7 +181,7 @@ __global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(
   // the next chunk (whose page ids are loaded one chunk ahead).
   using Src = GlobalChunk<D>;
   typename Src::Frags fa, fb;
-  SubProbs<1> sp;
+  u32x4_t sp[1];   // bf16 P^T of the sub-block in flight
   ChunkAcc<D, 1> acc;
   // Fold state (kFold): m and l in registers, the running o in LDS (the
   // wavefront is its own workgroup; lane l owns o_run[.][l]), which keeps it
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(
       Src::mask_k(fa);
       chunk_scores<D, 1>(acc, fa.k, qf, nvalid, s, scale_log2, sp);
       Src::mask_v(fa);
-      chunk_values<D, 1>(acc, fa.v, sp);
+      sub_values<D, 1>(acc, fa.v, sp);
       if (s + 1 >= n_sub) break;
       if (s + 2 < kSubs) {
         src.fetch(s + 2, fa, s + 2 < n_sub);
@@ -225,27 +225,38 @@ __global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(
       Src::mask_k(fb);
       chunk_scores<D, 1>(acc, fb.k, qf, nvalid, s + 1, scale_log2, sp);
       Src::mask_v(fb);
-      chunk_values<D, 1>(acc, fb.v, sp);
+      sub_values<D, 1>(acc, fb.v, sp);
       if (s + 2 >= n_sub) break;
     }
     if constexpr (kFold) {
       const MergeCoef k = merge_coef(m_run, acc.m[0]);
-      l_run = merge_val(l_run, acc.l[0], k);
+      l_run = merge_val(l_run, chunk_l(acc, 0), k);
+      if (__all(k.alpha == 1.0f)) {
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        f32x4_t r = o_run[dt][lane];
+        for (int dt = 0; dt < D / 16; ++dt) {
+          f32x4_t r = o_run[dt][lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = merge_val(r[i], acc.o[0][dt][i], k);
-        o_run[dt][lane] = r;
+          for (int i = 0; i < 4; ++i) r[i] = merge_val_unit(r[i], acc.o[0][dt][i], k);
+          o_run[dt][lane] = r;
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          f32x4_t r = o_run[dt][lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = merge_val(r[i], acc.o[0][dt][i], k);
+          o_run[dt][lane] = r;
+        }
       }
       m_run = k.m;
     } else {
+      const float lc = chunk_l(acc, 0);   // cross-lane: every lane takes part
       if (row_ok) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = acc.o[0][dt];
         if (g == 0) {
           rec[D] = acc.m[0];
-          rec[D + 1] = acc.l[0];
+          rec[D + 1] = lc;
         }
       }
       rec += D + 4;

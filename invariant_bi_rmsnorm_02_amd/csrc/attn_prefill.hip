@@ -61,39 +61,29 @@ __device__ __forceinline__ void wait_vmem_then_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// D: head dim.  STAGES: LDS ring depth in sub-blocks (divides the 8 of a
-// chunk, so a sub-block's stage is static).  REGFOLD: column blocks whose fold
-// state stays in registers (the rest wait in LDS).  OCC: workgroups per CU the
-// register budget aims at.
-template <int D, int STAGES, int REGFOLD, int OCC>
+// D: head dim.  REGFOLD: column blocks whose fold state stays in registers
+// (the rest wait in LDS).  OCC: workgroups per CU the register budget aims at.
+template <int D, int REGFOLD, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const int32_t* __restrict__ q_start,
     const int32_t* __restrict__ ctx_lens, int num_seqs, int tiles, int max_q_len, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table, int max_pages,
     int Hq, int Hkv, int log2_ps, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int TE = kTile * D;                          // elements per tile
-  constexpr int kPieces = 2 * TE * 2 / 1024;             // 1 KB loads per sub-block (K or V: two tiles)
+  constexpr int kPieces = 2 * TE * 2 / 1024;             // 1 KB loads per sub-block of K (two tiles); V the same
   constexpr int IPW = kPieces / kWaves;                  // ... per wavefront
   static_assert(IPW >= 1 && kPieces % kWaves == 0, "staging split");
-  // Tiles sit TS elements apart in a stage: the 128-byte pad puts tile 1 on
-  // the other half of the LDS banks, so a K fragment read (lanes 0-7 in tile
-  // 0, lanes 8-15 in tile 1) is free of bank conflicts.
+  // Tiles sit TS elements apart: the 128-byte pad puts tile 1 on the other
+  // half of the LDS banks, so a K fragment read (lanes 0-7 in tile 0, lanes
+  // 8-15 in tile 1) is free of bank conflicts.
   constexpr int TS = TE + 64;
-  // One array per stage (K tiles at 0 and TS, V tiles at 2 TS and 3 TS), so the compiler can tell the
-  // stages' loads apart and wait only for the stage an LDS read needs.
-  __shared__ __attribute__((aligned(16))) uint16_t st0[4 * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t st1[4 * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t st2[4 * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t st3[4 * TS];
-  static_assert(STAGES == 2 || STAGES == 4, "one array per stage above");
+  // Two K stages and two V stages, each its own array, so the compiler can
+  // tell the stages' loads apart and wait only for the stage an LDS read needs.
+  __shared__ __attribute__((aligned(16))) uint16_t sk0[2 * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t sk1[2 * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv0[2 * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv1[2 * TS];
   static_assert(REGFOLD >= 0 && REGFOLD <= kNB, "fold split");
-  auto stage = [&](auto idx) -> uint16_t* {
-    constexpr int i = decltype(idx)::value;
-    if constexpr (i == 0) return st0;
-    else if constexpr (i == 1) return st1;
-    else if constexpr (i == 2) return st2;
-    else return st3;
-  };
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
   // Work placement (arithmetic does not depend on it).  Items (sequence,
@@ -135,7 +125,6 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
   if (nq <= 0 || ctx < 0 || row0 >= rows) return;
   const int lim = ctx + (min(row0 + kRowsPerBlock, rows) - 1) / G + 1;   // keys >= lim: no row sees them
   const int wrow0 = row0 + wave * kRowsPerWave;
-  const int wave_lim = wrow0 < rows ? ctx + (min(wrow0 + kRowsPerWave, rows) - 1) / G + 1 : 0;
 
   int pos[kNB];
   bool row_ok[kNB];
@@ -153,38 +142,40 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
   }
 
   const int ps = 1 << log2_ps;
-  const int ppc = kChunk >> log2_ps;   // pages per chunk
   const int32_t* bt = block_table + (int64_t)sq * max_pages;
-  const int64_t page_elems = (int64_t)(Hkv << log2_ps) * D;
-  const int64_t head_off = (int64_t)h * ps * D;
-  // Raw block-table entries of chunk c, one logical page per lane (lane l:
-  // page c * ppc + l % ppc), read from a clamped index; validated where used,
-  // so loading the next chunk's entries early never waits.
-  auto raw_pages = [&](int c) { return bt[min(c * ppc + (lane % ppc), max_pages - 1)]; };
-
-  // Loads of sub-block u (keys 32 u .. 32 u + 31) into a stage: this
-  // wavefront's IPW 1 KB pieces of the K tiles and of the V tiles.  `pages`
-  // holds the raw entries of the sub-block's chunk.  Issued for every u, also
-  // past the end (as zeros), so every wavefront always has the same number of
-  // loads in flight.
-  auto issue = [&](int u, int pages, uint16_t* dst) {
-#pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int pc = wave * IPW + j;                     // piece of the sub-block
-      const int tt = pc * 1024 / (TE * 2);               // its tile (0 or 1)
-      const int inb = pc * 1024 - tt * (TE * 2);         // byte offset inside the tile
-      const int t0 = u * kSub + kTile * tt;              // the tile's first key
-      const int lp = t0 >> log2_ps;
-      const int raw = __builtin_amdgcn_readlane(pages, (t0 & (kChunk - 1)) >> log2_ps);
-      const bool ok = t0 < lim && lp < max_pages && raw >= 0 && raw < num_pages;
-      const int64_t tb = ok ? raw * page_elems + head_off + (int64_t)((t0 & (ps - 1)) >> 4) * TE : 0;
-      const uint32_t bytes = ok ? TE * 2 : 0;
-      lds_dma16(kc + tb, bytes, inb + lane * 16, dst + tt * TS + inb / 2);
-      lds_dma16(vc + tb, bytes, inb + lane * 16, dst + (2 + tt) * TS + inb / 2);
-    }
+  // Tile table of a chunk: lane l holds, for tile l % 16 of the chunk (keys
+  // 16 (l % 16) .. + 15), the tile's index in the cache counted in tiles of
+  // TE elements, or -1 when no row of the workgroup sees it, it lies past the
+  // block table, or its page id is outside the pool.  Built one chunk ahead
+  // from block-table entries read two chunks ahead (from a clamped index), so
+  // neither the read nor the table ever waits.
+  const int tiles_per_page = (Hkv << log2_ps) / kTile;
+  const int head_tiles = h * (ps / kTile);
+  auto raw_entry = [&](int c) {
+    return bt[min(c * (kChunk >> log2_ps) + (((lane & 15) * kTile) >> log2_ps), max_pages - 1)];
   };
-  // Loads issued after sub-block u's when the wavefront waits for u.
-  constexpr int kAfter = (STAGES - 2) * 2 * IPW;
+  auto make_tab = [&](int c, int raw) {
+    const int t0 = c * kChunk + (lane & 15) * kTile;
+    const bool ok = t0 < lim && (t0 >> log2_ps) < max_pages && raw >= 0 && raw < num_pages;
+    return ok ? raw * tiles_per_page + head_tiles + ((t0 & (ps - 1)) >> 4) : -1;
+  };
+
+  // The 1 KB pieces of sub-block u (keys 32 u .. 32 u + 31) that this
+  // wavefront loads, K or V, into a stage; `tab` is the table of u's chunk.
+  // A wavefront's pieces lie in one tile.  Issued for every u, also past the
+  // end (as zeros), so every wavefront always has the same number of loads in
+  // flight.
+  static_assert((TE * 2 / 1024) % IPW == 0, "a wavefront's pieces share a tile");
+  auto issue = [&](const uint16_t* cache, int u, int tab, uint16_t* dst) {
+    const int pc0 = wave * IPW;                          // first piece of the wavefront
+    const int tt = pc0 * 1024 / (TE * 2);                // its tile (0 or 1)
+    const int inb0 = pc0 * 1024 - tt * (TE * 2);         // byte offset inside the tile
+    const int tile = __builtin_amdgcn_readlane(tab, 2 * (u & (kSubs - 1)) + tt);
+    const uint16_t* base = cache + (tile >= 0 ? (int64_t)tile * TE : 0);
+#pragma unroll
+    for (int j = 0; j < IPW; ++j)
+      lds_dma16(base, tile >= 0 ? TE * 2 : 0, inb0 + 1024 * j + lane * 16, dst + tt * TS + (inb0 + 1024 * j) / 2);
+  };
 
   // Running state of the fold over chunks (per column block).  The
   // accumulators are touched once per chunk; those of column blocks >= REGFOLD
@@ -211,97 +202,127 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
     for (int dt = 0; dt < D / 16; ++dt) fold_put(nb, dt, f32x4_t{0.f, 0.f, 0.f, 0.f});
   }
 
-  const int nch = (lim + kChunk - 1) / kChunk;
-  const int last_subs = (lim - (nch - 1) * kChunk + kSub - 1) / kSub;
-
+  // Software pipeline over sub-blocks u = 0 .. nsub - 1 (chunk c = u / 8,
+  // sub-block s = u % 8).  Step u waits for K(u + 1) and V(u), refills the
+  // stages that step u - 1 finished with (K(u + 2), V(u + 1)), and then, in one
+  // branch-free stretch, issues the score MFMAs of u + 1 while it computes the
+  // probabilities of u and their value MFMAs.  Sub-block u + 1's mask and
+  // reference update close the step.  Per column this is the chunk step's
+  // order exactly; only independent work of two sub-blocks is interleaved.
+  // Every wavefront runs every sub-block below the workgroup's limit; one its
+  // columns cannot see is an exact identity (all p = 0, alpha = 1).
+  const int nsub = (lim + kSub - 1) / kSub;
+  int c = 0;
+  int cur_tab = make_tab(0, raw_entry(0)), next_tab = make_tab(1, raw_entry(1)), raw_ahead = raw_entry(2);
   ChunkAcc<D, kNB> ca;
+  chunk_init(ca);
   int nvalid[kNB];
-  int cur_pages = raw_pages(0), next_pages = raw_pages(1);
-  static_assert(STAGES - 1 <= kSubs, "prologue stays in chunk 0");
-  issue(0, cur_pages, stage(StageIdx<0>{}));
-  if constexpr (STAGES == 4) {
-    issue(1, cur_pages, stage(StageIdx<1>{}));
-    issue(2, cur_pages, stage(StageIdx<2>{}));
-  }
-  // Outer loop over chunks, the 8 sub-blocks of a chunk written out so that
-  // stages are static: sub-block u = 8 c + s sits in stage s % 4.
-  for (int c = 0; c < nch; ++c) {
-    const int after_pages = raw_pages(c + 2);
-    chunk_init(ca);
+  auto set_nvalid = [&]() {
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
       nvalid[nb] = row_ok[nb] ? max(0, min(kChunk, pos[nb] + 1 - c * kChunk)) : 0;
-    const int subs = c == nch - 1 ? last_subs : kSubs;
-    // One 32-key sub-block: wait for its stage, refill the stage that the
-    // previous step read with sub-block u + 3, run the chunk step.
-    auto step = [&](auto sidx, auto cur_stage, auto refill_stage) {
-      constexpr int s = decltype(sidx)::value;
-      const int u = c * kSubs + s;
-      wait_vmem_then_barrier<kAfter>();
-      issue(u + STAGES - 1, s + STAGES - 1 < kSubs ? cur_pages : next_pages, stage(refill_stage));
-      const int sub0 = u * kSub;
-      if (sub0 < wave_lim) {   // some column of this wave sees a key here
-        const uint16_t* sK = stage(cur_stage);
-        const uint16_t* sV = sK + 2 * TS;
-        const int l16 = n;
-        u32x4_t kf[2][D / 32], vf[D / 16];
-        // Same operand addressing as decode, inside the LDS copy of the two tiles.
-        const int kofs = (l16 >> 3) * TS + g * 128 + (l16 & 7) * 8;
+  };
+  set_nvalid();
+  // Same operand addressing as decode, inside the LDS copy of the two tiles.
+  const int kofs = (n >> 3) * TS + g * 128 + (n & 7) * 8;
+  const int vofs = (g >> 1) * TS + (g & 1) * 128 + n * 8;
+  auto scores = [&](const uint16_t* sK, f32x4_t (&S)[kNB][2]) {
+    u32x4_t kf[2][D / 32];
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int ks = 0; ks < D / 32; ++ks)
-            kf[b][ks] = *reinterpret_cast<const u32x4_t*>(&sK[kofs + 4 * ks * 128 + 8 * b * 8]);
-        SubProbs<kNB> sp;
-        chunk_scores<D, kNB>(ca, kf, qf, nvalid, s, scale_log2, sp);
-        // V is read once the K fragments are dead, which keeps the two apart
-        // in the register file.
-        const int vofs = (g >> 1) * TS + (g & 1) * 128 + l16 * 8;
+      for (int ks = 0; ks < D / 32; ++ks)
+        kf[b][ks] = *reinterpret_cast<const u32x4_t*>(&sK[kofs + 4 * ks * 128 + 8 * b * 8]);
+    sub_scores<D, kNB>(kf, qf, S);
+  };
+
+  f32x4_t S[kNB][2];
+  issue(kc, 0, cur_tab, sk0);
+  issue(vc, 0, cur_tab, sv0);
+  issue(kc, 1, cur_tab, sk1);
+  wait_vmem_then_barrier<0>();
+  scores(sk0, S);
+  sub_mask<kNB>(S, nvalid, 0);
+  sub_reference<D, kNB>(ca, S, scale_log2);
+
+  // P = u % 2: step u reads K stage (u + 1) % 2 and V stage u % 2 and refills
+  // K stage u % 2 and V stage (u + 1) % 2.
+  auto step = [&](int u, auto par) {
+    constexpr int P = decltype(par)::value;
+    uint16_t* const sk_rd = P == 0 ? sk1 : sk0;
+    uint16_t* const sk_wr = P == 0 ? sk0 : sk1;
+    uint16_t* const sv_rd = P == 0 ? sv0 : sv1;
+    uint16_t* const sv_wr = P == 0 ? sv1 : sv0;
+    wait_vmem_then_barrier<0>();
+    issue(kc, u + 2, ((u + 2) >> 3) == c ? cur_tab : next_tab, sk_wr);
+    issue(vc, u + 1, ((u + 1) >> 3) == c ? cur_tab : next_tab, sv_wr);
+
+    f32x4_t Sn[kNB][2];
+    scores(sk_rd, Sn);
+    u32x4_t pb[kNB];
+    sub_probs<D, kNB>(ca, S, scale_log2, pb);
+    u32x4_t vf[D / 16];
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *reinterpret_cast<const u32x4_t*>(&sV[vofs + dt * 256]);
-        // The sub-block holding the limit: V of keys >= lim may be stale.
-        if (sub0 + kSub > lim) {
-          const KeepMask km = keep_mask(lim - (sub0 + 8 * g));
+    for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *reinterpret_cast<const u32x4_t*>(&sv_rd[vofs + dt * 256]);
+    // The sub-block holding the limit: V of keys >= lim may be stale.
+    if ((u + 1) * kSub > lim) {
+      const KeepMask km = keep_mask(lim - (u * kSub + 8 * g));
 #pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) vf[dt] = apply_keep(vf[dt], km);
-        }
-        chunk_values<D, kNB>(ca, vf, sp);
-      }
-    };
-    // Sub-block s reads stage s % STAGES and refills the stage read by s - 1.
-    auto run = [&](auto sidx) {
-      constexpr int s = decltype(sidx)::value;
-      if (s < subs) step(sidx, StageIdx<s % STAGES>{}, StageIdx<(s + STAGES - 1) % STAGES>{});
-    };
-    static_assert(kSubs == 8, "sub-blocks below are written out");
-    run(StageIdx<0>{});
-    run(StageIdx<1>{});
-    run(StageIdx<2>{});
-    run(StageIdx<3>{});
-    run(StageIdx<4>{});
-    run(StageIdx<5>{});
-    run(StageIdx<6>{});
-    run(StageIdx<7>{});
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      if (nvalid[nb] > 0) {
-        const MergeCoef k = merge_coef(m_run[nb], ca.m[nb]);
-        l_run[nb] = merge_val(l_run[nb], ca.l[nb], k);
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          f32x4_t o = fold_get(nb, dt);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = merge_val(o[i], ca.o[nb][dt][i], k);
-          fold_put(nb, dt, o);
-        }
-        m_run[nb] = k.m;
-      }
+      for (int dt = 0; dt < D / 16; ++dt) vf[dt] = apply_keep(vf[dt], km);
     }
-    cur_pages = next_pages;
-    next_pages = after_pages;
+    sub_values<D, kNB>(ca, vf, pb);
+
+    // Chunk end: fold the chunk into the running state, start the next one.
+    if (((u + 1) & (kSubs - 1)) == 0 || u + 1 == nsub) {
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const float lc = chunk_l(ca, nb);   // cross-lane: every lane takes part
+        if (nvalid[nb] > 0) {
+          const MergeCoef k = merge_coef(m_run[nb], ca.m[nb]);
+          l_run[nb] = merge_val(l_run[nb], lc, k);
+          if (__all(k.alpha == 1.0f)) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+              f32x4_t o = fold_get(nb, dt);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) o[i] = merge_val_unit(o[i], ca.o[nb][dt][i], k);
+              fold_put(nb, dt, o);
+            }
+          } else {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+              f32x4_t o = fold_get(nb, dt);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) o[i] = merge_val(o[i], ca.o[nb][dt][i], k);
+              fold_put(nb, dt, o);
+            }
+          }
+          m_run[nb] = k.m;
+        }
+      }
+      ++c;
+      cur_tab = next_tab;
+      next_tab = make_tab(c + 1, raw_ahead);
+      raw_ahead = raw_entry(c + 2);
+      chunk_init(ca);
+      set_nvalid();
+    }
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) S[nb][b] = Sn[nb][b];
+    if (u + 1 < nsub) {
+      sub_mask<kNB>(S, nvalid, (u + 1) & (kSubs - 1));
+      sub_reference<D, kNB>(ca, S, scale_log2);
+    }
+  };
+  for (int u = 0; u < nsub; u += 2) {
+    step(u, StageIdx<0>{});
+    if (u + 1 >= nsub) break;
+    step(u + 1, StageIdx<1>{});
   }
-  // The ring's last loads (zeros past the end) must land before the
-  // workgroup's LDS is released.
+  // The last loads (zeros past the end) must land before the workgroup's LDS
+  // is released.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
@@ -322,9 +343,8 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
 }
 
 // The library's configuration: two workgroups per CU (registers <= 256 and
-// LDS <= 80 KB each), a two-stage ring and column block 0's fold state in
-// registers.
-constexpr int kLibStages = 2, kLibRegFold = 1, kLibOcc = 2;
+// LDS <= 80 KB each) and column block 0's fold state in registers.
+constexpr int kLibRegFold = 1, kLibOcc = 2;
 
 template <int D>
 hipError_t launch(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens, int num_seqs,
@@ -333,7 +353,10 @@ hipError_t launch(const void* q, int64_t ld_q, const int32_t* q_start, const int
   const int tiles = (max_q_len * G + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t blocks = (int64_t)tiles * g.num_kv_heads * num_seqs;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_prefill_kernel<D, kLibStages, kLibRegFold, kLibOcc>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+  // Tile indices into the cache are 32-bit (a 288 GB pool holds < 2^27 tiles).
+  if ((int64_t)g.num_pages * (((int64_t)g.num_kv_heads << g.log2_page) / kTile) > 0x7fffffff)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_prefill_kernel<D, kLibRegFold, kLibOcc>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), ld_q, q_start, ctx_lens, num_seqs, tiles, max_q_len,
                      static_cast<const uint16_t*>(g.k_cache), static_cast<const uint16_t*>(g.v_cache),
                      g.num_pages, g.block_table, g.max_pages_per_seq, g.num_q_heads, g.num_kv_heads,
