@@ -223,8 +223,9 @@ __global__ __launch_bounds__(64) void split_decode_merge_kernel(const float* __r
     m = k.m;
   }
   uint16_t* op = out + ((int64_t)b * Hq + head) * D + lane * E;
+  const float inv = finalize_inv(l);
 #pragma unroll
-  for (int e = 0; e < E; ++e) op[e] = C > 0 ? static_cast<uint16_t>(f32_to_bf16(finalize_val(acc[e], l))) : 0;
+  for (int e = 0; e < E; ++e) op[e] = C > 0 ? static_cast<uint16_t>(f32_to_bf16(finalize_val(acc[e], inv))) : 0;
   if (lse != nullptr && lane == 0) lse[(int64_t)b * Hq + head] = C > 0 ? finalize_lse(m, l) : -INFINITY;
 }
 

@@ -17,16 +17,19 @@
 // order with a lazily raised reference max m (log2 units): for sub-block s and
 // one query column, with c = scale * log2(e) and S_j = q . k_j (masked: -inf),
 //   mx    = c * max_j S_j                            (= max_j of c S_j: rounding is monotone)
-//   if mx > m + 8:  alpha = (m == -inf ? 1 : 2^(m - mx)),  m = mx   (else alpha = 1)
+//   if mx > m + 8:  alpha = (m == m0 ? 1 : 2^(m - mx)),  m = mx   (else alpha = 1)
 //   l     = l * alpha,  o = o * alpha
-//   p_j   = 2^(fma(S_j, c, -m'))                     (m' = m, or 0 while m = -inf)
+//   p_j   = 2^(fma(S_j, c, -m))
 //   l     = l + sum_j p_j                            (per lane, see below)
 //   o     = o + sum_j bf16(p_j) v_j                  (one MFMA per 16 head dims)
-// starting from (m, l, o) = (-inf, 0, 0).  Any reference gives the same
+// starting from (m, l, o) = (m0, 0, 0), m0 = -FLT_MAX: no score is visible
+// yet.  The first visible score always moves m (any finite mx > m0 + 8 = m0),
+// so a p is only ever taken against a real score's reference; masked scores
+// are -inf and give p = 2^-inf = 0 whatever m is.  Any reference gives the same
 // softmax in exact arithmetic; raising it only when a score passes it by more
 // than 2^8 keeps every p_j <= 256 (far inside fp32 and bf16 range) while the
 // rescale of o, the costly part of an online softmax, almost never runs.
-// While m = -inf every p so far was 0, so l and o are zeros and alpha = 1
+// While m = m0 every p so far was 0, so l and o are zeros and alpha = 1
 // leaves them as they are.  A sub-block with no key visible to a column leaves
 // that column's (m, l, o) bit-identical (alpha = 1, p = 0), so a kernel may
 // skip sub-blocks that no column of its wave can see.  Each lane keeps its
@@ -52,14 +55,15 @@ constexpr int kChunk = 256;   // fixed split size in tokens
 constexpr int kSub = 32;      // keys per sub-block
 constexpr int kSubs = kChunk / kSub;
 constexpr float kRefSlack = 8.0f;   // log2 units a score may pass the reference max by
+constexpr float kRefNone = -3.402823466e38f;   // the reference before any visible score (-FLT_MAX)
 
 // Key (relative to the sub-block) of MFMA row m' of S^T block b.
 __device__ __forceinline__ int sub_key_of_row(int mr, int b) { return 8 * (mr >> 2) + 4 * b + (mr & 3); }
 
 template <int D, int NB>
 struct ChunkAcc {
-  float m[NB];             // reference max (log2 units), -inf before the first visible key
-  float nm[NB];            // -m, or 0 while m = -inf (the exponent offset)
+  float m[NB];             // reference max (log2 units), kRefNone before the first visible key
+  float thr[NB];           // m + kRefSlack
   float l[NB];             // this lane's part of the running sum of 2^(c S - m)
   f32x4_t o[NB][D / 16];   // lane: column n = lane % 16, head dims 16 dt + 4 g + i
 };
@@ -68,8 +72,8 @@ template <int D, int NB>
 __device__ __forceinline__ void chunk_init(ChunkAcc<D, NB>& a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    a.m[nb] = -INFINITY;
-    a.nm[nb] = 0.0f;
+    a.m[nb] = kRefNone;
+    a.thr[nb] = kRefNone + kRefSlack;
     a.l[nb] = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) a.o[nb][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -119,24 +123,33 @@ __device__ __forceinline__ void sub_mask(f32x4_t (&S)[NB][2], const int (&n_vali
   }
 }
 
+// Max of three scores with v_max3_f32.  Scores are MFMA results or -inf and
+// never NaN; fmaxf would first quiet each (possibly signalling) MFMA result.
+__device__ __forceinline__ float max3_score(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // The column max needs the other lane groups only when some lane's own keys
 // pass the reference by more than the slack; otherwise no column of the
 // wavefront moves and the exchange is skipped.  A column that moves has its l
-// and o multiplied by alpha = 2^(m_old - m_new) (alpha = 1 while m_old = -inf:
-// l and o are zeros then); the others keep theirs, as alpha = 1 would.
+// and o multiplied by alpha = 2^(m_old - m_new) (alpha = 1 while m_old =
+// kRefNone: l and o are zeros then); the others keep theirs, as alpha = 1 would.
 template <int D, int NB>
 __device__ __forceinline__ void sub_reference(ChunkAcc<D, NB>& a, const f32x4_t (&S)[NB][2], float scale_log2) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    float mx = S[nb][0][0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, S[nb][j >> 2][j & 3]);
-    if (__any(mx * scale_log2 > a.m[nb] + kRefSlack)) {
+    float mx = max3_score(S[nb][0][0], S[nb][0][1], S[nb][0][2]);
+    mx = max3_score(mx, S[nb][0][3], S[nb][1][0]);
+    mx = max3_score(mx, S[nb][1][1], S[nb][1][2]);
+    mx = max3_score(mx, S[nb][1][3], S[nb][1][3]);
+    if (__any(mx * scale_log2 > a.thr[nb])) {
       const float cm = max_xor32(max_xor16(mx)) * scale_log2;
-      if (cm > a.m[nb] + kRefSlack) {
-        const float alpha = a.m[nb] == -INFINITY ? 1.0f : exp2_hw(a.m[nb] - cm);
+      if (cm > a.thr[nb]) {
+        const float alpha = a.m[nb] == kRefNone ? 1.0f : exp2_hw(a.m[nb] - cm);
         a.m[nb] = cm;
-        a.nm[nb] = -cm;
+        a.thr[nb] = cm + kRefSlack;
         a.l[nb] = a.l[nb] * alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
@@ -155,7 +168,7 @@ __device__ __forceinline__ void sub_probs(ChunkAcc<D, NB>& a, const f32x4_t (&S)
   for (int nb = 0; nb < NB; ++nb) {
     float p[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = exp2_hw(fmaf(S[nb][j >> 2][j & 3], scale_log2, a.nm[nb]));
+    for (int j = 0; j < 8; ++j) p[j] = exp2_hw(fmaf(S[nb][j >> 2][j & 3], scale_log2, -a.m[nb]));
     float l = a.l[nb];
 #pragma unroll
     for (int j = 0; j < 8; ++j) l = l + p[j];
@@ -215,9 +228,11 @@ __device__ __forceinline__ float merge_val_unit(float acc, float accc, const Mer
   return fmaf(accc, k.beta, acc);
 }
 
-// Final normalisation; +0.0f turns a -0 into +0 so that a zero result has one
+// Final normalisation: one correctly rounded reciprocal per row, then a
+// product per element; +0.0f turns a -0 into +0 so that a zero result has one
 // bit pattern whichever keys contributed exact zeros.
-__device__ __forceinline__ float finalize_val(float acc, float l) { return acc / l + 0.0f; }
+__device__ __forceinline__ float finalize_inv(float l) { return 1.0f / l; }
+__device__ __forceinline__ float finalize_val(float acc, float inv_l) { return acc * inv_l + 0.0f; }
 __device__ __forceinline__ float finalize_lse(float m, float l) { return (m + log2_hw(l)) * kLn2; }
 
 // Page ids of one chunk, one per lane: lane l holds logical page

@@ -265,12 +265,13 @@ __global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(
   if constexpr (kFold) {
     if (row_ok) {
       uint16_t* op = out + ((int64_t)b * Hq + h * G + n) * D + 4 * g;
+      const float inv = finalize_inv(l_run);
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         const f32x4_t a = o_run[dt][lane];
         *reinterpret_cast<u32x2_t*>(op + 16 * dt) =
-            u32x2_t{pack_bf16x2(finalize_val(a[0], l_run), finalize_val(a[1], l_run)),
-                    pack_bf16x2(finalize_val(a[2], l_run), finalize_val(a[3], l_run))};
+            u32x2_t{pack_bf16x2(finalize_val(a[0], inv), finalize_val(a[1], inv)),
+                    pack_bf16x2(finalize_val(a[2], inv), finalize_val(a[3], inv))};
       }
       if (lse != nullptr && g == 0) lse[(int64_t)b * Hq + h * G + n] = finalize_lse(m_run, l_run);
     }
@@ -299,8 +300,9 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
   }
   uint16_t* op = out + ((int64_t)b * Hq + head) * D + lane * E;
   if (C > 0) {
+    const float inv = finalize_inv(l);
 #pragma unroll
-    for (int e = 0; e < E; ++e) op[e] = static_cast<uint16_t>(f32_to_bf16(finalize_val(acc[e], l)));
+    for (int e = 0; e < E; ++e) op[e] = static_cast<uint16_t>(f32_to_bf16(finalize_val(acc[e], inv)));
     if (lse != nullptr && lane == 0) lse[(int64_t)b * Hq + head] = finalize_lse(m, l);
   } else {
 #pragma unroll

@@ -14,15 +14,16 @@
 // it with the same merge step as decode, so row p is bitwise what decode
 // returns at seq_len p + 1.
 //
-// K/V sub-blocks travel from HBM straight into a four-stage LDS ring (buffer
-// loads that write LDS, no register staging), three sub-blocks ahead of the
-// one being computed.  Each 1 KB load lies inside one 16-token tile, so one
-// scalar buffer resource per load covers it; a tile whose page is missing,
-// past the block table or wholly past the last visible key gets an empty
-// resource and lands as zeros.  Keys of a valid page past the last visible key
-// are masked where they are used (scores of such keys are never visible; their
-// V entries are zeroed on the one sub-block that straddles the limit).  Block-
-// table entries are read one chunk ahead.
+// K and V sub-blocks travel from HBM straight into LDS (buffer loads that
+// write LDS, no register staging): K one sub-block ahead of the scores that
+// use it, V one ahead of the values.  Each 1 KB load lies inside one 16-token
+// tile, so one scalar buffer resource per load covers it; a tile whose page is
+// missing, past the block table or wholly past the last visible key gets an
+// empty resource and lands as zeros.  Keys of a valid page past the last
+// visible key are masked where they are used (scores of such keys are never
+// visible; their V entries are zeroed in LDS on the one sub-block that
+// straddles the limit).  Tile indices come from a per-chunk table built one
+// chunk ahead.
 #include "attn_chunk.hpp"
 #include "kv_layout.hpp"
 #include "launch.hpp"
@@ -256,6 +257,18 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
     wait_vmem_then_barrier<0>();
     issue(kc, u + 2, ((u + 2) >> 3) == c ? cur_tab : next_tab, sk_wr);
     issue(vc, u + 1, ((u + 1) >> 3) == c ? cur_tab : next_tab, sv_wr);
+    // The sub-block holding the limit (the workgroup's last): V entries of keys
+    // >= lim may hold stale data (even NaN); they are zeroed in LDS, once, so
+    // that their p = 0 adds exact zeros.  Keeping this test at the top keeps
+    // the rest of the step one branch-free stretch.
+    if ((u + 1) * kSub > lim) {
+      const int kv0 = lim - u * kSub;   // first stale key of the sub-block, 1 .. 31
+      for (int i = tid; i < (kSub - kv0) * D; i += kThreads) {
+        const int k = kv0 + i / D, d = i % D;
+        sv_rd[(k >> 4) * TS + v_tile_off(k & 15, d)] = 0;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
 
     f32x4_t Sn[kNB][2];
     scores(sk_rd, Sn);
@@ -264,12 +277,6 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
     u32x4_t vf[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) vf[dt] = *reinterpret_cast<const u32x4_t*>(&sv_rd[vofs + dt * 256]);
-    // The sub-block holding the limit: V of keys >= lim may be stale.
-    if ((u + 1) * kSub > lim) {
-      const KeepMask km = keep_mask(lim - (u * kSub + 8 * g));
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) vf[dt] = apply_keep(vf[dt], km);
-    }
     sub_values<D, kNB>(ca, vf, pb);
 
     // Chunk end: fold the chunk into the running state, start the next one.
@@ -331,12 +338,13 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
     const int rho = wrow0 + 16 * nb + n;
     const int tok = rho / G, hh = rho - tok * G;
     uint16_t* op = out + ((int64_t)(qs + tok) * Hq + h * G + hh) * D + 4 * g;
+    const float inv = finalize_inv(l_run[nb]);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const f32x4_t a = fold_get(nb, dt);
       *reinterpret_cast<u32x2_t*>(op + 16 * dt) =
-          u32x2_t{pack_bf16x2(finalize_val(a[0], l_run[nb]), finalize_val(a[1], l_run[nb])),
-                  pack_bf16x2(finalize_val(a[2], l_run[nb]), finalize_val(a[3], l_run[nb]))};
+          u32x2_t{pack_bf16x2(finalize_val(a[0], inv), finalize_val(a[1], inv)),
+                  pack_bf16x2(finalize_val(a[2], inv), finalize_val(a[3], inv))};
     }
     if (lse != nullptr && g == 0) lse[(int64_t)(qs + tok) * Hq + h * G + hh] = finalize_lse(m_run[nb], l_run[nb]);
   }
