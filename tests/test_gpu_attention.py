@@ -347,6 +347,84 @@ def test_prefill_equals_token_by_token_decode(hq, hkv, d):
         assert_bitwise(out[qs[s] + i], od[0], f"row {i}: prefill vs single decode")
 
 
+def _steep_kv(kind):
+    """K whose dimension 0 carries a steep score pattern against queries with
+    q[0] = 4 (the rest small noise): 'ramp' rises by about 12 log2 units per
+    32-key sub-block; 'spikes' puts isolated keys far above everything before
+    them, inside and across 256-key chunks."""
+    def fn(r, L, hkv, d, base, device="cpu"):
+        k, v = W.request_kv(r, L, hkv, d, base, device=device)
+        k = k.float() * 0.3
+        j = torch.arange(L, device=device, dtype=torch.float32)
+        if kind == "ramp":
+            k[:, :, 0] = 0.75 * j[:, None]
+        else:
+            for pos, h in ((5, 40.0), (77, 60.0), (300, 90.0), (301, 95.0), (700, 140.0), (990, 180.0)):
+                if pos < L:
+                    k[pos, :, 0] += h
+        return k.to(torch.bfloat16), v
+    return fn
+
+
+def _assert_weight_rounding_bound(gpu, q, k, v, scale, ref, what):
+    """Element-wise form of the attention error bound: with w the exact
+    softmax weights (per kv head group, from the oracle's inputs), rounding
+    each p to bf16 (unit roundoff 2^-8: 8 significant bits) moves o_d by at
+    most 2^-8 sum_j w_j |v_jd|, and the bf16 output adds at most 2^-8 |o_d|
+    (a 2 % margin and 1e-6 absolute cover the fp32 sums).  A near-one-hot
+    softmax whose few values cancel can exceed a fixed fraction of the row
+    RMS while still meeting this bound."""
+    hq, hkv = q.shape[0], k.shape[1]
+    G = hq // hkv
+    g = f64(gpu)
+    for h in range(hq):
+        kk, vv = k[:, h // G], v[:, h // G]
+        sc = scale * (kk @ q[h])
+        w = np.exp(sc - sc.max())
+        w /= w.sum()
+        bound = 1.02 * 2.0 ** -8 * (w @ np.abs(vv) + np.abs(ref[h])) + 1e-6
+        err = np.abs(g[h] - ref[h])
+        assert np.all(err <= bound), f"{what} head {h}: error {err.max():.3e} above the bound at {int(np.argmax(err - bound))}"
+
+
+@pytest.mark.parametrize("kind", ["ramp", "spikes"])
+def test_lazy_reference_moves(kind):
+    """Scores that pass the running reference by far more than the slack, on
+    most sub-blocks (ramp) or at isolated keys (spikes), so that every raise of
+    the reference with its rescale of l and o, inside a chunk and in the merge
+    across chunks, runs: prefill against the oracle on sampled rows and
+    bitwise against decode on every row."""
+    prefixes, chunks = [0, 250, 700], [300, 512, 300]
+    log_case(f"lazy reference moves kind={kind}")
+    total = [p + n for p, n in zip(prefixes, chunks)]
+    bt = Batch(range(3), total, 32, 8, 128, W.SEED_MIXED, kv_fn=_steep_kv(kind))
+    qs_ = []
+    for s, n in enumerate(chunks):
+        qq = W.randn_bf16((n, 32, 128), W.SEED_MIXED, "q", 700 + s, device=DEV).float() * 0.3
+        qq[:, :, 0] = 4.0
+        qs_.append(qq.to(torch.bfloat16))
+    q = torch.cat(qs_).contiguous()
+    q_start = torch.tensor([0] + np.cumsum(chunks).tolist(), dtype=torch.int32, device=DEV)
+    ctx = torch.tensor(prefixes, dtype=torch.int32, device=DEV)
+    out, lse = _prefill(bt, q, q_start, ctx, max(chunks))
+    qs = q_start.cpu().tolist()
+    for s, (p, n) in enumerate(zip(prefixes, chunks)):
+        lens = torch.arange(p + 1, p + n + 1, dtype=torch.int32, device=DEV)
+        btab = bt.bt[s:s + 1].repeat(n, 1).contiguous()
+        qd = q[qs[s]:qs[s + 1]].contiguous()
+        od, ld = bi.bi_attn_decode(qd, bt.kc, bt.vc, btab, lens, p + n, bt.scale,
+                                   lse=torch.empty((n, 32), dtype=torch.float32, device=DEV))
+        assert_bitwise(out[qs[s]:qs[s + 1]], od, f"{kind} seq {s}: prefill rows vs decode")
+        assert_bitwise(lse[qs[s]:qs[s + 1]], ld, f"{kind} seq {s}: prefill lse vs decode")
+        k, v = f64(bt.kv[s][0]), f64(bt.kv[s][1])
+        qq = f64(q[qs[s]:qs[s + 1]])
+        for i in sorted({0, 40, n // 2, n - 1}):
+            ro, rl = O.decode_attention(qq[i][None], [k[:p + i + 1]], [v[:p + i + 1]], bt.scale)
+            _assert_weight_rounding_bound(out[qs[s] + i], qq[i], k[:p + i + 1], v[:p + i + 1], bt.scale, ro[0],
+                                          f"{kind} seq {s} row {i}")
+            assert_f32_close(lse[qs[s] + i], rl[0], f"{kind} seq {s} row {i} lse")
+
+
 def test_prefill_co_batch_invariance():
     prefixes, chunks = [300, 900, 0, 4000], [512, 100, 256, 333]
     bt, q, q_start, ctx = _prefill_setup(prefixes, chunks)
