@@ -128,7 +128,7 @@ bi_status bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new, con
 
 /*
  * Workspace for bi_attn_decode: per (sequence, q head, chunk) partial results
- * (max, sum, D accumulators), fp32: num_seqs * num_q_heads * ceil(max_seq_len/256)
+ * (reference max, sum, D accumulators), fp32: num_seqs * num_q_heads * ceil(max_seq_len/256)
  * * (head_dim + 4) * 4 bytes
  * (accumulators, max, sum, 2 pad words per record), rounded up to 256 bytes.
  */
@@ -143,9 +143,12 @@ size_t bi_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
  *   s_j = softmax_scale * <q[b, h], K_b[j, g]>,  j < L_b = seq_lens[b]
  *   out[b, h] = bf16( sum_j softmax(s)_j V_b[j, g] ),  lse[b, h] = log sum_j exp(s_j)
  * The keys are split into fixed 256-token chunks anchored at position 0 (only
- * the last is partial); each chunk yields (max, sum, accumulators) and the
- * chunks are merged in ascending order, starting from (-inf, 0, 0), by a
- * log-sum-exp step.  The chunking depends on nothing but L_b.
+ * the last is partial); each chunk yields (m, sum, accumulators) with the sum
+ * and accumulators taken relative to a reference m that is raised only when a
+ * score passes it by more than 8 in log2 units (so true max - 8 <= m <= true
+ * max), and the chunks are merged in ascending order, starting from
+ * (-inf, 0, 0), by a log-sum-exp step with the same lazy reference.  In exact
+ * arithmetic this is the softmax; the chunking depends on nothing but L_b.
  * q: [num_seqs][num_q_heads][head_dim] bf16, consecutive sequences ld_q
  *   elements apart (ld_q >= Hq * D, ld_q % 8 == 0); out: contiguous
  *   [num_seqs][num_q_heads][head_dim] bf16;
