@@ -57,9 +57,6 @@ constexpr int kSubs = kChunk / kSub;
 constexpr float kRefSlack = 8.0f;   // log2 units a score may pass the reference max by
 constexpr float kRefNone = -3.402823466e38f;   // the reference before any visible score (-FLT_MAX)
 
-// Key (relative to the sub-block) of MFMA row m' of S^T block b.
-__device__ __forceinline__ int sub_key_of_row(int mr, int b) { return 8 * (mr >> 2) + 4 * b + (mr & 3); }
-
 template <int D, int NB>
 struct ChunkAcc {
   float m[NB];             // reference max (log2 units), kRefNone before the first visible key
@@ -267,6 +264,5 @@ __device__ __forceinline__ KeepMask keep_mask(int nv) {
 __device__ __forceinline__ u32x4_t apply_keep(u32x4_t v, const KeepMask& k) {
   return u32x4_t{v[0] & k.w[0], v[1] & k.w[1], v[2] & k.w[2], v[3] & k.w[3]};
 }
-__device__ __forceinline__ u32x4_t keep_first(u32x4_t v, int nv) { return apply_keep(v, keep_mask(nv)); }
 
 }  // namespace bi
