@@ -441,6 +441,67 @@ def test_prefill_co_batch_invariance():
     assert_bitwise(lse[qs[1]:qs[2]], l1, "sequence 1 prefill lse alone vs co-batched")
 
 
+def test_shared_prefix_pages_are_bitwise_transparent():
+    """Prefix caching: requests A and B share the physical pages of a 320-token
+    prefix (20 pages, across the first chunk boundary); C holds B's tokens in
+    pages of its own.  B and C give bitwise the same decode and prefill
+    outputs, and B matches the oracle."""
+    hq, hkv, d, ps = 32, 8, 128, 16
+    P, la, lb = 320, 150, 400
+    npre, na, nb = P // ps, -(-la // ps), -(-lb // ps)
+    nc = npre + nb
+    pool = npre + na + nb + nc + 3
+    perm = torch.randperm(pool, generator=torch.Generator().manual_seed(11)).to(torch.int32)
+    pre, pa = perm[:npre], perm[npre:npre + na]
+    pb, pc = perm[npre + na:npre + na + nb], perm[npre + na + nb:npre + na + nb + nc]
+    pages = [torch.cat([pre, pa]), torch.cat([pre, pb]), pc]
+    mp = max(len(x) for x in pages)
+    bt = torch.full((3, mp), -1, dtype=torch.int32)
+    for i, x in enumerate(pages):
+        bt[i, :len(x)] = x
+    bt = bt.to(DEV)
+
+    def slots(pg, t0, t1):
+        t = torch.arange(t0, t1, dtype=torch.int64)
+        return (pg[(t // ps)].to(torch.int64) * ps + t % ps).to(torch.int32)
+
+    kp, vp = W.request_kv(900, P, hkv, d, W.SEED_MIXED, device=DEV)
+    ka, va = W.request_kv(901, la, hkv, d, W.SEED_MIXED, device=DEV)
+    kb, vb = W.request_kv(902, lb, hkv, d, W.SEED_MIXED, device=DEV)
+    kc, vc = bi.alloc_kv_cache(pool, hkv, d, ps, fill=NAN)
+    k_all = torch.cat([kp, ka, kb, kp, kb]).contiguous()
+    v_all = torch.cat([vp, va, vb, vp, vb]).contiguous()
+    sm = torch.cat([slots(pages[0], 0, P), slots(pages[0], P, P + la), slots(pages[1], P, P + lb),
+                    slots(pages[2], 0, P + lb)]).to(DEV)
+    bi.bi_kv_append(k_all, v_all, sm, kc, vc)
+
+    # decode: B (shared prefix) and C (own pages) with one query, A beside them
+    q = W.randn_bf16((3, hq, d), W.SEED_MIXED, "q", 903, device=DEV)
+    q[2] = q[1]
+    lens = torch.tensor([P + la, P + lb, P + lb], dtype=torch.int32, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    out, lse = bi.bi_attn_decode(q, kc, vc, bt, lens, P + lb, scale,
+                                 lse=torch.empty((3, hq), dtype=torch.float32, device=DEV))
+    assert_bitwise(out[1], out[2], "decode: shared prefix pages vs own pages")
+    assert_bitwise(lse[1], lse[2], "decode lse: shared prefix pages vs own pages")
+    ro, rl = O.decode_attention(f64(q[1:2]), [f64(torch.cat([kp, kb]))], [f64(torch.cat([vp, vb]))], scale)
+    assert_bf16_close(out[1], ro[0], "decode B vs oracle")
+    assert_f32_close(lse[1], rl[0], "decode B lse vs oracle")
+    ra, _ = O.decode_attention(f64(q[0:1]), [f64(torch.cat([kp, ka]))], [f64(torch.cat([vp, va]))], scale)
+    assert_bf16_close(out[0], ra[0], "decode A vs oracle")
+
+    # prefill: the last 200 tokens of B and of C as the chunk, the same queries
+    n = 200
+    qp = W.randn_bf16((n, hq, d), W.SEED_MIXED, "q", 904, device=DEV)
+    qq = torch.cat([qp, qp]).contiguous()
+    q_start = torch.tensor([0, n, 2 * n], dtype=torch.int32, device=DEV)
+    ctx = torch.tensor([P + lb - n, P + lb - n], dtype=torch.int32, device=DEV)
+    op, lp = bi.bi_attn_prefill(qq, q_start, ctx, n, kc, vc, bt[1:].contiguous(), scale,
+                                lse=torch.empty((2 * n, hq), dtype=torch.float32, device=DEV))
+    assert_bitwise(op[:n], op[n:], "prefill: shared prefix pages vs own pages")
+    assert_bitwise(lp[:n], lp[n:], "prefill lse: shared prefix pages vs own pages")
+
+
 # ---------------------------------------------------------------- edges and errors
 
 def test_decode_edges():
