@@ -264,6 +264,30 @@ bi_status bi_lm_head_logprobs(const void* a, int64_t lda, const void* w, int64_t
                               float* lse, int64_t m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
                               bi_stream_t stream);
 
+/*
+ * Greedy sampling from the lm_head without materialising the logits ([BINR]
+ * answers on sampler/trainer agreement: the sampled token and its logprob
+ * must not depend on the batch).
+ *   z[i, j]      = sum_k a[i, k] w[j, k]            (as in bi_lm_head_logprobs)
+ *   token[i]     = the lowest j with z[i, j] = max_j z[i, j]
+ *   logprob[i]   = z[i, token[i]] - lse[i]
+ * The (max, sum of exp) pairs of every 64-column tile are formed and folded
+ * exactly as in bi_lm_head_logprobs, with the column of each maximum carried
+ * along (ties go to the lower index, which makes the choice independent of
+ * the combination order), so logprob[i] is bitwise bi_lm_head_logprobs'
+ * out[i, token[i]].  No [m, n] buffer is read or written.
+ * a, w: as in bi_lm_head_logprobs (n need not be a multiple of 4);
+ * token: [m] int32, 4-byte aligned; logprob: [m] fp32 or NULL;
+ * workspace: device memory of at least bi_lm_head_greedy_workspace_bytes(m, n)
+ *   bytes, 256-byte aligned, owned by the caller; its contents on entry do not
+ *   matter.
+ * Errors: as bi_lm_head_logprobs.  Nothing is written on error.
+ */
+size_t bi_lm_head_greedy_workspace_bytes(int64_t m, int64_t n);
+bi_status bi_lm_head_greedy(const void* a, int64_t lda, const void* w, int64_t ldw, int32_t* token, float* logprob,
+                            int64_t m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
+                            bi_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

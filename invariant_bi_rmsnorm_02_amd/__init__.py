@@ -43,6 +43,9 @@ _SIGNATURES = {
     "bi_lm_head_logprobs_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
     "bi_lm_head_logprobs": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64,
                                      _c_p, _c_size, _c_p]),
+    "bi_lm_head_greedy_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
+    "bi_lm_head_greedy": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_size,
+                                   _c_p]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -357,3 +360,38 @@ def bi_lm_head_logprobs(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Te
         lse.data_ptr() if lse is not None else None, m, n, k, workspace.data_ptr(), workspace.numel(),
         _stream(stream)))
     return out
+
+
+def lm_head_greedy_workspace_bytes(m: int, n: int) -> int:
+    return int(lib().bi_lm_head_greedy_workspace_bytes(m, n))
+
+
+def bi_lm_head_greedy(a: torch.Tensor, w: torch.Tensor, token: Optional[torch.Tensor] = None,
+                      logprob: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None):
+    """token[m] = argmax_n (a @ w.T)[m, n] (lowest index on ties) and its fp32
+    logprob, without writing the logits.  Returns (token, logprob)."""
+    _dev(a, "a", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    m, k = a.shape
+    n, k2 = w.shape
+    if k != k2:
+        raise ValueError("inner dimensions differ")
+    if token is None:
+        token = torch.empty((m,), dtype=torch.int32, device=a.device)
+    _dev(token, "token", torch.int32)
+    if token.shape != (m,) or not token.is_contiguous():
+        raise ValueError("token must be a contiguous [m] tensor")
+    if logprob is not None:
+        _dev(logprob, "logprob", torch.float32)
+        if logprob.shape != (m,) or not logprob.is_contiguous():
+            raise ValueError("logprob must be a contiguous [m] tensor")
+    need = lm_head_greedy_workspace_bytes(m, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=a.device)
+    _dev(workspace, "workspace", torch.uint8)
+    _check("bi_lm_head_greedy", lib().bi_lm_head_greedy(
+        a.data_ptr(), _rows(a, "a"), w.data_ptr(), _rows(w, "w"), token.data_ptr(),
+        logprob.data_ptr() if logprob is not None else None, m, n, k, workspace.data_ptr(), workspace.numel(),
+        _stream(stream)))
+    return token, logprob

@@ -241,4 +241,27 @@ bi_status bi_lm_head_logprobs(const void* a, int64_t lda, const void* w, int64_t
   return from_hip(bi::launch_lm_head_logprobs(a, lda, w, ldw, out, ldo, lse, m, n, k, workspace, as_stream(stream)));
 }
 
+size_t bi_lm_head_greedy_workspace_bytes(int64_t m, int64_t n) {
+  if (m <= 0 || n <= 0) return 0;
+  return bi::lm_head_greedy_workspace_bytes(m, n);
+}
+
+bi_status bi_lm_head_greedy(const void* a, int64_t lda, const void* w, int64_t ldw, int32_t* token, float* logprob,
+                            int64_t m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
+                            bi_stream_t stream) {
+  if (m < 0 || n <= 0 || k <= 0) return BI_ERR_INVALID_ARG;
+  if (m == 0) return BI_OK;
+  if (!a || !w || !token) return BI_ERR_INVALID_ARG;
+  if (k % 32) return BI_ERR_UNSUPPORTED;
+  if (m > (1 << 30) || n > (1 << 30) || k > (1 << 30)) return BI_ERR_UNSUPPORTED;
+  if (lda < k || ldw < k || lda % 8 || ldw % 8) return BI_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(w)) return BI_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(token) & 3u) || (logprob && (reinterpret_cast<uintptr_t>(logprob) & 3u)))
+    return BI_ERR_INVALID_ARG;
+  if (!bi::gemm_supported(lda, ldw, m, n, k) || !bi::lm_head_supported(lda, ldw, k)) return BI_ERR_UNSUPPORTED;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return BI_ERR_WORKSPACE;
+  if (workspace_bytes < bi::lm_head_greedy_workspace_bytes(m, n)) return BI_ERR_WORKSPACE;
+  return from_hip(bi::launch_lm_head_greedy(a, lda, w, ldw, token, logprob, m, n, k, workspace, as_stream(stream)));
+}
+
 }  // extern "C"

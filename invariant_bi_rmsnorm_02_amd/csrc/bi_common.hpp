@@ -52,6 +52,7 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
+__device__ __forceinline__ int shfl_xor(int v, int mask) { return __shfl_xor(v, mask, kWave); }
 
 // Butterfly sum over the lanes of a wavefront.  Partners add the same two
 // values (addition is commutative), so after each step both hold identical

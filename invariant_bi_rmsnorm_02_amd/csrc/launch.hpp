@@ -52,6 +52,10 @@ hipError_t launch_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids,
 
 // lm_head + log_softmax fused into the GEMM epilogue (lm_head.hip).
 size_t lm_head_workspace_bytes(int64_t m, int64_t n);
+size_t lm_head_greedy_workspace_bytes(int64_t m, int64_t n);
+hipError_t launch_lm_head_greedy(const void* a, int64_t lda, const void* w, int64_t ldw, int32_t* token,
+                                 float* logprob, int64_t m, int64_t n, int64_t k, void* workspace,
+                                 hipStream_t stream);
 bool lm_head_supported(int64_t lda, int64_t ldw, int64_t k);
 hipError_t launch_lm_head_logprobs(const void* a, int64_t lda, const void* w, int64_t ldw, float* out, int64_t ldo,
                                    float* lse, int64_t m, int64_t n, int64_t k, void* workspace,

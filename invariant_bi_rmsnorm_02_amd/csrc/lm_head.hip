@@ -21,7 +21,15 @@
 // Every row's result is a function of its own z values only, so it does not
 // depend on the batch.  z is read and written once more (8 bytes per logit)
 // instead of the 12 of a separate log_softmax pass.
+//
+// Greedy sampling (bi_lm_head_greedy) runs the same two kernels with the
+// column index of each maximum carried along (ties to the lower index) and no
+// z written at all: the second kernel folds the same pairs in the same tree,
+// so its lse - and the chosen token's logprob, max - lse - is bitwise what the
+// logprobs path gives for that token.
 #include <algorithm>
+#include <climits>
+#include <type_traits>
 
 #include "gemm_kernel.hpp"
 #include "launch.hpp"
@@ -35,11 +43,12 @@ constexpr int kFinThreads = 1024;
 constexpr int64_t kFinBlocks = 512;    // finalize workgroups aimed at when rows are few
 constexpr int64_t kFinSegsMax = 256;
 
-template <class Cfg>
+template <class Cfg, class Pair>
 __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void lm_head_lse_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
-    float* __restrict__ Z, int64_t ldz, MaxSum* __restrict__ part, int M, int N, int K, int tiles_m, int tiles_n,
+    float* __restrict__ Z, int64_t ldz, Pair* __restrict__ part, int M, int N, int K, int tiles_m, int tiles_n,
     int vec_store) {
+  constexpr bool kArg = std::is_same<Pair, MaxSumArg>::value;
 
   int tile_m, tile_n;
   gemm_map_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
@@ -64,15 +73,17 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void lm_head_lse_kernel(
   gemm_zero<Cfg>(acc);
   gemm_mainloop<Cfg>(op, K, rows_a, acc);
 
-  gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) {
-    gemm_store4_f32(Z + (int64_t)(m0 + m) * ldz + n, v, cnt, vec_store);
-  });
+  if constexpr (!kArg) {
+    gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) {
+      gemm_store4_f32(Z + (int64_t)(m0 + m) * ldz + n, v, cnt, vec_store);
+    });
+  }
 
   // Tile pairs.  Lane (l16, g) of wavefront (wn, wm) holds, for m-block j,
   // row wm * WTM + 16 j + l16 at columns wn * WTN + 16 i + 4 g + e.  The
   // wavefronts exchange them through the ring's first W stage, which the main
   // loop has finished with (it ends with every load landed and a barrier).
-  using Xw = MaxSum[Cfg::WGN][Cfg::WGM][Cfg::MB][16];
+  using Xw = Pair[Cfg::WGN][Cfg::WGM][Cfg::MB][16];
   static_assert(sizeof(Xw) <= Cfg::TN * Cfg::BK * sizeof(uint16_t), "exchange fits the ring stage");
   Xw& xw = *reinterpret_cast<Xw*>(GemmRing<Cfg>::template w<0>());
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -96,7 +107,17 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void lm_head_lse_kernel(
     float s = mx == -INFINITY ? 0.0f : exp2_hw((v[0] - mx) * kLog2e);
 #pragma unroll
     for (int q = 1; q < Cfg::NB * 4; ++q) s = s + (mx == -INFINITY ? 0.0f : exp2_hw((v[q] - mx) * kLog2e));
-    const MaxSum t = combine_xor32(combine_xor16(MaxSum{mx, s}));
+    Pair t;
+    if constexpr (kArg) {
+      // The lane's lowest column holding its maximum (columns rise with q).
+      int ix = INT_MAX;
+#pragma unroll
+      for (int q = Cfg::NB * 4 - 1; q >= 0; --q)
+        if (v[q] == mx && mx != -INFINITY) ix = n0 + wn * Cfg::WTN + 16 * (q >> 2) + 4 * g + (q & 3);
+      t = combine_xor32(combine_xor16(MaxSumArg{mx, s, ix}));
+    } else {
+      t = combine_xor32(combine_xor16(MaxSum{mx, s}));
+    }
     if (g == 0) xw[wn][wm][j][l16] = t;
   }
   __syncthreads();
@@ -105,7 +126,7 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void lm_head_lse_kernel(
     for (int j = 0; j < Cfg::MB; ++j) {
       const int row = wm * Cfg::WTM + 16 * j + l16;
       if (row >= rows_a) continue;
-      MaxSum t = xw[0][wm][j][l16];
+      Pair t = xw[0][wm][j][l16];
 #pragma unroll
       for (int w = 1; w < Cfg::WGN; ++w) t = combine(t, xw[w][wm][j][l16]);
       part[(int64_t)(m0 + row) * tiles_n + tile_n] = t;
@@ -113,23 +134,33 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void lm_head_lse_kernel(
   }
 }
 
+// The row's pairs folded in one fixed tree that depends on tiles_n alone:
+// thread t takes tiles t, t + 1024, ... in order; a butterfly over the
+// wavefront; the 16 wavefront results in ascending order.  Every thread of the
+// workgroup returns the total.
+template <class Pair>
+__device__ __forceinline__ Pair fold_row_pairs(const Pair* __restrict__ pr, int tiles_n, Pair empty) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  Pair acc = empty;
+  for (int t = tid; t < tiles_n; t += kFinThreads) acc = combine(acc, pr[t]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc = combine(acc, shfl_xor_pair(acc, o));
+  __shared__ Pair wpart[kFinThreads / kWave];
+  if (lane == 0) wpart[wave] = acc;
+  __syncthreads();
+  Pair tot = wpart[0];
+#pragma unroll
+  for (int w = 1; w < kFinThreads / kWave; ++w) tot = combine(tot, wpart[w]);
+  return tot;
+}
+
 __global__ __launch_bounds__(kFinThreads) void lse_finalize_kernel(float* __restrict__ Z, int64_t ldz,
                                                                    const MaxSum* __restrict__ part, int tiles_n,
                                                                    int N, int segs, float* __restrict__ lse_out) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x / segs;
   const int seg = blockIdx.x - (int)(row * segs);
-  const MaxSum* pr = part + row * tiles_n;
-  MaxSum acc{-INFINITY, 0.0f};
-  for (int t = tid; t < tiles_n; t += kFinThreads) acc = combine(acc, pr[t]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) acc = combine(acc, MaxSum{shfl_xor(acc.m, o), shfl_xor(acc.s, o)});
-  __shared__ MaxSum wpart[kFinThreads / kWave];
-  if (lane == 0) wpart[wave] = acc;
-  __syncthreads();
-  MaxSum tot = wpart[0];
-#pragma unroll
-  for (int w = 1; w < kFinThreads / kWave; ++w) tot = combine(tot, wpart[w]);
+  const MaxSum tot = fold_row_pairs(part + row * tiles_n, tiles_n, MaxSum{-INFINITY, 0.0f});
   const float lse = lse_of(tot);
   if (lse_out != nullptr && seg == 0 && tid == 0) lse_out[row] = lse;
   f32x4_t* zr = reinterpret_cast<f32x4_t*>(Z + row * ldz);
@@ -139,6 +170,19 @@ __global__ __launch_bounds__(kFinThreads) void lse_finalize_kernel(float* __rest
   for (int i = seg * per + tid; i < hi; i += kFinThreads) {
     const f32x4_t v = zr[i];
     zr[i] = f32x4_t{v[0] - lse, v[1] - lse, v[2] - lse, v[3] - lse};
+  }
+}
+
+// Greedy: the row's token (lowest index of its maximum logit) and that
+// token's logprob, max - lse.
+__global__ __launch_bounds__(kFinThreads) void greedy_finalize_kernel(const MaxSumArg* __restrict__ part,
+                                                                      int tiles_n, int32_t* __restrict__ token,
+                                                                      float* __restrict__ logprob) {
+  const int64_t row = blockIdx.x;
+  const MaxSumArg tot = fold_row_pairs(part + row * tiles_n, tiles_n, MaxSumArg{-INFINITY, 0.0f, INT_MAX});
+  if (threadIdx.x == 0) {
+    token[row] = tot.i;
+    if (logprob != nullptr) logprob[row] = tot.m - lse_of(MaxSum{tot.m, tot.s});
   }
 }
 
@@ -161,7 +205,7 @@ hipError_t launch_lm_head_logprobs(const void* a, int64_t lda, const void* w, in
   const int tiles_m = static_cast<int>((m + LseCfg::TM - 1) / LseCfg::TM);
   const int tiles_n = lse_tiles(n);
   auto* part = static_cast<MaxSum*>(workspace);
-  hipLaunchKernelGGL((lm_head_lse_kernel<LseCfg>), dim3(static_cast<unsigned>(tiles_m * tiles_n)),
+  hipLaunchKernelGGL((lm_head_lse_kernel<LseCfg, MaxSum>), dim3(static_cast<unsigned>(tiles_m * tiles_n)),
                      dim3(LseCfg::kThreads), 0, stream, static_cast<const uint16_t*>(a), lda,
                      static_cast<const uint16_t*>(w), ldw, out, ldo, part, (int)m, (int)n, (int)k, tiles_m, tiles_n,
                      1);
@@ -172,6 +216,30 @@ hipError_t launch_lm_head_logprobs(const void* a, int64_t lda, const void* w, in
                                                                             (n / 4 + kFinThreads - 1) / kFinThreads})));
   hipLaunchKernelGGL(lse_finalize_kernel, dim3(static_cast<unsigned>(m * segs)), dim3(kFinThreads), 0, stream, out,
                      ldo, part, tiles_n, (int)n, segs, lse);
+  return hipGetLastError();
+}
+
+size_t lm_head_greedy_workspace_bytes(int64_t m, int64_t n) {
+  const size_t bytes = static_cast<size_t>(m) * static_cast<size_t>(lse_tiles(n)) * sizeof(MaxSumArg);
+  return (bytes + 255) / 256 * 256;
+}
+
+hipError_t launch_lm_head_greedy(const void* a, int64_t lda, const void* w, int64_t ldw, int32_t* token,
+                                 float* logprob, int64_t m, int64_t n, int64_t k, void* workspace,
+                                 hipStream_t stream) {
+  if (m == 0 || n == 0) return hipSuccess;
+  if (!gemm_offsets_fit<LseCfg>(lda, ldw, k)) return hipErrorInvalidValue;
+  const int tiles_m = static_cast<int>((m + LseCfg::TM - 1) / LseCfg::TM);
+  const int tiles_n = lse_tiles(n);
+  auto* part = static_cast<MaxSumArg*>(workspace);
+  hipLaunchKernelGGL((lm_head_lse_kernel<LseCfg, MaxSumArg>), dim3(static_cast<unsigned>(tiles_m * tiles_n)),
+                     dim3(LseCfg::kThreads), 0, stream, static_cast<const uint16_t*>(a), lda,
+                     static_cast<const uint16_t*>(w), ldw, nullptr, 0, part, (int)m, (int)n, (int)k, tiles_m,
+                     tiles_n, 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(greedy_finalize_kernel, dim3(static_cast<unsigned>(m)), dim3(kFinThreads), 0, stream, part,
+                     tiles_n, token, logprob);
   return hipGetLastError();
 }
 

@@ -76,6 +76,16 @@ def test_host_validation_without_gpu(lib):
     assert lmh(2, 1024, 64, 1024, W256, 16) == bi.BI_ERR_WORKSPACE
     assert lmh(2, 1024, 64, 1022, W256, 1 << 30) == bi.BI_ERR_INVALID_ARG
     assert lmh(0, 1024, 64, 1024, None, 0) == bi.BI_OK
+    # greedy lm_head: k % 32, misaligned token, short or missing or misaligned workspace, empty batch
+    T4 = ctypes.c_void_p(64)
+    gr = lambda m, n, k, tok, ws, nbytes: lib.bi_lm_head_greedy(P, k, P, k, tok, None, m, n, k, ws, nbytes, None)
+    assert gr(2, 1026, 48, T4, W256, 1 << 30) == bi.BI_ERR_UNSUPPORTED
+    assert gr(2, 1026, 64, ctypes.c_void_p(66), W256, 1 << 30) == bi.BI_ERR_INVALID_ARG
+    assert gr(2, 1026, 64, None, W256, 1 << 30) == bi.BI_ERR_INVALID_ARG
+    assert gr(2, 1026, 64, T4, None, 1 << 30) == bi.BI_ERR_WORKSPACE
+    assert gr(2, 1026, 64, T4, ctypes.c_void_p(272), 1 << 30) == bi.BI_ERR_WORKSPACE
+    assert gr(2, 1026, 64, T4, W256, 16) == bi.BI_ERR_WORKSPACE
+    assert gr(0, 1026, 64, None, None, 0) == bi.BI_OK
     assert lib.bi_kv_append(P, P, 640, P, 3, P, P, 4, 8, 80, 16, None) == bi.BI_ERR_UNSUPPORTED
     assert lib.bi_kv_append(P, P, 1000, P, 3, P, P, 4, 8, 128, 16, None) == bi.BI_ERR_INVALID_ARG
 
@@ -89,6 +99,9 @@ def test_workspace_size_formula(lib):
     # one (max, sum) pair of fp32 per (row, 64-column tile), rounded to 256 bytes
     assert bi.lm_head_logprobs_workspace_bytes(2048, 151936) == 2048 * 2374 * 8
     assert bi.lm_head_logprobs_workspace_bytes(3, 100) == 256
+    # greedy: (max, sum, index) of 12 bytes per (row, 64-column tile), rounded to 256 bytes
+    assert bi.lm_head_greedy_workspace_bytes(2048, 151936) == (2048 * 2374 * 12 + 255) // 256 * 256
+    assert bi.lm_head_greedy_workspace_bytes(3, 100) == 256
 
 
 def test_adaptive_library_exports_its_header():

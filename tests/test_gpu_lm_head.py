@@ -112,3 +112,74 @@ def test_lm_head_logprobs_workspace_reuse_and_errors():
         bi.bi_lm_head_logprobs(a_small, w, out=out, workspace=ws[:64])
     assert e.value.status == bi.BI_ERR_WORKSPACE
     assert bool((out == 7.0).all()), "nothing written on error"
+
+
+# ---------------------------------------------------------------- greedy sampling
+
+@pytest.mark.parametrize("m,n,k", [(1, 1024, 256), (3, 2053, 256), (70, 2052, 512), (5, V // 8, K), (1, V, K)])
+def test_lm_head_greedy_parity(m, n, k):
+    """The token is the argmax (lowest index on ties) of the library's own fp32
+    logits - the decision taken in the kernel's precision - and its logprob is
+    bitwise the logprobs path's value at that token; where the oracle's top two
+    logits are clearly apart its argmax agrees too."""
+    log_case(f"lm_head greedy parity m={m} n={n} k={k}")
+    a = W.rows_for_requests(range(m), k, W.SEED_MOE, device=DEV)
+    w = _weights(n, k)
+    tok, lp = bi.bi_lm_head_greedy(a, w, logprob=torch.empty(m, dtype=torch.float32, device=DEV))
+    z = bi.bi_gemm(a, w, out_dtype=torch.float32).cpu().numpy()
+    assert tok.cpu().numpy().tolist() == np.argmax(z, axis=1).tolist(), "token = argmax of the fp32 logits"
+    if n % 4 == 0:
+        full = bi.bi_lm_head_logprobs(a, w)
+        picked = full[torch.arange(m, device=DEV), tok.long()]
+        assert_bitwise(lp, picked, "greedy logprob vs logprobs path at the token")
+    zo = O.gemm(f64(a), f64(w))
+    top2 = np.sort(zo, axis=1)[:, -2:]
+    clear = (top2[:, 1] - top2[:, 0]) > 1e-3
+    ref_tok = np.argmax(zo, axis=1)
+    assert (tok.cpu().numpy()[clear] == ref_tok[clear]).all(), "oracle argmax where the top two are apart"
+    ref_lp = O.log_softmax(zo)[np.arange(m), tok.cpu().numpy()]
+    assert_f32_close(lp, ref_lp, "greedy logprob vs oracle")
+
+
+def test_lm_head_greedy_ties_and_closed_forms():
+    # equal logits at columns 5, 700 and 1500 (identical weight rows), larger than the rest: the lowest wins
+    a = torch.zeros((2, 256), dtype=torch.bfloat16, device=DEV)
+    a[:, 0] = 1.0
+    w = _weights(2048, 256) * 0.5
+    for j in (1500, 700, 5):
+        w[j] = 0.0
+        w[j, 0] = 3.0
+    tok, lp = bi.bi_lm_head_greedy(a, w, logprob=torch.empty(2, dtype=torch.float32, device=DEV))
+    assert tok.tolist() == [5, 5]
+    # all logits equal (zero weights): token 0, logprob -ln n
+    wz = torch.zeros((4100, 256), dtype=torch.bfloat16, device=DEV)
+    tok, lp = bi.bi_lm_head_greedy(a, wz, logprob=torch.empty(2, dtype=torch.float32, device=DEV))
+    assert tok.tolist() == [0, 0]
+    assert_f32_close(lp, np.full(2, -math.log(4100)), "zero weights: logprob = -ln n")
+    # the maximum in the ragged last tile
+    w2 = _weights(2053, 256) * 0.5
+    w2[2052] = 0.0
+    w2[2052, 0] = 3.0
+    assert bi.bi_lm_head_greedy(a, w2)[0].tolist() == [2052, 2052]
+
+
+def test_lm_head_greedy_batch_invariance_and_workspace():
+    n = V // 8
+    w = _weights(n)
+    ref = None
+    ws = torch.full((bi.lm_head_greedy_workspace_bytes(512, n),), 0x7f, dtype=torch.uint8, device=DEV)
+    for T in (1, 64, 512):
+        for pos in sorted({0, T // 3, T - 1}):
+            ids = list(range(1, T))
+            ids.insert(pos, 0)
+            a = W.rows_for_requests(ids, K, W.SEED_MOE, device=DEV)
+            tok, lp = bi.bi_lm_head_greedy(a, w, logprob=torch.empty(T, dtype=torch.float32, device=DEV),
+                                          workspace=ws)
+            got = (int(tok[pos]), lp[pos].clone())
+            if ref is None:
+                ref = got
+            assert got[0] == ref[0], f"token of request 0 at T={T} slot={pos}"
+            assert_bitwise(got[1], ref[1], f"logprob of request 0 at T={T} slot={pos}")
+    with pytest.raises(bi.BiError) as e:
+        bi.bi_lm_head_greedy(W.rows_for_requests(range(4), K, W.SEED_MOE, device=DEV), w, workspace=ws[:64])
+    assert e.value.status == bi.BI_ERR_WORKSPACE
