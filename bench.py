@@ -17,7 +17,8 @@ events on the launch stream; at B=256 it is a single kernel, below the
 1024 (sequence, kv head) threshold a chunk kernel plus a merge kernel).
 `kernels` holds per-kernel times at every workload shape (B = 1..256,
 the M ~ 2300 GEMMs and chunked prefill of the mixed batch, the 235B-shaped
-lm_head + log_softmax (two calls and fused) and decode attention) as GB/s or
+lm_head + log_softmax (two calls and fused), greedy token + logprob from the
+lm_head, and decode attention) as GB/s or
 TFLOP/s and fraction of roofline.  `cpu_baseline` times the fp64 oracle on the host on a sample of
 the same step.
 """
@@ -351,7 +352,16 @@ def kernel_table(torch, bi, W, step, reps, everything):
         us = time_fn(torch, lambda i=0: bi.bi_lm_head_logprobs(ht, wl, out=lp, workspace=lws), max(5, reps // 4))
         out.append(entry("lm_head+log_softmax fused 4096->151936 fp32", us, bytes_gemm(T, V, 4096, 4),
                          flops_gemm(T, V, 4096), extra={"T": T}))
-        del ht, z, lp, lws
+        # Greedy sampling (bi_lm_head_greedy): the token and its logprob, no logits
+        # written; algorithmic work is the operands read plus 8 bytes per row.
+        gws = torch.empty((bi.lm_head_greedy_workspace_bytes(T, V),), dtype=torch.uint8, device=dev)
+        tok = torch.empty((T,), dtype=torch.int32, device=dev)
+        tlp = torch.empty((T,), dtype=torch.float32, device=dev)
+        us = time_fn(torch, lambda i=0: bi.bi_lm_head_greedy(ht, wl, token=tok, logprob=tlp, workspace=gws),
+                     max(5, reps // 4))
+        out.append(entry("lm_head greedy token+logprob 4096->151936", us, 2 * (T * 4096 + V * 4096) + 8 * T,
+                         flops_gemm(T, V, 4096), extra={"T": T}))
+        del ht, z, lp, lws, gws, tok, tlp
     del wl
     torch.cuda.empty_cache()
     # Routed experts: 128 experts, top-8, 4096->1536->4096.  Each timed launch
