@@ -19,7 +19,8 @@ events on the launch stream; at B=256 it is a single kernel, below the
 the M ~ 2300 GEMMs and chunked prefill of the mixed batch, the 235B-shaped
 lm_head + log_softmax (two calls and fused), greedy token + logprob from the
 lm_head, and decode attention) as GB/s or
-TFLOP/s and fraction of roofline.  `cpu_baseline` times the fp64 oracle on the host on a sample of
+TFLOP/s and fraction of roofline, plus a whole Qwen3-8B-shaped decoder layer
+(O projection, residual adds and gated MLP included) at B = 1, 64, 256.  `cpu_baseline` times the fp64 oracle on the host on a sample of
 the same step.
 """
 from __future__ import annotations
@@ -406,6 +407,49 @@ def kernel_table(torch, bi, W, step, reps, everything):
     return out
 
 
+# ---------------------------------------------------------------- whole decoder layer
+
+def bytes_layer(B, lens, h=4096, hq=32, hkv=8, d=128, f=12288):
+    """Algorithmic bytes of one decode-layer call: each step's own operands."""
+    qkv = (hq + 2 * hkv) * d
+    return (2 * bytes_rmsnorm(B, h) + bytes_gemm(B, qkv, h) + bytes_append(B, hkv, d)
+            + bytes_decode(lens, hq, hkv, d) + bytes_gemm(B, h, hq * d) + bytes_gemm(B, 2 * f, h)
+            + 6 * B * f + bytes_gemm(B, h, f) + 2 * 6 * B * h)
+
+
+def layer_table(torch, bi, W, step, reps):
+    """A whole Qwen3-8B-shaped decoder layer (invariant_bi_rmsnorm_02_amd.layer:
+    QKV, attention, O projection + residual, gated MLP + residual) decoding
+    the first B requests of the step's caches, and its two pointwise kernels."""
+    from invariant_bi_rmsnorm_02_amd.layer import DecoderLayer
+    dev, base = "cuda", W.SEED_DECODE
+    w_o = W.randn_bf16((4096, 4096), base, "w", W.WEIGHTS + 4, std=0.02, device=dev)
+    w_gu = W.randn_bf16((2 * 12288, 4096), base, "w", W.WEIGHTS + 5, std=0.02, device=dev)
+    layer = DecoderLayer(step.w_qkv, w_o, w_gu, step.w_down, step.g1, step.g2, 32, 8, 128, EPS)
+    out = []
+    for B in (1, 64, 256):
+        if B > step.B:
+            continue
+        x, bt, lt, slots = step.x[:B], step.bt[:B], step.lens_t[:B], step.new_slots[:B]
+        us = time_fn(torch, lambda i=0: layer.decode(x, step.kc, step.vc, bt, lt, slots, step.max_len,
+                                                     workspace=step.ws), max(10, reps // 2))
+        e = entry("decoder layer decode (Qwen3-8B, 12 launches)", us, bytes_layer(B, step.lens[:B]),
+                  extra={"B": B, "sum_L": sum(step.lens[:B])})
+        e["tokens_per_s_per_layer"] = round(B / (us[0] * 1e-6), 1)
+        out.append(e)
+    B = step.B
+    gu = W.rows_for_requests(range(B), 2 * 12288, base, device=dev)
+    m = torch.empty((B, 12288), dtype=torch.bfloat16, device=dev)
+    us = time_fn(torch, lambda i=0: bi.bi_silu_mul(gu, out=m), reps)
+    out.append(entry("silu_mul [B,2x12288]", us, 6 * B * 12288, extra={"B": B}))
+    y = torch.empty_like(step.x)
+    us = time_fn(torch, lambda i=0: bi.bi_add(step.x, step.h, out=y), reps)
+    out.append(entry("add [B,4096]", us, 6 * B * 4096, extra={"B": B}))
+    del layer, w_o, w_gu, gu, m, y
+    torch.cuda.empty_cache()
+    return out
+
+
 # ---------------------------------------------------------------- cost of invariance
 
 def cost_of_invariance(torch, bi, step, reps):
@@ -552,6 +596,8 @@ ONLY = {
     "prefill-4x512": "chunked prefill, 4 x 512 tokens over the seeded prefixes, 32/8 heads, D=128",
     "rmsnorm-2300": "RMSNorm [2300, 4096]",
     "lm-head-t2048": "fused lm_head + log_softmax, T=2048, vocab 151936",
+    "layer-decode-b1": "Qwen3-8B-shaped decoder layer, decode of 1 request",
+    "layer-decode-b256": "Qwen3-8B-shaped decoder layer, decode of 256 requests (the decode-step caches)",
 }
 
 
@@ -579,6 +625,14 @@ def run_only(torch, bi, W, what, reps):
         ctx = torch.tensor(prefixes, dtype=torch.int32, device=dev)
         btp = pb.block_table.to(dev)
         fn = lambda: bi.bi_attn_prefill(qp, qs, ctx, 512, kc, vc, btp, 1 / math.sqrt(128), out=op)
+    elif what.startswith("layer-decode"):
+        from invariant_bi_rmsnorm_02_amd.layer import DecoderLayer
+        step = DecodeStep(torch, bi, W, int(what.rsplit("b", 1)[1]))
+        w_o = W.randn_bf16((4096, 4096), W.SEED_DECODE, "w", W.WEIGHTS + 4, std=0.02, device=dev)
+        w_gu = W.randn_bf16((2 * 12288, 4096), W.SEED_DECODE, "w", W.WEIGHTS + 5, std=0.02, device=dev)
+        layer = DecoderLayer(step.w_qkv, w_o, w_gu, step.w_down, step.g1, step.g2, 32, 8, 128, EPS)
+        fn = lambda: layer.decode(step.x, step.kc, step.vc, step.bt, step.lens_t, step.new_slots, step.max_len,
+                                  workspace=step.ws)
     elif what == "rmsnorm-2300":
         x = W.rows_for_requests(range(2300), 4096, W.SEED_MIXED, device=dev)
         g = W.randn_bf16((4096,), W.SEED_MIXED, "gamma", W.WEIGHTS, std=0.1, mean=1.0, device=dev)
@@ -670,6 +724,8 @@ def main():
     if args.kernels != "none":
         print("[bench] per-kernel table", file=sys.stderr, flush=True)
         result["kernels"] = kernel_table(torch, bi, W, step, args.reps, args.kernels == "all")
+        print("[bench] decoder layer", file=sys.stderr, flush=True)
+        result["kernels"] += layer_table(torch, bi, W, step, args.reps)
         print("[bench] cost of invariance", file=sys.stderr, flush=True)
         result["cost_of_invariance"] = cost_of_invariance(torch, bi, step, args.reps)
     if not args.no_cpu_baseline:

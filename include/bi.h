@@ -288,6 +288,29 @@ bi_status bi_lm_head_greedy(const void* a, int64_t lda, const void* w, int64_t l
                             int64_t m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
                             bi_stream_t stream);
 
+/*
+ * Elementwise steps of a decoder layer ([TML] section "1. Batch-Invariant
+ * RMSNorm" context: only reductions need a batch-independent order; these have
+ * none).  Every output element depends on its own input elements only.
+ *   bi_add:      out[i, j] = bf16(x[i, j] + y[i, j])   (the residual add; the fp32
+ *                sum of two bf16 is exact unless their exponents differ by more
+ *                than 16, and then it is far from a bf16 rounding midpoint, so
+ *                the result is the correctly rounded exact sum)
+ *   bi_silu_mul: out[i, j] = bf16(silu(g) * u), g = gate_up[i, j],
+ *                u = gate_up[i, f + j], silu(g) = g / (1 + e^-g), in fp32 with one
+ *                rounding (the gated MLP on a fused gate/up projection [T, 2f])
+ * All tensors bf16, rows strided (ld* elements, multiples of 8, >= the row's
+ * width), 16-byte aligned; cols and f multiples of 8.  bi_add's out may be x or
+ * y itself (in place); other overlaps are not allowed.
+ * Errors: BI_ERR_INVALID_ARG (pointers, strides, alignment), BI_ERR_UNSUPPORTED
+ * (widths not a multiple of 8, rows or widths beyond 2^30, more than 2^34
+ * output elements).  Nothing is written on error.
+ */
+bi_status bi_add(const void* x, int64_t ldx, const void* y, int64_t ldy, void* out, int64_t ldo, int64_t rows,
+                 int64_t cols, bi_stream_t stream);
+bi_status bi_silu_mul(const void* gate_up, int64_t ld_gu, void* out, int64_t ldo, int64_t rows, int64_t f,
+                      bi_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,8 @@ _SIGNATURES = {
     "bi_lm_head_greedy_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
     "bi_lm_head_greedy": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_size,
                                    _c_p]),
+    "bi_add": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
+    "bi_silu_mul": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -395,3 +397,36 @@ def bi_lm_head_greedy(a: torch.Tensor, w: torch.Tensor, token: Optional[torch.Te
         logprob.data_ptr() if logprob is not None else None, m, n, k, workspace.data_ptr(), workspace.numel(),
         _stream(stream)))
     return token, logprob
+
+
+def bi_add(x: torch.Tensor, y: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out = bf16(x + y) elementwise over [rows, cols] (out may be x or y)."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(y, "y", torch.bfloat16)
+    if x.dim() != 2 or x.shape != y.shape:
+        raise ValueError("x and y must be [rows, cols] of one shape")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", torch.bfloat16)
+    if out.shape != x.shape:
+        raise ValueError("out shape")
+    rows, cols = x.shape
+    _check("bi_add", lib().bi_add(x.data_ptr(), _rows(x, "x"), y.data_ptr(), _rows(y, "y"), out.data_ptr(),
+                                  _rows(out, "out"), rows, cols, _stream(stream)))
+    return out
+
+
+def bi_silu_mul(gate_up: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[i, j] = bf16(silu(gate_up[i, j]) * gate_up[i, f + j]), f = gate_up.shape[1] // 2."""
+    _dev(gate_up, "gate_up", torch.bfloat16)
+    if gate_up.dim() != 2 or gate_up.shape[1] % 2:
+        raise ValueError("gate_up must be [rows, 2f]")
+    rows, f = gate_up.shape[0], gate_up.shape[1] // 2
+    if out is None:
+        out = torch.empty((rows, f), dtype=torch.bfloat16, device=gate_up.device)
+    _dev(out, "out", torch.bfloat16)
+    if out.shape != (rows, f):
+        raise ValueError("out shape")
+    _check("bi_silu_mul", lib().bi_silu_mul(gate_up.data_ptr(), _rows(gate_up, "gate_up"), out.data_ptr(),
+                                            _rows(out, "out"), rows, f, _stream(stream)))
+    return out

@@ -264,4 +264,28 @@ bi_status bi_lm_head_greedy(const void* a, int64_t lda, const void* w, int64_t l
   return from_hip(bi::launch_lm_head_greedy(a, lda, w, ldw, token, logprob, m, n, k, workspace, as_stream(stream)));
 }
 
+bi_status bi_add(const void* x, int64_t ldx, const void* y, int64_t ldy, void* out, int64_t ldo, int64_t rows,
+                 int64_t cols, bi_stream_t stream) {
+  if (rows < 0 || cols < 0) return BI_ERR_INVALID_ARG;
+  if (rows == 0 || cols == 0) return BI_OK;
+  if (!x || !y || !out) return BI_ERR_INVALID_ARG;
+  if (cols % 8) return BI_ERR_UNSUPPORTED;
+  if (rows > (1 << 30) || cols > (1 << 30) || rows * (cols / 8) > (int64_t(1) << 31)) return BI_ERR_UNSUPPORTED;
+  if (ldx < cols || ldy < cols || ldo < cols || ldx % 8 || ldy % 8 || ldo % 8) return BI_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(out)) return BI_ERR_INVALID_ARG;
+  return from_hip(bi::launch_add(x, ldx, y, ldy, out, ldo, rows, cols, as_stream(stream)));
+}
+
+bi_status bi_silu_mul(const void* gate_up, int64_t ld_gu, void* out, int64_t ldo, int64_t rows, int64_t f,
+                      bi_stream_t stream) {
+  if (rows < 0 || f < 0) return BI_ERR_INVALID_ARG;
+  if (rows == 0 || f == 0) return BI_OK;
+  if (!gate_up || !out) return BI_ERR_INVALID_ARG;
+  if (f % 8) return BI_ERR_UNSUPPORTED;
+  if (rows > (1 << 30) || f > (1 << 29) || rows * (f / 8) > (int64_t(1) << 31)) return BI_ERR_UNSUPPORTED;
+  if (ld_gu < 2 * f || ldo < f || ld_gu % 8 || ldo % 8) return BI_ERR_INVALID_ARG;
+  if (!aligned16(gate_up) || !aligned16(out)) return BI_ERR_INVALID_ARG;
+  return from_hip(bi::launch_silu_mul(gate_up, ld_gu, out, ldo, rows, f, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -53,6 +53,11 @@ hipError_t launch_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids,
 // lm_head + log_softmax fused into the GEMM epilogue (lm_head.hip).
 size_t lm_head_workspace_bytes(int64_t m, int64_t n);
 size_t lm_head_greedy_workspace_bytes(int64_t m, int64_t n);
+// Elementwise steps of the decoder layer (pointwise.hip).
+hipError_t launch_add(const void* x, int64_t ldx, const void* y, int64_t ldy, void* out, int64_t ldo, int64_t rows,
+                      int64_t cols, hipStream_t stream);
+hipError_t launch_silu_mul(const void* gu, int64_t ldgu, void* out, int64_t ldo, int64_t rows, int64_t f,
+                           hipStream_t stream);
 hipError_t launch_lm_head_greedy(const void* a, int64_t lda, const void* w, int64_t ldw, int32_t* token,
                                  float* logprob, int64_t m, int64_t n, int64_t k, void* workspace,
                                  hipStream_t stream);

@@ -1,0 +1,86 @@
+"""A pre-norm decoder layer (Qwen3-style shapes) composed from the library's
+entry points.  Every step is one C-ABI call on the caller's stream; this module
+only sequences them and slices views (q, k and v are read straight out of the
+fused QKV projection, the gate and up halves out of the fused gate/up one).
+
+    h  = rmsnorm(x, g1)                        bi_rmsnorm
+    qkv = h W_qkv^T                            bi_gemm
+    cache <- k, v                              bi_kv_append
+    a  = attention(q, cache)                   bi_attn_decode / bi_attn_prefill
+    r  = x + a W_o^T                           bi_gemm, bi_add
+    h2 = rmsnorm(r, g2)                        bi_rmsnorm
+    y  = r + (silu(gate) * up) W_down^T        bi_gemm, bi_silu_mul, bi_gemm, bi_add
+
+Each step is batch-invariant on its own (row-wise reductions in a fixed order,
+one GEMM tile and K order, fixed 256-token KV chunks, pointwise work), so a
+token's output does not depend on the batch it is computed in, nor on whether
+it is prefilled or decoded.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import (bi_add, bi_attn_decode, bi_attn_decode_workspace_bytes, bi_attn_prefill, bi_gemm, bi_kv_append,
+               bi_rmsnorm, bi_silu_mul)
+
+
+class DecoderLayer:
+    """Weights (bf16, on the device): w_qkv [(Hq + 2 Hkv) D, H], w_o [H, Hq D],
+    w_gu [2 F, H] (gate rows first, then up), w_down [H, F]; g1, g2 [H]."""
+
+    def __init__(self, w_qkv: torch.Tensor, w_o: torch.Tensor, w_gu: torch.Tensor, w_down: torch.Tensor,
+                 g1: torch.Tensor, g2: torch.Tensor, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 eps: float = 1e-6):
+        self.w_qkv, self.w_o, self.w_gu, self.w_down, self.g1, self.g2 = w_qkv, w_o, w_gu, w_down, g1, g2
+        self.hq, self.hkv, self.d, self.eps = num_q_heads, num_kv_heads, head_dim, eps
+        self.scale = 1.0 / math.sqrt(head_dim)
+        hd = (num_q_heads + 2 * num_kv_heads) * head_dim
+        if w_qkv.shape[0] != hd or w_o.shape != (w_qkv.shape[1], num_q_heads * head_dim):
+            raise ValueError("w_qkv / w_o shapes do not match the head layout")
+        if w_gu.shape[0] % 2 or w_down.shape != (w_qkv.shape[1], w_gu.shape[0] // 2):
+            raise ValueError("w_gu / w_down shapes")
+
+    def _qkv(self, x: torch.Tensor):
+        T = x.shape[0]
+        h = bi_rmsnorm(x, self.g1, self.eps)
+        qkv = bi_gemm(h, self.w_qkv)
+        a, b = self.hq * self.d, (self.hq + self.hkv) * self.d
+        q = qkv[:, :a].view(T, self.hq, self.d)
+        k = qkv[:, a:b].view(T, self.hkv, self.d)
+        v = qkv[:, b:].view(T, self.hkv, self.d)
+        return q, k, v
+
+    def _tail(self, x: torch.Tensor, attn: torch.Tensor) -> torch.Tensor:
+        T = x.shape[0]
+        r = bi_add(x, bi_gemm(attn.view(T, self.hq * self.d), self.w_o))
+        h2 = bi_rmsnorm(r, self.g2, self.eps)
+        m = bi_silu_mul(bi_gemm(h2, self.w_gu))
+        return bi_add(r, bi_gemm(m, self.w_down), out=r)
+
+    def decode(self, x: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+               seq_lens: torch.Tensor, slot_mapping: torch.Tensor, max_seq_len: int,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """x [B, H]: the newest token of each of B sequences; seq_lens count it;
+        slot_mapping [B] is where its K/V goes.  Returns y [B, H]."""
+        q, k, v = self._qkv(x)
+        bi_kv_append(k, v, slot_mapping, k_cache, v_cache)
+        if workspace is None:
+            need = bi_attn_decode_workspace_bytes(x.shape[0], self.hq, self.d, max_seq_len)
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+        attn, _ = bi_attn_decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, self.scale,
+                                 workspace=workspace)
+        return self._tail(x, attn)
+
+    def prefill(self, x: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                q_start: torch.Tensor, ctx_lens: torch.Tensor, slot_mapping: torch.Tensor,
+                max_q_len: int) -> torch.Tensor:
+        """x [T, H]: the new tokens of S sequences back to back (sequence s at
+        rows q_start[s] .. q_start[s+1]-1, positions ctx_lens[s] ...);
+        slot_mapping [T].  Returns y [T, H]."""
+        q, k, v = self._qkv(x)
+        bi_kv_append(k, v, slot_mapping, k_cache, v_cache)
+        attn, _ = bi_attn_prefill(q, q_start, ctx_lens, max_q_len, k_cache, v_cache, block_table, self.scale)
+        return self._tail(x, attn)

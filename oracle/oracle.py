@@ -282,3 +282,55 @@ def moe_ffn(x: np.ndarray, experts: np.ndarray, weights: np.ndarray,
             h = silu(np.asarray(w_up[e], dtype=np.float64) @ x[t])
             y[t] += float(weights[t, s]) * (np.asarray(w_down[e], dtype=np.float64) @ h)
     return y
+
+
+# ---------------------------------------------------------------------------
+# One decoder layer (workload support; the pages describe no layer)
+# ---------------------------------------------------------------------------
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """x rounded to the nearest bfloat16 (ties to even), returned as float64."""
+    return bf16_to_f64(f64_to_bf16_bits(x))
+
+
+def silu_mul(gate_up: np.ndarray) -> np.ndarray:
+    """silu(g) * u for rows of a fused gate/up projection [.., 2F]: g is the first
+    F columns, u the last F.  Reading (no layer is on the pages): the gated MLP
+    of a Qwen3-style decoder layer, down(silu(gate(h)) * up(h))."""
+    gu = np.asarray(gate_up, dtype=np.float64)
+    f = gu.shape[-1] // 2
+    return silu(gu[..., :f]) * gu[..., f:]
+
+
+def decoder_layer(x: np.ndarray, k_prefix: np.ndarray, v_prefix: np.ndarray, weights: dict,
+                  num_q_heads: int, num_kv_heads: int, head_dim: int, eps: float,
+                  scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One pre-norm decoder layer over the T new tokens x [T, H] of one sequence
+    whose cache already holds P tokens (k_prefix, v_prefix [P, Hkv, D]).
+
+    Reading (no layer is on the pages): the step sequence of a Qwen3-style layer,
+        h = rmsnorm(x, g1); q, k, v = h W_qkv^T; a = causal attention of q over
+        the prefix and the new k, v; r = x + a W_o^T; h2 = rmsnorm(r, g2);
+        y = r + (silu(h2 W_gate^T) * h2 W_up^T) W_down^T
+    with W_gu = [W_gate; W_up] stacked along the output dimension.  The layer's
+    activations are bfloat16 tensors, so every step's output is rounded to
+    bfloat16 (ties to even) before the next step reads it; each step itself is
+    the float64 definition above.  Returns y [T, H] and the new k, v [T, Hkv, D].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    P = np.asarray(k_prefix).shape[0]
+    hq, hkv, d = num_q_heads, num_kv_heads, head_dim
+    h = round_bf16(rmsnorm(x, weights["g1"], eps))
+    qkv = round_bf16(gemm(h, weights["w_qkv"]))
+    q = qkv[:, :hq * d].reshape(T, hq, d)
+    k = qkv[:, hq * d:(hq + hkv) * d].reshape(T, hkv, d)
+    v = qkv[:, (hq + hkv) * d:].reshape(T, hkv, d)
+    K = np.concatenate([np.asarray(k_prefix, dtype=np.float64).reshape(P, hkv, d), k])
+    V = np.concatenate([np.asarray(v_prefix, dtype=np.float64).reshape(P, hkv, d), v])
+    a = round_bf16(prefill_attention(q, K, V, P, scale)[0]).reshape(T, hq * d)
+    r = round_bf16(x + round_bf16(gemm(a, weights["w_o"])))
+    h2 = round_bf16(rmsnorm(r, weights["g2"], eps))
+    m = round_bf16(silu_mul(round_bf16(gemm(h2, weights["w_gu"]))))
+    y = round_bf16(r + round_bf16(gemm(m, weights["w_down"])))
+    return y, k, v

@@ -1,0 +1,206 @@
+"""A whole pre-norm decoder layer (invariant_bi_rmsnorm_02_amd.layer) on the GPU:
+parity with the oracle's layer at a reduced shape, and at the Qwen3-8B shape a
+token's layer output - and the K/V it appends - bitwise the same whatever it
+is batched with, and whether its chunk is prefilled in one call or decoded one
+token at a time."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from _helpers import O, assert_bf16_close, assert_bitwise, bi, ensure_lib, f64, log_case
+from invariant_bi_rmsnorm_02_amd.layer import DecoderLayer
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+NAN = float("nan")
+EPS = 1e-6
+SEED = 61
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+
+
+def _layer(H, hq, hkv, d, F, seed=SEED):
+    w = lambda n, k, i: W.randn_bf16((n, k), seed, "w", i, std=0.02, device=DEV)
+    g = lambda i: W.randn_bf16((H,), seed, "gamma", i, std=0.1, mean=1.0, device=DEV)
+    return DecoderLayer(w((hq + 2 * hkv) * d, H, 1), w(H, hq * d, 2), w(2 * F, H, 3), w(H, F, 4), g(5), g(6),
+                        hq, hkv, d, EPS)
+
+
+def _np_weights(layer):
+    return dict(g1=f64(layer.g1), g2=f64(layer.g2), w_qkv=f64(layer.w_qkv), w_o=f64(layer.w_o),
+                w_gu=f64(layer.w_gu), w_down=f64(layer.w_down))
+
+
+class Caches:
+    """Sequences whose caches hold `prefix[s]` earlier tokens (random K/V) and
+    have room for `new[s]` more; unused slots are NaN."""
+
+    def __init__(self, prefix, new, hkv, d, seed, perm_index=0):
+        self.prefix, self.new = list(prefix), list(new)
+        total = [p + n for p, n in zip(prefix, new)]
+        self.pb = W.allocate_pages(total, seed, 16, 3, perm_index)
+        self.kc, self.vc = bi.alloc_kv_cache(self.pb.num_pages, hkv, d, 16, fill=NAN)
+        self.kv = [W.request_kv(900 + s, p, hkv, d, seed, device=DEV) for s, p in enumerate(prefix)]
+        self.bt = self.pb.block_table.to(DEV)
+        starts = np.cumsum([0] + total[:-1]).tolist()
+        self.slots = [self.pb.slot_mapping[st:st + t].to(DEV) for st, t in zip(starts, total)]
+        for s, p in enumerate(prefix):
+            if p:
+                bi.bi_kv_append(self.kv[s][0], self.kv[s][1], self.slots[s][:p], self.kc, self.vc)
+
+
+def _tokens(n, H, seed, tag):
+    return W.randn_bf16((n, H), seed, "x", tag, device=DEV)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 8), (3, 4096), (257, 1032), (0, 64)])
+def test_add_parity(rows, cols):
+    """bf16(x + y): the fp32 sum of two bf16 values rounds to the same bf16 as
+    the exact sum (exact when the exponents differ by at most 16, else far
+    from a rounding midpoint), so the result is bit-exact."""
+    log_case(f"add rows={rows} cols={cols}")
+    x = W.randn_bf16((rows, cols), SEED, "x", 7, device=DEV)
+    y = W.randn_bf16((rows, cols), SEED, "x", 8, std=3e-3, device=DEV)
+    if rows > 2:
+        y[1] = -x[1]                      # exact cancellation to +0
+        y[2, :8] = x[2, :8] * 2.0 ** -20  # far-apart exponents
+    out = bi.bi_add(x, y)
+    torch.cuda.synchronize()
+    want = O.f64_to_bf16_bits(O.round_bf16(f64(x) + f64(y))).view(np.int16)
+    assert np.array_equal(out.view(torch.int16).cpu().numpy(), want.reshape(rows, cols))
+
+
+def test_add_strided_and_in_place():
+    x = W.randn_bf16((40, 3 * 512), SEED, "x", 9, device=DEV)
+    a, b = x[:, :512], x[:, 1024:]
+    want = bi.bi_add(a.contiguous(), b.contiguous())
+    assert_bitwise(bi.bi_add(a, b), want, "strided add")
+    c = a.clone()
+    bi.bi_add(c, b, out=c)
+    assert_bitwise(c, want, "in-place add")
+
+
+@pytest.mark.parametrize("rows,f", [(1, 8), (5, 12288), (129, 1544), (0, 16)])
+def test_silu_mul_parity(rows, f):
+    """silu(g) * u in fp32 with one rounding: within one bf16 ulp of the
+    correctly rounded value, and equal to it for nearly every element."""
+    log_case(f"silu_mul rows={rows} f={f}")
+    gu = W.randn_bf16((rows, 2 * f), SEED, "x", 10, std=2.0, device=DEV)
+    out = bi.bi_silu_mul(gu)
+    torch.cuda.synchronize()
+    ref = O.round_bf16(O.silu_mul(f64(gu)))
+    got = f64(out)
+    if rows == 0:
+        assert got.shape == (0, f)
+        return
+    ulp = np.maximum(np.abs(ref), 2.0 ** -126) * 2.0 ** -7
+    assert np.all(np.abs(got - ref) <= ulp), "silu_mul off by more than one bf16 ulp"
+    assert np.mean(got == ref) >= 0.99, f"silu_mul: only {np.mean(got == ref):.4f} exactly rounded"
+
+
+def test_silu_mul_closed_forms():
+    """silu(0) = 0, silu(g) -> g for large g and -> -0 for very negative g;
+    u = 1 returns silu(g) itself."""
+    g = torch.tensor([0.0, 40.0, -200.0, 1.0, -1.0, 2.0, 3.0, -3.0], dtype=torch.bfloat16, device=DEV)
+    gu = torch.cat([g, torch.ones(8, dtype=torch.bfloat16, device=DEV)]).view(1, 16)
+    got = f64(bi.bi_silu_mul(gu))[0]
+    assert got[0] == 0.0 and got[1] == 40.0 and got[2] == 0.0
+    ref = O.round_bf16(O.silu_mul(f64(gu)))[0]
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -7)
+
+
+def test_pointwise_validation():
+    x = torch.zeros((4, 12), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(RuntimeError):
+        bi.bi_add(x, x)                          # cols not a multiple of 8
+    with pytest.raises(RuntimeError):
+        bi.bi_silu_mul(torch.zeros((4, 24), dtype=torch.bfloat16, device=DEV))   # f = 12
+    with pytest.raises(RuntimeError):
+        bi.bi_add(torch.zeros((4, 16), dtype=torch.bfloat16, device=DEV)[:, 1:9],
+                  torch.zeros((4, 8), dtype=torch.bfloat16, device=DEV))        # misaligned base
+
+
+def test_layer_parity_small():
+    H, hq, hkv, d, F = 1024, 8, 2, 128, 2048
+    layer = _layer(H, hq, hkv, d, F)
+    npw = _np_weights(layer)
+    # decode: three sequences, the new token of each (cache lengths 0, 299, 699 before it)
+    log_case("layer parity: decode")
+    prefix = [0, 299, 699]
+    c = Caches(prefix, [1, 1, 1], hkv, d, SEED)
+    x = _tokens(3, H, SEED, 1)
+    lens = torch.tensor([p + 1 for p in prefix], dtype=torch.int32, device=DEV)
+    slots = torch.stack([c.slots[s][p] for s, p in enumerate(prefix)])
+    y = layer.decode(x, c.kc, c.vc, c.bt, lens, slots, 700)
+    for s, p in enumerate(prefix):
+        ry, _, _ = O.decoder_layer(f64(x[s:s + 1]), f64(c.kv[s][0]), f64(c.kv[s][1]), npw, hq, hkv, d, EPS,
+                                   layer.scale)
+        assert_bf16_close(y[s:s + 1], ry, f"decode layer, sequence {s} (cache {p})", tol=2e-2)
+    # prefill: two sequences' chunks (prefixes 0 and 260, 40 and 100 new tokens)
+    log_case("layer parity: prefill")
+    prefix, new = [0, 260], [40, 100]
+    c = Caches(prefix, new, hkv, d, SEED, perm_index=1)
+    x = _tokens(sum(new), H, SEED, 2)
+    q_start = torch.tensor([0, new[0], sum(new)], dtype=torch.int32, device=DEV)
+    ctx = torch.tensor(prefix, dtype=torch.int32, device=DEV)
+    slots = torch.cat([c.slots[s][p:p + n] for s, (p, n) in enumerate(zip(prefix, new))])
+    y = layer.prefill(x, c.kc, c.vc, c.bt, q_start, ctx, slots, max(new))
+    for s, (p, n) in enumerate(zip(prefix, new)):
+        rows = slice(int(q_start[s]), int(q_start[s + 1]))
+        ry, _, _ = O.decoder_layer(f64(x[rows]), f64(c.kv[s][0]), f64(c.kv[s][1]), npw, hq, hkv, d, EPS,
+                                   layer.scale)
+        assert_bf16_close(y[rows], ry, f"prefill layer, sequence {s}", tol=2e-2)
+
+
+QWEN = dict(H=4096, hq=32, hkv=8, d=128, F=12288)
+
+
+def test_layer_batch_invariance():
+    """Request 0 (700 cached tokens) decodes its next token alone, among 8 and
+    among 63 others of random lengths; its output row and the cache page its
+    new K/V lands in are bitwise the same every time."""
+    layer = _layer(**QWEN)
+    x0 = _tokens(1, QWEN["H"], SEED, 3)
+    ref = None
+    for B, perm in ((1, 0), (9, 1), (64, 2)):
+        log_case(f"layer batch invariance B={B}")
+        prefix = [700] + [W.rand_int(1, 3000, SEED, "len", 50 + i) for i in range(B - 1)]
+        c = Caches(prefix, [1] * B, QWEN["hkv"], QWEN["d"], SEED, perm_index=perm)
+        x = torch.cat([x0, _tokens(B - 1, QWEN["H"], SEED, 100 + B)]) if B > 1 else x0
+        lens = torch.tensor([p + 1 for p in prefix], dtype=torch.int32, device=DEV)
+        slots = torch.stack([c.slots[s][p] for s, p in enumerate(prefix)])
+        y = layer.decode(x, c.kc, c.vc, c.bt, lens, slots, max(prefix) + 1)
+        assert bool(torch.isfinite(y).all()), f"non-finite layer output at B={B}"
+        page = int(c.pb.block_table[0, 700 // 16])
+        got = (y[0].clone(), c.kc[page].clone(), c.vc[page].clone())
+        if ref is None:
+            ref = got
+            continue
+        assert_bitwise(got[0], ref[0], f"layer output of request 0 at B={B}")
+        assert_bitwise(got[1], ref[1], f"K page holding request 0's new token at B={B}")
+        assert_bitwise(got[2], ref[2], f"V page holding request 0's new token at B={B}")
+
+
+def test_layer_prefill_equals_decode():
+    """A 40-token chunk after 300 cached tokens: prefilled in one call, or
+    decoded one token at a time, gives bitwise the same output rows and
+    leaves bitwise the same cache."""
+    layer = _layer(**QWEN)
+    P, n = 300, 40
+    x = _tokens(n, QWEN["H"], SEED, 4)
+    a = Caches([P], [n], QWEN["hkv"], QWEN["d"], SEED)
+    b = Caches([P], [n], QWEN["hkv"], QWEN["d"], SEED)
+    log_case("layer prefill vs decode")
+    yp = layer.prefill(x, a.kc, a.vc, a.bt, torch.tensor([0, n], dtype=torch.int32, device=DEV),
+                       torch.tensor([P], dtype=torch.int32, device=DEV), a.slots[0][P:P + n], n)
+    assert bool(torch.isfinite(yp).all()), "non-finite prefill layer output"
+    for i in range(n):
+        yd = layer.decode(x[i:i + 1], b.kc, b.vc, b.bt, torch.tensor([P + i + 1], dtype=torch.int32, device=DEV),
+                          b.slots[0][P + i:P + i + 1], P + n)
+        assert_bitwise(yd[0], yp[i], f"token {i}: decode vs prefill")
+    assert_bitwise(a.kc, b.kc, "K cache after prefill vs after decoding")
+    assert_bitwise(a.vc, b.vc, "V cache after prefill vs after decoding")

@@ -313,3 +313,69 @@ def test_moe_routing_and_weighting():
     for t in range(T):
         scale = sum(weights[t, s] * (experts[t, s] + 1) for s in range(k))
         assert np.allclose(y[t], scale * sx[t], atol=1e-14)
+
+
+# ---------------------------------------------------------------- decoder layer (composition)
+
+def test_silu_mul_halves_and_closed_form():
+    # g = ln 3 -> silu = 0.75 ln 3; the first half gates, the second multiplies
+    gu = np.array([[math.log(3.0), 0.0, 2.0, 5.0]])
+    out = O.silu_mul(gu)
+    assert out.shape == (1, 2)
+    assert out[0, 0] == pytest.approx(0.75 * math.log(3.0) * 2.0, abs=1e-14)
+    assert out[0, 1] == 0.0                                    # silu(0) = 0, whatever u is
+    # silu(x) - silu(-x) = x (sigma(x) + sigma(-x) = 1): the gate is the first half
+    x = np.array([0.3, -1.7, 4.0])
+    a = O.silu_mul(np.concatenate([x, np.ones(3)])[None])[0]
+    b = O.silu_mul(np.concatenate([-x, np.ones(3)])[None])[0]
+    assert np.allclose(a - b, x, atol=1e-14)
+
+
+def _tiny_layer(rng, H=16, hq=2, hkv=1, d=8, F=16):
+    r = lambda *s: O.round_bf16(rng.standard_normal(s) * 0.3)
+    return dict(g1=O.round_bf16(1.0 + 0.1 * rng.standard_normal(H)), g2=O.round_bf16(1.0 + 0.1 * rng.standard_normal(H)),
+                w_qkv=r((hq + 2 * hkv) * d, H), w_o=r(H, hq * d), w_gu=r(2 * F, H), w_down=r(H, F))
+
+
+def test_decoder_layer_residual_path():
+    """With W_o = W_down = 0 both branches add exact zeros: y is x itself, and
+    k, v are the rounded projection of the rounded rmsnorm of x."""
+    rng = np.random.default_rng(5)
+    H, hq, hkv, d = 16, 2, 1, 8
+    w = _tiny_layer(rng)
+    w["w_o"] = np.zeros_like(w["w_o"])
+    w["w_down"] = np.zeros_like(w["w_down"])
+    x = O.round_bf16(rng.standard_normal((3, H)))
+    kp, vp = O.round_bf16(rng.standard_normal((5, hkv, d))), O.round_bf16(rng.standard_normal((5, hkv, d)))
+    y, k, v = O.decoder_layer(x, kp, vp, w, hq, hkv, d, 1e-6, 0.35)
+    assert np.array_equal(y, x)
+    qkv = O.round_bf16(O.round_bf16(O.rmsnorm(x, w["g1"], 1e-6)) @ w["w_qkv"].T)
+    assert np.array_equal(k.reshape(3, -1), qkv[:, hq * d:(hq + hkv) * d])
+    assert np.array_equal(v.reshape(3, -1), qkv[:, (hq + hkv) * d:])
+
+
+def test_decoder_layer_wiring_closed_forms():
+    """Single-token sequence (attention = its own v), W_qkv's v block and W_o the
+    identity: r = round(x + h).  Then gate = I, up = 2 I, W_down = I:
+    y = round(r + round(silu(h2) * 2 h2)) - which a swapped gate/up
+    (silu(2 h2) * h2) or a residual taken from h instead of x would miss."""
+    rng = np.random.default_rng(6)
+    H = 8
+    hq = hkv = 1
+    d = H
+    eye = np.eye(H)
+    w = dict(g1=O.round_bf16(1.0 + 0.1 * rng.standard_normal(H)), g2=O.round_bf16(1.0 + 0.1 * rng.standard_normal(H)),
+             w_qkv=np.concatenate([rng.standard_normal((H, H)), rng.standard_normal((H, H)), eye]),
+             w_o=eye, w_gu=np.concatenate([eye, 2.0 * eye]), w_down=eye)
+    w["w_qkv"] = O.round_bf16(w["w_qkv"])
+    x = O.round_bf16(rng.standard_normal((1, H)))
+    empty = np.zeros((0, hkv, d))
+    y, _, v = O.decoder_layer(x, empty, empty, w, hq, hkv, d, 1e-6, 0.5)
+    h = O.round_bf16(O.rmsnorm(x, w["g1"], 1e-6))
+    assert np.array_equal(v.reshape(1, H), h)                   # v = h (identity block)
+    r = O.round_bf16(x + h)                                    # attention over one key returns v exactly
+    h2 = O.round_bf16(O.rmsnorm(r, w["g2"], 1e-6))
+    m = O.round_bf16(O.silu(h2) * O.round_bf16(2.0 * h2))
+    assert np.array_equal(y, O.round_bf16(r + m))
+    swapped = O.round_bf16(O.silu(O.round_bf16(2.0 * h2)) * h2)
+    assert not np.array_equal(m, swapped)
