@@ -43,10 +43,24 @@ class DecoderLayer:
         if w_gu.shape[0] % 2 or w_down.shape != (w_qkv.shape[1], w_gu.shape[0] // 2):
             raise ValueError("w_gu / w_down shapes")
 
+    # The three reductions of the layer, one library call each.
+    def _norm(self, x: torch.Tensor, gamma: torch.Tensor) -> torch.Tensor:
+        return bi_rmsnorm(x, gamma, self.eps)
+
+    def _gemm(self, a: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+        return bi_gemm(a, w)
+
+    def _attend(self, q, k_cache, v_cache, block_table, seq_lens, max_seq_len, workspace):
+        if workspace is None:
+            need = bi_attn_decode_workspace_bytes(q.shape[0], self.hq, self.d, max_seq_len)
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        return bi_attn_decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, self.scale,
+                              workspace=workspace)[0]
+
     def _qkv(self, x: torch.Tensor):
         T = x.shape[0]
-        h = bi_rmsnorm(x, self.g1, self.eps)
-        qkv = bi_gemm(h, self.w_qkv)
+        h = self._norm(x, self.g1)
+        qkv = self._gemm(h, self.w_qkv)
         a, b = self.hq * self.d, (self.hq + self.hkv) * self.d
         q = qkv[:, :a].view(T, self.hq, self.d)
         k = qkv[:, a:b].view(T, self.hkv, self.d)
@@ -55,10 +69,10 @@ class DecoderLayer:
 
     def _tail(self, x: torch.Tensor, attn: torch.Tensor) -> torch.Tensor:
         T = x.shape[0]
-        r = bi_add(x, bi_gemm(attn.view(T, self.hq * self.d), self.w_o))
-        h2 = bi_rmsnorm(r, self.g2, self.eps)
-        m = bi_silu_mul(bi_gemm(h2, self.w_gu))
-        return bi_add(r, bi_gemm(m, self.w_down), out=r)
+        r = bi_add(x, self._gemm(attn.view(T, self.hq * self.d), self.w_o))
+        h2 = self._norm(r, self.g2)
+        m = bi_silu_mul(self._gemm(h2, self.w_gu))
+        return bi_add(r, self._gemm(m, self.w_down), out=r)
 
     def decode(self, x: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                seq_lens: torch.Tensor, slot_mapping: torch.Tensor, max_seq_len: int,
@@ -67,11 +81,7 @@ class DecoderLayer:
         slot_mapping [B] is where its K/V goes.  Returns y [B, H]."""
         q, k, v = self._qkv(x)
         bi_kv_append(k, v, slot_mapping, k_cache, v_cache)
-        if workspace is None:
-            need = bi_attn_decode_workspace_bytes(x.shape[0], self.hq, self.d, max_seq_len)
-            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
-        attn, _ = bi_attn_decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, self.scale,
-                                 workspace=workspace)
+        attn = self._attend(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, workspace)
         return self._tail(x, attn)
 
     def prefill(self, x: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
