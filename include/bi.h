@@ -81,12 +81,17 @@ bi_status bi_rmsnorm(const void* x, int64_t ldx, const void* gamma, float eps,
  * c: [m, n] of c_dtype (BI_BF16 or BI_F32), row stride ldc >= n (any value;
  *    c aligned to its element size; ldc % 4 == 0 with a 16-byte-aligned c lets
  *    the epilogue use vector stores, which does not change any value).
- * One tile shape, one MFMA instruction and one ascending K loop with a single
- * fp32 accumulator per output element are used for every m: no split-K and no
- * shape-dependent configuration, so row m of C does not depend on the other rows
- * of A.  k % 32 == 0; m, n >= 0 (m == 0 or n == 0 is a no-op); k >= 32.
- * BI_ERR_UNSUPPORTED when a 64-row slice of A or W spans 2^31 bytes or more
- * (63 * ld + k >= 2^30 elements) or the tile count overflows 32 bits.
+ * One MFMA instruction and one ascending K loop with a single fp32
+ * accumulator per output element, for every m: no split-K, so row m of C does
+ * not depend on the other rows of A.  The output tile is chosen from n alone,
+ * never from m: 64 x 64 when n < 32768, 128 (n) x 256 (m) when n >= 32768 (a
+ * weight that wide fills the GPU with 128-row strips even at m = 1); both give
+ * every element the same bits.  k % 32 == 0; m, n >= 0 (m == 0 or n == 0 is a
+ * no-op); k >= 32.
+ * BI_ERR_UNSUPPORTED when a tile's slice of A or W spans 2^31 bytes or more
+ * ((rows - 1) * ld + k >= 2^30 elements, rows = 64 for A and W of the 64 x 64
+ * tile, 256 for A and 128 for W of the wide one) or the tile count overflows
+ * 32 bits.
  */
 bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw,
                   void* c, int64_t ldc, int32_t c_dtype,
@@ -244,7 +249,8 @@ bi_status bi_log_softmax(const float* logits, int64_t ld_in, float* out, int64_t
  *   z[i, j]   = sum_k a[i, k] w[j, k]        (bi_gemm's tile and fp32 K chain)
  *   out[i, j] = z[i, j] - lse[i],  lse[i] = log sum_j exp(z[i, j])
  * lse is reduced in one fixed tree that depends on n only: (max, sum of exp)
- * pairs over 64-column tiles, folded in ascending tile order.  It is not
+ * pairs over the GEMM's n-tiles (64 columns when n < 32768, 128 from 32768 on),
+ * folded in ascending tile order.  It is not
  * bi_log_softmax's tree, so the two agree to rounding, not bit for bit; each
  * is batch-invariant on its own.
  * a: [m, k] bf16, row stride lda; w: [n, k] bf16, row stride ldw (k % 32 == 0,
@@ -271,8 +277,8 @@ bi_status bi_lm_head_logprobs(const void* a, int64_t lda, const void* w, int64_t
  *   z[i, j]      = sum_k a[i, k] w[j, k]            (as in bi_lm_head_logprobs)
  *   token[i]     = the lowest j with z[i, j] = max_j z[i, j]
  *   logprob[i]   = z[i, token[i]] - lse[i]
- * The (max, sum of exp) pairs of every 64-column tile are formed and folded
- * exactly as in bi_lm_head_logprobs, with the column of each maximum carried
+ * The (max, sum of exp) pairs of every n-tile are formed and folded exactly
+ * as in bi_lm_head_logprobs, with the column of each maximum carried
  * along (ties go to the lower index, which makes the choice independent of
  * the combination order), so logprob[i] is bitwise bi_lm_head_logprobs'
  * out[i, token[i]].  No [m, n] buffer is read or written.

@@ -3,9 +3,9 @@
 // Matrix Multiplication", figs. "Data-Parallel Matrix Multiplication" and
 // "Split-K Matmul").
 //
-// The library instantiates exactly one configuration (gemm.hip) and uses it for
-// every shape.  Whatever the configuration, the arithmetic of an output element
-// is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
+// The library instantiates two configurations and picks one from the weight's
+// row count N alone (gemm_with_cfg), never from M.  Whatever the
+// configuration, the arithmetic of an output element is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
 // k = 0, 32, 64, ... in ascending order, no split of K.  Nothing here depends on
 // M except which rows are loaded and which 16-row MFMA blocks are skipped
 // because all their rows are past M.
@@ -372,14 +372,35 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
   });
 }
 
-// The library's one GEMM configuration, used by bi_gemm, the expert GEMMs of
-// bi_moe_ffn and the fused lm_head.  Chosen by timing candidates at every
-// workload shape on MI355X, and used for every M: 64 (n) x 64 (m) output tile,
-// 2 x 2 wavefronts of 32 x 32, K in 64-wide stages, a 5-stage LDS ring (80 KB,
-// two workgroups per CU).  A small n-extent keeps enough workgroups streaming
-// weights at decode batch sizes (N / 64 of them), which is what bounds those
-// HBM-bound shapes.
+// The library's GEMM configuration for every weight narrower than
+// kGemmWideMinN rows (bi_gemm, the expert GEMMs of bi_moe_ffn).  Chosen by
+// timing candidates at every workload shape on MI355X, and used for every M:
+// 64 (n) x 64 (m) output tile, 2 x 2 wavefronts of 32 x 32, K in 64-wide
+// stages, a 5-stage LDS ring (80 KB, two workgroups per CU).  A small n-extent
+// keeps enough workgroups streaming weights at decode batch sizes (N / 64 of
+// them), which is what bounds those HBM-bound shapes.
 using GemmLibraryCfg = GemmCfg<64, 64, 2, 2, 5, 64, 2>;
+
+// The configuration for wide weights (N >= kGemmWideMinN, e.g. a vocabulary
+// projection): 128 (n) x 256 (m) output tile, 2 x 4 wavefronts of 64 x 64, a
+// 3-stage ring of 64-wide K stages (144 KB, one workgroup per CU).  Such a
+// weight has at least one 128-row strip per CU, so its stream fills the chip
+// even at one m-tile, and the larger tile reads each operand from L2 half (W)
+// or a quarter (A) as often as the 64 x 64 tile, which is what bounds the
+// 64 x 64 tile once M is large.  The choice depends on N alone: a given
+// weight runs the same tile for every M.  Every element's arithmetic is the
+// same in both configurations (one fp32 chain of the same MFMA over k
+// ascending), so the tile decides speed, never bits.
+using GemmWideCfg = GemmCfg<128, 256, 2, 4, 3, 64, 1>;
+constexpr int64_t kGemmWideMinN = 256 * GemmWideCfg::TN;
+
+// Calls f(Cfg{}) with the configuration of a weight with n rows and returns
+// its result (host code).
+template <class F>
+inline auto gemm_with_cfg(int64_t n, F&& f) {
+  if (n >= kGemmWideMinN) return f(GemmWideCfg{});
+  return f(GemmLibraryCfg{});
+}
 
 template <class Cfg>
 hipError_t launch_gemm_cfg(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc,

@@ -61,7 +61,6 @@ hipError_t launch_silu_mul(const void* gu, int64_t ldgu, void* out, int64_t ldo,
 hipError_t launch_lm_head_greedy(const void* a, int64_t lda, const void* w, int64_t ldw, int32_t* token,
                                  float* logprob, int64_t m, int64_t n, int64_t k, void* workspace,
                                  hipStream_t stream);
-bool lm_head_supported(int64_t lda, int64_t ldw, int64_t k);
 hipError_t launch_lm_head_logprobs(const void* a, int64_t lda, const void* w, int64_t ldw, float* out, int64_t ldo,
                                    float* lse, int64_t m, int64_t n, int64_t k, void* workspace,
                                    hipStream_t stream);

@@ -4,15 +4,17 @@
 // Nondeterminism in LLM Inference", section "2. Batch-Invariant Matrix
 // Multiplication" for the product itself).
 //
-//   z[m, n]  = sum_k a[m, k] w[n, k]          (the library GEMM: same tile, same
-//                                              fp32 MFMA chain per element)
+//   z[m, n]  = sum_k a[m, k] w[n, k]          (the library GEMM: bi_gemm's tile
+//                                              for this n, same fp32 MFMA
+//                                              chain per element)
 //   out[m, n] = z[m, n] - lse[m],   lse[m] = log sum_n e^z[m, n]
 //
 // Two kernels, one fixed reduction tree for lse that depends on n alone:
-//  1. the GEMM writes z into `out` and, for every (row, 64-column tile), the
-//     pair (max, sum e^(z - max)) of the row's 64 values: each lane folds its
-//     8 values in column order, lanes l ^ 16 and l ^ 32 are combined, then the
-//     tile's n-wavefronts in ascending order;
+//  1. the GEMM writes z into `out` and, for every (row, n-tile), the pair
+//     (max, sum e^(z - max)) of the row's values in the tile (64 columns, or
+//     128 for a weight of at least kGemmWideMinN rows: the tile is a function
+//     of n): each lane folds its values in column order, lanes l ^ 16 and
+//     l ^ 32 are combined, then the tile's n-wavefronts in ascending order;
 //  2. every workgroup of a row folds the row's tile pairs (thread t: tiles t,
 //     t + 1024, ... in order; a butterfly over the wavefront; the 16 wavefront
 //     results in ascending order) and subtracts lse from its segment of the
@@ -38,7 +40,6 @@
 namespace bi {
 namespace {
 
-using LseCfg = GemmLibraryCfg;
 constexpr int kFinThreads = 1024;
 constexpr int64_t kFinBlocks = 512;    // finalize workgroups aimed at when rows are few
 constexpr int64_t kFinSegsMax = 256;
@@ -186,7 +187,10 @@ __global__ __launch_bounds__(kFinThreads) void greedy_finalize_kernel(const MaxS
   }
 }
 
-int lse_tiles(int64_t n) { return static_cast<int>((n + LseCfg::TN - 1) / LseCfg::TN); }
+// n-tiles of the GEMM configuration bi_gemm uses for this n: the row's pairs.
+int lse_tiles(int64_t n) {
+  return gemm_with_cfg(n, [&](auto cfg) { return static_cast<int>((n + decltype(cfg)::TN - 1) / decltype(cfg)::TN); });
+}
 
 }  // namespace
 
@@ -195,21 +199,22 @@ size_t lm_head_workspace_bytes(int64_t m, int64_t n) {
   return (bytes + 255) / 256 * 256;
 }
 
-bool lm_head_supported(int64_t lda, int64_t ldw, int64_t k) { return gemm_offsets_fit<LseCfg>(lda, ldw, k); }
-
 hipError_t launch_lm_head_logprobs(const void* a, int64_t lda, const void* w, int64_t ldw, float* out, int64_t ldo,
                                    float* lse, int64_t m, int64_t n, int64_t k, void* workspace,
                                    hipStream_t stream) {
   if (m == 0 || n == 0) return hipSuccess;
-  if (!gemm_offsets_fit<LseCfg>(lda, ldw, k)) return hipErrorInvalidValue;
-  const int tiles_m = static_cast<int>((m + LseCfg::TM - 1) / LseCfg::TM);
   const int tiles_n = lse_tiles(n);
   auto* part = static_cast<MaxSum*>(workspace);
-  hipLaunchKernelGGL((lm_head_lse_kernel<LseCfg, MaxSum>), dim3(static_cast<unsigned>(tiles_m * tiles_n)),
-                     dim3(LseCfg::kThreads), 0, stream, static_cast<const uint16_t*>(a), lda,
-                     static_cast<const uint16_t*>(w), ldw, out, ldo, part, (int)m, (int)n, (int)k, tiles_m, tiles_n,
-                     1);
-  hipError_t e = hipGetLastError();
+  hipError_t e = gemm_with_cfg(n, [&](auto cfg) {
+    using Cfg = decltype(cfg);
+    if (!gemm_offsets_fit<Cfg>(lda, ldw, k)) return hipErrorInvalidValue;
+    const int tiles_m = static_cast<int>((m + Cfg::TM - 1) / Cfg::TM);
+    hipLaunchKernelGGL((lm_head_lse_kernel<Cfg, MaxSum>), dim3(static_cast<unsigned>(tiles_m * tiles_n)),
+                       dim3(Cfg::kThreads), 0, stream, static_cast<const uint16_t*>(a), lda,
+                       static_cast<const uint16_t*>(w), ldw, out, ldo, part, (int)m, (int)n, (int)k, tiles_m,
+                       tiles_n, 1);
+    return hipGetLastError();
+  });
   if (e != hipSuccess) return e;
   // Segments per row: enough workgroups to spread few rows over the GPU.
   const int segs = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({kFinSegsMax, (kFinBlocks + m - 1) / m,
@@ -228,15 +233,18 @@ hipError_t launch_lm_head_greedy(const void* a, int64_t lda, const void* w, int6
                                  float* logprob, int64_t m, int64_t n, int64_t k, void* workspace,
                                  hipStream_t stream) {
   if (m == 0 || n == 0) return hipSuccess;
-  if (!gemm_offsets_fit<LseCfg>(lda, ldw, k)) return hipErrorInvalidValue;
-  const int tiles_m = static_cast<int>((m + LseCfg::TM - 1) / LseCfg::TM);
   const int tiles_n = lse_tiles(n);
   auto* part = static_cast<MaxSumArg*>(workspace);
-  hipLaunchKernelGGL((lm_head_lse_kernel<LseCfg, MaxSumArg>), dim3(static_cast<unsigned>(tiles_m * tiles_n)),
-                     dim3(LseCfg::kThreads), 0, stream, static_cast<const uint16_t*>(a), lda,
-                     static_cast<const uint16_t*>(w), ldw, nullptr, 0, part, (int)m, (int)n, (int)k, tiles_m,
-                     tiles_n, 1);
-  hipError_t e = hipGetLastError();
+  hipError_t e = gemm_with_cfg(n, [&](auto cfg) {
+    using Cfg = decltype(cfg);
+    if (!gemm_offsets_fit<Cfg>(lda, ldw, k)) return hipErrorInvalidValue;
+    const int tiles_m = static_cast<int>((m + Cfg::TM - 1) / Cfg::TM);
+    hipLaunchKernelGGL((lm_head_lse_kernel<Cfg, MaxSumArg>), dim3(static_cast<unsigned>(tiles_m * tiles_n)),
+                       dim3(Cfg::kThreads), 0, stream, static_cast<const uint16_t*>(a), lda,
+                       static_cast<const uint16_t*>(w), ldw, nullptr, 0, part, (int)m, (int)n, (int)k, tiles_m,
+                       tiles_n, 1);
+    return hipGetLastError();
+  });
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(greedy_finalize_kernel, dim3(static_cast<unsigned>(m)), dim3(kFinThreads), 0, stream, part,
                      tiles_n, token, logprob);

@@ -48,6 +48,8 @@ def test_host_validation_without_gpu(lib):
     # a 64-row slice of W spanning 2^31 bytes cannot be addressed by one buffer resource
     assert lib.bi_gemm(P, 64, P, 1 << 25, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_UNSUPPORTED
     assert lib.bi_gemm(P, 1 << 25, P, 64, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_UNSUPPORTED
+    # a weight of >= 32768 rows runs the 128 x 256 tile: 128 W rows must span < 2^31 bytes
+    assert lib.bi_gemm(P, 64, P, 9_000_000, P, 1 << 15, 0, 4, 1 << 15, 64, None) == bi.BI_ERR_UNSUPPORTED
     # decode: head_dim 96, group size 3, page size 12, missing workspace
     args = dict(q=P, kc=P, vc=P, pages=8, bt=P, mp=4, lens=P, b=2, msl=64, hq=32, hkv=8, d=128, ps=16)
 
@@ -96,11 +98,15 @@ def test_workspace_size_formula(lib):
     raw = 3 * 32 * 4 * (128 + 4) * 4
     assert n == (raw + 255) // 256 * 256
     assert bi.bi_attn_decode_workspace_bytes(1, 1, 64, 256) == 256 * ((68 * 4 + 255) // 256)
-    # one (max, sum) pair of fp32 per (row, 64-column tile), rounded to 256 bytes
-    assert bi.lm_head_logprobs_workspace_bytes(2048, 151936) == 2048 * 2374 * 8
+    # one (max, sum) pair of fp32 per (row, n-tile), rounded to 256 bytes; the
+    # n-tile is the GEMM's: 64 columns below 32768, 128 from 32768 on
+    assert bi.lm_head_logprobs_workspace_bytes(2048, 151936) == 2048 * 1187 * 8
+    assert bi.lm_head_logprobs_workspace_bytes(5, 32764) == (5 * 512 * 8 + 255) // 256 * 256
+    assert bi.lm_head_logprobs_workspace_bytes(5, 32768) == (5 * 256 * 8 + 255) // 256 * 256
     assert bi.lm_head_logprobs_workspace_bytes(3, 100) == 256
-    # greedy: (max, sum, index) of 12 bytes per (row, 64-column tile), rounded to 256 bytes
-    assert bi.lm_head_greedy_workspace_bytes(2048, 151936) == (2048 * 2374 * 12 + 255) // 256 * 256
+    # greedy: (max, sum, index) of 12 bytes per (row, n-tile), rounded to 256 bytes
+    assert bi.lm_head_greedy_workspace_bytes(2048, 151936) == (2048 * 1187 * 12 + 255) // 256 * 256
+    assert bi.lm_head_greedy_workspace_bytes(3, 18992) == (3 * 297 * 12 + 255) // 256 * 256
     assert bi.lm_head_greedy_workspace_bytes(3, 100) == 256
 
 

@@ -158,6 +158,49 @@ def test_gemm_fp32_lm_head_invariance():
         assert_bitwise(row, ref, f"lm_head token 0 at T={t}")
 
 
+def test_gemm_wide_tile_gives_the_same_bits():
+    """A weight of at least 32768 rows runs the 128 x 256 tile, a narrower one
+    the 64 x 64 tile; both take every element's fp32 MFMA chain over k in the
+    same order, so the tile changes no bit.  The same columns computed as one
+    wide weight and as two narrow slices must agree bitwise (bf16 and fp32
+    outputs, ragged m and n tails), and integer inputs must give the oracle
+    rounded once on the wide path too."""
+    k, n = 320, 32768 + 200
+    w = W.randn_bf16((n, k), 11, "w", 1, std=0.05, device=DEV)
+    for m in (1, 37, 300):
+        log_case(f"gemm wide tile m={m} n={n} k={k}")
+        a = W.randn_bf16((m, k), 11, "x", m, device=DEV)
+        cut = n // 2
+        for dt in (torch.bfloat16, torch.float32):
+            wide = bi.bi_gemm(a, w, out_dtype=dt)
+            narrow = torch.cat([bi.bi_gemm(a, w[:cut], out_dtype=dt), bi.bi_gemm(a, w[cut:], out_dtype=dt)], dim=1)
+            assert_bitwise(wide, narrow, f"wide vs narrow tile m={m} {dt}")
+        ref = O.gemm(f64(a), f64(w[::97]))
+        assert_bf16_close(bi.bi_gemm(a, w)[:, ::97], ref, f"wide tile parity m={m}")
+        assert_f32_close(wide[:, ::97], ref, f"wide tile fp32 parity m={m}")
+    ai, wi = _int_bf16((3, 256), 5), _int_bf16((33000, 256), 6)
+    want = torch.from_numpy(O.f64_to_bf16_bits(O.gemm(f64(ai), f64(wi))).view(np.int16))
+    assert torch.equal(bi.bi_gemm(ai.to(DEV), wi.to(DEV)).view(torch.int16).cpu(), want)
+
+
+def test_gemm_wide_tile_batch_invariance():
+    # The full lm_head (4096 -> 151936, the wide tile): token 0's fp32 logits at
+    # T in {1, 64, 512} and shuffled positions.
+    k, n = 4096, 151936
+    w = W.randn_bf16((n, k), W.SEED_MOE, "w", W.WEIGHTS, std=0.02, device=DEV)
+    ref = None
+    for t in (1, 64, 512):
+        pos = (t * 7) // 9
+        ids = list(range(1, t))
+        ids.insert(pos, 0)
+        a = W.rows_for_requests(ids, k, W.SEED_MOE, device=DEV)
+        row = bi.bi_gemm(a, w, out_dtype=torch.float32)[pos].clone()
+        if ref is None:
+            ref = row
+            assert_f32_close(row[None, ::61], O.gemm(f64(a[pos:pos + 1]), f64(w[::61])), "full lm_head")
+        assert_bitwise(row, ref, f"full lm_head token 0 at T={t} slot={pos}")
+
+
 def test_gemm_run_to_run():
     a = W.rows_for_requests(range(64), 4096, 2, device=DEV)
     w = W.randn_bf16((6144, 4096), 2, "w", 1, std=0.02, device=DEV)

@@ -33,7 +33,8 @@ def _ref(a, w):
     return lp, z[:, 0] - lp[:, 0]
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 1024, 256), (3, 2052, 256), (70, 2052, 512), (5, V // 8, K)])
+@pytest.mark.parametrize("m,n,k", [(1, 1024, 256), (3, 2052, 256), (70, 2052, 512), (5, V // 8, K),
+                                   (300, 32900, 256)])
 def test_lm_head_logprobs_parity(m, n, k):
     log_case(f"lm_head logprobs parity m={m} n={n} k={k}")
     a = W.rows_for_requests(range(m), k, W.SEED_MOE, device=DEV)
@@ -116,7 +117,8 @@ def test_lm_head_logprobs_workspace_reuse_and_errors():
 
 # ---------------------------------------------------------------- greedy sampling
 
-@pytest.mark.parametrize("m,n,k", [(1, 1024, 256), (3, 2053, 256), (70, 2052, 512), (5, V // 8, K), (1, V, K)])
+@pytest.mark.parametrize("m,n,k", [(1, 1024, 256), (3, 2053, 256), (70, 2052, 512), (5, V // 8, K), (1, V, K),
+                                   (37, 32901, 256)])
 def test_lm_head_greedy_parity(m, n, k):
     """The token is the argmax (lowest index on ties) of the library's own fp32
     logits - the decision taken in the kernel's precision - and its logprob is
