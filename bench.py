@@ -714,7 +714,7 @@ def main():
                                f"decode attention 32/8 heads D128 paged (16) KV L~U[1,4096], RMSNorm, "
                                f"MLP GEMMs 4096->12288->4096", "batch": args.batch, "sum_kv_len": sum(step.lens),
                    "step_bytes": nbytes, "step_flops": step.step_flops(), "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "bi_attn_decode (attn_decode_partial_kernel; whole-sequence fold, no merge launch at B=256)",
+        "roofline": {"bound": "hbm", "kernel": "bi_attn_decode (decode_order_kernel + attn_decode_queue_kernel: whole-sequence wavefronts from a longest-first work queue, no merge launch at B=256)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated; "

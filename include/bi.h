@@ -162,7 +162,11 @@ size_t bi_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
  * max_seq_len: host-side upper bound of seq_lens (sizes the grid; a seq_len
  * above it is clamped to it).  Page ids outside [0, num_pages) read as zeros.
  * A sequence with seq_len <= 0 gets out = 0 and lse = -inf.
- * workspace: >= bi_attn_decode_workspace_bytes(...) bytes of device memory.
+ * workspace: >= bi_attn_decode_workspace_bytes(...) bytes of device memory,
+ *   16-byte aligned, owned by the caller; its contents on entry do not
+ *   matter.  It holds the chunk partials, or, once num_seqs * num_kv_heads
+ *   >= 1024 (whole-sequence wavefronts), the work order of the sequences
+ *   (longest first) and its counter.  Concurrent calls need separate workspaces.
  * head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 and the group size
  * num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}; page_size in {16, 32, 64, 128, 256}.
  */

@@ -13,6 +13,7 @@
 // normalisation and bf16 output.  No atomics, no cross-workgroup ordering:
 // every value is written by exactly one workgroup.
 #include <algorithm>
+#include <climits>
 
 #include "attn_chunk.hpp"
 #include "kv_layout.hpp"
@@ -120,19 +121,20 @@ struct GlobalChunk {
   }
 };
 
-// kFold == false: each chunk's partial goes to its workspace record and the
-// merge kernel folds them.  kFold == true (the wavefront owns every chunk of
-// its sequence): the wavefront folds each chunk's partial into a running state
-// right after computing it - per element the same merge step, in the same
-// ascending order, as the merge kernel - and writes out / lse itself.
+// One wavefront's work: chunks c_first .. c_first + chunks_per_wave - 1 of
+// kv head h of sequence b.  kFold == false: each chunk's partial goes to its
+// workspace record and the merge kernel folds them.  kFold == true (the
+// wavefront owns every chunk of its sequence): the wavefront folds each
+// chunk's partial into a running state right after computing it - per element
+// the same merge step, in the same ascending order, as the merge kernel - and
+// writes out / lse itself.
 template <int D, bool kFold>
-__global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(
-    const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc,
+__device__ __forceinline__ void decode_wave(
+    int b, int h, int c_first, const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table,
     int max_pages, const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq, int Hkv, int log2_ps,
     float scale_log2, float* __restrict__ ws, int max_chunks, int chunks_per_wave, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
-  const int c_first = blockIdx.x * chunks_per_wave, h = blockIdx.y, b = blockIdx.z;
   const int L = min(seq_lens[b], max_seq_len);
   if constexpr (kFold) {
     if (L <= 0) {   // the merge kernel's result for an empty sequence
@@ -278,6 +280,83 @@ __global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(
   }
 }
 
+#define BI_DECODE_ARGS                                                                                      \
+  const uint16_t *__restrict__ q, int64_t ldq, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc, \
+      int num_pages, const int32_t *__restrict__ block_table, int max_pages, const int32_t *__restrict__ seq_lens, \
+      int max_seq_len, int Hq, int Hkv, int log2_ps, float scale_log2, float *__restrict__ ws, int max_chunks,     \
+      int chunks_per_wave, uint16_t *__restrict__ out, float *__restrict__ lse
+#define BI_DECODE_PASS                                                                                       \
+  q, ldq, kc, vc, num_pages, block_table, max_pages, seq_lens, max_seq_len, Hq, Hkv, log2_ps, scale_log2, ws, \
+      max_chunks, chunks_per_wave, out, lse
+
+// Grid: chunk group x kv head x sequence, one wavefront each.
+template <int D, bool kFold>
+__global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(BI_DECODE_ARGS) {
+  decode_wave<D, kFold>(blockIdx.z, blockIdx.y, blockIdx.x * chunks_per_wave, BI_DECODE_PASS);
+}
+
+// Whole-sequence wavefronts fed from a work queue.  Items are (sequence, kv
+// head) pairs, sequences in the order decode_order_kernel wrote (most chunks
+// first), kv head fastest.  Each wavefront takes the next item from the
+// counter whenever it finishes one, so a CU whose sequences happen to be short
+// takes more of them, and the longest items start first.  Every item is
+// computed by one wavefront exactly as attn_decode_partial_kernel<D, true>
+// computes it, so which wavefront takes which item changes no bit.  The
+// counter only grows, so every wavefront leaves once it passes `items`.
+template <int D>
+__global__ __launch_bounds__(64, 2) void attn_decode_queue_kernel(BI_DECODE_ARGS, const int32_t* __restrict__ order,
+                                                                  int* __restrict__ next, int items) {
+  for (;;) {
+    int it = 0;
+    if (threadIdx.x == 0) it = atomicAdd(next, 1);
+    it = __shfl(it, 0, kWave);
+    if (it >= items) break;
+    decode_wave<D, true>(order[it / Hkv], it % Hkv, 0, BI_DECODE_PASS);
+  }
+}
+
+// The queue's order: sequences by descending chunk count (sequences with more
+// than kOrderBuckets - 1 chunks share the first bucket; order inside a bucket is
+// whatever the atomics give, which is scheduling only), and the queue's counter
+// set to zero.  One workgroup; it runs before the queue kernel on the same
+// stream.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBuckets = kOrderThreads;
+__global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32_t* __restrict__ seq_lens,
+                                                                     int num_seqs, int max_seq_len,
+                                                                     int32_t* __restrict__ order,
+                                                                     int* __restrict__ next) {
+  __shared__ int cnt[kOrderBuckets];
+  __shared__ int wsum[kOrderThreads / kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  auto bucket = [&](int b) {
+    const int L = min(seq_lens[b], max_seq_len);
+    const int c = L > 0 ? (L + kChunk - 1) / kChunk : 0;
+    return kOrderBuckets - 1 - min(c, kOrderBuckets - 1);
+  };
+  cnt[tid] = 0;
+  __syncthreads();
+  for (int b = tid; b < num_seqs; b += kOrderThreads) atomicAdd(&cnt[bucket(b)], 1);
+  __syncthreads();
+  // Exclusive prefix sum over the buckets: inclusive within each wavefront,
+  // then the totals of the wavefronts before it.
+  const int v = cnt[tid];
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = x;
+  __syncthreads();
+  int off = 0;
+  for (int w = 0; w < wave; ++w) off += wsum[w];
+  cnt[tid] = off + x - v;
+  __syncthreads();
+  for (int b = tid; b < num_seqs; b += kOrderThreads) order[atomicAdd(&cnt[bucket(b)], 1)] = b;
+  if (tid == 0) *next = 0;
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq,
@@ -321,6 +400,16 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
 // 0.51-0.59 with one wavefront per chunk; below that, one chunk per wavefront
 // keeps more loads in flight.
 constexpr int kDecodeWaves = 1024;
+// Wavefronts of the queue kernel (scheduling only): two per CU, and at most
+// half the items, so that wavefronts which finish early take the remaining
+// ones.  Measured on MI355X against one wavefront per item in grid order
+// (which puts consecutive items, and so a CU's share of the lengths, at the
+// mercy of the batch): 10-16% faster at 1024-4096 items (Qwen3-8B shapes at
+// B = 128 / 256 / 512: 187 -> 167, 355 -> 314, 705 -> 638 us; Qwen3-235B at
+// B = 256 / 512: 195 -> 164, 382 -> 325 us), and 4 or 6 wavefronts per CU were
+// 3-8% slower than 2; one wavefront per item sorted longest first was slower
+// still (a CU then receives consecutive, equally long items).
+int decode_queue_waves(int items) { return std::max(1, std::min(items / 2, 512)); }
 int decode_chunks_per_wave(int num_seqs, int num_kv_heads, int max_chunks) {
   return (int64_t)num_seqs * num_kv_heads >= kDecodeWaves ? max_chunks : 1;
 }
@@ -335,11 +424,30 @@ hipError_t launch(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t*
   const auto* kcs = static_cast<const uint16_t*>(g.k_cache);
   const auto* vcs = static_cast<const uint16_t*>(g.v_cache);
   auto* os = static_cast<uint16_t*>(out);
-  if (cpw == max_chunks) {
-    // Every wavefront owns a whole sequence: it folds the chunks itself.
+  const int64_t items64 = (int64_t)num_seqs * g.num_kv_heads;
+  if (cpw == max_chunks && items64 > INT_MAX / 2) {
+    // The queue's counter would overflow: one wavefront per item, in grid order.
     hipLaunchKernelGGL((attn_decode_partial_kernel<D, true>), dim3(1, g.num_kv_heads, num_seqs), dim3(64), 0, stream,
                        qs, ld_q, kcs, vcs, g.num_pages, g.block_table, g.max_pages_per_seq, seq_lens, max_seq_len,
                        g.num_q_heads, g.num_kv_heads, g.log2_page, g.scale_log2, ws, max_chunks, cpw, os, lse);
+    return hipGetLastError();
+  }
+  if (cpw == max_chunks) {
+    // Every wavefront owns a whole sequence and folds its chunks itself; the
+    // (sequence, kv head) items come from a queue, longest first.  The queue
+    // (a counter, then the order) lives at the start of the workspace, which
+    // this path does not otherwise use.
+    auto* next = static_cast<int*>(workspace);
+    auto* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 16);
+    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, seq_lens, num_seqs, max_seq_len,
+                       order, next);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int items = static_cast<int>(items64);
+    hipLaunchKernelGGL((attn_decode_queue_kernel<D>), dim3(decode_queue_waves(items)), dim3(64), 0, stream,
+                       qs, ld_q, kcs, vcs, g.num_pages, g.block_table, g.max_pages_per_seq, seq_lens, max_seq_len,
+                       g.num_q_heads, g.num_kv_heads, g.log2_page, g.scale_log2, ws, max_chunks, cpw, os, lse, order,
+                       next, items);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((attn_decode_partial_kernel<D, false>), dim3((max_chunks + cpw - 1) / cpw, g.num_kv_heads, num_seqs),

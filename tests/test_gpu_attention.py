@@ -523,6 +523,35 @@ def test_decode_edges():
     assert torch.isfinite(o4.float()).all()
 
 
+def test_decode_work_queue_edges():
+    """At 1024 or more (sequence, kv head) items the decode wavefronts take
+    whole sequences from a work queue, longest first.  Empty sequences, lengths
+    clamped by max_seq_len and a workspace full of garbage must give, for every
+    request, bitwise what decoding it alone gives (one request: the per-chunk
+    path and the merge kernel)."""
+    B, msl = 160, 600
+    lens = [int(x) for x in torch.randint(1, 700, (B,), generator=torch.Generator().manual_seed(5))]
+    bt = Batch(range(B), lens, 32, 8, 128, 23)
+    run_lens = list(lens)
+    for i in (0, 17, 159):
+        run_lens[i] = 0
+    ws = torch.full((bi.bi_attn_decode_workspace_bytes(B, 32, 128, msl),), 255, dtype=torch.uint8, device=DEV)
+    lt = torch.tensor(run_lens, dtype=torch.int32, device=DEV)
+    out, lse = bt.decode(max_seq_len=msl, lens=lt, workspace=ws)
+    clamped = [i for i in range(B) if run_lens[i] > msl]
+    assert clamped, "some lengths exceed max_seq_len"
+    for i in (0, 17, 159, 1, 2, 80, 158, *clamped[:4]):
+        log_case(f"decode queue edges request {i} len {run_lens[i]}")
+        o1, l1 = bi.bi_attn_decode(bt.q[i:i + 1], bt.kc, bt.vc, bt.bt[i:i + 1], lt[i:i + 1], msl, bt.scale,
+                                   lse=torch.empty((1, 32), dtype=torch.float32, device=DEV))
+        assert_bitwise(out[i:i + 1], o1, f"request {i}: queue vs alone")
+        assert_bitwise(lse[i:i + 1], l1, f"request {i} lse: queue vs alone")
+        if run_lens[i] == 0:
+            assert torch.all(out[i].view(torch.int16) == 0) and torch.all(torch.isneginf(lse[i]))
+    again, _ = bt.decode(max_seq_len=msl, lens=lt, workspace=ws)
+    assert_bitwise(again, out, "queue: repeat with the workspace left by the previous call")
+
+
 def test_attention_errors():
     bt = Batch([0], [10], 32, 8, 128, 22)
     with pytest.raises(bi.BiError) as e:
