@@ -134,8 +134,9 @@ bi_status bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new, con
 /*
  * Workspace for bi_attn_decode: per (sequence, q head, chunk) partial results
  * (reference max, sum, D accumulators), fp32: num_seqs * num_q_heads * ceil(max_seq_len/256)
- * * (head_dim + 4) * 4 bytes
- * (accumulators, max, sum, 2 pad words per record), rounded up to 256 bytes.
+ * * (head_dim + 4) * 4 bytes (accumulators, max, sum, 2 pad words per
+ * record), rounded up to 256 bytes; then the work queue: 16 bytes plus
+ * 2 * num_seqs * ceil(max_seq_len/256) int32; the total rounded up to 256 bytes.
  */
 size_t bi_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                       int32_t max_seq_len);
@@ -164,9 +165,10 @@ size_t bi_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int
  * A sequence with seq_len <= 0 gets out = 0 and lse = -inf.
  * workspace: >= bi_attn_decode_workspace_bytes(...) bytes of device memory,
  *   16-byte aligned, owned by the caller; its contents on entry do not
- *   matter.  It holds the chunk partials, or, once num_seqs * num_kv_heads
- *   >= 1024 (whole-sequence wavefronts), the work order of the sequences
- *   (longest first) and its counter.  Concurrent calls need separate workspaces.
+ *   matter.  It holds the chunk partials (or a fold of a sequence's first
+ *   chunks in chunk 0's record) and the work queue's items and counter.
+ *   Concurrent calls need separate workspaces.  num_seqs * num_kv_heads
+ *   <= 2^29 (else BI_ERR_UNSUPPORTED).
  * head_dim in {64, 128}; num_q_heads % num_kv_heads == 0 and the group size
  * num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}; page_size in {16, 32, 64, 128, 256}.
  */

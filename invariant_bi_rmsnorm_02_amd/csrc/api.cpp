@@ -129,10 +129,7 @@ bi_status bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new, con
 size_t bi_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                       int32_t max_seq_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  const int64_t chunks = max_seq_len > 0 ? (max_seq_len + BI_KV_CHUNK - 1) / BI_KV_CHUNK : 1;
-  const size_t bytes = (size_t)num_seqs * (size_t)num_q_heads * (size_t)chunks *
-                       (size_t)(head_dim + 4) * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  return bi::attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len);
 }
 
 bi_status bi_attn_decode(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache, int32_t num_pages,
@@ -150,6 +147,7 @@ bi_status bi_attn_decode(const void* q, int64_t ld_q, const void* k_cache, const
   if (!aligned16(q) || !aligned16(out)) return BI_ERR_INVALID_ARG;
   if (ld_q < (int64_t)num_q_heads * head_dim || ld_q % 8) return BI_ERR_INVALID_ARG;
   if (num_seqs > 65535 || num_kv_heads > 65535) return BI_ERR_UNSUPPORTED;  // grid y/z limits
+  if ((int64_t)num_seqs * num_kv_heads > (1 << 29)) return BI_ERR_UNSUPPORTED;  // work-queue item count
   if (!workspace || !aligned16(workspace)) return BI_ERR_WORKSPACE;
   if (workspace_bytes < bi_attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len))
     return BI_ERR_WORKSPACE;

@@ -123,14 +123,15 @@ struct GlobalChunk {
 
 // One wavefront's work: chunks c_first .. c_first + chunks_per_wave - 1 of
 // kv head h of sequence b.  kFold == false: each chunk's partial goes to its
-// workspace record and the merge kernel folds them.  kFold == true (the
-// wavefront owns every chunk of its sequence): the wavefront folds each
-// chunk's partial into a running state right after computing it - per element
-// the same merge step, in the same ascending order, as the merge kernel - and
-// writes out / lse itself.
+// workspace record and the merge kernel folds them.  kFold == true (c_first
+// is 0): the wavefront folds each chunk's partial into a running state right
+// after computing it - per element the same merge step, in the same ascending
+// order, as the merge kernel - and then either writes out / lse (it had every
+// chunk of the sequence) or, with to_record, stores the running state in
+// chunk 0's record, from which the merge kernel continues the same fold.
 template <int D, bool kFold>
 __device__ __forceinline__ void decode_wave(
-    int b, int h, int c_first, const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc,
+    int b, int h, int c_first, bool to_record, const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table,
     int max_pages, const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq, int Hkv, int log2_ps,
     float scale_log2, float* __restrict__ ws, int max_chunks, int chunks_per_wave, uint16_t* __restrict__ out,
@@ -265,7 +266,15 @@ __device__ __forceinline__ void decode_wave(
     }
   }
   if constexpr (kFold) {
-    if (row_ok) {
+    if (row_ok && to_record) {
+      // rec is chunk c_first = 0's record (the fold path never advances it).
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = o_run[dt][lane];
+      if (g == 0) {
+        rec[D] = m_run;
+        rec[D + 1] = l_run;
+      }
+    } else if (row_ok) {
       uint16_t* op = out + ((int64_t)b * Hq + h * G + n) * D + 4 * g;
       const float inv = finalize_inv(l_run);
 #pragma unroll
@@ -292,51 +301,82 @@ __device__ __forceinline__ void decode_wave(
 // Grid: chunk group x kv head x sequence, one wavefront each.
 template <int D, bool kFold>
 __global__ __launch_bounds__(64, 2) void attn_decode_partial_kernel(BI_DECODE_ARGS) {
-  decode_wave<D, kFold>(blockIdx.z, blockIdx.y, blockIdx.x * chunks_per_wave, BI_DECODE_PASS);
+  decode_wave<D, kFold>(blockIdx.z, blockIdx.y, blockIdx.x * chunks_per_wave, false, BI_DECODE_PASS);
 }
 
-// Whole-sequence wavefronts fed from a work queue.  Items are (sequence, kv
-// head) pairs, sequences in the order decode_order_kernel wrote (most chunks
-// first), kv head fastest.  Each wavefront takes the next item from the
-// counter whenever it finishes one, so a CU whose sequences happen to be short
-// takes more of them, and the longest items start first.  Every item is
-// computed by one wavefront exactly as attn_decode_partial_kernel<D, true>
-// computes it, so which wavefront takes which item changes no bit.  The
-// counter only grows, so every wavefront leaves once it passes `items`.
-template <int D>
-__global__ __launch_bounds__(64, 2) void attn_decode_queue_kernel(BI_DECODE_ARGS, const int32_t* __restrict__ order,
-                                                                  int* __restrict__ next, int items) {
+// Wavefronts fed from a work queue.  An item is (sequence, chunk group, kv
+// head): chunk group j is chunks j * cg .. j * cg + cg - 1 (cg = chunks_per_wave),
+// items in the order decode_order_kernel wrote (most chunks first), kv head
+// fastest.  Group 0 is folded in-wave: into out / lse when it holds the whole
+// sequence, else into chunk 0's record; a later group writes one partial per
+// chunk, and the merge kernel continues the fold from chunk 0's record with
+// chunks cg, cg + 1, ... in ascending order - the same left fold, step for
+// step, as one wavefront folding the whole sequence (folding the stored state
+// into the empty start state is exact for m and l and can only turn a -0 in o
+// into +0, which the final + 0.0f makes one bit pattern anyway).  Each
+// wavefront takes the next item from the counter whenever it finishes one, so
+// a CU whose items happen to be short takes more of them.  Which wavefront
+// takes which item, and cg itself, change no bit.  The counter only grows, so
+// every wavefront leaves once it passes the item count.  kGroups == false: cg
+// covers every chunk, so every item is a whole sequence (no partials, no merge
+// kernel), and the kernel holds only the fold path.
+template <int D, bool kGroups>
+__global__ __launch_bounds__(64, 2) void attn_decode_queue_kernel(BI_DECODE_ARGS, const int32_t* __restrict__ item_seq,
+                                                                  const int32_t* __restrict__ item_group,
+                                                                  int* __restrict__ next,
+                                                                  const int* __restrict__ total) {
+  const int items = *total;
   for (;;) {
     int it = 0;
     if (threadIdx.x == 0) it = atomicAdd(next, 1);
     it = __shfl(it, 0, kWave);
     if (it >= items) break;
-    decode_wave<D, true>(order[it / Hkv], it % Hkv, 0, BI_DECODE_PASS);
+    const int i = it / Hkv, h = it % Hkv;
+    const int b = item_seq[i], grp = kGroups ? item_group[i] : 0;
+    if (!kGroups) {
+      decode_wave<D, true>(b, h, 0, false, BI_DECODE_PASS);
+    } else if (grp == 0) {
+      const int L = min(seq_lens[b], max_seq_len);
+      const int C = L > 0 ? (L + kChunk - 1) / kChunk : 0;
+      decode_wave<D, true>(b, h, 0, C > chunks_per_wave, BI_DECODE_PASS);
+    } else {
+      decode_wave<D, false>(b, h, grp * chunks_per_wave, false, BI_DECODE_PASS);
+    }
   }
 }
 
-// The queue's order: sequences by descending chunk count (sequences with more
-// than kOrderBuckets - 1 chunks share the first bucket; order inside a bucket is
-// whatever the atomics give, which is scheduling only), and the queue's counter
-// set to zero.  One workgroup; it runs before the queue kernel on the same
-// stream.
+// The queue's items: every (sequence, chunk group of cg chunks) pair, a
+// sequence with no key counting as one item (its wavefront writes out = 0 and
+// lse = -inf), ordered by descending chunks in the group (more than
+// kOrderBuckets - 1 chunks share the first bucket; the order inside a bucket is
+// whatever the atomics give, which is scheduling only); the item count times
+// Hkv, and the queue's counter set to zero.  One workgroup; it runs before the
+// queue kernel on the same stream.
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderBuckets = kOrderThreads;
 __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32_t* __restrict__ seq_lens,
-                                                                     int num_seqs, int max_seq_len,
-                                                                     int32_t* __restrict__ order,
-                                                                     int* __restrict__ next) {
+                                                                     int num_seqs, int max_seq_len, int cg, int Hkv,
+                                                                     int32_t* __restrict__ item_seq,
+                                                                     int32_t* __restrict__ item_group,
+                                                                     int* __restrict__ next, int* __restrict__ total) {
   __shared__ int cnt[kOrderBuckets];
   __shared__ int wsum[kOrderThreads / kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  auto bucket = [&](int b) {
+  auto chunks = [&](int b) {
     const int L = min(seq_lens[b], max_seq_len);
-    const int c = L > 0 ? (L + kChunk - 1) / kChunk : 0;
-    return kOrderBuckets - 1 - min(c, kOrderBuckets - 1);
+    return L > 0 ? (L + kChunk - 1) / kChunk : 0;
+  };
+  auto groups = [&](int c) { return c > 0 ? (c + cg - 1) / cg : 1; };
+  auto bucket = [&](int c, int j) {
+    const int n = c > 0 ? min(cg, c - j * cg) : 0;
+    return kOrderBuckets - 1 - min(n, kOrderBuckets - 1);
   };
   cnt[tid] = 0;
   __syncthreads();
-  for (int b = tid; b < num_seqs; b += kOrderThreads) atomicAdd(&cnt[bucket(b)], 1);
+  for (int b = tid; b < num_seqs; b += kOrderThreads) {
+    const int c = chunks(b), ng = groups(c);
+    for (int j = 0; j < ng; ++j) atomicAdd(&cnt[bucket(c, j)], 1);
+  }
   __syncthreads();
   // Exclusive prefix sum over the buckets: inclusive within each wavefront,
   // then the totals of the wavefronts before it.
@@ -352,25 +392,39 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32
   int off = 0;
   for (int w = 0; w < wave; ++w) off += wsum[w];
   cnt[tid] = off + x - v;
+  if (tid == kOrderThreads - 1) *total = (off + x) * Hkv;
   __syncthreads();
-  for (int b = tid; b < num_seqs; b += kOrderThreads) order[atomicAdd(&cnt[bucket(b)], 1)] = b;
+  for (int b = tid; b < num_seqs; b += kOrderThreads) {
+    const int c = chunks(b), ng = groups(c);
+    for (int j = 0; j < ng; ++j) {
+      const int p = atomicAdd(&cnt[bucket(c, j)], 1);
+      item_seq[p] = b;
+      item_group[p] = j;
+    }
+  }
   if (tid == 0) *next = 0;
 }
 
+// Folds a sequence's records in ascending order: chunk 0's record, then
+// chunks cg, cg + 1, ..., C - 1 (cg = 1: every chunk's partial; cg > 1: chunk
+// 0's record holds the fold of chunks 0 .. cg - 1).  Sequences with C <= done
+// were finished by their queue wavefront.
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq,
-    int max_chunks, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int max_chunks, int cg, int done, uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int E = D / 64;  // head dims per lane
   const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int L = min(seq_lens[b], max_seq_len);
   const int C = L > 0 ? (L + kChunk - 1) / kChunk : 0;
-  const float* rec = ws + ((int64_t)b * Hq + head) * max_chunks * (D + 4);
+  if (C <= done) return;
+  const float* rec0 = ws + ((int64_t)b * Hq + head) * max_chunks * (D + 4);
 
   float m = -INFINITY, l = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  for (int c = 0; c < C; ++c, rec += D + 4) {
+  for (int c = 0; c < C; c = (c == 0 ? cg : c + 1)) {
+    const float* rec = rec0 + (int64_t)c * (D + 4);
     const MergeCoef k = merge_coef(m, rec[D]);
     l = merge_val(l, rec[D + 1], k);
 #pragma unroll
@@ -390,28 +444,55 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
   }
 }
 
-// Consecutive chunks per wavefront.  This is scheduling only: every chunk is
-// reduced the same way whichever wavefront runs it, and the in-wave fold is the
-// merge kernel's fold, so the bits of a result do not depend on it (the
-// batch-invariance tests compare batches that take both branches).  Measured on
-// MI355X (Qwen3-8B and Qwen3-235B decode shapes): once there are at least
-// kDecodeWaves (sequence, kv head) pairs - four wavefronts per CU - wavefronts
-// that stream and fold a whole sequence reach 0.71-0.75 of HBM, against
-// 0.51-0.59 with one wavefront per chunk; below that, one chunk per wavefront
-// keeps more loads in flight.
-constexpr int kDecodeWaves = 1024;
-// Wavefronts of the queue kernel (scheduling only): two per CU, and at most
-// half the items, so that wavefronts which finish early take the remaining
-// ones.  Measured on MI355X against one wavefront per item in grid order
-// (which puts consecutive items, and so a CU's share of the lengths, at the
-// mercy of the batch): 10-16% faster at 1024-4096 items (Qwen3-8B shapes at
-// B = 128 / 256 / 512: 187 -> 167, 355 -> 314, 705 -> 638 us; Qwen3-235B at
-// B = 256 / 512: 195 -> 164, 382 -> 325 us), and 4 or 6 wavefronts per CU were
-// 3-8% slower than 2; one wavefront per item sorted longest first was slower
-// still (a CU then receives consecutive, equally long items).
-int decode_queue_waves(int items) { return std::max(1, std::min(items / 2, 512)); }
-int decode_chunks_per_wave(int num_seqs, int num_kv_heads, int max_chunks) {
-  return (int64_t)num_seqs * num_kv_heads >= kDecodeWaves ? max_chunks : 1;
+// Scheduling (none of it changes a bit: a chunk is reduced the same way
+// whichever wavefront runs it, and every fold is the same ascending left fold).
+//  - Few chunks in the batch (at most kDecodeGridItems (sequence, kv head,
+//    chunk) items): one wavefront per chunk on a grid, every partial written,
+//    then the merge kernel; the grid is (nearly) resident at once, and a work
+//    queue's extra launch would only add latency.
+//  - Otherwise a work queue of (sequence, chunk group, kv head) items, groups
+//    of cg chunks with cg chosen so that there are at most about
+//    kDecodeQueueItems of them (cg = every chunk, i.e. whole sequences and no
+//    merge launch, once the batch alone gives that many (sequence, kv head)
+//    pairs), fed to at most kDecodeQueueWaves wavefronts (two per CU).
+// Measured on MI355X: whole-sequence wavefronts from the queue at 1024-4096
+// (sequence, kv head) pairs are 10-16% faster than one wavefront per pair in
+// grid order (Qwen3-8B at B = 128 / 256 / 512: 187 -> 167, 355 -> 314,
+// 705 -> 638 us; Qwen3-235B at B = 256 / 512: 195 -> 164, 382 -> 325 us); four
+// or six wavefronts per CU were 3-8% slower than two, and one wavefront per
+// pair sorted longest first was slower still (a CU then receives consecutive,
+// equally long items).  With fewer pairs a whole-sequence wavefront bounds the
+// call by its sequence's length, so sequences are cut into chunk groups:
+// Qwen3-8B at B = 64 / 96: 120 -> 105, 176 -> 135 us; Qwen3-235B at B = 64 /
+// 128: 69 -> 63, 129 -> 102 us.  Aiming at 2048 or 4096 groups instead of 1024
+// was 5-15% slower.  At 4096 chunk items the two are close (Qwen3-8B B = 32:
+// grid 4% faster; Qwen3-235B B = 64: queue 9% faster).
+constexpr int64_t kDecodeGridItems = 2048;
+constexpr int64_t kDecodeQueueItems = 1024;
+constexpr int64_t kDecodeQueueWaves = 512;
+
+struct DecodeQueue {
+  int* next;          // the counter
+  int* total;         // item count x Hkv, written by decode_order_kernel
+  int32_t* item_seq;
+  int32_t* item_group;
+};
+
+// The queue lives after the chunk records: the records' bytes rounded up to
+// 256, then the counter and the count (16 bytes), then two arrays of
+// num_seqs * max_chunks int32 (a sequence has at most max_chunks groups).
+size_t decode_records_bytes(int64_t num_seqs, int64_t hq, int64_t d, int64_t max_chunks) {
+  const size_t bytes = (size_t)num_seqs * (size_t)hq * (size_t)max_chunks * (size_t)(d + 4) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+DecodeQueue decode_queue(void* workspace, int num_seqs, int hq, int d, int max_chunks) {
+  char* base = static_cast<char*>(workspace) + decode_records_bytes(num_seqs, hq, d, max_chunks);
+  DecodeQueue qd;
+  qd.next = reinterpret_cast<int*>(base);
+  qd.total = qd.next + 1;
+  qd.item_seq = reinterpret_cast<int32_t*>(base + 16);
+  qd.item_group = qd.item_seq + (int64_t)num_seqs * max_chunks;
+  return qd;
 }
 
 template <int D>
@@ -419,49 +500,52 @@ hipError_t launch(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t*
                   int max_seq_len, void* out, float* lse, void* workspace, hipStream_t stream) {
   const int max_chunks = (max_seq_len + kChunk - 1) / kChunk;
   float* ws = static_cast<float*>(workspace);
-  const int cpw = decode_chunks_per_wave(num_seqs, g.num_kv_heads, max_chunks);
   const auto* qs = static_cast<const uint16_t*>(q);
   const auto* kcs = static_cast<const uint16_t*>(g.k_cache);
   const auto* vcs = static_cast<const uint16_t*>(g.v_cache);
   auto* os = static_cast<uint16_t*>(out);
-  const int64_t items64 = (int64_t)num_seqs * g.num_kv_heads;
-  if (cpw == max_chunks && items64 > INT_MAX / 2) {
-    // The queue's counter would overflow: one wavefront per item, in grid order.
-    hipLaunchKernelGGL((attn_decode_partial_kernel<D, true>), dim3(1, g.num_kv_heads, num_seqs), dim3(64), 0, stream,
-                       qs, ld_q, kcs, vcs, g.num_pages, g.block_table, g.max_pages_per_seq, seq_lens, max_seq_len,
-                       g.num_q_heads, g.num_kv_heads, g.log2_page, g.scale_log2, ws, max_chunks, cpw, os, lse);
-    return hipGetLastError();
-  }
-  if (cpw == max_chunks) {
-    // Every wavefront owns a whole sequence and folds its chunks itself; the
-    // (sequence, kv head) items come from a queue, longest first.  The queue
-    // (a counter, then the order) lives at the start of the workspace, which
-    // this path does not otherwise use.
-    auto* next = static_cast<int*>(workspace);
-    auto* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 16);
-    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, seq_lens, num_seqs, max_seq_len,
-                       order, next);
+  const int64_t pairs = (int64_t)num_seqs * g.num_kv_heads;
+  const int64_t chunk_items = pairs * max_chunks;
+  if (chunk_items <= kDecodeGridItems) {
+    hipLaunchKernelGGL((attn_decode_partial_kernel<D, false>), dim3(max_chunks, g.num_kv_heads, num_seqs), dim3(64), 0,
+                       stream, qs, ld_q, kcs, vcs, g.num_pages, g.block_table, g.max_pages_per_seq, seq_lens,
+                       max_seq_len, g.num_q_heads, g.num_kv_heads, g.log2_page, g.scale_log2, ws, max_chunks, 1, os,
+                       lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int items = static_cast<int>(items64);
-    hipLaunchKernelGGL((attn_decode_queue_kernel<D>), dim3(decode_queue_waves(items)), dim3(64), 0, stream,
-                       qs, ld_q, kcs, vcs, g.num_pages, g.block_table, g.max_pages_per_seq, seq_lens, max_seq_len,
-                       g.num_q_heads, g.num_kv_heads, g.log2_page, g.scale_log2, ws, max_chunks, cpw, os, lse, order,
-                       next, items);
+    hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(64), 0, stream, ws, seq_lens,
+                       max_seq_len, g.num_q_heads, max_chunks, 1, -1, os, lse);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((attn_decode_partial_kernel<D, false>), dim3((max_chunks + cpw - 1) / cpw, g.num_kv_heads, num_seqs),
-                     dim3(64), 0, stream, qs, ld_q, kcs, vcs, g.num_pages, g.block_table, g.max_pages_per_seq,
-                     seq_lens, max_seq_len, g.num_q_heads, g.num_kv_heads, g.log2_page, g.scale_log2, ws,
-                     max_chunks, cpw, os, lse);
+  int64_t cg = std::min<int64_t>(max_chunks, std::max<int64_t>(1, chunk_items / kDecodeQueueItems));
+  auto upper = [&](int64_t c) { return pairs * ((max_chunks + c - 1) / c); };   // items, at most
+  while (upper(cg) > INT_MAX / 2 && cg < max_chunks) cg = std::min<int64_t>(max_chunks, 2 * cg);
+  if (upper(cg) > INT_MAX / 2) return hipErrorInvalidValue;
+  const DecodeQueue qd = decode_queue(workspace, num_seqs, g.num_q_heads, D, max_chunks);
+  hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, seq_lens, num_seqs, max_seq_len,
+                     (int)cg, g.num_kv_heads, qd.item_seq, qd.item_group, qd.next, qd.total);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(64), 0, stream, ws,
-                     seq_lens, max_seq_len, g.num_q_heads, max_chunks, os, lse);
+  const int waves = static_cast<int>(std::min<int64_t>(upper(cg), kDecodeQueueWaves));
+  auto queue = cg >= max_chunks ? attn_decode_queue_kernel<D, false> : attn_decode_queue_kernel<D, true>;
+  hipLaunchKernelGGL(queue, dim3(waves), dim3(64), 0, stream, qs, ld_q, kcs, vcs, g.num_pages, g.block_table,
+                     g.max_pages_per_seq, seq_lens, max_seq_len, g.num_q_heads, g.num_kv_heads, g.log2_page,
+                     g.scale_log2, ws, max_chunks, (int)cg, os, lse, qd.item_seq, qd.item_group, qd.next, qd.total);
+  e = hipGetLastError();
+  if (e != hipSuccess || cg >= max_chunks) return e;
+  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(64), 0, stream, ws, seq_lens,
+                     max_seq_len, g.num_q_heads, max_chunks, (int)cg, (int)cg, os, lse);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t attn_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, int64_t max_seq_len) {
+  const int64_t chunks = max_seq_len > 0 ? (max_seq_len + kChunk - 1) / kChunk : 1;
+  const size_t bytes = decode_records_bytes(num_seqs, num_q_heads, head_dim, chunks) + 16 +
+                       2 * sizeof(int32_t) * (size_t)num_seqs * (size_t)chunks;
+  return (bytes + 255) & ~(size_t)255;
+}
 
 hipError_t launch_attn_decode(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t* seq_lens,
                               int num_seqs, int max_seq_len, void* out, float* lse, void* workspace,

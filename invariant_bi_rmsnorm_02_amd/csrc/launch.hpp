@@ -35,6 +35,10 @@ struct AttnGeom {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
+// Bytes of workspace bi_attn_decode needs: the per-(sequence, q head, chunk)
+// records and the work queue (attn_decode.hip).
+size_t attn_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, int64_t max_seq_len);
+
 hipError_t launch_attn_decode(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t* seq_lens, int num_seqs,
                               int max_seq_len, void* out, float* lse, void* workspace,
                               hipStream_t stream);

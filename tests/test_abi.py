@@ -93,11 +93,13 @@ def test_host_validation_without_gpu(lib):
 
 
 def test_workspace_size_formula(lib):
-    # one (D + 4)-float record per (sequence, q head, 256-token chunk), rounded to 256 bytes
+    # one (D + 4)-float record per (sequence, q head, 256-token chunk), rounded to 256 bytes, then the
+    # work queue: a 16-byte header and two int32 entries per (sequence, chunk), rounded to 256 bytes
+    r256 = lambda x: (x + 255) // 256 * 256
     n = bi.bi_attn_decode_workspace_bytes(3, 32, 128, 1000)
-    raw = 3 * 32 * 4 * (128 + 4) * 4
-    assert n == (raw + 255) // 256 * 256
-    assert bi.bi_attn_decode_workspace_bytes(1, 1, 64, 256) == 256 * ((68 * 4 + 255) // 256)
+    assert n == r256(r256(3 * 32 * 4 * (128 + 4) * 4) + 16 + 8 * 3 * 4)
+    assert bi.bi_attn_decode_workspace_bytes(1, 1, 64, 256) == r256(r256(68 * 4) + 16 + 8)
+    assert bi.bi_attn_decode_workspace_bytes(256, 32, 128, 4096) == r256(r256(256 * 32 * 16 * 132 * 4) + 16 + 8 * 256 * 16)
     # one (max, sum) pair of fp32 per (row, n-tile), rounded to 256 bytes; the
     # n-tile is the GEMM's: 64 columns below 32768, 128 from 32768 on
     assert bi.lm_head_logprobs_workspace_bytes(2048, 151936) == 2048 * 1187 * 8

@@ -523,25 +523,29 @@ def test_decode_edges():
     assert torch.isfinite(o4.float()).all()
 
 
-def test_decode_work_queue_edges():
-    """At 1024 or more (sequence, kv head) items the decode wavefronts take
-    whole sequences from a work queue, longest first.  Empty sequences, lengths
-    clamped by max_seq_len and a workspace full of garbage must give, for every
-    request, bitwise what decoding it alone gives (one request: the per-chunk
-    path and the merge kernel)."""
-    B, msl = 160, 600
-    lens = [int(x) for x in torch.randint(1, 700, (B,), generator=torch.Generator().manual_seed(5))]
+@pytest.mark.parametrize("B,max_len,msl", [(160, 1400, 1200), (40, 4500, 4000)])
+def test_decode_work_queue_edges(B, max_len, msl):
+    """Past 4096 (sequence, kv head, chunk) items the decode wavefronts take
+    their work from a queue: whole sequences once there are enough (sequence,
+    kv head) pairs (160 x 8 here), otherwise groups of chunks whose partials
+    the merge kernel folds after the group-0 wavefront's running state (40 x 8
+    here, groups of 5 chunks).  Empty sequences, lengths clamped by max_seq_len
+    and a workspace full of garbage must give, for every request, bitwise what
+    decoding it alone gives (one request: one wavefront per chunk and the merge
+    kernel)."""
+    lens = [int(x) for x in torch.randint(1, max_len, (B,), generator=torch.Generator().manual_seed(5))]
     bt = Batch(range(B), lens, 32, 8, 128, 23)
     run_lens = list(lens)
-    for i in (0, 17, 159):
+    for i in (0, 17, B - 1):
         run_lens[i] = 0
     ws = torch.full((bi.bi_attn_decode_workspace_bytes(B, 32, 128, msl),), 255, dtype=torch.uint8, device=DEV)
     lt = torch.tensor(run_lens, dtype=torch.int32, device=DEV)
     out, lse = bt.decode(max_seq_len=msl, lens=lt, workspace=ws)
     clamped = [i for i in range(B) if run_lens[i] > msl]
     assert clamped, "some lengths exceed max_seq_len"
-    for i in (0, 17, 159, 1, 2, 80, 158, *clamped[:4]):
-        log_case(f"decode queue edges request {i} len {run_lens[i]}")
+    longest = sorted(range(B), key=lambda i: -min(run_lens[i], msl))[:3]
+    for i in (0, 17, B - 1, 1, 2, B // 2, B - 2, *clamped[:3], *longest):
+        log_case(f"decode queue edges B={B} request {i} len {run_lens[i]}")
         o1, l1 = bi.bi_attn_decode(bt.q[i:i + 1], bt.kc, bt.vc, bt.bt[i:i + 1], lt[i:i + 1], msl, bt.scale,
                                    lse=torch.empty((1, 32), dtype=torch.float32, device=DEV))
         assert_bitwise(out[i:i + 1], o1, f"request {i}: queue vs alone")
