@@ -404,6 +404,32 @@ def kernel_table(torch, bi, W, step, reps, everything):
                          extra={"B": B, "sum_L": sum(lens)}))
         del kc, vc
     torch.cuda.empty_cache()
+    # Long-context decode (32/8 heads, D 128): the tracked request at KV 32768
+    # co-batched with B - 1 requests of seeded lengths in [1, 32768].
+    n_long = 256
+    lens = [32768] + W.decode_lengths(range(1, n_long), W.SEED_LONG, 1, 32768)
+    pb = W.allocate_pages(lens, W.SEED_LONG)
+    kc, vc = bi.alloc_kv_cache(pb.num_pages, 8, 128, 16, dev, fill=0.0)
+    lo = 0
+    for r0 in range(0, n_long, 16):
+        part = range(r0, min(n_long, r0 + 16))
+        kv = [W.request_kv(r, lens[r], 8, 128, W.SEED_LONG, device=dev) for r in part]
+        hi = lo + sum(lens[r] for r in part)
+        bi.bi_kv_append(torch.cat([k for k, _ in kv]), torch.cat([v for _, v in kv]), pb.slot_mapping[lo:hi].to(dev),
+                        kc, vc)
+        lo = hi
+        del kv
+    q = W.randn_bf16((n_long, 32, 128), W.SEED_LONG, "q", 0, device=dev)
+    o = torch.empty_like(q)
+    btd, lt = pb.block_table.to(dev), torch.tensor(lens, dtype=torch.int32, device=dev)
+    ws = torch.empty((bi.bi_attn_decode_workspace_bytes(n_long, 32, 128, 32768),), dtype=torch.uint8, device=dev)
+    for B in (1, 16, 64, 256):
+        us = time_fn(torch, lambda i=0: bi.bi_attn_decode(q[:B], kc, vc, btd[:B], lt[:B], 32768, 1 / math.sqrt(128),
+                                                           out=o[:B], workspace=ws), max(5, reps // 4))
+        out.append(entry("attn decode long-context 32/8 D128", us, bytes_decode(lens[:B], 32, 8, 128),
+                         flops_decode(lens[:B], 32, 128), extra={"B": B, "sum_L": sum(lens[:B])}))
+    del kc, vc, q, o, ws
+    torch.cuda.empty_cache()
     return out
 
 

@@ -405,6 +405,8 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32
   if (tid == 0) *next = 0;
 }
 
+constexpr int kMergeBatch = 16;
+
 // Folds a sequence's records in ascending order: chunk 0's record, then
 // chunks cg, cg + 1, ..., C - 1 (cg = 1: every chunk's partial; cg > 1: chunk
 // 0's record holds the fold of chunks 0 .. cg - 1).  Sequences with C <= done
@@ -423,13 +425,31 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(
   float m = -INFINITY, l = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  for (int c = 0; c < C; c = (c == 0 ? cg : c + 1)) {
-    const float* rec = rec0 + (int64_t)c * (D + 4);
-    const MergeCoef k = merge_coef(m, rec[D]);
-    l = merge_val(l, rec[D + 1], k);
+  // The records folded, in order: t = 0 is chunk 0's, t >= 1 is chunk cg - 1 + t.
+  // They are loaded kMergeBatch at a time ahead of the fold, so a long
+  // sequence waits for one load latency per batch rather than per chunk; the
+  // fold itself runs record by record in the same order.
+  const int T = C > 0 ? 1 + max(0, C - cg) : 0;
+  for (int t0 = 0; t0 < T; t0 += kMergeBatch) {
+    float rm[kMergeBatch], rl[kMergeBatch], ra[kMergeBatch][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = merge_val(acc[e], rec[lane * E + e], k);
-    m = k.m;
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int t = min(t0 + j, T - 1);
+      const float* rec = rec0 + (int64_t)(t == 0 ? 0 : cg - 1 + t) * (D + 4);
+      rm[j] = rec[D];
+      rl[j] = rec[D + 1];
+#pragma unroll
+      for (int e = 0; e < E; ++e) ra[j][e] = rec[lane * E + e];
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      if (t0 + j >= T) break;
+      const MergeCoef k = merge_coef(m, rm[j]);
+      l = merge_val(l, rl[j], k);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = merge_val(acc[e], ra[j][e], k);
+      m = k.m;
+    }
   }
   uint16_t* op = out + ((int64_t)b * Hq + head) * D + lane * E;
   if (C > 0) {

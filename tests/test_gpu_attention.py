@@ -288,6 +288,39 @@ def test_decode_growing_cache_with_random_co_batch():
         assert_bitwise(l[pos], l1[0], f"tracked lse at L={L} with {k} co-batched")
 
 
+def test_decode_long_context_co_batch_invariance():
+    """The long-context workload at its size: one request at KV 32768 (and at
+    20001, a partial last chunk) decoded alone and among 15, 63 and 255 others
+    with seeded lengths in [1, 32768], at random slots.  The batches take every
+    scheduling path of bi_attn_decode (one wavefront per chunk; the work queue
+    with chunk groups and the merge; whole sequences), and the tracked output
+    and lse must be bitwise the same in all of them."""
+    hq, hkv, d, n_others = 32, 8, 128, 255
+    lens = [32768] + W.decode_lengths(range(1, n_others + 1), W.SEED_LONG, 1, 32768)
+    bt = Batch(range(n_others + 1), lens, hq, hkv, d, W.SEED_LONG, perm_index=3)
+    rng = np.random.default_rng(9)
+    for L in (32768, 20001):
+        ref = None
+        for B in (1, 16, 64, 256):
+            others = sorted(rng.choice(np.arange(1, n_others + 1), size=B - 1, replace=False).tolist())
+            pos = int(rng.integers(0, B))
+            ids = others[:pos] + [0] + others[pos:]
+            log_case(f"long-context decode L={L} B={B} slot={pos}")
+            idx = torch.tensor(ids, device=DEV)
+            lt = bt.lens[idx].clone()
+            lt[pos] = L
+            out, lse = bi.bi_attn_decode(bt.q[idx].contiguous(), bt.kc, bt.vc, bt.bt[idx].contiguous(), lt, 32768,
+                                         bt.scale, lse=torch.empty((B, hq), dtype=torch.float32, device=DEV))
+            got = (out[pos].clone(), lse[pos].clone())
+            if ref is None:
+                ref = got
+                ro, rl = O.decode_attention(f64(bt.q[:1]), [f64(bt.kv[0][0][:L])], [f64(bt.kv[0][1][:L])], bt.scale)
+                assert_bf16_close(got[0][None], ro, f"long-context L={L}")
+                assert_f32_close(got[1][None], rl, f"long-context lse L={L}")
+            assert_bitwise(got[0], ref[0], f"tracked output L={L} at B={B} slot={pos}")
+            assert_bitwise(got[1], ref[1], f"tracked lse L={L} at B={B} slot={pos}")
+
+
 # ---------------------------------------------------------------- prefill
 
 def _prefill_setup(prefixes, chunk_lens, hq=32, hkv=8, d=128, base=W.SEED_MIXED, perm_index=0):
