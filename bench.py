@@ -624,6 +624,7 @@ ONLY = {
     "lm-head-t2048": "fused lm_head + log_softmax, T=2048, vocab 151936",
     "layer-decode-b1": "Qwen3-8B-shaped decoder layer, decode of 1 request",
     "layer-decode-b256": "Qwen3-8B-shaped decoder layer, decode of 256 requests (the decode-step caches)",
+    "moe-t2048": "routed experts, 128 x (4096->1536->4096) top-8, T=2048",
 }
 
 
@@ -659,6 +660,15 @@ def run_only(torch, bi, W, what, reps):
         layer = DecoderLayer(step.w_qkv, w_o, w_gu, step.w_down, step.g1, step.g2, 32, 8, 128, EPS)
         fn = lambda: layer.decode(step.x, step.kc, step.vc, step.bt, step.lens_t, step.new_slots, step.max_len,
                                   workspace=step.ws)
+    elif what == "moe-t2048":
+        E, K8, F, T = 128, 8, 1536, 2048
+        w_up, w_down = W.moe_weights(E, 4096, F, W.SEED_MOE, device=dev)
+        x = W.rows_for_requests(range(T), 4096, W.SEED_MOE, device=dev)
+        ex, wt = W.moe_routing(range(T), E, K8, W.SEED_MOE)
+        ex, wt = ex.to(dev), wt.to(dev)
+        y = torch.empty((T, 4096), dtype=torch.bfloat16, device=dev)
+        mws = torch.empty((bi.moe_workspace_bytes(T, K8, E, 4096, F),), dtype=torch.uint8, device=dev)
+        fn = lambda: bi.bi_moe_ffn(x, ex, wt, w_up, w_down, out=y, workspace=mws)
     elif what == "rmsnorm-2300":
         x = W.rows_for_requests(range(2300), 4096, W.SEED_MIXED, device=dev)
         g = W.randn_bf16((4096,), W.SEED_MIXED, "gamma", W.WEIGHTS, std=0.1, mean=1.0, device=dev)
