@@ -284,6 +284,31 @@ def moe_ffn(x: np.ndarray, experts: np.ndarray, weights: np.ndarray,
     return y
 
 
+def moe_route(x: np.ndarray, w_gate: np.ndarray, top_k: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Token routing of a mixture-of-experts layer (workload support: the
+    Qwen3-235B-A22B-shaped layer; routing is not on the pages).
+
+    logits = x @ w_gate^T (x [T, H], w_gate [E, H]); every token takes the
+    top_k experts of largest logit, a larger logit first and, among equal
+    logits, the lower expert index first (reading: a fixed tie-break, so the
+    choice is a function of the token's logits alone); the weights are the
+    softmax of the chosen logits, i.e. the softmax over all experts restricted
+    to the chosen ones and renormalised.  Returns (experts [T, top_k] int64,
+    weights [T, top_k], logits [T, E]).
+    """
+    logits = gemm(x, w_gate)
+    T, E = logits.shape
+    experts = np.zeros((T, top_k), dtype=np.int64)
+    weights = np.zeros((T, top_k))
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-logits[t, e], e))[:top_k]
+        experts[t] = order
+        z = logits[t, order]
+        p = np.exp(z - z.max())
+        weights[t] = p / p.sum()
+    return experts, weights, logits
+
+
 # ---------------------------------------------------------------------------
 # One decoder layer (workload support; the pages describe no layer)
 # ---------------------------------------------------------------------------

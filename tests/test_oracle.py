@@ -317,6 +317,51 @@ def test_moe_routing_and_weighting():
 
 # ---------------------------------------------------------------- decoder layer (composition)
 
+def test_moe_route_closed_forms():
+    # Equal logits: the tie-break takes the lowest expert indices, weights 1/k.
+    x = np.ones((2, 4))
+    experts, weights, logits = O.moe_route(x, np.zeros((16, 4)), 8)
+    assert experts.tolist() == [list(range(8))] * 2
+    assert np.array_equal(weights, np.full((2, 8), 1 / 8))
+    assert np.array_equal(logits, np.zeros((2, 16)))
+    # One-hot token and gate rows c_e e_0: logits are c_e; the top 3 of
+    # c = [0, 5, -1, 5, 2] are experts 1, 3 (tie, lower index first), 4.
+    c = np.array([0.0, 5.0, -1.0, 5.0, 2.0])
+    w_gate = np.zeros((5, 3))
+    w_gate[:, 0] = c
+    experts, weights, _ = O.moe_route(np.array([[1.0, 0.0, 0.0]]), w_gate, 3)
+    assert experts[0].tolist() == [1, 3, 4]
+    z = np.exp(np.array([5.0, 5.0, 2.0]) - 5.0)
+    assert np.allclose(weights[0], z / z.sum(), rtol=0, atol=1e-15)
+    # Two experts: the weights are the logistic function of the logit gap.
+    experts, weights, _ = O.moe_route(np.array([[2.0]]), np.array([[0.25], [1.0]]), 2)
+    assert experts[0].tolist() == [1, 0]
+    assert abs(weights[0, 0] - 1 / (1 + math.exp(-1.5))) < 1e-15
+
+
+def test_moe_route_brute_force():
+    # Small integer inputs: exact logits; the chosen set is the k-subset of
+    # largest logit sum with the lexicographically smallest indices among ties,
+    # listed by (-logit, index); found here by enumerating every k-subset.
+    import itertools
+    rng = np.random.default_rng(11)
+    for _ in range(30):
+        E, k, H = int(rng.integers(3, 9)), int(rng.integers(1, 4)), 3
+        x = rng.integers(-2, 3, (1, H)).astype(float)
+        w = rng.integers(-2, 3, (E, H)).astype(float)
+        lg = (w @ x[0])
+        best = None
+        for sub in itertools.combinations(range(E), k):
+            key = (-sum(lg[list(sub)]), sorted(sub))
+            if best is None or key < best[0]:
+                best = (key, sub)
+        want = sorted(best[1], key=lambda e: (-lg[e], e))
+        experts, weights, logits = O.moe_route(x, w, k)
+        assert np.array_equal(logits[0], lg)
+        assert experts[0].tolist() == want, (lg, experts[0], want)
+        assert abs(weights[0].sum() - 1.0) < 1e-12 and np.all(np.diff(weights[0]) <= 0)
+
+
 def test_silu_mul_halves_and_closed_form():
     # g = ln 3 -> silu = 0.75 ln 3; the first half gates, the second multiplies
     gu = np.array([[math.log(3.0), 0.0, 2.0, 5.0]])
