@@ -369,6 +369,7 @@ def kernel_table(torch, bi, W, step, reps, everything):
     # uses another routing set, so repeats cannot be served from the Infinity Cache.
     E, K8, F = 128, 8, 1536
     w_up, w_down = W.moe_weights(E, 4096, F, W.SEED_MOE, device=dev)
+    w_gate = W.randn_bf16((E, 4096), W.SEED_MOE, "gate", W.WEIGHTS, std=0.02, device=dev)
     for T in (1, 64, 512, 2048):
         sets = 16 if T == 1 else 2
         xs, rts = [], []
@@ -384,8 +385,29 @@ def kernel_table(torch, bi, W, step, reps, everything):
         nbytes = sum(bytes_moe(r[2].numpy(), E, 4096, F) for r in rts) / sets
         out.append(entry("moe experts 128x(4096->1536->4096) top-8", us, nbytes, flops_moe(T, K8, 4096, F),
                          extra={"T": T}))
-        del xs, rts, y, mws
-    del w_up, w_down
+        # The router (gate GEMM 4096->128 with fp32 logits, top-8, softmax weights),
+        # and router + experts as one routed layer.
+        ids_r = torch.empty((T, K8), dtype=torch.int32, device=dev)
+        wts_r = torch.empty((T, K8), dtype=torch.float32, device=dev)
+        lg_r = torch.empty((T, E), dtype=torch.float32, device=dev)
+        us = time_fn(torch, lambda i=0: bi.bi_moe_route(xs[i % sets], w_gate, K8, logits=lg_r, expert_ids=ids_r,
+                                                         expert_weights=wts_r), max(5, reps // 4))
+        out.append(entry("moe router 4096->128 top-8", us, 2 * (T * 4096 + E * 4096) + 4 * T * E + 8 * T * K8,
+                         flops_gemm(T, E, 4096), extra={"T": T}))
+
+        def routed(i=0):
+            bi.bi_moe_route(xs[i % sets], w_gate, K8, logits=lg_r, expert_ids=ids_r, expert_weights=wts_r)
+            bi.bi_moe_ffn(xs[i % sets], ids_r, wts_r, w_up, w_down, out=y, workspace=mws)
+
+        routed()
+        torch.cuda.synchronize()
+        used = ids_r.cpu().numpy()
+        us = time_fn(torch, routed, max(5, reps // 4))
+        out.append(entry("moe layer routed (router + experts)", us,
+                         bytes_moe(used, E, 4096, F) + 2 * E * 4096 + 4 * T * E, flops_moe(T, K8, 4096, F)
+                         + flops_gemm(T, E, 4096), extra={"T": T}))
+        del xs, rts, y, mws, ids_r, wts_r, lg_r
+    del w_up, w_down, w_gate
     torch.cuda.empty_cache()
     for B in (1, 64, 256):
         lens = W.decode_lengths(range(B), W.SEED_MOE)

@@ -230,6 +230,34 @@ bi_status bi_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, c
  * outputs; about num_tokens * top_k * (2 * ffn + 4 * hidden) bytes); else
  * BI_ERR_WORKSPACE.
  */
+/*
+ * Router of the mixture-of-experts layer (workload support, the Qwen3-235B-
+ * A22B-shaped layer: 128 experts, top-8; routing is not on the pages, and the
+ * invariance rule is [BINR]'s answer on a fixed per-element reduction order
+ * regardless of batch size or position in the batch).
+ *   logits[t, e]         = sum_k x[t, k] w_gate[e, k]      (bi_gemm, fp32 out)
+ *   expert_ids[t, s]     = the s-th expert in the order: larger logit first,
+ *                          lower expert index first among equal logits (a NaN
+ *                          logit counts below every number), s < top_k
+ *   expert_weights[t, s] = e_s / sum_{j < top_k} e_j,  e_s = exp(l_s - l_0),
+ *                          l_s the logit of expert_ids[t, s], the sum in fp32
+ *                          in slot order
+ * The order is total, so the choice is a function of the token's logits alone
+ * (and those are bi_gemm's, batch-invariant); the slot order is the order
+ * bi_moe_ffn sums the experts in.
+ * x: [num_tokens, hidden] bf16, row stride ldx (ldx % 8 == 0, 16-byte aligned);
+ * w_gate: [num_experts, hidden] bf16, contiguous, 16-byte aligned;
+ * logits: [num_tokens, num_experts] fp32, contiguous (written);
+ * expert_ids: [num_tokens, top_k] int32 and expert_weights: [num_tokens, top_k]
+ *   fp32, contiguous.  All outputs are owned by the caller.
+ * 1 <= top_k <= num_experts (else BI_ERR_INVALID_ARG); top_k <= 64,
+ * num_experts <= 1024 and hidden % 32 == 0 (else BI_ERR_UNSUPPORTED);
+ * num_tokens == 0 is a no-op.
+ */
+bi_status bi_moe_route(const void* x, int64_t ldx, const void* w_gate, int32_t num_tokens, int32_t hidden,
+                       int32_t num_experts, int32_t top_k, float* logits, int32_t* expert_ids, float* expert_weights,
+                       bi_stream_t stream);
+
 size_t bi_moe_workspace_bytes(int32_t num_tokens, int32_t top_k, int32_t num_experts,
                               int32_t hidden, int32_t ffn);
 bi_status bi_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids, const float* expert_weights,

@@ -38,6 +38,7 @@ _SIGNATURES = {
                                  _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p]),
     "bi_log_softmax": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_moe_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "bi_moe_route": (_c_i32, [_c_p, _c_i64, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p]),
     "bi_moe_ffn": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_i32,
                             _c_p, _c_i64, _c_p, _c_size, _c_p]),
     "bi_lm_head_logprobs_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
@@ -328,6 +329,36 @@ def bi_moe_ffn(x: torch.Tensor, expert_ids: torch.Tensor, expert_weights: torch.
                                           H, F, out.data_ptr(), _rows(out, "out"), workspace.data_ptr(),
                                           workspace.numel(), _stream(stream)))
     return out
+
+
+def bi_moe_route(x: torch.Tensor, w_gate: torch.Tensor, top_k: int, logits: Optional[torch.Tensor] = None,
+                 expert_ids: Optional[torch.Tensor] = None, expert_weights: Optional[torch.Tensor] = None,
+                 stream=None):
+    """x [T, H] bf16; w_gate [E, H] bf16 -> (expert_ids [T, top_k] int32,
+    expert_weights [T, top_k] fp32, logits [T, E] fp32)."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(w_gate, "w_gate", torch.bfloat16)
+    T, H = x.shape
+    E, H2 = w_gate.shape
+    if H2 != H or not w_gate.is_contiguous():
+        raise ValueError("w_gate must be a contiguous [E, H] tensor")
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    if expert_ids is None:
+        expert_ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
+    if expert_weights is None:
+        expert_weights = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
+    _dev(logits, "logits", torch.float32)
+    _dev(expert_ids, "expert_ids", torch.int32)
+    _dev(expert_weights, "expert_weights", torch.float32)
+    for t, name, shape in ((logits, "logits", (T, E)), (expert_ids, "expert_ids", (T, top_k)),
+                           (expert_weights, "expert_weights", (T, top_k))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {shape} tensor")
+    _check("bi_moe_route", lib().bi_moe_route(x.data_ptr(), _rows(x, "x"), w_gate.data_ptr(), T, H, E, top_k,
+                                              logits.data_ptr(), expert_ids.data_ptr(), expert_weights.data_ptr(),
+                                              _stream(stream)))
+    return expert_ids, expert_weights, logits
 
 
 def lm_head_logprobs_workspace_bytes(m: int, n: int) -> int:

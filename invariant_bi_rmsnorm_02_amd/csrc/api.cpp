@@ -217,6 +217,25 @@ bi_status bi_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids, cons
                                      w_down, hidden, ffn, y, ldy, workspace, as_stream(stream)));
 }
 
+bi_status bi_moe_route(const void* x, int64_t ldx, const void* w_gate, int32_t num_tokens, int32_t hidden,
+                       int32_t num_experts, int32_t top_k, float* logits, int32_t* expert_ids, float* expert_weights,
+                       bi_stream_t stream) {
+  if (num_tokens < 0 || hidden <= 0 || num_experts <= 0 || top_k <= 0 || top_k > num_experts)
+    return BI_ERR_INVALID_ARG;
+  if (top_k > 64 || num_experts > 1024) return BI_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return BI_OK;
+  if (!x || !w_gate || !logits || !expert_ids || !expert_weights) return BI_ERR_INVALID_ARG;
+  if (hidden % 32) return BI_ERR_UNSUPPORTED;
+  if (ldx < hidden || ldx % 8) return BI_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_gate)) return BI_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(expert_ids) & 3u) ||
+      (reinterpret_cast<uintptr_t>(expert_weights) & 3u))
+    return BI_ERR_INVALID_ARG;
+  if (!bi::gemm_supported(ldx, hidden, num_tokens, num_experts, hidden)) return BI_ERR_UNSUPPORTED;
+  return from_hip(bi::launch_moe_route(x, ldx, w_gate, num_tokens, hidden, num_experts, top_k, logits, expert_ids,
+                                       expert_weights, as_stream(stream)));
+}
+
 size_t bi_lm_head_logprobs_workspace_bytes(int64_t m, int64_t n) {
   if (m <= 0 || n <= 0) return 0;
   return bi::lm_head_workspace_bytes(m, n);

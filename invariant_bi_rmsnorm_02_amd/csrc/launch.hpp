@@ -54,6 +54,11 @@ hipError_t launch_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids,
                           int T, int top_k, int E, const void* w_up, const void* w_down, int H, int F, void* y,
                           int64_t ldy, void* workspace, hipStream_t stream);
 
+// Router of the MoE layer: fp32 logits with the library GEMM, then the top-k
+// experts and their softmax weights per token (moe.hip).
+hipError_t launch_moe_route(const void* x, int64_t ldx, const void* w_gate, int T, int H, int E, int top_k,
+                            float* logits, int32_t* expert_ids, float* expert_weights, hipStream_t stream);
+
 // lm_head + log_softmax fused into the GEMM epilogue (lm_head.hip).
 size_t lm_head_workspace_bytes(int64_t m, int64_t n);
 size_t lm_head_greedy_workspace_bytes(int64_t m, int64_t n);

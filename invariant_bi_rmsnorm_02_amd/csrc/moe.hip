@@ -20,7 +20,15 @@
 //     the batch decides) changes which workgroup computes it, not how.
 //  4. moe_combine_kernel (one workgroup per token): fp32 sum over s ascending
 //     of w[t, s] * o[pos[t, s]], rounded once to bf16.
+//
+// The router (bi_moe_route) feeds it: logits = x W_gate^T with the library
+// GEMM (fp32 out), then moe_topk_kernel (one wavefront per token) picks the
+// top_k experts in a total order - the larger logit first, the lower expert
+// index among equal logits, a NaN logit below every number - so the choice
+// depends on the token's logits alone and not on any reduction order; the
+// weights are the softmax of the chosen logits, summed in slot order.
 #include <algorithm>
+#include <climits>
 
 #include "gemm_kernel.hpp"
 #include "launch.hpp"
@@ -223,6 +231,62 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   }
 }
 
+// Top-k of one token's router logits.  Lane l holds experts l, l + 64, ...
+// (PER of them).  Round s: every lane offers its best remaining expert, a
+// butterfly over the wavefront keeps the better of each pair - the larger key,
+// or the lower index on equal keys: a total order, so the winner is the same
+// whatever the pairing - and the winner's lane marks it taken.  Then lane 0
+// forms the weights: e_s = 2^((l_s - l_0) log2 e), their fp32 sum in slot
+// order, w_s = e_s / sum.
+template <int PER>
+__global__ __launch_bounds__(64) void moe_topk_kernel(const float* __restrict__ logits, int E, int top_k,
+                                                      int32_t* __restrict__ ids, float* __restrict__ wts) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const float* lr = logits + (int64_t)t * E;
+  float key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    const float v = e < E ? lr[e] : -INFINITY;
+    key[i] = (e < E && !__builtin_isnan(v)) ? v : -INFINITY;
+  }
+  uint32_t taken = 0;
+  __shared__ int chosen[64];
+  for (int s = 0; s < top_k; ++s) {
+    float bv = -INFINITY;
+    int bi_ = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i;
+      const bool ok = e < E && !((taken >> i) & 1u);
+      if (ok && (key[i] > bv || (key[i] == bv && e < bi_))) {
+        bv = key[i];
+        bi_ = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi_, o, kWave);
+      if (ov > bv || (ov == bv && oi < bi_)) {
+        bv = ov;
+        bi_ = oi;
+      }
+    }
+    if (bi_ != INT_MAX && (bi_ & 63) == lane) taken |= 1u << (bi_ >> 6);
+    if (lane == 0) chosen[s] = bi_;
+  }
+  if (lane == 0) {
+    const float l0 = lr[chosen[0]];
+    float sum = 0.0f;
+    for (int s = 0; s < top_k; ++s) sum = sum + exp2_hw((lr[chosen[s]] - l0) * kLog2e);
+    for (int s = 0; s < top_k; ++s) {
+      ids[(int64_t)t * top_k + s] = chosen[s];
+      wts[(int64_t)t * top_k + s] = exp2_hw((lr[chosen[s]] - l0) * kLog2e) / sum;
+    }
+  }
+}
+
 }  // namespace
 
 size_t moe_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t H, int64_t F) {
@@ -272,6 +336,25 @@ hipError_t launch_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids,
                      (int64_t)H * F, offsets, tiles, src, E, H, F, tn_down, static_cast<void*>(o));
   hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(256), 0, stream, o, pos, expert_weights, top_k, H,
                      static_cast<uint16_t*>(y), ldy);
+  return hipGetLastError();
+}
+
+}  // namespace bi
+
+namespace bi {
+
+hipError_t launch_moe_route(const void* x, int64_t ldx, const void* w_gate, int T, int H, int E, int top_k,
+                            float* logits, int32_t* expert_ids, float* expert_weights, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  hipError_t e = launch_gemm(x, ldx, w_gate, H, logits, E, true, T, E, H, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>(T)), block(64);
+  if (E <= 64)
+    hipLaunchKernelGGL(moe_topk_kernel<1>, grid, block, 0, stream, logits, E, top_k, expert_ids, expert_weights);
+  else if (E <= 256)
+    hipLaunchKernelGGL(moe_topk_kernel<4>, grid, block, 0, stream, logits, E, top_k, expert_ids, expert_weights);
+  else
+    hipLaunchKernelGGL(moe_topk_kernel<16>, grid, block, 0, stream, logits, E, top_k, expert_ids, expert_weights);
   return hipGetLastError();
 }
 

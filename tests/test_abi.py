@@ -45,6 +45,15 @@ def test_host_validation_without_gpu(lib):
     assert moe(4, 4096, ctypes.c_void_p(256), 16) == bi.BI_ERR_WORKSPACE
     assert moe(0, 4096, None, 0) == bi.BI_OK
     assert lib.bi_moe_workspace_bytes(2048, 8, 128, 4096, 1536) >= 2048 * 8 * (2 * 1536 + 4 * 4096)
+    # MoE router: top_k above the experts, too many experts, hidden not a multiple of 32, empty batch
+    route = lambda T, H, E, k: lib.bi_moe_route(P, H, P, T, H, E, k, P, P, P, None)
+    assert route(4, 4096, 8, 9) == bi.BI_ERR_INVALID_ARG
+    assert route(4, 4096, 2048, 8) == bi.BI_ERR_UNSUPPORTED
+    assert route(4, 4096, 128, 65) == bi.BI_ERR_UNSUPPORTED
+    assert route(4, 4016, 128, 8) == bi.BI_ERR_UNSUPPORTED
+    assert route(4, 4096, 128, 0) == bi.BI_ERR_INVALID_ARG
+    assert route(0, 4096, 128, 8) == bi.BI_OK
+    assert lib.bi_moe_route(None, 4096, P, 4, 4096, 128, 8, P, P, P, None) == bi.BI_ERR_INVALID_ARG
     # a 64-row slice of W spanning 2^31 bytes cannot be addressed by one buffer resource
     assert lib.bi_gemm(P, 64, P, 1 << 25, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_UNSUPPORTED
     assert lib.bi_gemm(P, 1 << 25, P, 64, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_UNSUPPORTED

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import workloads as W
-from _helpers import O, assert_bf16_close, assert_bitwise, bi, ensure_lib, f64, log_case
+from _helpers import O, assert_bf16_close, assert_bitwise, assert_f32_close, bi, ensure_lib, f64, log_case
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -143,3 +143,104 @@ def test_moe_errors():
         bi.bi_moe_ffn(bad_h, ids, wt, torch.zeros((E, F, 48), dtype=torch.bfloat16, device=DEV),
                       torch.zeros((E, 48, F), dtype=torch.bfloat16, device=DEV))
     assert e.value.status == bi.BI_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- the router (bi_moe_route)
+
+def _gate(E=E_FULL, H=H_FULL):
+    return W.randn_bf16((E, H), W.SEED_MOE, "gate", W.WEIGHTS, std=0.02)
+
+
+def _order(lg, k):
+    """Top-k of every row of lg in the router's order: larger first, lower index on ties."""
+    return np.array([sorted(range(lg.shape[1]), key=lambda e: (-lg[t, e], e))[:k] for t in range(lg.shape[0])])
+
+
+@pytest.mark.parametrize("T", [1, 37, 300])
+def test_moe_route_parity(T):
+    """Logits against the oracle (fp32 absolute); the choice - an integer decided
+    by floating point - exactly equal to the order of the library's own fp32
+    logits, and equal to the oracle's where its top k + 1 logits are clearly
+    apart; the weights against the oracle's softmax of its logits of the chosen
+    experts."""
+    log_case(f"moe route parity T={T}")
+    x, wg = W.rows_for_requests(range(T), H_FULL, W.SEED_MOE), _gate()
+    ids, wts, logits = bi.bi_moe_route(x.to(DEV), wg.to(DEV), K_FULL)
+    ref_ids, ref_w, ref_lg = O.moe_route(f64(x), f64(wg), K_FULL)
+    assert_f32_close(logits, ref_lg, f"router logits T={T}")
+    ids_np, lg = ids.cpu().numpy(), logits.cpu().double().numpy()
+    assert np.array_equal(ids_np, _order(lg, K_FULL)), "choice = order of the library's fp32 logits"
+    top = -np.sort(-ref_lg, axis=1)[:, :K_FULL + 1]
+    clear = np.all(-np.diff(top, axis=1) > 1e-3, axis=1)
+    assert clear.sum() >= max(1, T // 2)
+    assert np.array_equal(ids_np[clear], ref_ids[clear]), "choice = oracle's where the logits are apart"
+    for t in range(T):
+        z = ref_lg[t, ids_np[t]]
+        p = np.exp(z - z.max())
+        assert np.max(np.abs(wts[t].cpu().double().numpy() - p / p.sum())) <= 1e-3
+    assert np.allclose(wts.cpu().double().numpy().sum(axis=1), 1.0, atol=1e-6)
+
+
+def test_moe_route_ties_and_closed_forms():
+    x = W.rows_for_requests(range(5), 512, W.SEED_MOE).to(DEV)
+    # A zero gate: every logit is 0, so experts 0..7 by the tie-break, weights exactly 1/8.
+    ids, wts, lg = bi.bi_moe_route(x, torch.zeros((128, 512), dtype=torch.bfloat16, device=DEV), 8)
+    assert torch.equal(ids.cpu(), torch.arange(8, dtype=torch.int32).repeat(5, 1))
+    assert torch.equal(wts.cpu(), torch.full((5, 8), 0.125))
+    assert torch.equal(lg.cpu(), torch.zeros((5, 128)))
+    # Expert e + 64 repeats expert e's gate row: bitwise equal logits, so every
+    # chosen expert e is followed by e + 64, with the same weight.
+    g = W.randn_bf16((64, 512), W.SEED_MOE, "gate", 77, std=0.05).to(DEV)
+    ids, wts, lg = bi.bi_moe_route(x, torch.cat([g, g]).contiguous(), 8)
+    assert_bitwise(lg[:, :64], lg[:, 64:], "duplicated gate rows")
+    ids = ids.cpu()
+    assert torch.equal(ids[:, 0::2] + 64, ids[:, 1::2]), ids
+    assert torch.all(ids[:, 0::2] < 64)
+    assert_bitwise(wts[:, 0::2], wts[:, 1::2], "tied weights")
+    # E = 5, top_k = 5: every expert, in logit order.
+    ids, wts, lg = bi.bi_moe_route(x, g[:5].contiguous(), 5)
+    assert np.array_equal(ids.cpu().numpy(), _order(lg.cpu().double().numpy(), 5))
+
+
+def test_moe_route_batch_invariance():
+    """Token 0's logits, choice and weights: bitwise the same at T = 1, 64, 512
+    and shuffled positions."""
+    wg = _gate().to(DEV)
+    ref = None
+    for T, slot in ((1, 0), (64, 37), (512, 300), (512, 0)):
+        log_case(f"moe route invariance T={T} slot={slot}")
+        others = list(range(1, T))
+        ids_ = others[:slot] + [0] + others[slot:]
+        x = W.rows_for_requests(ids_, H_FULL, W.SEED_MOE, device=DEV)
+        ids, wts, lg = bi.bi_moe_route(x, wg, K_FULL)
+        got = (ids[slot].clone(), wts[slot].clone(), lg[slot].clone())
+        if ref is None:
+            ref = got
+        for a, b, what in zip(got, ref, ("ids", "weights", "logits")):
+            assert_bitwise(a, b, f"token 0 {what} at T={T} slot={slot}")
+
+
+def test_moe_layer_routed_invariance_and_parity(full_weights):
+    """The whole routed layer (bi_moe_route then bi_moe_ffn): token 0's output
+    bitwise the same at T = 1, 64, 512; and against the oracle's routed layer
+    on tokens whose routing is clear."""
+    w_up, w_down = full_weights
+    wg = _gate().to(DEV)
+    ref = None
+    for T, slot in ((1, 0), (64, 10), (512, 411)):
+        log_case(f"routed moe layer T={T} slot={slot}")
+        others = list(range(1, T))
+        ids_ = others[:slot] + [0] + others[slot:]
+        x = W.rows_for_requests(ids_, H_FULL, W.SEED_MOE, device=DEV)
+        ids, wts, _ = bi.bi_moe_route(x, wg, K_FULL)
+        y = bi.bi_moe_ffn(x, ids, wts, w_up, w_down)
+        if ref is None:
+            ref = y[slot].clone()
+            ex, rw, rl = O.moe_route(f64(x[:1]), f64(wg), K_FULL)
+            ex = ex[0].tolist()
+            assert ids[0].cpu().tolist() == ex
+            ups = [f64(w_up[e]) for e in ex]
+            downs = [f64(w_down[e]) for e in ex]
+            yr = O.moe_ffn(f64(x[:1]), np.arange(K_FULL)[None, :], rw, ups, downs)
+            assert_bf16_close(y[:1], yr, "routed layer vs oracle")
+        assert_bitwise(y[slot], ref, f"routed layer token 0 at T={T} slot={slot}")

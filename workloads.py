@@ -23,7 +23,7 @@ import torch
 
 WEIGHTS = 999_983          # request id reserved for weight tensors
 _KINDS = {"x": 1, "gamma": 2, "w": 3, "q": 4, "k": 5, "v": 6, "len": 7, "perm": 8,
-          "route": 9, "logits": 10, "misc": 11}
+          "route": 9, "logits": 10, "misc": 11, "gate": 12}
 
 PAGE = 16                  # KV page size (tokens per page)
 
