@@ -589,6 +589,29 @@ def test_decode_work_queue_edges(B, max_len, msl):
     assert_bitwise(again, out, "queue: repeat with the workspace left by the previous call")
 
 
+@pytest.mark.parametrize("B,hq,hkv,d,ps,max_len", [(40, 8, 8, 64, 32, 3000), (300, 16, 1, 128, 256, 2000),
+                                                   (130, 64, 4, 128, 64, 4096), (600, 4, 2, 64, 16, 1000)])
+def test_decode_queue_geometries(B, hq, hkv, d, ps, max_len):
+    """The work-queue paths (whole sequences, chunk groups + merge) across head
+    sizes, group sizes 1..16 and page sizes 16..256: every request of the batch
+    bitwise equal to decoding it alone (the per-chunk path), and sampled
+    requests against the oracle."""
+    lens = [int(x) for x in torch.randint(1, max_len + 1, (B,), generator=torch.Generator().manual_seed(B + d))]
+    bt = Batch(range(B), lens, hq, hkv, d, 31, page_size=ps)
+    log_case(f"decode queue geometry B={B} {hq}/{hkv} D={d} page={ps}")
+    out, lse = bt.decode(max_seq_len=max_len)
+    for i in range(B):
+        o1, l1 = bi.bi_attn_decode(bt.q[i:i + 1], bt.kc, bt.vc, bt.bt[i:i + 1], bt.lens[i:i + 1], max_len, bt.scale,
+                                   lse=torch.empty((1, hq), dtype=torch.float32, device=DEV))
+        assert_bitwise(out[i:i + 1], o1, f"request {i} (L={lens[i]}): batch vs alone")
+        assert_bitwise(lse[i:i + 1], l1, f"request {i} lse: batch vs alone")
+    longest = max(range(B), key=lambda i: lens[i])
+    for i in (0, longest):
+        ro, rl = bt.oracle([i])
+        assert_bf16_close(out[i], ro[0], f"request {i} vs oracle")
+        assert_f32_close(lse[i:i + 1], rl, f"request {i} lse vs oracle")
+
+
 def test_attention_errors():
     bt = Batch([0], [10], 32, 8, 128, 22)
     with pytest.raises(bi.BiError) as e:
