@@ -90,6 +90,29 @@ def test_lm_head_logprobs_batch_invariance():
             assert_bitwise(row, ref, f"token 0 logprobs at T={T} slot={pos}")
 
 
+def test_lm_head_full_vocab_batch_invariance():
+    """The lm_head at the workload's size (4096 -> 151936, the wide tile):
+    token 0's logprobs row, greedy token and token logprob bitwise the same at
+    T = 1, 64, 512, 2048 and shuffled slots."""
+    w = _weights(V)
+    ref = gref = None
+    for T, pos in ((1, 0), (64, 50), (512, 0), (2048, 1500)):
+        log_case(f"full-vocab lm_head invariance T={T} slot={pos}")
+        ids = list(range(1, T))
+        ids.insert(pos, 0)
+        a = W.rows_for_requests(ids, K, W.SEED_MOE, device=DEV)
+        row = bi.bi_lm_head_logprobs(a, w)[pos].clone()
+        tok, lp = bi.bi_lm_head_greedy(a, w, logprob=torch.empty(T, dtype=torch.float32, device=DEV))
+        got = (int(tok[pos]), lp[pos].clone())
+        torch.cuda.empty_cache()
+        if ref is None:
+            ref, gref = row, got
+        assert_bitwise(row, ref, f"token 0 logprobs at T={T} slot={pos}")
+        assert got[0] == gref[0], f"greedy token of request 0 at T={T} slot={pos}"
+        assert_bitwise(got[1], gref[1], f"greedy logprob of request 0 at T={T} slot={pos}")
+    assert_bitwise(ref[gref[0]:gref[0] + 1], gref[1].reshape(1), "greedy logprob == logprobs row at the token")
+
+
 def test_lm_head_logprobs_matches_two_calls():
     """Same mathematics as bi_gemm (fp32) + bi_log_softmax; a different fixed
     reduction tree for lse, so equal to rounding, not to the bit."""
