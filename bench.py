@@ -310,11 +310,20 @@ def kernel_table(torch, bi, W, step, reps, everything):
         us = time_fn(torch, lambda i=0: bi.bi_gemm(src, w, out=c), max(5, reps // 2))
         out.append(entry(name, us, bytes_gemm(M, n, k), flops_gemm(M, n, k), extra={"M": M}))
     del a, a2
-    xr = W.rows_for_requests(range(M), 4096, W.SEED_MIXED, device=dev)
-    yr = torch.empty_like(xr)
-    us = time_fn(torch, lambda i=0: bi.bi_rmsnorm(xr, step.g1, EPS, out=yr), reps)
+    # RMSNorm over the mixed batch's rows, rotating through copies (> 768 MB in
+    # all) so that the Infinity Cache cannot serve repeats, and beside it a plain
+    # device copy moving the same bytes the same way: the floor for a pass of
+    # this size.
+    x0 = W.rows_for_requests(range(M), 4096, W.SEED_MIXED, device=dev)
+    ncp = (768 << 20) // x0.nbytes + 1
+    xr = [x0] + [x0.clone() for _ in range(ncp - 1)]
+    yr = [torch.empty_like(x0) for _ in range(ncp)]
+    us = time_fn(torch, lambda i=0: bi.bi_rmsnorm(xr[i % ncp], step.g1, EPS, out=yr[i % ncp]), reps)
     out.append(entry("rmsnorm [2300,4096]", us, bytes_rmsnorm(M, 4096), extra={"rows": M}))
-    del xr, yr
+    us = time_fn(torch, lambda i=0: yr[i % ncp].copy_(xr[(i + 1) % ncp]), reps)
+    out.append(entry("device copy, the bytes of rmsnorm [2300,4096] (floor)", us, 4 * M * 4096,
+                     extra={"rows": M, "kind": "torch copy_, not a library kernel"}))
+    del x0, xr, yr
     prefixes = [W.rand_int(0, 8192, W.SEED_MIXED, "len", 100 + s) for s in range(4)]
     chunks = [512] * 4
     total = [p + n for p, n in zip(prefixes, chunks)]
