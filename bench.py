@@ -288,13 +288,19 @@ def kernel_table(torch, bi, W, step, reps, everything):
         us = time_fn(torch, lambda i=0: bi.bi_gemm(up, wd[i % len(wd)], out=down), reps)
         out.append(entry("gemm down 12288->4096", us, bytes_gemm(B, 4096, 12288), flops_gemm(B, 4096, 12288),
                          extra=tag))
-        q = step.q[:B]
+        # Each repetition decodes another group of B requests (step.B // B
+        # disjoint groups, 2.1 GB of KV together), so the Infinity Cache cannot
+        # serve repeats; bytes and flops are the groups' mean.
+        ng = max(1, step.B // B)
+        grp = [slice(j * B, (j + 1) * B) for j in range(ng)]
         attn, lse = step.attn[:B], step.lse[:B]
-        bt, lt = step.bt[:B], step.lens_t[:B]
-        us = time_fn(torch, lambda i=0: bi.bi_attn_decode(q, step.kc, step.vc, bt, lt, 4096, step.scale, out=attn,
+        us = time_fn(torch, lambda i=0: bi.bi_attn_decode(step.q[grp[i % ng]], step.kc, step.vc, step.bt[grp[i % ng]],
+                                                           step.lens_t[grp[i % ng]], 4096, step.scale, out=attn,
                                                            lse=lse, workspace=step.ws), reps)
-        out.append(entry("attn decode 32/8 D128", us, bytes_decode(lens, 32, 8, 128), flops_decode(lens, 32, 128),
-                         extra=dict(tag, sum_L=sum(lens))))
+        glens = [step.lens[sl] for sl in grp]
+        out.append(entry("attn decode 32/8 D128", us, sum(bytes_decode(g, 32, 8, 128) for g in glens) / ng,
+                         sum(flops_decode(g, 32, 128) for g in glens) / ng,
+                         extra=dict(tag, sum_L=sum(map(sum, glens)) / ng, groups=ng)))
     del wq, wu, wd
     if not everything:
         return out
@@ -418,22 +424,31 @@ def kernel_table(torch, bi, W, step, reps, everything):
         del xs, rts, y, mws, ids_r, wts_r, lg_r
     del w_up, w_down, w_gate
     torch.cuda.empty_cache()
-    for B in (1, 64, 256):
-        lens = W.decode_lengths(range(B), W.SEED_MOE)
-        pb = W.allocate_pages(lens, W.SEED_MOE)
-        kc, vc = bi.alloc_kv_cache(pb.num_pages, 4, 128, 16, dev, fill=0.0)
-        kv = [W.request_kv(r, L, 4, 128, W.SEED_MOE, device=dev) for r, L in enumerate(lens)]
-        bi.bi_kv_append(torch.cat([k for k, _ in kv]), torch.cat([v for _, v in kv]), pb.slot_mapping.to(dev), kc, vc)
+    # 235B-shaped decode (64/4 heads): 256 requests' caches; a repetition at
+    # batch B decodes another of 256 // B disjoint groups (bytes: the mean).
+    lens = W.decode_lengths(range(256), W.SEED_MOE)
+    pb = W.allocate_pages(lens, W.SEED_MOE)
+    kc, vc = bi.alloc_kv_cache(pb.num_pages, 4, 128, 16, dev, fill=0.0)
+    for r0 in range(0, 256, 64):
+        kv = [W.request_kv(r, lens[r], 4, 128, W.SEED_MOE, device=dev) for r in range(r0, r0 + 64)]
+        lo = sum(lens[:r0])
+        bi.bi_kv_append(torch.cat([k for k, _ in kv]), torch.cat([v for _, v in kv]),
+                        pb.slot_mapping[lo:lo + sum(lens[r0:r0 + 64])].to(dev), kc, vc)
         del kv
-        q = W.randn_bf16((B, 64, 128), W.SEED_MOE, "q", 0, device=dev)
-        o = torch.empty_like(q)
-        btd, lt = pb.block_table.to(dev), torch.tensor(lens, dtype=torch.int32, device=dev)
-        ws = torch.empty((bi.bi_attn_decode_workspace_bytes(B, 64, 128, 4096),), dtype=torch.uint8, device=dev)
-        us = time_fn(torch, lambda i=0: bi.bi_attn_decode(q, kc, vc, btd, lt, 4096, 1 / math.sqrt(128), out=o,
-                                                           workspace=ws), reps)
-        out.append(entry("attn decode 64/4 D128", us, bytes_decode(lens, 64, 4, 128), flops_decode(lens, 64, 128),
-                         extra={"B": B, "sum_L": sum(lens)}))
-        del kc, vc
+    q = W.randn_bf16((256, 64, 128), W.SEED_MOE, "q", 0, device=dev)
+    o = torch.empty_like(q)
+    btd, lt = pb.block_table.to(dev), torch.tensor(lens, dtype=torch.int32, device=dev)
+    ws = torch.empty((bi.bi_attn_decode_workspace_bytes(256, 64, 128, 4096),), dtype=torch.uint8, device=dev)
+    for B in (1, 64, 256):
+        ng = 256 // B
+        grp = [slice(j * B, (j + 1) * B) for j in range(ng)]
+        us = time_fn(torch, lambda i=0: bi.bi_attn_decode(q[grp[i % ng]], kc, vc, btd[grp[i % ng]], lt[grp[i % ng]],
+                                                           4096, 1 / math.sqrt(128), out=o[:B], workspace=ws), reps)
+        glens = [lens[sl] for sl in grp]
+        out.append(entry("attn decode 64/4 D128", us, sum(bytes_decode(g, 64, 4, 128) for g in glens) / ng,
+                         sum(flops_decode(g, 64, 128) for g in glens) / ng,
+                         extra={"B": B, "sum_L": sum(map(sum, glens)) / ng, "groups": ng}))
+    del kc, vc, q, o, ws
     torch.cuda.empty_cache()
     # Long-context decode (32/8 heads, D 128): the tracked request at KV 32768
     # co-batched with B - 1 requests of seeded lengths in [1, 32768].
@@ -454,11 +469,25 @@ def kernel_table(torch, bi, W, step, reps, everything):
     o = torch.empty_like(q)
     btd, lt = pb.block_table.to(dev), torch.tensor(lens, dtype=torch.int32, device=dev)
     ws = torch.empty((bi.bi_attn_decode_workspace_bytes(n_long, 32, 128, 32768),), dtype=torch.uint8, device=dev)
+    # B = 1 rotates over the four longest requests (the tracked one and three
+    # others of 31 K+), the larger batches over disjoint groups, so repeats are
+    # not served from the Infinity Cache (bytes: the mean of the groups used).
+    longest = sorted(range(n_long), key=lambda r: -lens[r])[:4]
     for B in (1, 16, 64, 256):
-        us = time_fn(torch, lambda i=0: bi.bi_attn_decode(q[:B], kc, vc, btd[:B], lt[:B], 32768, 1 / math.sqrt(128),
-                                                           out=o[:B], workspace=ws), max(5, reps // 4))
-        out.append(entry("attn decode long-context 32/8 D128", us, bytes_decode(lens[:B], 32, 8, 128),
-                         flops_decode(lens[:B], 32, 128), extra={"B": B, "sum_L": sum(lens[:B])}))
+        grp = [[r] for r in longest] if B == 1 else [list(range(j * B, (j + 1) * B)) for j in range(n_long // B)]
+        idx = [torch.tensor(g_, device=dev) for g_ in grp]
+        ng = len(grp)
+        qs_ = [q[ix] for ix in idx]
+        bts_ = [btd[ix].contiguous() for ix in idx]
+        lts_ = [lt[ix] for ix in idx]
+        us = time_fn(torch, lambda i=0: bi.bi_attn_decode(qs_[i % ng], kc, vc, bts_[i % ng], lts_[i % ng], 32768,
+                                                           1 / math.sqrt(128), out=o[:B], workspace=ws),
+                     max(5, reps // 4))
+        glens = [[lens[r] for r in g_] for g_ in grp]
+        out.append(entry("attn decode long-context 32/8 D128", us, sum(bytes_decode(g_, 32, 8, 128) for g_ in glens)
+                         / ng, sum(flops_decode(g_, 32, 128) for g_ in glens) / ng,
+                         extra={"B": B, "sum_L": sum(map(sum, glens)) / ng, "groups": ng}))
+        del qs_, bts_, lts_
     del kc, vc, q, o, ws
     torch.cuda.empty_cache()
     return out
