@@ -668,7 +668,14 @@ def cpu_baseline(torch, W, step, sample, min_seconds=10.0, max_reps=50):
     lens = step.lens[:S]
     nbytes = (2 * bytes_rmsnorm(S, 4096) + bytes_gemm(S, 6144, 4096) + bytes_append(S, 8, 128)
               + bytes_decode(lens, 32, 8, 128) + bytes_gemm(S, 12288, 4096) + bytes_gemm(S, 4096, 12288))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(nbytes * reps / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpu_model": model,
             "seconds": round(dt, 2), "reps": reps, "ms_per_step": round(dt / reps * 1e3, 1),
             "sample": f"the decode step for requests 0-{S - 1} of {step.B} (all weights, their KV caches), "
                       f"fp64 numpy oracle, repeated {reps} times; rate = algorithmic bytes / oracle seconds"}
