@@ -587,6 +587,8 @@ def test_decode_work_queue_edges(B, max_len, msl):
             assert torch.all(out[i].view(torch.int16) == 0) and torch.all(torch.isneginf(lse[i]))
     again, _ = bt.decode(max_seq_len=msl, lens=lt, workspace=ws)
     assert_bitwise(again, out, "queue: repeat with the workspace left by the previous call")
+    no_lse, _ = bi.bi_attn_decode(bt.q, bt.kc, bt.vc, bt.bt, lt, msl, bt.scale, lse=None, workspace=ws)
+    assert_bitwise(no_lse, out, "queue: no lse output")
 
 
 @pytest.mark.parametrize("B,hq,hkv,d,ps,max_len", [(40, 8, 8, 64, 32, 3000), (300, 16, 1, 128, 256, 2000),

@@ -197,6 +197,12 @@ def test_moe_route_ties_and_closed_forms():
     assert torch.equal(ids[:, 0::2] + 64, ids[:, 1::2]), ids
     assert torch.all(ids[:, 0::2] < 64)
     assert_bitwise(wts[:, 0::2], wts[:, 1::2], "tied weights")
+    # Many experts (the 16-per-lane instance): E = 300 and 1024, top 16.
+    for E in (300, 1024):
+        ge = W.randn_bf16((E, 512), W.SEED_MOE, "gate", 1000 + E, std=0.05).to(DEV)
+        ids, wts, lg = bi.bi_moe_route(x, ge, 16)
+        assert np.array_equal(ids.cpu().numpy(), _order(lg.cpu().double().numpy(), 16)), f"E={E}"
+        assert np.allclose(wts.cpu().double().numpy().sum(axis=1), 1.0, atol=1e-6)
     # E = 5, top_k = 5: every expert, in logit order.
     ids, wts, lg = bi.bi_moe_route(x, g[:5].contiguous(), 5)
     assert np.array_equal(ids.cpu().numpy(), _order(lg.cpu().double().numpy(), 5))
