@@ -260,6 +260,107 @@ class DecodeStep:
                 + flops_decode(self.lens, self.HQ, self.D))
 
 
+# ---------------------------------------------------------------- the mixed-batch step
+
+class MixedStep:
+    """Qwen3-8B-shaped chunked-prefill + decode step: 4 prefill chunks of 512
+    tokens over the seeded prefixes and 252 decode requests with seeded KV
+    lengths in [1, 8192], in one batch of M = 2300 rows.  RMSNorm, QKV GEMM, KV
+    append (all 2300 new tokens), chunked prefill (the 2048 chunk rows), decode
+    (the 252 decode rows), RMSNorm, MLP GEMMs; q/k/v are strided views of the
+    QKV output.  Weights are the decode step's."""
+
+    D_DEC = 252
+
+    def __init__(self, torch, bi, W, step, dev="cuda"):
+        self.torch, self.bi, self.step = torch, bi, step
+        base = W.SEED_MIXED
+        self.prefixes = [W.rand_int(0, 8192, base, "len", 100 + s) for s in range(4)]
+        self.dlens = W.decode_lengths(range(1000, 1000 + self.D_DEC), base, 1, 8192)
+        lens = [p + 512 for p in self.prefixes] + self.dlens
+        pb = W.allocate_pages(lens, base)
+        self.kc, self.vc = bi.alloc_kv_cache(pb.num_pages, 8, 128, 16, dev, fill=0.0)
+        ids = list(range(4)) + list(range(1000, 1000 + self.D_DEC))
+        lo = 0
+        for j0 in range(0, len(ids), 32):
+            part = list(range(j0, min(len(ids), j0 + 32)))
+            kv = [W.request_kv(ids[j], lens[j], 8, 128, base, device=dev) for j in part]
+            hi = lo + sum(lens[j] for j in part)
+            bi.bi_kv_append(torch.cat([k for k, _ in kv]), torch.cat([v for _, v in kv]),
+                            pb.slot_mapping[lo:hi].to(dev), self.kc, self.vc)
+            lo = hi
+            del kv
+        starts = [0]
+        for L in lens[:-1]:
+            starts.append(starts[-1] + L)
+        # slots the step's new tokens go to: each chunk's 512 positions, each decode request's last one
+        new = [starts[s] + self.prefixes[s] + i for s in range(4) for i in range(512)]
+        new += [starts[4 + r] + self.dlens[r] - 1 for r in range(self.D_DEC)]
+        self.new_slots = pb.slot_mapping[torch.tensor(new)].to(dev)
+        bt = pb.block_table.to(dev)
+        self.bt_pre, self.bt_dec = bt[:4].contiguous(), bt[4:].contiguous()
+        self.q_start = torch.tensor([0, 512, 1024, 1536, 2048], dtype=torch.int32, device=dev)
+        self.ctx = torch.tensor(self.prefixes, dtype=torch.int32, device=dev)
+        self.lens_dec = torch.tensor(self.dlens, dtype=torch.int32, device=dev)
+        M = self.M = 2048 + self.D_DEC
+        e = dict(dtype=torch.bfloat16, device=dev)
+        self.x = W.rows_for_requests(range(M), 4096, base, device=dev)
+        self.h, self.qkv = torch.empty((M, 4096), **e), torch.empty((M, 6144), **e)
+        self.attn, self.h2 = torch.empty((M, 32, 128), **e), torch.empty((M, 4096), **e)
+        self.up, self.down = torch.empty((M, 12288), **e), torch.empty((M, 4096), **e)
+        self.ws = torch.empty((bi.bi_attn_decode_workspace_bytes(self.D_DEC, 32, 128, 8192),), dtype=torch.uint8,
+                              device=dev)
+        self.scale = 1.0 / math.sqrt(128)
+
+    def run(self):
+        bi, st = self.bi, self.step
+        bi.bi_rmsnorm(self.x, st.g1, EPS, out=self.h)
+        bi.bi_gemm(self.h, st.w_qkv, out=self.qkv)
+        q = self.qkv[:, :4096].view(self.M, 32, 128)
+        bi.bi_kv_append(self.qkv[:, 4096:5120].view(self.M, 8, 128), self.qkv[:, 5120:].view(self.M, 8, 128),
+                        self.new_slots, self.kc, self.vc)
+        bi.bi_attn_prefill(q[:2048], self.q_start, self.ctx, 512, self.kc, self.vc, self.bt_pre, self.scale,
+                           out=self.attn[:2048])
+        bi.bi_attn_decode(q[2048:], self.kc, self.vc, self.bt_dec, self.lens_dec, 8192, self.scale,
+                          out=self.attn[2048:], workspace=self.ws)
+        bi.bi_rmsnorm(self.attn.view(self.M, 4096), st.g2, EPS, out=self.h2)
+        bi.bi_gemm(self.h2, st.w_up, out=self.up)
+        bi.bi_gemm(self.up, st.w_down, out=self.down)
+
+    def work(self):
+        M = self.M
+        nbytes = (2 * bytes_rmsnorm(M, 4096) + bytes_gemm(M, 6144, 4096) + bytes_append(M, 8, 128)
+                  + bytes_prefill(self.prefixes, [512] * 4, 32, 8, 128) + bytes_decode(self.dlens, 32, 8, 128)
+                  + bytes_gemm(M, 12288, 4096) + bytes_gemm(M, 4096, 12288))
+        flops = (flops_gemm(M, 6144, 4096) + flops_gemm(M, 12288, 4096) + flops_gemm(M, 4096, 12288)
+                 + flops_prefill(self.prefixes, [512] * 4, 32, 128) + flops_decode(self.dlens, 32, 128))
+        return nbytes, flops
+
+
+def mixed_step_line(torch, bi, W, step, steps=10):
+    ms = MixedStep(torch, bi, W, step)
+    for _ in range(3):
+        ms.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ms.run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    nbytes, flops = ms.work()
+    t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
+    line = {"workload": "Qwen3-8B-shaped mixed step: 4 prefill chunks of 512 tokens over prefixes "
+                        f"{ms.prefixes} + {ms.D_DEC} decode requests (KV 1-8192), M = {ms.M} rows",
+            "us": round(us, 1), "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "flops": flops, "bytes": nbytes,
+            "frac_roofline": round(t_roof / (us * 1e-6), 4)}
+    del ms
+    torch.cuda.empty_cache()
+    return line
+
+
 # ---------------------------------------------------------------- per-kernel table
 
 def copies(w, total=768 << 20):
@@ -827,6 +928,9 @@ def main():
     if args.kernels != "none":
         print("[bench] per-kernel table", file=sys.stderr, flush=True)
         result["kernels"] = kernel_table(torch, bi, W, step, args.reps, args.kernels == "all")
+        if args.kernels == "all":
+            print("[bench] mixed prefill + decode step", file=sys.stderr, flush=True)
+            result["mixed_step"] = mixed_step_line(torch, bi, W, step)
         print("[bench] decoder layer", file=sys.stderr, flush=True)
         result["kernels"] += layer_table(torch, bi, W, step, args.reps)
         print("[bench] cost of invariance", file=sys.stderr, flush=True)
