@@ -793,6 +793,7 @@ ONLY = {
     "layer-decode-b1": "Qwen3-8B-shaped decoder layer, decode of 1 request",
     "layer-decode-b256": "Qwen3-8B-shaped decoder layer, decode of 256 requests (the decode-step caches)",
     "moe-t2048": "routed experts, 128 x (4096->1536->4096) top-8, T=2048",
+    "mixed-step": "Qwen3-8B-shaped mixed step: 4 x 512 prefill tokens + 252 decode requests, M=2300",
 }
 
 
@@ -837,6 +838,9 @@ def run_only(torch, bi, W, what, reps):
         y = torch.empty((T, 4096), dtype=torch.bfloat16, device=dev)
         mws = torch.empty((bi.moe_workspace_bytes(T, K8, E, 4096, F),), dtype=torch.uint8, device=dev)
         fn = lambda: bi.bi_moe_ffn(x, ex, wt, w_up, w_down, out=y, workspace=mws)
+    elif what == "mixed-step":
+        ms = MixedStep(torch, bi, W, DecodeStep(torch, bi, W, 256))
+        fn = ms.run
     elif what == "rmsnorm-2300":
         x = W.rows_for_requests(range(2300), 4096, W.SEED_MIXED, device=dev)
         g = W.randn_bf16((4096,), W.SEED_MIXED, "gamma", W.WEIGHTS, std=0.1, mean=1.0, device=dev)
