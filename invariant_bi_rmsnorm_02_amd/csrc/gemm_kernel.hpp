@@ -3,9 +3,9 @@
 // Matrix Multiplication", figs. "Data-Parallel Matrix Multiplication" and
 // "Split-K Matmul").
 //
-// The library instantiates two configurations and picks one from the weight's
-// row count N alone (gemm_with_cfg), never from M.  Whatever the
-// configuration, the arithmetic of an output element is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
+// The library instantiates two configurations (gemm_with_cfg_mn picks one from
+// the shape; the fused lm_head reads N alone).  Whatever the configuration,
+// the arithmetic of an output element is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
 // k = 0, 32, 64, ... in ascending order, no split of K.  Nothing here depends on
 // M except which rows are loaded and which 16-row MFMA blocks are skipped
 // because all their rows are past M.
@@ -372,10 +372,10 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
   });
 }
 
-// The library's GEMM configuration for every weight narrower than
-// kGemmWideMinN rows (bi_gemm, the expert GEMMs of bi_moe_ffn).  Chosen by
-// timing candidates at every workload shape on MI355X, and used for every M:
-// 64 (n) x 64 (m) output tile, 2 x 2 wavefronts of 32 x 32, K in 64-wide
+// The library's GEMM configuration for weights narrower than kGemmWideMinN
+// rows at small and medium M (bi_gemm below the large-M rule of
+// gemm_with_cfg_mn, the expert GEMMs of bi_moe_ffn).  Chosen by timing
+// candidates at every workload shape on MI355X: 64 (n) x 64 (m) output tile, 2 x 2 wavefronts of 32 x 32, K in 64-wide
 // stages, a 5-stage LDS ring (80 KB, two workgroups per CU).  A small n-extent
 // keeps enough workgroups streaming weights at decode batch sizes (N / 64 of
 // them), which is what bounds those HBM-bound shapes.
@@ -387,18 +387,41 @@ using GemmLibraryCfg = GemmCfg<64, 64, 2, 2, 5, 64, 2>;
 // weight has at least one 128-row strip per CU, so its stream fills the chip
 // even at one m-tile, and the larger tile reads each operand from L2 half (W)
 // or a quarter (A) as often as the 64 x 64 tile, which is what bounds the
-// 64 x 64 tile once M is large.  The choice depends on N alone: a given
-// weight runs the same tile for every M.  Every element's arithmetic is the
-// same in both configurations (one fp32 chain of the same MFMA over k
-// ascending), so the tile decides speed, never bits.
+// 64 x 64 tile once M is large.  Every element's arithmetic is the same in
+// both configurations (one fp32 chain of the same MFMA over k ascending, one
+// rounding at the end), so the tile decides speed, never bits: the choice may
+// read M without making any row depend on the rest of the batch.
 using GemmWideCfg = GemmCfg<128, 256, 2, 4, 3, 64, 1>;
 constexpr int64_t kGemmWideMinN = 256 * GemmWideCfg::TN;
+// Large-M rule of bi_gemm: at least this many rows and at least one wide tile
+// per CU.  Measured on MI355X with the Qwen3-8B step weights (QKV 4096 -> 6144,
+// up 4096 -> 12288, down 12288 -> 4096): at M = 2300 the wide tile takes 138 /
+// 262 / 338 us against 196 / 377 / 406 us, at M = 1024 it is no slower where
+// it has 256 tiles, and at M = 256 it is 1.2-2.9x slower (too few weight
+// streams).
+constexpr int64_t kGemmWideMinM = 1024;
+constexpr int64_t kGemmWideMinTiles = 256;
 
 // Calls f(Cfg{}) with the configuration of a weight with n rows and returns
-// its result (host code).
+// its result (host code).  Used where the configuration must not depend on M
+// (the fused lm_head, whose workspace holds one record per n-tile).
 template <class F>
 inline auto gemm_with_cfg(int64_t n, F&& f) {
   if (n >= kGemmWideMinN) return f(GemmWideCfg{});
+  return f(GemmLibraryCfg{});
+}
+
+// bi_gemm's configuration: the wide tile for wide weights, and also for any
+// weight once M reaches kGemmWideMinM rows and the wide grid has at least
+// kGemmWideMinTiles tiles, where the wide tile's operand offsets fit its
+// buffer resources (else the 64 x 64 tile, whose bits are the same).
+template <class F>
+inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, F&& f) {
+  using Wd = GemmWideCfg;
+  const bool large_m = m >= kGemmWideMinM &&
+                       ((m + Wd::TM - 1) / Wd::TM) * ((n + Wd::TN - 1) / Wd::TN) >= kGemmWideMinTiles &&
+                       gemm_offsets_fit<Wd>(lda, ldw, k);
+  if (n >= kGemmWideMinN || large_m) return f(Wd{});
   return f(GemmLibraryCfg{});
 }
 

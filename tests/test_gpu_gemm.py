@@ -183,6 +183,26 @@ def test_gemm_wide_tile_gives_the_same_bits():
     assert torch.equal(bi.bi_gemm(ai.to(DEV), wi.to(DEV)).view(torch.int16).cpu(), want)
 
 
+@pytest.mark.parametrize("n,k", [(12288 + 72, 4096), (4096, 12288), (6144, 4096)])
+def test_gemm_large_m_rule_gives_the_same_bits(n, k):
+    """From 1024 rows on, a weight whose 128 x 256 grid has at least 256 tiles
+    runs that tile instead of 64 x 64 (the Qwen3-8B step weights at M = 2300;
+    the up projection, with a ragged n tail, already at M = 1024).  The whole
+    product at M in {1024, 1100, 2300} must equal, bit for bit, the same rows
+    computed in slices of at most 512 rows (64 x 64 tile), in bf16 and fp32."""
+    w = W.randn_bf16((n, k), 12, "w", n, std=0.02, device=DEV)
+    for m in (1024, 1100, 2300):
+        log_case(f"gemm large-m rule m={m} n={n} k={k}")
+        a = W.randn_bf16((m, k), 12, "x", m, device=DEV)
+        for dt in (torch.bfloat16, torch.float32):
+            whole = bi.bi_gemm(a, w, out_dtype=dt)
+            sliced = torch.cat([bi.bi_gemm(a[r:r + 512], w, out_dtype=dt) for r in range(0, m, 512)])
+            assert_bitwise(whole, sliced, f"large-m rule m={m} n={n} {dt}")
+        ref = O.gemm(f64(a[::97]), f64(w[::89]))
+        assert_bf16_close(bi.bi_gemm(a, w)[::97, ::89], ref, f"large-m rule parity m={m} n={n}")
+        assert_f32_close(whole[::97, ::89], ref, f"large-m rule fp32 parity m={m} n={n}")
+
+
 def test_gemm_wide_tile_batch_invariance():
     # The full lm_head (4096 -> 151936, the wide tile): token 0's fp32 logits at
     # T in {1, 64, 512} and shuffled positions.
