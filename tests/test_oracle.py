@@ -237,13 +237,18 @@ def test_prefill_causal_mask_and_decode_equivalence():
     v = rng.standard_normal((P + n, Hkv, D))
     q = rng.standard_normal((n, Hq, D))
     out, lse = O.prefill_attention(q, k, v, P, 0.35)
-    # Keys after a query's position must not matter: poison them.
+    # Keys after a query's position must not matter: poison every key past
+    # position P + i and hand the oracle the whole poisoned cache and chunk.
+    # Rows 0..i see only clean keys and must not move; a mask that lets row i
+    # see one key too many picks up the poison.
     for i in range(n):
         k2, v2 = k.copy(), v.copy()
         k2[P + i + 1:] = 1e3
         v2[P + i + 1:] = -1e3
-        o2, l2 = O.prefill_attention(q[i:i + 1], k2[:P + i + 1], v2[:P + i + 1], P + i, 0.35)
-        assert np.allclose(o2[0], out[i], atol=1e-13) and np.allclose(l2[0], lse[i], atol=1e-13)
+        o2, l2 = O.prefill_attention(q, k2, v2, P, 0.35)
+        assert np.allclose(o2[:i + 1], out[:i + 1], atol=1e-13) and np.allclose(l2[:i + 1], lse[:i + 1], atol=1e-13)
+        if i + 1 < n:
+            assert not np.allclose(o2[i + 1], out[i + 1], atol=1e-3), "the poison reaches the next row"
         od, ld = O.decode_attention(q[i:i + 1], [k[:P + i + 1]], [v[:P + i + 1]], 0.35)
         assert np.allclose(od[0], out[i], atol=1e-13) and np.allclose(ld[0], lse[i], atol=1e-13)
     # The first chunk query with P = 0 sees exactly one key: o = v0.
