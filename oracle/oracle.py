@@ -329,7 +329,7 @@ def silu_mul(gate_up: np.ndarray) -> np.ndarray:
 
 def decoder_layer(x: np.ndarray, k_prefix: np.ndarray, v_prefix: np.ndarray, weights: dict,
                   num_q_heads: int, num_kv_heads: int, head_dim: int, eps: float,
-                  scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                  scale: float, steps: dict = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """One pre-norm decoder layer over the T new tokens x [T, H] of one sequence
     whose cache already holds P tokens (k_prefix, v_prefix [P, Hkv, D]).
 
@@ -341,6 +341,8 @@ def decoder_layer(x: np.ndarray, k_prefix: np.ndarray, v_prefix: np.ndarray, wei
     activations are bfloat16 tensors, so every step's output is rounded to
     bfloat16 (ties to even) before the next step reads it; each step itself is
     the float64 definition above.  Returns y [T, H] and the new k, v [T, Hkv, D].
+    A ``steps`` dict, if given, receives every step's rounded output (h, qkv,
+    a, c = a W_o^T, r, h2, gu, m, d = m W_down^T) for error propagation checks.
     """
     x = np.asarray(x, dtype=np.float64)
     T = x.shape[0]
@@ -354,8 +356,13 @@ def decoder_layer(x: np.ndarray, k_prefix: np.ndarray, v_prefix: np.ndarray, wei
     K = np.concatenate([np.asarray(k_prefix, dtype=np.float64).reshape(P, hkv, d), k])
     V = np.concatenate([np.asarray(v_prefix, dtype=np.float64).reshape(P, hkv, d), v])
     a = round_bf16(prefill_attention(q, K, V, P, scale)[0]).reshape(T, hq * d)
-    r = round_bf16(x + round_bf16(gemm(a, weights["w_o"])))
+    c = round_bf16(gemm(a, weights["w_o"]))
+    r = round_bf16(x + c)
     h2 = round_bf16(rmsnorm(r, weights["g2"], eps))
-    m = round_bf16(silu_mul(round_bf16(gemm(h2, weights["w_gu"]))))
-    y = round_bf16(r + round_bf16(gemm(m, weights["w_down"])))
+    gu = round_bf16(gemm(h2, weights["w_gu"]))
+    m = round_bf16(silu_mul(gu))
+    dn = round_bf16(gemm(m, weights["w_down"]))
+    y = round_bf16(r + dn)
+    if steps is not None:
+        steps.update(h=h, qkv=qkv, a=a, c=c, r=r, h2=h2, gu=gu, m=m, d=dn)
     return y, k, v
