@@ -288,16 +288,23 @@ def test_decode_growing_cache_with_random_co_batch():
         assert_bitwise(l[pos], l1[0], f"tracked lse at L={L} with {k} co-batched")
 
 
-def test_decode_long_context_co_batch_invariance():
+@pytest.fixture(scope="module")
+def long_batch():
+    """The long-context workload's requests: request 0 with a 32768-token
+    cache, 255 others with seeded lengths in [1, 32768]."""
+    lens = [32768] + W.decode_lengths(range(1, 256), W.SEED_LONG, 1, 32768)
+    return Batch(range(256), lens, 32, 8, 128, W.SEED_LONG, perm_index=3)
+
+
+def test_decode_long_context_co_batch_invariance(long_batch):
     """The long-context workload at its size: one request at KV 32768 (and at
     20001, a partial last chunk) decoded alone and among 15, 63 and 255 others
     with seeded lengths in [1, 32768], at random slots.  The batches take every
     scheduling path of bi_attn_decode (one wavefront per chunk; the work queue
     with chunk groups and the merge; whole sequences), and the tracked output
     and lse must be bitwise the same in all of them."""
-    hq, hkv, d, n_others = 32, 8, 128, 255
-    lens = [32768] + W.decode_lengths(range(1, n_others + 1), W.SEED_LONG, 1, 32768)
-    bt = Batch(range(n_others + 1), lens, hq, hkv, d, W.SEED_LONG, perm_index=3)
+    hq, n_others = 32, 255
+    bt = long_batch
     rng = np.random.default_rng(9)
     for L in (32768, 20001):
         ref = None
@@ -319,6 +326,43 @@ def test_decode_long_context_co_batch_invariance():
                 assert_f32_close(got[1][None], rl, f"long-context lse L={L}")
             assert_bitwise(got[0], ref[0], f"tracked output L={L} at B={B} slot={pos}")
             assert_bitwise(got[1], ref[1], f"tracked lse L={L} at B={B} slot={pos}")
+
+
+def test_decode_long_context_growth_sweep(long_batch):
+    """The long-context workload's growth check, sampled at every chunk
+    boundary: the tracked request at KV lengths 256k - 1, 256k and 256k + 1 for
+    every k up to 32768 (the last chunk one token short of full, full, and a
+    new one-token chunk), with a new seeded query at every length.  At each
+    length it is decoded alone (max_seq_len = its length) and among 0..255
+    others drawn at random from the 255 (max_seq_len 32768), at a random slot;
+    output and lse must be bitwise equal.  Sampled lengths against the oracle."""
+    bt, hq = long_batch, 32
+    rng = np.random.default_rng(12)
+    steps = sorted({L for k in range(129) for L in (256 * k - 1, 256 * k, 256 * k + 1) if 1 <= L <= 32768})
+    sample = {1, 255, 257, 4097, 16383, 32767, 32768}
+    for L in steps:
+        q = W.randn_bf16((1, hq, 128), W.SEED_LONG, "q", 20_000 + L, device=DEV)
+        lt1 = torch.tensor([L], dtype=torch.int32, device=DEV)
+        o1, l1 = bi.bi_attn_decode(q, bt.kc, bt.vc, bt.bt[:1], lt1, L, bt.scale,
+                                   lse=torch.empty((1, hq), dtype=torch.float32, device=DEV))
+        k = int(rng.integers(0, 256))
+        others = rng.choice(np.arange(1, 256), size=k, replace=False).tolist()
+        pos = int(rng.integers(0, k + 1))
+        ids = others[:pos] + [0] + others[pos:]
+        idx = torch.tensor(ids, device=DEV)
+        qq = bt.q[idx].clone()
+        qq[pos] = q[0]
+        lt = bt.lens[idx].clone()
+        lt[pos] = L
+        o, l = bi.bi_attn_decode(qq, bt.kc, bt.vc, bt.bt[idx].contiguous(), lt, 32768, bt.scale,
+                                 lse=torch.empty((k + 1, hq), dtype=torch.float32, device=DEV))
+        if L in sample:
+            log_case(f"long-context growth L={L} with {k} co-batched at slot {pos}")
+            ro, rl = O.decode_attention(f64(q), [f64(bt.kv[0][0][:L])], [f64(bt.kv[0][1][:L])], bt.scale)
+            assert_bf16_close(o1, ro, f"growth L={L} vs oracle")
+            assert_f32_close(l1, rl, f"growth L={L} lse vs oracle")
+        assert_bitwise(o[pos], o1[0], f"tracked output at L={L} with {k} co-batched (slot {pos})")
+        assert_bitwise(l[pos], l1[0], f"tracked lse at L={L} with {k} co-batched (slot {pos})")
 
 
 # ---------------------------------------------------------------- prefill
@@ -558,7 +602,7 @@ def test_decode_edges():
 
 @pytest.mark.parametrize("B,max_len,msl", [(160, 1400, 1200), (40, 4500, 4000)])
 def test_decode_work_queue_edges(B, max_len, msl):
-    """Past 4096 (sequence, kv head, chunk) items the decode wavefronts take
+    """Past 2048 (sequence, kv head, chunk) items the decode wavefronts take
     their work from a queue: whole sequences once there are enough (sequence,
     kv head) pairs (160 x 8 here), otherwise groups of chunks whose partials
     the merge kernel folds after the group-0 wavefront's running state (40 x 8
@@ -589,6 +633,38 @@ def test_decode_work_queue_edges(B, max_len, msl):
     assert_bitwise(again, out, "queue: repeat with the workspace left by the previous call")
     no_lse, _ = bi.bi_attn_decode(bt.q, bt.kc, bt.vc, bt.bt, lt, msl, bt.scale, lse=None, workspace=ws)
     assert_bitwise(no_lse, out, "queue: no lse output")
+
+
+@pytest.mark.parametrize("B,hq,hkv,msl", [
+    (16, 32, 8, 4096),     # 16 x 8 x 16 = 2048 chunk items: one wavefront per chunk, then the merge kernel
+    (17, 32, 8, 4096),     # 2176 items: work queue, chunk groups of 2 + merge
+    (2048, 8, 1, 256),     # 2048 items (one chunk each): per-chunk grid
+    (2049, 8, 1, 256),     # 2049 items: work queue, whole sequences (one chunk is the whole sequence)
+    (127, 32, 8, 1024),    # 1016 (sequence, kv head) pairs: queue with chunk groups + merge
+    (128, 32, 8, 1024),    # 1024 pairs: whole-sequence queue, no merge
+    (1023, 16, 1, 1024),   # 1023 pairs: chunk groups of 3 + merge
+    (1024, 16, 1, 1024)])  # 1024 pairs: whole sequences
+def test_decode_dispatch_edges(B, hq, hkv, msl):
+    """bi_attn_decode picks its schedule from the batch shape: per-chunk grid
+    up to 2048 (sequence, kv head, chunk) items, then a work queue of chunk
+    groups, and whole sequences from 1024 (sequence, kv head) pairs on.  The
+    arithmetic of a request is the same on every path; at both sides of each
+    threshold sampled requests (first, last, longest, random) must equal,
+    bit for bit, the request decoded alone."""
+    lens = [int(x) for x in torch.randint(1, msl + 1, (B,), generator=torch.Generator().manual_seed(B * 7 + hkv))]
+    lens[B // 3] = msl
+    bt = Batch(range(B), lens, hq, hkv, 128, 37)
+    log_case(f"decode dispatch edge B={B} {hq}/{hkv} max_seq_len={msl}")
+    out, lse = bt.decode(max_seq_len=msl)
+    picks = sorted({0, B - 1, B // 3, *torch.randint(0, B, (13,), generator=torch.Generator().manual_seed(B)).tolist()})
+    for i in picks:
+        o1, l1 = bi.bi_attn_decode(bt.q[i:i + 1], bt.kc, bt.vc, bt.bt[i:i + 1], bt.lens[i:i + 1], msl, bt.scale,
+                                   lse=torch.empty((1, hq), dtype=torch.float32, device=DEV))
+        assert_bitwise(out[i:i + 1], o1, f"request {i} (L={lens[i]}): B={B} vs alone")
+        assert_bitwise(lse[i:i + 1], l1, f"request {i} lse: B={B} vs alone")
+    ro, rl = bt.oracle([B // 3])
+    assert_bf16_close(out[B // 3], ro[0], f"request {B // 3} vs oracle")
+    assert_f32_close(lse[B // 3:B // 3 + 1], rl, f"request {B // 3} lse vs oracle")
 
 
 @pytest.mark.parametrize("B,hq,hkv,d,ps,max_len", [(40, 8, 8, 64, 32, 3000), (300, 16, 1, 128, 256, 2000),

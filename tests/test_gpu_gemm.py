@@ -203,6 +203,27 @@ def test_gemm_large_m_rule_gives_the_same_bits(n, k):
         assert_f32_close(whole[::97, ::89], ref, f"large-m rule fp32 parity m={m} n={n}")
 
 
+@pytest.mark.parametrize("n,k,m_lo,m_hi", [
+    (12288, 4096, 1023, 1024),   # up projection: 96 wide n-tiles, so the 1024-row rule decides
+    (6144, 4096, 1280, 1281),    # QKV: 48 n-tiles x 5 / 6 m-tiles = 240 / 288 wide tiles
+    (4096, 12288, 1792, 1793)])  # down: 32 n-tiles x 7 / 8 m-tiles = 224 / 256 wide tiles
+def test_gemm_tile_rule_edges(n, k, m_lo, m_hi):
+    """bi_gemm runs the 64 x 64 tile at m_lo and the 128 x 256 tile at m_hi
+    (the large-M rule: at least 1024 rows and at least 256 wide tiles).  The
+    rows the two products share, and both products against the same rows in
+    256-row slices (64 x 64 tile), must agree bit for bit."""
+    w = W.randn_bf16((n, k), 13, "w", n, std=0.02, device=DEV)
+    a = W.randn_bf16((m_hi, k), 13, "x", m_hi, device=DEV)
+    log_case(f"gemm tile rule edge n={n} k={k} m={m_lo}/{m_hi}")
+    for dt in (torch.bfloat16, torch.float32):
+        lo = bi.bi_gemm(a[:m_lo], w, out_dtype=dt)
+        hi = bi.bi_gemm(a, w, out_dtype=dt)
+        sliced = torch.cat([bi.bi_gemm(a[r:r + 256], w, out_dtype=dt) for r in range(0, m_hi, 256)])
+        assert_bitwise(hi[:m_lo], lo, f"rows shared by m={m_lo} and m={m_hi} ({dt})")
+        assert_bitwise(hi, sliced, f"m={m_hi} vs 256-row slices ({dt})")
+        assert_bitwise(lo, sliced[:m_lo], f"m={m_lo} vs 256-row slices ({dt})")
+
+
 def test_gemm_wide_tile_batch_invariance():
     # The full lm_head (4096 -> 151936, the wide tile): token 0's fp32 logits at
     # T in {1, 64, 512} and shuffled positions.

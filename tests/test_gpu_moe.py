@@ -75,10 +75,10 @@ def test_moe_parity_full_shape_sampled(full_weights):
 
 
 def test_moe_batch_invariance(full_weights):
-    """Token 0's output bits at T = 1, 8, 64, 512, at shuffled positions."""
+    """Token 0's output bits at T = 1, 8, 64, 512, 2048, at shuffled positions."""
     w_up, w_down = full_weights
     ref = None
-    for T, slot in ((1, 0), (8, 0), (8, 5), (64, 37), (512, 300)):
+    for T, slot in ((1, 0), (8, 0), (8, 5), (64, 37), (512, 300), (2048, 1500), (2048, 2047)):
         log_case(f"moe invariance T={T} slot={slot}")
         others = list(range(1, T))
         ids = others[:slot] + [0] + others[slot:]
@@ -209,11 +209,11 @@ def test_moe_route_ties_and_closed_forms():
 
 
 def test_moe_route_batch_invariance():
-    """Token 0's logits, choice and weights: bitwise the same at T = 1, 64, 512
-    and shuffled positions."""
+    """Token 0's logits, choice and weights: bitwise the same at T = 1, 64, 512,
+    2048 and shuffled positions."""
     wg = _gate().to(DEV)
     ref = None
-    for T, slot in ((1, 0), (64, 37), (512, 300), (512, 0)):
+    for T, slot in ((1, 0), (64, 37), (512, 300), (512, 0), (2048, 777)):
         log_case(f"moe route invariance T={T} slot={slot}")
         others = list(range(1, T))
         ids_ = others[:slot] + [0] + others[slot:]
@@ -228,12 +228,12 @@ def test_moe_route_batch_invariance():
 
 def test_moe_layer_routed_invariance_and_parity(full_weights):
     """The whole routed layer (bi_moe_route then bi_moe_ffn): token 0's output
-    bitwise the same at T = 1, 64, 512; and against the oracle's routed layer
-    on tokens whose routing is clear."""
+    bitwise the same at T = 1, 64, 512, 2048; and against the oracle's routed
+    layer on tokens whose routing is clear."""
     w_up, w_down = full_weights
     wg = _gate().to(DEV)
     ref = None
-    for T, slot in ((1, 0), (64, 10), (512, 411)):
+    for T, slot in ((1, 0), (64, 10), (512, 411), (2048, 1234)):
         log_case(f"routed moe layer T={T} slot={slot}")
         others = list(range(1, T))
         ids_ = others[:slot] + [0] + others[slot:]
