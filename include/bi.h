@@ -181,6 +181,38 @@ bi_status bi_attn_decode(const void* q, int64_t ld_q, const void* k_cache, const
                          void* workspace, size_t workspace_bytes, bi_stream_t stream);
 
 /*
+ * Size of the fixed decode scratch array of bi_attn_decode_noalloc: 128 MiB
+ * per GPU the library runs on (e.g. the Qwen3-8B-shaped decode at 256
+ * sequences of up to 4096 tokens needs 69 MB of it).
+ */
+#define BI_DECODE_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * Decode attention that allocates nothing, for callers that cannot allocate
+ * or pass device memory of their own for a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Arguments,
+ * results and status codes are those of bi_attn_decode without the workspace;
+ * the kernels and their arithmetic are the same, so the outputs are bitwise
+ * equal to bi_attn_decode's.  The workspace is a fixed device array of
+ * BI_DECODE_SCRATCH_BYTES inside the library (one per GPU, held from when the
+ * library's code is loaded on that GPU until the process ends); its address
+ * is looked up once per device, on the first call with that device current.
+ *   BI_ERR_WORKSPACE when bi_attn_decode_workspace_bytes(num_seqs,
+ *   num_q_heads, head_dim, max_seq_len) exceeds BI_DECODE_SCRATCH_BYTES
+ *   (nothing is enqueued); BI_ERR_HIP when the stream does not belong to the
+ *   current device or the lookup fails.
+ * Every call on one GPU uses that GPU's one array: calls that can overlap on
+ * a GPU (several streams, several host threads) race and must be ordered by
+ * the caller.  The array keeps what the last call left; no call needs it
+ * cleared (the work-queue counter is written by the call's first kernel).
+ */
+bi_status bi_attn_decode_noalloc(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache,
+                                 int32_t num_pages, const int32_t* block_table, int32_t max_pages_per_seq,
+                                 const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                 float softmax_scale, void* out, float* lse, bi_stream_t stream);
+
+/*
  * Chunked-prefill attention over the paged cache ([TML] "3. Batch-Invariant
  * Attention", figs. "FlashAttention2 Strategy" and "FlashAttention with KV
  * Cache"; [HADA] Attention).  Sequence s has ctx_lens[s] cached tokens and a

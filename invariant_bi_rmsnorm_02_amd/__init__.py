@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "bi.h")
 BI_OK, BI_ERR_INVALID_ARG, BI_ERR_UNSUPPORTED, BI_ERR_WORKSPACE, BI_ERR_HIP = 0, -1, -2, -3, -4
 BI_BF16, BI_F32 = 0, 1
 BI_KV_CHUNK = 256
+BI_DECODE_SCRATCH_BYTES = 128 << 20
 
 _c_i32, _c_i64, _c_f32, _c_size, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -34,6 +35,8 @@ _SIGNATURES = {
     "bi_attn_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "bi_attn_decode": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                 _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_size, _c_p]),
+    "bi_attn_decode_noalloc": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i32, _c_i32,
+                                        _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p]),
     "bi_attn_prefill": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_i32,
                                  _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p]),
     "bi_log_softmax": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
@@ -239,6 +242,38 @@ def bi_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         block_table.shape[1], seq_lens.data_ptr(), b, int(max_seq_len), hq, hkv, d, ps, float(softmax_scale),
         out.data_ptr(), lse.data_ptr() if lse is not None else None, workspace.data_ptr(), ws_bytes,
         _stream(stream)))
+    return out, lse
+
+
+def bi_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                           softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None):
+    """Decode attention with the library's fixed scratch array as its workspace
+    (the C entry point allocates nothing).  `out` is required, so this
+    wrapper allocates nothing either.  Returns (out, lse)."""
+    pages, hkv, ps, d = _cache_geom(k_cache, v_cache)
+    _dev(q, "q", torch.bfloat16)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    b, hq, dq = q.shape
+    if dq != d:
+        raise ValueError("q must be [B, Hq, D]")
+    ldq = _tokens(q, "q")
+    if block_table.dim() != 2 or block_table.shape[0] != b or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [B, max_pages] tensor")
+    if seq_lens.shape != (b,) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be [B]")
+    _dev(out, "out", torch.bfloat16)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out shape")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if lse.shape != (b, hq) or not lse.is_contiguous():
+            raise ValueError("lse must be [B, Hq]")
+    _check("bi_attn_decode_noalloc", lib().bi_attn_decode_noalloc(
+        q.data_ptr(), ldq, k_cache.data_ptr(), v_cache.data_ptr(), pages, block_table.data_ptr(),
+        block_table.shape[1], seq_lens.data_ptr(), b, int(max_seq_len), hq, hkv, d, ps, float(softmax_scale),
+        out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(stream)))
     return out, lse
 
 

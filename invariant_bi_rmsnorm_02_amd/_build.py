@@ -27,7 +27,7 @@ ADAPTIVE_SHARED = ["gemm.hip", "rmsnorm.hip"]   # libbi objects linked into the 
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "rmsnorm.hip", "gemm.hip", "kv_append.hip", "attn_decode.hip",
-           "attn_prefill.hip", "log_softmax.hip", "moe.hip", "lm_head.hip", "pointwise.hip"]
+           "attn_prefill.hip", "log_softmax.hip", "moe.hip", "lm_head.hip", "pointwise.hip", "scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

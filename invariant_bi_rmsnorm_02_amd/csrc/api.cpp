@@ -62,6 +62,22 @@ bi::AttnGeom make_geom(const void* k_cache, const void* v_cache, int32_t num_pag
   return g;
 }
 
+// Checks of bi_attn_decode's arguments other than the workspace.
+bi_status check_decode(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache, int32_t num_pages,
+                       const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t page_size, float softmax_scale, const void* out) {
+  bi_status st = check_attn_geom(k_cache, v_cache, num_pages, block_table, max_pages_per_seq,
+                                 num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale);
+  if (st != BI_OK) return st;
+  if (!q || !seq_lens || !out) return BI_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out)) return BI_ERR_INVALID_ARG;
+  if (ld_q < (int64_t)num_q_heads * head_dim || ld_q % 8) return BI_ERR_INVALID_ARG;
+  if (num_seqs > 65535 || num_kv_heads > 65535) return BI_ERR_UNSUPPORTED;  // grid y/z limits
+  if ((int64_t)num_seqs * num_kv_heads > (1 << 29)) return BI_ERR_UNSUPPORTED;  // work-queue item count
+  return BI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,14 +156,9 @@ bi_status bi_attn_decode(const void* q, int64_t ld_q, const void* k_cache, const
                          void* workspace, size_t workspace_bytes, bi_stream_t stream) {
   if (num_seqs < 0 || max_seq_len < 0) return BI_ERR_INVALID_ARG;
   if (num_seqs == 0) return BI_OK;
-  bi_status st = check_attn_geom(k_cache, v_cache, num_pages, block_table, max_pages_per_seq,
-                                 num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale);
+  bi_status st = check_decode(q, ld_q, k_cache, v_cache, num_pages, block_table, max_pages_per_seq, seq_lens,
+                              num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale, out);
   if (st != BI_OK) return st;
-  if (!q || !seq_lens || !out) return BI_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(out)) return BI_ERR_INVALID_ARG;
-  if (ld_q < (int64_t)num_q_heads * head_dim || ld_q % 8) return BI_ERR_INVALID_ARG;
-  if (num_seqs > 65535 || num_kv_heads > 65535) return BI_ERR_UNSUPPORTED;  // grid y/z limits
-  if ((int64_t)num_seqs * num_kv_heads > (1 << 29)) return BI_ERR_UNSUPPORTED;  // work-queue item count
   if (!workspace || !aligned16(workspace)) return BI_ERR_WORKSPACE;
   if (workspace_bytes < bi_attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len))
     return BI_ERR_WORKSPACE;
@@ -155,6 +166,26 @@ bi_status bi_attn_decode(const void* q, int64_t ld_q, const void* k_cache, const
                                    num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale);
   return from_hip(bi::launch_attn_decode(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, workspace,
                                          as_stream(stream)));
+}
+
+bi_status bi_attn_decode_noalloc(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache,
+                                 int32_t num_pages, const int32_t* block_table, int32_t max_pages_per_seq,
+                                 const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                 float softmax_scale, void* out, float* lse, bi_stream_t stream) {
+  if (num_seqs < 0 || max_seq_len < 0) return BI_ERR_INVALID_ARG;
+  if (num_seqs == 0) return BI_OK;
+  bi_status st = check_decode(q, ld_q, k_cache, v_cache, num_pages, block_table, max_pages_per_seq, seq_lens,
+                              num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale, out);
+  if (st != BI_OK) return st;
+  if (bi_attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len) > BI_DECODE_SCRATCH_BYTES)
+    return BI_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  if (bi::decode_scratch(as_stream(stream), &scratch, &scratch_bytes) != hipSuccess) return BI_ERR_HIP;
+  return bi_attn_decode(q, ld_q, k_cache, v_cache, num_pages, block_table, max_pages_per_seq, seq_lens, num_seqs,
+                        max_seq_len, num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale, out, lse,
+                        scratch, scratch_bytes, stream);
 }
 
 bi_status bi_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens,

@@ -43,6 +43,11 @@ hipError_t launch_attn_decode(const void* q, int64_t ld_q, const AttnGeom& g, co
                               int max_seq_len, void* out, float* lse, void* workspace,
                               hipStream_t stream);
 
+// The device address and size of this device's fixed decode scratch array
+// (scratch.hip).  Looked up once per device (hipGetSymbolAddress, with the
+// device current); the stream must belong to the current device.
+hipError_t decode_scratch(hipStream_t stream, void** ptr, size_t* bytes);
+
 hipError_t launch_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens,
                                int num_seqs, int max_q_len, const AttnGeom& g, void* out, float* lse,
                                hipStream_t stream);
