@@ -283,7 +283,7 @@ bi_status bi_lm_head_logprobs(const void* a, int64_t lda, const void* w, int64_t
   if (lda < k || ldw < k || ldo < n || lda % 8 || ldw % 8 || ldo % 4) return BI_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(w) || !aligned16(out)) return BI_ERR_INVALID_ARG;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return BI_ERR_INVALID_ARG;
-  if (!bi::gemm_supported(lda, ldw, m, n, k)) return BI_ERR_UNSUPPORTED;
+  if (!bi::lm_head_supported(lda, ldw, m, n, k)) return BI_ERR_UNSUPPORTED;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return BI_ERR_WORKSPACE;
   if (workspace_bytes < bi::lm_head_workspace_bytes(m, n)) return BI_ERR_WORKSPACE;
   return from_hip(bi::launch_lm_head_logprobs(a, lda, w, ldw, out, ldo, lse, m, n, k, workspace, as_stream(stream)));
@@ -306,7 +306,7 @@ bi_status bi_lm_head_greedy(const void* a, int64_t lda, const void* w, int64_t l
   if (!aligned16(a) || !aligned16(w)) return BI_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(token) & 3u) || (logprob && (reinterpret_cast<uintptr_t>(logprob) & 3u)))
     return BI_ERR_INVALID_ARG;
-  if (!bi::gemm_supported(lda, ldw, m, n, k)) return BI_ERR_UNSUPPORTED;
+  if (!bi::lm_head_supported(lda, ldw, m, n, k)) return BI_ERR_UNSUPPORTED;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return BI_ERR_WORKSPACE;
   if (workspace_bytes < bi::lm_head_greedy_workspace_bytes(m, n)) return BI_ERR_WORKSPACE;
   return from_hip(bi::launch_lm_head_greedy(a, lda, w, ldw, token, logprob, m, n, k, workspace, as_stream(stream)));

@@ -3,8 +3,9 @@
 // Matrix Multiplication", figs. "Data-Parallel Matrix Multiplication" and
 // "Split-K Matmul").
 //
-// The library instantiates two configurations (gemm_with_cfg_mn picks one from
-// the shape; the fused lm_head reads N alone).  Whatever the configuration,
+// The library instantiates four configurations (gemm_with_cfg_mn picks one
+// from the shape; every one gives every element the same bits).  Whatever the
+// configuration,
 // the arithmetic of an output element is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
 // k = 0, 32, 64, ... in ascending order, no split of K.  Nothing here depends on
 // M except which rows are loaded and which 16-row MFMA blocks are skipped
@@ -34,7 +35,7 @@ struct GemmCfg {
   static constexpr int TN = TN_, TM = TM_;          // workgroup tile: W rows x A rows
   static constexpr int WGN = WGN_, WGM = WGM_;      // wavefront grid
   static constexpr int S = S_;                      // LDS ring depth (stages)
-  static constexpr int BK = BK_;                    // K per stage (64 or 128)
+  static constexpr int BK = BK_;                    // K per stage (32, 64 or 128)
   static constexpr int OCC = OCC_;                  // workgroups per CU the registers and LDS aim at
   static constexpr int kThreads = 64 * WGN * WGM;
   static constexpr int WTN = TN / WGN, WTM = TM / WGM;
@@ -47,7 +48,7 @@ struct GemmCfg {
   static_assert(S >= 2 && S <= 8, "ring depth");
   static_assert((S - 2) * (LW + LA) < 64, "loads in flight per wave fit the wait counter");
   static_assert(S * (TN + TM) * BK * 2 * OCC <= 160 * 1024, "LDS per CU");
-  static_assert(BK == 64 || BK == 128, "stage depth");
+  static_assert(BK == 32 || BK == 64 || BK == 128, "stage depth");
 };
 
 // Host-side limit: every offset of a workgroup's buffer resource must fit in
@@ -58,11 +59,23 @@ inline bool gemm_offsets_fit(int64_t lda, int64_t ldw, int64_t k) {
   return ((int64_t)(Cfg::TN - 1) * ldw + k) * 2 < lim && ((int64_t)(Cfg::TM - 1) * lda + k) * 2 < lim;
 }
 
-// LDS element offset of 16-byte chunk c of tile row r (KC chunks per row).  The
-// XOR swizzle puts the 16 rows that one MFMA operand read touches at one chunk
-// index into distinct 16-byte bank groups.
+// The XOR swizzle of tile row r's 16-byte chunks (KC chunks per row).  An
+// MFMA operand read has 16 consecutive rows read one chunk index each; the
+// swizzle spreads every 8 of them over distinct 16-byte bank groups.  Rows of
+// 128 or 256 bytes (KC = 8, 16) take r mod KC; rows of 64 bytes (KC = 4) put
+// four rows in one 256-byte bank period, so the XOR takes the row's group of
+// four instead.
 template <int KC>
-__device__ __forceinline__ int gemm_lds_off(int r, int c) { return r * KC * 8 + ((c ^ (r & (KC - 1))) << 3); }
+__device__ __forceinline__ int gemm_swz(int r) {
+  if constexpr (KC == 4)
+    return (r >> 2) & 3;
+  else
+    return r & (KC - 1);
+}
+
+// LDS element offset of 16-byte chunk c of tile row r (KC chunks per row).
+template <int KC>
+__device__ __forceinline__ int gemm_lds_off(int r, int c) { return r * KC * 8 + ((c ^ gemm_swz<KC>(r)) << 3); }
 
 __device__ __forceinline__ void gemm_map_tile(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
   // Workgroup i runs on XCD i % 8.  Give each XCD a contiguous range of tiles
@@ -109,7 +122,7 @@ __device__ __forceinline__ int gemm_slot_row(int i) {
 template <class Cfg>
 __device__ __forceinline__ int gemm_slot_chunk(int i) {
   constexpr int KC = Cfg::kChunks;
-  return ((threadIdx.x + i * Cfg::kThreads) % KC) ^ (gemm_slot_row<Cfg>(i) & (KC - 1));
+  return ((threadIdx.x + i * Cfg::kThreads) % KC) ^ gemm_swz<KC>(gemm_slot_row<Cfg>(i));
 }
 // Byte offset of load slot i's chunk within its row.
 template <class Cfg>
@@ -373,8 +386,8 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
 }
 
 // The library's GEMM configuration for weights narrower than kGemmWideMinN
-// rows at small and medium M (bi_gemm below the large-M rule of
-// gemm_with_cfg_mn, the expert GEMMs of bi_moe_ffn).  Chosen by timing
+// rows at medium M (bi_gemm between the narrow and large-M rules of
+// gemm_with_cfg_mn) and for the expert GEMMs of bi_moe_ffn.  Chosen by timing
 // candidates at every workload shape on MI355X: 64 (n) x 64 (m) output tile, 2 x 2 wavefronts of 32 x 32, K in 64-wide
 // stages, a 5-stage LDS ring (80 KB, two workgroups per CU).  A small n-extent
 // keeps enough workgroups streaming weights at decode batch sizes (N / 64 of
@@ -382,46 +395,78 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
 using GemmLibraryCfg = GemmCfg<64, 64, 2, 2, 5, 64, 2>;
 
 // The configuration for wide weights (N >= kGemmWideMinN, e.g. a vocabulary
-// projection): 128 (n) x 256 (m) output tile, 2 x 4 wavefronts of 64 x 64, a
-// 3-stage ring of 64-wide K stages (144 KB, one workgroup per CU).  Such a
-// weight has at least one 128-row strip per CU, so its stream fills the chip
-// even at one m-tile, and the larger tile reads each operand from L2 half (W)
-// or a quarter (A) as often as the 64 x 64 tile, which is what bounds the
-// 64 x 64 tile once M is large.  Every element's arithmetic is the same in
-// both configurations (one fp32 chain of the same MFMA over k ascending, one
-// rounding at the end), so the tile decides speed, never bits: the choice may
-// read M without making any row depend on the rest of the batch.
+// projection) at small M: 128 (n) x 256 (m) output tile, 2 x 4 wavefronts of
+// 64 x 64, a 3-stage ring of 64-wide K stages (144 KB, one workgroup per CU).
+// Such a weight has at least one 128-row strip per CU, so its stream fills the
+// chip even at one m-tile.
 using GemmWideCfg = GemmCfg<128, 256, 2, 4, 3, 64, 1>;
 constexpr int64_t kGemmWideMinN = 256 * GemmWideCfg::TN;
-// Large-M rule of bi_gemm: at least this many rows and at least one wide tile
-// per CU.  Measured on MI355X with the Qwen3-8B step weights (QKV 4096 -> 6144,
-// up 4096 -> 12288, down 12288 -> 4096): at M = 2300 the wide tile takes 138 /
-// 262 / 338 us against 196 / 377 / 406 us, at M = 1024 it is no slower where
-// it has 256 tiles, and at M = 256 it is 1.2-2.9x slower (too few weight
-// streams).
-constexpr int64_t kGemmWideMinM = 1024;
-constexpr int64_t kGemmWideMinTiles = 256;
 
-// Calls f(Cfg{}) with the configuration of a weight with n rows and returns
-// its result (host code).  Used where the configuration must not depend on M
-// (the fused lm_head, whose workspace holds one record per n-tile).
+// The configuration for large M: 256 x 256 output tile, 2 x 4 wavefronts of
+// 128 (n) x 64 (m), a 2-stage ring of 64-wide K stages (128 KB, one workgroup
+// per CU).  Each wavefront issues 64 MFMAs per stage against 24 fragment reads
+// and one barrier, and the tile reads each operand from L2 half as often as
+// the 128 x 256 tile.  Measured on MI355X against the 128 x 256 tile (same
+// inputs, bitwise equal): Qwen3-8B step weights at M = 2300, QKV 102-110 /
+// 131, up 216-219 / 252, down 279 / 335 us; lm_head (fp32) at M = 512 / 2048,
+// 615-635 / 757 and 2242-2292 / 2738 us.  Deeper rings of 32-wide stages on
+// the same tile (4 or 5 stages) and the 4 x 2 wavefront layout were 2-15 %
+// slower; at M <= 256 this tile is 1.3-4.6x slower (too few weight streams).
+using GemmBigCfg = GemmCfg<256, 256, 2, 4, 2, 64, 1>;
+// Large-M rule: at least this many rows and, for a weight below
+// kGemmWideMinN rows, at least kGemmBigMinTiles tiles of the big grid (the
+// Qwen3-8B QKV weight at M = 1024 has 96 and runs 25 % slower on it than on
+// 64 x 64; at 128 and more - down at 1793 rows, QKV at 1281, up at 1024 - the
+// big tile wins).  For the vocabulary projection the big tile wins from
+// kGemmBigMinMWide rows on (it is 16 % slower at M = 64).
+constexpr int64_t kGemmBigMinM = 1024;
+constexpr int64_t kGemmBigMinTiles = 128;
+constexpr int64_t kGemmBigMinMWide = 512;
+
+// The configuration for small M and weights of at most kGemmNarrowMaxN rows:
+// 16 (n) x 64 (m) tile, 1 x 2 wavefronts of 16 x 32, a 6-stage ring of 64-wide
+// K stages (60 KB, two workgroups per CU).  At decode batch sizes such a
+// weight must be streamed by many workgroups: N / 16 of them instead of N / 64
+// (one CU pulls at most about 50 GB/s from HBM).  Measured on MI355X against
+// the 64 x 64 tile (bitwise equal): down 12288 -> 4096 at M = 1 / 8 / 64, 31.6
+// / 29.3 / 39.6 against 39.6 / 40.2 / 62.7 us; QKV 4096 -> 6144, 11.5 / 11.6
+// / 15.9 against 13.8 / 13.3 / 18.4 us.  The up projection (N = 12288) already
+// has 192 64-row strips and gains nothing; at M = 256 the narrow tile re-reads
+// A N / 16 times and is 1.6-1.7x slower.
+using GemmNarrowCfg = GemmCfg<16, 64, 1, 2, 6, 64, 2>;
+constexpr int64_t kGemmNarrowMaxM = 64;
+constexpr int64_t kGemmNarrowMaxN = 8192;
+
+// Tile rule of the vocabulary-sized weights (N >= kGemmWideMinN) and of the
+// fused lm_head: the big tile from kGemmBigMinMWide rows on, else the wide
+// one.  The fused lm_head's per-row reduction records do not depend on the
+// tile (lm_head.hip), so this choice changes no bit either.
 template <class F>
-inline auto gemm_with_cfg(int64_t n, F&& f) {
-  if (n >= kGemmWideMinN) return f(GemmWideCfg{});
-  return f(GemmLibraryCfg{});
+inline auto gemm_with_cfg_wide(int64_t lda, int64_t ldw, int64_t m, int64_t k, F&& f) {
+  if (m >= kGemmBigMinMWide && gemm_offsets_fit<GemmBigCfg>(lda, ldw, k)) return f(GemmBigCfg{});
+  return f(GemmWideCfg{});
 }
 
-// bi_gemm's configuration: the wide tile for wide weights, and also for any
-// weight once M reaches kGemmWideMinM rows and the wide grid has at least
-// kGemmWideMinTiles tiles, where the wide tile's operand offsets fit its
-// buffer resources (else the 64 x 64 tile, whose bits are the same).
+// bi_gemm's configuration.  Every configuration computes every output element
+// with the same fp32 chain of v_mfma_f32_16x16x32_bf16 steps over k = 0, 32,
+// 64, ... and one rounding, so the tile decides speed, never bits: the choice
+// may read M without making any row depend on the rest of the batch (the
+// tests compare whole products bitwise across every threshold below).
+//   N >= kGemmWideMinN:                                     gemm_with_cfg_wide
+//   M >= kGemmBigMinM and >= kGemmBigMinTiles big tiles:    256 x 256
+//   M <= kGemmNarrowMaxM and N <= kGemmNarrowMaxN:          16 x 64
+//   otherwise:                                              64 x 64
+// (a configuration whose tile offsets would not fit its buffer resources is
+// skipped for the next one; the 64 x 64 tile is checked by the caller).
 template <class F>
 inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, F&& f) {
-  using Wd = GemmWideCfg;
-  const bool large_m = m >= kGemmWideMinM &&
-                       ((m + Wd::TM - 1) / Wd::TM) * ((n + Wd::TN - 1) / Wd::TN) >= kGemmWideMinTiles &&
-                       gemm_offsets_fit<Wd>(lda, ldw, k);
-  if (n >= kGemmWideMinN || large_m) return f(Wd{});
+  using Bg = GemmBigCfg;
+  if (n >= kGemmWideMinN) return gemm_with_cfg_wide(lda, ldw, m, k, f);
+  const bool big = m >= kGemmBigMinM &&
+                   ((m + Bg::TM - 1) / Bg::TM) * ((n + Bg::TN - 1) / Bg::TN) >= kGemmBigMinTiles &&
+                   gemm_offsets_fit<Bg>(lda, ldw, k);
+  if (big) return f(Bg{});
+  if (m <= kGemmNarrowMaxM && n <= kGemmNarrowMaxN) return f(GemmNarrowCfg{});
   return f(GemmLibraryCfg{});
 }
 

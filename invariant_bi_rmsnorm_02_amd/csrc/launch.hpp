@@ -64,7 +64,9 @@ hipError_t launch_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids,
 hipError_t launch_moe_route(const void* x, int64_t ldx, const void* w_gate, int T, int H, int E, int top_k,
                             float* logits, int32_t* expert_ids, float* expert_weights, hipStream_t stream);
 
-// lm_head + log_softmax fused into the GEMM epilogue (lm_head.hip).
+// lm_head + log_softmax fused into the GEMM epilogue (lm_head.hip).  False
+// when the tile count or a workgroup's buffer offsets would overflow.
+bool lm_head_supported(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k);
 size_t lm_head_workspace_bytes(int64_t m, int64_t n);
 size_t lm_head_greedy_workspace_bytes(int64_t m, int64_t n);
 // Elementwise steps of the decoder layer (pointwise.hip).

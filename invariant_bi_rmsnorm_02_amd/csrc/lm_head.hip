@@ -4,22 +4,25 @@
 // Nondeterminism in LLM Inference", section "2. Batch-Invariant Matrix
 // Multiplication" for the product itself).
 //
-//   z[m, n]  = sum_k a[m, k] w[n, k]          (the library GEMM: bi_gemm's tile
-//                                              for this n, same fp32 MFMA
-//                                              chain per element)
+//   z[m, n]  = sum_k a[m, k] w[n, k]          (the library GEMM: the same fp32
+//                                              MFMA chain per element as
+//                                              bi_gemm, in any of its tiles)
 //   out[m, n] = z[m, n] - lse[m],   lse[m] = log sum_n e^z[m, n]
 //
 // Two kernels, one fixed reduction tree for lse that depends on n alone:
-//  1. the GEMM writes z into `out` and, for every (row, n-tile), the pair
-//     (max, sum e^(z - max)) of the row's values in the tile (64 columns, or
-//     128 for a weight of at least kGemmWideMinN rows: the tile is a function
-//     of n): each lane folds its values in column order, lanes l ^ 16 and
-//     l ^ 32 are combined, then the tile's n-wavefronts in ascending order;
-//  2. every workgroup of a row folds the row's tile pairs (thread t: tiles t,
-//     t + 1024, ... in order; a butterfly over the wavefront; the 16 wavefront
-//     results in ascending order) and subtracts lse from its segment of the
-//     row in place.  A row is split into several segments when there are few
-//     rows (scheduling only: every workgroup of a row computes the same lse).
+//  1. the GEMM writes z into `out` and, for every (row, record), the pair
+//     (max, sum e^(z - max)) of the row's values in the record's columns.  A
+//     record is 64 columns, or 128 for a weight of at least kGemmWideMinN rows,
+//     made of two units of half that width: each lane folds its values of a
+//     unit in column order, lanes l ^ 16 and l ^ 32 are combined, then the
+//     record's two units in ascending order.  Records and units are a function
+//     of n alone, whichever GEMM tile computes them (the tile may follow M:
+//     gemm_with_cfg_wide), so every tile writes the same pairs;
+//  2. every workgroup of a row folds the row's record pairs (thread t:
+//     records t, t + 1024, ... in order; a butterfly over the wavefront; the 16
+//     wavefront results in ascending order) and subtracts lse from its segment
+//     of the row in place.  A row is split into several segments when there are
+//     few rows (scheduling only: every workgroup of a row computes the same lse).
 // Every row's result is a function of its own z values only, so it does not
 // depend on the batch.  z is read and written once more (8 bytes per logit)
 // instead of the 12 of a separate log_softmax pass.
@@ -44,12 +47,29 @@ constexpr int kFinThreads = 1024;
 constexpr int64_t kFinBlocks = 512;    // finalize workgroups aimed at when rows are few
 constexpr int64_t kFinSegsMax = 256;
 
-template <class Cfg, class Pair>
+// Record geometry of a weight with n rows: a record is the n-tile of the tile
+// bi_gemm used for such weights at small M (128 columns from kGemmWideMinN
+// rows on, else 64), a unit is one wavefront's columns of that tile.
+template <int REC_, int UNIT_>
+struct LseGeom {
+  static constexpr int REC = REC_, UNIT = UNIT_;
+};
+using LseGeomWide = LseGeom<GemmWideCfg::TN, GemmWideCfg::WTN>;
+using LseGeomNarrow = LseGeom<GemmLibraryCfg::TN, GemmLibraryCfg::WTN>;
+
+template <class Cfg, class Geom, class Pair>
 __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void lm_head_lse_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
     float* __restrict__ Z, int64_t ldz, Pair* __restrict__ part, int M, int N, int K, int tiles_m, int tiles_n,
-    int vec_store) {
+    int recs_n, int vec_store) {
   constexpr bool kArg = std::is_same<Pair, MaxSumArg>::value;
+  constexpr int UNIT = Geom::UNIT, REC = Geom::REC;
+  constexpr int UPW = Cfg::WTN / UNIT;    // units per wavefront
+  constexpr int NBU = UNIT / 16;          // MFMA column blocks per unit
+  constexpr int UPT = Cfg::TN / UNIT;     // units per tile
+  constexpr int UPR = REC / UNIT;         // units per record
+  constexpr int RPT = Cfg::TN / REC;      // records per tile
+  static_assert(Cfg::WTN % UNIT == 0 && UNIT % 16 == 0 && REC % UNIT == 0 && Cfg::TN % REC == 0, "record geometry");
 
   int tile_m, tile_n;
   gemm_map_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
@@ -80,11 +100,11 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void lm_head_lse_kernel(
     });
   }
 
-  // Tile pairs.  Lane (l16, g) of wavefront (wn, wm) holds, for m-block j,
+  // Unit pairs.  Lane (l16, g) of wavefront (wn, wm) holds, for m-block j,
   // row wm * WTM + 16 j + l16 at columns wn * WTN + 16 i + 4 g + e.  The
-  // wavefronts exchange them through the ring's first W stage, which the main
-  // loop has finished with (it ends with every load landed and a barrier).
-  using Xw = Pair[Cfg::WGN][Cfg::WGM][Cfg::MB][16];
+  // pairs are exchanged through the ring's first W stage, which the main loop
+  // has finished with (it ends with every load landed and a barrier).
+  using Xw = Pair[UPT][Cfg::TM];
   static_assert(sizeof(Xw) <= Cfg::TN * Cfg::BK * sizeof(uint16_t), "exchange fits the ring stage");
   Xw& xw = *reinterpret_cast<Xw*>(GemmRing<Cfg>::template w<0>());
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -92,51 +112,54 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void lm_head_lse_kernel(
   const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int j = 0; j < Cfg::MB; ++j) {
-    float v[Cfg::NB * 4];
 #pragma unroll
-    for (int i = 0; i < Cfg::NB; ++i)
+    for (int u = 0; u < UPW; ++u) {
+      const int c0 = n0 + wn * Cfg::WTN + u * UNIT;   // first column of the unit
+      float v[NBU * 4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int n = n0 + wn * Cfg::WTN + 16 * i + 4 * g + e;
-        v[4 * i + e] = n < N ? acc[i][j][e] : -INFINITY;
+      for (int i = 0; i < NBU; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = c0 + 16 * i + 4 * g + e;
+          v[4 * i + e] = n < N ? acc[u * NBU + i][j][e] : -INFINITY;
+        }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < NBU * 4; ++q) mx = fmaxf(mx, v[q]);
+      // Column order; every term is >= 0 and never -0, so starting from the
+      // first term is 0 + term to the bit.  All-masked lanes (mx = -inf) hold 0.
+      float s = mx == -INFINITY ? 0.0f : exp2_hw((v[0] - mx) * kLog2e);
+#pragma unroll
+      for (int q = 1; q < NBU * 4; ++q) s = s + (mx == -INFINITY ? 0.0f : exp2_hw((v[q] - mx) * kLog2e));
+      Pair t;
+      if constexpr (kArg) {
+        // The lane's lowest column holding its maximum (columns rise with q).
+        int ix = INT_MAX;
+#pragma unroll
+        for (int q = NBU * 4 - 1; q >= 0; --q)
+          if (v[q] == mx && mx != -INFINITY) ix = c0 + 16 * (q >> 2) + 4 * g + (q & 3);
+        t = combine_xor32(combine_xor16(MaxSumArg{mx, s, ix}));
+      } else {
+        t = combine_xor32(combine_xor16(MaxSum{mx, s}));
       }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < Cfg::NB * 4; ++q) mx = fmaxf(mx, v[q]);
-    // Column order; every term is >= 0 and never -0, so starting from the
-    // first term is 0 + term to the bit.  All-masked lanes (mx = -inf) hold 0.
-    float s = mx == -INFINITY ? 0.0f : exp2_hw((v[0] - mx) * kLog2e);
-#pragma unroll
-    for (int q = 1; q < Cfg::NB * 4; ++q) s = s + (mx == -INFINITY ? 0.0f : exp2_hw((v[q] - mx) * kLog2e));
-    Pair t;
-    if constexpr (kArg) {
-      // The lane's lowest column holding its maximum (columns rise with q).
-      int ix = INT_MAX;
-#pragma unroll
-      for (int q = Cfg::NB * 4 - 1; q >= 0; --q)
-        if (v[q] == mx && mx != -INFINITY) ix = n0 + wn * Cfg::WTN + 16 * (q >> 2) + 4 * g + (q & 3);
-      t = combine_xor32(combine_xor16(MaxSumArg{mx, s, ix}));
-    } else {
-      t = combine_xor32(combine_xor16(MaxSum{mx, s}));
+      if (g == 0) xw[wn * UPW + u][wm * Cfg::WTM + 16 * j + l16] = t;
     }
-    if (g == 0) xw[wn][wm][j][l16] = t;
   }
   __syncthreads();
-  if (wn == 0 && g == 0) {
+  // A record's units in ascending order, one (record, row) per thread.
+  for (int idx = threadIdx.x; idx < RPT * Cfg::TM; idx += Cfg::kThreads) {
+    const int r = idx / Cfg::TM, row = idx - r * Cfg::TM;
+    const int rec = n0 / REC + r;
+    if (row >= rows_a || rec >= recs_n) continue;
+    Pair t = xw[r * UPR][row];
 #pragma unroll
-    for (int j = 0; j < Cfg::MB; ++j) {
-      const int row = wm * Cfg::WTM + 16 * j + l16;
-      if (row >= rows_a) continue;
-      Pair t = xw[0][wm][j][l16];
-#pragma unroll
-      for (int w = 1; w < Cfg::WGN; ++w) t = combine(t, xw[w][wm][j][l16]);
-      part[(int64_t)(m0 + row) * tiles_n + tile_n] = t;
-    }
+    for (int u = 1; u < UPR; ++u) t = combine(t, xw[r * UPR + u][row]);
+    part[(int64_t)(m0 + row) * recs_n + rec] = t;
   }
 }
 
-// The row's pairs folded in one fixed tree that depends on tiles_n alone:
-// thread t takes tiles t, t + 1024, ... in order; a butterfly over the
+// The row's pairs folded in one fixed tree that depends on tiles_n (the
+// record count) alone: thread t takes records t, t + 1024, ... in order; a butterfly over the
 // wavefront; the 16 wavefront results in ascending order.  Every thread of the
 // workgroup returns the total.
 template <class Pair>
@@ -187,12 +210,46 @@ __global__ __launch_bounds__(kFinThreads) void greedy_finalize_kernel(const MaxS
   }
 }
 
-// n-tiles of the GEMM configuration bi_gemm uses for this n: the row's pairs.
+// Records of a row: the row's pairs.
 int lse_tiles(int64_t n) {
-  return gemm_with_cfg(n, [&](auto cfg) { return static_cast<int>((n + decltype(cfg)::TN - 1) / decltype(cfg)::TN); });
+  const int64_t rec = n >= kGemmWideMinN ? LseGeomWide::REC : LseGeomNarrow::REC;
+  return static_cast<int>((n + rec - 1) / rec);
+}
+
+// Launches lm_head_lse_kernel with the GEMM tile of gemm_with_cfg_wide (wide
+// weights) or the 64 x 64 tile, and the record geometry of n.
+template <class Pair>
+hipError_t launch_lse_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, float* out, int64_t ldo,
+                           Pair* part, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  const int recs_n = lse_tiles(n);
+  auto go = [&](auto cfg, auto geom) {
+    using Cfg = decltype(cfg);
+    using Geom = decltype(geom);
+    if (!gemm_offsets_fit<Cfg>(lda, ldw, k)) return hipErrorInvalidValue;
+    const int tiles_m = static_cast<int>((m + Cfg::TM - 1) / Cfg::TM);
+    const int tiles_n = static_cast<int>((n + Cfg::TN - 1) / Cfg::TN);
+    hipLaunchKernelGGL((lm_head_lse_kernel<Cfg, Geom, Pair>), dim3(static_cast<unsigned>(tiles_m * tiles_n)),
+                       dim3(Cfg::kThreads), 0, stream, static_cast<const uint16_t*>(a), lda,
+                       static_cast<const uint16_t*>(w), ldw, out, ldo, part, (int)m, (int)n, (int)k, tiles_m,
+                       tiles_n, recs_n, 1);
+    return hipGetLastError();
+  };
+  if (n >= kGemmWideMinN)
+    return gemm_with_cfg_wide(lda, ldw, m, k, [&](auto cfg) { return go(cfg, LseGeomWide{}); });
+  return go(GemmLibraryCfg{}, LseGeomNarrow{});
 }
 
 }  // namespace
+
+bool lm_head_supported(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k) {
+  auto ok = [&](auto cfg) {
+    using C = decltype(cfg);
+    const int64_t tiles = ((m + C::TM - 1) / C::TM) * ((n + C::TN - 1) / C::TN);
+    return tiles <= 0x7fffffff && gemm_offsets_fit<C>(lda, ldw, k);
+  };
+  if (n >= kGemmWideMinN) return gemm_with_cfg_wide(lda, ldw, m, k, ok);
+  return ok(GemmLibraryCfg{});
+}
 
 size_t lm_head_workspace_bytes(int64_t m, int64_t n) {
   const size_t bytes = static_cast<size_t>(m) * static_cast<size_t>(lse_tiles(n)) * sizeof(MaxSum);
@@ -205,16 +262,7 @@ hipError_t launch_lm_head_logprobs(const void* a, int64_t lda, const void* w, in
   if (m == 0 || n == 0) return hipSuccess;
   const int tiles_n = lse_tiles(n);
   auto* part = static_cast<MaxSum*>(workspace);
-  hipError_t e = gemm_with_cfg(n, [&](auto cfg) {
-    using Cfg = decltype(cfg);
-    if (!gemm_offsets_fit<Cfg>(lda, ldw, k)) return hipErrorInvalidValue;
-    const int tiles_m = static_cast<int>((m + Cfg::TM - 1) / Cfg::TM);
-    hipLaunchKernelGGL((lm_head_lse_kernel<Cfg, MaxSum>), dim3(static_cast<unsigned>(tiles_m * tiles_n)),
-                       dim3(Cfg::kThreads), 0, stream, static_cast<const uint16_t*>(a), lda,
-                       static_cast<const uint16_t*>(w), ldw, out, ldo, part, (int)m, (int)n, (int)k, tiles_m,
-                       tiles_n, 1);
-    return hipGetLastError();
-  });
+  hipError_t e = launch_lse_gemm(a, lda, w, ldw, out, ldo, part, m, n, k, stream);
   if (e != hipSuccess) return e;
   // Segments per row: enough workgroups to spread few rows over the GPU.
   const int segs = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({kFinSegsMax, (kFinBlocks + m - 1) / m,
@@ -235,16 +283,7 @@ hipError_t launch_lm_head_greedy(const void* a, int64_t lda, const void* w, int6
   if (m == 0 || n == 0) return hipSuccess;
   const int tiles_n = lse_tiles(n);
   auto* part = static_cast<MaxSumArg*>(workspace);
-  hipError_t e = gemm_with_cfg(n, [&](auto cfg) {
-    using Cfg = decltype(cfg);
-    if (!gemm_offsets_fit<Cfg>(lda, ldw, k)) return hipErrorInvalidValue;
-    const int tiles_m = static_cast<int>((m + Cfg::TM - 1) / Cfg::TM);
-    hipLaunchKernelGGL((lm_head_lse_kernel<Cfg, MaxSumArg>), dim3(static_cast<unsigned>(tiles_m * tiles_n)),
-                       dim3(Cfg::kThreads), 0, stream, static_cast<const uint16_t*>(a), lda,
-                       static_cast<const uint16_t*>(w), ldw, nullptr, 0, part, (int)m, (int)n, (int)k, tiles_m,
-                       tiles_n, 1);
-    return hipGetLastError();
-  });
+  hipError_t e = launch_lse_gemm(a, lda, w, ldw, static_cast<float*>(nullptr), 0, part, m, n, k, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(greedy_finalize_kernel, dim3(static_cast<unsigned>(m)), dim3(kFinThreads), 0, stream, part,
                      tiles_n, token, logprob);

@@ -159,15 +159,15 @@ def test_gemm_fp32_lm_head_invariance():
 
 
 def test_gemm_wide_tile_gives_the_same_bits():
-    """A weight of at least 32768 rows runs the 128 x 256 tile, a narrower one
-    the 64 x 64 tile; both take every element's fp32 MFMA chain over k in the
-    same order, so the tile changes no bit.  The same columns computed as one
+    """A weight of at least 32768 rows runs the 128 x 256 tile (256 x 256 from
+    512 rows on), a narrower one the 64 x 64 tile; all take every element's
+    fp32 MFMA chain over k in the same order, so the tile changes no bit.  The same columns computed as one
     wide weight and as two narrow slices must agree bitwise (bf16 and fp32
     outputs, ragged m and n tails), and integer inputs must give the oracle
     rounded once on the wide path too."""
     k, n = 320, 32768 + 200
     w = W.randn_bf16((n, k), 11, "w", 1, std=0.05, device=DEV)
-    for m in (1, 37, 300):
+    for m in (1, 37, 300, 600):
         log_case(f"gemm wide tile m={m} n={n} k={k}")
         a = W.randn_bf16((m, k), 11, "x", m, device=DEV)
         cut = n // 2
@@ -185,7 +185,7 @@ def test_gemm_wide_tile_gives_the_same_bits():
 
 @pytest.mark.parametrize("n,k", [(12288 + 72, 4096), (4096, 12288), (6144, 4096)])
 def test_gemm_large_m_rule_gives_the_same_bits(n, k):
-    """From 1024 rows on, a weight whose 128 x 256 grid has at least 256 tiles
+    """From 1024 rows on, a weight whose 256 x 256 grid has at least 128 tiles
     runs that tile instead of 64 x 64 (the Qwen3-8B step weights at M = 2300;
     the up projection, with a ragged n tail, already at M = 1024).  The whole
     product at M in {1024, 1100, 2300} must equal, bit for bit, the same rows
@@ -204,12 +204,12 @@ def test_gemm_large_m_rule_gives_the_same_bits(n, k):
 
 
 @pytest.mark.parametrize("n,k,m_lo,m_hi", [
-    (12288, 4096, 1023, 1024),   # up projection: 96 wide n-tiles, so the 1024-row rule decides
-    (6144, 4096, 1280, 1281),    # QKV: 48 n-tiles x 5 / 6 m-tiles = 240 / 288 wide tiles
-    (4096, 12288, 1792, 1793)])  # down: 32 n-tiles x 7 / 8 m-tiles = 224 / 256 wide tiles
+    (12288, 4096, 1023, 1024),   # up projection: 48 big n-tiles, so the 1024-row rule decides
+    (6144, 4096, 1280, 1281),    # QKV: 24 n-tiles x 5 / 6 m-tiles = 120 / 144 big tiles
+    (4096, 12288, 1792, 1793)])  # down: 16 n-tiles x 7 / 8 m-tiles = 112 / 128 big tiles
 def test_gemm_tile_rule_edges(n, k, m_lo, m_hi):
-    """bi_gemm runs the 64 x 64 tile at m_lo and the 128 x 256 tile at m_hi
-    (the large-M rule: at least 1024 rows and at least 256 wide tiles).  The
+    """bi_gemm runs the 64 x 64 tile at m_lo and the 256 x 256 tile at m_hi
+    (the large-M rule: at least 1024 rows and at least 128 big tiles).  The
     rows the two products share, and both products against the same rows in
     256-row slices (64 x 64 tile), must agree bit for bit."""
     w = W.randn_bf16((n, k), 13, "w", n, std=0.02, device=DEV)
@@ -222,6 +222,30 @@ def test_gemm_tile_rule_edges(n, k, m_lo, m_hi):
         assert_bitwise(hi[:m_lo], lo, f"rows shared by m={m_lo} and m={m_hi} ({dt})")
         assert_bitwise(hi, sliced, f"m={m_hi} vs 256-row slices ({dt})")
         assert_bitwise(lo, sliced[:m_lo], f"m={m_lo} vs 256-row slices ({dt})")
+
+
+@pytest.mark.parametrize("n,k", [(4096, 12288), (6144, 4096), (8192, 512), (8200, 512), (12288, 4096)])
+def test_gemm_narrow_tile_edges(n, k):
+    """Up to 64 rows a weight of at most 8192 rows runs the 16 x 64 tile, from
+    65 rows (or above 8192 weight rows) the 64 x 64 one.  Rows shared by
+    M = 1, 64 and 65, and 32-row slices, must agree bit for bit, and
+    integer inputs must give the oracle rounded once on the narrow path."""
+    w = W.randn_bf16((n, k), 14, "w", n, std=0.02, device=DEV)
+    a = W.randn_bf16((65, k), 14, "x", k, device=DEV)
+    log_case(f"gemm narrow tile edge n={n} k={k}")
+    for dt in (torch.bfloat16, torch.float32):
+        c65 = bi.bi_gemm(a, w, out_dtype=dt)
+        c64 = bi.bi_gemm(a[:64].contiguous(), w, out_dtype=dt)
+        c1 = bi.bi_gemm(a[:1].contiguous(), w, out_dtype=dt)
+        sl = torch.cat([bi.bi_gemm(a[r:r + 32].contiguous(), w, out_dtype=dt) for r in range(0, 65, 32)])
+        assert_bitwise(c65[:64], c64, f"rows at M=64 vs M=65 ({dt})")
+        assert_bitwise(c65[:1], c1, f"row 0 at M=1 vs M=65 ({dt})")
+        assert_bitwise(c65, sl, f"M=65 vs 32-row slices ({dt})")
+    ref = O.gemm(f64(a[:64:16]), f64(w[::37]))
+    assert_bf16_close(bi.bi_gemm(a[:64].contiguous(), w)[::16, ::37], ref, f"narrow tile parity n={n}")
+    ai, wi = _int_bf16((7, 256), 15), _int_bf16((n, 256), 16)
+    want = torch.from_numpy(O.f64_to_bf16_bits(O.gemm(f64(ai), f64(wi))).view(np.int16))
+    assert torch.equal(bi.bi_gemm(ai.to(DEV), wi.to(DEV)).view(torch.int16).cpu(), want)
 
 
 def test_gemm_wide_tile_batch_invariance():

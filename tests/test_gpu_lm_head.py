@@ -91,12 +91,13 @@ def test_lm_head_logprobs_batch_invariance():
 
 
 def test_lm_head_full_vocab_batch_invariance():
-    """The lm_head at the workload's size (4096 -> 151936, the wide tile):
-    token 0's logprobs row, greedy token and token logprob bitwise the same at
-    T = 1, 64, 512, 2048 and shuffled slots."""
+    """The lm_head at the workload's size (4096 -> 151936): token 0's logprobs
+    row, greedy token and token logprob bitwise the same at T = 1, 64, 511
+    (128 x 256 GEMM tile), 512, 2048 (256 x 256 tile) and shuffled slots; the
+    per-row reduction records do not depend on the tile."""
     w = _weights(V)
     ref = gref = None
-    for T, pos in ((1, 0), (64, 50), (512, 0), (2048, 1500)):
+    for T, pos in ((1, 0), (64, 50), (511, 510), (512, 0), (2048, 1500)):
         log_case(f"full-vocab lm_head invariance T={T} slot={pos}")
         ids = list(range(1, T))
         ids.insert(pos, 0)
@@ -208,3 +209,29 @@ def test_lm_head_greedy_batch_invariance_and_workspace():
     with pytest.raises(bi.BiError) as e:
         bi.bi_lm_head_greedy(W.rows_for_requests(range(4), K, W.SEED_MOE, device=DEV), w, workspace=ws[:64])
     assert e.value.status == bi.BI_ERR_WORKSPACE
+
+
+def test_lm_head_tile_switch_edge():
+    """Rows shared by T = 511 (128 x 256 tile) and T = 512 (256 x 256 tile):
+    bitwise equal logprobs, lse and greedy results, on a vocabulary with a
+    ragged last record (32768 + 200 columns: the big tile's last n-tile holds
+    one partial record and one past the end)."""
+    n = 32768 + 200
+    w = _weights(n, 512)
+    a = W.rows_for_requests(range(512), 512, W.SEED_MOE, device=DEV)
+    lse_lo = torch.empty(511, dtype=torch.float32, device=DEV)
+    lse_hi = torch.empty(512, dtype=torch.float32, device=DEV)
+    lo = bi.bi_lm_head_logprobs(a[:511].contiguous(), w, lse=lse_lo)
+    hi = bi.bi_lm_head_logprobs(a, w, lse=lse_hi)
+    assert_bitwise(hi[:511], lo, "logprobs rows at T=511 vs T=512")
+    assert_bitwise(lse_hi[:511], lse_lo, "lse at T=511 vs T=512")
+    t_lo, p_lo = bi.bi_lm_head_greedy(a[:511].contiguous(), w, logprob=torch.empty(511, dtype=torch.float32, device=DEV))
+    t_hi, p_hi = bi.bi_lm_head_greedy(a, w, logprob=torch.empty(512, dtype=torch.float32, device=DEV))
+    assert_bitwise(t_hi[:511], t_lo, "greedy tokens at T=511 vs T=512")
+    assert_bitwise(p_hi[:511], p_lo, "greedy logprobs at T=511 vs T=512")
+    ref_lp, ref_lse = _ref(a[::97], w)
+    assert_f32_close(hi[::97], ref_lp, "logprobs (big tile) vs oracle")
+    assert_f32_close(lse_hi[::97], ref_lse, "lse (big tile) vs oracle")
+    z = bi.bi_gemm(a, w, out_dtype=torch.float32)
+    zlo = bi.bi_gemm(a[:511].contiguous(), w, out_dtype=torch.float32)
+    assert_bitwise(z[:511], zlo, "fp32 logits at T=511 vs T=512")
