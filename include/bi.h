@@ -227,14 +227,24 @@ bi_status bi_attn_decode_noalloc(const void* q, int64_t ld_q, const void* k_cach
  * fp32 or NULL.  q_start: [num_seqs + 1] int32, non-decreasing from 0;
  * ctx_lens: [num_seqs] int32.  max_q_len: host-side upper bound of n_s (sizes
  * the grid; longer chunks are clamped to it).  Same size limits as decode.
+ * workspace: NULL, or at least bi_attn_prefill_workspace_bytes(num_seqs)
+ *   bytes of device memory, 16-byte aligned, owned by the caller, contents on
+ *   entry irrelevant (else BI_ERR_WORKSPACE).  With it and more than 16
+ *   sequences, a small kernel first ranks the sequences (longest last key
+ *   first) into a table the attention workgroups read to place their work;
+ *   otherwise every workgroup ranks the sequences itself (num_seqs^2 / 64
+ *   steps each - fine for a few sequences, costly for hundreds).  Placement
+ *   only: the results are the same bits either way.  Concurrent calls need
+ *   separate workspaces.
  */
+size_t bi_attn_prefill_workspace_bytes(int32_t num_seqs);
 bi_status bi_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens,
                           int32_t num_seqs, int32_t max_q_len,
                           const void* k_cache, const void* v_cache, int32_t num_pages,
                           const int32_t* block_table, int32_t max_pages_per_seq,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t page_size, float softmax_scale, void* out, float* lse,
-                          bi_stream_t stream);
+                          void* workspace, size_t workspace_bytes, bi_stream_t stream);
 
 /*
  * Mixture-of-experts FFN over a batch of tokens (the routed expert layer of the

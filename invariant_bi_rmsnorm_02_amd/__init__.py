@@ -37,8 +37,9 @@ _SIGNATURES = {
                                 _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_size, _c_p]),
     "bi_attn_decode_noalloc": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i32, _c_i32,
                                         _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p]),
+    "bi_attn_prefill_workspace_bytes": (_c_size, [_c_i32]),
     "bi_attn_prefill": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_i32,
-                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p]),
+                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_p, _c_p, _c_p, _c_size, _c_p]),
     "bi_log_softmax": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_moe_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "bi_moe_route": (_c_i32, [_c_p, _c_i64, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p]),
@@ -277,11 +278,18 @@ def bi_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     return out, lse
 
 
+def bi_attn_prefill_workspace_bytes(num_seqs: int) -> int:
+    return int(lib().bi_attn_prefill_workspace_bytes(num_seqs))
+
+
 def bi_attn_prefill(q: torch.Tensor, q_start: torch.Tensor, ctx_lens: torch.Tensor, max_q_len: int,
                     k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                     softmax_scale: float, out: Optional[torch.Tensor] = None,
-                    lse: Optional[torch.Tensor] = None, stream=None):
-    """Chunked-prefill attention; returns (out, lse)."""
+                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    order_table: bool = True, stream=None):
+    """Chunked-prefill attention; returns (out, lse).  The workspace holds the
+    placement order table (allocated here when not given); order_table=False
+    passes none, and the kernel ranks the sequences itself."""
     pages, hkv, ps, d = _cache_geom(k_cache, v_cache)
     _dev(q, "q", torch.bfloat16)
     _dev(q_start, "q_start", torch.int32)
@@ -305,10 +313,19 @@ def bi_attn_prefill(q: torch.Tensor, q_start: torch.Tensor, ctx_lens: torch.Tens
         _dev(lse, "lse", torch.float32)
         if lse.shape != (t, hq) or not lse.is_contiguous():
             raise ValueError("lse must be [T, Hq]")
+    ws_ptr, ws_bytes = None, 0
+    if order_table:
+        if workspace is None:
+            workspace = torch.empty((max(bi_attn_prefill_workspace_bytes(s), 256),), dtype=torch.uint8,
+                                    device=q.device)
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check("bi_attn_prefill", lib().bi_attn_prefill(
         q.data_ptr(), ldq, q_start.data_ptr(), ctx_lens.data_ptr(), s, int(max_q_len), k_cache.data_ptr(),
         v_cache.data_ptr(), pages, block_table.data_ptr(), block_table.shape[1], hq, hkv, d, ps,
-        float(softmax_scale), out.data_ptr(), lse.data_ptr() if lse is not None else None, _stream(stream)))
+        float(softmax_scale), out.data_ptr(), lse.data_ptr() if lse is not None else None, ws_ptr, ws_bytes,
+        _stream(stream)))
     return out, lse
 
 

@@ -136,7 +136,7 @@ bi_status bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new, con
   if (head_dim != 64 && head_dim != 128) return BI_ERR_UNSUPPORTED;
   const int l2 = log2_exact(page_size);
   if (l2 < 4 || l2 > 8) return BI_ERR_UNSUPPORTED;
-  if ((int64_t)num_pages * page_size > 0x7fffffff) return BI_ERR_UNSUPPORTED;
+  if ((int64_t)num_pages * page_size > 0x7fffffff || num_kv_heads > 65535) return BI_ERR_UNSUPPORTED;
   if (ld_new < (int64_t)num_kv_heads * head_dim || ld_new % 8) return BI_ERR_INVALID_ARG;
   return from_hip(bi::launch_kv_append(k_new, v_new, ld_new, slot_mapping, num_tokens, k_cache, v_cache,
                                        num_pages, num_kv_heads, head_dim, page_size, as_stream(stream)));
@@ -193,7 +193,7 @@ bi_status bi_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, c
                           int32_t num_pages, const int32_t* block_table, int32_t max_pages_per_seq,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t page_size, float softmax_scale, void* out, float* lse,
-                          bi_stream_t stream) {
+                          void* workspace, size_t workspace_bytes, bi_stream_t stream) {
   if (num_seqs < 0 || max_q_len < 0) return BI_ERR_INVALID_ARG;
   if (num_seqs == 0 || max_q_len == 0) return BI_OK;
   bi_status st = check_attn_geom(k_cache, v_cache, num_pages, block_table, max_pages_per_seq,
@@ -204,10 +204,17 @@ bi_status bi_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, c
   if (ld_q < (int64_t)num_q_heads * head_dim || ld_q % 8) return BI_ERR_INVALID_ARG;
   if (num_seqs > 65535 || num_kv_heads > 65535) return BI_ERR_UNSUPPORTED;
   if ((int64_t)max_q_len * (num_q_heads / num_kv_heads) > (1 << 30)) return BI_ERR_UNSUPPORTED;
+  if (workspace && (!aligned16(workspace) || workspace_bytes < bi::attn_prefill_workspace_bytes(num_seqs)))
+    return BI_ERR_WORKSPACE;
   const bi::AttnGeom g = make_geom(k_cache, v_cache, num_pages, block_table, max_pages_per_seq,
                                    num_q_heads, num_kv_heads, head_dim, page_size, softmax_scale);
-  return from_hip(bi::launch_attn_prefill(q, ld_q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse,
+  return from_hip(bi::launch_attn_prefill(q, ld_q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse, workspace,
                                           as_stream(stream)));
+}
+
+size_t bi_attn_prefill_workspace_bytes(int32_t num_seqs) {
+  if (num_seqs <= 0) return 0;
+  return bi::attn_prefill_workspace_bytes(num_seqs);
 }
 
 bi_status bi_log_softmax(const float* logits, int64_t ld_in, float* out, int64_t ld_out, int64_t rows,

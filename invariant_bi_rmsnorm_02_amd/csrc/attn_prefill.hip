@@ -69,7 +69,8 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, const int32_t* __restrict__ q_start,
     const int32_t* __restrict__ ctx_lens, int num_seqs, int tiles, int max_q_len, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int num_pages, const int32_t* __restrict__ block_table, int max_pages,
-    int Hq, int Hkv, int log2_ps, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int Hq, int Hkv, int log2_ps, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const int32_t* __restrict__ order) {
   constexpr int TE = kTile * D;                          // elements per tile
   constexpr int kPieces = 2 * TE * 2 / 1024;             // 1 KB loads per sub-block of K (two tiles); V the same
   constexpr int IPW = kPieces / kWaves;                  // ... per wavefront
@@ -101,7 +102,10 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
   const int rank = item / tiles, tile = tiles - 1 - item % tiles;
   auto seq_key = [&](int j) { return ctx_lens[j] + min(q_start[j + 1] - q_start[j], max_q_len); };
   int sq = 0;
-  for (int base = 0; base < num_seqs; base += kWave) {
+  // The sequence of this rank: from the order table when prefill_order_kernel
+  // wrote one, else ranked here (every sequence against every other).
+  if (order != nullptr) sq = order[rank];
+  for (int base = 0; order == nullptr && base < num_seqs; base += kWave) {
     const int i = base + lane;
     const int ki = i < num_seqs ? seq_key(i) : 0;
     int r = 0;   // sequences ordered before sequence i
@@ -354,9 +358,39 @@ __global__ __launch_bounds__(kThreads, OCC) void attn_prefill_kernel(
 // LDS <= 80 KB each) and column block 0's fold state in registers.
 constexpr int kLibRegFold = 1, kLibOcc = 2;
 
+// The prefill kernel's placement order: order[rank] = the sequence of that
+// rank, sequences ranked by descending last key, ties by index (the ranking
+// the prefill kernel otherwise computes in every workgroup).  One thread per
+// sequence counts the sequences ordered before it, reading the keys 256 at a
+// time from LDS; the ranks form a permutation, so every entry is written once.
+constexpr int kOrderThreads = 256;
+constexpr int kOrderMinSeqs = 16;
+__global__ __launch_bounds__(kOrderThreads) void prefill_order_kernel(const int32_t* __restrict__ q_start,
+                                                                      const int32_t* __restrict__ ctx_lens,
+                                                                      int num_seqs, int max_q_len,
+                                                                      int32_t* __restrict__ order) {
+  __shared__ int keys[kOrderThreads];
+  auto seq_key = [&](int j) { return ctx_lens[j] + min(q_start[j + 1] - q_start[j], max_q_len); };
+  const int i = blockIdx.x * kOrderThreads + threadIdx.x;
+  const int ki = i < num_seqs ? seq_key(i) : 0;
+  int r = 0;
+  for (int base = 0; base < num_seqs; base += kOrderThreads) {
+    __syncthreads();
+    const int j = base + threadIdx.x;
+    keys[threadIdx.x] = j < num_seqs ? seq_key(j) : 0;
+    __syncthreads();
+    const int n = min(kOrderThreads, num_seqs - base);
+    for (int u = 0; u < n; ++u) {
+      const int kj = keys[u];
+      r += (kj > ki || (kj == ki && base + u < i)) ? 1 : 0;
+    }
+  }
+  if (i < num_seqs) order[r] = i;
+}
+
 template <int D>
 hipError_t launch(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens, int num_seqs,
-                  int max_q_len, const AttnGeom& g, void* out, float* lse, hipStream_t stream) {
+                  int max_q_len, const AttnGeom& g, void* out, float* lse, int32_t* order, hipStream_t stream) {
   const int G = g.num_q_heads / g.num_kv_heads;
   const int tiles = (max_q_len * G + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t blocks = (int64_t)tiles * g.num_kv_heads * num_seqs;
@@ -364,22 +398,35 @@ hipError_t launch(const void* q, int64_t ld_q, const int32_t* q_start, const int
   // Tile indices into the cache are 32-bit (a 288 GB pool holds < 2^27 tiles).
   if ((int64_t)g.num_pages * (((int64_t)g.num_kv_heads << g.log2_page) / kTile) > 0x7fffffff)
     return hipErrorInvalidValue;
+  if (order != nullptr) {
+    hipLaunchKernelGGL(prefill_order_kernel, dim3((num_seqs + kOrderThreads - 1) / kOrderThreads),
+                       dim3(kOrderThreads), 0, stream, q_start, ctx_lens, num_seqs, max_q_len, order);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((attn_prefill_kernel<D, kLibRegFold, kLibOcc>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), ld_q, q_start, ctx_lens, num_seqs, tiles, max_q_len,
                      static_cast<const uint16_t*>(g.k_cache), static_cast<const uint16_t*>(g.v_cache),
                      g.num_pages, g.block_table, g.max_pages_per_seq, g.num_q_heads, g.num_kv_heads,
-                     g.log2_page, g.scale_log2, static_cast<uint16_t*>(out), lse);
+                     g.log2_page, g.scale_log2, static_cast<uint16_t*>(out), lse, order);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t attn_prefill_workspace_bytes(int64_t num_seqs) {
+  return ((size_t)num_seqs * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
 hipError_t launch_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens,
                                int num_seqs, int max_q_len, const AttnGeom& g, void* out, float* lse,
-                               hipStream_t stream) {
+                               void* workspace, hipStream_t stream) {
   if (num_seqs == 0 || max_q_len == 0) return hipSuccess;
-  return g.head_dim == 64 ? launch<64>(q, ld_q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse, stream)
-                          : launch<128>(q, ld_q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse, stream);
+  // With few sequences every workgroup ranks them in a few steps itself, and
+  // the order kernel's launch would cost more than it saves.
+  auto* order = num_seqs > kOrderMinSeqs ? static_cast<int32_t*>(workspace) : nullptr;
+  return g.head_dim == 64 ? launch<64>(q, ld_q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse, order, stream)
+                          : launch<128>(q, ld_q, q_start, ctx_lens, num_seqs, max_q_len, g, out, lse, order, stream);
 }
 
 }  // namespace bi

@@ -48,9 +48,12 @@ hipError_t launch_attn_decode(const void* q, int64_t ld_q, const AttnGeom& g, co
 // device current); the stream must belong to the current device.
 hipError_t decode_scratch(hipStream_t stream, void** ptr, size_t* bytes);
 
+// Bytes of the optional prefill workspace (the placement order table).
+size_t attn_prefill_workspace_bytes(int64_t num_seqs);
+
 hipError_t launch_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, const int32_t* ctx_lens,
                                int num_seqs, int max_q_len, const AttnGeom& g, void* out, float* lse,
-                               hipStream_t stream);
+                               void* workspace, hipStream_t stream);
 
 // Mixture-of-experts FFN (moe.hip).
 size_t moe_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t H, int64_t F);

@@ -13,7 +13,7 @@
 //     pairs, stable in pair order (p = t * top_k + s), via ballot prefix sums;
 //     row r of the order holds pair src; pos[p] = r.  Also each expert's first
 //     row and first 64-row tile.
-//  3. Grouped GEMMs with the library's one GEMM configuration and K loop
+//  3. Grouped GEMMs with a library GEMM configuration and its K loop
 //     (gemm_kernel.hpp): h[r] = bf16(SiLU(W_up[e] x[token(r)])) with the A rows
 //     gathered from x, then o[r] = W_down[e] h[r] in fp32.  A row's result
 //     depends only on that row: where it sits among its expert's rows (which
@@ -36,8 +36,22 @@
 namespace bi {
 namespace {
 
-using Cfg = GemmLibraryCfg;
 constexpr int kRouteThreads = 256;
+
+// The grouped GEMMs' configurations.  Both are library GEMM tiles (the same
+// fp32 MFMA chain per element over k ascending), so the choice between them,
+// made from the average rows per expert, changes no bit.  With few rows per
+// expert the 64 x 64 tile gives every expert's weights many streaming
+// workgroups; from 32 rows per expert on, the 128 x 256 tile holds an
+// expert's rows in one m-tile (each weight slab is read once) and re-reads
+// the gathered rows for 12 n-tiles of the up projection instead of 24.
+// Measured on MI355X, 128 experts 4096 -> 1536 -> 4096, top 8, us (64 x 64 /
+// 128 x 256): T = 64: 546 / 575; 512: 676 / 661; 1024: 910 / 734; 2048:
+// 1366 / 888.  128 x 128, 256 x 128, 256 x 256 and 64 x 256 tiles were within
+// 5 % of the better one or slower.
+using MoeSmallCfg = GemmLibraryCfg;
+using MoeLargeCfg = GemmWideCfg;
+constexpr int64_t kMoeLargeRowsPerExpert = 32;
 
 // Workspace carve-up, shared by the host-side size query and the launcher.
 struct MoeWs {
@@ -91,7 +105,8 @@ __global__ __launch_bounds__(kRouteThreads) void moe_count_kernel(const int32_t*
 }
 
 __global__ __launch_bounds__(kRouteThreads) void moe_place_kernel(const int32_t* __restrict__ ids, int P, int E,
-                                                                   int top_k, const int32_t* __restrict__ counts,
+                                                                   int top_k, int tile_rows,
+                                                                   const int32_t* __restrict__ counts,
                                                                    int32_t* __restrict__ offsets,
                                                                    int32_t* __restrict__ tiles,
                                                                    int32_t* __restrict__ pos,
@@ -104,7 +119,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_place_kernel(const int32_t*
   for (int j = threadIdx.x; j < e; j += kRouteThreads) {
     const int c = counts[j];
     off += c;
-    til += (c + Cfg::TM - 1) / Cfg::TM;
+    til += (c + tile_rows - 1) / tile_rows;
   }
   off = block_sum_int(off, red);
   til = block_sum_int(til, red);
@@ -113,7 +128,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_place_kernel(const int32_t*
     tiles[e] = til;
     if (e == E - 1) {
       offsets[E] = off + counts[e];
-      tiles[E] = til + (counts[e] + Cfg::TM - 1) / Cfg::TM;
+      tiles[E] = til + (counts[e] + tile_rows - 1) / tile_rows;
     }
   }
   // Stable placement of expert e's pairs in pair order.
@@ -142,11 +157,24 @@ __global__ __launch_bounds__(kRouteThreads) void moe_place_kernel(const int32_t*
   }
 }
 
+// Placement of the grouped GEMMs' tiles: workgroup i runs on XCD i % 8, and
+// each XCD takes a contiguous range of (m-tile, n-tile) pairs in m-tile-major
+// order, so the n-tiles of one m-tile - which share its gathered A rows - run
+// together on one XCD and find those rows in its L2.  Only placement changes.
+__device__ __forceinline__ void moe_map_tile(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int q = total >> 3, r = total & 7;
+  const int x = pid & 7, j = pid >> 3;
+  const int lin = (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+  tm = lin / tiles_n;
+  tn = lin - tm * tiles_n;
+}
+
 // Grouped expert GEMM over the expert-major rows.  kUp: A rows are gathered
 // from x (row src[r]), W = W_up[e] ([F, H]), output bf16(SiLU(.)) into h.
 // Otherwise A = h rows (contiguous), W = W_down[e] ([H, F]), fp32 output into o.
-template <bool kUp>
-__global__ __launch_bounds__(Cfg::kThreads, 2) void moe_gemm_kernel(
+template <class Cfg, bool kUp, bool kMajor = true>
+__global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void moe_gemm_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int a_rows, const uint16_t* __restrict__ Wb,
     int64_t w_expert_stride, const int32_t* __restrict__ offsets, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ src, int E, int N, int K, int tiles_n, void* __restrict__ out) {
@@ -157,7 +185,10 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void moe_gemm_kernel(
   const int tiles_m = tiles[E];
   if ((int)blockIdx.x >= tiles_m * tiles_n) return;
   int mt, tn;
-  gemm_map_tile(blockIdx.x, tiles_m, tiles_n, mt, tn);
+  if constexpr (kMajor)
+    moe_map_tile(blockIdx.x, tiles_m, tiles_n, mt, tn);
+  else
+    gemm_map_tile(blockIdx.x, tiles_m, tiles_n, mt, tn);
   // Expert owning global m-tile mt: the last e with tiles[e] <= mt.
   int lo = 0, hi = E;  // tiles[lo] <= mt < tiles[hi]
   while (hi - lo > 1) {
@@ -296,19 +327,25 @@ size_t moe_workspace_bytes(int64_t T, int64_t top_k, int64_t E, int64_t H, int64
 bool moe_supported(int64_t T, int64_t ldx, int64_t top_k, int64_t E, int64_t H, int64_t F) {
   const int64_t P = T * top_k;
   if (P > (1 << 24)) return false;
-  // Buffer resources: all of x (gathered rows), a 64-row slice of a weight, of
-  // h and of o must each span fewer than 2^31 bytes.
+  // Buffer resources: all of x (gathered rows), a tile's slice of a weight, of
+  // h and of o must each span fewer than 2^31 bytes (checked for the larger
+  // of the two configurations' tiles).
   const int64_t lim = (int64_t)1 << 31;
   if (((T - 1) * ldx + H) * 2 >= lim) return false;
-  if (((int64_t)(Cfg::TN - 1) * H + H) * 2 >= lim || ((int64_t)(Cfg::TN - 1) * F + F) * 2 >= lim) return false;
-  const int64_t tiles_m = (P + (Cfg::TM - 1) * E) / Cfg::TM + 1;
-  const int64_t tiles_n = (std::max(H, F) + Cfg::TN - 1) / Cfg::TN;
+  constexpr int64_t tn = std::max(MoeSmallCfg::TN, MoeLargeCfg::TN), tm = std::max(MoeSmallCfg::TM, MoeLargeCfg::TM);
+  if (((tn - 1) * H + H) * 2 >= lim || ((tn - 1) * F + F) * 2 >= lim) return false;
+  if (((tm - 1) * F + F) * 2 >= lim) return false;
+  const int64_t tiles_m = (P + (MoeSmallCfg::TM - 1) * E) / MoeSmallCfg::TM + 1;
+  const int64_t tiles_n = (std::max(H, F) + MoeSmallCfg::TN - 1) / MoeSmallCfg::TN;
   return tiles_m * tiles_n <= 0x7fffffff;
 }
 
-hipError_t launch_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids, const float* expert_weights,
-                          int T, int top_k, int E, const void* w_up, const void* w_down, int H, int F, void* y,
-                          int64_t ldy, void* workspace, hipStream_t stream) {
+// The MoE layer with the grouped GEMMs on configuration Cfg (kMajor: tiles
+// placed by moe_map_tile, else by the dense GEMM's gemm_map_tile).
+template <class Cfg, bool kMajor = true>
+hipError_t launch_moe_ffn_cfg(const void* x, int64_t ldx, const int32_t* expert_ids, const float* expert_weights,
+                              int T, int top_k, int E, const void* w_up, const void* w_down, int H, int F, void* y,
+                              int64_t ldy, void* workspace, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const MoeWs L = moe_ws_layout(T, top_k, E, H, F);
   char* ws = static_cast<char*>(workspace);
@@ -322,21 +359,32 @@ hipError_t launch_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids,
   const int P = T * top_k;
 
   hipLaunchKernelGGL(moe_count_kernel, dim3(E), dim3(kRouteThreads), 0, stream, expert_ids, P, E, counts, pos);
-  hipLaunchKernelGGL(moe_place_kernel, dim3(E), dim3(kRouteThreads), 0, stream, expert_ids, P, E, top_k, counts,
-                     offsets, tiles, pos, src);
+  hipLaunchKernelGGL(moe_place_kernel, dim3(E), dim3(kRouteThreads), 0, stream, expert_ids, P, E, top_k, Cfg::TM,
+                     counts, offsets, tiles, pos, src);
   // Grid: an upper bound on the m-tiles of all experts together (each expert
   // adds at most one partial tile); workgroups past the real count exit.
   const int tiles_m_bound = (P + (Cfg::TM - 1) * E) / Cfg::TM + 1;
   const int tn_up = (F + Cfg::TN - 1) / Cfg::TN, tn_down = (H + Cfg::TN - 1) / Cfg::TN;
-  hipLaunchKernelGGL(moe_gemm_kernel<true>, dim3(tiles_m_bound * tn_up), dim3(Cfg::kThreads), 0, stream,
+  hipLaunchKernelGGL((moe_gemm_kernel<Cfg, true, kMajor>), dim3(tiles_m_bound * tn_up), dim3(Cfg::kThreads), 0, stream,
                      static_cast<const uint16_t*>(x), ldx, T, static_cast<const uint16_t*>(w_up), (int64_t)F * H,
                      offsets, tiles, src, E, F, H, tn_up, static_cast<void*>(h));
-  hipLaunchKernelGGL(moe_gemm_kernel<false>, dim3(tiles_m_bound * tn_down), dim3(Cfg::kThreads), 0, stream,
+  hipLaunchKernelGGL((moe_gemm_kernel<Cfg, false, kMajor>), dim3(tiles_m_bound * tn_down), dim3(Cfg::kThreads), 0, stream,
                      static_cast<const uint16_t*>(h), (int64_t)F, P, static_cast<const uint16_t*>(w_down),
                      (int64_t)H * F, offsets, tiles, src, E, H, F, tn_down, static_cast<void*>(o));
   hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(256), 0, stream, o, pos, expert_weights, top_k, H,
                      static_cast<uint16_t*>(y), ldy);
   return hipGetLastError();
+}
+
+hipError_t launch_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids, const float* expert_weights,
+                          int T, int top_k, int E, const void* w_up, const void* w_down, int H, int F, void* y,
+                          int64_t ldy, void* workspace, hipStream_t stream) {
+  const int64_t P = (int64_t)T * top_k;
+  if (P >= kMoeLargeRowsPerExpert * (int64_t)E)
+    return launch_moe_ffn_cfg<MoeLargeCfg>(x, ldx, expert_ids, expert_weights, T, top_k, E, w_up, w_down, H, F, y,
+                                           ldy, workspace, stream);
+  return launch_moe_ffn_cfg<MoeSmallCfg>(x, ldx, expert_ids, expert_weights, T, top_k, E, w_up, w_down, H, F, y,
+                                         ldy, workspace, stream);
 }
 
 }  // namespace bi

@@ -78,6 +78,12 @@ def test_host_validation_without_gpu(lib):
     assert dec(wsb=100) == bi.BI_ERR_WORKSPACE
     assert dec(b=0) == bi.BI_OK
     assert dec(ldq=4000) == bi.BI_ERR_INVALID_ARG
+    # prefill: a workspace that is short or misaligned is refused before any launch
+    pre = lambda ws, nbytes: lib.bi_attn_prefill(P, 4096, P, P, 40, 64, P, P, 8, P, 4, 32, 8, 128, 16, 0.1, P, None,
+                                                 ws, nbytes, None)
+    assert lib.bi_attn_prefill_workspace_bytes(40) >= 160
+    assert pre(P, 100) == bi.BI_ERR_WORKSPACE
+    assert pre(ctypes.c_void_p(24), 1 << 20) == bi.BI_ERR_WORKSPACE
     assert lib.bi_log_softmax(P, 6, P, 8, 2, 6, None) == bi.BI_ERR_UNSUPPORTED
     # fused lm_head + log_softmax: n % 4, k % 32, short or missing or misaligned workspace, ldo, empty batch
     W256 = ctypes.c_void_p(256)

@@ -78,14 +78,41 @@ def _tile_positions(off, d):
 D_ALL = [0]
 
 
-@pytest.mark.parametrize("ps", [16, 64])
-def test_kv_append_layout_bit_exact(ps):
-    hkv, d, pages, t = 8, 128, 40, 300
+def _run_slots(pages, ps):
+    """A chunk-like slot mapping: whole 16-token tiles in order (page-aligned
+    and not), runs that start or end mid-tile, a run broken by a padding
+    token, a run whose tiles are out of order, and scattered single tokens."""
+    g = torch.Generator().manual_seed(5)
+    perm = torch.randperm(pages, generator=g).tolist()
+    base = lambda i: perm[i] * ps
+    runs = [list(range(base(0), base(0) + 48)),            # three whole tiles of one page (ps >= 64) or three pages
+            list(range(base(1) + 5, base(1) + 40)),        # starts mid-tile
+            list(range(base(2), base(2) + 16)),
+            list(range(base(3) + 16, base(3) + 16 + 20)),
+            [base(4) + 3, base(4) + 1, base(4) + 2]]
+    broken = list(range(base(5), base(5) + 32))
+    broken[20] = -1                                        # padding inside a tile
+    swapped = list(range(base(6), base(6) + 16))
+    swapped[3], swapped[4] = swapped[4], swapped[3]        # one tile, tokens out of order
+    s = [x for r in runs for x in r] + broken + swapped
+    singles = torch.randperm(pages * ps, generator=g).tolist()
+    used = set(s)
+    s += [x for x in singles if x not in used and x // ps not in perm[:7]][:21]
+    return torch.tensor(s, dtype=torch.int32)
+
+
+@pytest.mark.parametrize("ps,d,kind", [(16, 128, "random"), (64, 128, "random"), (16, 128, "runs"),
+                                       (64, 128, "runs"), (16, 64, "runs"), (256, 64, "runs")])
+def test_kv_append_layout_bit_exact(ps, d, kind):
+    hkv, pages = 8, 40
     D_ALL[0] = d
+    slots = torch.randperm(pages * ps, generator=torch.Generator().manual_seed(3))[:300].to(torch.int32) \
+        if kind == "random" else _run_slots(pages, ps)
+    t = slots.shape[0]
     k_new = W.randn_bf16((t, hkv, d), 1, "k", 0, device=DEV)
     v_new = W.randn_bf16((t, hkv, d), 1, "v", 0, device=DEV)
-    slots = torch.randperm(pages * ps, generator=torch.Generator().manual_seed(3))[:t].to(torch.int32)
-    slots[7] = -1                                    # padding token: skipped
+    if kind == "random":
+        slots[7] = -1                                # padding token: skipped
     kc, vc = bi.alloc_kv_cache(pages, hkv, d, ps, fill=0.5)
     bi.bi_kv_append(k_new, v_new, slots.to(DEV), kc, vc)
     ek = torch.full((pages, hkv, ps * d), 0.5, dtype=torch.bfloat16)
@@ -500,6 +527,36 @@ def test_lazy_reference_moves(kind):
             _assert_weight_rounding_bound(out[qs[s] + i], qq[i], k[:p + i + 1], v[:p + i + 1], bt.scale, ro[0],
                                           f"{kind} seq {s} row {i}")
             assert_f32_close(lse[qs[s] + i], rl[0], f"{kind} seq {s} row {i} lse")
+
+
+def test_prefill_many_short_sequences():
+    """300 short chunks (1..40 new tokens over caches of 0..600): with the
+    placement order table (more than 16 sequences) and without it, bitwise the
+    same outputs; sampled rows against the oracle and against decode."""
+    rng = np.random.default_rng(30)
+    S = 300
+    prefixes = [int(x) for x in rng.integers(0, 601, S)]
+    chunks = [int(x) for x in rng.integers(1, 41, S)]
+    bt, q, q_start, ctx = _prefill_setup(prefixes, chunks, perm_index=4)
+    log_case(f"prefill many sequences S={S}")
+    lse_a = torch.empty((q.shape[0], 32), dtype=torch.float32, device=DEV)
+    lse_b = torch.empty((q.shape[0], 32), dtype=torch.float32, device=DEV)
+    ws = torch.full((bi.bi_attn_prefill_workspace_bytes(S),), 255, dtype=torch.uint8, device=DEV)
+    oa, _ = bi.bi_attn_prefill(q, q_start, ctx, 40, bt.kc, bt.vc, bt.bt, bt.scale, lse=lse_a, workspace=ws)
+    ob, _ = bi.bi_attn_prefill(q, q_start, ctx, 40, bt.kc, bt.vc, bt.bt, bt.scale, lse=lse_b, order_table=False)
+    assert_bitwise(oa, ob, "order table vs in-kernel ranking")
+    assert_bitwise(lse_a, lse_b, "order table vs in-kernel ranking (lse)")
+    qs = q_start.cpu().tolist()
+    for s_ in (0, 7, 150, S - 1):
+        i = chunks[s_] - 1
+        row = qs[s_] + i
+        L = prefixes[s_] + i + 1
+        ro, rl = O.decode_attention(f64(q[row:row + 1]), [f64(bt.kv[s_][0][:L])], [f64(bt.kv[s_][1][:L])], bt.scale)
+        assert_bf16_close(oa[row], ro[0], f"sequence {s_} last row vs oracle")
+        assert_f32_close(lse_a[row:row + 1], rl, f"sequence {s_} last row lse vs oracle")
+        od, _ = bi.bi_attn_decode(q[row:row + 1], bt.kc, bt.vc, bt.bt[s_:s_ + 1],
+                                  torch.tensor([L], dtype=torch.int32, device=DEV), L, bt.scale)
+        assert_bitwise(oa[row], od[0], f"sequence {s_} last row: prefill vs decode")
 
 
 def test_prefill_co_batch_invariance():
