@@ -10,8 +10,11 @@
 // V fragments go from HBM straight into registers in MFMA layout; the next
 // 32-key sub-block is in flight while the current one is computed.
 // Kernel 2 (grid: q head x sequence): the ascending fold of those partials,
-// normalisation and bf16 output.  No atomics, no cross-workgroup ordering:
-// every value is written by exactly one workgroup.
+// normalisation and bf16 output.  No floating-point atomics and no ordering
+// between workgroups: every output value and every partial is written by
+// exactly one wavefront.  (The work-queue path below hands out items with an
+// integer atomic counter and sorts them with LDS integer atomics; that decides
+// only which wavefront computes an item, never a value.)
 #include <algorithm>
 #include <climits>
 
