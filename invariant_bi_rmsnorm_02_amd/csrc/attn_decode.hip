@@ -408,52 +408,57 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32
   if (tid == 0) *next = 0;
 }
 
-constexpr int kMergeBatch = 16;
+constexpr int kMergeBatch = 64;
+constexpr int kMergeThreads = 256;
 
 // Folds a sequence's records in ascending order: chunk 0's record, then
 // chunks cg, cg + 1, ..., C - 1 (cg = 1: every chunk's partial; cg > 1: chunk
 // 0's record holds the fold of chunks 0 .. cg - 1).  Sequences with C <= done
 // were finished by their queue wavefront.
 template <int D>
-__global__ __launch_bounds__(64) void attn_decode_merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq,
     int max_chunks, int cg, int done, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int E = D / 64;  // head dims per lane
-  const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  constexpr int E = D / 64;             // head dims per lane
+  constexpr int R = D + 4;              // floats per record
+  constexpr int kPieces = R / 4;        // 16-byte pieces per record
+  const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int L = min(seq_lens[b], max_seq_len);
   const int C = L > 0 ? (L + kChunk - 1) / kChunk : 0;
   if (C <= done) return;
-  const float* rec0 = ws + ((int64_t)b * Hq + head) * max_chunks * (D + 4);
+  const float* rec0 = ws + ((int64_t)b * Hq + head) * max_chunks * R;
 
+  // The records folded, in order: t = 0 is chunk 0's, t >= 1 is chunk cg - 1 + t.
+  // The whole workgroup copies them into LDS kMergeBatch at a time (16-byte
+  // pieces, every load of a batch in flight at once), so a long sequence
+  // waits for one load latency per batch; wavefront 0 then folds the batch
+  // record by record in the same order.
+  __shared__ __attribute__((aligned(16))) float srec[kMergeBatch * R];
   float m = -INFINITY, l = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  // The records folded, in order: t = 0 is chunk 0's, t >= 1 is chunk cg - 1 + t.
-  // They are loaded kMergeBatch at a time ahead of the fold, so a long
-  // sequence waits for one load latency per batch rather than per chunk; the
-  // fold itself runs record by record in the same order.
   const int T = C > 0 ? 1 + max(0, C - cg) : 0;
   for (int t0 = 0; t0 < T; t0 += kMergeBatch) {
-    float rm[kMergeBatch], rl[kMergeBatch], ra[kMergeBatch][E];
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const int t = min(t0 + j, T - 1);
-      const float* rec = rec0 + (int64_t)(t == 0 ? 0 : cg - 1 + t) * (D + 4);
-      rm[j] = rec[D];
-      rl[j] = rec[D + 1];
-#pragma unroll
-      for (int e = 0; e < E; ++e) ra[j][e] = rec[lane * E + e];
+    const int nb = min(kMergeBatch, T - t0);
+    if (t0 > 0) __syncthreads();     // wavefront 0 is done with the previous batch
+    for (int p = tid; p < nb * kPieces; p += kMergeThreads) {
+      const int j = p / kPieces, q = p - j * kPieces, t = t0 + j;
+      const float* rec = rec0 + (int64_t)(t == 0 ? 0 : cg - 1 + t) * R;
+      *reinterpret_cast<f32x4_t*>(&srec[j * R + 4 * q]) = *reinterpret_cast<const f32x4_t*>(rec + 4 * q);
     }
+    __syncthreads();
+    if (tid < 64) {
+      for (int j = 0; j < nb; ++j) {
+        const float* rj = &srec[j * R];
+        const MergeCoef k = merge_coef(m, rj[D]);
+        l = merge_val(l, rj[D + 1], k);
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      if (t0 + j >= T) break;
-      const MergeCoef k = merge_coef(m, rm[j]);
-      l = merge_val(l, rl[j], k);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = merge_val(acc[e], ra[j][e], k);
-      m = k.m;
+        for (int e = 0; e < E; ++e) acc[e] = merge_val(acc[e], rj[lane * E + e], k);
+        m = k.m;
+      }
     }
   }
+  if (tid >= 64) return;
   uint16_t* op = out + ((int64_t)b * Hq + head) * D + lane * E;
   if (C > 0) {
     const float inv = finalize_inv(l);
@@ -536,7 +541,7 @@ hipError_t launch(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t*
                        lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(64), 0, stream, ws, seq_lens,
+    hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(kMergeThreads), 0, stream, ws, seq_lens,
                        max_seq_len, g.num_q_heads, max_chunks, 1, -1, os, lse);
     return hipGetLastError();
   }
@@ -556,7 +561,7 @@ hipError_t launch(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t*
                      g.scale_log2, ws, max_chunks, (int)cg, os, lse, qd.item_seq, qd.item_group, qd.next, qd.total);
   e = hipGetLastError();
   if (e != hipSuccess || cg >= max_chunks) return e;
-  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(64), 0, stream, ws, seq_lens,
+  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(kMergeThreads), 0, stream, ws, seq_lens,
                      max_seq_len, g.num_q_heads, max_chunks, (int)cg, (int)cg, os, lse);
   return hipGetLastError();
 }
