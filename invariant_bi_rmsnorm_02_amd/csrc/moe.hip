@@ -87,18 +87,31 @@ __device__ __forceinline__ int block_sum_int(int v, int* red) {
   return t;
 }
 
+// Pairs per thread per pass of the count and place kernels: each thread has
+// this many coalesced id loads in flight at once instead of one.
+constexpr int kPairsPerThread = 16;
+
 __global__ __launch_bounds__(kRouteThreads) void moe_count_kernel(const int32_t* __restrict__ ids, int P, int E,
                                                                    int32_t* __restrict__ counts,
                                                                    int32_t* __restrict__ pos) {
   __shared__ int red[kRouteThreads / 64];
   const int e = blockIdx.x;
   int c = 0;
-  for (int p = threadIdx.x; p < P; p += kRouteThreads) {
-    const int id = ids[p];
-    c += id == e;
-    // Pairs whose expert id is out of range belong to no expert; workgroup 0
-    // marks them so the combine skips them.
-    if (e == 0 && (id < 0 || id >= E)) pos[p] = -1;
+  for (int base = 0; base < P; base += kRouteThreads * kPairsPerThread) {
+    int id[kPairsPerThread];
+#pragma unroll
+    for (int j = 0; j < kPairsPerThread; ++j) {
+      const int p = base + j * kRouteThreads + (int)threadIdx.x;
+      id[j] = p < P ? ids[p] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPairsPerThread; ++j) {
+      const int p = base + j * kRouteThreads + (int)threadIdx.x;
+      c += (p < P && id[j] == e) ? 1 : 0;
+      // Pairs whose expert id is out of range belong to no expert; workgroup
+      // 0 marks them so the combine skips them.
+      if (e == 0 && p < P && (id[j] < 0 || id[j] >= E)) pos[p] = -1;
+    }
   }
   c = block_sum_int(c, red);
   if (threadIdx.x == 0) counts[e] = c;
@@ -112,7 +125,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_place_kernel(const int32_t*
                                                                    int32_t* __restrict__ pos,
                                                                    int32_t* __restrict__ src) {
   __shared__ int red[kRouteThreads / 64];
-  __shared__ int wave_tot[kRouteThreads / 64];
+  __shared__ int wave_tot[2][kPairsPerThread][kRouteThreads / 64];
   const int e = blockIdx.x;
   // First row and first tile of expert e: sums over the experts before it.
   int off = 0, til = 0;
@@ -131,29 +144,47 @@ __global__ __launch_bounds__(kRouteThreads) void moe_place_kernel(const int32_t*
       tiles[E] = til + (counts[e] + tile_rows - 1) / tile_rows;
     }
   }
-  // Stable placement of expert e's pairs in pair order.
+  // Stable placement of expert e's pairs in pair order.  A pass covers
+  // kPairsPerThread slices of kRouteThreads consecutive pairs; within a slice
+  // a pair's rank is the hits of the waves before it plus the hits of the
+  // lanes before it (ballot), and slices follow each other in pair order.
+  // The per-wave hit counts are double-buffered, so one barrier per pass
+  // suffices: a pass writes the buffer the previous pass did not read.
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t lanes_before = (1ull << lane) - 1ull;
   int run = off;
-  for (int base = 0; base < P; base += kRouteThreads) {
-    const int p = base + threadIdx.x;
-    const bool hit = p < P && ids[p] == e;
-    const uint64_t bal = __ballot(hit);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    __syncthreads();
-    if (lane == 0) wave_tot[wave] = __popcll(bal);
-    __syncthreads();
-    int wbase = 0, total = 0;
+  int buf = 0;
+  for (int base = 0; base < P; base += kRouteThreads * kPairsPerThread, buf ^= 1) {
+    int id[kPairsPerThread];
 #pragma unroll
-    for (int w = 0; w < kRouteThreads / 64; ++w) {
-      wbase += w < wave ? wave_tot[w] : 0;
-      total += wave_tot[w];
+    for (int j = 0; j < kPairsPerThread; ++j) {
+      const int p = base + j * kRouteThreads + (int)threadIdx.x;
+      id[j] = p < P ? ids[p] : -1;
     }
-    if (hit) {
-      const int r = run + wbase + before;
-      pos[p] = r;
-      src[r] = p / top_k;
+    uint64_t bal[kPairsPerThread];
+#pragma unroll
+    for (int j = 0; j < kPairsPerThread; ++j) {
+      bal[j] = __ballot(id[j] == e);
+      if (lane == 0) wave_tot[buf][j][wave] = __popcll(bal[j]);
     }
-    run += total;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPairsPerThread; ++j) {
+      int wbase = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < kRouteThreads / 64; ++w) {
+        const int t = wave_tot[buf][j][w];
+        wbase += w < wave ? t : 0;
+        total += t;
+      }
+      if (id[j] == e) {
+        const int p = base + j * kRouteThreads + (int)threadIdx.x;
+        const int r = run + wbase + __popcll(bal[j] & lanes_before);
+        pos[p] = r;
+        src[r] = p / top_k;
+      }
+      run += total;
+    }
   }
 }
 
