@@ -3,7 +3,7 @@
 // Matrix Multiplication", figs. "Data-Parallel Matrix Multiplication" and
 // "Split-K Matmul").
 //
-// The library instantiates four configurations (gemm_with_cfg_mn picks one
+// The library instantiates five configurations (gemm_with_cfg_mn picks one
 // from the shape; every one gives every element the same bits).  Whatever the
 // configuration,
 // the arithmetic of an output element is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
@@ -437,6 +437,23 @@ using GemmNarrowCfg = GemmCfg<16, 64, 1, 2, 6, 64, 2>;
 constexpr int64_t kGemmNarrowMaxM = 64;
 constexpr int64_t kGemmNarrowMaxN = 8192;
 
+// The configuration for the smallest batches: 32 (n) x 16 (m) tile, 2 x 1
+// wavefronts of 16 x 16, a 6-stage ring of 128-wide K stages (72 KB, two
+// workgroups per CU).  With one 16-row block of A there is nothing to share
+// between wavefronts along m, so each wavefront streams its own 16 weight rows
+// with five 4 KB stages in flight.  Used up to kGemmSkinnyMaxM rows, and up to
+// kGemmNarrowMaxM rows for weights of at most kGemmSkinnyMaxN rows.  Measured
+// on MI355X against the 16 x 64 / 64 x 64 tiles (bitwise equal), us: down
+// 12288 -> 4096 at M = 1 / 16 / 32 / 64, 24.9 / 27.1 / 27.3 / 42.2 against
+// 33.7 / 31.8 / 37.0 / 46.1; O 4096 -> 4096 at M = 1 / 64, 8.9 / 15.0 against
+// 12.2 / 17.2; QKV 4096 -> 6144 at M = 1 / 16, 11.3 / 12.1 against 13.4 /
+// 13.3; up 4096 -> 12288 at M = 1 / 16, 22.0 / 22.4 against 23.1 / 22.0.  At
+// M = 32 the wider weights read every weight row twice and lose to the 16 x
+// 64 and 64 x 64 tiles.
+using GemmSkinnyCfg = GemmCfg<32, 16, 2, 1, 6, 128, 2>;
+constexpr int64_t kGemmSkinnyMaxM = 16;
+constexpr int64_t kGemmSkinnyMaxN = 4096;
+
 // Tile rule of the vocabulary-sized weights (N >= kGemmWideMinN) and of the
 // fused lm_head: the big tile from kGemmBigMinMWide rows on, else the wide
 // one.  The fused lm_head's per-row reduction records do not depend on the
@@ -454,10 +471,13 @@ inline auto gemm_with_cfg_wide(int64_t lda, int64_t ldw, int64_t m, int64_t k, F
 // tests compare whole products bitwise across every threshold below).
 //   N >= kGemmWideMinN:                                     gemm_with_cfg_wide
 //   M >= kGemmBigMinM and >= kGemmBigMinTiles big tiles:    256 x 256
+//   M <= kGemmSkinnyMaxM, or M <= kGemmNarrowMaxM and
+//     N <= kGemmSkinnyMaxN:                                 32 x 16
 //   M <= kGemmNarrowMaxM and N <= kGemmNarrowMaxN:          16 x 64
 //   otherwise:                                              64 x 64
-// (a configuration whose tile offsets would not fit its buffer resources is
-// skipped for the next one; the 64 x 64 tile is checked by the caller).
+// (the big tile is skipped for the next rule when its offsets would not fit
+// its buffer resources; the caller checks the chosen one, and the 32 x 16 and
+// 16 x 64 tiles span fewer rows of A and W than the 64 x 64 tile).
 template <class F>
 inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, F&& f) {
   using Bg = GemmBigCfg;
@@ -466,6 +486,7 @@ inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int
                    ((m + Bg::TM - 1) / Bg::TM) * ((n + Bg::TN - 1) / Bg::TN) >= kGemmBigMinTiles &&
                    gemm_offsets_fit<Bg>(lda, ldw, k);
   if (big) return f(Bg{});
+  if (m <= kGemmSkinnyMaxM || (m <= kGemmNarrowMaxM && n <= kGemmSkinnyMaxN)) return f(GemmSkinnyCfg{});
   if (m <= kGemmNarrowMaxM && n <= kGemmNarrowMaxN) return f(GemmNarrowCfg{});
   return f(GemmLibraryCfg{});
 }

@@ -224,28 +224,34 @@ def test_gemm_tile_rule_edges(n, k, m_lo, m_hi):
         assert_bitwise(lo, sliced[:m_lo], f"m={m_lo} vs 256-row slices ({dt})")
 
 
-@pytest.mark.parametrize("n,k", [(4096, 12288), (6144, 4096), (8192, 512), (8200, 512), (12288, 4096)])
-def test_gemm_narrow_tile_edges(n, k):
-    """Up to 64 rows a weight of at most 8192 rows runs the 16 x 64 tile, from
-    65 rows (or above 8192 weight rows) the 64 x 64 one.  Rows shared by
-    M = 1, 64 and 65, and 32-row slices, must agree bit for bit, and
-    integer inputs must give the oracle rounded once on the narrow path."""
+@pytest.mark.parametrize("n,k", [(4096, 12288), (4097, 512), (6144, 4096), (8192, 512), (8200, 512),
+                                 (12288, 4096)])
+def test_gemm_small_m_tile_edges(n, k):
+    """Up to 16 rows every weight narrower than the wide rule runs the 32 x 16
+    tile, and so does a weight of at most 4096 rows up to 64 rows; otherwise up
+    to 64 rows a weight of at most 8192 rows runs the 16 x 64 tile, and from 65
+    rows (or above 8192 weight rows) the 64 x 64 one.  Rows shared by M = 1,
+    16, 17, 64 and 65, and 16- and 32-row slices, must agree bit for bit, and
+    integer inputs must give the oracle rounded once on the small-M paths."""
     w = W.randn_bf16((n, k), 14, "w", n, std=0.02, device=DEV)
     a = W.randn_bf16((65, k), 14, "x", k, device=DEV)
-    log_case(f"gemm narrow tile edge n={n} k={k}")
+    log_case(f"gemm small-M tile edges n={n} k={k}")
     for dt in (torch.bfloat16, torch.float32):
         c65 = bi.bi_gemm(a, w, out_dtype=dt)
-        c64 = bi.bi_gemm(a[:64].contiguous(), w, out_dtype=dt)
-        c1 = bi.bi_gemm(a[:1].contiguous(), w, out_dtype=dt)
-        sl = torch.cat([bi.bi_gemm(a[r:r + 32].contiguous(), w, out_dtype=dt) for r in range(0, 65, 32)])
-        assert_bitwise(c65[:64], c64, f"rows at M=64 vs M=65 ({dt})")
-        assert_bitwise(c65[:1], c1, f"row 0 at M=1 vs M=65 ({dt})")
-        assert_bitwise(c65, sl, f"M=65 vs 32-row slices ({dt})")
-    ref = O.gemm(f64(a[:64:16]), f64(w[::37]))
-    assert_bf16_close(bi.bi_gemm(a[:64].contiguous(), w)[::16, ::37], ref, f"narrow tile parity n={n}")
-    ai, wi = _int_bf16((7, 256), 15), _int_bf16((n, 256), 16)
-    want = torch.from_numpy(O.f64_to_bf16_bits(O.gemm(f64(ai), f64(wi))).view(np.int16))
-    assert torch.equal(bi.bi_gemm(ai.to(DEV), wi.to(DEV)).view(torch.int16).cpu(), want)
+        for m in (64, 17, 16, 1):
+            cm = bi.bi_gemm(a[:m].contiguous(), w, out_dtype=dt)
+            assert_bitwise(c65[:m], cm, f"rows at M={m} vs M=65 ({dt})")
+        for step in (16, 32):
+            sl = torch.cat([bi.bi_gemm(a[r:r + step].contiguous(), w, out_dtype=dt) for r in range(0, 65, step)])
+            assert_bitwise(c65, sl, f"M=65 vs {step}-row slices ({dt})")
+    for m, rs in ((64, 16), (16, 5)):
+        ref = O.gemm(f64(a[:m:rs]), f64(w[::37]))
+        assert_bf16_close(bi.bi_gemm(a[:m].contiguous(), w)[::rs, ::37], ref, f"small-M parity n={n} M={m}")
+    wi = _int_bf16((n, 256), 16)
+    for rows in (7, 40):
+        ai = _int_bf16((rows, 256), 15)
+        want = torch.from_numpy(O.f64_to_bf16_bits(O.gemm(f64(ai), f64(wi))).view(np.int16))
+        assert torch.equal(bi.bi_gemm(ai.to(DEV), wi.to(DEV)).view(torch.int16).cpu(), want)
 
 
 def test_gemm_wide_tile_batch_invariance():
