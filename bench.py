@@ -788,6 +788,8 @@ ONLY = {
     "gemm-up-m2300": "up GEMM 4096->12288 at M=2300 (mixed batch), bf16 out",
     "gemm-up-m256": "up GEMM 4096->12288 at M=256 (decode step), bf16 out",
     "prefill-4x512": "chunked prefill, 4 x 512 tokens over the seeded prefixes, 32/8 heads, D=128",
+    "prefill-1x4096": "chunked prefill, 1 x 512 tokens over a 4096-token prefix, 32/8 heads, D=128",
+    "prefill-4x4096": "chunked prefill, 4 x 512 tokens over 4096-token prefixes, 32/8 heads, D=128",
     "rmsnorm-2300": "RMSNorm [2300, 4096]",
     "lm-head-t2048": "fused lm_head + log_softmax, T=2048, vocab 151936",
     "layer-decode-b1": "Qwen3-8B-shaped decoder layer, decode of 1 request",
@@ -807,17 +809,21 @@ def run_only(torch, bi, W, what, reps):
         a = W.rows_for_requests(range(M), 4096, W.SEED_MIXED, device=dev)
         c = torch.empty((M, 12288), dtype=torch.bfloat16, device=dev)
         fn = lambda: bi.bi_gemm(a, w, out=c)
-    elif what == "prefill-4x512":
-        prefixes = [W.rand_int(0, 8192, W.SEED_MIXED, "len", 100 + s) for s in range(4)]
+    elif what.startswith("prefill-"):
+        if what == "prefill-4x512":
+            prefixes = [W.rand_int(0, 8192, W.SEED_MIXED, "len", 100 + s) for s in range(4)]
+        else:
+            prefixes = [4096] * int(what.split("-")[1].split("x")[0])
+        ns = len(prefixes)
         total = [p + 512 for p in prefixes]
         pb = W.allocate_pages(total, W.SEED_MIXED)
         kc, vc = bi.alloc_kv_cache(pb.num_pages, 8, 128, 16, dev, fill=0.0)
         kv = [W.request_kv(s, L, 8, 128, W.SEED_MIXED, device=dev) for s, L in enumerate(total)]
         bi.bi_kv_append(torch.cat([k for k, _ in kv]), torch.cat([v for _, v in kv]), pb.slot_mapping.to(dev),
                         kc, vc)
-        qp = W.randn_bf16((2048, 32, 128), W.SEED_MIXED, "q", 0, device=dev)
+        qp = W.randn_bf16((512 * ns, 32, 128), W.SEED_MIXED, "q", 0, device=dev)
         op = torch.empty_like(qp)
-        qs = torch.tensor([0, 512, 1024, 1536, 2048], dtype=torch.int32, device=dev)
+        qs = torch.tensor([512 * i for i in range(ns + 1)], dtype=torch.int32, device=dev)
         ctx = torch.tensor(prefixes, dtype=torch.int32, device=dev)
         btp = pb.block_table.to(dev)
         fn = lambda: bi.bi_attn_prefill(qp, qs, ctx, 512, kc, vc, btp, 1 / math.sqrt(128), out=op)
