@@ -3,7 +3,7 @@
 // Matrix Multiplication", figs. "Data-Parallel Matrix Multiplication" and
 // "Split-K Matmul").
 //
-// The library instantiates five configurations (gemm_with_cfg_mn picks one
+// The library instantiates seven configurations (gemm_with_cfg_mn picks one
 // from the shape; every one gives every element the same bits).  Whatever the
 // configuration,
 // the arithmetic of an output element is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
@@ -454,6 +454,25 @@ using GemmSkinnyCfg = GemmCfg<32, 16, 2, 1, 6, 128, 2>;
 constexpr int64_t kGemmSkinnyMaxM = 16;
 constexpr int64_t kGemmSkinnyMaxN = 4096;
 
+// The configurations for medium M (between the narrow and large-M rules): a
+// 64 (n) x 128 (m) tile, 2 x 2 wavefronts of 32 x 64, a 3-stage ring of
+// 64-wide K stages (72 KB, two workgroups per CU), and a 128 x 128 tile, 2 x 2
+// wavefronts of 64 x 64, a 4-stage ring (128 KB, one workgroup per CU).  The
+// rule takes the largest of 128 x 128, 64 x 128 and 64 x 64 whose grid has at
+// least kGemmMidMinTiles tiles: larger tiles re-read A and W from L2 fewer
+// times, but below about 192 workgroups the weight stream no longer fills the
+// chip.  Measured on MI355X with weights streamed from HBM (twelve rotating
+// copies), us, 128 x 128 / 64 x 128 / 64 x 64, the chosen one first: QKV
+// 4096 -> 6144 at M = 128 / 256 / 512: 22.4 (64 x 64; 31.7, 42.6) / 31.5
+// (64 x 128; 37.4, 42.5) / 42.8 (128 x 128; 53.0, 52.1); up 4096 -> 12288 at
+// M = 128 / 256 / 512: 37.0 (64 x 128; 42.0) / 45.1 (128 x 128; 55.5) / 83.9
+// (128 x 128; best 81.2 on 64 x 128); down 12288 -> 4096 at M = 128 / 256 /
+// 512: 62.5 / 63.2 (64 x 64) / 87.9 (64 x 128; 105.5 on 64 x 64); O 4096 ->
+// 4096 at M = 512: 30.9 (64 x 128; 36.0 on 64 x 64).
+using GemmMidCfg = GemmCfg<64, 128, 2, 2, 3, 64, 2>;
+using GemmSquareCfg = GemmCfg<128, 128, 2, 2, 4, 64, 1>;
+constexpr int64_t kGemmMidMinTiles = 192;
+
 // Tile rule of the vocabulary-sized weights (N >= kGemmWideMinN) and of the
 // fused lm_head: the big tile from kGemmBigMinMWide rows on, else the wide
 // one.  The fused lm_head's per-row reduction records do not depend on the
@@ -474,10 +493,12 @@ inline auto gemm_with_cfg_wide(int64_t lda, int64_t ldw, int64_t m, int64_t k, F
 //   M <= kGemmSkinnyMaxM, or M <= kGemmNarrowMaxM and
 //     N <= kGemmSkinnyMaxN:                                 32 x 16
 //   M <= kGemmNarrowMaxM and N <= kGemmNarrowMaxN:          16 x 64
+//   M > kGemmNarrowMaxM and >= kGemmMidMinTiles tiles:      128 x 128, else 64 x 128
 //   otherwise:                                              64 x 64
-// (the big tile is skipped for the next rule when its offsets would not fit
-// its buffer resources; the caller checks the chosen one, and the 32 x 16 and
-// 16 x 64 tiles span fewer rows of A and W than the 64 x 64 tile).
+// (the big, 128 x 128 and 64 x 128 tiles are skipped for the next rule when
+// their offsets would not fit their buffer resources; the caller checks the
+// chosen one, and the 32 x 16 and 16 x 64 tiles span fewer rows of A and W
+// than the 64 x 64 tile).
 template <class F>
 inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, F&& f) {
   using Bg = GemmBigCfg;
@@ -488,6 +509,15 @@ inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int
   if (big) return f(Bg{});
   if (m <= kGemmSkinnyMaxM || (m <= kGemmNarrowMaxM && n <= kGemmSkinnyMaxN)) return f(GemmSkinnyCfg{});
   if (m <= kGemmNarrowMaxM && n <= kGemmNarrowMaxN) return f(GemmNarrowCfg{});
+  if (m > kGemmNarrowMaxM) {
+    auto tiles = [&](auto cfg) {
+      using C = decltype(cfg);
+      return ((m + C::TM - 1) / C::TM) * ((n + C::TN - 1) / C::TN);
+    };
+    if (tiles(GemmSquareCfg{}) >= kGemmMidMinTiles && gemm_offsets_fit<GemmSquareCfg>(lda, ldw, k))
+      return f(GemmSquareCfg{});
+    if (tiles(GemmMidCfg{}) >= kGemmMidMinTiles && gemm_offsets_fit<GemmMidCfg>(lda, ldw, k)) return f(GemmMidCfg{});
+  }
   return f(GemmLibraryCfg{});
 }
 
