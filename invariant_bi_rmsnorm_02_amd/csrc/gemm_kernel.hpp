@@ -3,7 +3,7 @@
 // Matrix Multiplication", figs. "Data-Parallel Matrix Multiplication" and
 // "Split-K Matmul").
 //
-// The library instantiates seven configurations (gemm_with_cfg_mn picks one
+// The library instantiates eight configurations (gemm_with_cfg_mn picks one
 // from the shape; every one gives every element the same bits).  Whatever the
 // configuration,
 // the arithmetic of an output element is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
@@ -470,6 +470,15 @@ constexpr int64_t kGemmSkinnyMaxN = 4096;
 // 512: 62.5 / 63.2 (64 x 64) / 87.9 (64 x 128; 105.5 on 64 x 64); O 4096 ->
 // 4096 at M = 512: 30.9 (64 x 128; 36.0 on 64 x 64).
 using GemmMidCfg = GemmCfg<64, 128, 2, 2, 3, 64, 2>;
+// And for weights of at most kGemmSkinnyMaxN rows at up to kGemmThinMaxM rows
+// (the O and down projections of a decode batch): 32 (n) x 64 (m), 2 x 2
+// wavefronts of 16 x 32, a 6-stage ring (72 KB, two workgroups per CU), so
+// twice as many workgroups stream the weight as with 64 x 64.  Measured as
+// above: down at M = 96 / 128, 37.8 / 45.7 against 51.0 / 62.6 us; O at
+// M = 96 / 128, 15.3 / 16.9 against 18.5 / 21.3 us; at M = 256 it is 25-30 %
+// slower than 64 x 64.
+using GemmThinCfg = GemmCfg<32, 64, 2, 2, 6, 64, 2>;
+constexpr int64_t kGemmThinMaxM = 128;
 using GemmSquareCfg = GemmCfg<128, 128, 2, 2, 4, 64, 1>;
 constexpr int64_t kGemmMidMinTiles = 192;
 
@@ -493,10 +502,11 @@ inline auto gemm_with_cfg_wide(int64_t lda, int64_t ldw, int64_t m, int64_t k, F
 //   M <= kGemmSkinnyMaxM, or M <= kGemmNarrowMaxM and
 //     N <= kGemmSkinnyMaxN:                                 32 x 16
 //   M <= kGemmNarrowMaxM and N <= kGemmNarrowMaxN:          16 x 64
+//   M <= kGemmThinMaxM and N <= kGemmSkinnyMaxN:            32 x 64
 //   M > kGemmNarrowMaxM and >= kGemmMidMinTiles tiles:      128 x 128, else 64 x 128
 //   otherwise:                                              64 x 64
-// (the big, 128 x 128 and 64 x 128 tiles are skipped for the next rule when
-// their offsets would not fit their buffer resources; the caller checks the
+// (the big, 32 x 64, 128 x 128 and 64 x 128 tiles are skipped for the next
+// rule when their offsets would not fit their buffer resources; the caller checks the
 // chosen one, and the 32 x 16 and 16 x 64 tiles span fewer rows of A and W
 // than the 64 x 64 tile).
 template <class F>
@@ -509,6 +519,8 @@ inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int
   if (big) return f(Bg{});
   if (m <= kGemmSkinnyMaxM || (m <= kGemmNarrowMaxM && n <= kGemmSkinnyMaxN)) return f(GemmSkinnyCfg{});
   if (m <= kGemmNarrowMaxM && n <= kGemmNarrowMaxN) return f(GemmNarrowCfg{});
+  if (m <= kGemmThinMaxM && n <= kGemmSkinnyMaxN && gemm_offsets_fit<GemmThinCfg>(lda, ldw, k))
+    return f(GemmThinCfg{});
   if (m > kGemmNarrowMaxM) {
     auto tiles = [&](auto cfg) {
       using C = decltype(cfg);

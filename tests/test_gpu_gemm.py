@@ -254,15 +254,17 @@ def test_gemm_small_m_tile_edges(n, k):
         assert torch.equal(bi.bi_gemm(ai.to(DEV), wi.to(DEV)).view(torch.int16).cpu(), want)
 
 
-@pytest.mark.parametrize("n", [4096, 6144, 12288])
+@pytest.mark.parametrize("n", [4096, 4097, 6144, 12288])
 def test_gemm_medium_m_tile_edges(n):
-    """From 65 rows bi_gemm runs the largest of the 128 x 128, 64 x 128 and
-    64 x 64 tiles whose grid has at least 192 tiles (for N = 4096 / 6144 /
-    12288 the switches sit at M = 256/257 and 640/641, 128/129 and 384/385,
-    and 128/129).  Whole products at M on both sides of every switch must
-    equal, row for row, the same rows computed as 64-row slices (the small-M
-    tiles), bf16 and fp32, and integer inputs must give the oracle rounded
-    once on the medium tiles."""
+    """From 65 rows bi_gemm runs the 32 x 64 tile up to 128 rows for weights
+    of at most 4096 rows, else the largest of the 128 x 128, 64 x 128 and
+    64 x 64 tiles whose grid has at least 192 tiles (for N = 4096 the switches
+    sit at M = 128/129, 256/257 and 640/641; for 4097 at 256/257 and 640/641;
+    for 6144 at 128/129 and 384/385; for 12288 at 128/129).  Whole products at
+    M on both sides of every switch must equal, row for row, the same rows
+    computed as 64-row slices (the small-M tiles), bf16 and fp32, and integer
+    inputs must give the oracle rounded once on the medium tiles (100 rows:
+    the 32 x 64 tile at N = 4096; 300 rows: a medium tile)."""
     k = 512
     w = W.randn_bf16((n, k), 17, "w", n, std=0.05, device=DEV)
     a = W.randn_bf16((700, k), 17, "x", k, device=DEV)
@@ -272,9 +274,11 @@ def test_gemm_medium_m_tile_edges(n):
         for m in (65, 128, 129, 256, 257, 384, 385, 640, 641, 700):
             cm = bi.bi_gemm(a[:m].contiguous(), w, out_dtype=dt)
             assert_bitwise(cm, sl[:m], f"n={n} M={m} vs 64-row slices ({dt})")
-    ai, wi = _int_bf16((300, 256), 18), _int_bf16((n, 256), 19)
-    want = torch.from_numpy(O.f64_to_bf16_bits(O.gemm(f64(ai), f64(wi))).view(np.int16))
-    assert torch.equal(bi.bi_gemm(ai.to(DEV), wi.to(DEV)).view(torch.int16).cpu(), want)
+    wi = _int_bf16((n, 256), 19)
+    for rows in (100, 300):
+        ai = _int_bf16((rows, 256), 18)
+        want = torch.from_numpy(O.f64_to_bf16_bits(O.gemm(f64(ai), f64(wi))).view(np.int16))
+        assert torch.equal(bi.bi_gemm(ai.to(DEV), wi.to(DEV)).view(torch.int16).cpu(), want)
 
 
 def test_gemm_wide_tile_batch_invariance():
