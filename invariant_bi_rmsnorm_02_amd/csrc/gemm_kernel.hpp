@@ -3,7 +3,7 @@
 // Matrix Multiplication", figs. "Data-Parallel Matrix Multiplication" and
 // "Split-K Matmul").
 //
-// The library instantiates eight configurations (gemm_with_cfg_mn picks one
+// The library instantiates nine configurations (gemm_with_cfg_mn picks one
 // from the shape; every one gives every element the same bits).  Whatever the
 // configuration,
 // the arithmetic of an output element is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
@@ -441,17 +441,22 @@ constexpr int64_t kGemmNarrowMaxN = 8192;
 // wavefronts of 16 x 16, a 6-stage ring of 128-wide K stages (72 KB, two
 // workgroups per CU).  With one 16-row block of A there is nothing to share
 // between wavefronts along m, so each wavefront streams its own 16 weight rows
-// with five 4 KB stages in flight.  Used up to kGemmSkinnyMaxM rows, and up to
-// kGemmNarrowMaxM rows for weights of at most kGemmSkinnyMaxN rows.  Measured
+// with five 4 KB stages in flight.  Used up to kGemmSkinnyMaxM rows.  Measured
 // on MI355X against the 16 x 64 / 64 x 64 tiles (bitwise equal), us: down
-// 12288 -> 4096 at M = 1 / 16 / 32 / 64, 24.9 / 27.1 / 27.3 / 42.2 against
-// 33.7 / 31.8 / 37.0 / 46.1; O 4096 -> 4096 at M = 1 / 64, 8.9 / 15.0 against
-// 12.2 / 17.2; QKV 4096 -> 6144 at M = 1 / 16, 11.3 / 12.1 against 13.4 /
-// 13.3; up 4096 -> 12288 at M = 1 / 16, 22.0 / 22.4 against 23.1 / 22.0.  At
-// M = 32 the wider weights read every weight row twice and lose to the 16 x
-// 64 and 64 x 64 tiles.
+// 12288 -> 4096 at M = 1 / 16, 24.9 / 27.1 against 33.7 / 31.8; O 4096 ->
+// 4096 at M = 1, 8.9 against 12.2; QKV 4096 -> 6144 at M = 1 / 16, 11.3 /
+// 12.1 against 13.4 / 13.3; up 4096 -> 12288 at M = 1 / 16, 22.0 / 22.4
+// against 23.1 / 22.0.
 using GemmSkinnyCfg = GemmCfg<32, 16, 2, 1, 6, 128, 2>;
 constexpr int64_t kGemmSkinnyMaxM = 16;
+// For weights of at most kGemmSkinnyMaxN rows (the O and down projections) at
+// 17 to kGemmNarrowMaxM rows: 16 (n) x 64 (m), 1 x 4 wavefronts of 16 x 16, a
+// 4-stage ring of 128-wide K stages (80 KB, two workgroups per CU): N / 16
+// workgroups stream the weight and the four 16-row blocks of A share each of
+// its stages.  Measured as above, us, against the 32 x 16 tile: down at M = 32
+// / 48 / 64, 27.4 / 31.7 / 35.4 against 27.2 / 43.7 / 42.1; O at M = 32 / 48 /
+// 64, 11.9 / 12.9 / 13.8 against 12.4 / 17.5 / 16.2.
+using GemmStripCfg = GemmCfg<16, 64, 1, 4, 4, 128, 2>;
 constexpr int64_t kGemmSkinnyMaxN = 4096;
 
 // The configurations for medium M (between the narrow and large-M rules): a
@@ -499,16 +504,16 @@ inline auto gemm_with_cfg_wide(int64_t lda, int64_t ldw, int64_t m, int64_t k, F
 // tests compare whole products bitwise across every threshold below).
 //   N >= kGemmWideMinN:                                     gemm_with_cfg_wide
 //   M >= kGemmBigMinM and >= kGemmBigMinTiles big tiles:    256 x 256
-//   M <= kGemmSkinnyMaxM, or M <= kGemmNarrowMaxM and
-//     N <= kGemmSkinnyMaxN:                                 32 x 16
-//   M <= kGemmNarrowMaxM and N <= kGemmNarrowMaxN:          16 x 64
+//   M <= kGemmSkinnyMaxM:                                   32 x 16
+//   M <= kGemmNarrowMaxM and N <= kGemmSkinnyMaxN:          16 x 64, 4 wavefronts
+//   M <= kGemmNarrowMaxM and N <= kGemmNarrowMaxN:          16 x 64, 2 wavefronts
 //   M <= kGemmThinMaxM and N <= kGemmSkinnyMaxN:            32 x 64
 //   M > kGemmNarrowMaxM and >= kGemmMidMinTiles tiles:      128 x 128, else 64 x 128
 //   otherwise:                                              64 x 64
 // (the big, 32 x 64, 128 x 128 and 64 x 128 tiles are skipped for the next
-// rule when their offsets would not fit their buffer resources; the caller checks the
-// chosen one, and the 32 x 16 and 16 x 64 tiles span fewer rows of A and W
-// than the 64 x 64 tile).
+// rule when their offsets would not fit their buffer resources; the caller
+// checks the chosen one, and the 32 x 16 and 16 x 64 tiles span fewer rows of
+// A and W than the 64 x 64 tile).
 template <class F>
 inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, F&& f) {
   using Bg = GemmBigCfg;
@@ -517,7 +522,8 @@ inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int
                    ((m + Bg::TM - 1) / Bg::TM) * ((n + Bg::TN - 1) / Bg::TN) >= kGemmBigMinTiles &&
                    gemm_offsets_fit<Bg>(lda, ldw, k);
   if (big) return f(Bg{});
-  if (m <= kGemmSkinnyMaxM || (m <= kGemmNarrowMaxM && n <= kGemmSkinnyMaxN)) return f(GemmSkinnyCfg{});
+  if (m <= kGemmSkinnyMaxM) return f(GemmSkinnyCfg{});
+  if (m <= kGemmNarrowMaxM && n <= kGemmSkinnyMaxN) return f(GemmStripCfg{});
   if (m <= kGemmNarrowMaxM && n <= kGemmNarrowMaxN) return f(GemmNarrowCfg{});
   if (m <= kGemmThinMaxM && n <= kGemmSkinnyMaxN && gemm_offsets_fit<GemmThinCfg>(lda, ldw, k))
     return f(GemmThinCfg{});
