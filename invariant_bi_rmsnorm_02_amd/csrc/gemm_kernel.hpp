@@ -3,7 +3,7 @@
 // Matrix Multiplication", figs. "Data-Parallel Matrix Multiplication" and
 // "Split-K Matmul").
 //
-// The library instantiates nine configurations (gemm_with_cfg_mn picks one
+// The library instantiates eight configurations (gemm_with_cfg_mn picks one
 // from the shape; every one gives every element the same bits).  Whatever the
 // configuration,
 // the arithmetic of an output element is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
@@ -423,17 +423,10 @@ constexpr int64_t kGemmBigMinM = 1024;
 constexpr int64_t kGemmBigMinTiles = 128;
 constexpr int64_t kGemmBigMinMWide = 512;
 
-// The configuration for small M and weights of at most kGemmNarrowMaxN rows:
-// 16 (n) x 64 (m) tile, 1 x 2 wavefronts of 16 x 32, a 6-stage ring of 64-wide
-// K stages (60 KB, two workgroups per CU).  At decode batch sizes such a
-// weight must be streamed by many workgroups: N / 16 of them instead of N / 64
-// (one CU pulls at most about 50 GB/s from HBM).  Measured on MI355X against
-// the 64 x 64 tile (bitwise equal): down 12288 -> 4096 at M = 1 / 8 / 64, 31.6
-// / 29.3 / 39.6 against 39.6 / 40.2 / 62.7 us; QKV 4096 -> 6144, 11.5 / 11.6
-// / 15.9 against 13.8 / 13.3 / 18.4 us.  The up projection (N = 12288) already
-// has 192 64-row strips and gains nothing; at M = 256 the narrow tile re-reads
-// A N / 16 times and is 1.6-1.7x slower.
-using GemmNarrowCfg = GemmCfg<16, 64, 1, 2, 6, 64, 2>;
+// Small M: up to kGemmNarrowMaxM rows the weight must be streamed by many
+// workgroups (one CU pulls at most about 50 GB/s from HBM), so the tiles
+// below are narrow in n; up to kGemmNarrowMaxN weight rows they beat the
+// 64 x 64 tile, whose N / 64 workgroups are too few.
 constexpr int64_t kGemmNarrowMaxM = 64;
 constexpr int64_t kGemmNarrowMaxN = 8192;
 
@@ -476,12 +469,16 @@ constexpr int64_t kGemmSkinnyMaxN = 4096;
 // 4096 at M = 512: 30.9 (64 x 128; 36.0 on 64 x 64).
 using GemmMidCfg = GemmCfg<64, 128, 2, 2, 3, 64, 2>;
 // And for weights of at most kGemmSkinnyMaxN rows at up to kGemmThinMaxM rows
-// (the O and down projections of a decode batch): 32 (n) x 64 (m), 2 x 2
+// (the O and down projections of a decode batch), and of at most
+// kGemmNarrowMaxN rows at 17 to kGemmNarrowMaxM rows: 32 (n) x 64 (m), 2 x 2
 // wavefronts of 16 x 32, a 6-stage ring (72 KB, two workgroups per CU), so
 // twice as many workgroups stream the weight as with 64 x 64.  Measured as
 // above: down at M = 96 / 128, 37.8 / 45.7 against 51.0 / 62.6 us; O at
-// M = 96 / 128, 15.3 / 16.9 against 18.5 / 21.3 us; at M = 256 it is 25-30 %
-// slower than 64 x 64.
+// M = 96 / 128, 15.3 / 16.9 against 18.5 / 21.3 us (at M = 256 it is 25-30 %
+// slower than 64 x 64); QKV 4096 -> 6144 at M = 32 / 48 / 64, 13.5 / 15.7 /
+// 17.7 against 15.2 / 19.3 / 22.1 us on a 2-wavefront 16 x 64 tile and 18.1 /
+// 20.6 / 22.4 us on 64 x 64.  Up 4096 -> 12288 at M = 48 / 64 is 15-20 %
+// faster on 64 x 64.
 using GemmThinCfg = GemmCfg<32, 64, 2, 2, 6, 64, 2>;
 constexpr int64_t kGemmThinMaxM = 128;
 using GemmSquareCfg = GemmCfg<128, 128, 2, 2, 4, 64, 1>;
@@ -505,9 +502,9 @@ inline auto gemm_with_cfg_wide(int64_t lda, int64_t ldw, int64_t m, int64_t k, F
 //   N >= kGemmWideMinN:                                     gemm_with_cfg_wide
 //   M >= kGemmBigMinM and >= kGemmBigMinTiles big tiles:    256 x 256
 //   M <= kGemmSkinnyMaxM:                                   32 x 16
-//   M <= kGemmNarrowMaxM and N <= kGemmSkinnyMaxN:          16 x 64, 4 wavefronts
-//   M <= kGemmNarrowMaxM and N <= kGemmNarrowMaxN:          16 x 64, 2 wavefronts
-//   M <= kGemmThinMaxM and N <= kGemmSkinnyMaxN:            32 x 64
+//   M <= kGemmNarrowMaxM and N <= kGemmSkinnyMaxN:          16 x 64
+//   M <= kGemmThinMaxM and N <= kGemmSkinnyMaxN, or
+//     M <= kGemmNarrowMaxM and N <= kGemmNarrowMaxN:        32 x 64
 //   M > kGemmNarrowMaxM and >= kGemmMidMinTiles tiles:      128 x 128, else 64 x 128
 //   otherwise:                                              64 x 64
 // (the big, 32 x 64, 128 x 128 and 64 x 128 tiles are skipped for the next
@@ -524,8 +521,8 @@ inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int
   if (big) return f(Bg{});
   if (m <= kGemmSkinnyMaxM) return f(GemmSkinnyCfg{});
   if (m <= kGemmNarrowMaxM && n <= kGemmSkinnyMaxN) return f(GemmStripCfg{});
-  if (m <= kGemmNarrowMaxM && n <= kGemmNarrowMaxN) return f(GemmNarrowCfg{});
-  if (m <= kGemmThinMaxM && n <= kGemmSkinnyMaxN && gemm_offsets_fit<GemmThinCfg>(lda, ldw, k))
+  if (((m <= kGemmThinMaxM && n <= kGemmSkinnyMaxN) || (m <= kGemmNarrowMaxM && n <= kGemmNarrowMaxN)) &&
+      gemm_offsets_fit<GemmThinCfg>(lda, ldw, k))
     return f(GemmThinCfg{});
   if (m > kGemmNarrowMaxM) {
     auto tiles = [&](auto cfg) {
