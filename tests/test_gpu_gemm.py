@@ -225,12 +225,13 @@ def test_gemm_tile_rule_edges(n, k, m_lo, m_hi):
 
 
 @pytest.mark.parametrize("n,k", [(4096, 12288), (4097, 512), (6144, 4096), (8192, 512), (8200, 512),
-                                 (12288, 4096)])
+                                 (12288, 4096), (16383, 512), (16384, 512)])
 def test_gemm_small_m_tile_edges(n, k):
     """Up to 16 rows every weight narrower than the wide rule runs the 32 x 16
-    tile; up to 64 rows a weight of at most 4096 rows runs the 16 x 64 tile
-    and one of at most 8192 rows the 32 x 64 tile; from 65 rows (or above 8192
-    weight rows) the larger tiles.  Rows shared by M = 1,
+    tile (from 16384 weight rows, up to 32 rows, the 32 x 64 tile); up to 64
+    rows a weight of at most 4096 rows runs the 16 x 64 tile and one of at most
+    8192 rows the 32 x 64 tile; from 65 rows (or above 8192 weight rows) the
+    larger tiles.  Rows shared by M = 1,
     16, 17, 64 and 65, and 16- and 32-row slices, must agree bit for bit, and
     integer inputs must give the oracle rounded once on the small-M paths."""
     w = W.randn_bf16((n, k), 14, "w", n, std=0.02, device=DEV)
