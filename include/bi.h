@@ -83,16 +83,24 @@ bi_status bi_rmsnorm(const void* x, int64_t ldx, const void* gamma, float eps,
  *    the epilogue use vector stores, which does not change any value).
  * One MFMA instruction and one ascending K loop with a single fp32
  * accumulator per output element, for every m: no split-K, so row m of C does
- * not depend on the other rows of A.  Two output tiles, 64 x 64 and 128 (n) x
- * 256 (m), give every element the same bits, so the tile only sets the speed:
- * 128 x 256 when n >= 32768 (a weight that wide fills the GPU with 128-row
- * strips even at m = 1), or when m >= 1024 and that tile's grid has at least
- * 256 tiles and its operand offsets fit (below); 64 x 64 otherwise.
+ * not depend on the other rows of A.  Every output tile gives every element
+ * the same bits, so the tile only sets the speed; it is chosen from m and n
+ * (n x m, first rule that applies):
+ *   n >= 32768 (a vocabulary-sized weight): 256 x 256 from m >= 512, else
+ *     128 x 256;
+ *   m >= 1024 and at least 128 tiles of 256 x 256: 256 x 256;
+ *   m <= 32 and n >= 16384: 32 x 64;    m <= 16: 32 x 16;
+ *   m <= 64 and n <= 4096: 16 x 64;
+ *   m <= 128 and n <= 4096, or m <= 64 and n <= 8192: 32 x 64;
+ *   m > 64: 128 x 128, else 64 x 128, if that tile's grid has at least 192
+ *     tiles;
+ *   otherwise 64 x 64.
+ * (The 256 x 256, 32 x 64, 128 x 128 and 64 x 128 tiles are passed over for
+ * the next rule when their operand offsets would not fit, below.)
  * k % 32 == 0; m, n >= 0 (m == 0 or n == 0 is a no-op); k >= 32.
- * BI_ERR_UNSUPPORTED when a tile's slice of A or W spans 2^31 bytes or more
- * ((rows - 1) * ld + k >= 2^30 elements, rows = 64 for A and W of the 64 x 64
- * tile, 256 for A and 128 for W of the wide one; for n < 32768 the large-m
- * rule then keeps the 64 x 64 tile) or the tile count overflows 32 bits.
+ * BI_ERR_UNSUPPORTED when the chosen tile's slice of A or W spans 2^31 bytes
+ * or more ((rows - 1) * ld + k >= 2^30 elements, rows = the tile's m or n
+ * extent) or the tile count overflows 32 bits.
  */
 bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw,
                   void* c, int64_t ldc, int32_t c_dtype,
