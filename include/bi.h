@@ -107,6 +107,39 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw,
                   int64_t m, int64_t n, int64_t k, bi_stream_t stream);
 
 /*
+ * GEMM with the residual add in its epilogue (the O and down projections of a
+ * decoder layer; [TML] "2. Batch-Invariant Matrix Multiplication" for the
+ * product, "Achieving Batch-Invariant Kernels" for the elementwise step):
+ *   y[m, n] = bf16( x[m, n] + bf16( sum_k A[m, k] * W[n, k] ) )
+ * bit for bit bi_gemm (bf16 output) followed by bi_add, without the
+ * intermediate product in memory.  a, w, m, n, k and the tile rule: as bi_gemm.
+ * x, y: [m, n] bf16, row strides ldx, ldy (>= n, multiples of 8), 16-byte
+ * aligned; y may be x itself (ldy == ldx: the in-place residual), other
+ * overlaps are not allowed.
+ * Errors: those of bi_gemm, and BI_ERR_INVALID_ARG for x or y.  m == 0 or
+ * n == 0 is a no-op.
+ */
+bi_status bi_gemm_add(const void* a, int64_t lda, const void* w, int64_t ldw, const void* x, int64_t ldx,
+                      void* y, int64_t ldy, int64_t m, int64_t n, int64_t k, bi_stream_t stream);
+
+/*
+ * GEMM with the gated activation in its epilogue (the gate/up projection of a
+ * decoder layer's MLP).  w_gate_up: [2f, k] bf16 holding the gate and up rows
+ * interleaved: row 2j is gate row j, row 2j + 1 is up row j.
+ *   out[m, j] = bf16( silu(g) * u ),  g = bf16( sum_k A[m, k] * w[2j, k] ),
+ *                                     u = bf16( sum_k A[m, k] * w[2j + 1, k] )
+ * bit for bit bi_gemm on the [gate; up] weight followed by bi_silu_mul (every
+ * GEMM output element is the same function of its own A row and W row, so
+ * where a W row sits changes no bit).  a, m, k and the tile rule: as bi_gemm
+ * with n = 2f.  out: [m, f] bf16, row stride ldo (>= f, a multiple of 8),
+ * 16-byte aligned.  f <= 2^29.
+ * Errors: those of bi_gemm, and BI_ERR_INVALID_ARG for out.  m == 0 or f == 0
+ * is a no-op.
+ */
+bi_status bi_gemm_silu_mul(const void* a, int64_t lda, const void* w_gate_up, int64_t ldw, void* out, int64_t ldo,
+                           int64_t m, int64_t f, int64_t k, bi_stream_t stream);
+
+/*
  * Paged KV cache layout (one pool per layer; page = `page_size` tokens, a
  * multiple of 16).  Both caches are [num_pages][num_kv_heads][page block] bf16;
  * a page block holds page_size / 16 tiles of 16 tokens, one after the other,

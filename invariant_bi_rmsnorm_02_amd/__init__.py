@@ -31,6 +31,8 @@ _SIGNATURES = {
     "bi_version": (ctypes.c_char_p, []),
     "bi_rmsnorm": (_c_i32, [_c_p, _c_i64, _c_p, _c_f32, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_gemm": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i32, _c_i64, _c_i64, _c_i64, _c_p]),
+    "bi_gemm_add": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p]),
+    "bi_gemm_silu_mul": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_kv_append": (_c_i32, [_c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
     "bi_attn_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "bi_attn_decode": (_c_i32, [_c_p, _c_i64, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
@@ -158,6 +160,63 @@ def bi_gemm(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None
     cdt = BI_F32 if out.dtype == torch.float32 else BI_BF16
     _check("bi_gemm", lib().bi_gemm(a.data_ptr(), _rows(a, "a"), w.data_ptr(), _rows(w, "w"), out.data_ptr(),
                                     _rows(out, "out"), cdt, m, n, k, _stream(stream)))
+    return out
+
+
+def bi_gemm_add(a: torch.Tensor, w: torch.Tensor, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """out = bf16(x + bf16(a w^T)): bi_gemm and bi_add in one kernel (out may be x)."""
+    _dev(a, "a", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    _dev(x, "x", torch.bfloat16)
+    m, k = a.shape
+    n, k2 = w.shape
+    if k != k2:
+        raise ValueError("inner dimensions differ")
+    if x.shape != (m, n):
+        raise ValueError("x must be [m, n]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    _dev(out, "out", torch.bfloat16)
+    if out.shape != (m, n):
+        raise ValueError("out shape")
+    _check("bi_gemm_add", lib().bi_gemm_add(a.data_ptr(), _rows(a, "a"), w.data_ptr(), _rows(w, "w"),
+                                            x.data_ptr(), _rows(x, "x"), out.data_ptr(), _rows(out, "out"),
+                                            m, n, k, _stream(stream)))
+    return out
+
+
+def interleave_gate_up(w_gu: torch.Tensor) -> torch.Tensor:
+    """The [gate; up] weight [2f, k] with its rows interleaved (gate row j at
+    2j, up row j at 2j + 1), the layout bi_gemm_silu_mul reads.  A one-time
+    re-layout of a weight (a copy), done when a layer is built."""
+    if w_gu.dim() != 2 or w_gu.shape[0] % 2:
+        raise ValueError("w_gu must be [2f, k]")
+    f, k = w_gu.shape[0] // 2, w_gu.shape[1]
+    return w_gu.view(2, f, k).transpose(0, 1).contiguous().view(2 * f, k)
+
+
+def bi_gemm_silu_mul(a: torch.Tensor, w_gate_up: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """out[:, j] = bf16(silu(g_j) * u_j) with g_j, u_j the bf16 products of a with rows 2j and 2j + 1 of
+    the interleaved weight (interleave_gate_up): bi_gemm and bi_silu_mul in one kernel."""
+    _dev(a, "a", torch.bfloat16)
+    _dev(w_gate_up, "w_gate_up", torch.bfloat16)
+    m, k = a.shape
+    n, k2 = w_gate_up.shape
+    if k != k2:
+        raise ValueError("inner dimensions differ")
+    if n % 2:
+        raise ValueError("w_gate_up must have 2f rows")
+    f = n // 2
+    if out is None:
+        out = torch.empty((m, f), dtype=torch.bfloat16, device=a.device)
+    _dev(out, "out", torch.bfloat16)
+    if out.shape != (m, f):
+        raise ValueError("out shape")
+    _check("bi_gemm_silu_mul", lib().bi_gemm_silu_mul(a.data_ptr(), _rows(a, "a"), w_gate_up.data_ptr(),
+                                                      _rows(w_gate_up, "w_gate_up"), out.data_ptr(),
+                                                      _rows(out, "out"), m, f, k, _stream(stream)))
     return out
 
 

@@ -26,7 +26,7 @@ ADAPTIVE_SOURCES = ["adaptive.hip"]
 ADAPTIVE_SHARED = ["gemm.hip", "rmsnorm.hip"]   # libbi objects linked into the comparator library
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "rmsnorm.hip", "gemm.hip", "kv_append.hip", "attn_decode.hip",
+SOURCES = ["api.cpp", "rmsnorm.hip", "gemm.hip", "gemm_fused.hip", "kv_append.hip", "attn_decode.hip",
            "attn_prefill.hip", "log_softmax.hip", "moe.hip", "lm_head.hip", "pointwise.hip", "scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -124,6 +124,41 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* 
   return from_hip(bi::launch_gemm(a, lda, w, ldw, c, ldc, c_dtype == BI_F32, m, n, k, as_stream(stream)));
 }
 
+// The A and W checks of bi_gemm (k, strides, alignment, offset range).
+static bi_status check_gemm_operands(const void* a, int64_t lda, const void* w, int64_t ldw, int64_t m, int64_t n,
+                                     int64_t k) {
+  if (k % 32) return BI_ERR_UNSUPPORTED;
+  if (m > (1 << 30) || n > (1 << 30) || k > (1 << 30)) return BI_ERR_UNSUPPORTED;
+  if (lda < k || ldw < k || lda % 8 || ldw % 8) return BI_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(w)) return BI_ERR_INVALID_ARG;
+  if (!bi::gemm_supported(lda, ldw, m, n, k)) return BI_ERR_UNSUPPORTED;
+  return BI_OK;
+}
+
+bi_status bi_gemm_add(const void* a, int64_t lda, const void* w, int64_t ldw, const void* x, int64_t ldx, void* y,
+                      int64_t ldy, int64_t m, int64_t n, int64_t k, bi_stream_t stream) {
+  if (m < 0 || n < 0 || k <= 0) return BI_ERR_INVALID_ARG;
+  if (m == 0 || n == 0) return BI_OK;
+  if (!a || !w || !x || !y) return BI_ERR_INVALID_ARG;
+  if (ldx < n || ldy < n || ldx % 8 || ldy % 8 || !aligned16(x) || !aligned16(y)) return BI_ERR_INVALID_ARG;
+  if (x == y && ldx != ldy) return BI_ERR_INVALID_ARG;
+  const bi_status st = check_gemm_operands(a, lda, w, ldw, m, n, k);
+  if (st != BI_OK) return st;
+  return from_hip(bi::launch_gemm_add(a, lda, w, ldw, x, ldx, y, ldy, m, n, k, as_stream(stream)));
+}
+
+bi_status bi_gemm_silu_mul(const void* a, int64_t lda, const void* w_gate_up, int64_t ldw, void* out, int64_t ldo,
+                           int64_t m, int64_t f, int64_t k, bi_stream_t stream) {
+  if (m < 0 || f < 0 || k <= 0) return BI_ERR_INVALID_ARG;
+  if (m == 0 || f == 0) return BI_OK;
+  if (!a || !w_gate_up || !out) return BI_ERR_INVALID_ARG;
+  if (f > (1 << 29)) return BI_ERR_UNSUPPORTED;
+  if (ldo < f || ldo % 8 || !aligned16(out)) return BI_ERR_INVALID_ARG;
+  const bi_status st = check_gemm_operands(a, lda, w_gate_up, ldw, m, 2 * f, k);
+  if (st != BI_OK) return st;
+  return from_hip(bi::launch_gemm_silu_mul(a, lda, w_gate_up, ldw, out, ldo, m, f, k, as_stream(stream)));
+}
+
 bi_status bi_kv_append(const void* k_new, const void* v_new, int64_t ld_new, const int32_t* slot_mapping,
                        int32_t num_tokens, void* k_cache, void* v_cache, int32_t num_pages,
                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size, bi_stream_t stream) {

@@ -348,10 +348,14 @@ __device__ __forceinline__ void gemm_store4_f32(float* cp, f32x4_t v, int cnt, b
   }
 }
 
-template <class Cfg, bool kF32Out>
-__global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
-    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
+// One workgroup's output tile of C = A W^T: picks the tile from blockIdx.x,
+// accumulates it over the whole of K and hands every finished output group to
+// st(r, n, v, cnt): global row r of C, global column n, v = C[r][n .. n+3] in
+// fp32 (before any rounding), cnt = columns of v below N.  bi_gemm's kernel
+// stores the groups; the fused kernels (gemm_fused.hip) transform them first.
+template <class Cfg, class Store>
+__device__ __forceinline__ void gemm_tile(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t ldw, int M,
+                                          int N, int K, int tiles_m, int tiles_n, Store&& st) {
   int tile_m, tile_n;
   gemm_map_tile(blockIdx.x, tiles_m, tiles_n, tile_m, tile_n);
   const int m0 = tile_m * Cfg::TM, n0 = tile_n * Cfg::TN;
@@ -377,11 +381,18 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
   gemm_mainloop<Cfg>(op, K, rows_a, acc);
 
   // Epilogue: lane holds C[m][n .. n+3].
-  gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) {
+  gemm_epilogue<Cfg>(acc, rows_a, n0, N, [&](int m, int n, f32x4_t v, int cnt) { st(m0 + m, n, v, cnt); });
+}
+
+template <class Cfg, bool kF32Out>
+__global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ W, int64_t ldw,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n, int vec_store) {
+  gemm_tile<Cfg>(A, lda, W, ldw, M, N, K, tiles_m, tiles_n, [&](int r, int n, f32x4_t v, int cnt) {
     if constexpr (kF32Out)
-      gemm_store4_f32(static_cast<float*>(C) + (int64_t)(m0 + m) * ldc + n, v, cnt, vec_store);
+      gemm_store4_f32(static_cast<float*>(C) + (int64_t)r * ldc + n, v, cnt, vec_store);
     else
-      gemm_store4_bf16(static_cast<uint16_t*>(C) + (int64_t)(m0 + m) * ldc + n, v, cnt, vec_store);
+      gemm_store4_bf16(static_cast<uint16_t*>(C) + (int64_t)r * ldc + n, v, cnt, vec_store);
   });
 }
 

@@ -18,6 +18,14 @@ bool gemm_supported(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc,
                        bool c_f32, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
+// bi_gemm with a residual add / the gated activation in the epilogue
+// (gemm_fused.hip); same tile rule and support test as bi_gemm (for
+// launch_gemm_silu_mul with n = 2 f).
+hipError_t launch_gemm_add(const void* a, int64_t lda, const void* w, int64_t ldw, const void* x, int64_t ldx,
+                           void* y, int64_t ldy, int64_t m, int64_t n, int64_t k, hipStream_t stream);
+hipError_t launch_gemm_silu_mul(const void* a, int64_t lda, const void* w, int64_t ldw, void* out, int64_t ldo,
+                                int64_t m, int64_t f, int64_t k, hipStream_t stream);
+
 hipError_t launch_kv_append(const void* k_new, const void* v_new, int64_t ld_new, const int32_t* slot_mapping,
                             int num_tokens, void* k_cache, void* v_cache, int num_pages,
                             int num_kv_heads, int head_dim, int page_size, hipStream_t stream);

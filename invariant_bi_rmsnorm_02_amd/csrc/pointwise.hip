@@ -9,9 +9,10 @@
 //             halves of a fused gate/up projection row
 //
 // One thread per 8 contiguous elements (one 16-byte load per operand); rows
-// are strided, so the views of a fused projection need no copy.
-#include "bi_common.hpp"
+// are strided, so the views of a fused projection need no copy.  The
+// arithmetic itself is in pointwise.hpp (shared with the fused GEMM epilogues).
 #include "launch.hpp"
+#include "pointwise.hpp"
 
 namespace bi {
 namespace {
@@ -28,11 +29,10 @@ __global__ __launch_bounds__(kPwThreads) void add_kernel(const uint16_t* x, int6
   const u32x4_t b = *reinterpret_cast<const u32x4_t*>(y + r * ldy + c);
   u32x4_t o;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(bf16_lo(a[e]) + bf16_lo(b[e]), bf16_hi(a[e]) + bf16_hi(b[e]));
+  for (int e = 0; e < 4; ++e)
+    o[e] = pack_bf16x2(pw_add(bf16_lo(a[e]), bf16_lo(b[e])), pw_add(bf16_hi(a[e]), bf16_hi(b[e])));
   *reinterpret_cast<u32x4_t*>(out + r * ldo + c) = o;
 }
-
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + exp2_hw(-g * kLog2e)) * u; }
 
 __global__ __launch_bounds__(kPwThreads) void silu_mul_kernel(const uint16_t* gu, int64_t ldgu, uint16_t* out,
                                                               int64_t ldo, int f, int f8, int64_t total8) {
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kPwThreads) void silu_mul_kernel(const uint16_t* gu
   u32x4_t o;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    o[e] = pack_bf16x2(silu_mul(bf16_lo(g[e]), bf16_lo(u[e])), silu_mul(bf16_hi(g[e]), bf16_hi(u[e])));
+    o[e] = pack_bf16x2(pw_silu_mul(bf16_lo(g[e]), bf16_lo(u[e])), pw_silu_mul(bf16_hi(g[e]), bf16_hi(u[e])));
   *reinterpret_cast<u32x4_t*>(out + r * ldo + c) = o;
 }
 

@@ -7,9 +7,15 @@ fused QKV projection, the gate and up halves out of the fused gate/up one).
     qkv = h W_qkv^T                            bi_gemm
     cache <- k, v                              bi_kv_append
     a  = attention(q, cache)                   bi_attn_decode / bi_attn_prefill
-    r  = x + a W_o^T                           bi_gemm, bi_add
+    r  = x + a W_o^T                           bi_gemm_add
     h2 = rmsnorm(r, g2)                        bi_rmsnorm
-    y  = r + (silu(gate) * up) W_down^T        bi_gemm, bi_silu_mul, bi_gemm, bi_add
+    y  = r + (silu(gate) * up) W_down^T        bi_gemm_silu_mul, bi_gemm_add
+
+The residual adds and the gated activation run in the epilogues of the GEMMs
+before them (bi_gemm_add, bi_gemm_silu_mul on the gate/up weight with its
+rows interleaved).  Each fused call gives bit for bit what the unfused pair
+(bi_gemm then bi_add / bi_silu_mul) gives; a `trace` call runs the unfused
+steps so that every intermediate can be checked.
 
 Each step is batch-invariant on its own (row-wise reductions in a fixed order,
 one GEMM tile and K order, fixed 256-token KV chunks, pointwise work), so a
@@ -23,18 +29,21 @@ from typing import Optional
 
 import torch
 
-from . import (bi_add, bi_attn_decode, bi_attn_decode_workspace_bytes, bi_attn_prefill, bi_gemm, bi_kv_append,
-               bi_lm_head_greedy, bi_lm_head_logprobs, bi_moe_ffn, bi_moe_route, bi_rmsnorm, bi_silu_mul)
+from . import (bi_add, bi_attn_decode, bi_attn_decode_workspace_bytes, bi_attn_prefill, bi_gemm, bi_gemm_add,
+               bi_gemm_silu_mul, bi_kv_append, bi_lm_head_greedy, bi_lm_head_logprobs, bi_moe_ffn, bi_moe_route,
+               bi_rmsnorm, bi_silu_mul, interleave_gate_up)
 
 
 class DecoderLayer:
     """Weights (bf16, on the device): w_qkv [(Hq + 2 Hkv) D, H], w_o [H, Hq D],
-    w_gu [2 F, H] (gate rows first, then up), w_down [H, F]; g1, g2 [H]."""
+    w_gu [2 F, H] (gate rows first, then up), w_down [H, F]; g1, g2 [H].  The
+    layer keeps w_gu only as its row-interleaved copy (w_gu_il), the layout of
+    bi_gemm_silu_mul; the w_gu property gives the [gate; up] layout back."""
 
     def __init__(self, w_qkv: torch.Tensor, w_o: torch.Tensor, w_gu: torch.Tensor, w_down: torch.Tensor,
                  g1: torch.Tensor, g2: torch.Tensor, num_q_heads: int, num_kv_heads: int, head_dim: int,
                  eps: float = 1e-6):
-        self.w_qkv, self.w_o, self.w_gu, self.w_down, self.g1, self.g2 = w_qkv, w_o, w_gu, w_down, g1, g2
+        self.w_qkv, self.w_o, self.w_down, self.g1, self.g2 = w_qkv, w_o, w_down, g1, g2
         self.hq, self.hkv, self.d, self.eps = num_q_heads, num_kv_heads, head_dim, eps
         self.scale = 1.0 / math.sqrt(head_dim)
         hd = (num_q_heads + 2 * num_kv_heads) * head_dim
@@ -42,6 +51,13 @@ class DecoderLayer:
             raise ValueError("w_qkv / w_o shapes do not match the head layout")
         if w_gu.shape[0] % 2 or w_down.shape != (w_qkv.shape[1], w_gu.shape[0] // 2):
             raise ValueError("w_gu / w_down shapes")
+        self.w_gu_il = interleave_gate_up(w_gu)
+
+    @property
+    def w_gu(self) -> torch.Tensor:
+        """The gate/up weight in its [gate; up] layout (a copy)."""
+        f = self.w_gu_il.shape[0] // 2
+        return self.w_gu_il.view(f, 2, -1).transpose(0, 1).reshape(2 * f, -1)
 
     # The three reductions of the layer, one library call each.
     def _norm(self, x: torch.Tensor, gamma: torch.Tensor) -> torch.Tensor:
@@ -71,14 +87,20 @@ class DecoderLayer:
 
     def _tail(self, x: torch.Tensor, attn: torch.Tensor, trace: Optional[dict]) -> torch.Tensor:
         T = x.shape[0]
-        c = self._gemm(attn.view(T, self.hq * self.d), self.w_o)
+        a2 = attn.view(T, self.hq * self.d)
+        if trace is None:
+            r = bi_gemm_add(a2, self.w_o, x)
+            h2 = self._norm(r, self.g2)
+            m = bi_gemm_silu_mul(h2, self.w_gu_il)
+            return bi_gemm_add(m, self.w_down, r, out=r)
+        c = self._gemm(a2, self.w_o)
         r = bi_add(x, c)
         h2 = self._norm(r, self.g2)
-        gu = self._gemm(h2, self.w_gu)
+        gu = self._gemm(h2, self.w_gu_il)                  # columns gate 0, up 0, gate 1, up 1, ...
+        gu = torch.cat((gu[:, 0::2], gu[:, 1::2]), dim=1)   # [gate | up]
         m = bi_silu_mul(gu)
         d = self._gemm(m, self.w_down)
-        if trace is not None:   # r is overwritten by the last add below
-            trace.update(attn=attn, c=c, r=r.clone(), h2=h2, gu=gu, m=m, d=d)
+        trace.update(attn=attn, c=c, r=r.clone(), h2=h2, gu=gu, m=m, d=d)   # r is overwritten below
         return bi_add(r, d, out=r)
 
     def decode(self, x: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
@@ -136,8 +158,12 @@ class MoEDecoderLayer(DecoderLayer):
 
     def _tail(self, x: torch.Tensor, attn: torch.Tensor, trace: Optional[dict]) -> torch.Tensor:
         T = x.shape[0]
-        c = self._gemm(attn.view(T, self.hq * self.d), self.w_o)
-        r = bi_add(x, c)
+        a2 = attn.view(T, self.hq * self.d)
+        if trace is None:
+            r = bi_gemm_add(a2, self.w_o, x)
+        else:
+            c = self._gemm(a2, self.w_o)
+            r = bi_add(x, c)
         h2 = self._norm(r, self.g2)
         ids, wts, logits = bi_moe_route(h2, self.w_gate, self.top_k)
         e = bi_moe_ffn(h2, ids, wts, self.w_up, self.w_down_e)

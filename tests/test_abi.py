@@ -38,6 +38,17 @@ def test_host_validation_without_gpu(lib):
     assert lib.bi_gemm(P, 64, P, 64, P, 64, 7, 4, 4, 64, None) == bi.BI_ERR_INVALID_ARG   # dtype
     assert lib.bi_gemm(P, 32, P, 64, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_INVALID_ARG   # lda < k
     assert lib.bi_gemm(P, 64, P, 64, P, 64, 0, 0, 4, 64, None) == bi.BI_OK
+    # fused epilogues: the GEMM checks, then x / y / out
+    assert lib.bi_gemm_add(P, 64, P, 64, P, 64, P, 64, 4, 4, 48, None) == bi.BI_ERR_UNSUPPORTED   # k % 32
+    assert lib.bi_gemm_add(P, 64, P, 64, P, 12, P, 64, 4, 16, 64, None) == bi.BI_ERR_INVALID_ARG  # ldx < n
+    assert lib.bi_gemm_add(P, 64, P, 64, P, 64, P, 72, 4, 16, 64, None) == bi.BI_ERR_INVALID_ARG  # y = x, ldy != ldx
+    assert lib.bi_gemm_add(P, 64, P, 64, None, 64, P, 64, 4, 16, 64, None) == bi.BI_ERR_INVALID_ARG
+    assert lib.bi_gemm_add(P, 64, P, 64, P, 64, P, 64, 0, 16, 64, None) == bi.BI_OK
+    assert lib.bi_gemm_silu_mul(P, 64, P, 64, P, 16, 4, 16, 48, None) == bi.BI_ERR_UNSUPPORTED    # k % 32
+    assert lib.bi_gemm_silu_mul(P, 64, P, 64, P, 8, 4, 16, 64, None) == bi.BI_ERR_INVALID_ARG     # ldo < f
+    assert lib.bi_gemm_silu_mul(P, 64, P, 64, P, 20, 4, 16, 64, None) == bi.BI_ERR_INVALID_ARG    # ldo % 8
+    assert lib.bi_gemm_silu_mul(P, 64, P, 64, P, 16, 4, (1 << 29) + 1, 64, None) == bi.BI_ERR_UNSUPPORTED
+    assert lib.bi_gemm_silu_mul(P, 64, P, 64, P, 16, 4, 0, 64, None) == bi.BI_OK
     # MoE: hidden not a multiple of 32, missing workspace, empty batch
     moe = lambda T, H, ws, nbytes: lib.bi_moe_ffn(P, H, P, P, T, 8, 128, P, P, H, 1536, P, H, ws, nbytes, None)
     assert moe(4, 4016, P, 1 << 30) == bi.BI_ERR_UNSUPPORTED

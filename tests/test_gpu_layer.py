@@ -124,6 +124,114 @@ def test_pointwise_validation():
                   torch.zeros((4, 8), dtype=torch.bfloat16, device=DEV))        # misaligned base
 
 
+def _padded(rows, cols, pad, seed, tag, std=1.0):
+    """A [rows, cols] bf16 view whose rows are `cols + pad` elements apart."""
+    buf = W.randn_bf16((rows, cols + pad), seed, "x", tag, std=std, device=DEV)
+    return buf[:, :cols]
+
+
+# (M, N, K): the decode and mixed-batch shapes of the O and down projections
+# (every tile of the rule: 32 x 16, 16 x 64, 32 x 64, 64 x 64, 64 x 128, 128 x 128,
+# 256 x 256), and small shapes with a ragged last n-group (N % 4 != 0).
+GEMM_ADD_SHAPES = [(1, 4096, 4096), (16, 4096, 12288), (17, 4096, 4096), (64, 4096, 12288), (65, 4096, 4096),
+                   (128, 4096, 12288), (300, 4096, 4096), (700, 4096, 4096), (2300, 4096, 12288),
+                   (5, 100, 64), (37, 38, 96), (130, 202, 128)]
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_ADD_SHAPES)
+def test_gemm_add_equals_unfused(m, n, k):
+    """bi_gemm_add is bit for bit bi_gemm (bf16) followed by bi_add: into a new
+    tensor, in place (y = x) and with padded row strides."""
+    log_case(f"gemm_add m={m} n={n} k={k}")
+    a = W.randn_bf16((m, k), SEED, "x", 20, device=DEV)
+    w = W.randn_bf16((n, k), SEED, "w", 21, std=0.02, device=DEV)
+    pad = 8 - n % 8 if n % 8 else 8
+    x = _padded(m, n, pad, SEED, 22)
+    c = torch.empty((m, n + pad), dtype=torch.bfloat16, device=DEV)[:, :n]
+    bi.bi_gemm(a, w, out=c)
+    want = torch.empty_like(c)
+    if n % 8 == 0:
+        bi.bi_add(x, c, out=want)
+    else:   # bi_add takes widths in multiples of 8: run it on the padded rows
+        xp, cp = x.as_strided((m, n + pad), x.stride()), c.as_strided((m, n + pad), c.stride())
+        cp[:, n:] = 0
+        wp = torch.empty((m, n + pad), dtype=torch.bfloat16, device=DEV)
+        bi.bi_add(xp, cp, out=wp)
+        want = wp[:, :n]
+    got = torch.empty((m, n + pad), dtype=torch.bfloat16, device=DEV)[:, :n]
+    bi.bi_gemm_add(a, w, x, out=got)
+    assert_bitwise(got, want, f"gemm_add {m}x{n}x{k}")
+    if n % 8 == 0:
+        assert_bitwise(bi.bi_gemm_add(a, w, x), want, f"gemm_add, new output {m}x{n}x{k}")
+    y = x.as_strided((m, n + pad), x.stride()).clone()[:, :n]
+    bi.bi_gemm_add(a, w, y, out=y)
+    assert_bitwise(y, want, f"gemm_add in place {m}x{n}x{k}")
+
+
+# (M, f, K): the gate/up projection of the decode and mixed-batch layers on
+# every tile of the rule, and small shapes (f odd: a last (gate, up) pair alone).
+GEMM_SILU_SHAPES = [(1, 12288, 4096), (16, 12288, 4096), (32, 12288, 4096), (33, 12288, 4096),
+                    (64, 12288, 4096), (65, 12288, 4096), (256, 12288, 4096), (1100, 12288, 4096),
+                    (3, 8, 64), (20, 25, 96), (70, 203, 128)]
+
+
+@pytest.mark.parametrize("m,f,k", GEMM_SILU_SHAPES)
+def test_gemm_silu_mul_equals_unfused(m, f, k):
+    """bi_gemm_silu_mul on the row-interleaved weight is bit for bit bi_gemm on
+    the [gate; up] weight followed by bi_silu_mul."""
+    log_case(f"gemm_silu_mul m={m} f={f} k={k}")
+    a = W.randn_bf16((m, k), SEED, "x", 23, device=DEV)
+    w = W.randn_bf16((2 * f, k), SEED, "w", 24, std=0.05, device=DEV)
+    w_il = bi.interleave_gate_up(w)
+    assert_bitwise(w_il[0::2], w[:f], "interleaved gate rows")
+    assert_bitwise(w_il[1::2], w[f:], "interleaved up rows")
+    gu = bi.bi_gemm(a, w)
+    fp = (f + 7) // 8 * 8       # bi_silu_mul takes f in multiples of 8: pad with zero columns
+    gp = torch.zeros((m, 2 * fp), dtype=torch.bfloat16, device=DEV)
+    gp[:, :f], gp[:, fp:fp + f] = gu[:, :f], gu[:, f:]
+    want = bi.bi_silu_mul(gp)[:, :f]
+    if f % 8 == 0:
+        assert_bitwise(bi.bi_gemm_silu_mul(a, w_il), want, f"gemm_silu_mul {m}x{f}x{k}")
+    out = torch.full((m, fp + 8), float("nan"), dtype=torch.bfloat16, device=DEV)
+    bi.bi_gemm_silu_mul(a, w_il, out=out[:, :f])
+    assert_bitwise(out[:, :f], want, f"gemm_silu_mul strided out {m}x{f}x{k}")
+    assert bool(torch.isnan(out[:, f:].float()).all()), "gemm_silu_mul wrote past f"
+
+
+def test_fused_gemm_oracle_parity():
+    """The fused calls against the oracle's definitions (bf16 product rounded,
+    then the elementwise step in fp64 and one rounding): within one bf16 ulp of
+    the oracle on the elementwise step, given the GEMM's bf16 output."""
+    m, n, k = 37, 96, 256
+    a = W.randn_bf16((m, k), SEED, "x", 25, device=DEV)
+    w = W.randn_bf16((n, k), SEED, "w", 26, std=0.05, device=DEV)
+    x = W.randn_bf16((m, n), SEED, "x", 27, device=DEV)
+    y = f64(bi.bi_gemm_add(a, w, x))
+    c = f64(bi.bi_gemm(a, w))
+    assert_bf16_close(bi.bi_gemm(a, w), O.gemm(f64(a), f64(w)), "gemm_add's product")
+    assert np.array_equal(y, O.round_bf16(f64(x) + c)), "gemm_add: x + bf16(product) not correctly rounded"
+    f = n // 2
+    wg = W.randn_bf16((2 * f, k), SEED, "w", 28, std=0.05, device=DEV)
+    h = f64(bi.bi_gemm_silu_mul(a, bi.interleave_gate_up(wg)))
+    gu = f64(bi.bi_gemm(a, wg))
+    ref = O.round_bf16(O.silu_mul(gu))
+    ulp = np.maximum(np.abs(ref), 2.0 ** -126) * 2.0 ** -7
+    assert np.all(np.abs(h - ref) <= ulp), "gemm_silu_mul off by more than one bf16 ulp"
+
+
+def test_fused_gemm_validation():
+    a = torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((16, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        bi.bi_gemm_add(a, w, torch.zeros((4, 8), dtype=torch.bfloat16, device=DEV))     # x not [m, n]
+    with pytest.raises(RuntimeError):
+        bi.bi_gemm_add(a, w, torch.zeros((4, 20), dtype=torch.bfloat16, device=DEV)[:, 2:18])  # misaligned x
+    with pytest.raises(ValueError):
+        bi.bi_gemm_silu_mul(a, torch.zeros((15, 64), dtype=torch.bfloat16, device=DEV))  # odd row count
+    with pytest.raises(RuntimeError):
+        bi.bi_gemm_silu_mul(a, w, out=torch.zeros((4, 12), dtype=torch.bfloat16, device=DEV)[:, :8])  # ldo
+
+
 U = 2.0 ** -8      # unit roundoff of bf16 (8 significant bits, round to nearest)
 
 
@@ -210,6 +318,7 @@ def test_layer_parity(shape):
     slots = torch.stack([c.slots[s][p] for s, p in enumerate(prefix)])
     tr = {}
     y = layer.decode(x, c.kc, c.vc, c.bt, lens, slots, 700, trace=tr)
+    assert_bitwise(layer.decode(x, c.kc, c.vc, c.bt, lens, slots, 700), y, f"{shape} decode: fused vs traced")
     torch.cuda.synchronize()
     for s, p in enumerate(prefix):
         rows = slice(s, s + 1)
@@ -227,6 +336,8 @@ def test_layer_parity(shape):
     slots = torch.cat([c.slots[s][p:p + n] for s, (p, n) in enumerate(zip(prefix, new))])
     tr = {}
     y = layer.prefill(x, c.kc, c.vc, c.bt, q_start, ctx, slots, max(new), trace=tr)
+    assert_bitwise(layer.prefill(x, c.kc, c.vc, c.bt, q_start, ctx, slots, max(new)), y,
+                   f"{shape} prefill: fused vs traced")
     torch.cuda.synchronize()
     for s, (p, n) in enumerate(zip(prefix, new)):
         rows = slice(int(q_start[s]), int(q_start[s + 1]))
