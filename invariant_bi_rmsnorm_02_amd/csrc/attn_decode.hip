@@ -408,68 +408,156 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32
   if (tid == 0) *next = 0;
 }
 
-constexpr int kMergeBatch = 64;
 constexpr int kMergeThreads = 256;
 
 // Folds a sequence's records in ascending order: chunk 0's record, then
 // chunks cg, cg + 1, ..., C - 1 (cg = 1: every chunk's partial; cg > 1: chunk
 // 0's record holds the fold of chunks 0 .. cg - 1).  Sequences with C <= done
-// were finished by their queue wavefront.
-template <int D>
+// were finished by their queue wavefront.  A workgroup folds DS of the D head
+// dims of one (sequence, q head) (DS < D: blockIdx.x = head * (D / DS) +
+// slice); every element is folded by the same operations whatever DS is (the
+// reference and the sum are per head: each slice's workgroup folds them
+// identically, and slice 0 writes the lse), so DS is a launch choice: few
+// (sequence, head) pairs are spread over more workgroups.
+template <int D, int DS>
 __global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(
     const float* __restrict__ ws, const int32_t* __restrict__ seq_lens, int max_seq_len, int Hq,
     int max_chunks, int cg, int done, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int E = D / 64;             // head dims per lane
-  constexpr int R = D + 4;              // floats per record
-  constexpr int kPieces = R / 4;        // 16-byte pieces per record
-  const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  static_assert(D % DS == 0 && DS % 32 == 0, "dim slices");
+  constexpr int E = DS >= 64 ? DS / 64 : 1;        // head dims per lane
+  constexpr int NL = DS / E;                        // lanes that fold
+  constexpr int R = D + 4;                          // floats per record in the workspace
+  constexpr int RS = DS + 4;                        // floats per record in LDS: the slice, then m, l
+  constexpr int kPieces = RS / 4;                   // 16-byte pieces per record
+  constexpr int kBatch = DS == D ? 64 : 128;        // records per LDS batch
+  constexpr int kLoads = (kBatch * kPieces + kMergeThreads - 1) / kMergeThreads;   // per thread per batch
+  const int head = blockIdx.x / (D / DS), slice = blockIdx.x % (D / DS), b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63;
   const int L = min(seq_lens[b], max_seq_len);
   const int C = L > 0 ? (L + kChunk - 1) / kChunk : 0;
   if (C <= done) return;
   const float* rec0 = ws + ((int64_t)b * Hq + head) * max_chunks * R;
 
   // The records folded, in order: t = 0 is chunk 0's, t >= 1 is chunk cg - 1 + t.
-  // The whole workgroup copies them into LDS kMergeBatch at a time (16-byte
-  // pieces, every load of a batch in flight at once), so a long sequence
-  // waits for one load latency per batch; wavefront 0 then folds the batch
-  // record by record in the same order.
-  __shared__ __attribute__((aligned(16))) float srec[kMergeBatch * R];
+  // The whole workgroup copies them into LDS kBatch at a time (16-byte pieces,
+  // every load of a batch issued before the first store waits), so a long
+  // sequence waits for one load latency per batch.  Wavefront 0 then folds the
+  // batch in two passes that split merge_coef / merge_val by what depends on
+  // the running state:
+  //  1. the references: 64 records at a time (lane j holds record j's mc), a
+  //     ballot finds the first record that passes the current reference by
+  //     more than the slack; the reference becomes its mc and the search goes
+  //     on after it.  That is the record-by-record rule (records that do not
+  //     pass leave the reference as it is), in one ballot per raise.  Lane j
+  //     keeps the reference before record j and forms record j's alpha and
+  //     beta with merge_coef, all lanes at once;
+  //  2. the fold: l and the accumulators take merge_val with each record's
+  //     coefficients in record order, eight records' operands read ahead.
+  // Every value is computed by the same operations on the same operands as a
+  // record-by-record merge_coef / merge_val loop, so the bits are the same.
+  __shared__ __attribute__((aligned(16))) float srec[kBatch * RS];
+  __shared__ __attribute__((aligned(8))) f32x2_t scoef[kBatch];
   float m = -INFINITY, l = 0.0f, acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
   const int T = C > 0 ? 1 + max(0, C - cg) : 0;
-  for (int t0 = 0; t0 < T; t0 += kMergeBatch) {
-    const int nb = min(kMergeBatch, T - t0);
+  for (int t0 = 0; t0 < T; t0 += kBatch) {
+    const int nb = min(kBatch, T - t0);
     if (t0 > 0) __syncthreads();     // wavefront 0 is done with the previous batch
-    for (int p = tid; p < nb * kPieces; p += kMergeThreads) {
-      const int j = p / kPieces, q = p - j * kPieces, t = t0 + j;
-      const float* rec = rec0 + (int64_t)(t == 0 ? 0 : cg - 1 + t) * R;
-      *reinterpret_cast<f32x4_t*>(&srec[j * R + 4 * q]) = *reinterpret_cast<const f32x4_t*>(rec + 4 * q);
+    f32x4_t piece[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int p = tid + i * kMergeThreads, j = p / kPieces, q = p - j * kPieces, t = t0 + j;
+      const int src = q < DS / 4 ? slice * DS + 4 * q : D;   // the slice's dims, then (m, l, pad)
+      if (p < nb * kPieces)
+        piece[i] = *reinterpret_cast<const f32x4_t*>(rec0 + (int64_t)(t == 0 ? 0 : cg - 1 + t) * R + src);
+    }
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int p = tid + i * kMergeThreads, j = p / kPieces, q = p - j * kPieces;
+      if (p < nb * kPieces) *reinterpret_cast<f32x4_t*>(&srec[j * RS + 4 * q]) = piece[i];
     }
     __syncthreads();
     if (tid < 64) {
-      for (int j = 0; j < nb; ++j) {
-        const float* rj = &srec[j * R];
-        const MergeCoef k = merge_coef(m, rj[D]);
-        l = merge_val(l, rj[D + 1], k);
+      for (int j0 = 0; j0 < nb; j0 += 64) {
+        const bool have = j0 + lane < nb;
+        const float mc = have ? srec[(j0 + lane) * RS + DS] : 0.0f;
+        float m_before = m;   // lane: the reference before its record
+        int from = 0;
+        for (;;) {
+          const uint64_t raise = __ballot(have && lane >= from && mc > m + kRefSlack);
+          if (raise == 0) break;
+          const int j = (int)__builtin_ctzll(raise);
+          const float mj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mc), j));
+          m_before = lane > j ? mj : m_before;
+          m = mj;
+          from = j + 1;
+        }
+        if (have) {
+          const MergeCoef k = merge_coef(m_before, mc);
+          scoef[j0 + lane] = f32x2_t{k.alpha, k.beta};
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < NL) {
+      auto fold = [&](f32x2_t ab, float lc, const float (&c)[E]) {
+        const MergeCoef k{0.0f, ab[0], ab[1]};
+        l = merge_val(l, lc, k);
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = merge_val(acc[e], rj[lane * E + e], k);
-        m = k.m;
+        for (int e = 0; e < E; ++e) acc[e] = merge_val(acc[e], c[e], k);
+      };
+      int j = 0;
+      for (; j + 8 <= nb; j += 8) {
+        f32x2_t ab[8];
+        float lc[8], c[8][E];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          ab[u] = scoef[j + u];
+          lc[u] = srec[(j + u) * RS + DS + 1];
+#pragma unroll
+          for (int e = 0; e < E; ++e) c[u][e] = srec[(j + u) * RS + lane * E + e];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) fold(ab[u], lc[u], c[u]);
+      }
+      for (; j < nb; ++j) {
+        float c[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) c[e] = srec[j * RS + lane * E + e];
+        fold(scoef[j], srec[j * RS + DS + 1], c);
       }
     }
   }
-  if (tid >= 64) return;
-  uint16_t* op = out + ((int64_t)b * Hq + head) * D + lane * E;
+  if (tid >= NL) return;
+  uint16_t* op = out + ((int64_t)b * Hq + head) * D + slice * DS + lane * E;
+  const bool write_lse = lse != nullptr && lane == 0 && slice == 0;
   if (C > 0) {
     const float inv = finalize_inv(l);
 #pragma unroll
     for (int e = 0; e < E; ++e) op[e] = static_cast<uint16_t>(f32_to_bf16(finalize_val(acc[e], inv)));
-    if (lse != nullptr && lane == 0) lse[(int64_t)b * Hq + head] = finalize_lse(m, l);
+    if (write_lse) lse[(int64_t)b * Hq + head] = finalize_lse(m, l);
   } else {
 #pragma unroll
     for (int e = 0; e < E; ++e) op[e] = 0;
-    if (lse != nullptr && lane == 0) lse[(int64_t)b * Hq + head] = -INFINITY;
+    if (write_lse) lse[(int64_t)b * Hq + head] = -INFINITY;
   }
+}
+
+// The merge launch: (sequence, q head) pairs below kMergeSliceBelow get one
+// workgroup per 32 head dims, so a few long sequences are folded by more CUs
+// (every slice folds its dims with the same operations; no bit moves).
+constexpr int kMergeSliceBelow = 1024;
+template <int D>
+hipError_t launch_merge(const float* ws, const int32_t* seq_lens, int max_seq_len, int Hq, int num_seqs,
+                        int max_chunks, int cg, int done, uint16_t* out, float* lse, hipStream_t stream) {
+  if ((int64_t)Hq * num_seqs < kMergeSliceBelow)
+    hipLaunchKernelGGL((attn_decode_merge_kernel<D, 32>), dim3(Hq * (D / 32), num_seqs), dim3(kMergeThreads), 0,
+                       stream, ws, seq_lens, max_seq_len, Hq, max_chunks, cg, done, out, lse);
+  else
+    hipLaunchKernelGGL((attn_decode_merge_kernel<D, D>), dim3(Hq, num_seqs), dim3(kMergeThreads), 0, stream, ws,
+                       seq_lens, max_seq_len, Hq, max_chunks, cg, done, out, lse);
+  return hipGetLastError();
 }
 
 // Scheduling (none of it changes a bit: a chunk is reduced the same way
@@ -541,9 +629,7 @@ hipError_t launch(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t*
                        lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(kMergeThreads), 0, stream, ws, seq_lens,
-                       max_seq_len, g.num_q_heads, max_chunks, 1, -1, os, lse);
-    return hipGetLastError();
+    return launch_merge<D>(ws, seq_lens, max_seq_len, g.num_q_heads, num_seqs, max_chunks, 1, -1, os, lse, stream);
   }
   int64_t cg = std::min<int64_t>(max_chunks, std::max<int64_t>(1, chunk_items / kDecodeQueueItems));
   auto upper = [&](int64_t c) { return pairs * ((max_chunks + c - 1) / c); };   // items, at most
@@ -561,9 +647,8 @@ hipError_t launch(const void* q, int64_t ld_q, const AttnGeom& g, const int32_t*
                      g.scale_log2, ws, max_chunks, (int)cg, os, lse, qd.item_seq, qd.item_group, qd.next, qd.total);
   e = hipGetLastError();
   if (e != hipSuccess || cg >= max_chunks) return e;
-  hipLaunchKernelGGL(attn_decode_merge_kernel<D>, dim3(g.num_q_heads, num_seqs), dim3(kMergeThreads), 0, stream, ws, seq_lens,
-                     max_seq_len, g.num_q_heads, max_chunks, (int)cg, (int)cg, os, lse);
-  return hipGetLastError();
+  return launch_merge<D>(ws, seq_lens, max_seq_len, g.num_q_heads, num_seqs, max_chunks, (int)cg, (int)cg, os, lse,
+                         stream);
 }
 
 }  // namespace
