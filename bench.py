@@ -686,14 +686,16 @@ def cost_of_invariance(torch, bi, step, reps):
         q, attn = step.q[:B], step.attn[:B]
         aa = torch.empty_like(attn)
         bt, lt = step.bt[:B], step.lens_t[:B]
-        wsa = torch.empty((A.lib().bia_attn_decode_workspace_bytes(B, 32, 8, 128),), dtype=torch.uint8, device=dev)
+        wsa = torch.empty((A.lib().bia_attn_decode_workspace_bytes(B, 32, 8, 128, 4096, 16),), dtype=torch.uint8,
+                          device=dev)
         ti = time_fn(torch, lambda i=0: bi.bi_attn_decode(q, step.kc, step.vc, bt, lt, 4096, step.scale, out=attn,
                                                           workspace=step.ws), reps)
         ta = time_fn(torch, lambda i=0: A.bia_attn_decode(q, step.kc, step.vc, bt, lt, 4096, step.scale, out=aa,
                                                           workspace=wsa), reps)
         out.append({"op": "attn decode 32/8 D128", "B": B, "us_invariant": round(ti[0], 2),
                     "us_adaptive": round(ta[0], 2), "cost": round(ti[0] / ta[0] - 1, 3),
-                    "splits": A.decode_splits(B, 8), "mismatched": mism(aa, attn), "elements": aa.numel()})
+                    "split_keys": A.decode_split_keys(B, 8, 4096, 16), "mismatched": mism(aa, attn),
+                    "elements": aa.numel()})
     del wq, wu, wd
     torch.cuda.empty_cache()
     return out

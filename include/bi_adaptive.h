@@ -41,16 +41,19 @@ bi_status bia_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void*
                    bi_stream_t stream);
 
 /*
- * Decode attention with a fixed number of KV splits, arguments as
- * bi_attn_decode.  splits = max(1, ceil(512 / (num_seqs * num_kv_heads)));
- * sequence s is cut into pieces of ceil(L_s / splits) keys rounded up to 32,
- * each reduced with the library's chunk step, then folded in order with the
- * library's merge step.  workspace: at least
- * bia_attn_decode_workspace_bytes(...) bytes, 16-byte aligned.
+ * Decode attention with the split size chosen from the batch, arguments as
+ * bi_attn_decode.  It is libbi.so's decode (the same chunk step, work queue,
+ * in-wave fold and merge) with one change: chunks of split_keys keys instead
+ * of 256, where S = max(1, ceil(512 / (num_seqs * num_kv_heads))) splits of a
+ * max_seq_len-key sequence give ceil(max_seq_len / S) keys, rounded up to a
+ * power of two between max(32, page_size) and 512
+ * (bia_attn_decode_split_keys).  At 256 keys the result is libbi.so's, bit for
+ * bit.  workspace: at least bia_attn_decode_workspace_bytes(...) bytes,
+ * 256-byte aligned (BI_ERR_WORKSPACE otherwise).
  */
-int32_t bia_attn_decode_splits(int32_t num_seqs, int32_t num_kv_heads);
+int32_t bia_attn_decode_split_keys(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t page_size);
 size_t bia_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim);
+                                       int32_t head_dim, int32_t max_seq_len, int32_t page_size);
 bi_status bia_attn_decode(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache,
                           int32_t num_pages, const int32_t* block_table, int32_t max_pages_per_seq,
                           const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,

@@ -23,8 +23,8 @@ _SIGNATURES = {
     "bia_gemm_splits": (_i32, [_i64, _i64, _i64]),
     "bia_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bia_gemm": (_i32, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _sz, _p]),
-    "bia_attn_decode_splits": (_i32, [_i32, _i32]),
-    "bia_attn_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "bia_attn_decode_split_keys": (_i32, [_i32, _i32, _i32, _i32]),
+    "bia_attn_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "bia_attn_decode": (_i32, [_p, _i64, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                _p, _p, _p, _sz, _p]),
     "bia_rmsnorm_slices": (_i32, [_i64, _i64]),
@@ -83,8 +83,9 @@ def bia_gemm(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = Non
     return out
 
 
-def decode_splits(num_seqs: int, num_kv_heads: int) -> int:
-    return int(lib().bia_attn_decode_splits(num_seqs, num_kv_heads))
+def decode_split_keys(num_seqs: int, num_kv_heads: int, max_seq_len: int, page_size: int) -> int:
+    """Keys per split the comparator picks for this batch (256: libbi's own decode)."""
+    return int(lib().bia_attn_decode_split_keys(num_seqs, num_kv_heads, max_seq_len, page_size))
 
 
 def bia_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
@@ -96,7 +97,7 @@ def bia_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     b, hq, _ = q.shape
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    ws = _ws(int(lib().bia_attn_decode_workspace_bytes(b, hq, hkv, d)), workspace, q.device)
+    ws = _ws(int(lib().bia_attn_decode_workspace_bytes(b, hq, hkv, d, int(max_seq_len), ps)), workspace, q.device)
     _check("bia_attn_decode", lib().bia_attn_decode(
         q.data_ptr(), _tokens(q, "q"), k_cache.data_ptr(), v_cache.data_ptr(), pages, block_table.data_ptr(),
         block_table.shape[1], seq_lens.data_ptr(), b, int(max_seq_len), hq, hkv, d, ps, float(softmax_scale),

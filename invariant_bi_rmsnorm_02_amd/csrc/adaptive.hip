@@ -7,9 +7,9 @@
 //     Batch-Invariant Matrix Multiplication", fig. "Split-K Matmul"): the split
 //     count follows the tile count, so row m's K order depends on M;
 //   - split-KV with a fixed NUMBER of splits (section "3. Batch-Invariant
-//     Attention", fig. "Fixed Number Split KV Strategy"): the split size is
-//     ceil(L / S) with S chosen from the batch, so the chunk boundaries move
-//     with L and with the batch;
+//     Attention", fig. "Fixed Number Split KV Strategy"): the split size
+//     follows a split count S chosen from the batch, so the chunk boundaries
+//     move with the batch;
 //   - split-reduction RMSNorm at small batch (section "1. Batch-Invariant
 //     RMSNorm", fig. "Split-Reduction RMSNorm"): a row's sum of squares is cut
 //     into a number of slices that depends on the number of rows.
@@ -18,10 +18,9 @@
 // parallelisation, not the code quality.
 #include <algorithm>
 
-#include "attn_chunk.hpp"
+#include "attn_decode_impl.hpp"
 #include "bi_adaptive.h"
 #include "gemm_kernel.hpp"
-#include "kv_layout.hpp"
 #include "launch.hpp"
 
 namespace bi {
@@ -89,149 +88,39 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-// ------------------------------------------------------------------ fixed split-count decode
+// ------------------------------------------------------------------ decode with a batch-chosen split size
 
-// Keys per split for a sequence of L tokens when the batch asks for `splits`
-// splits: ceil(L / splits) rounded up to whole 32-key sub-blocks.
-__device__ __host__ inline int split_keys(int L, int splits) {
-  const int c = (L + splits - 1) / splits;
-  return (c + kSub - 1) / kSub * kSub;
+// libbi's decode (attn_decode_impl.hpp: the chunk step, the work queue and its
+// placement, the in-wave fold, the merge) with one thing changed: the split
+// size is picked from the batch, as a fixed split COUNT would pick it.  S =
+// ceil(kTargetWorkgroups / (num_seqs * Hkv)) splits of a max_seq_len-key
+// sequence, i.e. ceil(max_seq_len / S) keys, taken as the next power of two
+// from max(32, page size) up to kDecodeMaxSplit.  At 256 keys the call is
+// libbi's own decode, bit for bit; any other size moves the chunk boundaries,
+// and with them the bits, as the batch changes.
+constexpr int kDecodeMinSplit = 32;
+constexpr int kDecodeMaxSplit = 512;    // longer splits spill the decode loop's fragment registers
+
+int decode_split_keys(int num_seqs, int num_kv_heads, int max_seq_len, int page_size) {
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  const int64_t splits = std::max<int64_t>(1, (kTargetWorkgroups + pairs - 1) / pairs);
+  const int64_t want = (std::max(max_seq_len, 1) + splits - 1) / splits;
+  int cs = std::max(kDecodeMinSplit, page_size);
+  while (cs < want && cs < kDecodeMaxSplit) cs *= 2;
+  return cs;
 }
 
 template <int D>
-__global__ __launch_bounds__(64, 2) void split_decode_partial_kernel(
-    const uint16_t* __restrict__ q, int64_t ldq, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    int num_pages, const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    int max_seq_len, int Hq, int Hkv, int log2_ps, float scale_log2, int splits, float* __restrict__ ws) {
-  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int L = min(seq_lens[b], max_seq_len);
-  const int cs = split_keys(max(L, 1), splits);
-  const int start = sp * cs;
-  if (start >= L) return;
-  const int len = min(cs, L - start);
-  const int G = Hq / Hkv;
-  const int lane = threadIdx.x, n = lane & 15, g = lane >> 4, l16 = lane & 15;
-  const int ps = 1 << log2_ps;
-
-  u32x4_t qf[1][D / 32];
-  const uint16_t* qp = q + (int64_t)b * ldq + (h * G + n) * D + 8 * g;
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) qf[0][ks] = n < G ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : zero4();
-
-  const int32_t* bt = block_table + (int64_t)b * max_pages;
-  auto page_of = [&](int key) {
-    const int lp = key >> log2_ps;
-    int pg = (lp < max_pages && key < L) ? bt[lp] : -1;
-    return (pg >= 0 && pg < num_pages) ? pg : -1;
-  };
-  struct Frags {
-    u32x4_t k[2][D / 32];
-    u32x4_t v[D / 16];
-    bool kok;   // this lane's K page exists
-    int vnv;    // keys of this lane's V group inside the split (<= 0: none)
-  };
-  // Raw fragments of sub-block j (keys start + 32 j ..).  Masks are applied
-  // only where a fragment is consumed (as in the invariant decode), so no load
-  // is waited for early: keys of missing pages read page 0 and are zeroed, V
-  // keys past the split are zeroed, K rows past it are masked in the score step.
-  auto fetch = [&](int j, Frags& f) {
-    const int key0 = start + kSub * j;
-    const int kkey = key0 + kTile * (l16 >> 3);
-    const int kpage = page_of(kkey);
-    f.kok = kpage >= 0;
-    const int64_t kb = tile_base(f.kok ? kpage : 0, h, kkey & (ps - 1), Hkv, log2_ps, D) + (int64_t)g * 128 +
-                       (l16 & 7) * 8;
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        f.k[bb][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kc + kb + 4 * ks * 128 + 8 * bb * 8));
-    const int vkey = key0 + kTile * (g >> 1);
-    const int vpage = page_of(vkey);
-    f.vnv = vpage >= 0 ? (start + len) - (key0 + 8 * g) : 0;
-    const int64_t vb = tile_base(vpage >= 0 ? vpage : 0, h, vkey & (ps - 1), Hkv, log2_ps, D) + (g & 1) * 128 +
-                       l16 * 8;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      f.v[dt] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vc + vb + dt * 256));
-  };
-  auto mask_k = [](Frags& f) {
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) f.k[bb][ks] = f.kok ? f.k[bb][ks] : zero4();
-  };
-  auto mask_v = [](Frags& f) {
-    const KeepMask km = keep_mask(f.vnv);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) f.v[dt] = apply_keep(f.v[dt], km);
-  };
-
-  const int nvalid[1] = {len};
-  const int n_sub = (len + kSub - 1) / kSub;
-  ChunkAcc<D, 1> acc;
-  chunk_init(acc);
-  u32x4_t spb[1];
-  // Ping-pong over sub-blocks; the fetch of a sub-block past the split is still
-  // issued (from valid memory, its result unused) so every path keeps the same
-  // loads in flight.
-  Frags fa, fb;
-  fetch(0, fa);
-  for (int j = 0; j < n_sub; j += 2) {
-    fetch(j + 1, fb);
-    mask_k(fa);
-    chunk_scores<D, 1>(acc, fa.k, qf, nvalid, j, scale_log2, spb);
-    mask_v(fa);
-    sub_values<D, 1>(acc, fa.v, spb);
-    if (j + 1 >= n_sub) break;
-    fetch(j + 2, fa);
-    mask_k(fb);
-    chunk_scores<D, 1>(acc, fb.k, qf, nvalid, j + 1, scale_log2, spb);
-    mask_v(fb);
-    sub_values<D, 1>(acc, fb.v, spb);
+hipError_t launch_split_decode(int cs, const void* q, int64_t ld_q, const AttnGeom& g, const int32_t* seq_lens,
+                               int num_seqs, int max_seq_len, void* out, float* lse, void* ws, hipStream_t st) {
+  switch (cs) {
+    case 32: return launch<D, 32>(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, ws, st);
+    case 64: return launch<D, 64>(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, ws, st);
+    case 128: return launch<D, 128>(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, ws, st);
+    case 256: return launch<D, 256>(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, ws, st);
+    case 512: return launch<D, 512>(q, ld_q, g, seq_lens, num_seqs, max_seq_len, out, lse, ws, st);
+    default: return hipErrorInvalidValue;
   }
-  const float lc = chunk_l(acc, 0);   // cross-lane: every lane takes part
-  if (n < G) {
-    float* rec = ws + (((int64_t)b * Hq + h * G + n) * splits + sp) * (D + 4);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = acc.o[0][dt];
-    if (g == 0) {
-      rec[D] = acc.m[0];
-      rec[D + 1] = lc;
-    }
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(64) void split_decode_merge_kernel(const float* __restrict__ ws,
-                                                                const int32_t* __restrict__ seq_lens,
-                                                                int max_seq_len, int Hq, int splits,
-                                                                uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int E = D / 64;
-  const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int L = min(seq_lens[b], max_seq_len);
-  const int C = L > 0 ? (L + split_keys(L, splits) - 1) / split_keys(L, splits) : 0;
-  const float* rec = ws + ((int64_t)b * Hq + head) * splits * (D + 4);
-  float m = -INFINITY, l = 0.0f, acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  for (int c = 0; c < C; ++c, rec += D + 4) {
-    const MergeCoef k = merge_coef(m, rec[D]);
-    l = merge_val(l, rec[D + 1], k);
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = merge_val(acc[e], rec[lane * E + e], k);
-    m = k.m;
-  }
-  uint16_t* op = out + ((int64_t)b * Hq + head) * D + lane * E;
-  const float inv = finalize_inv(l);
-#pragma unroll
-  for (int e = 0; e < E; ++e) op[e] = C > 0 ? static_cast<uint16_t>(f32_to_bf16(finalize_val(acc[e], inv))) : 0;
-  if (lse != nullptr && lane == 0) lse[(int64_t)b * Hq + head] = C > 0 ? finalize_lse(m, l) : -INFINITY;
-}
-
-int decode_splits(int num_seqs, int num_kv_heads) {
-  const int64_t items = (int64_t)num_seqs * num_kv_heads;
-  return static_cast<int>(std::max<int64_t>(1, (kTargetWorkgroups + items - 1) / items));
 }
 
 // ------------------------------------------------------------------ split-reduction RMSNorm
@@ -336,14 +225,17 @@ bi_status bia_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void*
   return from_hip(hipGetLastError());
 }
 
-int32_t bia_attn_decode_splits(int32_t num_seqs, int32_t num_kv_heads) {
-  return num_seqs > 0 && num_kv_heads > 0 ? decode_splits(num_seqs, num_kv_heads) : 1;
+int32_t bia_attn_decode_split_keys(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t page_size) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || page_size < 16 || page_size > 256 || (page_size & (page_size - 1)))
+    return kChunk;
+  return decode_split_keys(num_seqs, num_kv_heads, max_seq_len, page_size);
 }
 
 size_t bia_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim) {
+                                       int32_t head_dim, int32_t max_seq_len, int32_t page_size) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
-  return (size_t)num_seqs * num_q_heads * decode_splits(num_seqs, num_kv_heads) * (head_dim + 4) * sizeof(float);
+  const int cs = bia_attn_decode_split_keys(num_seqs, num_kv_heads, max_seq_len, page_size);
+  return decode_workspace_bytes_cs(num_seqs, num_q_heads, head_dim, std::max(max_seq_len, 1), cs);
 }
 
 bi_status bia_attn_decode(const void* q, int64_t ld_q, const void* k_cache, const void* v_cache, int32_t num_pages,
@@ -356,37 +248,35 @@ bi_status bia_attn_decode(const void* q, int64_t ld_q, const void* k_cache, cons
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return BI_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache)) return BI_ERR_INVALID_ARG;
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || num_pages <= 0) return BI_ERR_INVALID_ARG;
+  if (max_pages_per_seq <= 0) return BI_ERR_INVALID_ARG;
   const int G = num_q_heads / num_kv_heads;
   if (G > 16 || (head_dim != 64 && head_dim != 128)) return BI_ERR_UNSUPPORTED;
   int l2 = 0;
   while ((1 << l2) < page_size) ++l2;
   if ((1 << l2) != page_size || l2 < 4 || l2 > 8) return BI_ERR_UNSUPPORTED;
   if (ld_q < (int64_t)num_q_heads * head_dim || ld_q % 8) return BI_ERR_INVALID_ARG;
-  if (num_seqs > 65535) return BI_ERR_UNSUPPORTED;
-  if (!workspace || !aligned16(workspace) ||
-      workspace_bytes < bia_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim))
+  if (num_seqs > 65535 || max_seq_len > (1 << 24)) return BI_ERR_UNSUPPORTED;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      workspace_bytes < bia_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                        page_size))
     return BI_ERR_WORKSPACE;
-  const int splits = decode_splits(num_seqs, num_kv_heads);
-  const float sl = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
+  const int cs = decode_split_keys(num_seqs, num_kv_heads, max_seq_len, page_size);
+  AttnGeom g;
+  g.k_cache = k_cache;
+  g.v_cache = v_cache;
+  g.num_pages = num_pages;
+  g.block_table = block_table;
+  g.max_pages_per_seq = max_pages_per_seq;
+  g.num_q_heads = num_q_heads;
+  g.num_kv_heads = num_kv_heads;
+  g.head_dim = head_dim;
+  g.log2_page = l2;
+  g.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* ws = static_cast<float*>(workspace);
   const int msl = std::max(max_seq_len, 1);
-  if (head_dim == 64) {
-    hipLaunchKernelGGL(split_decode_partial_kernel<64>, dim3(splits, num_kv_heads, num_seqs), dim3(64), 0, st,
-                       static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k_cache),
-                       static_cast<const uint16_t*>(v_cache), num_pages, block_table, max_pages_per_seq, seq_lens,
-                       msl, num_q_heads, num_kv_heads, l2, sl, splits, ws);
-    hipLaunchKernelGGL(split_decode_merge_kernel<64>, dim3(num_q_heads, num_seqs), dim3(64), 0, st, ws, seq_lens,
-                       msl, num_q_heads, splits, static_cast<uint16_t*>(out), lse);
-  } else {
-    hipLaunchKernelGGL(split_decode_partial_kernel<128>, dim3(splits, num_kv_heads, num_seqs), dim3(64), 0, st,
-                       static_cast<const uint16_t*>(q), ld_q, static_cast<const uint16_t*>(k_cache),
-                       static_cast<const uint16_t*>(v_cache), num_pages, block_table, max_pages_per_seq, seq_lens,
-                       msl, num_q_heads, num_kv_heads, l2, sl, splits, ws);
-    hipLaunchKernelGGL(split_decode_merge_kernel<128>, dim3(num_q_heads, num_seqs), dim3(64), 0, st, ws, seq_lens,
-                       msl, num_q_heads, splits, static_cast<uint16_t*>(out), lse);
-  }
-  return from_hip(hipGetLastError());
+  return from_hip(head_dim == 64 ? launch_split_decode<64>(cs, q, ld_q, g, seq_lens, num_seqs, msl, out, lse, workspace, st)
+                                 : launch_split_decode<128>(cs, q, ld_q, g, seq_lens, num_seqs, msl, out, lse, workspace,
+                                                            st));
 }
 
 int32_t bia_rmsnorm_slices(int64_t rows, int64_t hidden) {

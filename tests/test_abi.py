@@ -153,5 +153,6 @@ def test_adaptive_library_exports_its_header():
     for n in names:
         assert hasattr(lib, n), n
     assert A.gemm_splits(1, 6144, 4096) > 1 and A.gemm_splits(2300, 6144, 4096) == 1
-    assert A.decode_splits(1, 8) == 64 and A.decode_splits(256, 8) == 1
+    assert A.decode_split_keys(1, 8, 4096, 16) == 64 and A.decode_split_keys(256, 8, 4096, 16) == 512
+    assert A.decode_split_keys(4, 8, 4096, 16) == 256 and A.decode_split_keys(1, 8, 100, 256) == 256
     assert lib.bia_gemm(None, 64, None, 64, None, 64, 4, 4, 64, None, 0, None) == bi.BI_ERR_INVALID_ARG

@@ -60,12 +60,18 @@ def test_splitk_gemm_is_not_batch_invariant():
 
 
 def test_split_decode_parity_and_negative_control():
+    """The comparator is libbi's decode with a split size picked from the
+    batch: request 0 decoded among 64 (512-key splits) and alone (32-key
+    splits) is close to the oracle both times but not bitwise equal; libbi
+    gives it the same bits either way."""
     hq, hkv, d = 32, 8, 128
     lens = W.decode_lengths(range(64), W.SEED_DECODE)
     big = Batch(range(64), lens, hq, hkv, d, W.SEED_DECODE)
     out64, _ = A.bia_attn_decode(big.q, big.kc, big.vc, big.bt, big.lens, max(lens), big.scale)
     one = Batch([0], lens[:1], hq, hkv, d, W.SEED_DECODE)
-    log_case(f"split decode L0={lens[0]} splits B=1: {A.decode_splits(1, hkv)}, B=64: {A.decode_splits(64, hkv)}")
+    k64, k1 = A.decode_split_keys(64, hkv, max(lens), 16), A.decode_split_keys(1, hkv, lens[0], 16)
+    log_case(f"split decode L0={lens[0]} split keys B=1: {k1}, B=64: {k64}")
+    assert k64 == 512 and k1 < 256
     out1, _ = A.bia_attn_decode(one.q, one.kc, one.vc, one.bt, one.lens, lens[0], one.scale)
     ref, _ = big.oracle([0, 5, 63])
     got = out64[[0, 5, 63]].cpu()
@@ -77,6 +83,22 @@ def test_split_decode_parity_and_negative_control():
     a1, _ = one.decode()
     a64, _ = big.decode()
     assert_bitwise(a1[0], a64[0], "bi_attn_decode request 0")
+
+
+def test_split_decode_at_256_keys_is_libbi():
+    """Four requests over 8 kv heads ask for 16 splits of 4096 keys: 256-key
+    splits, libbi's own chunk size, so the comparator gives libbi's bits."""
+    hq, hkv, d = 32, 8, 128
+    lens = W.decode_lengths(range(4), W.SEED_DECODE)
+    four = Batch(range(4), lens, hq, hkv, d, W.SEED_DECODE)
+    assert A.decode_split_keys(4, hkv, 4096, 16) == 256
+    got, gl = A.bia_attn_decode(four.q, four.kc, four.vc, four.bt, four.lens, 4096, four.scale,
+                                lse=torch.empty((4, hq), dtype=torch.float32, device=DEV))
+    want = torch.empty_like(got)
+    wl = torch.empty((4, hq), dtype=torch.float32, device=DEV)
+    bi.bi_attn_decode(four.q, four.kc, four.vc, four.bt, four.lens, 4096, four.scale, out=want, lse=wl)
+    assert_bitwise(got, want, "256-key splits == bi_attn_decode")
+    assert_bitwise(gl, wl, "256-key splits lse == bi_attn_decode lse")
 
 
 def test_split_rmsnorm_parity_and_negative_control():
