@@ -704,7 +704,7 @@ def cost_of_invariance(torch, bi, step, reps):
 # ---------------------------------------------------------------- HBM traffic (rocprofv3 counters)
 
 COUNTERS_MD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_step_b256_hbm_counters.md")
-DECODE_SOURCES = ["attn_decode.hip", "attn_chunk.hpp", "kv_layout.hpp", "bi_common.hpp"]
+DECODE_SOURCES = ["attn_decode.hip", "attn_decode_impl.hpp", "attn_chunk.hpp", "kv_layout.hpp", "bi_common.hpp"]
 
 
 def decode_traffic():
