@@ -31,6 +31,7 @@ _SIGNATURES = {
     "bi_version": (ctypes.c_char_p, []),
     "bi_rmsnorm": (_c_i32, [_c_p, _c_i64, _c_p, _c_f32, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_gemm": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i32, _c_i64, _c_i64, _c_i64, _c_p]),
+    "bi_gemm_tile": (_c_i32, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
     "bi_gemm_add": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_gemm_silu_mul": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_kv_append": (_c_i32, [_c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
@@ -161,6 +162,13 @@ def bi_gemm(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None
     _check("bi_gemm", lib().bi_gemm(a.data_ptr(), _rows(a, "a"), w.data_ptr(), _rows(w, "w"), out.data_ptr(),
                                     _rows(out, "out"), cdt, m, n, k, _stream(stream)))
     return out
+
+
+def gemm_tile(m: int, n: int, k: int, lda: Optional[int] = None, ldw: Optional[int] = None) -> Tuple[int, int]:
+    """(weight rows, A rows) of the output tile bi_gemm runs for an m x n x k product on the current device."""
+    tn, tm = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("bi_gemm_tile", lib().bi_gemm_tile(lda or k, ldw or k, m, n, k, ctypes.byref(tn), ctypes.byref(tm)))
+    return tn.value, tm.value
 
 
 def bi_gemm_add(a: torch.Tensor, w: torch.Tensor, x: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -124,6 +124,15 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* 
   return from_hip(bi::launch_gemm(a, lda, w, ldw, c, ldc, c_dtype == BI_F32, m, n, k, as_stream(stream)));
 }
 
+bi_status bi_gemm_tile(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, int32_t* tile_n, int32_t* tile_m) {
+  if (!tile_n || !tile_m || m <= 0 || n <= 0 || k <= 0 || lda < k || ldw < k) return BI_ERR_INVALID_ARG;
+  int tn = 0, tm = 0;
+  bi::gemm_tile_dims(lda, ldw, m, n, k, &tn, &tm);
+  *tile_n = tn;
+  *tile_m = tm;
+  return BI_OK;
+}
+
 // The A and W checks of bi_gemm (k, strides, alignment, offset range).
 static bi_status check_gemm_operands(const void* a, int64_t lda, const void* w, int64_t ldw, int64_t m, int64_t n,
                                      int64_t k) {

@@ -1,9 +1,33 @@
 // bi_gemm's launcher: the configuration of gemm_with_cfg_mn (gemm_kernel.hpp,
 // which also holds the kernel and why every configuration gives the same bits).
+#include <atomic>
+
 #include "gemm_kernel.hpp"
 #include "launch.hpp"
 
 namespace bi {
+
+int gemm_device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  const int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+void gemm_tile_dims(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, int* tile_n, int* tile_m) {
+  gemm_with_cfg_mn(lda, ldw, m, n, k, [&](auto cfg) {
+    using C = decltype(cfg);
+    *tile_n = C::TN;
+    *tile_m = C::TM;
+    return 0;
+  });
+}
 
 bool gemm_supported(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k) {
   return gemm_with_cfg_mn(lda, ldw, m, n, k, [&](auto cfg) {

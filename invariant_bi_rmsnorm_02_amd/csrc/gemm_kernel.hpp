@@ -3,7 +3,7 @@
 // Matrix Multiplication", figs. "Data-Parallel Matrix Multiplication" and
 // "Split-K Matmul").
 //
-// The library instantiates eight configurations (gemm_with_cfg_mn picks one
+// The library instantiates fourteen configurations (gemm_with_cfg_mn picks one
 // from the shape; every one gives every element the same bits).  Whatever the
 // configuration,
 // the arithmetic of an output element is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
@@ -424,14 +424,8 @@ constexpr int64_t kGemmWideMinN = 256 * GemmWideCfg::TN;
 // the same tile (4 or 5 stages) and the 4 x 2 wavefront layout were 2-15 %
 // slower; at M <= 256 this tile is 1.3-4.6x slower (too few weight streams).
 using GemmBigCfg = GemmCfg<256, 256, 2, 4, 2, 64, 1>;
-// Large-M rule: at least this many rows and, for a weight below
-// kGemmWideMinN rows, at least kGemmBigMinTiles tiles of the big grid (the
-// Qwen3-8B QKV weight at M = 1024 has 96 and runs 25 % slower on it than on
-// 64 x 64; at 128 and more - down at 1793 rows, QKV at 1281, up at 1024 - the
-// big tile wins).  For the vocabulary projection the big tile wins from
-// kGemmBigMinMWide rows on (it is 16 % slower at M = 64).
-constexpr int64_t kGemmBigMinM = 1024;
-constexpr int64_t kGemmBigMinTiles = 128;
+// For the vocabulary projection the big tile wins from kGemmBigMinMWide rows
+// on (it is 16 % slower at M = 64).
 constexpr int64_t kGemmBigMinMWide = 512;
 
 // Small M: up to kGemmNarrowMaxM rows the weight must be streamed by many
@@ -513,32 +507,71 @@ inline auto gemm_with_cfg_wide(int64_t lda, int64_t ldw, int64_t m, int64_t k, F
   return f(GemmWideCfg{});
 }
 
+// Further large- and medium-M tiles for the round-count rule below (n x m,
+// wavefront grid, ring, K per stage, workgroups per CU): 256 x 192 (2 x 4
+// wavefronts of 128 x 48, two 64-wide stages, 112 KB), 192 x 256 (2 x 4 of
+// 96 x 64, 112 KB), 256 x 160 (2 x 2 of 128 x 80, three stages, 160 KB),
+// 256 x 128 (2 x 4 of 128 x 32, three stages, 144 KB), 192 x 128 and
+// 128 x 192 (2 x 2 wavefronts, four stages, 160 KB).
+using Gemm256x192Cfg = GemmCfg<256, 192, 2, 4, 2, 64, 1>;
+using Gemm192x256Cfg = GemmCfg<192, 256, 2, 4, 2, 64, 1>;
+using Gemm256x160Cfg = GemmCfg<256, 160, 2, 2, 3, 64, 1>;
+using Gemm256x128Cfg = GemmCfg<256, 128, 2, 4, 3, 64, 1>;
+using Gemm192x128Cfg = GemmCfg<192, 128, 2, 2, 4, 64, 1>;
+using Gemm128x192Cfg = GemmCfg<128, 192, 2, 2, 4, 64, 1>;
+
+// Compute units of the current device (the number of tile slots per round is
+// this times a configuration's workgroups per CU).  Only speed depends on it.
+int gemm_device_cus();
+
+// The estimated time of configuration C on an m x n x k product, in us.  A
+// grid of T tiles puts L = ceil(T / CUs) workgroups on the busiest compute
+// unit.  One workgroup per CU (OCC = 1): L rounds, each one tile's flops /
+// rate + c0.  Two per CU (OCC = 2): L / 2 rounds with two tiles sharing a CU
+// at (rate, c0), and when L is odd one more with the CU to itself at (rate1,
+// c1), which is markedly faster per tile.  The rates (TFLOP/s per tile) and
+// constants (us) were fitted, weighting each time by its inverse, to every
+// configuration's times on the Qwen3-8B weights (QKV, O, up, fused gate/up,
+// down) at M = 129 .. 4096 on MI355X (160 shapes); over those the rule's picks
+// take 0.7 % more time in total than the fastest configuration of each shape.
+struct GemmRate {
+  double tflops, c0_us;
+  double tflops1 = 0.0, c1_us = 0.0;  // OCC = 2: a round with one workgroup per CU
+};
+template <class C>
+inline double gemm_estimate_us(int64_t m, int64_t n, int64_t k, GemmRate r, int cus) {
+  const int64_t tiles = ((m + C::TM - 1) / C::TM) * ((n + C::TN - 1) / C::TN);
+  const int64_t per_cu = (tiles + cus - 1) / cus;
+  const double mflop = 2.0 * C::TM * C::TN * (double)k / 1e6;
+  if (C::OCC == 1) return (double)per_cu * (mflop / r.tflops + r.c0_us);
+  return (double)(per_cu / 2) * (mflop / r.tflops + r.c0_us) + (double)(per_cu % 2) * (mflop / r.tflops1 + r.c1_us);
+}
+
 // bi_gemm's configuration.  Every configuration computes every output element
 // with the same fp32 chain of v_mfma_f32_16x16x32_bf16 steps over k = 0, 32,
 // 64, ... and one rounding, so the tile decides speed, never bits: the choice
 // may read M without making any row depend on the rest of the batch (the
-// tests compare whole products bitwise across every threshold below).
+// tests compare whole products bitwise across the tiles the rule picks).
 //   N >= kGemmWideMinN:                                     gemm_with_cfg_wide
-//   M >= kGemmBigMinM and >= kGemmBigMinTiles big tiles:    256 x 256
 //   M <= kGemmThinWideMaxM and N >= kGemmThinMinN:          32 x 64
 //   M <= kGemmSkinnyMaxM:                                   32 x 16
 //   M <= kGemmNarrowMaxM and N <= kGemmSkinnyMaxN:          16 x 64
 //   M <= kGemmThinMaxM and N <= kGemmSkinnyMaxN, or
 //     M <= kGemmNarrowMaxM and N <= kGemmNarrowMaxN:        32 x 64
-//   M > kGemmNarrowMaxM and >= kGemmMidMinTiles tiles:      128 x 128, else 64 x 128
-//   otherwise:                                              64 x 64
-// (the big, 32 x 64, 128 x 128 and 64 x 128 tiles are skipped for the next
-// rule when their offsets would not fit their buffer resources; the caller
-// checks the chosen one, and the 32 x 16 and 16 x 64 tiles span fewer rows of
-// A and W than the 64 x 64 tile).
+//   M <= kGemmThinMaxM:                                     128 x 128, else 64 x 128, with at least
+//                                                           kGemmMidMinTiles tiles; else 64 x 64
+//   otherwise (M > kGemmThinMaxM): the configuration with the least
+//     gemm_estimate_us among 256 x 256, 256 x 192, 192 x 256, 256 x 160,
+//     256 x 128, 128 x 256, 192 x 128, 128 x 192, 128 x 128, 64 x 128 and
+//     64 x 64 (first in that order on a tie).  Above 128 rows the grid's
+//     round count decides much of the time: a tile that leaves most CUs idle
+//     in its last round loses to a smaller one whose rounds are full.
+// (a tile whose offsets would not fit its buffer resources is passed over;
+// the caller checks the chosen one, and the 32 x 16, 16 x 64 and 64 x 64
+// tiles span fewer rows of A and W than any other).
 template <class F>
 inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, F&& f) {
-  using Bg = GemmBigCfg;
   if (n >= kGemmWideMinN) return gemm_with_cfg_wide(lda, ldw, m, k, f);
-  const bool big = m >= kGemmBigMinM &&
-                   ((m + Bg::TM - 1) / Bg::TM) * ((n + Bg::TN - 1) / Bg::TN) >= kGemmBigMinTiles &&
-                   gemm_offsets_fit<Bg>(lda, ldw, k);
-  if (big) return f(Bg{});
   if (m <= kGemmThinWideMaxM && n >= kGemmThinMinN && gemm_offsets_fit<GemmThinCfg>(lda, ldw, k))
     return f(GemmThinCfg{});
   if (m <= kGemmSkinnyMaxM) return f(GemmSkinnyCfg{});
@@ -546,16 +579,56 @@ inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int
   if (((m <= kGemmThinMaxM && n <= kGemmSkinnyMaxN) || (m <= kGemmNarrowMaxM && n <= kGemmNarrowMaxN)) &&
       gemm_offsets_fit<GemmThinCfg>(lda, ldw, k))
     return f(GemmThinCfg{});
-  if (m > kGemmNarrowMaxM) {
+  if (m <= kGemmThinMaxM) {
     auto tiles = [&](auto cfg) {
       using C = decltype(cfg);
       return ((m + C::TM - 1) / C::TM) * ((n + C::TN - 1) / C::TN);
     };
-    if (tiles(GemmSquareCfg{}) >= kGemmMidMinTiles && gemm_offsets_fit<GemmSquareCfg>(lda, ldw, k))
+    if (m > kGemmNarrowMaxM && tiles(GemmSquareCfg{}) >= kGemmMidMinTiles &&
+        gemm_offsets_fit<GemmSquareCfg>(lda, ldw, k))
       return f(GemmSquareCfg{});
-    if (tiles(GemmMidCfg{}) >= kGemmMidMinTiles && gemm_offsets_fit<GemmMidCfg>(lda, ldw, k)) return f(GemmMidCfg{});
+    if (m > kGemmNarrowMaxM && tiles(GemmMidCfg{}) >= kGemmMidMinTiles && gemm_offsets_fit<GemmMidCfg>(lda, ldw, k))
+      return f(GemmMidCfg{});
+    return f(GemmLibraryCfg{});
   }
-  return f(GemmLibraryCfg{});
+  const int cus = gemm_device_cus();
+  int pick = 10;  // 64 x 64: always fits
+  double best = 0.0;
+  bool have = false;
+  auto consider = [&](int id, auto cfg, GemmRate r) {
+    using C = decltype(cfg);
+    if (!gemm_offsets_fit<C>(lda, ldw, k)) return;
+    const double t = gemm_estimate_us<C>(m, n, k, r, cus);
+    if (!have || t < best) {
+      have = true;
+      best = t;
+      pick = id;
+    }
+  };
+  consider(0, GemmBigCfg{}, {6.10, 8.8});
+  consider(1, Gemm256x192Cfg{}, {5.30, 4.7});
+  consider(2, Gemm192x256Cfg{}, {5.55, 7.5});
+  consider(3, Gemm256x160Cfg{}, {4.70, 7.4});
+  consider(4, Gemm256x128Cfg{}, {5.08, 7.8});
+  consider(5, GemmWideCfg{}, {5.18, 7.5});
+  consider(6, Gemm192x128Cfg{}, {4.22, 6.2});
+  consider(7, Gemm128x192Cfg{}, {4.05, 4.3});
+  consider(8, GemmSquareCfg{}, {3.63, 3.1});
+  consider(9, GemmMidCfg{}, {1.39, -7.2, 2.65, 2.2});
+  consider(10, GemmLibraryCfg{}, {1.08, -5.0, 1.86, 0.0});
+  switch (pick) {
+    case 0: return f(GemmBigCfg{});
+    case 1: return f(Gemm256x192Cfg{});
+    case 2: return f(Gemm192x256Cfg{});
+    case 3: return f(Gemm256x160Cfg{});
+    case 4: return f(Gemm256x128Cfg{});
+    case 5: return f(GemmWideCfg{});
+    case 6: return f(Gemm192x128Cfg{});
+    case 7: return f(Gemm128x192Cfg{});
+    case 8: return f(GemmSquareCfg{});
+    case 9: return f(GemmMidCfg{});
+    default: return f(GemmLibraryCfg{});
+  }
 }
 
 template <class Cfg>

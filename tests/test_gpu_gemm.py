@@ -185,14 +185,13 @@ def test_gemm_wide_tile_gives_the_same_bits():
 
 @pytest.mark.parametrize("n,k", [(12288 + 72, 4096), (4096, 12288), (6144, 4096)])
 def test_gemm_large_m_rule_gives_the_same_bits(n, k):
-    """From 1024 rows on, a weight whose 256 x 256 grid has at least 128 tiles
-    runs that tile instead of 64 x 64 (the Qwen3-8B step weights at M = 2300;
-    the up projection, with a ragged n tail, already at M = 1024).  The whole
-    product at M in {1024, 1100, 2300} must equal, bit for bit, the same rows
-    computed in slices of at most 512 rows (64 x 64 tile), in bf16 and fp32."""
+    """Above 128 rows the tile comes from the round-count estimate (the
+    Qwen3-8B step weights at M = 1024, 1100 and 2300, the up projection with a
+    ragged n tail).  The whole product must equal, bit for bit, the same rows
+    computed in slices of at most 512 rows, in bf16 and fp32."""
     w = W.randn_bf16((n, k), 12, "w", n, std=0.02, device=DEV)
     for m in (1024, 1100, 2300):
-        log_case(f"gemm large-m rule m={m} n={n} k={k}")
+        log_case(f"gemm large-m rule m={m} n={n} k={k} tile={bi.gemm_tile(m, n, k)}")
         a = W.randn_bf16((m, k), 12, "x", m, device=DEV)
         for dt in (torch.bfloat16, torch.float32):
             whole = bi.bi_gemm(a, w, out_dtype=dt)
@@ -203,25 +202,72 @@ def test_gemm_large_m_rule_gives_the_same_bits(n, k):
         assert_f32_close(whole[::97, ::89], ref, f"large-m rule fp32 parity m={m} n={n}")
 
 
-@pytest.mark.parametrize("n,k,m_lo,m_hi", [
-    (12288, 4096, 1023, 1024),   # up projection: 48 big n-tiles, so the 1024-row rule decides
-    (6144, 4096, 1280, 1281),    # QKV: 24 n-tiles x 5 / 6 m-tiles = 120 / 144 big tiles
-    (4096, 12288, 1792, 1793)])  # down: 16 n-tiles x 7 / 8 m-tiles = 112 / 128 big tiles
-def test_gemm_tile_rule_edges(n, k, m_lo, m_hi):
-    """bi_gemm runs the 64 x 64 tile at m_lo and the 256 x 256 tile at m_hi
-    (the large-M rule: at least 1024 rows and at least 128 big tiles).  The
-    rows the two products share, and both products against the same rows in
-    256-row slices (64 x 64 tile), must agree bit for bit."""
-    w = W.randn_bf16((n, k), 13, "w", n, std=0.02, device=DEV)
-    a = W.randn_bf16((m_hi, k), 13, "x", m_hi, device=DEV)
-    log_case(f"gemm tile rule edge n={n} k={k} m={m_lo}/{m_hi}")
+# Every tile the rule may pick above 128 rows, with the weight shapes searched
+# for a product that reaches it (the rule depends on m, n, k and the device's
+# compute units, so the test finds its shapes instead of fixing them).
+LARGE_M_TILES = [(256, 256), (256, 192), (192, 256), (256, 160), (256, 128), (128, 256), (192, 128),
+                 (128, 192), (128, 128), (64, 128), (64, 64)]
+SEARCH_NK = [(n, k) for k in (4096, 512) for n in (1024, 2048, 4096, 6144, 12288)]
+
+
+def _find_m(tile, limit=4400):
+    for n, k in SEARCH_NK:
+        for m in range(129, limit, 7):
+            if bi.gemm_tile(m, n, k) == tile:
+                return m, n, k
+    return None
+
+
+@pytest.mark.parametrize("tile", LARGE_M_TILES)
+def test_gemm_every_large_m_tile_gives_the_same_bits(tile):
+    """For each tile of the large-M rule, a product the rule runs on it must
+    equal, bit for bit, the same rows computed in 128-row slices (which run the
+    medium-M tiles), in bf16 and fp32, and sampled entries the oracle."""
+    found = _find_m(tile)
+    assert found is not None, f"no shape reaches tile {tile}"
+    m, n, k = found
+    log_case(f"gemm tile {tile}: m={m} n={n} k={k}")
+    w = W.randn_bf16((n, k), 14, "w", n + k, std=0.02, device=DEV)
+    a = W.randn_bf16((m, k), 14, "x", m, device=DEV)
     for dt in (torch.bfloat16, torch.float32):
-        lo = bi.bi_gemm(a[:m_lo], w, out_dtype=dt)
-        hi = bi.bi_gemm(a, w, out_dtype=dt)
-        sliced = torch.cat([bi.bi_gemm(a[r:r + 256], w, out_dtype=dt) for r in range(0, m_hi, 256)])
-        assert_bitwise(hi[:m_lo], lo, f"rows shared by m={m_lo} and m={m_hi} ({dt})")
-        assert_bitwise(hi, sliced, f"m={m_hi} vs 256-row slices ({dt})")
-        assert_bitwise(lo, sliced[:m_lo], f"m={m_lo} vs 256-row slices ({dt})")
+        whole = bi.bi_gemm(a, w, out_dtype=dt)
+        sliced = torch.cat([bi.bi_gemm(a[r:r + 128], w, out_dtype=dt) for r in range(0, m, 128)])
+        assert_bitwise(whole, sliced, f"tile {tile} m={m} n={n} k={k} {dt}")
+    ref = O.gemm(f64(a[::131]), f64(w[::113]))
+    assert_f32_close(whole[::131, ::113], ref, f"tile {tile} fp32 parity")
+
+
+def _rule_edges(n, k, lo=129, hi=4400, limit=4):
+    """Consecutive m where the rule's tile changes."""
+    out, prev = [], bi.gemm_tile(lo, n, k)
+    for m in range(lo + 1, hi):
+        t = bi.gemm_tile(m, n, k)
+        if t != prev:
+            out.append((m - 1, m, prev, t))
+            if len(out) >= limit:
+                break
+        prev = t
+    return out
+
+
+@pytest.mark.parametrize("n,k", [(12288, 4096), (6144, 4096), (4096, 12288)])
+def test_gemm_tile_rule_edges(n, k):
+    """At the first rows counts where the large-M rule changes tile for the
+    Qwen3-8B weights, m_lo and m_hi = m_lo + 1 run different tiles; the rows
+    the two products share, and both products against the same rows in
+    256-row slices, must agree bit for bit."""
+    edges = _rule_edges(n, k)
+    assert edges, f"the rule never changes tile for n={n} k={k}"
+    w = W.randn_bf16((n, k), 13, "w", n, std=0.02, device=DEV)
+    for m_lo, m_hi, t_lo, t_hi in edges:
+        a = W.randn_bf16((m_hi, k), 13, "x", m_hi, device=DEV)
+        log_case(f"gemm tile rule edge n={n} k={k} m={m_lo}/{m_hi}: {t_lo} -> {t_hi}")
+        for dt in (torch.bfloat16, torch.float32):
+            lo = bi.bi_gemm(a[:m_lo], w, out_dtype=dt)
+            hi = bi.bi_gemm(a, w, out_dtype=dt)
+            sliced = torch.cat([bi.bi_gemm(a[r:r + 256], w, out_dtype=dt) for r in range(0, m_hi, 256)])
+            assert_bitwise(hi[:m_lo], lo, f"rows shared by m={m_lo} and m={m_hi} ({dt})")
+            assert_bitwise(hi, sliced, f"m={m_hi} vs 256-row slices ({dt})")
 
 
 @pytest.mark.parametrize("n,k", [(4096, 12288), (4097, 512), (6144, 4096), (8192, 512), (8200, 512),
