@@ -84,20 +84,17 @@ bi_status bi_rmsnorm(const void* x, int64_t ldx, const void* gamma, float eps,
  * One MFMA instruction and one ascending K loop with a single fp32
  * accumulator per output element, for every m: no split-K, so row m of C does
  * not depend on the other rows of A.  Every output tile gives every element
- * the same bits, so the tile only sets the speed; it is chosen from m and n
- * (n x m, first rule that applies):
+ * the same bits, so the tile only sets the speed; it is chosen from the
+ * shape (n x m, first rule that applies):
  *   n >= 32768 (a vocabulary-sized weight): 256 x 256 from m >= 512, else
  *     128 x 256;
- *   m <= 32 and n >= 16384: 32 x 64;    m <= 16: 32 x 16;
- *   m <= 64 and n <= 4096: 16 x 64;
- *   m <= 128 and n <= 4096, or m <= 64 and n <= 8192: 32 x 64;
- *   m <= 128: 128 x 128 (m > 64), else 64 x 128 (m > 64), if that tile's grid
- *     has at least 192 tiles; otherwise 64 x 64;
- *   m > 128: of 256 x 256, 256 x 192, 192 x 256, 256 x 160, 256 x 128,
- *     128 x 256, 192 x 128, 128 x 192, 128 x 128, 64 x 128 and 64 x 64, the
- *     one whose grid is estimated to finish first (from the workgroups its
- *     busiest compute unit runs and per-tile rates measured on MI355X;
- *     bi_gemm_tile reports the choice).
+ *   m <= 32 and n >= 16384: 32 x 64;
+ *   otherwise, of twenty-one configurations (tiles from 256 x 256 down to
+ *     16 x 64 and 32 x 16), the one whose grid is estimated to finish first,
+ *     from the workgroups its busiest compute unit runs and per-round costs
+ *     measured on MI355X (bi_gemm_tile reports the choice).  When k is a
+ *     multiple of 64 but not of 128, tiles with 128-wide K stages are left
+ *     out, so that an exact zero gets the same sign from every candidate.
  * (A tile is passed over for the next candidate when its operand offsets
  * would not fit, below.)
  * k % 32 == 0; m, n >= 0 (m == 0 or n == 0 is a no-op); k >= 32.
@@ -110,13 +107,18 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw,
                   int64_t m, int64_t n, int64_t k, bi_stream_t stream);
 
 /*
- * The output tile bi_gemm (and bi_gemm_add, bi_gemm_silu_mul with n = 2f)
- * runs for these arguments on the current device: *tile_n weight rows by
- * *tile_m rows of A.  It changes no result bit; tests use it to reach every
- * tile.  Host-only, no GPU work.  BI_ERR_INVALID_ARG for a null pointer,
- * m, n or k <= 0, or lda, ldw < k.
+ * The kernel configuration bi_gemm (and bi_gemm_add, bi_gemm_silu_mul with
+ * n = 2f) runs for these arguments on the current device: an output tile of
+ * tile_n weight rows by tile_m rows of A, waves_n x waves_m wavefronts, an LDS
+ * ring of `stages` stages of stage_k values of K, aimed at per_cu workgroups
+ * per compute unit.  It changes no result bit; tests use it to reach every
+ * configuration.  Host-only, no GPU work.  BI_ERR_INVALID_ARG for a null
+ * pointer, m, n or k <= 0, or lda, ldw < k.
  */
-bi_status bi_gemm_tile(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, int32_t* tile_n, int32_t* tile_m);
+typedef struct {
+  int32_t tile_n, tile_m, waves_n, waves_m, stages, stage_k, per_cu;
+} bi_gemm_config;
+bi_status bi_gemm_tile(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, bi_gemm_config* config);
 
 /*
  * GEMM with the residual add in its epilogue (the O and down projections of a

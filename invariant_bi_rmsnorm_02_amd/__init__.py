@@ -31,7 +31,7 @@ _SIGNATURES = {
     "bi_version": (ctypes.c_char_p, []),
     "bi_rmsnorm": (_c_i32, [_c_p, _c_i64, _c_p, _c_f32, _c_p, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_gemm": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i32, _c_i64, _c_i64, _c_i64, _c_p]),
-    "bi_gemm_tile": (_c_i32, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
+    "bi_gemm_tile": (_c_i32, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_gemm_add": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_gemm_silu_mul": (_c_i32, [_c_p, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p]),
     "bi_kv_append": (_c_i32, [_c_p, _c_p, _c_i64, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
@@ -164,11 +164,21 @@ def bi_gemm(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None
     return out
 
 
+class _GemmConfig(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in ("tile_n", "tile_m", "waves_n", "waves_m", "stages", "stage_k", "per_cu")]
+
+
+def gemm_config(m: int, n: int, k: int, lda: Optional[int] = None, ldw: Optional[int] = None) -> Tuple[int, ...]:
+    """(tile n, tile m, wavefronts n, wavefronts m, stages, K per stage, workgroups per CU) of the kernel
+    configuration bi_gemm runs for an m x n x k product on the current device."""
+    c = _GemmConfig()
+    _check("bi_gemm_tile", lib().bi_gemm_tile(lda or k, ldw or k, m, n, k, ctypes.byref(c)))
+    return tuple(getattr(c, f) for f, _ in _GemmConfig._fields_)
+
+
 def gemm_tile(m: int, n: int, k: int, lda: Optional[int] = None, ldw: Optional[int] = None) -> Tuple[int, int]:
     """(weight rows, A rows) of the output tile bi_gemm runs for an m x n x k product on the current device."""
-    tn, tm = ctypes.c_int32(0), ctypes.c_int32(0)
-    _check("bi_gemm_tile", lib().bi_gemm_tile(lda or k, ldw or k, m, n, k, ctypes.byref(tn), ctypes.byref(tm)))
-    return tn.value, tm.value
+    return gemm_config(m, n, k, lda, ldw)[:2]
 
 
 def bi_gemm_add(a: torch.Tensor, w: torch.Tensor, x: torch.Tensor, out: Optional[torch.Tensor] = None,

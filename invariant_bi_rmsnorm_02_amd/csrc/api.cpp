@@ -124,12 +124,11 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* 
   return from_hip(bi::launch_gemm(a, lda, w, ldw, c, ldc, c_dtype == BI_F32, m, n, k, as_stream(stream)));
 }
 
-bi_status bi_gemm_tile(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, int32_t* tile_n, int32_t* tile_m) {
-  if (!tile_n || !tile_m || m <= 0 || n <= 0 || k <= 0 || lda < k || ldw < k) return BI_ERR_INVALID_ARG;
-  int tn = 0, tm = 0;
-  bi::gemm_tile_dims(lda, ldw, m, n, k, &tn, &tm);
-  *tile_n = tn;
-  *tile_m = tm;
+bi_status bi_gemm_tile(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, bi_gemm_config* config) {
+  if (!config || m <= 0 || n <= 0 || k <= 0 || lda < k || ldw < k) return BI_ERR_INVALID_ARG;
+  int v[7];
+  bi::gemm_config_of(lda, ldw, m, n, k, v);
+  *config = bi_gemm_config{v[0], v[1], v[2], v[3], v[4], v[5], v[6]};
   return BI_OK;
 }
 

@@ -3,11 +3,11 @@
 // Matrix Multiplication", figs. "Data-Parallel Matrix Multiplication" and
 // "Split-K Matmul").
 //
-// The library instantiates fourteen configurations (gemm_with_cfg_mn picks one
-// from the shape; every one gives every element the same bits).  Whatever the
-// configuration,
-// the arithmetic of an output element is the same: one fp32 accumulator, v_mfma_f32_16x16x32_bf16 steps over
-// k = 0, 32, 64, ... in ascending order, no split of K.  Nothing here depends on
+// The library instantiates twenty-one configurations (gemm_with_cfg_mn picks
+// one from the shape; every one gives every element the same bits).  Whatever
+// the configuration, the arithmetic of an output element is the same: one fp32
+// accumulator, v_mfma_f32_16x16x32_bf16 steps over k = 0, 32, 64, ... in
+// ascending order, no split of K.  Nothing here depends on
 // M except which rows are loaded and which 16-row MFMA blocks are skipped
 // because all their rows are past M.
 //
@@ -396,106 +396,65 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::OCC) void gemm_kernel(
   });
 }
 
-// The library's GEMM configuration for weights narrower than kGemmWideMinN
-// rows at medium M (bi_gemm between the narrow and large-M rules of
-// gemm_with_cfg_mn) and for the expert GEMMs of bi_moe_ffn.  Chosen by timing
-// candidates at every workload shape on MI355X: 64 (n) x 64 (m) output tile, 2 x 2 wavefronts of 32 x 32, K in 64-wide
-// stages, a 5-stage LDS ring (80 KB, two workgroups per CU).  A small n-extent
-// keeps enough workgroups streaming weights at decode batch sizes (N / 64 of
-// them), which is what bounds those HBM-bound shapes.
+// The configurations (n x m output tile; wavefront grid; LDS ring depth x K
+// per stage; workgroups per CU the registers and LDS aim at).  Each stage of
+// the ring holds (TN + TM) x BK bf16 values.
+//
+// 64 x 64, 2 x 2 wavefronts of 32 x 32, 5 x 64, two per CU (80 KB each).  Also
+// the expert GEMMs of bi_moe_ffn and the narrow-weight fused lm_head.
 using GemmLibraryCfg = GemmCfg<64, 64, 2, 2, 5, 64, 2>;
-
-// The configuration for wide weights (N >= kGemmWideMinN, e.g. a vocabulary
-// projection) at small M: 128 (n) x 256 (m) output tile, 2 x 4 wavefronts of
-// 64 x 64, a 3-stage ring of 64-wide K stages (144 KB, one workgroup per CU).
-// Such a weight has at least one 128-row strip per CU, so its stream fills the
-// chip even at one m-tile.
+// 128 x 256, 2 x 4 wavefronts of 64 x 64, 3 x 64, one per CU (144 KB).  With
+// at least one 128-row strip per CU a vocabulary-sized weight fills the chip
+// even at one m-tile, so it serves such weights (N >= kGemmWideMinN) below
+// kGemmBigMinMWide rows.
 using GemmWideCfg = GemmCfg<128, 256, 2, 4, 3, 64, 1>;
 constexpr int64_t kGemmWideMinN = 256 * GemmWideCfg::TN;
-
-// The configuration for large M: 256 x 256 output tile, 2 x 4 wavefronts of
-// 128 (n) x 64 (m), a 2-stage ring of 64-wide K stages (128 KB, one workgroup
-// per CU).  Each wavefront issues 64 MFMAs per stage against 24 fragment reads
-// and one barrier, and the tile reads each operand from L2 half as often as
-// the 128 x 256 tile.  Measured on MI355X against the 128 x 256 tile (same
-// inputs, bitwise equal): Qwen3-8B step weights at M = 2300, QKV 102-110 /
-// 131, up 216-219 / 252, down 279 / 335 us; lm_head (fp32) at M = 512 / 2048,
-// 615-635 / 757 and 2242-2292 / 2738 us.  Deeper rings of 32-wide stages on
-// the same tile (4 or 5 stages) and the 4 x 2 wavefront layout were 2-15 %
-// slower; at M <= 256 this tile is 1.3-4.6x slower (too few weight streams).
+// 256 x 256, 2 x 4 wavefronts of 128 x 64, 2 x 64, one per CU (128 KB).  Each
+// wavefront issues 64 MFMAs per stage against 24 fragment reads and one
+// barrier; deeper rings of 32-wide stages and the 4 x 2 wavefront layout were
+// 2-15 % slower on MI355X.  Vocabulary-sized weights take it from
+// kGemmBigMinMWide rows (it is 16 % slower than 128 x 256 at M = 64 there).
 using GemmBigCfg = GemmCfg<256, 256, 2, 4, 2, 64, 1>;
-// For the vocabulary projection the big tile wins from kGemmBigMinMWide rows
-// on (it is 16 % slower at M = 64).
 constexpr int64_t kGemmBigMinMWide = 512;
-
-// Small M: up to kGemmNarrowMaxM rows the weight must be streamed by many
-// workgroups (one CU pulls at most about 50 GB/s from HBM), so the tiles
-// below are narrow in n; up to kGemmNarrowMaxN weight rows they beat the
-// 64 x 64 tile, whose N / 64 workgroups are too few.
-constexpr int64_t kGemmNarrowMaxM = 64;
-constexpr int64_t kGemmNarrowMaxN = 8192;
-
-// The configuration for the smallest batches: 32 (n) x 16 (m) tile, 2 x 1
-// wavefronts of 16 x 16, a 6-stage ring of 128-wide K stages (72 KB, two
-// workgroups per CU).  With one 16-row block of A there is nothing to share
-// between wavefronts along m, so each wavefront streams its own 16 weight rows
-// with five 4 KB stages in flight.  Used up to kGemmSkinnyMaxM rows.  Measured
-// on MI355X against the 16 x 64 / 64 x 64 tiles (bitwise equal), us: down
-// 12288 -> 4096 at M = 1 / 16, 24.9 / 27.1 against 33.7 / 31.8; O 4096 ->
-// 4096 at M = 1, 8.9 against 12.2; QKV 4096 -> 6144 at M = 1 / 16, 11.3 /
-// 12.1 against 13.4 / 13.3; up 4096 -> 12288 at M = 1 / 16, 22.0 / 22.4
-// against 23.1 / 22.0.
-using GemmSkinnyCfg = GemmCfg<32, 16, 2, 1, 6, 128, 2>;
-constexpr int64_t kGemmSkinnyMaxM = 16;
-// For weights of at most kGemmSkinnyMaxN rows (the O and down projections) at
-// 17 to kGemmNarrowMaxM rows: 16 (n) x 64 (m), 1 x 4 wavefronts of 16 x 16, a
-// 4-stage ring of 128-wide K stages (80 KB, two workgroups per CU): N / 16
-// workgroups stream the weight and the four 16-row blocks of A share each of
-// its stages.  Measured as above, us, against the 32 x 16 tile: down at M = 32
-// / 48 / 64, 27.4 / 31.7 / 35.4 against 27.2 / 43.7 / 42.1; O at M = 32 / 48 /
-// 64, 11.9 / 12.9 / 13.8 against 12.4 / 17.5 / 16.2.
-using GemmStripCfg = GemmCfg<16, 64, 1, 4, 4, 128, 2>;
-constexpr int64_t kGemmSkinnyMaxN = 4096;
-
-// The configurations for medium M (between the narrow and large-M rules): a
-// 64 (n) x 128 (m) tile, 2 x 2 wavefronts of 32 x 64, a 3-stage ring of
-// 64-wide K stages (72 KB, two workgroups per CU), and a 128 x 128 tile, 2 x 2
-// wavefronts of 64 x 64, a 4-stage ring (128 KB, one workgroup per CU).  The
-// rule takes the largest of 128 x 128, 64 x 128 and 64 x 64 whose grid has at
-// least kGemmMidMinTiles tiles: larger tiles re-read A and W from L2 fewer
-// times, but below about 192 workgroups the weight stream no longer fills the
-// chip.  Measured on MI355X with weights streamed from HBM (twelve rotating
-// copies), us, 128 x 128 / 64 x 128 / 64 x 64, the chosen one first: QKV
-// 4096 -> 6144 at M = 128 / 256 / 512: 22.4 (64 x 64; 31.7, 42.6) / 31.5
-// (64 x 128; 37.4, 42.5) / 42.8 (128 x 128; 53.0, 52.1); up 4096 -> 12288 at
-// M = 128 / 256 / 512: 37.0 (64 x 128; 42.0) / 45.1 (128 x 128; 55.5) / 83.9
-// (128 x 128; best 81.2 on 64 x 128); down 12288 -> 4096 at M = 128 / 256 /
-// 512: 62.5 / 63.2 (64 x 64) / 87.9 (64 x 128; 105.5 on 64 x 64); O 4096 ->
-// 4096 at M = 512: 30.9 (64 x 128; 36.0 on 64 x 64).
+// Large- and medium-M tiles: 256 x 192 (2 x 4 of 128 x 48, 2 x 64, 112 KB),
+// 192 x 256 (2 x 4 of 96 x 64, 2 x 64, 112 KB), 256 x 160 (2 x 2 of 128 x 80,
+// 3 x 64, 160 KB), 256 x 128 (2 x 4 of 128 x 32, 3 x 64, 144 KB), 192 x 128,
+// 128 x 192 and 128 x 128 (2 x 2, 4 x 64, 160 / 160 / 128 KB), 96 x 192
+// (2 x 2 of 48 x 96, 4 x 64, 144 KB) and 96 x 128 (2 x 2 of 48 x 64, 5 x 64,
+// 140 KB), all one per CU.
+using Gemm256x192Cfg = GemmCfg<256, 192, 2, 4, 2, 64, 1>;
+using Gemm192x256Cfg = GemmCfg<192, 256, 2, 4, 2, 64, 1>;
+using Gemm256x160Cfg = GemmCfg<256, 160, 2, 2, 3, 64, 1>;
+using Gemm256x128Cfg = GemmCfg<256, 128, 2, 4, 3, 64, 1>;
+using Gemm192x128Cfg = GemmCfg<192, 128, 2, 2, 4, 64, 1>;
+using Gemm128x192Cfg = GemmCfg<128, 192, 2, 2, 4, 64, 1>;
+using GemmSquareCfg = GemmCfg<128, 128, 2, 2, 4, 64, 1>;
+using Gemm96x192Cfg = GemmCfg<96, 192, 2, 2, 4, 64, 1>;
+using Gemm96x128Cfg = GemmCfg<96, 128, 2, 2, 5, 64, 1>;
+// Decode-batch tiles, narrow in n so that many workgroups stream the weight
+// (one CU pulls only a few tens of GB/s from HBM): 64 x 128 (2 x 2 of 32 x 64,
+// 3 x 64) and 96 x 64 (2 x 2 of 48 x 32, 4 x 64), two per CU; 64 x 64 with
+// 4 x 128 (128 KB), one per CU; 32 x 64 (2 x 2 of 16 x 32) with 6 x 64, two per
+// CU, or 4 x 128, one per CU; 32 x 32 (2 x 2 of 16 x 16, 8 x 128, 128 KB);
+// 16 x 64 (1 x 4 of 16 x 16) with 4 x 128, two per CU, or 8 x 128, one per CU
+// (the four 16-row blocks of A share each weight stage); and 32 x 16 (2 x 1 of
+// 16 x 16, 6 x 128, two per CU), where each wavefront streams its own 16
+// weight rows.
 using GemmMidCfg = GemmCfg<64, 128, 2, 2, 3, 64, 2>;
-// And for weights of at most kGemmSkinnyMaxN rows at up to kGemmThinMaxM rows
-// (the O and down projections of a decode batch), and of at most
-// kGemmNarrowMaxN rows at 17 to kGemmNarrowMaxM rows: 32 (n) x 64 (m), 2 x 2
-// wavefronts of 16 x 32, a 6-stage ring (72 KB, two workgroups per CU), so
-// twice as many workgroups stream the weight as with 64 x 64.  Measured as
-// above: down at M = 96 / 128, 37.8 / 45.7 against 51.0 / 62.6 us; O at
-// M = 96 / 128, 15.3 / 16.9 against 18.5 / 21.3 us (at M = 256 it is 25-30 %
-// slower than 64 x 64); QKV 4096 -> 6144 at M = 32 / 48 / 64, 13.5 / 15.7 /
-// 17.7 against 15.2 / 19.3 / 22.1 us on a 2-wavefront 16 x 64 tile and 18.1 /
-// 20.6 / 22.4 us on 64 x 64.  Up 4096 -> 12288 at M = 48 / 64 is 15-20 %
-// faster on 64 x 64.
+using Gemm96x64Cfg = GemmCfg<96, 64, 2, 2, 4, 64, 2>;
+using Gemm64x64K128Cfg = GemmCfg<64, 64, 2, 2, 4, 128, 1>;
 using GemmThinCfg = GemmCfg<32, 64, 2, 2, 6, 64, 2>;
-constexpr int64_t kGemmThinMaxM = 128;
-// From kGemmThinMinN weight rows (a fused gate and up projection) the 32 x 64
-// tile also serves 1 to kGemmThinWideMaxM rows: with 512 and more n-tiles the
-// grid fills the chip without the 32 x 16 tile's 16-row m-tiles.  Measured on
-// 4096 -> 24576 at M = 1 / 16 / 32: 41.8 / 38.3 / 41.0 us against 44.9 / 46.9
-// us (32 x 16) and 43.8 us (64 x 64, M = 32); at M = 64 the 64 x 64 tile is
-// 5 % faster.
+using Gemm32x64K128Cfg = GemmCfg<32, 64, 2, 2, 4, 128, 1>;
+using Gemm32x32Cfg = GemmCfg<32, 32, 2, 2, 8, 128, 1>;
+using GemmStripCfg = GemmCfg<16, 64, 1, 4, 4, 128, 2>;
+using Gemm16x64K128Cfg = GemmCfg<16, 64, 1, 4, 8, 128, 1>;
+using GemmSkinnyCfg = GemmCfg<32, 16, 2, 1, 6, 128, 2>;
+// From kGemmThinMinN weight rows (a fused gate and up projection) at 1 to
+// kGemmThinWideMaxM rows the 32 x 64 tile with two workgroups per CU is taken
+// without estimate: on 4096 -> 24576 at M = 1 .. 32 it was 5-8 % faster than
+// the estimate's pick (96 x 64) on MI355X.
 constexpr int64_t kGemmThinMinN = 16384;
 constexpr int64_t kGemmThinWideMaxM = 32;
-using GemmSquareCfg = GemmCfg<128, 128, 2, 2, 4, 64, 1>;
-constexpr int64_t kGemmMidMinTiles = 192;
 
 // Tile rule of the vocabulary-sized weights (N >= kGemmWideMinN) and of the
 // fused lm_head: the big tile from kGemmBigMinMWide rows on, else the wide
@@ -507,44 +466,36 @@ inline auto gemm_with_cfg_wide(int64_t lda, int64_t ldw, int64_t m, int64_t k, F
   return f(GemmWideCfg{});
 }
 
-// Further large- and medium-M tiles for the round-count rule below (n x m,
-// wavefront grid, ring, K per stage, workgroups per CU): 256 x 192 (2 x 4
-// wavefronts of 128 x 48, two 64-wide stages, 112 KB), 192 x 256 (2 x 4 of
-// 96 x 64, 112 KB), 256 x 160 (2 x 2 of 128 x 80, three stages, 160 KB),
-// 256 x 128 (2 x 4 of 128 x 32, three stages, 144 KB), 192 x 128 and
-// 128 x 192 (2 x 2 wavefronts, four stages, 160 KB).
-using Gemm256x192Cfg = GemmCfg<256, 192, 2, 4, 2, 64, 1>;
-using Gemm192x256Cfg = GemmCfg<192, 256, 2, 4, 2, 64, 1>;
-using Gemm256x160Cfg = GemmCfg<256, 160, 2, 2, 3, 64, 1>;
-using Gemm256x128Cfg = GemmCfg<256, 128, 2, 4, 3, 64, 1>;
-using Gemm192x128Cfg = GemmCfg<192, 128, 2, 2, 4, 64, 1>;
-using Gemm128x192Cfg = GemmCfg<128, 192, 2, 2, 4, 64, 1>;
-
-// Compute units of the current device (the number of tile slots per round is
-// this times a configuration's workgroups per CU).  Only speed depends on it.
+// Compute units of the current device (a grid of T tiles puts ceil(T / CUs)
+// workgroups on its busiest CU).  Only speed depends on it.
 int gemm_device_cus();
 
-// The estimated time of configuration C on an m x n x k product, in us.  A
-// grid of T tiles puts L = ceil(T / CUs) workgroups on the busiest compute
-// unit.  One workgroup per CU (OCC = 1): L rounds, each one tile's flops /
-// rate + c0.  Two per CU (OCC = 2): L / 2 rounds with two tiles sharing a CU
-// at (rate, c0), and when L is odd one more with the CU to itself at (rate1,
-// c1), which is markedly faster per tile.  The rates (TFLOP/s per tile) and
-// constants (us) were fitted, weighting each time by its inverse, to every
-// configuration's times on the Qwen3-8B weights (QKV, O, up, fused gate/up,
-// down) at M = 129 .. 4096 on MI355X (160 shapes); over those the rule's picks
-// take 0.7 % more time in total than the fastest configuration of each shape.
-struct GemmRate {
-  double tflops, c0_us;
-  double tflops1 = 0.0, c1_us = 0.0;  // OCC = 2: a round with one workgroup per CU
+// The estimated time of configuration C on an m x n x k product, in us.  The
+// busiest CU runs L = ceil(tiles / CUs) workgroups.  One per CU at a time
+// (OCC = 1): L rounds.  OCC = 2: L / 2 rounds with two workgroups sharing the
+// CU, and when L is odd one more with the CU to itself, which is markedly
+// faster per tile.  A round costs w us per MB of the tile's weight rows
+// (TN x K bf16) + f us per MFLOP of its MFMA work (the tile's rows of A that
+// exist, at most M) + c us; (w1, f1, c1) is the lone-workgroup round.  The
+// coefficients were fitted (non-negative least squares, each time weighted by
+// its inverse) to every configuration's times on MI355X with the weights
+// streamed from HBM: the Qwen3-8B projections QKV 4096 -> 6144, O 4096 ->
+// 4096, up 4096 -> 12288, fused gate/up 4096 -> 24576 and down 12288 -> 4096
+// at M = 1 .. 4096 (155 shapes).  On those the rule's picks took 0.5 % more
+// time in total than the fastest configuration of each shape.
+struct GemmCost {
+  double w, f, c;
+  double w1 = 0.0, f1 = 0.0, c1 = 0.0;
 };
 template <class C>
-inline double gemm_estimate_us(int64_t m, int64_t n, int64_t k, GemmRate r, int cus) {
+inline double gemm_estimate_us(int64_t m, int64_t n, int64_t k, const GemmCost& q, int cus) {
   const int64_t tiles = ((m + C::TM - 1) / C::TM) * ((n + C::TN - 1) / C::TN);
   const int64_t per_cu = (tiles + cus - 1) / cus;
-  const double mflop = 2.0 * C::TM * C::TN * (double)k / 1e6;
-  if (C::OCC == 1) return (double)per_cu * (mflop / r.tflops + r.c0_us);
-  return (double)(per_cu / 2) * (mflop / r.tflops + r.c0_us) + (double)(per_cu % 2) * (mflop / r.tflops1 + r.c1_us);
+  const double rows = (double)(m < C::TM ? m : C::TM);
+  const double wmb = 2.0 * C::TN * (double)k * 1e-6, mflop = 2.0 * rows * C::TN * (double)k * 1e-6;
+  const double shared = q.w * wmb + q.f * mflop + q.c;
+  if (C::OCC == 1) return (double)per_cu * shared;
+  return (double)(per_cu / 2) * shared + (double)(per_cu % 2) * (q.w1 * wmb + q.f1 * mflop + q.c1);
 }
 
 // bi_gemm's configuration.  Every configuration computes every output element
@@ -552,70 +503,59 @@ inline double gemm_estimate_us(int64_t m, int64_t n, int64_t k, GemmRate r, int 
 // 64, ... and one rounding, so the tile decides speed, never bits: the choice
 // may read M without making any row depend on the rest of the batch (the
 // tests compare whole products bitwise across the tiles the rule picks).
-//   N >= kGemmWideMinN:                                     gemm_with_cfg_wide
-//   M <= kGemmThinWideMaxM and N >= kGemmThinMinN:          32 x 64
-//   M <= kGemmSkinnyMaxM:                                   32 x 16
-//   M <= kGemmNarrowMaxM and N <= kGemmSkinnyMaxN:          16 x 64
-//   M <= kGemmThinMaxM and N <= kGemmSkinnyMaxN, or
-//     M <= kGemmNarrowMaxM and N <= kGemmNarrowMaxN:        32 x 64
-//   M <= kGemmThinMaxM:                                     128 x 128, else 64 x 128, with at least
-//                                                           kGemmMidMinTiles tiles; else 64 x 64
-//   otherwise (M > kGemmThinMaxM): the configuration with the least
-//     gemm_estimate_us among 256 x 256, 256 x 192, 192 x 256, 256 x 160,
-//     256 x 128, 128 x 256, 192 x 128, 128 x 192, 128 x 128, 64 x 128 and
-//     64 x 64 (first in that order on a tie).  Above 128 rows the grid's
-//     round count decides much of the time: a tile that leaves most CUs idle
-//     in its last round loses to a smaller one whose rounds are full.
-// (a tile whose offsets would not fit its buffer resources is passed over;
-// the caller checks the chosen one, and the 32 x 16, 16 x 64 and 64 x 64
-// tiles span fewer rows of A and W than any other).
+//   N >= kGemmWideMinN:                                  gemm_with_cfg_wide
+//   M <= kGemmThinWideMaxM and N >= kGemmThinMinN:       32 x 64, two per CU
+//   otherwise: the candidate with the least gemm_estimate_us (first in the
+//     list below on a tie).
+// A candidate is passed over when its operand offsets would not fit its
+// buffer resources, and one with 128-wide K stages when K is a multiple of 64
+// but not of 128.  A tile's last stage runs all of its MFMA steps, those past
+// K on zeros; a step on zeros leaves the accumulator as it is, except that it
+// turns an exact -0 into +0.  With that exclusion either every candidate ends
+// on at least one such step (K not a multiple of 64) or none does, so even the
+// sign of an exact zero does not depend on the tile.  The caller checks the
+// chosen tile; if none fits, the 32 x 16 tile is returned (it spans fewer rows
+// than any other).
 template <class F>
 inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, F&& f) {
   if (n >= kGemmWideMinN) return gemm_with_cfg_wide(lda, ldw, m, k, f);
   if (m <= kGemmThinWideMaxM && n >= kGemmThinMinN && gemm_offsets_fit<GemmThinCfg>(lda, ldw, k))
     return f(GemmThinCfg{});
-  if (m <= kGemmSkinnyMaxM) return f(GemmSkinnyCfg{});
-  if (m <= kGemmNarrowMaxM && n <= kGemmSkinnyMaxN) return f(GemmStripCfg{});
-  if (((m <= kGemmThinMaxM && n <= kGemmSkinnyMaxN) || (m <= kGemmNarrowMaxM && n <= kGemmNarrowMaxN)) &&
-      gemm_offsets_fit<GemmThinCfg>(lda, ldw, k))
-    return f(GemmThinCfg{});
-  if (m <= kGemmThinMaxM) {
-    auto tiles = [&](auto cfg) {
-      using C = decltype(cfg);
-      return ((m + C::TM - 1) / C::TM) * ((n + C::TN - 1) / C::TN);
-    };
-    if (m > kGemmNarrowMaxM && tiles(GemmSquareCfg{}) >= kGemmMidMinTiles &&
-        gemm_offsets_fit<GemmSquareCfg>(lda, ldw, k))
-      return f(GemmSquareCfg{});
-    if (m > kGemmNarrowMaxM && tiles(GemmMidCfg{}) >= kGemmMidMinTiles && gemm_offsets_fit<GemmMidCfg>(lda, ldw, k))
-      return f(GemmMidCfg{});
-    return f(GemmLibraryCfg{});
-  }
   const int cus = gemm_device_cus();
-  int pick = 10;  // 64 x 64: always fits
+  const bool k_pads_128 = (k % 128) != 0 && (k % 64) == 0;
+  int pick = -1;
   double best = 0.0;
-  bool have = false;
-  auto consider = [&](int id, auto cfg, GemmRate r) {
+  auto consider = [&](int id, auto cfg, GemmCost q) {
     using C = decltype(cfg);
+    if (C::BK == 128 && k_pads_128) return;
     if (!gemm_offsets_fit<C>(lda, ldw, k)) return;
-    const double t = gemm_estimate_us<C>(m, n, k, r, cus);
-    if (!have || t < best) {
-      have = true;
+    const double t = gemm_estimate_us<C>(m, n, k, q, cus);
+    if (pick < 0 || t < best) {
       best = t;
       pick = id;
     }
   };
-  consider(0, GemmBigCfg{}, {6.10, 8.8});
-  consider(1, Gemm256x192Cfg{}, {5.30, 4.7});
-  consider(2, Gemm192x256Cfg{}, {5.55, 7.5});
-  consider(3, Gemm256x160Cfg{}, {4.70, 7.4});
-  consider(4, Gemm256x128Cfg{}, {5.08, 7.8});
-  consider(5, GemmWideCfg{}, {5.18, 7.5});
-  consider(6, Gemm192x128Cfg{}, {4.22, 6.2});
-  consider(7, Gemm128x192Cfg{}, {4.05, 4.3});
-  consider(8, GemmSquareCfg{}, {3.63, 3.1});
-  consider(9, GemmMidCfg{}, {1.39, -7.2, 2.65, 2.2});
-  consider(10, GemmLibraryCfg{}, {1.08, -5.0, 1.86, 0.0});
+  consider(0, GemmBigCfg{}, {28.789, 0.061, 9.436});
+  consider(1, Gemm256x192Cfg{}, {30.123, 0.039, 7.480});
+  consider(2, Gemm192x256Cfg{}, {32.462, 0.063, 9.529});
+  consider(3, Gemm256x160Cfg{}, {17.765, 0.104, 9.087});
+  consider(4, Gemm256x128Cfg{}, {17.457, 0.065, 9.572});
+  consider(5, GemmWideCfg{}, {22.194, 0.113, 8.461});
+  consider(6, Gemm192x128Cfg{}, {18.472, 0.097, 7.899});
+  consider(7, Gemm128x192Cfg{}, {20.107, 0.141, 7.245});
+  consider(8, Gemm96x192Cfg{}, {21.946, 0.157, 7.526});
+  consider(9, GemmSquareCfg{}, {20.521, 0.112, 5.966});
+  consider(10, Gemm96x128Cfg{}, {21.514, 0.133, 6.511});
+  consider(11, GemmMidCfg{}, {77.378, 0.091, 0.808, 39.154, 0.070, 5.419});
+  consider(12, Gemm96x64Cfg{}, {0.000, 0.657, 5.408, 22.353, 0.060, 5.723});
+  consider(13, GemmLibraryCfg{}, {57.408, 0.000, 0.928, 23.489, 0.133, 4.674});
+  consider(14, Gemm64x64K128Cfg{}, {24.700, 0.078, 3.553});
+  consider(15, GemmThinCfg{}, {84.145, 0.000, 0.000, 34.108, 0.226, 3.949});
+  consider(16, Gemm32x64K128Cfg{}, {36.872, 0.084, 2.112});
+  consider(17, Gemm32x32Cfg{}, {29.535, 0.000, 2.520});
+  consider(18, GemmStripCfg{}, {100.503, 0.353, 0.000, 56.774, 0.321, 2.920});
+  consider(19, Gemm16x64K128Cfg{}, {47.860, 0.347, 1.434});
+  consider(20, GemmSkinnyCfg{}, {35.889, 0.000, 3.331, 22.032, 0.461, 5.352});
   switch (pick) {
     case 0: return f(GemmBigCfg{});
     case 1: return f(Gemm256x192Cfg{});
@@ -625,9 +565,19 @@ inline auto gemm_with_cfg_mn(int64_t lda, int64_t ldw, int64_t m, int64_t n, int
     case 5: return f(GemmWideCfg{});
     case 6: return f(Gemm192x128Cfg{});
     case 7: return f(Gemm128x192Cfg{});
-    case 8: return f(GemmSquareCfg{});
-    case 9: return f(GemmMidCfg{});
-    default: return f(GemmLibraryCfg{});
+    case 8: return f(Gemm96x192Cfg{});
+    case 9: return f(GemmSquareCfg{});
+    case 10: return f(Gemm96x128Cfg{});
+    case 11: return f(GemmMidCfg{});
+    case 12: return f(Gemm96x64Cfg{});
+    case 13: return f(GemmLibraryCfg{});
+    case 14: return f(Gemm64x64K128Cfg{});
+    case 15: return f(GemmThinCfg{});
+    case 16: return f(Gemm32x64K128Cfg{});
+    case 17: return f(Gemm32x32Cfg{});
+    case 18: return f(GemmStripCfg{});
+    case 19: return f(Gemm16x64K128Cfg{});
+    default: return f(GemmSkinnyCfg{});
   }
 }
 

@@ -65,9 +65,9 @@ def test_host_validation_without_gpu(lib):
     assert route(4, 4096, 128, 0) == bi.BI_ERR_INVALID_ARG
     assert route(0, 4096, 128, 8) == bi.BI_OK
     assert lib.bi_moe_route(None, 4096, P, 4, 4096, 128, 8, P, P, P, None) == bi.BI_ERR_INVALID_ARG
-    # a slice of W spanning 2^31 bytes cannot be addressed by one buffer resource (m = 65,
-    # n = 4: the 32 x 64 tile reads 32-row slices of W); up to 16 rows the 32 x 16 tile
-    # reads 32-row slices of W and 16-row slices of A
+    # a slice of W or A spanning 2^31 bytes cannot be addressed by one buffer resource: at
+    # k = 64 (a multiple of 64, not of 128) the rule's candidates read at least 32-row
+    # slices of W and 16-row slices of A, so no tile fits these strides
     assert lib.bi_gemm(P, 64, P, 1 << 26, P, 64, 0, 65, 4, 64, None) == bi.BI_ERR_UNSUPPORTED
     assert lib.bi_gemm(P, 64, P, 1 << 26, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_UNSUPPORTED
     assert lib.bi_gemm(P, 1 << 27, P, 64, P, 64, 0, 4, 4, 64, None) == bi.BI_ERR_UNSUPPORTED

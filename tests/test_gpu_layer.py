@@ -131,8 +131,8 @@ def _padded(rows, cols, pad, seed, tag, std=1.0):
 
 
 # (M, N, K): the decode and mixed-batch shapes of the O and down projections
-# (every tile of the rule: 32 x 16, 16 x 64, 32 x 64, 64 x 64, 64 x 128, 128 x 128,
-# 256 x 256), and small shapes with a ragged last n-group (N % 4 != 0).
+# (tiles from 16 x 64 to 256 x 160 under the rule), and small shapes with a ragged
+# last n-group (N % 4 != 0).
 GEMM_ADD_SHAPES = [(1, 4096, 4096), (16, 4096, 12288), (17, 4096, 4096), (64, 4096, 12288), (65, 4096, 4096),
                    (128, 4096, 12288), (300, 4096, 4096), (700, 4096, 4096), (2300, 4096, 12288),
                    (5, 100, 64), (37, 38, 96), (130, 202, 128)]
