@@ -304,8 +304,9 @@ bi_status bi_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, c
 /*
  * Mixture-of-experts FFN over a batch of tokens (the routed expert layer of the
  * Qwen3-235B-A22B-shaped workload; the expert FFN is not on the pages).  The
- * invariance rule is [BINR]'s answer on a fixed per-element reduction order
- * regardless of batch size or position in the batch: a token's output depends
+ * invariance rule is [BINR]'s answer on a fixed per-element reduction order,
+ * one that neither the batch's size nor a row's place in it may change: a
+ * token's output depends
  * only on its own x row, routing and the weights, never on which other tokens
  * share its experts.
  *   y[t] = bf16( sum over s = 0 .. top_k-1 ascending, in fp32, of
@@ -331,8 +332,8 @@ bi_status bi_attn_prefill(const void* q, int64_t ld_q, const int32_t* q_start, c
 /*
  * Router of the mixture-of-experts layer (workload support, the Qwen3-235B-
  * A22B-shaped layer: 128 experts, top-8; routing is not on the pages, and the
- * invariance rule is [BINR]'s answer on a fixed per-element reduction order
- * regardless of batch size or position in the batch).
+ * invariance rule is [BINR]'s answer on a fixed per-element reduction order,
+ * one that neither the batch's size nor a row's place in it may change).
  *   logits[t, e]         = sum_k x[t, k] w_gate[e, k]      (bi_gemm, fp32 out)
  *   expert_ids[t, s]     = the s-th expert in the order: larger logit first,
  *                          lower expert index first among equal logits (a NaN

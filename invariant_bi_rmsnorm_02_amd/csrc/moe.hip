@@ -1,8 +1,9 @@
 // Mixture-of-experts FFN for a batch of tokens, batch-invariant: a token's
 // output depends only on its own hidden state, its routing and the weights,
 // never on which other tokens share its experts ("Batch Invariance and
-// Numerical Reproducibility", answer on a fixed per-element reduction order
-// "regardless of batch size or position in the batch").  The expert FFN itself
+// Numerical Reproducibility", answer on a fixed per-element reduction order:
+// the order may not change with the batch's size or a row's place in it).  The
+// expert FFN itself
 // is not on the pages; it is the workload's: y_t = sum over the top-k slots s,
 // in ascending s, of w[t, s] * W_down[e] SiLU(W_up[e] x_t), e = experts[t, s].
 //

@@ -254,7 +254,7 @@ def test_gemm_every_configuration_gives_the_same_bits(cfg):
     assert_f32_close(whole[::131, ::113], ref, f"config {cfg} fp32 parity")
 
 
-def _rule_edges(n, k, lo=1, hi=1100):
+def _rule_edges(n, k, lo=1, hi=4400):
     """Consecutive m where the rule's configuration changes."""
     out, prev = [], bi.gemm_config(lo, n, k)
     for m in range(lo + 1, hi + 1):
@@ -268,25 +268,27 @@ def _rule_edges(n, k, lo=1, hi=1100):
 @pytest.mark.parametrize("n,k", [(12288, 4096), (6144, 4096), (4096, 12288), (4096, 4096), (24576, 4096),
                                  (4097, 512), (8200, 512)])
 def test_gemm_tile_rule_edges(n, k):
-    """At every rows count up to 1100 where the rule changes configuration for
+    """At every rows count up to 4400 where the rule changes configuration for
     these weights (the Qwen3-8B projections and two ragged ones), m_lo and
     m_hi = m_lo + 1 run different kernels; the rows the two products share,
-    and the larger product against the same rows in 64-row slices, must agree
-    bit for bit."""
+    and the larger product against the same rows in slices (64 rows up to
+    1100, else 256), must agree bit for bit."""
     edges = _rule_edges(n, k)
     assert edges, f"the rule never changes configuration for n={n} k={k}"
     w = W.randn_bf16((n, k), 13, "w", n, std=0.02, device=DEV)
-    a_all = W.randn_bf16((1100, k), 13, "x", 1100, device=DEV)
+    a_all = W.randn_bf16((edges[-1][1], k), 13, "x", 4400, device=DEV)
     for m_lo, m_hi, c_lo, c_hi in edges:
         a = a_all[:m_hi]
         log_case(f"gemm tile rule edge n={n} k={k} m={m_lo}/{m_hi}: {c_lo} -> {c_hi}")
+        step = 64 if m_hi <= 1100 else 256
         for dt in (torch.bfloat16, torch.float32):
             lo = bi.bi_gemm(a[:m_lo], w, out_dtype=dt)
             hi = bi.bi_gemm(a, w, out_dtype=dt)
             assert_bitwise(hi[:m_lo], lo, f"rows shared by m={m_lo} and m={m_hi} ({dt})")
             if m_hi > 64:
-                sliced = torch.cat([bi.bi_gemm(a[r:r + 64], w, out_dtype=dt) for r in range(0, m_hi, 64)])
-                assert_bitwise(hi, sliced, f"m={m_hi} vs 64-row slices ({dt})")
+                sliced = torch.cat([bi.bi_gemm(a[r:r + step], w, out_dtype=dt) for r in range(0, m_hi, step)])
+                assert_bitwise(hi, sliced, f"m={m_hi} vs {step}-row slices ({dt})")
+            del lo, hi
 
 
 @pytest.mark.parametrize("k", [192, 160, 4096])
