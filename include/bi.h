@@ -95,6 +95,8 @@ bi_status bi_rmsnorm(const void* x, int64_t ldx, const void* gamma, float eps,
  *     measured on MI355X (bi_gemm_tile reports the choice).  When k is a
  *     multiple of 64 but not of 128, tiles with 128-wide K stages are left
  *     out, so that an exact zero gets the same sign from every candidate.
+ * A tile of at most 64 rows that holds all m rows reads the weight with
+ * non-temporal loads (each weight row is read once).
  * (A tile is passed over for the next candidate when its operand offsets
  * would not fit, below.)
  * k % 32 == 0; m, n >= 0 (m == 0 or n == 0 is a no-op); k >= 32.
@@ -111,12 +113,14 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw,
  * n = 2f) runs for these arguments on the current device: an output tile of
  * tile_n weight rows by tile_m rows of A, waves_n x waves_m wavefronts, an LDS
  * ring of `stages` stages of stage_k values of K, aimed at per_cu workgroups
- * per compute unit.  It changes no result bit; tests use it to reach every
- * configuration.  Host-only, no GPU work.  BI_ERR_INVALID_ARG for a null
- * pointer, m, n or k <= 0, or lda, ldw < k.
+ * per compute unit; stream_w = 1 when the weight loads are marked
+ * non-temporal (tiles of at most 64 rows when m fits in one of them).  It
+ * changes no result bit; tests use it to reach every configuration.
+ * Host-only, no GPU work.  BI_ERR_INVALID_ARG for a null pointer, m, n or
+ * k <= 0, or lda, ldw < k.
  */
 typedef struct {
-  int32_t tile_n, tile_m, waves_n, waves_m, stages, stage_k, per_cu;
+  int32_t tile_n, tile_m, waves_n, waves_m, stages, stage_k, per_cu, stream_w;
 } bi_gemm_config;
 bi_status bi_gemm_tile(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, bi_gemm_config* config);
 

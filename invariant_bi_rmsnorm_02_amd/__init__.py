@@ -165,12 +165,13 @@ def bi_gemm(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None
 
 
 class _GemmConfig(ctypes.Structure):
-    _fields_ = [(f, ctypes.c_int32) for f in ("tile_n", "tile_m", "waves_n", "waves_m", "stages", "stage_k", "per_cu")]
+    _fields_ = [(f, ctypes.c_int32) for f in ("tile_n", "tile_m", "waves_n", "waves_m", "stages", "stage_k", "per_cu",
+                                              "stream_w")]
 
 
 def gemm_config(m: int, n: int, k: int, lda: Optional[int] = None, ldw: Optional[int] = None) -> Tuple[int, ...]:
-    """(tile n, tile m, wavefronts n, wavefronts m, stages, K per stage, workgroups per CU) of the kernel
-    configuration bi_gemm runs for an m x n x k product on the current device."""
+    """(tile n, tile m, wavefronts n, wavefronts m, stages, K per stage, workgroups per CU, non-temporal
+    weight loads) of the kernel configuration bi_gemm runs for an m x n x k product on the current device."""
     c = _GemmConfig()
     _check("bi_gemm_tile", lib().bi_gemm_tile(lda or k, ldw or k, m, n, k, ctypes.byref(c)))
     return tuple(getattr(c, f) for f, _ in _GemmConfig._fields_)

@@ -126,9 +126,9 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* 
 
 bi_status bi_gemm_tile(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, bi_gemm_config* config) {
   if (!config || m <= 0 || n <= 0 || k <= 0 || lda < k || ldw < k) return BI_ERR_INVALID_ARG;
-  int v[7];
+  int v[8];
   bi::gemm_config_of(lda, ldw, m, n, k, v);
-  *config = bi_gemm_config{v[0], v[1], v[2], v[3], v[4], v[5], v[6]};
+  *config = bi_gemm_config{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
   return BI_OK;
 }
 

@@ -20,11 +20,11 @@ int gemm_device_cus() {
   return n;
 }
 
-void gemm_config_of(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, int out[7]) {
+void gemm_config_of(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, int out[8]) {
   gemm_with_cfg_mn(lda, ldw, m, n, k, [&](auto cfg) {
     using C = decltype(cfg);
-    const int v[7] = {C::TN, C::TM, C::WGN, C::WGM, C::S, C::BK, C::OCC};
-    for (int i = 0; i < 7; ++i) out[i] = v[i];
+    const int v[8] = {C::TN, C::TM, C::WGN, C::WGM, C::S, C::BK, C::OCC, C::CPW == kCpolNt ? 1 : 0};
+    for (int i = 0; i < 8; ++i) out[i] = v[i];
     return 0;
   });
 }

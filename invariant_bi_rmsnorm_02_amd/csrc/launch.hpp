@@ -15,8 +15,9 @@ hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* gamma, float e
 // False when the tile count or a workgroup's buffer offsets would overflow.
 bool gemm_supported(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k);
 // The output tile (n x m) bi_gemm's rule picks for these arguments.
-// bi_gemm's configuration for a shape: tile n, tile m, wavefronts n, m, stages, K per stage, per CU.
-void gemm_config_of(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, int out[7]);
+// bi_gemm's configuration for a shape: tile n, tile m, wavefronts n, m, stages, K per stage, per CU,
+// non-temporal weight loads (0 / 1).
+void gemm_config_of(int64_t lda, int64_t ldw, int64_t m, int64_t n, int64_t k, int out[8]);
 
 hipError_t launch_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, void* c, int64_t ldc,
                        bool c_f32, int64_t m, int64_t n, int64_t k, hipStream_t stream);

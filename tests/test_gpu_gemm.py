@@ -202,16 +202,18 @@ def test_gemm_large_m_rule_gives_the_same_bits(n, k):
 
 
 # Every configuration of the estimate-based rule (tile n, tile m, wavefronts n,
-# m, stages, K per stage, workgroups per CU).  The rule depends on m, n, k and
+# m, stages, K per stage, workgroups per CU, non-temporal weight loads).  The rule depends on m, n, k and
 # the device's compute units, so the tests search for a product that reaches
 # each configuration instead of fixing its shape.
-RULE_CONFIGS = [(256, 256, 2, 4, 2, 64, 1), (256, 192, 2, 4, 2, 64, 1), (192, 256, 2, 4, 2, 64, 1),
-                (256, 160, 2, 2, 3, 64, 1), (256, 128, 2, 4, 3, 64, 1), (128, 256, 2, 4, 3, 64, 1),
-                (192, 128, 2, 2, 4, 64, 1), (128, 192, 2, 2, 4, 64, 1), (96, 192, 2, 2, 4, 64, 1),
-                (128, 128, 2, 2, 4, 64, 1), (96, 128, 2, 2, 5, 64, 1), (64, 128, 2, 2, 3, 64, 2),
-                (96, 64, 2, 2, 4, 64, 2), (64, 64, 2, 2, 5, 64, 2), (64, 64, 2, 2, 4, 128, 1),
-                (32, 64, 2, 2, 6, 64, 2), (32, 64, 2, 2, 4, 128, 1), (32, 32, 2, 2, 8, 128, 1),
-                (16, 64, 1, 4, 4, 128, 2), (16, 64, 1, 4, 8, 128, 1), (32, 16, 2, 1, 6, 128, 2)]
+_BASE_CONFIGS = [(256, 256, 2, 4, 2, 64, 1), (256, 192, 2, 4, 2, 64, 1), (192, 256, 2, 4, 2, 64, 1),
+                 (256, 160, 2, 2, 3, 64, 1), (256, 128, 2, 4, 3, 64, 1), (128, 256, 2, 4, 3, 64, 1),
+                 (192, 128, 2, 2, 4, 64, 1), (128, 192, 2, 2, 4, 64, 1), (96, 192, 2, 2, 4, 64, 1),
+                 (128, 128, 2, 2, 4, 64, 1), (96, 128, 2, 2, 5, 64, 1), (64, 128, 2, 2, 3, 64, 2),
+                 (96, 64, 2, 2, 4, 64, 2), (64, 64, 2, 2, 5, 64, 2), (64, 64, 2, 2, 4, 128, 1),
+                 (32, 64, 2, 2, 6, 64, 2), (32, 64, 2, 2, 4, 128, 1), (32, 32, 2, 2, 8, 128, 1),
+                 (16, 64, 1, 4, 4, 128, 2), (16, 64, 1, 4, 8, 128, 1), (32, 16, 2, 1, 6, 128, 2)]
+# The last field: weight loads non-temporal (tiles of at most 64 rows holding all m rows).
+RULE_CONFIGS = [c + (0,) for c in _BASE_CONFIGS] + [c + (1,) for c in _BASE_CONFIGS if c[1] <= 64]
 SEARCH_NK = [(n, k) for k in (4096, 512, 12288) for n in (4096, 6144, 12288, 24576, 1024, 2048, 8192)]
 SEARCH_M = list(range(1, 257)) + list(range(257, 4400, 7))
 
