@@ -43,15 +43,20 @@ constexpr int kRouteThreads = 256;
 // fp32 MFMA chain per element over k ascending), so the choice between them,
 // made from the average rows per expert, changes no bit.  With few rows per
 // expert the 64 x 64 tile gives every expert's weights many streaming
-// workgroups; from 32 rows per expert on, the 128 x 256 tile holds an
+// workgroups; above 32 rows per expert, the 128 x 256 tile holds an
 // expert's rows in one m-tile (each weight slab is read once) and re-reads
 // the gathered rows for 12 n-tiles of the up projection instead of 24.
 // Measured on MI355X, 128 experts 4096 -> 1536 -> 4096, top 8, us (64 x 64 /
 // 128 x 256): T = 64: 546 / 575; 512: 676 / 661; 1024: 910 / 734; 2048:
-// 1366 / 888.  128 x 128, 256 x 128, 256 x 256 and 64 x 256 tiles were within
-// 5 % of the better one or slower.
-using MoeSmallCfg = GemmLibraryCfg;
-using MoeLargeCfg = GemmWideCfg;
+// 1366 / 888.  128 x 128, 256 x 128, 256 x 256, 64 x 256, 96 x 128, 192 x 128,
+// 192 x 256, 128 x 192 and 96 x 192 tiles, and different tiles for the up and
+// down GEMMs, were within 5 % of the better one or slower.  Both read the
+// weights with non-temporal loads: an expert's rows mostly fit one m-tile, so
+// each weight strip is read by one workgroup (T = 8 / 64 / 512 on 64 x 64: 243
+// / 550 / 666 -> 215 / 493 / 623 us; T = 1024 / 2048 on 128 x 256: 717 / 861
+// -> 716 / 843 us).
+using MoeSmallCfg = GemmNt<GemmLibraryCfg>::type;
+using MoeLargeCfg = GemmNt<GemmWideCfg>::type;
 constexpr int64_t kMoeLargeRowsPerExpert = 32;
 
 // Workspace carve-up, shared by the host-side size query and the launcher.
@@ -412,7 +417,7 @@ hipError_t launch_moe_ffn(const void* x, int64_t ldx, const int32_t* expert_ids,
                           int T, int top_k, int E, const void* w_up, const void* w_down, int H, int F, void* y,
                           int64_t ldy, void* workspace, hipStream_t stream) {
   const int64_t P = (int64_t)T * top_k;
-  if (P >= kMoeLargeRowsPerExpert * (int64_t)E)
+  if (P > kMoeLargeRowsPerExpert * (int64_t)E)
     return launch_moe_ffn_cfg<MoeLargeCfg>(x, ldx, expert_ids, expert_weights, T, top_k, E, w_up, w_down, H, F, y,
                                            ldy, workspace, stream);
   return launch_moe_ffn_cfg<MoeSmallCfg>(x, ldx, expert_ids, expert_weights, T, top_k, E, w_up, w_down, H, F, y,

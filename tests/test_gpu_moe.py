@@ -75,12 +75,13 @@ def test_moe_parity_full_shape_sampled(full_weights):
 
 
 def test_moe_batch_invariance(full_weights):
-    """Token 0's output bits at T = 1, 8, 64, 511, 512, 2048, at shuffled positions
-    (from 32 rows per expert, T = 512 with 128 experts and top 8, the grouped
-    GEMMs switch from the 64 x 64 to the 128 x 256 tile)."""
+    """Token 0's output bits at T = 1, 8, 64, 511, 512, 513, 2048, at shuffled
+    positions (above 32 rows per expert, T = 513 with 128 experts and top 8,
+    the grouped GEMMs switch from the 64 x 64 to the 128 x 256 tile)."""
     w_up, w_down = full_weights
     ref = None
-    for T, slot in ((1, 0), (8, 0), (8, 5), (64, 37), (511, 200), (512, 300), (2048, 1500), (2048, 2047)):
+    for T, slot in ((1, 0), (8, 0), (8, 5), (64, 37), (511, 200), (512, 300), (513, 400), (2048, 1500),
+                    (2048, 2047)):
         log_case(f"moe invariance T={T} slot={slot}")
         others = list(range(1, T))
         ids = others[:slot] + [0] + others[slot:]
