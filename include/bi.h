@@ -87,7 +87,7 @@ bi_status bi_rmsnorm(const void* x, int64_t ldx, const void* gamma, float eps,
  * the same bits, so the tile only sets the speed; it is chosen from the
  * shape (n x m, first rule that applies):
  *   n >= 32768 (a vocabulary-sized weight): 256 x 256 from m >= 512, else
- *     128 x 256;
+ *     128 x 256 (with non-temporal weight loads up to m = 256);
  *   m <= 32 and n >= 16384: 32 x 64;
  *   otherwise, of twenty-one configurations (tiles from 256 x 256 down to
  *     16 x 64 and 32 x 16), the one whose grid is estimated to finish first,

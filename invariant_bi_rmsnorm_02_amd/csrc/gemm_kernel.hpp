@@ -463,16 +463,6 @@ using GemmSkinnyCfg = GemmCfg<32, 16, 2, 1, 6, 128, 2>;
 constexpr int64_t kGemmThinMinN = 16384;
 constexpr int64_t kGemmThinWideMaxM = 32;
 
-// Tile rule of the vocabulary-sized weights (N >= kGemmWideMinN) and of the
-// fused lm_head: the big tile from kGemmBigMinMWide rows on, else the wide
-// one.  The fused lm_head's per-row reduction records do not depend on the
-// tile (lm_head.hip), so this choice changes no bit either.
-template <class F>
-inline auto gemm_with_cfg_wide(int64_t lda, int64_t ldw, int64_t m, int64_t k, F&& f) {
-  if (m >= kGemmBigMinMWide && gemm_offsets_fit<GemmBigCfg>(lda, ldw, k)) return f(GemmBigCfg{});
-  return f(GemmWideCfg{});
-}
-
 // The same configuration with its weight loads non-temporal.
 template <class C>
 struct GemmNt;
@@ -480,6 +470,18 @@ template <int TN, int TM, int WGN, int WGM, int S, int BK, int OCC, int CPW>
 struct GemmNt<GemmCfg<TN, TM, WGN, WGM, S, BK, OCC, CPW>> {
   using type = GemmCfg<TN, TM, WGN, WGM, S, BK, OCC, kCpolNt>;
 };
+
+// Tile rule of the vocabulary-sized weights (N >= kGemmWideMinN) and of the
+// fused lm_head: the big tile from kGemmBigMinMWide rows on, else the wide
+// one, with non-temporal weight loads while its single m-tile holds all of M
+// (each weight strip is then read once).  The fused lm_head's per-row reduction records do not depend on the
+// tile (lm_head.hip), so this choice changes no bit either.
+template <class F>
+inline auto gemm_with_cfg_wide(int64_t lda, int64_t ldw, int64_t m, int64_t k, F&& f) {
+  if (m >= kGemmBigMinMWide && gemm_offsets_fit<GemmBigCfg>(lda, ldw, k)) return f(GemmBigCfg{});
+  if (m <= GemmWideCfg::TM) return f(GemmNt<GemmWideCfg>::type{});
+  return f(GemmWideCfg{});
+}
 
 // Calls f on configuration C, with its weight loads marked non-temporal when
 // the grid has one m-tile of at most 64 rows: then every weight strip is read
