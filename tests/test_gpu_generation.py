@@ -14,6 +14,8 @@ and split RMSNorm, each choosing its split from the batch size) is run the same
 way as the negative control: its logprobs change with the co-batch, and its
 completions are expected to split into several unique ones.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -26,7 +28,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 SEED = 71
 H, HQ, HKV, D, F, V = 4096, 32, 8, 128, 12288, 151936
-LAYERS, PROMPT, GEN, RUNS, OTHERS = 2, 16, 64, 16, 255
+# BI_GENERATION_RUNS sets the number of completions per side (16 by default;
+# the pages' own count, 1000, takes about ten minutes).
+LAYERS, PROMPT, GEN, OTHERS = 2, 16, 64, 255
+RUNS = int(os.environ.get("BI_GENERATION_RUNS", "16"))
 EPS = 1e-6
 
 
@@ -144,7 +149,8 @@ def _unique(model, what):
     outs = []
     for run in range(RUNS):
         outs.append(_generate(model, run))
-        print(f"[gen] {what} run {run}: batch sizes {outs[-1][2][:6]}..., tokens {outs[-1][0][:8]}...", flush=True)
+        if run < 16 or run % 50 == 0:
+            print(f"[gen] {what} run {run}: batch sizes {outs[-1][2][:6]}..., tokens {outs[-1][0][:8]}...", flush=True)
     return outs
 
 
