@@ -131,7 +131,7 @@ def time_fn(torch, fn, reps, warmup=3, per_graph=10):
             graphs.append(g)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    for g in graphs[:1]:
+    for g in graphs:    # every graph replays once untimed
         g.replay()
     torch.cuda.synchronize()
     ts = []
