@@ -114,7 +114,8 @@ bi_status bi_gemm(const void* a, int64_t lda, const void* w, int64_t ldw,
  * tile_n weight rows by tile_m rows of A, waves_n x waves_m wavefronts, an LDS
  * ring of `stages` stages of stage_k values of K, aimed at per_cu workgroups
  * per compute unit; stream_w = 1 when the weight loads are marked
- * non-temporal (tiles of at most 64 rows when m fits in one of them).  It
+ * non-temporal (when one m-tile holds all m rows: tiles of at most 64 rows,
+ * and the 128 x 256 tile of vocabulary-sized weights).  It
  * changes no result bit; tests use it to reach every configuration.
  * Host-only, no GPU work.  BI_ERR_INVALID_ARG for a null pointer, m, n or
  * k <= 0, or lda, ldw < k.
