@@ -76,7 +76,7 @@ def test_lm_head_logprobs_batch_invariance():
     w = _weights(n)
     ref = None
     ws = None
-    for T in (1, 64, 512):
+    for T in (1, 17, 64, 512):
         for pos in sorted({0, T // 3, T - 1}):
             ids = list(range(1, T))
             ids.insert(pos, 0)
@@ -92,12 +92,13 @@ def test_lm_head_logprobs_batch_invariance():
 
 def test_lm_head_full_vocab_batch_invariance():
     """The lm_head at the workload's size (4096 -> 151936): token 0's logprobs
-    row, greedy token and token logprob bitwise the same at T = 1, 64, 511
+    row, greedy token and token logprob bitwise the same at T = 1, 17, 64, 511
     (128 x 256 GEMM tile), 512, 2048 (256 x 256 tile) and shuffled slots; the
-    per-row reduction records do not depend on the tile."""
+    per-row reduction records do not depend on the tile, and a tile's 16-row
+    blocks past its last row (skipped in the epilogue) change nothing."""
     w = _weights(V)
     ref = gref = None
-    for T, pos in ((1, 0), (64, 50), (511, 510), (512, 0), (2048, 1500)):
+    for T, pos in ((1, 0), (17, 16), (64, 50), (511, 510), (512, 0), (2048, 1500)):
         log_case(f"full-vocab lm_head invariance T={T} slot={pos}")
         ids = list(range(1, T))
         ids.insert(pos, 0)
